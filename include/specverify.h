@@ -1,0 +1,161 @@
+/*
+ * specverify -- batched speculative-sampling verify step for AMD Instinct
+ * MI355X (gfx950), C ABI.
+ *
+ * One call verifies a batch of B sequences, each with up to K drafted tokens:
+ *
+ *   1. temperature softmax over the vocabulary for every target position
+ *      0..L_b and every draft position 0..L_b-1 of row b;
+ *   2. optionally the top-p (nucleus) filter on each of those distributions;
+ *   3. for j = 0..L_b-1 the acceptance test u < min(1, p'(x_j)/q'(x_j)), where
+ *      the first failing j is the row's first rejection n_b (n_b = L_b if
+ *      none fails);
+ *   4. one more token: on a rejection, drawn from max(0, p'_n - q'_n)/Z by
+ *      inverse CDF; otherwise a bonus token drawn from p'_L.
+ *
+ * The method is the one on the page "Speculative Decoding للمحترف: ضاعف سرعة
+ * Llama 70B لـ 2.4x بدون فقد token واحد": section "المفهوم بالتقريب" (accept
+ * agreed tokens, reject the first disagreeing one and resample it), section
+ * "التعريف الرياضي من Leviathan et al." (the equation for the acceptance
+ * probability alpha(x) = min(1, p_target(x)/p_draft(x)) and the equation for
+ * the corrected distribution p'(x) = max(0, p_target(x) - p_draft(x))/Z),
+ * section "كود شغّال على vLLM" (the knobs K, temperature and top_p).  The bonus
+ * token is the one of the page "Faster LLM Inference via Sequential Monte
+ * Carlo", section 2 (the scoring step over K+1 positions).  Per-row draft
+ * lengths follow the page "HiSpec: Hierarchical Speculative Decoding for LLMs",
+ * section 2 (per-sequence acceptance in a batch without padding).
+ *
+ * Uniforms come from Philox4x32-10 (Salmon et al., SC'11) with key = (seed low
+ * word, seed high word) and counter = (row, position, 0, 0): output word 0
+ * gives the acceptance uniform, word 1 the resampling uniform, each as
+ * (word >> 8) * 2^-24.  Any implementation following that contract reproduces
+ * the outputs bit for bit, decisions lying within rounding of a boundary
+ * aside.
+ *
+ * Memory: every pointer argument is caller-owned device memory unless stated
+ * otherwise.  Inputs are only read; outputs are written in full for every row.
+ * The library owns a small scratch buffer per (device, stream), grown on first
+ * use and kept until spec_verify_release().  Calls are asynchronous on the
+ * given stream and never synchronise the host (except a first call on a
+ * stream, or a call that outgrows the cached scratch, which allocates).
+ * Concurrent calls on the same stream from several host threads are not
+ * supported; calls on different streams may run concurrently.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPECVERIFY_ABI_VERSION 1
+#define SPECVERIFY_MAX_K 16
+
+/* Element type of a logits tensor. */
+typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
+
+/* Describes a device tensor of logits [B, P, V] whose V axis is contiguous.
+ * Element (b, p, v) lives at data + (b*stride_b + p*stride_p + v) elements.
+ * data must be aligned to the element size; strides may be anything >= 0
+ * (rows need not start on 16-byte boundaries). */
+typedef struct {
+    const void* data;
+    int32_t dtype;       /* sv_dtype */
+    int32_t B, P, V;     /* P = K+1 for target logits, K for draft logits */
+    int64_t stride_b;    /* elements */
+    int64_t stride_p;    /* elements */
+} sv_logits;
+
+/* Status codes.  Negative values are errors. */
+enum {
+    SV_OK = 0,
+    SV_EINVAL = -1,   /* NULL pointer, bad temperature or top_p, bad stride */
+    SV_ESHAPE = -2,   /* B, K or V out of range, or the two tensors disagree */
+    SV_EDTYPE = -3,   /* unknown dtype, or target and draft dtypes differ */
+    SV_EHIP = -4,     /* a HIP runtime call failed; see spec_verify_strerror */
+    SV_ENOMEM = -5,   /* scratch allocation failed */
+    SV_EALIGN = -6    /* a pointer is not aligned to its element size */
+};
+
+/* Probe record layout (float64), per row b and position j in [0, K]:
+ *   [0] target max logit          [1] target sum_v exp((l_v - max)/T)
+ *   [2] draft max logit           [3] draft sum_v exp((l_v - max)/T)
+ *   [4] p'(x_j), filtered target  [5] q'(x_j), filtered draft
+ *   [6] kept target mass (1 when top-p is off)
+ *   [7] kept draft mass  (1 when top-p is off)
+ * and per row b:
+ *   [0] Z, the mass the final token is drawn from
+ *   [1] t = u * Z, the inverse-CDF threshold
+ *   [2] u, the resampling uniform
+ *   [3] n, the first-rejection index
+ * Entries for positions a row does not evaluate are NaN. */
+#define SV_PROBE_POS 8
+#define SV_PROBE_ROW 4
+
+/*
+ * spec_verify -- the verify step (steps 1-4 above) for B rows.
+ *
+ * target_logits   [B, K+1, V] target logits, bf16 or fp32.
+ * draft_logits    [B, K, V] draft logits, same dtype, B and V; 1 <= K <= 16.
+ * draft_tokens    device int32 [B, K], contiguous; entry (b, j) is the drafted
+ *                 id at position j, read only for j < L_b.
+ * draft_len       device int32 [B] with L_b in [0, K], or NULL for L_b = K.
+ *                 Positions >= L_b (and target positions > L_b) are never read.
+ * temperature     > 0, finite; logits are divided by it before the softmax.
+ * top_p           in (0, 1]; 1 switches the nucleus filter off.
+ * seed            64-bit Philox key.
+ * out_tokens      device int32 [B, K+1], contiguous: the n_b accepted drafted
+ *                 ids, then the resampled or bonus token, then -1.
+ * out_n_accepted  device int32 [B]: n_b in [0, L_b], or -1 for an invalid row.
+ * stream          hipStream_t to run on (NULL = the default stream).
+ *
+ * Errors: arguments the host can check return SV_EINVAL / SV_ESHAPE /
+ * SV_EDTYPE / SV_EALIGN and launch nothing.  Data errors cannot be reported
+ * synchronously: a row whose L_b lies outside [0, K], whose drafted id at some
+ * j < L_b lies outside [0, V), or one of whose needed logit rows holds a NaN, a
+ * +inf or only -inf, gets out_n_accepted = -1 and out_tokens = -1 throughout.
+ * Launch failures return SV_EHIP.
+ */
+int spec_verify(const sv_logits* target_logits, const sv_logits* draft_logits,
+                const int32_t* draft_tokens, const int32_t* draft_len,
+                float temperature, float top_p, uint64_t seed,
+                int32_t* out_tokens, int32_t* out_n_accepted, void* stream);
+
+/*
+ * spec_verify_probe -- spec_verify plus the intermediate values behind each
+ * decision, for testing.  probe_pos: device float64 [B, K+1, SV_PROBE_POS];
+ * probe_row: device float64 [B, SV_PROBE_ROW]; layouts above.  Same errors as
+ * spec_verify; the probe pointers must not be NULL.
+ */
+int spec_verify_probe(const sv_logits* target_logits, const sv_logits* draft_logits,
+                      const int32_t* draft_tokens, const int32_t* draft_len,
+                      float temperature, float top_p, uint64_t seed,
+                      int32_t* out_tokens, int32_t* out_n_accepted,
+                      double* probe_pos, double* probe_row, void* stream);
+
+/* Human-readable text for a status code (for SV_EHIP, the last HIP error). */
+const char* spec_verify_strerror(int status);
+
+/* Frees every cached scratch buffer.  The caller must ensure no call is in
+ * flight on any stream. */
+void spec_verify_release(void);
+
+/* Returns SPECVERIFY_ABI_VERSION. */
+int spec_verify_abi_version(void);
+
+/* Kernel timing for measurement.  While enabled, every launch is bracketed by
+ * HIP events on its stream.  spec_verify_profile_read synchronises those
+ * events and writes, for each of the n kernel kinds (0 statistics pass,
+ * 1 nucleus selection, 2 resample), the summed duration in milliseconds and
+ * the number of launches since the last read; it returns the number of kinds
+ * written.  Host arrays ms[n], launches[n]. */
+int spec_verify_profile_enable(int enable);
+int spec_verify_profile_read(double* ms, int64_t* launches, int n);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

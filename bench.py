@@ -1,0 +1,241 @@
+"""Benchmark of the batched speculative-sampling verify step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Workload: B=64 rows, K=5 drafted tokens, V=128256 (Llama-3 vocabulary),
+bfloat16 logits, temperature 0.7, top-p off -- the batched workload of the
+seeded generator.  Three distinct input sets (3 x 180.6 MB, more than the
+256 MB Infinity Cache) are resident in HBM and rotated call by call, so no
+call finds its inputs in the cache.  A step is one spec_verify call: the
+statistics pass over every needed logit row, the accept scan and the
+residual/bonus resample.
+
+Prints one JSON line.  `value` is verified draft positions per second; the
+roofline object prices the dominant kernel (the statistics pass) against
+MI355X's 8 TB/s HBM peak using the logical bytes it must read, sum_b
+(2 L_b + 1) V e; the cpu_baseline object times the float64 oracle on the
+host cores on a bounded sample of the same workload.
+"""
+
+import argparse
+import hashlib
+import json
+import multiprocessing as mp
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+WORKLOAD_CFG = 2
+N_SETS = 3
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_stats_batched.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "rejection_sampling_verifier_amd", "csrc", f)
+                  for f in ("sv_kernels.hip", "sv_device.h", "sv_internal.h")]
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic():
+    """HBM bytes per statistics-pass launch from the committed counter runs,
+    or None when the kernel sources changed since they were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle, unchanged, on a bounded sample
+# ---------------------------------------------------------------------------
+_SAMPLE = None
+
+
+def _oracle_rows(args):
+    import oracle
+
+    si, rows = args
+    inp = _SAMPLE[si]
+    oracle.verify(inp.target, inp.draft, inp.draft_tokens, inp.draft_len, inp.temperature, inp.top_p, inp.seed,
+                  rows=rows)
+    return sum(int(inp.lengths()[r]) for r in rows)
+
+
+def cpu_baseline(sets, budget_rows):
+    global _SAMPLE
+    _SAMPLE = sets
+    cores = max(1, min(16, os.cpu_count() or 1))
+    work = []
+    n = 0
+    for si, inp in enumerate(sets):
+        for b in range(inp.B):
+            if n >= budget_rows:
+                break
+            work.append((si, [b]))
+            n += 1
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(cores) as pool:
+        positions = sum(pool.map(_oracle_rows, work, chunksize=1))
+    dt = time.perf_counter() - t0
+    return {
+        "value": positions / dt,
+        "unit": "positions/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": f"{len(work)} batch rows ({positions} draft positions) of the B=64 K=5 V=128256 bf16 "
+                  f"workload, float64 NumPy oracle, one row per task over {cores} processes, {dt:.1f} s wall",
+    }
+
+
+# ---------------------------------------------------------------------------
+# GPU timing
+# ---------------------------------------------------------------------------
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=192)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the verify step is built and timed on a single MI355X "
+              "(batch rows shard across GPUs with no exchange; see the design notes).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from rejection_sampling_verifier_amd import binding, workloads
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    binding.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    print(f"[bench] generating {N_SETS} input sets of workload {WORKLOAD_CFG}", file=sys.stderr, flush=True)
+    sets = [workloads.make_inputs(WORKLOAD_CFG, s) for s in range(N_SETS)]
+    w = sets[0].workload
+
+    def put(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    dsets = []
+    for inp in sets:
+        dsets.append((put(inp.target), put(inp.draft), torch.from_numpy(inp.draft_tokens).to(dev),
+                      None if inp.draft_len is None else torch.from_numpy(inp.draft_len).to(dev),
+                      float(inp.temperature), float(inp.top_p), inp.seed))
+    B, K = sets[0].B, sets[0].K
+    outs = [(torch.empty((B, K + 1), dtype=torch.int32, device=dev), torch.empty((B,), dtype=torch.int32, device=dev))
+            for _ in range(N_SETS)]
+    logical = sets[0].logical_bytes()
+    positions = sets[0].positions()
+    assert all(s.logical_bytes() == logical and s.positions() == positions for s in sets)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        t, d, x, dl, T, tp, seed = dsets[i % N_SETS]
+        o = outs[i % N_SETS]
+        binding.verify(t, d, x, dl, T, tp, seed, stream=stream, out_tokens=o[0],
+                       out_n_accepted=o[1])
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region 1: whole calls
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_total = ev0.elapsed_time(ev1)
+    ms_step = ms_total / args.steps
+    print(f"[bench] {args.steps} steps: {ms_step * 1e3:.2f} us/step", file=sys.stderr, flush=True)
+
+    # timed region 2: per-kernel HIP events recorded by the library on the
+    # launch stream around every kernel
+    binding.profile_read()
+    binding.profile_enable(True)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    binding.profile_enable(False)
+    prof = binding.profile_read()
+    stats_ms, stats_n = prof["stats"]
+    res_ms, res_n = prof["resample"]
+    stats_avg_s = stats_ms / 1e3 / max(stats_n, 1)
+    achieved = logical / stats_avg_s / 1e9
+    print(f"[bench] stats kernel {stats_ms / max(stats_n, 1) * 1e3:.2f} us, resample "
+          f"{res_ms / max(res_n, 1) * 1e3:.2f} us ({stats_n} launches)", file=sys.stderr, flush=True)
+
+    traffic = stored_traffic()
+    roofline = {
+        "bound": "hbm",
+        "achieved": round(achieved, 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": traffic,
+        "kernel": "k_stats (statistics pass)",
+        "kernel_us": round(stats_avg_s * 1e6, 3),
+        "algorithmic_bytes_per_launch": logical,
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(sets, args.cpu_rows)
+
+    value = positions / (ms_step / 1e3)
+    line = {
+        "metric": "verified draft positions/sec + logits HBM GB/s (% of peak) at B=64,K=5,V=128256",
+        "value": round(value, 1),
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "B": B, "K": K, "V": sets[0].V, "temperature": float(sets[0].temperature), "top_p": 1.0,
+            "logical_bytes_per_step": logical,
+            "positions_per_step": positions,
+            "logits_GBps": round(logical / (ms_step / 1e3) / 1e9, 1),
+            "logits_frac_of_peak": round(logical / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+            "input_sets_rotated": N_SETS,
+            "parallelism": "single GPU",
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -206,6 +206,7 @@ class OracleResult:
     probe_row: np.ndarray     # [B, PROBE_ROW] float64
     min_margin: np.ndarray    # [B] smallest decision margin in the row
     n_decisions: np.ndarray   # [B] decisions taken in the row
+    n_flagged: np.ndarray     # [B] decisions with margin below FLAG_BAND
     rows: np.ndarray          # the rows computed
 
     @property
@@ -247,6 +248,7 @@ def verify(target, draft, draft_tokens, draft_len, temperature, top_p, seed, row
     probe_row = np.full((B, PROBE_ROW), np.nan)
     min_margin = np.full(B, np.inf)
     n_dec = np.zeros(B, dtype=np.int64)
+    n_flag = np.zeros(B, dtype=np.int64)
 
     for b in rows:
         L = int(lens[b])
@@ -290,4 +292,5 @@ def verify(target, draft, draft_tokens, draft_len, temperature, top_p, seed, row
         all_m = extra + d.margins
         n_dec[b] = len(all_m)
         min_margin[b] = min(m for _, _, m in all_m)
-    return OracleResult(tokens, n_acc, probe_pos, probe_row, min_margin, n_dec, rows)
+        n_flag[b] = sum(1 for _, _, m in all_m if m < FLAG_BAND)
+    return OracleResult(tokens, n_acc, probe_pos, probe_row, min_margin, n_dec, n_flag, rows)

@@ -1,0 +1,311 @@
+// Host side of the specverify C ABI: argument checks, scratch management,
+// kernel dispatch and optional per-kernel timing.  The operation itself is
+// described in include/specverify.h.
+
+#include <cfloat>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "../../include/specverify.h"
+#include "sv_internal.h"
+
+namespace {
+
+using sv::Params;
+
+struct Scratch {
+    void* ptr = nullptr;
+    size_t bytes = 0;
+};
+
+struct Layout {
+    size_t part, rv, rowp, cmass, row_cnt, res_cnt, total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+Layout layout(int64_t B, int nslot, int nch, int nch2) {
+    Layout L;
+    size_t off = 0;
+    L.row_cnt = off;
+    off = align256(off + static_cast<size_t>(B) * sv::kCounterStride * 4);
+    L.res_cnt = off;
+    off = align256(off + static_cast<size_t>(B) * sv::kCounterStride * 4);
+    L.part = off;
+    off = align256(off + static_cast<size_t>(B) * nslot * nch * sizeof(sv::Partial));
+    L.rv = off;
+    off = align256(off + static_cast<size_t>(B) * nslot * sizeof(sv::RvState));
+    L.rowp = off;
+    off = align256(off + static_cast<size_t>(B) * sizeof(sv::RowParam));
+    L.cmass = off;
+    off = align256(off + static_cast<size_t>(B) * nch2 * 2 * sizeof(double));
+    L.total = off;
+    return L;
+}
+
+std::mutex g_mu;
+std::map<std::pair<int, hipStream_t>, Scratch> g_scratch;
+thread_local std::string g_hip_msg;
+
+struct EvPair {
+    hipEvent_t a, b;
+    int kind;
+};
+bool g_prof = false;
+std::vector<EvPair> g_events;
+
+int hip_fail(hipError_t e, const char* what) {
+    g_hip_msg = std::string(what) + ": " + hipGetErrorString(e);
+    return SV_EHIP;
+}
+
+int env_int(const char* name, int dflt) {
+    const char* s = std::getenv(name);
+    if (!s || !*s) return dflt;
+    return std::atoi(s);
+}
+
+bool misaligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) != 0; }
+
+int check_logits(const sv_logits* t) {
+    if (!t || !t->data) return SV_EINVAL;
+    if (t->dtype != SV_F32 && t->dtype != SV_BF16) return SV_EDTYPE;
+    if (t->stride_b < 0 || t->stride_p < 0) return SV_EINVAL;
+    if (misaligned(t->data, t->dtype == SV_BF16 ? 2 : 4)) return SV_EALIGN;
+    return SV_OK;
+}
+
+// Returns the scratch for (device, stream), growing it when needed.  Counters
+// are zeroed on allocation; kernels leave them at zero after every call.
+int get_scratch(hipStream_t stream, size_t bytes, void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lk(g_mu);
+    Scratch& s = g_scratch[{dev, stream}];
+    if (s.bytes < bytes) {
+        if (s.ptr) {
+            e = hipStreamSynchronize(stream);
+            if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+            (void)hipFree(s.ptr);
+            s.ptr = nullptr;
+            s.bytes = 0;
+        }
+        void* p = nullptr;
+        const size_t want = bytes + bytes / 4;
+        e = hipMalloc(&p, want);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return SV_ENOMEM;
+        }
+        e = hipMemsetAsync(p, 0, want, stream);
+        if (e != hipSuccess) {
+            (void)hipFree(p);
+            return hip_fail(e, "hipMemsetAsync");
+        }
+        s.ptr = p;
+        s.bytes = want;
+    }
+    *out = s.ptr;
+    return SV_OK;
+}
+
+template <typename F>
+int timed_launch(int kind, hipStream_t stream, F&& launch) {
+    EvPair ev{nullptr, nullptr, kind};
+    if (g_prof) {
+        if (hipEventCreate(&ev.a) != hipSuccess || hipEventCreate(&ev.b) != hipSuccess)
+            return hip_fail(hipGetLastError(), "hipEventCreate");
+        (void)hipEventRecord(ev.a, stream);
+    }
+    const hipError_t e = launch();
+    if (e != hipSuccess) return hip_fail(e, "kernel launch");
+    if (g_prof) {
+        (void)hipEventRecord(ev.b, stream);
+        std::lock_guard<std::mutex> lk(g_mu);
+        g_events.push_back(ev);
+    }
+    return SV_OK;
+}
+
+int verify_impl(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_tokens, const int32_t* draft_len,
+                float temperature, float top_p, uint64_t seed, int32_t* out_tokens, int32_t* out_n,
+                double* probe_pos, double* probe_row, void* stream_v) {
+    int rc = check_logits(tl);
+    if (rc) return rc;
+    rc = check_logits(dl);
+    if (rc) return rc;
+    if (!draft_tokens || !out_tokens || !out_n) return SV_EINVAL;
+    if (misaligned(draft_tokens, 4) || misaligned(out_tokens, 4) || misaligned(out_n, 4) ||
+        (draft_len && misaligned(draft_len, 4)))
+        return SV_EALIGN;
+    if (tl->dtype != dl->dtype) return SV_EDTYPE;
+    const int B = tl->B, V = tl->V, K = tl->P - 1;
+    if (B <= 0 || V <= 0 || K < 1 || K > SPECVERIFY_MAX_K) return SV_ESHAPE;
+    if (dl->B != B || dl->V != V || dl->P != K) return SV_ESHAPE;
+    if (B > (1 << 22) || V > (1 << 24)) return SV_ESHAPE;
+    if (!(temperature > 0.f) || !std::isfinite(temperature)) return SV_EINVAL;
+    if (!(top_p > 0.f && top_p <= 1.f)) return SV_EINVAL;
+    const double c = 1.4426950408889634074 / static_cast<double>(temperature);  // log2(e)/T
+    if (!(c < static_cast<double>(FLT_MAX))) return SV_EINVAL;
+
+    const int dtype = tl->dtype == SV_BF16 ? sv::DT_BF16 : sv::DT_F32;
+    const int E = dtype == sv::DT_BF16 ? 2 : 4;
+    const int nslot = 2 * K + 1;
+    // statistics pass: chunks of at most `cv` 16-byte vectors per workgroup
+    const int64_t nvec_max = (static_cast<int64_t>(V) * E + 15) / 16 + 1;
+    int cv = env_int("SPECVERIFY_STATS_VECS", sv::kThreads * sv::kStatsUnroll);
+    if (cv < 64) cv = 64;
+    const int64_t nch64 = (nvec_max + cv - 1) / cv;
+    const int nch = static_cast<int>(nch64);
+    cv = static_cast<int>((nvec_max + nch - 1) / nch);
+    // resample pass: chunks of ce2 ids (a multiple of one 2048-id tile)
+    const int tile = sv::kThreads * sv::kResTile;
+    int ce2 = env_int("SPECVERIFY_RESAMPLE_IDS", 2 * tile);
+    ce2 = ((ce2 + tile - 1) / tile) * tile;
+    if ((V + ce2 - 1) / ce2 > 1024) ce2 = (((V + 1023) / 1024 + tile - 1) / tile) * tile;
+    const int nch2 = (V + ce2 - 1) / ce2;
+    if (static_cast<int64_t>(B) * nslot * nch >= (1ll << 31)) return SV_ESHAPE;
+
+    hipStream_t stream = static_cast<hipStream_t>(stream_v);
+    const Layout lay = layout(B, nslot, nch, nch2);
+    void* scratch = nullptr;
+    rc = get_scratch(stream, lay.total, &scratch);
+    if (rc) return rc;
+    uint8_t* base = static_cast<uint8_t*>(scratch);
+
+    Params p;
+    std::memset(&p, 0, sizeof(p));
+    p.tgt = static_cast<const uint8_t*>(tl->data);
+    p.dft = static_cast<const uint8_t*>(dl->data);
+    p.tsb = tl->stride_b;
+    p.tsp = tl->stride_p;
+    p.dsb = dl->stride_b;
+    p.dsp = dl->stride_p;
+    p.tokens = draft_tokens;
+    p.dlen = draft_len;
+    p.out_tokens = out_tokens;
+    p.out_n = out_n;
+    p.probe_pos = probe_pos;
+    p.probe_row = probe_row;
+    p.B = B;
+    p.K = K;
+    p.V = V;
+    p.nslot = nslot;
+    p.nch = nch;
+    p.cv = cv;
+    p.nch2 = nch2;
+    p.ce2 = ce2;
+    // c = c_hi + c_lo with c_hi <= c rounded toward zero, so c_lo > 0.
+    float c_hi = static_cast<float>(c);
+    if (static_cast<double>(c_hi) > c) c_hi = std::nextafter(c_hi, 0.f);
+    float c_lo = static_cast<float>(c - static_cast<double>(c_hi));
+    if (!(c_lo >= FLT_MIN)) c_lo = FLT_MIN;
+    p.c_hi = c_hi;
+    p.c_lo = c_lo;
+    p.c64 = static_cast<double>(c_hi) + static_cast<double>(c_lo);
+    p.top_p = top_p;
+    p.key0 = static_cast<uint32_t>(seed & 0xFFFFFFFFull);
+    p.key1 = static_cast<uint32_t>(seed >> 32);
+    p.row_cnt = reinterpret_cast<uint32_t*>(base + lay.row_cnt);
+    p.res_cnt = reinterpret_cast<uint32_t*>(base + lay.res_cnt);
+    p.part = reinterpret_cast<sv::Partial*>(base + lay.part);
+    p.rv = reinterpret_cast<sv::RvState*>(base + lay.rv);
+    p.rowp = reinterpret_cast<sv::RowParam*>(base + lay.rowp);
+    p.cmass = reinterpret_cast<double*>(base + lay.cmass);
+
+    const bool topp = top_p < 1.f;
+    rc = timed_launch(sv::KK_STATS, stream, [&] { return sv::launch_stats(p, dtype, topp, stream); });
+    if (rc) return rc;
+    if (topp) {
+        rc = timed_launch(sv::KK_TOPP, stream, [&] { return sv::launch_topp(p, dtype, stream); });
+        if (rc) return rc;
+    }
+    return timed_launch(sv::KK_RESAMPLE, stream, [&] { return sv::launch_resample(p, dtype, topp, stream); });
+}
+
+}  // namespace
+
+extern "C" {
+
+int spec_verify(const sv_logits* target_logits, const sv_logits* draft_logits, const int32_t* draft_tokens,
+                const int32_t* draft_len, float temperature, float top_p, uint64_t seed, int32_t* out_tokens,
+                int32_t* out_n_accepted, void* stream) {
+    return verify_impl(target_logits, draft_logits, draft_tokens, draft_len, temperature, top_p, seed, out_tokens,
+                       out_n_accepted, nullptr, nullptr, stream);
+}
+
+int spec_verify_probe(const sv_logits* target_logits, const sv_logits* draft_logits, const int32_t* draft_tokens,
+                      const int32_t* draft_len, float temperature, float top_p, uint64_t seed,
+                      int32_t* out_tokens, int32_t* out_n_accepted, double* probe_pos, double* probe_row,
+                      void* stream) {
+    if (!probe_pos || !probe_row) return SV_EINVAL;
+    if (misaligned(probe_pos, 8) || misaligned(probe_row, 8)) return SV_EALIGN;
+    return verify_impl(target_logits, draft_logits, draft_tokens, draft_len, temperature, top_p, seed, out_tokens,
+                       out_n_accepted, probe_pos, probe_row, stream);
+}
+
+const char* spec_verify_strerror(int status) {
+    switch (status) {
+        case SV_OK: return "success";
+        case SV_EINVAL: return "invalid argument (NULL pointer, temperature, top_p or stride)";
+        case SV_ESHAPE: return "invalid shape (B, K, V out of range or target/draft mismatch)";
+        case SV_EDTYPE: return "invalid or mismatched dtype";
+        case SV_EHIP: return g_hip_msg.empty() ? "HIP runtime error" : g_hip_msg.c_str();
+        case SV_ENOMEM: return "scratch allocation failed";
+        case SV_EALIGN: return "pointer not aligned to its element size";
+        default: return "unknown status";
+    }
+}
+
+void spec_verify_release(void) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    for (auto& kv : g_scratch)
+        if (kv.second.ptr) (void)hipFree(kv.second.ptr);
+    g_scratch.clear();
+}
+
+int spec_verify_abi_version(void) { return SPECVERIFY_ABI_VERSION; }
+
+int spec_verify_profile_enable(int enable) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    g_prof = enable != 0;
+    return SV_OK;
+}
+
+int spec_verify_profile_read(double* ms, int64_t* launches, int n) {
+    if (n < 0 || (n > 0 && (!ms || !launches))) return SV_EINVAL;
+    std::vector<EvPair> evs;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        evs.swap(g_events);
+    }
+    const int kinds = n < sv::KK_COUNT ? n : sv::KK_COUNT;
+    for (int k = 0; k < kinds; ++k) {
+        ms[k] = 0.0;
+        launches[k] = 0;
+    }
+    int rc = SV_OK;
+    for (const EvPair& e : evs) {
+        float t = 0.f;
+        hipError_t err = hipEventSynchronize(e.b);
+        if (err == hipSuccess) err = hipEventElapsedTime(&t, e.a, e.b);
+        if (err != hipSuccess) rc = hip_fail(err, "hipEventElapsedTime");
+        if (e.kind < kinds) {
+            ms[e.kind] += t;
+            launches[e.kind] += 1;
+        }
+        (void)hipEventDestroy(e.a);
+        (void)hipEventDestroy(e.b);
+    }
+    return rc == SV_OK ? kinds : rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,163 @@
+// Device helpers for the verify-step kernels: element formats, wave64
+// reductions and scans, the Philox4x32-10 generator, order keys.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sv_internal.h"
+
+namespace sv {
+
+#define SV_INF __builtin_huge_valf()
+
+// ---------------------------------------------------------------------------
+// Element formats.  A logit row is read as aligned 16-byte vectors: 4 fp32
+// or 8 bf16 values.  bf16 widens to fp32 exactly by placing its 16 bits in
+// the high half of the word.
+// ---------------------------------------------------------------------------
+template <int DT> struct Fmt;
+template <> struct Fmt<DT_F32> {
+    static constexpr int E = 4, VE = 4;
+    static constexpr uint32_t NEG_INF_WORD = 0xFF800000u;
+};
+template <> struct Fmt<DT_BF16> {
+    static constexpr int E = 2, VE = 8;
+    static constexpr uint32_t NEG_INF_WORD = 0xFF80FF80u;
+};
+
+template <int DT> __device__ __forceinline__ void unpack(const uint4& v, float* f);
+template <> __device__ __forceinline__ void unpack<DT_F32>(const uint4& v, float* f) {
+    f[0] = __uint_as_float(v.x);
+    f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z);
+    f[3] = __uint_as_float(v.w);
+}
+template <> __device__ __forceinline__ void unpack<DT_BF16>(const uint4& v, float* f) {
+    f[0] = __uint_as_float(v.x << 16);
+    f[1] = __uint_as_float(v.x & 0xFFFF0000u);
+    f[2] = __uint_as_float(v.y << 16);
+    f[3] = __uint_as_float(v.y & 0xFFFF0000u);
+    f[4] = __uint_as_float(v.z << 16);
+    f[5] = __uint_as_float(v.z & 0xFFFF0000u);
+    f[6] = __uint_as_float(v.w << 16);
+    f[7] = __uint_as_float(v.w & 0xFFFF0000u);
+}
+
+template <int DT> __device__ __forceinline__ float load_elem(const uint8_t* row, int64_t i);
+template <> __device__ __forceinline__ float load_elem<DT_F32>(const uint8_t* row, int64_t i) {
+    return reinterpret_cast<const float*>(row)[i];
+}
+template <> __device__ __forceinline__ float load_elem<DT_BF16>(const uint8_t* row, int64_t i) {
+    return __uint_as_float(static_cast<uint32_t>(reinterpret_cast<const uint16_t*>(row)[i]) << 16);
+}
+
+// Loads ids [id0, id0 + nv) of a row into f[0..nv), nv <= 8, by 16-byte
+// vectors when the run is aligned and whole, by elements otherwise.
+template <int DT>
+__device__ __forceinline__ void load8(const uint8_t* row, int64_t id0, int nv, float* f) {
+    constexpr int E = Fmt<DT>::E, VE = Fmt<DT>::VE;
+    const uint8_t* p = row + id0 * E;
+    if (nv == 8 && (reinterpret_cast<uintptr_t>(p) & 15) == 0) {
+        const uint4* vp = reinterpret_cast<const uint4*>(p);
+#pragma unroll
+        for (int k = 0; k < 8 / VE; ++k) unpack<DT>(vp[k], f + k * VE);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) f[i] = (i < nv) ? load_elem<DT>(row, id0 + i) : -SV_INF;
+    }
+}
+
+// Temperature-scaled exponent 2^(l*c - o) with c = c_hi + c_lo.  Both fused
+// multiply-adds are needed to keep c exact to ~2^-48: a float c alone would
+// tilt every distribution by up to 2^-24 relative in the exponent.  c_lo > 0
+// keeps l = -inf at -inf (never -inf + inf).
+__device__ __forceinline__ float tempexp(float l, float c_hi, float c_lo, float o) {
+    return exp2f(fmaf(l, c_lo, fmaf(l, c_hi, -o)));
+}
+
+// Order key of a logit: unsigned compare of keys = numeric compare of values
+// (-0 and +0 share a key).
+__device__ __forceinline__ uint32_t order_key(float l) {
+    uint32_t u = __float_as_uint(l + 0.0f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t k) {
+    uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+    return __uint_as_float(u);
+}
+__device__ __forceinline__ bool is_kept(uint32_t key, int64_t id, uint32_t tau, int32_t cut) {
+    return key > tau || (key == tau && id <= cut);
+}
+
+// ---------------------------------------------------------------------------
+// Wave64 reductions and scans.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+    return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+__device__ __forceinline__ int wave_min_int(int v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
+    return v;
+}
+__device__ __forceinline__ int wave_max_int(int v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = max(v, __shfl_xor(v, o, 64));
+    return v;
+}
+// Inclusive prefix sum over the wave's lanes, fixed order.
+__device__ __forceinline__ double wave_incl_scan(double v, int lane) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        double t = __shfl_up(v, o, 64);
+        if (lane >= o) v += t;
+    }
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon et al., SC'11, section 3.2): per round, 32x32->64
+// products of counter words 0 and 2 with 0xD2511F53 and 0xCD9E8D57; output
+// (hi2 ^ c1 ^ k0, lo2, hi0 ^ c3 ^ k1, lo0); key bumped by the Weyl constants
+// 0x9E3779B9, 0xBB67AE85 between rounds.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r > 0) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const uint32_t hi0 = __umulhi(0xD2511F53u, c.x), lo0 = 0xD2511F53u * c.x;
+        const uint32_t hi2 = __umulhi(0xCD9E8D57u, c.z), lo2 = 0xCD9E8D57u * c.z;
+        c = make_uint4(hi2 ^ c.y ^ k0, lo2, hi0 ^ c.w ^ k1, lo0);
+    }
+    return c;
+}
+// 24-bit uniform in [0, 1 - 2^-24].
+__device__ __forceinline__ double word_uniform(uint32_t w) {
+    return static_cast<double>(w >> 8) * (1.0 / 16777216.0);
+}
+
+// Agent-scope release/acquire around the last-block-done counters: the
+// partial results of a block become visible to whichever block on any XCD
+// observes the final count.
+__device__ __forceinline__ uint32_t counter_arrive(uint32_t* cnt) {
+    return __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+
+}  // namespace sv

@@ -1,0 +1,87 @@
+// Internal structures shared by the host launcher and the gfx950 kernels of
+// the speculative-sampling verify step.  Not part of the public C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+constexpr int kThreads = 256;        // every kernel runs 4 wave64s per workgroup
+constexpr int kWaves = kThreads / 64;
+constexpr int kMaxK = 16;
+constexpr int kMaxSlots = 2 * kMaxK + 1;
+constexpr int kStatsUnroll = 4;      // 16-byte vectors in flight per lane per step
+constexpr int kResTile = 8;          // consecutive ids per lane in the resample pass
+
+enum DType : int { DT_F32 = 0, DT_BF16 = 1 };
+enum RowMode : int { MODE_SKIP = 0, MODE_RESID = 1, MODE_BONUS = 2 };
+enum KernelKind : int { KK_STATS = 0, KK_TOPP = 1, KK_RESAMPLE = 2, KK_COUNT = 3 };
+
+// Statistics of one chunk of one logit row, relative to an integer offset o:
+// s = sum over the chunk of 2^(l*c - o), c = log2(e)/T; m = max logit.
+struct Partial {
+    float o;
+    float m;
+    double s;
+};
+
+// Result of the statistics pass (and, with top-p, of the nucleus selection)
+// for one logit row.  kept is the mass of the kept tokens in the same units
+// as s (kept == s when the filter is off).  A token with order key k and id i
+// is kept iff k > tau, or k == tau and i <= cut.
+struct RvState {
+    float o;
+    float m;
+    double s;
+    double kept;
+    uint32_t tau;
+    int32_t cut;
+    int32_t valid;
+    int32_t pad;
+};
+
+// What the resample pass needs for one batch row.
+struct RowParam {
+    int32_t mode;
+    int32_t n;
+    float oT, oD;
+    double keptT, keptD;
+    uint32_t tauT, tauD;
+    int32_t cutT, cutD;
+    double u;
+};
+
+struct Params {
+    const uint8_t* tgt;
+    const uint8_t* dft;
+    int64_t tsb, tsp, dsb, dsp;   // strides in elements
+    const int32_t* tokens;        // [B, K]
+    const int32_t* dlen;          // [B] or null
+    int32_t* out_tokens;          // [B, K+1]
+    int32_t* out_n;               // [B]
+    double* probe_pos;            // [B, K+1, 8] or null
+    double* probe_row;            // [B, 4] or null
+    int B, K, V, nslot;
+    int nch, cv;                  // statistics pass: chunks per row, 16-byte vectors per chunk
+    int nch2, ce2;                // resample pass: chunks per row, ids per chunk
+    float c_hi, c_lo;             // c = log2(e)/T = c_hi + c_lo, c_lo > 0
+    double c64;                   // (double)c_hi + (double)c_lo
+    float top_p;
+    uint32_t key0, key1;          // Philox key
+    Partial* part;                // [B, nslot, nch]
+    RvState* rv;                  // [B, nslot]
+    RowParam* rowp;               // [B]
+    double* cmass;                // [B, nch2, 2]: residual (or bonus) mass, target mass
+    uint32_t* row_cnt;            // [B] x 16 words apart
+    uint32_t* res_cnt;            // [B] x 16 words apart
+};
+
+constexpr int kCounterStride = 16;  // counters one 64-byte line apart
+
+// Launchers (defined in sv_kernels.hip).
+hipError_t launch_stats(const Params& p, int dtype, bool topp, hipStream_t s);
+hipError_t launch_topp(const Params& p, int dtype, hipStream_t s);
+hipError_t launch_resample(const Params& p, int dtype, bool topp, hipStream_t s);
+
+}  // namespace sv

@@ -1,0 +1,1014 @@
+// gfx950 kernels of the batched speculative-sampling verify step.
+//
+// Method: page "Speculative Decoding للمحترف: ضاعف سرعة Llama 70B لـ 2.4x بدون
+// فقد token واحد", section "التعريف الرياضي من Leviathan et al." -- acceptance
+// probability alpha(x) = min(1, p_target(x)/p_draft(x)) and corrected
+// distribution p'(x) = max(0, p_target(x) - p_draft(x))/Z; section "المفهوم
+// بالتقريب" -- accept agreed tokens, reject the first disagreeing one;
+// section "كود شغّال على vLLM" -- temperature and top_p.  Bonus token: page
+// "Faster LLM Inference via Sequential Monte Carlo", section 2 (scoring over
+// K+1 positions).  Ragged per-row draft lengths: page "HiSpec: Hierarchical
+// Speculative Decoding for LLMs", section 2 (per-sequence acceptance in a
+// batch).
+//
+// Pipeline (all on one stream, no host synchronisation):
+//   k_stats     one workgroup per (row b, logit row, chunk of V): streams the
+//               chunk once from HBM with 16-byte loads and reduces it to
+//               (offset o, sum 2^(l*c - o), max).  Without top-p the last
+//               workgroup to finish a batch row runs the row epilogue
+//               (combine, gather p(x_j), q(x_j), Philox, accept scan).
+//   k_topp      (top-p only) one workgroup per logit row: exact nucleus cut
+//               (value key tau, tie cut by id, kept mass); the last logit row
+//               of a batch row runs the row epilogue.
+//   k_resample  one workgroup per (row b, chunk of V): residual or bonus mass
+//               of the chunk in float64; the last chunk of a row finds the
+//               chunk holding u*Z and rescans it in id order.
+//
+// Everything that streams V is bandwidth-bound (no dense contraction, so no
+// MFMA).  Rows are independent; the last-block-done counters use agent-scope
+// acquire/release so that partial results written on one XCD are seen by the
+// workgroup that finishes the row on another.
+
+#include "sv_device.h"
+#include "sv_internal.h"
+
+namespace sv {
+
+__device__ __forceinline__ double nan64() { return __builtin_nan(""); }
+
+template <int DT>
+__device__ __forceinline__ const uint8_t* row_ptr(const Params& P, bool tgt, int b, int j) {
+    constexpr int E = Fmt<DT>::E;
+    return tgt ? P.tgt + (static_cast<int64_t>(b) * P.tsb + static_cast<int64_t>(j) * P.tsp) * E
+               : P.dft + (static_cast<int64_t>(b) * P.dsb + static_cast<int64_t>(j) * P.dsp) * E;
+}
+
+__device__ __forceinline__ int row_len(const Params& P, int b, bool& ok) {
+    const int L = P.dlen ? P.dlen[b] : P.K;
+    ok = (L >= 0 && L <= P.K);
+    return ok ? L : 0;
+}
+
+// Geometry of one logit row on the aligned 16-byte grid.
+struct RowGrid {
+    const uint4* vp;   // first aligned vector touching the row
+    int head;          // ids of vector 0 that precede the row
+    int64_t nvec;      // vectors touching the row
+};
+template <int DT>
+__device__ __forceinline__ RowGrid row_grid(const uint8_t* row, int V) {
+    constexpr int E = Fmt<DT>::E;
+    const uintptr_t A = reinterpret_cast<uintptr_t>(row);
+    RowGrid g;
+    g.vp = reinterpret_cast<const uint4*>(A & ~static_cast<uintptr_t>(15));
+    g.head = static_cast<int>((A & 15) / E);
+    g.nvec = (static_cast<int64_t>(A & 15) + static_cast<int64_t>(V) * E + 15) >> 4;
+    return g;
+}
+// Ids of vector k outside [0, V) become -inf (only the first and last vector
+// of a row can hold such ids; reading them is safe because an aligned
+// 16-byte vector never crosses a page).
+template <int DT>
+__device__ __forceinline__ void mask_edge(float* f, int64_t k, int head, int V) {
+    constexpr int VE = Fmt<DT>::VE;
+#pragma unroll
+    for (int i = 0; i < VE; ++i) {
+        const int64_t id = k * VE + i - head;
+        if (id < 0 || id >= V) f[i] = -SV_INF;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Row epilogue: combine, gather, Philox, accept scan, outputs.
+// ---------------------------------------------------------------------------
+struct RowShared {
+    float o[kMaxSlots];
+    float m[kMaxSlots];
+    double s[kMaxSlots];
+    double kept[kMaxSlots];
+    uint32_t tau[kMaxSlots];
+    int32_t cut[kMaxSlots];
+    int32_t valid[kMaxSlots];
+    double px[kMaxK];
+    double qx[kMaxK];
+    int bad;
+    int n;
+    double u_res;
+};
+
+// rv index r of a batch row: target position j -> r = j; draft position j ->
+// r = Le + 1 + j.  Slot in the [B, 2K+1] scratch layout: target j -> j,
+// draft j -> K + 1 + j.
+__device__ __forceinline__ int rv_slot(int r, int Le, int K) { return r <= Le ? r : K + 1 + (r - Le - 1); }
+
+// Combines the chunk partials of logit row `slot` of batch row b (one wave).
+__device__ __forceinline__ void combine_partials(const Params& P, int b, int slot, int lane, float& O, float& M,
+                                                 double& S) {
+    const Partial* pp = P.part + (static_cast<size_t>(b) * P.nslot + slot) * P.nch;
+    O = -SV_INF;
+    M = -SV_INF;
+    for (int c = lane; c < P.nch; c += 64) {
+        O = fmaxf(O, pp[c].o);
+        M = fmaxf(M, pp[c].m);
+    }
+    O = wave_max(O);
+    M = wave_max(M);
+    S = 0.0;
+    for (int c = lane; c < P.nch; c += 64) {
+        const Partial q = pp[c];
+        S += (q.o == -SV_INF) ? q.s : ldexp(q.s, static_cast<int>(fmaxf(q.o - O, -1100.f)));
+    }
+    S = wave_sum(S);
+}
+
+template <int DT, bool TOPP>
+__device__ void row_finish(const Params& P, int b, int Le, bool rowok, RowShared& R) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int K = P.K, K1 = P.K + 1;
+    const int nrv = 2 * Le + 1;
+    if (tid == 0) {
+        int bad = rowok ? 0 : 1;
+        for (int r = 0; r < nrv; ++r) bad |= R.valid[r] ? 0 : 1;
+        R.bad = bad;
+    }
+    __syncthreads();
+    if (tid < 64) {
+        int bad_tok = 0;
+        bool rej = false;
+        double u_res = 0.0;
+        if (!R.bad && lane <= Le) {
+            const uint4 w = philox4x32_10(make_uint4(static_cast<uint32_t>(b), static_cast<uint32_t>(lane), 0u, 0u),
+                                          P.key0, P.key1);
+            u_res = word_uniform(w.y);
+            if (lane < Le) {
+                const int x = P.tokens[static_cast<int64_t>(b) * K + lane];
+                if (x < 0 || x >= P.V) {
+                    bad_tok = 1;
+                } else {
+                    const int rT = lane, rD = Le + 1 + lane;
+                    const float lt = load_elem<DT>(row_ptr<DT>(P, true, b, lane), x);
+                    const float ld = load_elem<DT>(row_ptr<DT>(P, false, b, lane), x);
+                    double pt = exp2(static_cast<double>(lt) * P.c64 - static_cast<double>(R.o[rT])) / R.kept[rT];
+                    double qd = exp2(static_cast<double>(ld) * P.c64 - static_cast<double>(R.o[rD])) / R.kept[rD];
+                    if (TOPP) {
+                        if (!is_kept(order_key(lt), x, R.tau[rT], R.cut[rT])) pt = 0.0;
+                        if (!is_kept(order_key(ld), x, R.tau[rD], R.cut[rD])) qd = 0.0;
+                    }
+                    const double r = qd > 0.0 ? pt / qd : (pt > 0.0 ? static_cast<double>(SV_INF) : 0.0);
+                    rej = !(word_uniform(w.x) < r);
+                    R.px[lane] = pt;
+                    R.qx[lane] = qd;
+                }
+            }
+        }
+        const unsigned long long badm = __ballot(bad_tok);
+        const unsigned long long rejm = __ballot(rej);
+        const int n = rejm ? (__ffsll(static_cast<long long>(rejm)) - 1) : Le;
+        const double un = __shfl(u_res, n, 64);
+        if (lane == 0) {
+            R.bad |= (badm != 0ull) ? 1 : 0;
+            R.n = R.bad ? 0 : n;
+            R.u_res = un;
+        }
+    }
+    __syncthreads();
+    const int bad = R.bad, n = R.n;
+    for (int j = tid; j < K1; j += kThreads) {
+        int v = -1;
+        if (!bad && j < n) v = P.tokens[static_cast<int64_t>(b) * K + j];
+        if (bad || j != n) P.out_tokens[static_cast<int64_t>(b) * K1 + j] = v;
+    }
+    if (tid == 0) {
+        P.out_n[b] = bad ? -1 : n;
+        RowParam rp;
+        rp.mode = bad ? MODE_SKIP : (n < Le ? MODE_RESID : MODE_BONUS);
+        rp.n = n;
+        rp.oT = R.o[n];
+        rp.keptT = R.kept[n];
+        rp.tauT = R.tau[n];
+        rp.cutT = R.cut[n];
+        const int rD = Le + 1 + n;
+        const bool resid = !bad && n < Le;
+        rp.oD = resid ? R.o[rD] : 0.f;
+        rp.keptD = resid ? R.kept[rD] : 1.0;
+        rp.tauD = resid ? R.tau[rD] : 0u;
+        rp.cutD = resid ? R.cut[rD] : -1;
+        rp.u = R.u_res;
+        P.rowp[b] = rp;
+        if (P.probe_row) {
+            double* pr = P.probe_row + static_cast<size_t>(b) * 4;
+            pr[0] = nan64();
+            pr[1] = nan64();
+            pr[2] = bad ? nan64() : R.u_res;
+            pr[3] = bad ? -1.0 : static_cast<double>(n);
+        }
+    }
+    if (P.probe_pos) {
+        double* pp = P.probe_pos + static_cast<size_t>(b) * K1 * 8;
+        for (int idx = tid; idx < K1 * 8; idx += kThreads) {
+            const int j = idx >> 3, f = idx & 7;
+            double v = nan64();
+            if (!bad) {
+                const int rD = Le + 1 + j;
+                switch (f) {
+                    case 0: if (j <= Le) v = R.m[j]; break;
+                    case 1: if (j <= Le) v = R.s[j] * exp2(static_cast<double>(R.o[j]) - static_cast<double>(R.m[j]) * P.c64); break;
+                    case 2: if (j < Le) v = R.m[rD]; break;
+                    case 3: if (j < Le) v = R.s[rD] * exp2(static_cast<double>(R.o[rD]) - static_cast<double>(R.m[rD]) * P.c64); break;
+                    case 4: if (j < Le) v = R.px[j]; break;
+                    case 5: if (j < Le) v = R.qx[j]; break;
+                    case 6: if (j <= Le) v = R.kept[j] / R.s[j]; break;
+                    default: if (j < Le) v = R.kept[rD] / R.s[rD]; break;
+                }
+            }
+            pp[idx] = v;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Statistics pass.
+// ---------------------------------------------------------------------------
+template <int DT, int U>
+__device__ __forceinline__ void stats_chunk(const uint8_t* row, int V, int64_t k0, int64_t k1, float c_hi,
+                                            float c_lo, float& m_run, float& o_run, float& s_run) {
+    constexpr int VE = Fmt<DT>::VE;
+    const RowGrid g = row_grid<DT>(row, V);
+    for (int64_t kb = k0; kb < k1; kb += static_cast<int64_t>(kThreads) * U) {
+        uint4 raw[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t k = kb + u * kThreads + threadIdx.x;
+            const uint32_t ni = Fmt<DT>::NEG_INF_WORD;
+            raw[u] = (k < k1) ? g.vp[k] : make_uint4(ni, ni, ni, ni);
+        }
+        float f[U * VE];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            unpack<DT>(raw[u], f + u * VE);
+            const int64_t k = kb + u * kThreads + threadIdx.x;
+            if (k < k1 && (k == 0 || k == g.nvec - 1)) mask_edge<DT>(f + u * VE, k, g.head, V);
+        }
+        float bm = -SV_INF;
+#pragma unroll
+        for (int i = 0; i < U * VE; ++i) bm = fmaxf(bm, f[i]);
+        m_run = fmaxf(m_run, bm);
+        const float ob = ceilf(bm * c_hi);
+        if (ob > o_run) {
+            if (o_run != -SV_INF) s_run = ldexpf(s_run, static_cast<int>(fmaxf(o_run - ob, -256.f)));
+            o_run = ob;
+        }
+        const float off = (o_run == -SV_INF) ? 0.f : o_run;
+        float acc[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float a = 0.f;
+#pragma unroll
+            for (int i = 0; i < VE; ++i) a += tempexp(f[u * VE + i], c_hi, c_lo, off);
+            acc[u] = a;
+        }
+        float t = 0.f;
+#pragma unroll
+        for (int u = 0; u < U; ++u) t += acc[u];
+        s_run += t;
+    }
+}
+
+template <int DT, bool TOPP>
+__global__ __launch_bounds__(kThreads) void k_stats(Params P) {
+    __shared__ float sh_o[kWaves], sh_s[kWaves], sh_m[kWaves];
+    __shared__ int s_last;
+    __shared__ RowShared R;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int item = blockIdx.x;
+    const int rvi = item / P.nch;
+    const int chunk = item - rvi * P.nch;
+    const int b = rvi / P.nslot;
+    const int slot = rvi - b * P.nslot;
+    bool rowok;
+    const int Le = row_len(P, b, rowok);
+    const bool tgt = slot <= P.K;
+    const int j = tgt ? slot : slot - P.K - 1;
+    if (tgt ? (j > Le) : (j >= Le)) return;  // padded position: never read
+
+    const uint8_t* row = row_ptr<DT>(P, tgt, b, j);
+    const RowGrid g = row_grid<DT>(row, P.V);
+    const int64_t k0 = static_cast<int64_t>(chunk) * P.cv;
+    const int64_t k1 = k0 + P.cv < g.nvec ? k0 + P.cv : g.nvec;
+    float m_run = -SV_INF, o_run = -SV_INF, s_run = 0.f;
+    stats_chunk<DT, kStatsUnroll>(row, P.V, k0, k1, P.c_hi, P.c_lo, m_run, o_run, s_run);
+
+    // Workgroup combine: exact power-of-two rescaling to the largest offset.
+    const float Ow = wave_max(o_run);
+    const float sc = (o_run == -SV_INF) ? s_run : ldexpf(s_run, static_cast<int>(fmaxf(o_run - Ow, -256.f)));
+    const float Sw = wave_sum(sc);
+    const float Mw = wave_max(m_run);
+    if (lane == 0) {
+        sh_o[wv] = Ow;
+        sh_s[wv] = Sw;
+        sh_m[wv] = Mw;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        float O = sh_o[0], M = sh_m[0];
+        for (int w = 1; w < kWaves; ++w) {
+            O = fmaxf(O, sh_o[w]);
+            M = fmaxf(M, sh_m[w]);
+        }
+        double S = 0.0;
+        for (int w = 0; w < kWaves; ++w)
+            S += (sh_o[w] == -SV_INF) ? static_cast<double>(sh_s[w])
+                                      : ldexp(static_cast<double>(sh_s[w]), static_cast<int>(fmaxf(sh_o[w] - O, -1100.f)));
+        Partial pr;
+        pr.o = O;
+        pr.m = M;
+        pr.s = S;
+        P.part[static_cast<size_t>(rvi) * P.nch + chunk] = pr;
+        if (!TOPP) {
+            const uint32_t need = static_cast<uint32_t>((2 * Le + 1) * P.nch);
+            s_last = (counter_arrive(&P.row_cnt[static_cast<size_t>(b) * kCounterStride]) + 1u == need) ? 1 : 0;
+        }
+    }
+    if (TOPP) return;
+    __syncthreads();
+    if (!s_last) return;
+    acquire_agent();
+    if (tid == 0) P.row_cnt[static_cast<size_t>(b) * kCounterStride] = 0u;
+    const int nrv = 2 * Le + 1;
+    for (int r = wv; r < nrv; r += kWaves) {
+        float O, M;
+        double S;
+        combine_partials(P, b, rv_slot(r, Le, P.K), lane, O, M, S);
+        if (lane == 0) {
+            R.o[r] = O;
+            R.m[r] = M;
+            R.s[r] = S;
+            R.kept[r] = S;
+            R.tau[r] = 0u;
+            R.cut[r] = -1;
+            R.valid[r] = (S > 0.0 && S < static_cast<double>(SV_INF)) ? 1 : 0;
+        }
+    }
+    __syncthreads();
+    row_finish<DT, false>(P, b, Le, rowok, R);
+}
+
+// ---------------------------------------------------------------------------
+// Block-wide helpers for the selection and resample passes.
+// ---------------------------------------------------------------------------
+// Inclusive/exclusive prefix sums over the workgroup's threads in thread
+// order (float64), plus the total.  Every thread must call it.
+__device__ __forceinline__ void block_scan(double x, double& incl, double& excl, double& total) {
+    __shared__ double ws[kWaves];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const double wi = wave_incl_scan(x, lane);
+    double we = __shfl_up(wi, 1, 64);
+    if (lane == 0) we = 0.0;
+    if (lane == 63) ws[wv] = wi;
+    __syncthreads();
+    double off = 0.0;
+    for (int k = 0; k < wv; ++k) off += ws[k];
+    double tot = 0.0;
+    for (int k = 0; k < kWaves; ++k) tot += ws[k];
+    incl = off + wi;
+    excl = off + we;
+    total = tot;
+    __syncthreads();
+}
+__device__ __forceinline__ int block_min_int(int v) {
+    __shared__ int ws[kWaves];
+    v = wave_min_int(v);
+    if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = v;
+    __syncthreads();
+    int r = ws[0];
+    for (int k = 1; k < kWaves; ++k) r = min(r, ws[k]);
+    __syncthreads();
+    return r;
+}
+__device__ __forceinline__ int block_max_int(int v) {
+    __shared__ int ws[kWaves];
+    v = wave_max_int(v);
+    if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = v;
+    __syncthreads();
+    int r = ws[0];
+    for (int k = 1; k < kWaves; ++k) r = max(r, ws[k]);
+    __syncthreads();
+    return r;
+}
+__device__ __forceinline__ int block_sum_int(int v) {
+    __shared__ int ws[kWaves];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = v;
+    __syncthreads();
+    int r = 0;
+    for (int k = 0; k < kWaves; ++k) r += ws[k];
+    __syncthreads();
+    return r;
+}
+
+// ---------------------------------------------------------------------------
+// Nucleus selection (top-p), one workgroup per logit row.
+//
+// The kept set is the shortest prefix of the tokens sorted by probability,
+// descending, ties by lower id, whose mass reaches top_p * S (section "كود
+// شغّال على vLLM" names top_p; the sorting definition is the reading taken).
+// Because p is increasing in the logit, the cut is found on logit order keys:
+//   pass A  histogram of the gap below the row's offset in 1/64-bit bins over
+//           16 bits (mass, count, min and max key per bin); the crossing bin
+//           holds the cut.  Bins are a monotone function of the logit, so a
+//           bin is a key interval;
+//   then    while the interval holds several keys: if at most kCollect tokens,
+//           collect them, sort by (key desc, id asc) and walk the running
+//           mass; else split the interval by the next 8 key bits (radix
+//           pass).  A single key is a tie group: keep the r lowest ids,
+//           found by an id-ordered counting pass.
+// ---------------------------------------------------------------------------
+constexpr int kGapBins = 1024;          // 16 bits of gap at 64 bins per bit
+constexpr float kGapPerBit = 64.f;
+constexpr int kCollect = 2048;
+
+struct SelShared {
+    double mass[kGapBins];
+    uint32_t cnt[kGapBins];
+    uint32_t kmin[kGapBins];
+    uint32_t kmax[kGapBins];
+    unsigned long long list[kCollect];
+    uint32_t nlist;
+    int sel_bin;
+    double sel_pre;
+    uint32_t r_klo, r_khi, r_cnt;
+    double r_A;
+    int r_cut;
+    int r_keepall;
+};
+
+template <int DT, typename F>
+__device__ __forceinline__ void for_each_vec(const uint8_t* row, int V, F&& fn) {
+    constexpr int VE = Fmt<DT>::VE;
+    const RowGrid g = row_grid<DT>(row, V);
+    for (int64_t k = threadIdx.x; k < g.nvec; k += kThreads) {
+        float f[VE];
+        unpack<DT>(g.vp[k], f);
+        if (k == 0 || k == g.nvec - 1) mask_edge<DT>(f, k, g.head, V);
+#pragma unroll
+        for (int i = 0; i < VE; ++i) fn(f[i], k * VE + i - g.head);
+    }
+}
+
+template <int DT>
+__device__ void select_nucleus(const Params& P, const uint8_t* row, float O, double S, SelShared& sh, double& kept,
+                               uint32_t& tau, int32_t& cut) {
+    const int tid = threadIdx.x;
+    const int V = P.V;
+    const float c_hi = P.c_hi, c_lo = P.c_lo;
+    const double Tm = static_cast<double>(P.top_p) * S;
+
+    for (int i = tid; i < kGapBins; i += kThreads) {
+        sh.mass[i] = 0.0;
+        sh.cnt[i] = 0u;
+        sh.kmin[i] = 0xFFFFFFFFu;
+        sh.kmax[i] = 0u;
+    }
+    if (tid == 0) sh.r_keepall = 0;
+    __syncthreads();
+    // Pass A: gap histogram.
+    for_each_vec<DT>(row, V, [&](float l, int64_t id) {
+        const float a = fmaf(l, c_lo, fmaf(l, c_hi, -O));
+        if (a > -16.f && id >= 0 && id < V) {
+            const float e = exp2f(a);
+            const int bin = max(0, static_cast<int>(floorf(-a * kGapPerBit)));
+            const uint32_t key = order_key(l);
+            atomicAdd(&sh.mass[bin], static_cast<double>(e));
+            atomicAdd(&sh.cnt[bin], 1u);
+            atomicMin(&sh.kmin[bin], key);
+            atomicMax(&sh.kmax[bin], key);
+        }
+    });
+    __syncthreads();
+    // Crossing bin: the smallest bin whose running mass from bin 0 reaches Tm.
+    {
+        constexpr int PER = kGapBins / kThreads;
+        double tsum = 0.0;
+        for (int i = 0; i < PER; ++i) tsum += sh.mass[tid * PER + i];
+        double incl, excl, total;
+        block_scan(tsum, incl, excl, total);
+        int found = 0x7FFFFFFF;
+        double pre = excl, fpre = 0.0;
+        for (int i = 0; i < PER; ++i) {
+            const int bin = tid * PER + i;
+            const double m = sh.mass[bin];
+            if (found == 0x7FFFFFFF && sh.cnt[bin] > 0 && pre + m >= Tm) {
+                found = bin;
+                fpre = pre;
+            }
+            pre += m;
+        }
+        const int fb = block_min_int(found);
+        if (found == fb && fb != 0x7FFFFFFF) {
+            sh.sel_bin = fb;
+            sh.sel_pre = fpre;
+        }
+        // smallest key among non-empty bins, for the overflow case
+        if (tid == 0 && fb == 0x7FFFFFFF) {
+            uint32_t kf = 0xFFFFFFFFu;
+            bool any = false;
+            for (int i = 0; i < kGapBins; ++i)
+                if (sh.cnt[i]) {
+                    kf = min(kf, sh.kmin[i]);
+                    any = true;
+                }
+            sh.sel_bin = kGapBins;
+            sh.sel_pre = total;
+            sh.r_klo = 0u;
+            sh.r_khi = any ? kf - 1u : 0xFFFFFFFFu;
+            sh.r_cnt = 0xFFFFFFFFu;  // unknown: forces a radix pass
+        }
+        __syncthreads();
+        if (tid == 0 && sh.sel_bin < kGapBins) {
+            const int sb = sh.sel_bin;
+            sh.r_klo = sh.kmin[sb];
+            sh.r_khi = sh.kmax[sb];
+            sh.r_cnt = sh.cnt[sb];
+        }
+        if (tid == 0) sh.r_A = sh.sel_pre;
+        __syncthreads();
+    }
+    // Refinement.
+    for (;;) {
+        const uint32_t klo = sh.r_klo, khi = sh.r_khi, rc = sh.r_cnt;
+        const double A = sh.r_A;
+        if (sh.r_keepall) {
+            // no interval reaches top_p * S (rounding with top_p near 1):
+            // every token is kept, as when no running sum reaches top_p
+            tau = 0u;
+            cut = 0x7FFFFFFF;
+            kept = S;
+            return;
+        }
+        if (klo == khi) {
+            // one key: a tie group of rc tokens of equal mass e
+            const float e = tempexp(key_value(klo), c_hi, c_lo, O);
+            const double need = (Tm - A) / static_cast<double>(e);
+            double rr = ceil(need);
+            if (!(rr >= 1.0)) rr = 1.0;
+            if (rr > static_cast<double>(rc)) rr = static_cast<double>(rc);
+            const uint32_t r = static_cast<uint32_t>(rr);
+            tau = klo;
+            kept = A + static_cast<double>(r) * static_cast<double>(e);
+            if (r >= rc) {
+                cut = 0x7FFFFFFF;
+                return;
+            }
+            // id of the r-th tied token in id order
+            int carry = 0;
+            if (tid == 0) sh.r_cut = -1;
+            __syncthreads();
+            for (int64_t t0 = 0; t0 < V; t0 += static_cast<int64_t>(kThreads) * kResTile) {
+                const int64_t id0 = t0 + static_cast<int64_t>(tid) * kResTile;
+                const int nv = static_cast<int>(min<int64_t>(max<int64_t>(V - id0, 0), kResTile));
+                float f[kResTile];
+                if (nv > 0) load8<DT>(row, id0, nv, f);
+                int cntl = 0;
+                for (int i = 0; i < nv; ++i) cntl += order_key(f[i]) == klo;
+                // exclusive prefix count of ties over threads
+                double ie, ee, te;
+                block_scan(static_cast<double>(cntl), ie, ee, te);
+                const int ex = carry + static_cast<int>(ee);
+                if (cntl > 0 && ex < static_cast<int>(r) && ex + cntl >= static_cast<int>(r)) {
+                    int c2 = ex;
+                    for (int i = 0; i < nv; ++i)
+                        if (order_key(f[i]) == klo && ++c2 == static_cast<int>(r)) {
+                            sh.r_cut = static_cast<int>(id0 + i);
+                            break;
+                        }
+                }
+                __syncthreads();
+                carry += static_cast<int>(te);
+                if (sh.r_cut >= 0) break;
+            }
+            cut = sh.r_cut;
+            return;
+        }
+        if (rc <= static_cast<uint32_t>(kCollect)) {
+            // collect, sort by (key desc, id asc), walk the running mass
+            if (tid == 0) sh.nlist = 0u;
+            __syncthreads();
+            for_each_vec<DT>(row, V, [&](float l, int64_t id) {
+                if (id >= 0 && id < V) {
+                    const uint32_t key = order_key(l);
+                    if (key >= klo && key <= khi) {
+                        const uint32_t at = atomicAdd(&sh.nlist, 1u);
+                        if (at < static_cast<uint32_t>(kCollect))
+                            sh.list[at] = (static_cast<unsigned long long>(~key) << 32) | static_cast<uint32_t>(id);
+                    }
+                }
+            });
+            __syncthreads();
+            const int n = static_cast<int>(min(sh.nlist, static_cast<uint32_t>(kCollect)));
+            int np2 = 1;
+            while (np2 < n) np2 <<= 1;
+            for (int i = n + tid; i < np2; i += kThreads) sh.list[i] = ~0ull;
+            __syncthreads();
+            // bitonic sort, ascending
+            for (int kk = 2; kk <= np2; kk <<= 1) {
+                for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+                    for (int i = tid; i < np2; i += kThreads) {
+                        const int ij = i ^ jj;
+                        if (ij > i) {
+                            const unsigned long long a = sh.list[i], c = sh.list[ij];
+                            const bool up = (i & kk) == 0;
+                            if ((a > c) == up) {
+                                sh.list[i] = c;
+                                sh.list[ij] = a;
+                            }
+                        }
+                    }
+                    __syncthreads();
+                }
+            }
+            // running mass in sorted order: each thread a run of 8, then a scan
+            const int per = (n + kThreads - 1) / kThreads;
+            const int s0 = tid * per, s1 = min(s0 + per, n);
+            double ts = 0.0;
+            for (int i = s0; i < s1; ++i)
+                ts += static_cast<double>(tempexp(key_value(~static_cast<uint32_t>(sh.list[i] >> 32)), c_hi, c_lo, O));
+            double incl, excl, total;
+            block_scan(ts, incl, excl, total);
+            int found = 0x7FFFFFFF;
+            double fk = 0.0;
+            double run = A + excl;
+            for (int i = s0; i < s1; ++i) {
+                run += static_cast<double>(tempexp(key_value(~static_cast<uint32_t>(sh.list[i] >> 32)), c_hi, c_lo, O));
+                if (run >= Tm) {
+                    found = i;
+                    fk = run;
+                    break;
+                }
+            }
+            const int fi = block_min_int(found);
+            if (fi == 0x7FFFFFFF) {
+                // rounding: no running sum reached Tm; keep the whole interval
+                if (tid == 0) {
+                    sh.r_A = A + total;
+                    sh.r_cut = n - 1;
+                }
+            } else if (found == fi) {
+                sh.r_A = fk;
+                sh.r_cut = fi;
+            }
+            __syncthreads();
+            const int at = sh.r_cut;
+            const unsigned long long e = sh.list[at < 0 ? 0 : at];
+            tau = ~static_cast<uint32_t>(e >> 32);
+            cut = static_cast<int32_t>(static_cast<uint32_t>(e));
+            kept = sh.r_A;
+            return;
+        }
+        // radix pass: split [klo, khi] by the next 8 bits
+        const uint32_t span = khi - klo;
+        const int shift = max(0, 32 - __clz(span) - 8);
+        for (int i = tid; i < 256; i += kThreads) {
+            sh.mass[i] = 0.0;
+            sh.cnt[i] = 0u;
+            sh.kmin[i] = 0xFFFFFFFFu;
+            sh.kmax[i] = 0u;
+        }
+        __syncthreads();
+        for_each_vec<DT>(row, V, [&](float l, int64_t id) {
+            if (id >= 0 && id < V) {
+                const uint32_t key = order_key(l);
+                if (key >= klo && key <= khi) {
+                    const int sb = static_cast<int>((key - klo) >> shift);
+                    atomicAdd(&sh.mass[sb], static_cast<double>(tempexp(l, c_hi, c_lo, O)));
+                    atomicAdd(&sh.cnt[sb], 1u);
+                    atomicMin(&sh.kmin[sb], key);
+                    atomicMax(&sh.kmax[sb], key);
+                }
+            }
+        });
+        __syncthreads();
+        if (tid == 0) {
+            double pre = A;
+            int pick = -1, lowest = -1;
+            double pick_pre = A, low_pre = A;
+            for (int sb = 255; sb >= 0; --sb) {
+                if (!sh.cnt[sb]) continue;
+                lowest = sb;
+                low_pre = pre;
+                if (pre + sh.mass[sb] >= Tm) {
+                    pick = sb;
+                    pick_pre = pre;
+                    break;
+                }
+                pre += sh.mass[sb];
+            }
+            if (pick < 0) {
+                pick = lowest;
+                pick_pre = low_pre;
+            }
+            if (pick < 0) {
+                sh.r_keepall = 1;
+            } else {
+                sh.r_klo = sh.kmin[pick];
+                sh.r_khi = sh.kmax[pick];
+                sh.r_cnt = sh.cnt[pick];
+                sh.r_A = pick_pre;
+            }
+        }
+        __syncthreads();
+    }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_topp(Params P) {
+    __shared__ SelShared sh;
+    __shared__ RowShared R;
+    __shared__ float s_o, s_m;
+    __shared__ double s_s;
+    __shared__ int s_last;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int rvi = blockIdx.x;
+    const int b = rvi / P.nslot;
+    const int slot = rvi - b * P.nslot;
+    bool rowok;
+    const int Le = row_len(P, b, rowok);
+    const bool tgt = slot <= P.K;
+    const int j = tgt ? slot : slot - P.K - 1;
+    if (tgt ? (j > Le) : (j >= Le)) return;
+    const uint8_t* row = row_ptr<DT>(P, tgt, b, j);
+    if (wv == 0) {
+        float O, M;
+        double S;
+        combine_partials(P, b, slot, lane, O, M, S);
+        if (lane == 0) {
+            s_o = O;
+            s_m = M;
+            s_s = S;
+        }
+    }
+    __syncthreads();
+    const float O = s_o;
+    const double S = s_s;
+    RvState st;
+    st.o = O;
+    st.m = s_m;
+    st.s = S;
+    st.kept = S;
+    st.tau = 0u;
+    st.cut = -1;
+    st.valid = (S > 0.0 && S < static_cast<double>(SV_INF)) ? 1 : 0;
+    st.pad = 0;
+    if (st.valid) {
+        double kept;
+        uint32_t tau;
+        int32_t cut;
+        select_nucleus<DT>(P, row, O, S, sh, kept, tau, cut);
+        st.kept = kept;
+        st.tau = tau;
+        st.cut = cut;
+    }
+    if (tid == 0) {
+        P.rv[rvi] = st;
+        s_last = (counter_arrive(&P.row_cnt[static_cast<size_t>(b) * kCounterStride]) + 1u ==
+                  static_cast<uint32_t>(2 * Le + 1))
+                     ? 1
+                     : 0;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    acquire_agent();
+    if (tid == 0) P.row_cnt[static_cast<size_t>(b) * kCounterStride] = 0u;
+    const int nrv = 2 * Le + 1;
+    for (int r = tid; r < nrv; r += kThreads) {
+        const RvState q = P.rv[static_cast<size_t>(b) * P.nslot + rv_slot(r, Le, P.K)];
+        R.o[r] = q.o;
+        R.m[r] = q.m;
+        R.s[r] = q.s;
+        R.kept[r] = q.kept;
+        R.tau[r] = q.tau;
+        R.cut[r] = q.cut;
+        R.valid[r] = q.valid;
+    }
+    __syncthreads();
+    row_finish<DT, true>(P, b, Le, rowok, R);
+}
+
+// ---------------------------------------------------------------------------
+// Resample pass.
+// ---------------------------------------------------------------------------
+template <int DT, bool TOPP>
+__device__ __forceinline__ void eval_run(const uint8_t* rowT, const uint8_t* rowD, bool resid, int64_t id0, int nv,
+                                         const RowParam& rp, float c_hi, float c_lo, float invT, float invD, float* w,
+                                         float* p) {
+    float lt[kResTile], ld[kResTile];
+    load8<DT>(rowT, id0, nv, lt);
+    if (resid) load8<DT>(rowD, id0, nv, ld);
+#pragma unroll
+    for (int i = 0; i < kResTile; ++i) {
+        float pt = tempexp(lt[i], c_hi, c_lo, rp.oT) * invT;
+        if (TOPP && !is_kept(order_key(lt[i]), id0 + i, rp.tauT, rp.cutT)) pt = 0.f;
+        float wi = pt;
+        if (resid) {
+            float qd = tempexp(ld[i], c_hi, c_lo, rp.oD) * invD;
+            if (TOPP && !is_kept(order_key(ld[i]), id0 + i, rp.tauD, rp.cutD)) qd = 0.f;
+            wi = fmaxf(pt - qd, 0.f);
+        }
+        if (i >= nv) {
+            pt = 0.f;
+            wi = 0.f;
+        }
+        w[i] = wi;
+        p[i] = pt;
+    }
+}
+
+template <int DT, bool TOPP>
+__global__ __launch_bounds__(kThreads) void k_resample(Params P) {
+    __shared__ double sh_w[kWaves], sh_p[kWaves];
+    __shared__ int s_last, s_sel, s_chunk, s_y;
+    __shared__ double s_t, s_Z, s_pre;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int b = blockIdx.x / P.nch2;
+    const int c = blockIdx.x - b * P.nch2;
+    const RowParam rp = P.rowp[b];
+    if (rp.mode == MODE_SKIP) return;
+    const bool resid = rp.mode == MODE_RESID;
+    const uint8_t* rowT = row_ptr<DT>(P, true, b, rp.n);
+    const uint8_t* rowD = resid ? row_ptr<DT>(P, false, b, rp.n) : nullptr;
+    const float invT = static_cast<float>(1.0 / rp.keptT);
+    const float invD = resid ? static_cast<float>(1.0 / rp.keptD) : 0.f;
+    const int64_t i0 = static_cast<int64_t>(c) * P.ce2;
+    const int64_t i1 = min<int64_t>(i0 + P.ce2, P.V);
+    const int64_t tile = static_cast<int64_t>(kThreads) * kResTile;
+
+    double aw = 0.0, ap = 0.0;
+    for (int64_t t0 = i0; t0 < i1; t0 += tile) {
+        const int64_t id0 = t0 + static_cast<int64_t>(tid) * kResTile;
+        const int nv = static_cast<int>(min<int64_t>(max<int64_t>(i1 - id0, 0), kResTile));
+        if (nv > 0) {
+            float w[kResTile], p[kResTile];
+            eval_run<DT, TOPP>(rowT, rowD, resid, id0, nv, rp, P.c_hi, P.c_lo, invT, invD, w, p);
+#pragma unroll
+            for (int i = 0; i < kResTile; ++i) {
+                aw += static_cast<double>(w[i]);
+                ap += static_cast<double>(p[i]);
+            }
+        }
+    }
+    aw = wave_sum(aw);
+    ap = wave_sum(ap);
+    if (lane == 0) {
+        sh_w[wv] = aw;
+        sh_p[wv] = ap;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        double W = 0.0, Pm = 0.0;
+        for (int w = 0; w < kWaves; ++w) {
+            W += sh_w[w];
+            Pm += sh_p[w];
+        }
+        double* cm = P.cmass + (static_cast<size_t>(b) * P.nch2 + c) * 2;
+        cm[0] = W;
+        cm[1] = Pm;
+        s_last = (counter_arrive(&P.res_cnt[static_cast<size_t>(b) * kCounterStride]) + 1u ==
+                  static_cast<uint32_t>(P.nch2))
+                     ? 1
+                     : 0;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    acquire_agent();
+    if (tid == 0) {
+        P.res_cnt[static_cast<size_t>(b) * kCounterStride] = 0u;
+        const double* cm = P.cmass + static_cast<size_t>(b) * P.nch2 * 2;
+        int sel = 0;
+        double Z = 0.0;
+        for (int k = 0; k < P.nch2; ++k) Z += cm[2 * k];
+        if (!(Z > 0.0)) {
+            // A rejection implies p(x) < q(x), hence positive residual mass;
+            // none survives only through rounding: draw from p' instead.
+            sel = 1;
+            Z = 0.0;
+            for (int k = 0; k < P.nch2; ++k) Z += cm[2 * k + 1];
+        }
+        const double t = rp.u * Z;
+        double pre = 0.0, cpre = 0.0, lpre = 0.0;
+        int ch = -1, last = -1;
+        for (int k = 0; k < P.nch2; ++k) {
+            const double m = cm[2 * k + sel];
+            if (m > 0.0) {
+                if (ch < 0 && pre + m > t) {
+                    ch = k;
+                    cpre = pre;
+                }
+                last = k;
+                lpre = pre;
+            }
+            pre += m;
+        }
+        if (ch < 0) {
+            ch = last < 0 ? 0 : last;
+            cpre = last < 0 ? 0.0 : lpre;
+        }
+        s_sel = sel;
+        s_chunk = ch;
+        s_pre = cpre;
+        s_t = t;
+        s_Z = Z;
+        s_y = -1;
+    }
+    __syncthreads();
+    // Rescan the chosen chunk in id order: tile by tile, a prefix sum over
+    // threads (each thread owns kResTile consecutive ids), then one thread
+    // walks its run.
+    const int sel = s_sel;
+    const double t = s_t;
+    const int64_t j0 = static_cast<int64_t>(s_chunk) * P.ce2;
+    const int64_t j1 = min<int64_t>(j0 + P.ce2, P.V);
+    double carry = s_pre;
+    int lastpos = -1;
+    for (int64_t t0 = j0; t0 < j1; t0 += tile) {
+        const int64_t id0 = t0 + static_cast<int64_t>(tid) * kResTile;
+        const int nv = static_cast<int>(min<int64_t>(max<int64_t>(j1 - id0, 0), kResTile));
+        float w[kResTile], p[kResTile];
+        double xs = 0.0;
+        if (nv > 0) {
+            eval_run<DT, TOPP>(rowT, rowD, resid, id0, nv, rp, P.c_hi, P.c_lo, invT, invD, w, p);
+#pragma unroll
+            for (int i = 0; i < kResTile; ++i) {
+                const float v = sel ? p[i] : w[i];
+                w[i] = v;
+                xs += static_cast<double>(v);
+                if (v > 0.f) lastpos = static_cast<int>(id0 + i);
+            }
+        }
+        double incl, excl, total;
+        block_scan(xs, incl, excl, total);
+        const int hit = (xs > 0.0 && carry + incl > t) ? tid : 0x7FFFFFFF;
+        const int first = block_min_int(hit);
+        if (first != 0x7FFFFFFF) {
+            if (tid == first) {
+                double run = carry + excl;
+                int y = -1, lastw = -1;
+                for (int i = 0; i < nv; ++i) {
+                    if (w[i] > 0.f) {
+                        lastw = static_cast<int>(id0 + i);
+                        if (y < 0 && run + static_cast<double>(w[i]) > t) y = lastw;
+                    }
+                    run += static_cast<double>(w[i]);
+                }
+                s_y = y >= 0 ? y : lastw;
+            }
+            __syncthreads();
+            break;
+        }
+        carry += total;
+    }
+    const int lp = block_max_int(lastpos);
+    if (tid == 0) {
+        const int y = s_y >= 0 ? s_y : (lp >= 0 ? lp : 0);
+        P.out_tokens[static_cast<size_t>(b) * (P.K + 1) + rp.n] = y;
+        if (P.probe_row) {
+            P.probe_row[static_cast<size_t>(b) * 4 + 0] = s_Z;
+            P.probe_row[static_cast<size_t>(b) * 4 + 1] = t;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers.
+// ---------------------------------------------------------------------------
+hipError_t launch_stats(const Params& p, int dtype, bool topp, hipStream_t s) {
+    const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(p.B) * p.nslot * p.nch);
+    if (dtype == DT_BF16) {
+        if (topp) hipLaunchKernelGGL((k_stats<DT_BF16, true>), dim3(grid), dim3(kThreads), 0, s, p);
+        else hipLaunchKernelGGL((k_stats<DT_BF16, false>), dim3(grid), dim3(kThreads), 0, s, p);
+    } else {
+        if (topp) hipLaunchKernelGGL((k_stats<DT_F32, true>), dim3(grid), dim3(kThreads), 0, s, p);
+        else hipLaunchKernelGGL((k_stats<DT_F32, false>), dim3(grid), dim3(kThreads), 0, s, p);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_topp(const Params& p, int dtype, hipStream_t s) {
+    const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(p.B) * p.nslot);
+    if (dtype == DT_BF16) hipLaunchKernelGGL((k_topp<DT_BF16>), dim3(grid), dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((k_topp<DT_F32>), dim3(grid), dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_resample(const Params& p, int dtype, bool topp, hipStream_t s) {
+    const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(p.B) * p.nch2);
+    if (dtype == DT_BF16) {
+        if (topp) hipLaunchKernelGGL((k_resample<DT_BF16, true>), dim3(grid), dim3(kThreads), 0, s, p);
+        else hipLaunchKernelGGL((k_resample<DT_BF16, false>), dim3(grid), dim3(kThreads), 0, s, p);
+    } else {
+        if (topp) hipLaunchKernelGGL((k_resample<DT_F32, true>), dim3(grid), dim3(kThreads), 0, s, p);
+        else hipLaunchKernelGGL((k_resample<DT_F32, false>), dim3(grid), dim3(kThreads), 0, s, p);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace sv

@@ -1,0 +1,78 @@
+"""The C-ABI library: it builds for gfx950, loads, exports every function
+include/specverify.h declares, and rejects bad arguments on the host before
+any GPU work (no compute call is made here)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from rejection_sampling_verifier_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "specverify.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        from rejection_sampling_verifier_amd import build
+        build.build(verbose=False)
+    return binding.load()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(spec_verify\w*)\s*\(", src)))
+
+
+def test_header_declares_the_interface():
+    names = declared_functions()
+    assert "spec_verify" in names and "spec_verify_probe" in names
+    assert set(names) == set(binding.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r" T (\w+)", out))
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_library_holds_gfx950_code():
+    out = subprocess.run(["strings", binding.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    assert "gfx950" in out
+
+
+def test_abi_version_and_messages(lib):
+    assert lib.spec_verify_abi_version() == 1
+    for code in (0, -1, -2, -3, -4, -5, -6):
+        assert len(lib.spec_verify_strerror(code)) > 3
+
+
+def _call(lib, B=2, K=3, V=100, dtype=0, T=1.0, top_p=1.0, tP=None, dP=None, tdata=0x1000, ddata=0x2000,
+          tokens=0x3000, out=0x4000, outn=0x5000, dtype_d=None, stride=(0, 0)):
+    t = binding.SvLogits(tdata, dtype, B, K + 1 if tP is None else tP, V, (K + 1) * V + stride[0], V + stride[1])
+    d = binding.SvLogits(ddata, dtype if dtype_d is None else dtype_d, B, K if dP is None else dP, V, K * V, V)
+    return lib.spec_verify(ctypes.byref(t), ctypes.byref(d), ctypes.c_void_p(tokens), ctypes.c_void_p(None),
+                           ctypes.c_float(T), ctypes.c_float(top_p), ctypes.c_uint64(0), ctypes.c_void_p(out),
+                           ctypes.c_void_p(outn), ctypes.c_void_p(None))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(tdata=0), -1), (dict(tokens=0), -1), (dict(out=0), -1),
+    (dict(dtype=7), -3), (dict(dtype_d=1), -3),
+    (dict(K=0), -2), (dict(K=17), -2), (dict(B=0), -2), (dict(V=0), -2), (dict(dP=2), -2), (dict(tP=3), -2),
+    (dict(T=0.0), -1), (dict(T=-1.0), -1), (dict(T=float("nan")), -1), (dict(T=float("inf")), -1),
+    (dict(T=1e-45), -1),
+    (dict(top_p=0.0), -1), (dict(top_p=1.5), -1), (dict(top_p=float("nan")), -1),
+    (dict(tdata=0x1002), -6), (dict(dtype=1, dtype_d=1, tdata=0x1001), -6), (dict(tokens=0x3002), -6),
+    (dict(stride=(-2 * 400, 0)), -1),
+])
+def test_host_validation(lib, kw, code):
+    assert _call(lib, **kw) == code

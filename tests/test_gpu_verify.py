@@ -1,0 +1,216 @@
+"""GPU parity: the HIP library against the float64 oracle on the same seeded
+inputs, element by element, through the C ABI.
+
+Bar: identical accepted counts and emitted tokens on every row whose oracle
+decisions all lie outside the 1e-6 flag band; probe values (normalisers,
+p'(x_j), q'(x_j), kept masses, Z, t) to 1e-5 relative; flagged decisions a
+small fraction of all decisions.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_helpers import check_parity, dev_array, run_gpu, run_oracle, say, to_device
+from rejection_sampling_verifier_amd import binding
+from rejection_sampling_verifier_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    binding.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def _parity(inp, rows=None, label=""):
+    say(f"[parity] {label} B={inp.B} K={inp.K} V={inp.V} {inp.target.dtype} T={inp.temperature} "
+        f"top_p={inp.top_p} seed={inp.seed:#x}")
+    gpu = run_gpu(inp)
+    res = run_oracle(inp, rows=rows)
+    c, f, d, fd = check_parity(inp, res, gpu)
+    say(f"    rows checked={c} flagged={f} decisions={d} flagged decisions={fd}")
+    assert c > 0
+    return c, f, d, fd
+
+
+# ---------------------------------------------------------------------------
+# The five workloads
+# ---------------------------------------------------------------------------
+
+def test_tiny_fp32_many_steps():
+    tot = [0, 0, 0, 0]
+    for step in range(60):
+        r = _parity(W.make_inputs(0, step), label=f"tiny step {step}")
+        tot = [a + b for a, b in zip(tot, r)]
+    assert tot[3] <= max(1, tot[2] // 1000)
+
+
+def test_single_stream_llama_vocab_fp32():
+    for step in range(3):
+        _parity(W.make_inputs(1, step), label=f"single-stream step {step}")
+
+
+def test_batched_bf16_full_size():
+    _parity(W.make_inputs(2, 0), label="batched full")
+
+
+def test_batched_bf16_ragged_vocab_tail():
+    # V = 5003: several statistics chunks and a ragged last 16-byte vector
+    for step in range(6):
+        _parity(W.make_inputs(2, 100 + step, B=64, V=5003), label="batched V=5003")
+
+
+def test_ragged_batch_full_size_sampled_rows():
+    inp = W.make_inputs(3, 0)
+    rows = np.arange(0, inp.B, 8)
+    _parity(inp, rows=rows, label="ragged full, every 8th row")
+
+
+def test_ragged_batch_shrunk():
+    for step in range(3):
+        _parity(W.make_inputs(3, 50 + step, B=48, V=9001), label="ragged V=9001")
+
+
+def test_filtered_shrunk():
+    for step in range(3):
+        _parity(W.make_inputs(4, 10 + step, B=16, V=20011), label="filtered V=20011")
+
+
+def test_filtered_full_size_sampled_rows():
+    inp = W.make_inputs(4, 0)
+    _parity(inp, rows=np.arange(0, inp.B, 16), label="filtered full, every 16th row")
+
+
+# ---------------------------------------------------------------------------
+# Edge cases
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V", [1, 7, 64, 1000, 4099])
+def test_small_vocabularies(dtype, V):
+    for s in range(3):
+        inp = W.synthetic(5, 3, V, dtype=dtype, temperature=0.8, seed=1000 + s, gen_seed=V * 10 + s)
+        _parity(inp, label=f"V={V} {dtype}")
+
+
+@pytest.mark.parametrize("K", [1, 2, 16])
+def test_draft_lengths(K):
+    inp = W.synthetic(9, K, 3001, dtype="bf16", temperature=0.7, sigma=0.3, seed=77 + K, gen_seed=K)
+    _parity(inp, label=f"K={K}")
+
+
+def test_zero_and_mixed_draft_lengths():
+    inp = W.synthetic(12, 4, 2500, dtype="f32", seed=5, gen_seed=41,
+                      draft_len=[0, 1, 2, 3, 4, 0, 4, 1, 0, 2, 3, 4])
+    _parity(inp, label="mixed L incl. 0")
+
+
+@pytest.mark.parametrize("top_p", [0.3, 0.6, 0.95])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_top_p_values(top_p, dtype):
+    inp = W.synthetic(8, 3, 6007, dtype=dtype, temperature=0.9, top_p=top_p, seed=3, gen_seed=int(top_p * 1000))
+    # drafts outside the draft's nucleus are legal inputs (q'(x) = 0 rule)
+    _parity(inp, label=f"top_p={top_p} {dtype}")
+
+
+def test_top_p_flat_rows_split_tie_groups():
+    # all-equal logits: the whole row is one tie group; the cut keeps the
+    # lowest ids; rows 2-3 draft ids outside the nucleus (r = 0/0 = 0, a
+    # degenerate residual the oracle flags)
+    inp = W.synthetic(4, 2, 1000, dtype="bf16", top_p=0.3705, seed=9, gen_seed=9)
+    inp.target[:] = W.f32_to_bf16_bits(np.zeros((4, 3, 1000), np.float32))
+    inp.draft[:] = W.f32_to_bf16_bits(np.zeros((4, 2, 1000), np.float32))
+    inp.draft_tokens[:] = [[3, 5], [1, 370], [800, 3], [10, 900]]
+    _parity(inp, label="flat rows, top_p=0.3705")
+
+
+def test_top_p_coarse_logits_many_ties():
+    rng = np.random.default_rng(3)
+    inp = W.synthetic(6, 3, 20000, dtype="bf16", top_p=0.8, seed=10, gen_seed=10)
+    t = np.round(rng.normal(0, 2, size=(6, 4, 20000)) * 2) / 2
+    d = t[:, :3] + np.round(rng.normal(0, 1, size=(6, 3, 20000)) * 2) / 2
+    inp.target[:] = W.f32_to_bf16_bits(t.astype(np.float32))
+    inp.draft[:] = W.f32_to_bf16_bits(d.astype(np.float32))
+    _parity(inp, label="coarse logits, top_p=0.8")
+
+
+def test_extreme_and_masked_logits():
+    inp = W.synthetic(6, 3, 3000, dtype="f32", temperature=0.5, seed=11, gen_seed=11)
+    inp.target[0] *= 3000.0            # logits of order 1e4
+    inp.draft[0] *= 3000.0
+    inp.target[1, :, 100:] = -np.inf   # masked vocabulary
+    inp.draft[1, :, 100:] = -np.inf
+    inp.draft_tokens[1] = [5, 17, 99]
+    inp.target[2, :, ::2] = -np.inf
+    _parity(inp, label="extreme / masked")
+
+
+def test_identical_models_accept_all():
+    inp = W.synthetic(10, 5, 4000, dtype="bf16", seed=12, gen_seed=12)
+    inp.draft[:] = inp.target[:, :5]
+    gpu = run_gpu(inp)
+    assert np.all(gpu[1] == 5)
+    np.testing.assert_array_equal(gpu[0][:, :5], inp.draft_tokens)
+    _parity(inp, label="identical models")
+
+
+def test_invalid_rows_emit_sentinels():
+    inp = W.synthetic(8, 3, 500, dtype="f32", seed=13, gen_seed=13, draft_len=[3, 3, 3, 3, 2, 3, 3, 3])
+    inp.target[1, 2, 7] = np.nan          # NaN in a needed target row
+    inp.draft[2, 0, 0] = np.inf           # +inf in a needed draft row
+    inp.target[3, 0, :] = -np.inf         # a needed row of only -inf
+    inp.draft[4, 2, :] = np.nan           # past L = 2: never read
+    inp.target[4, 3, :] = np.nan
+    inp.draft_tokens[5, 1] = 500          # id out of range
+    inp.draft_tokens[6, 2] = -3
+    inp.draft_len[7] = 4                  # length out of range
+    gpu = run_gpu(inp)
+    res = run_oracle(inp)
+    for b in (1, 2, 3, 5, 6, 7):
+        assert gpu[1][b] == -1 and np.all(gpu[0][b] == -1), b
+        assert res.n_accepted[b] == -1
+    check_parity(inp, res, gpu)
+
+
+def test_strided_unaligned_views():
+    # logits as views into larger buffers: row starts off the 16-byte grid
+    base = W.synthetic(7, 3, 3010, dtype="bf16", temperature=0.8, seed=14, gen_seed=14)
+    inp = W.synthetic(7, 3, 3001, dtype="bf16", temperature=0.8, seed=14, gen_seed=14)
+    inp.target = np.ascontiguousarray(base.target[:, :, 3:3004])
+    inp.draft = np.ascontiguousarray(base.draft[:, :, 5:3006])
+    inp.draft_tokens = np.minimum(base.draft_tokens, 3000).astype(np.int32)
+    tb = dev_array(base.target)
+    db = dev_array(base.draft)
+    t = tb[:, :, 3:3004]
+    d = db[:, :, 5:3006]
+    x = torch.from_numpy(inp.draft_tokens).cuda()
+    gpu = run_gpu(inp, tensors=(t, d, x, None))
+    res = run_oracle(inp)
+    c, f, _, _ = check_parity(inp, res, gpu)
+    assert c + f == 7
+
+
+def test_deterministic_repeats():
+    inp = W.make_inputs(2, 3, B=32, V=20000)
+    tensors = to_device(inp)
+    first = run_gpu(inp, probe=False, tensors=tensors)
+    for _ in range(20):
+        again = run_gpu(inp, probe=False, tensors=tensors)
+        np.testing.assert_array_equal(again[0], first[0])
+        np.testing.assert_array_equal(again[1], first[1])
+
+
+def test_stream_argument_and_plain_entry_point():
+    inp = W.make_inputs(2, 4, B=8, V=3000)
+    t, d, x, dl = to_device(inp)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        tok, n = binding.verify(t, d, x, dl, float(inp.temperature), float(inp.top_p), inp.seed)
+    s.synchronize()
+    ref = run_gpu(inp, probe=True, tensors=(t, d, x, dl))
+    np.testing.assert_array_equal(tok.cpu().numpy(), ref[0])
+    np.testing.assert_array_equal(n.cpu().numpy(), ref[1])

@@ -26,7 +26,7 @@ struct Scratch {
 };
 
 struct Layout {
-    size_t part, rv, rowp, cmass, row_cnt, res_cnt, total;
+    size_t part, rv, rowp, cmass, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -34,10 +34,6 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 Layout layout(int64_t B, int nslot, int nch, int nch2) {
     Layout L;
     size_t off = 0;
-    L.row_cnt = off;
-    off = align256(off + static_cast<size_t>(B) * sv::kCounterStride * 4);
-    L.res_cnt = off;
-    off = align256(off + static_cast<size_t>(B) * sv::kCounterStride * 4);
     L.part = off;
     off = align256(off + static_cast<size_t>(B) * nslot * nch * sizeof(sv::Partial));
     L.rv = off;
@@ -82,8 +78,9 @@ int check_logits(const sv_logits* t) {
     return SV_OK;
 }
 
-// Returns the scratch for (device, stream), growing it when needed.  Counters
-// are zeroed on allocation; kernels leave them at zero after every call.
+// Returns the scratch for (device, stream), growing it when needed.  Every
+// byte a call reads from it is written earlier in the same call, so its
+// previous contents never matter.
 int get_scratch(hipStream_t stream, size_t bytes, void** out) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -214,21 +211,21 @@ int verify_impl(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_t
     p.top_p = top_p;
     p.key0 = static_cast<uint32_t>(seed & 0xFFFFFFFFull);
     p.key1 = static_cast<uint32_t>(seed >> 32);
-    p.row_cnt = reinterpret_cast<uint32_t*>(base + lay.row_cnt);
-    p.res_cnt = reinterpret_cast<uint32_t*>(base + lay.res_cnt);
     p.part = reinterpret_cast<sv::Partial*>(base + lay.part);
     p.rv = reinterpret_cast<sv::RvState*>(base + lay.rv);
     p.rowp = reinterpret_cast<sv::RowParam*>(base + lay.rowp);
     p.cmass = reinterpret_cast<double*>(base + lay.cmass);
 
     const bool topp = top_p < 1.f;
-    rc = timed_launch(sv::KK_STATS, stream, [&] { return sv::launch_stats(p, dtype, topp, stream); });
+    rc = timed_launch(sv::KK_STATS, stream, [&] { return sv::launch_stats(p, dtype, stream); });
     if (rc) return rc;
     if (topp) {
         rc = timed_launch(sv::KK_TOPP, stream, [&] { return sv::launch_topp(p, dtype, stream); });
         if (rc) return rc;
     }
-    return timed_launch(sv::KK_RESAMPLE, stream, [&] { return sv::launch_resample(p, dtype, topp, stream); });
+    rc = timed_launch(sv::KK_RESAMPLE, stream, [&] { return sv::launch_resample(p, dtype, topp, stream); });
+    if (rc) return rc;
+    return timed_launch(sv::KK_PICK, stream, [&] { return sv::launch_pick(p, dtype, topp, stream); });
 }
 
 }  // namespace

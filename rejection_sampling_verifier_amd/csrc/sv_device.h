@@ -152,12 +152,4 @@ __device__ __forceinline__ double word_uniform(uint32_t w) {
     return static_cast<double>(w >> 8) * (1.0 / 16777216.0);
 }
 
-// Agent-scope release/acquire around the last-block-done counters: the
-// partial results of a block become visible to whichever block on any XCD
-// observes the final count.
-__device__ __forceinline__ uint32_t counter_arrive(uint32_t* cnt) {
-    return __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
-
 }  // namespace sv

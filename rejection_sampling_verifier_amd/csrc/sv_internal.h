@@ -16,7 +16,7 @@ constexpr int kResTile = 8;          // consecutive ids per lane in the resample
 
 enum DType : int { DT_F32 = 0, DT_BF16 = 1 };
 enum RowMode : int { MODE_SKIP = 0, MODE_RESID = 1, MODE_BONUS = 2 };
-enum KernelKind : int { KK_STATS = 0, KK_TOPP = 1, KK_RESAMPLE = 2, KK_COUNT = 3 };
+enum KernelKind : int { KK_STATS = 0, KK_TOPP = 1, KK_RESAMPLE = 2, KK_PICK = 3, KK_COUNT = 4 };
 
 // Statistics of one chunk of one logit row, relative to an integer offset o:
 // s = sum over the chunk of 2^(l*c - o), c = log2(e)/T; m = max logit.
@@ -73,15 +73,12 @@ struct Params {
     RvState* rv;                  // [B, nslot]
     RowParam* rowp;               // [B]
     double* cmass;                // [B, nch2, 2]: residual (or bonus) mass, target mass
-    uint32_t* row_cnt;            // [B] x 16 words apart
-    uint32_t* res_cnt;            // [B] x 16 words apart
 };
 
-constexpr int kCounterStride = 16;  // counters one 64-byte line apart
-
 // Launchers (defined in sv_kernels.hip).
-hipError_t launch_stats(const Params& p, int dtype, bool topp, hipStream_t s);
+hipError_t launch_stats(const Params& p, int dtype, hipStream_t s);
 hipError_t launch_topp(const Params& p, int dtype, hipStream_t s);
 hipError_t launch_resample(const Params& p, int dtype, bool topp, hipStream_t s);
+hipError_t launch_pick(const Params& p, int dtype, bool topp, hipStream_t s);
 
 }  // namespace sv

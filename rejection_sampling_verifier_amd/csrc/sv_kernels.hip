@@ -11,23 +11,27 @@
 // Speculative Decoding for LLMs", section 2 (per-sequence acceptance in a
 // batch).
 //
-// Pipeline (all on one stream, no host synchronisation):
+// Pipeline (all on one stream, no host synchronisation, no cross-workgroup
+// atomics: every hand-off is a kernel boundary):
 //   k_stats     one workgroup per (row b, logit row, chunk of V): streams the
 //               chunk once from HBM with 16-byte loads and reduces it to
-//               (offset o, sum 2^(l*c - o), max).  Without top-p the last
-//               workgroup to finish a batch row runs the row epilogue
-//               (combine, gather p(x_j), q(x_j), Philox, accept scan).
-//   k_topp      (top-p only) one workgroup per logit row: exact nucleus cut
-//               (value key tau, tie cut by id, kept mass); the last logit row
-//               of a batch row runs the row epilogue.
-//   k_resample  one workgroup per (row b, chunk of V): residual or bonus mass
-//               of the chunk in float64; the last chunk of a row finds the
-//               chunk holding u*Z and rescans it in id order.
+//               (offset o, sum 2^(l*c - o), max) -- one 16-byte partial.
+//   k_topp      (top-p only) one workgroup per logit row: combines its
+//               partials and finds the exact nucleus cut (value key tau, tie
+//               cut by id, kept mass).
+//   k_resample  one workgroup per (row b, chunk of V): first re-derives the
+//               row's decision (combine the row's partials, gather p'(x_j)
+//               and q'(x_j), Philox, accept scan -> n_b) -- a few KB of reads,
+//               cheaper than a synchronisation -- then sums the residual or
+//               bonus mass of its chunk in float64.  Chunk 0 writes the row's
+//               outputs.
+//   k_pick      one workgroup per row b: finds the chunk holding u*Z from the
+//               chunk masses and rescans it in id order for the token.
 //
 // Everything that streams V is bandwidth-bound (no dense contraction, so no
-// MFMA).  Rows are independent; the last-block-done counters use agent-scope
-// acquire/release so that partial results written on one XCD are seen by the
-// workgroup that finishes the row on another.
+// MFMA).  Agent-scope release/acquire between workgroups would cost an L2
+// writeback per workgroup on this part, which is why hand-offs go through
+// kernel boundaries instead.
 
 #include "sv_device.h"
 #include "sv_internal.h"
@@ -94,6 +98,7 @@ struct RowShared {
     int bad;
     int n;
     double u_res;
+    RowParam rp;
 };
 
 // rv index r of a batch row: target position j -> r = j; draft position j ->
@@ -121,22 +126,54 @@ __device__ __forceinline__ void combine_partials(const Params& P, int b, int slo
     S = wave_sum(S);
 }
 
+// Re-derives the decision of batch row b into R (all threads of the
+// workgroup take part): combine (or load) the statistics of the row's logit
+// rows, check validity, gather p'(x_j), q'(x_j), draw the Philox uniforms and
+// scan for the first rejection.  With write_outputs the workgroup also writes
+// the row's outputs, its probe records and the RowParam the pick pass reads.
 template <int DT, bool TOPP>
-__device__ void row_finish(const Params& P, int b, int Le, bool rowok, RowShared& R) {
-    const int tid = threadIdx.x, lane = tid & 63;
+__device__ void row_decide(const Params& P, int b, RowShared& R, bool write_outputs) {
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int K = P.K, K1 = P.K + 1;
+    bool rowok;
+    const int Le = row_len(P, b, rowok);
     const int nrv = 2 * Le + 1;
-    if (tid == 0) {
-        int bad = rowok ? 0 : 1;
-        for (int r = 0; r < nrv; ++r) bad |= R.valid[r] ? 0 : 1;
-        R.bad = bad;
+    if (TOPP) {
+        for (int r = tid; r < nrv; r += kThreads) {
+            const RvState q = P.rv[static_cast<size_t>(b) * P.nslot + rv_slot(r, Le, K)];
+            R.o[r] = q.o;
+            R.m[r] = q.m;
+            R.s[r] = q.s;
+            R.kept[r] = q.kept;
+            R.tau[r] = q.tau;
+            R.cut[r] = q.cut;
+            R.valid[r] = q.valid;
+        }
+    } else {
+        for (int r = wv; r < nrv; r += kWaves) {
+            float O, M;
+            double S;
+            combine_partials(P, b, rv_slot(r, Le, K), lane, O, M, S);
+            if (lane == 0) {
+                R.o[r] = O;
+                R.m[r] = M;
+                R.s[r] = S;
+                R.kept[r] = S;
+                R.tau[r] = 0u;
+                R.cut[r] = -1;
+                R.valid[r] = (S > 0.0 && S < static_cast<double>(SV_INF)) ? 1 : 0;
+            }
+        }
     }
     __syncthreads();
     if (tid < 64) {
-        int bad_tok = 0;
+        int bad = rowok ? 0 : 1;
+        for (int r = lane; r < nrv; r += 64) bad |= R.valid[r] ? 0 : 1;
         bool rej = false;
         double u_res = 0.0;
-        if (!R.bad && lane <= Le) {
+        const bool rowbad = __ballot(bad) != 0ull;
+        int bad_tok = 0;
+        if (!rowbad && lane <= Le) {
             const uint4 w = philox4x32_10(make_uint4(static_cast<uint32_t>(b), static_cast<uint32_t>(lane), 0u, 0u),
                                           P.key0, P.key1);
             u_res = word_uniform(w.y);
@@ -161,17 +198,33 @@ __device__ void row_finish(const Params& P, int b, int Le, bool rowok, RowShared
                 }
             }
         }
-        const unsigned long long badm = __ballot(bad_tok);
+        const bool anybad = rowbad || (__ballot(bad_tok) != 0ull);
         const unsigned long long rejm = __ballot(rej);
-        const int n = rejm ? (__ffsll(static_cast<long long>(rejm)) - 1) : Le;
+        const int n = anybad ? 0 : (rejm ? (__ffsll(static_cast<long long>(rejm)) - 1) : Le);
         const double un = __shfl(u_res, n, 64);
         if (lane == 0) {
-            R.bad |= (badm != 0ull) ? 1 : 0;
-            R.n = R.bad ? 0 : n;
+            R.bad = anybad ? 1 : 0;
+            R.n = n;
             R.u_res = un;
+            RowParam rp;
+            rp.mode = anybad ? MODE_SKIP : (n < Le ? MODE_RESID : MODE_BONUS);
+            rp.n = n;
+            rp.oT = R.o[n];
+            rp.keptT = R.kept[n];
+            rp.tauT = R.tau[n];
+            rp.cutT = R.cut[n];
+            const int rD = Le + 1 + n;
+            const bool resid = rp.mode == MODE_RESID;
+            rp.oD = resid ? R.o[rD] : 0.f;
+            rp.keptD = resid ? R.kept[rD] : 1.0;
+            rp.tauD = resid ? R.tau[rD] : 0u;
+            rp.cutD = resid ? R.cut[rD] : -1;
+            rp.u = un;
+            R.rp = rp;
         }
     }
     __syncthreads();
+    if (!write_outputs) return;
     const int bad = R.bad, n = R.n;
     for (int j = tid; j < K1; j += kThreads) {
         int v = -1;
@@ -180,21 +233,7 @@ __device__ void row_finish(const Params& P, int b, int Le, bool rowok, RowShared
     }
     if (tid == 0) {
         P.out_n[b] = bad ? -1 : n;
-        RowParam rp;
-        rp.mode = bad ? MODE_SKIP : (n < Le ? MODE_RESID : MODE_BONUS);
-        rp.n = n;
-        rp.oT = R.o[n];
-        rp.keptT = R.kept[n];
-        rp.tauT = R.tau[n];
-        rp.cutT = R.cut[n];
-        const int rD = Le + 1 + n;
-        const bool resid = !bad && n < Le;
-        rp.oD = resid ? R.o[rD] : 0.f;
-        rp.keptD = resid ? R.kept[rD] : 1.0;
-        rp.tauD = resid ? R.tau[rD] : 0u;
-        rp.cutD = resid ? R.cut[rD] : -1;
-        rp.u = R.u_res;
-        P.rowp[b] = rp;
+        P.rowp[b] = R.rp;
         if (P.probe_row) {
             double* pr = P.probe_row + static_cast<size_t>(b) * 4;
             pr[0] = nan64();
@@ -274,11 +313,9 @@ __device__ __forceinline__ void stats_chunk(const uint8_t* row, int V, int64_t k
     }
 }
 
-template <int DT, bool TOPP>
+template <int DT>
 __global__ __launch_bounds__(kThreads) void k_stats(Params P) {
     __shared__ float sh_o[kWaves], sh_s[kWaves], sh_m[kWaves];
-    __shared__ int s_last;
-    __shared__ RowShared R;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int item = blockIdx.x;
     const int rvi = item / P.nch;
@@ -324,33 +361,7 @@ __global__ __launch_bounds__(kThreads) void k_stats(Params P) {
         pr.m = M;
         pr.s = S;
         P.part[static_cast<size_t>(rvi) * P.nch + chunk] = pr;
-        if (!TOPP) {
-            const uint32_t need = static_cast<uint32_t>((2 * Le + 1) * P.nch);
-            s_last = (counter_arrive(&P.row_cnt[static_cast<size_t>(b) * kCounterStride]) + 1u == need) ? 1 : 0;
-        }
     }
-    if (TOPP) return;
-    __syncthreads();
-    if (!s_last) return;
-    acquire_agent();
-    if (tid == 0) P.row_cnt[static_cast<size_t>(b) * kCounterStride] = 0u;
-    const int nrv = 2 * Le + 1;
-    for (int r = wv; r < nrv; r += kWaves) {
-        float O, M;
-        double S;
-        combine_partials(P, b, rv_slot(r, Le, P.K), lane, O, M, S);
-        if (lane == 0) {
-            R.o[r] = O;
-            R.m[r] = M;
-            R.s[r] = S;
-            R.kept[r] = S;
-            R.tau[r] = 0u;
-            R.cut[r] = -1;
-            R.valid[r] = (S > 0.0 && S < static_cast<double>(SV_INF)) ? 1 : 0;
-        }
-    }
-    __syncthreads();
-    row_finish<DT, false>(P, b, Le, rowok, R);
 }
 
 // ---------------------------------------------------------------------------
@@ -723,10 +734,8 @@ __device__ void select_nucleus(const Params& P, const uint8_t* row, float O, dou
 template <int DT>
 __global__ __launch_bounds__(kThreads) void k_topp(Params P) {
     __shared__ SelShared sh;
-    __shared__ RowShared R;
     __shared__ float s_o, s_m;
     __shared__ double s_s;
-    __shared__ int s_last;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int rvi = blockIdx.x;
     const int b = rvi / P.nslot;
@@ -768,30 +777,7 @@ __global__ __launch_bounds__(kThreads) void k_topp(Params P) {
         st.tau = tau;
         st.cut = cut;
     }
-    if (tid == 0) {
-        P.rv[rvi] = st;
-        s_last = (counter_arrive(&P.row_cnt[static_cast<size_t>(b) * kCounterStride]) + 1u ==
-                  static_cast<uint32_t>(2 * Le + 1))
-                     ? 1
-                     : 0;
-    }
-    __syncthreads();
-    if (!s_last) return;
-    acquire_agent();
-    if (tid == 0) P.row_cnt[static_cast<size_t>(b) * kCounterStride] = 0u;
-    const int nrv = 2 * Le + 1;
-    for (int r = tid; r < nrv; r += kThreads) {
-        const RvState q = P.rv[static_cast<size_t>(b) * P.nslot + rv_slot(r, Le, P.K)];
-        R.o[r] = q.o;
-        R.m[r] = q.m;
-        R.s[r] = q.s;
-        R.kept[r] = q.kept;
-        R.tau[r] = q.tau;
-        R.cut[r] = q.cut;
-        R.valid[r] = q.valid;
-    }
-    __syncthreads();
-    row_finish<DT, true>(P, b, Le, rowok, R);
+    if (tid == 0) P.rv[rvi] = st;
 }
 
 // ---------------------------------------------------------------------------
@@ -825,13 +811,13 @@ __device__ __forceinline__ void eval_run(const uint8_t* rowT, const uint8_t* row
 
 template <int DT, bool TOPP>
 __global__ __launch_bounds__(kThreads) void k_resample(Params P) {
+    __shared__ RowShared R;
     __shared__ double sh_w[kWaves], sh_p[kWaves];
-    __shared__ int s_last, s_sel, s_chunk, s_y;
-    __shared__ double s_t, s_Z, s_pre;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int b = blockIdx.x / P.nch2;
     const int c = blockIdx.x - b * P.nch2;
-    const RowParam rp = P.rowp[b];
+    row_decide<DT, TOPP>(P, b, R, c == 0);
+    const RowParam rp = R.rp;
     if (rp.mode == MODE_SKIP) return;
     const bool resid = rp.mode == MODE_RESID;
     const uint8_t* rowT = row_ptr<DT>(P, true, b, rp.n);
@@ -872,16 +858,26 @@ __global__ __launch_bounds__(kThreads) void k_resample(Params P) {
         double* cm = P.cmass + (static_cast<size_t>(b) * P.nch2 + c) * 2;
         cm[0] = W;
         cm[1] = Pm;
-        s_last = (counter_arrive(&P.res_cnt[static_cast<size_t>(b) * kCounterStride]) + 1u ==
-                  static_cast<uint32_t>(P.nch2))
-                     ? 1
-                     : 0;
     }
-    __syncthreads();
-    if (!s_last) return;
-    acquire_agent();
+}
+
+// Per row: the chunk holding t = u*Z, then a rescan of that chunk in id order.
+template <int DT, bool TOPP>
+__global__ __launch_bounds__(kThreads) void k_pick(Params P) {
+    __shared__ int s_sel, s_chunk, s_y;
+    __shared__ double s_t, s_Z, s_pre;
+    const int tid = threadIdx.x;
+    const int b = blockIdx.x;
+    const RowParam rp = P.rowp[b];
+    // rowp was written by this call's resample pass; anything else is skipped
+    if ((rp.mode != MODE_RESID && rp.mode != MODE_BONUS) || rp.n < 0 || rp.n > P.K) return;
+    const bool resid = rp.mode == MODE_RESID;
+    const uint8_t* rowT = row_ptr<DT>(P, true, b, rp.n);
+    const uint8_t* rowD = resid ? row_ptr<DT>(P, false, b, rp.n) : nullptr;
+    const float invT = static_cast<float>(1.0 / rp.keptT);
+    const float invD = resid ? static_cast<float>(1.0 / rp.keptD) : 0.f;
+    const int64_t tile = static_cast<int64_t>(kThreads) * kResTile;
     if (tid == 0) {
-        P.res_cnt[static_cast<size_t>(b) * kCounterStride] = 0u;
         const double* cm = P.cmass + static_cast<size_t>(b) * P.nch2 * 2;
         int sel = 0;
         double Z = 0.0;
@@ -980,15 +976,10 @@ __global__ __launch_bounds__(kThreads) void k_resample(Params P) {
 // ---------------------------------------------------------------------------
 // Launchers.
 // ---------------------------------------------------------------------------
-hipError_t launch_stats(const Params& p, int dtype, bool topp, hipStream_t s) {
+hipError_t launch_stats(const Params& p, int dtype, hipStream_t s) {
     const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(p.B) * p.nslot * p.nch);
-    if (dtype == DT_BF16) {
-        if (topp) hipLaunchKernelGGL((k_stats<DT_BF16, true>), dim3(grid), dim3(kThreads), 0, s, p);
-        else hipLaunchKernelGGL((k_stats<DT_BF16, false>), dim3(grid), dim3(kThreads), 0, s, p);
-    } else {
-        if (topp) hipLaunchKernelGGL((k_stats<DT_F32, true>), dim3(grid), dim3(kThreads), 0, s, p);
-        else hipLaunchKernelGGL((k_stats<DT_F32, false>), dim3(grid), dim3(kThreads), 0, s, p);
-    }
+    if (dtype == DT_BF16) hipLaunchKernelGGL((k_stats<DT_BF16>), dim3(grid), dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((k_stats<DT_F32>), dim3(grid), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 
@@ -1007,6 +998,18 @@ hipError_t launch_resample(const Params& p, int dtype, bool topp, hipStream_t s)
     } else {
         if (topp) hipLaunchKernelGGL((k_resample<DT_F32, true>), dim3(grid), dim3(kThreads), 0, s, p);
         else hipLaunchKernelGGL((k_resample<DT_F32, false>), dim3(grid), dim3(kThreads), 0, s, p);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_pick(const Params& p, int dtype, bool topp, hipStream_t s) {
+    const unsigned grid = static_cast<unsigned>(p.B);
+    if (dtype == DT_BF16) {
+        if (topp) hipLaunchKernelGGL((k_pick<DT_BF16, true>), dim3(grid), dim3(kThreads), 0, s, p);
+        else hipLaunchKernelGGL((k_pick<DT_BF16, false>), dim3(grid), dim3(kThreads), 0, s, p);
+    } else {
+        if (topp) hipLaunchKernelGGL((k_pick<DT_F32, true>), dim3(grid), dim3(kThreads), 0, s, p);
+        else hipLaunchKernelGGL((k_pick<DT_F32, false>), dim3(grid), dim3(kThreads), 0, s, p);
     }
     return hipGetLastError();
 }

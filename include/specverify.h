@@ -154,6 +154,14 @@ int spec_verify_abi_version(void);
 int spec_verify_profile_enable(int enable);
 int spec_verify_profile_read(double* ms, int64_t* launches, int n);
 
+/* Measurement helper (not part of the verify step): reads every 16-byte
+ * vector of the device buffer buf[0..bytes) once, with the statistics pass's
+ * access pattern (workgroups of 256 threads, `unroll` in {2, 4, 8} vectors per
+ * thread), so that timing it on `stream` gives the streaming-read ceiling the
+ * verify kernels are measured against.  sink: device uint32[1024], written
+ * only to keep the loads alive.  buf must be 16-byte aligned. */
+int spec_verify_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int unroll, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -21,7 +21,8 @@ STATUS = {0: "SV_OK", -1: "SV_EINVAL", -2: "SV_ESHAPE", -3: "SV_EDTYPE", -4: "SV
 KERNEL_KINDS = ("stats", "topp", "resample", "pick")
 
 EXPORTS = ("spec_verify", "spec_verify_probe", "spec_verify_strerror", "spec_verify_release",
-           "spec_verify_abi_version", "spec_verify_profile_enable", "spec_verify_profile_read")
+           "spec_verify_abi_version", "spec_verify_profile_enable", "spec_verify_profile_read",
+           "spec_verify_stream_read")
 
 
 class SvLogits(ctypes.Structure):
@@ -69,6 +70,9 @@ def load(path=LIB_PATH):
     lib.spec_verify_profile_enable.restype = ctypes.c_int
     lib.spec_verify_profile_read.argtypes = [P(ctypes.c_double), P(ctypes.c_int64), ctypes.c_int]
     lib.spec_verify_profile_read.restype = ctypes.c_int
+    lib.spec_verify_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                                            ctypes.c_void_p]
+    lib.spec_verify_stream_read.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -151,3 +155,11 @@ def profile_read():
 
 def release():
     load().spec_verify_release()
+
+
+def stream_read(buf, sink, unroll=4, stream=None):
+    """Launch the streaming-read calibration kernel over a device tensor."""
+    lib = load()
+    sh = _stream_handle(stream, buf.device)
+    _check(lib, lib.spec_verify_stream_read(ctypes.c_void_p(buf.data_ptr()), buf.numel() * buf.element_size(),
+                                            ctypes.c_void_p(sink.data_ptr()), unroll, sh))

@@ -158,17 +158,17 @@ int verify_impl(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_t
     const int nslot = 2 * K + 1;
     // statistics pass: chunks of at most `cv` 16-byte vectors per workgroup
     const int64_t nvec_max = (static_cast<int64_t>(V) * E + 15) / 16 + 1;
-    int cv = env_int("SPECVERIFY_STATS_VECS", sv::kThreads * sv::kStatsUnroll);
-    if (cv < 64) cv = 64;
+    int unroll = env_int("SPECVERIFY_STATS_UNROLL", sv::kStatsUnroll);
+    if (unroll != 2 && unroll != 8) unroll = 4;
+    // chunks are whole steps of kThreads*unroll vectors; only a row's last
+    // chunk is partial
+    const int step = sv::kThreads * unroll;
+    int cv = env_int("SPECVERIFY_STATS_VECS", step);
+    cv = ((cv < step ? step : cv) + step - 1) / step * step;
     const int64_t nch64 = (nvec_max + cv - 1) / cv;
     const int nch = static_cast<int>(nch64);
-    cv = static_cast<int>((nvec_max + nch - 1) / nch);
-    // resample pass: chunks of ce2 ids (a multiple of one 2048-id tile)
-    const int tile = sv::kThreads * sv::kResTile;
-    int ce2 = env_int("SPECVERIFY_RESAMPLE_IDS", 2 * tile);
-    ce2 = ((ce2 + tile - 1) / tile) * tile;
-    if ((V + ce2 - 1) / ce2 > 1024) ce2 = (((V + 1023) / 1024 + tile - 1) / tile) * tile;
-    const int nch2 = (V + ce2 - 1) / ce2;
+    // resample pass: chunks of kResChunk ids
+    const int nch2 = (V + sv::kResChunk - 1) / sv::kResChunk;
     if (static_cast<int64_t>(B) * nslot * nch >= (1ll << 31)) return SV_ESHAPE;
 
     hipStream_t stream = static_cast<hipStream_t>(stream_v);
@@ -199,7 +199,6 @@ int verify_impl(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_t
     p.nch = nch;
     p.cv = cv;
     p.nch2 = nch2;
-    p.ce2 = ce2;
     // c = c_hi + c_lo with c_hi <= c rounded toward zero, so c_lo > 0.
     float c_hi = static_cast<float>(c);
     if (static_cast<double>(c_hi) > c) c_hi = std::nextafter(c_hi, 0.f);
@@ -217,7 +216,7 @@ int verify_impl(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_t
     p.cmass = reinterpret_cast<double*>(base + lay.cmass);
 
     const bool topp = top_p < 1.f;
-    rc = timed_launch(sv::KK_STATS, stream, [&] { return sv::launch_stats(p, dtype, stream); });
+    rc = timed_launch(sv::KK_STATS, stream, [&] { return sv::launch_stats(p, dtype, unroll, stream); });
     if (rc) return rc;
     if (topp) {
         rc = timed_launch(sv::KK_TOPP, stream, [&] { return sv::launch_topp(p, dtype, stream); });
@@ -270,6 +269,14 @@ void spec_verify_release(void) {
 }
 
 int spec_verify_abi_version(void) { return SPECVERIFY_ABI_VERSION; }
+
+int spec_verify_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int unroll, void* stream) {
+    if (!buf || !sink || bytes < 16) return SV_EINVAL;
+    if (misaligned(buf, 16) || misaligned(sink, 4)) return SV_EALIGN;
+    if (unroll != 2 && unroll != 4 && unroll != 8) return SV_EINVAL;
+    const hipError_t e = sv::launch_stream_read(buf, bytes, sink, unroll, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SV_OK : hip_fail(e, "stream read launch");
+}
 
 int spec_verify_profile_enable(int enable) {
     std::lock_guard<std::mutex> lk(g_mu);

@@ -44,6 +44,15 @@ template <> __device__ __forceinline__ void unpack<DT_BF16>(const uint4& v, floa
     f[7] = __uint_as_float(v.w & 0xFFFF0000u);
 }
 
+// 16-byte load through the global address space (global_load_dwordx4, not
+// the generic flat path the compiler picks for pointers held in a struct).
+typedef unsigned int sv_u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(1))) const sv_u32x4 sv_g_u32x4;
+__device__ __forceinline__ uint4 gload16(const uint4* p) {
+    const sv_u32x4 v = *(sv_g_u32x4*)(p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 template <int DT> __device__ __forceinline__ float load_elem(const uint8_t* row, int64_t i);
 template <> __device__ __forceinline__ float load_elem<DT_F32>(const uint8_t* row, int64_t i) {
     return reinterpret_cast<const float*>(row)[i];
@@ -61,20 +70,34 @@ __device__ __forceinline__ void load8(const uint8_t* row, int64_t id0, int nv, f
     if (nv == 8 && (reinterpret_cast<uintptr_t>(p) & 15) == 0) {
         const uint4* vp = reinterpret_cast<const uint4*>(p);
 #pragma unroll
-        for (int k = 0; k < 8 / VE; ++k) unpack<DT>(vp[k], f + k * VE);
+        for (int k = 0; k < 8 / VE; ++k) unpack<DT>(gload16(vp + k), f + k * VE);
     } else {
 #pragma unroll
         for (int i = 0; i < 8; ++i) f[i] = (i < nv) ? load_elem<DT>(row, id0 + i) : -SV_INF;
     }
 }
 
+// Hardware 2^x (v_exp_f32, ~1 ulp).  Arguments below -126 give results
+// below 2^-126 relative to the row's largest term, which no decision can see;
+// the library's exp2f would spend five more instructions on them.
+__device__ __forceinline__ float hw_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // Temperature-scaled exponent 2^(l*c - o) with c = c_hi + c_lo.  Both fused
 // multiply-adds are needed to keep c exact to ~2^-48: a float c alone would
 // tilt every distribution by up to 2^-24 relative in the exponent.  c_lo > 0
 // keeps l = -inf at -inf (never -inf + inf).
 __device__ __forceinline__ float tempexp(float l, float c_hi, float c_lo, float o) {
-    return exp2f(fmaf(l, c_lo, fmaf(l, c_hi, -o)));
+    return hw_exp2(fmaf(l, c_lo, fmaf(l, c_hi, -o)));
 }
+
+// max of three floats in one v_max3_f32 (no canonicalising moves; a NaN
+// input is caught later through the sum it poisons).
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+    float d;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(c));
+    return d;
+}
+
 
 // Order key of a logit: unsigned compare of keys = numeric compare of values
 // (-0 and +0 share a key).

@@ -11,8 +11,10 @@ constexpr int kThreads = 256;        // every kernel runs 4 wave64s per workgrou
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxK = 16;
 constexpr int kMaxSlots = 2 * kMaxK + 1;
-constexpr int kStatsUnroll = 4;      // 16-byte vectors in flight per lane per step
+constexpr int kStatsUnroll = 4;      // default 16-byte vectors in flight per lane per step
 constexpr int kResTile = 8;          // consecutive ids per lane in the resample pass
+constexpr int kResTiles = 2;         // tiles of kThreads*kResTile ids per resample chunk
+constexpr int kResChunk = kThreads * kResTile * kResTiles;
 
 enum DType : int { DT_F32 = 0, DT_BF16 = 1 };
 enum RowMode : int { MODE_SKIP = 0, MODE_RESID = 1, MODE_BONUS = 2 };
@@ -64,7 +66,7 @@ struct Params {
     double* probe_row;            // [B, 4] or null
     int B, K, V, nslot;
     int nch, cv;                  // statistics pass: chunks per row, 16-byte vectors per chunk
-    int nch2, ce2;                // resample pass: chunks per row, ids per chunk
+    int nch2;                     // resample pass: chunks of kResChunk ids per row
     float c_hi, c_lo;             // c = log2(e)/T = c_hi + c_lo, c_lo > 0
     double c64;                   // (double)c_hi + (double)c_lo
     float top_p;
@@ -76,9 +78,10 @@ struct Params {
 };
 
 // Launchers (defined in sv_kernels.hip).
-hipError_t launch_stats(const Params& p, int dtype, hipStream_t s);
+hipError_t launch_stats(const Params& p, int dtype, int unroll, hipStream_t s);
 hipError_t launch_topp(const Params& p, int dtype, hipStream_t s);
 hipError_t launch_resample(const Params& p, int dtype, bool topp, hipStream_t s);
 hipError_t launch_pick(const Params& p, int dtype, bool topp, hipStream_t s);
+hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int unroll, hipStream_t s);
 
 }  // namespace sv

@@ -131,13 +131,34 @@ __device__ __forceinline__ void combine_partials(const Params& P, int b, int slo
 // rows, check validity, gather p'(x_j), q'(x_j), draw the Philox uniforms and
 // scan for the first rejection.  With write_outputs the workgroup also writes
 // the row's outputs, its probe records and the RowParam the pick pass reads.
+// Merges two (offset, sum) statistics exactly: both sums are rescaled to the
+// larger integer offset by a power of two.  An empty side (offset -inf)
+// contributes its sum unscaled (0, or NaN from a bad logit).
+__device__ __forceinline__ double merge_stats(float Oa, double Sa, float Ob, double Sb, float& O) {
+    O = fmaxf(Oa, Ob);
+    const double sa = (Oa == -SV_INF) ? Sa : ldexp(Sa, static_cast<int>(fmaxf(Oa - O, -1100.f)));
+    const double sb = (Ob == -SV_INF) ? Sb : ldexp(Sb, static_cast<int>(fmaxf(Ob - O, -1100.f)));
+    return sa + sb;
+}
+
 template <int DT, bool TOPP>
 __device__ void row_decide(const Params& P, int b, RowShared& R, bool write_outputs) {
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
     const int K = P.K, K1 = P.K + 1;
     bool rowok;
     const int Le = row_len(P, b, rowok);
     const int nrv = 2 * Le + 1;
+    // Lanes j < Le of wave 0 start their dependent loads first (drafted id,
+    // then the two logits at it) so they overlap the statistics loads.
+    int x = -1;
+    float lt = 0.f, ld = 0.f;
+    if (tid < Le) {
+        x = P.tokens[static_cast<int64_t>(b) * K + tid];
+        if (x >= 0 && x < P.V) {
+            lt = load_elem<DT>(row_ptr<DT>(P, true, b, tid), x);
+            ld = load_elem<DT>(row_ptr<DT>(P, false, b, tid), x);
+        }
+    }
     if (TOPP) {
         for (int r = tid; r < nrv; r += kThreads) {
             const RvState q = P.rv[static_cast<size_t>(b) * P.nslot + rv_slot(r, Le, K)];
@@ -150,19 +171,39 @@ __device__ void row_decide(const Params& P, int b, RowShared& R, bool write_outp
             R.valid[r] = q.valid;
         }
     } else {
-        for (int r = wv; r < nrv; r += kWaves) {
-            float O, M;
-            double S;
-            combine_partials(P, b, rv_slot(r, Le, K), lane, O, M, S);
-            if (lane == 0) {
-                R.o[r] = O;
-                R.m[r] = M;
-                R.s[r] = S;
-                R.kept[r] = S;
-                R.tau[r] = 0u;
-                R.cut[r] = -1;
-                R.valid[r] = (S > 0.0 && S < static_cast<double>(SV_INF)) ? 1 : 0;
+        // G consecutive threads per logit row (G a power of two, within a wave)
+        int G = 64;
+        while (G > 1 && G * nrv > kThreads) G >>= 1;
+        const int r = tid / G, gl = tid - (tid / G) * G;
+        float O = -SV_INF, M = -SV_INF;
+        double S = 0.0;
+        if (r < nrv) {
+            const Partial* pp = P.part + (static_cast<size_t>(b) * P.nslot + rv_slot(r, Le, K)) * P.nch;
+            for (int c = gl; c < P.nch; c += G) {
+                const Partial q = pp[c];
+                float On;
+                S = merge_stats(O, S, q.o, q.s, On);
+                O = On;
+                M = fmaxf(M, q.m);
             }
+        }
+        for (int off = G >> 1; off >= 1; off >>= 1) {
+            const float O2 = __shfl_xor(O, off, 64);
+            const double S2 = __shfl_xor(S, off, 64);
+            const float M2 = __shfl_xor(M, off, 64);
+            float On;
+            S = merge_stats(O, S, O2, S2, On);
+            O = On;
+            M = fmaxf(M, M2);
+        }
+        if (r < nrv && gl == 0) {
+            R.o[r] = O;
+            R.m[r] = M;
+            R.s[r] = S;
+            R.kept[r] = S;
+            R.tau[r] = 0u;
+            R.cut[r] = -1;
+            R.valid[r] = (S > 0.0 && S < static_cast<double>(SV_INF)) ? 1 : 0;
         }
     }
     __syncthreads();
@@ -178,13 +219,10 @@ __device__ void row_decide(const Params& P, int b, RowShared& R, bool write_outp
                                           P.key0, P.key1);
             u_res = word_uniform(w.y);
             if (lane < Le) {
-                const int x = P.tokens[static_cast<int64_t>(b) * K + lane];
                 if (x < 0 || x >= P.V) {
                     bad_tok = 1;
                 } else {
                     const int rT = lane, rD = Le + 1 + lane;
-                    const float lt = load_elem<DT>(row_ptr<DT>(P, true, b, lane), x);
-                    const float ld = load_elem<DT>(row_ptr<DT>(P, false, b, lane), x);
                     double pt = exp2(static_cast<double>(lt) * P.c64 - static_cast<double>(R.o[rT])) / R.kept[rT];
                     double qd = exp2(static_cast<double>(ld) * P.c64 - static_cast<double>(R.o[rD])) / R.kept[rD];
                     if (TOPP) {
@@ -268,52 +306,80 @@ __device__ void row_decide(const Params& P, int b, RowShared& R, bool write_outp
 // ---------------------------------------------------------------------------
 // Statistics pass.
 // ---------------------------------------------------------------------------
-template <int DT, int U>
-__device__ __forceinline__ void stats_chunk(const uint8_t* row, int V, int64_t k0, int64_t k1, float c_hi,
-                                            float c_lo, float& m_run, float& o_run, float& s_run) {
+// One step of the statistics pass: U 16-byte vectors per lane, all loads
+// issued before any use.  EDGE handles a step that touches the row's first or
+// last vector or the end of the chunk (guarded loads, masked ids).
+template <int DT, int U, bool EDGE>
+__device__ __forceinline__ void stats_step(const RowGrid& g, int64_t kb, int64_t k1, int V, float c_hi, float c_lo,
+                                           float& m_run, float& o_run, float& s_run) {
     constexpr int VE = Fmt<DT>::VE;
-    const RowGrid g = row_grid<DT>(row, V);
-    for (int64_t kb = k0; kb < k1; kb += static_cast<int64_t>(kThreads) * U) {
-        uint4 raw[U];
+    constexpr int N = U * VE;
+    uint4 raw[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t k = kb + u * kThreads + threadIdx.x;
+    for (int u = 0; u < U; ++u) {
+        const int64_t k = kb + u * kThreads + threadIdx.x;
+        if (EDGE) {
             const uint32_t ni = Fmt<DT>::NEG_INF_WORD;
-            raw[u] = (k < k1) ? g.vp[k] : make_uint4(ni, ni, ni, ni);
+            raw[u] = (k < k1) ? gload16(g.vp + k) : make_uint4(ni, ni, ni, ni);
+        } else {
+            raw[u] = gload16(g.vp + k);
         }
-        float f[U * VE];
+    }
+    float f[N];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            unpack<DT>(raw[u], f + u * VE);
+    for (int u = 0; u < U; ++u) {
+        unpack<DT>(raw[u], f + u * VE);
+        if (EDGE) {
             const int64_t k = kb + u * kThreads + threadIdx.x;
             if (k < k1 && (k == 0 || k == g.nvec - 1)) mask_edge<DT>(f + u * VE, k, g.head, V);
         }
-        float bm = -SV_INF;
+    }
+    // N is a multiple of 4: a v_max3 tree
+    float bm = max3f(f[0], f[1], f[2]);
 #pragma unroll
-        for (int i = 0; i < U * VE; ++i) bm = fmaxf(bm, f[i]);
-        m_run = fmaxf(m_run, bm);
-        const float ob = ceilf(bm * c_hi);
-        if (ob > o_run) {
-            if (o_run != -SV_INF) s_run = ldexpf(s_run, static_cast<int>(fmaxf(o_run - ob, -256.f)));
-            o_run = ob;
-        }
-        const float off = (o_run == -SV_INF) ? 0.f : o_run;
-        float acc[U];
+    for (int i = 3; i + 1 < N; i += 2) bm = max3f(bm, f[i], f[i + 1]);
+    bm = fmaxf(bm, f[N - 1]);
+    m_run = fmaxf(m_run, bm);
+    const float ob = ceilf(bm * c_hi);
+    if (ob > o_run) {
+        if (o_run != -SV_INF) s_run = ldexpf(s_run, static_cast<int>(fmaxf(o_run - ob, -256.f)));
+        o_run = ob;
+    }
+    const float off = (o_run == -SV_INF) ? 0.f : o_run;
+    float acc[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float a = 0.f;
+    for (int u = 0; u < U; ++u) {
+        float e[VE];
 #pragma unroll
-            for (int i = 0; i < VE; ++i) a += tempexp(f[u * VE + i], c_hi, c_lo, off);
-            acc[u] = a;
-        }
-        float t = 0.f;
+        for (int i = 0; i < VE; ++i) e[i] = tempexp(f[u * VE + i], c_hi, c_lo, off);
 #pragma unroll
-        for (int u = 0; u < U; ++u) t += acc[u];
-        s_run += t;
+        for (int w = VE / 2; w >= 1; w >>= 1)
+#pragma unroll
+            for (int i = 0; i < w; ++i) e[i] += e[i + w];
+        acc[u] = e[0];
+    }
+#pragma unroll
+    for (int w = U / 2; w >= 1; w >>= 1)
+#pragma unroll
+        for (int i = 0; i < w; ++i) acc[i] += acc[i + w];
+    s_run += acc[0];
+}
+
+template <int DT, int U>
+__device__ __forceinline__ void stats_chunk(const uint8_t* row, int V, int64_t k0, int64_t k1, float c_hi,
+                                            float c_lo, float& m_run, float& o_run, float& s_run) {
+    const RowGrid g = row_grid<DT>(row, V);
+    constexpr int64_t STEP = static_cast<int64_t>(kThreads) * U;
+    for (int64_t kb = k0; kb < k1; kb += STEP) {
+        // uniform across the workgroup: whole step inside the chunk and away
+        // from the row's first and last vector
+        const bool inner = kb >= 1 && kb + STEP <= k1 && kb + STEP <= g.nvec - 1;
+        if (inner) stats_step<DT, U, false>(g, kb, k1, V, c_hi, c_lo, m_run, o_run, s_run);
+        else stats_step<DT, U, true>(g, kb, k1, V, c_hi, c_lo, m_run, o_run, s_run);
     }
 }
 
-template <int DT>
+template <int DT, int U>
 __global__ __launch_bounds__(kThreads) void k_stats(Params P) {
     __shared__ float sh_o[kWaves], sh_s[kWaves], sh_m[kWaves];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -333,7 +399,7 @@ __global__ __launch_bounds__(kThreads) void k_stats(Params P) {
     const int64_t k0 = static_cast<int64_t>(chunk) * P.cv;
     const int64_t k1 = k0 + P.cv < g.nvec ? k0 + P.cv : g.nvec;
     float m_run = -SV_INF, o_run = -SV_INF, s_run = 0.f;
-    stats_chunk<DT, kStatsUnroll>(row, P.V, k0, k1, P.c_hi, P.c_lo, m_run, o_run, s_run);
+    stats_chunk<DT, U>(row, P.V, k0, k1, P.c_hi, P.c_lo, m_run, o_run, s_run);
 
     // Workgroup combine: exact power-of-two rescaling to the largest offset.
     const float Ow = wave_max(o_run);
@@ -790,6 +856,10 @@ __device__ __forceinline__ void eval_run(const uint8_t* rowT, const uint8_t* row
     float lt[kResTile], ld[kResTile];
     load8<DT>(rowT, id0, nv, lt);
     if (resid) load8<DT>(rowD, id0, nv, ld);
+    else {
+#pragma unroll
+        for (int i = 0; i < kResTile; ++i) ld[i] = -SV_INF;
+    }
 #pragma unroll
     for (int i = 0; i < kResTile; ++i) {
         float pt = tempexp(lt[i], c_hi, c_lo, rp.oT) * invT;
@@ -824,24 +894,25 @@ __global__ __launch_bounds__(kThreads) void k_resample(Params P) {
     const uint8_t* rowD = resid ? row_ptr<DT>(P, false, b, rp.n) : nullptr;
     const float invT = static_cast<float>(1.0 / rp.keptT);
     const float invD = resid ? static_cast<float>(1.0 / rp.keptD) : 0.f;
-    const int64_t i0 = static_cast<int64_t>(c) * P.ce2;
-    const int64_t i1 = min<int64_t>(i0 + P.ce2, P.V);
-    const int64_t tile = static_cast<int64_t>(kThreads) * kResTile;
+    const int64_t i0 = static_cast<int64_t>(c) * kResChunk;
+    const int64_t i1 = min<int64_t>(i0 + kResChunk, P.V);
+    constexpr int64_t tile = static_cast<int64_t>(kThreads) * kResTile;
 
     double aw = 0.0, ap = 0.0;
-    for (int64_t t0 = i0; t0 < i1; t0 += tile) {
-        const int64_t id0 = t0 + static_cast<int64_t>(tid) * kResTile;
-        const int nv = static_cast<int>(min<int64_t>(max<int64_t>(i1 - id0, 0), kResTile));
-        if (nv > 0) {
-            float w[kResTile], p[kResTile];
-            eval_run<DT, TOPP>(rowT, rowD, resid, id0, nv, rp, P.c_hi, P.c_lo, invT, invD, w, p);
+    float w[kResTiles][kResTile], p[kResTiles][kResTile];
 #pragma unroll
-            for (int i = 0; i < kResTile; ++i) {
-                aw += static_cast<double>(w[i]);
-                ap += static_cast<double>(p[i]);
-            }
-        }
+    for (int t = 0; t < kResTiles; ++t) {
+        const int64_t id0 = i0 + t * tile + static_cast<int64_t>(tid) * kResTile;
+        const int nv = static_cast<int>(min<int64_t>(max<int64_t>(i1 - id0, 0), kResTile));
+        eval_run<DT, TOPP>(rowT, rowD, resid, id0, nv, rp, P.c_hi, P.c_lo, invT, invD, w[t], p[t]);
     }
+#pragma unroll
+    for (int t = 0; t < kResTiles; ++t)
+#pragma unroll
+        for (int i = 0; i < kResTile; ++i) {
+            aw += static_cast<double>(w[t][i]);
+            ap += static_cast<double>(p[t][i]);
+        }
     aw = wave_sum(aw);
     ap = wave_sum(ap);
     if (lane == 0) {
@@ -864,8 +935,8 @@ __global__ __launch_bounds__(kThreads) void k_resample(Params P) {
 // Per row: the chunk holding t = u*Z, then a rescan of that chunk in id order.
 template <int DT, bool TOPP>
 __global__ __launch_bounds__(kThreads) void k_pick(Params P) {
-    __shared__ int s_sel, s_chunk, s_y;
-    __shared__ double s_t, s_Z, s_pre;
+    __shared__ int s_y;
+    __shared__ double s_pre_first[kThreads], s_pre_last[kThreads];
     const int tid = threadIdx.x;
     const int b = blockIdx.x;
     const RowParam rp = P.rowp[b];
@@ -876,110 +947,162 @@ __global__ __launch_bounds__(kThreads) void k_pick(Params P) {
     const uint8_t* rowD = resid ? row_ptr<DT>(P, false, b, rp.n) : nullptr;
     const float invT = static_cast<float>(1.0 / rp.keptT);
     const float invD = resid ? static_cast<float>(1.0 / rp.keptD) : 0.f;
-    const int64_t tile = static_cast<int64_t>(kThreads) * kResTile;
-    if (tid == 0) {
-        const double* cm = P.cmass + static_cast<size_t>(b) * P.nch2 * 2;
-        int sel = 0;
-        double Z = 0.0;
-        for (int k = 0; k < P.nch2; ++k) Z += cm[2 * k];
-        if (!(Z > 0.0)) {
-            // A rejection implies p(x) < q(x), hence positive residual mass;
-            // none survives only through rounding: draw from p' instead.
-            sel = 1;
-            Z = 0.0;
-            for (int k = 0; k < P.nch2; ++k) Z += cm[2 * k + 1];
-        }
-        const double t = rp.u * Z;
-        double pre = 0.0, cpre = 0.0, lpre = 0.0;
-        int ch = -1, last = -1;
-        for (int k = 0; k < P.nch2; ++k) {
-            const double m = cm[2 * k + sel];
-            if (m > 0.0) {
-                if (ch < 0 && pre + m > t) {
-                    ch = k;
-                    cpre = pre;
-                }
-                last = k;
-                lpre = pre;
-            }
-            pre += m;
-        }
-        if (ch < 0) {
-            ch = last < 0 ? 0 : last;
-            cpre = last < 0 ? 0.0 : lpre;
-        }
-        s_sel = sel;
-        s_chunk = ch;
-        s_pre = cpre;
-        s_t = t;
-        s_Z = Z;
-        s_y = -1;
+
+    // Chunk masses: thread t owns chunks [t*g, t*g + g), summed in order; a
+    // block scan gives each thread its prefix.
+    const double* cm = P.cmass + static_cast<size_t>(b) * P.nch2 * 2;
+    const int g = (P.nch2 + kThreads - 1) / kThreads;
+    const int c0 = min(tid * g, P.nch2), c1 = min(c0 + g, P.nch2);
+    double wsum = 0.0, psum = 0.0;
+    for (int k = c0; k < c1; ++k) {
+        wsum += cm[2 * k];
+        psum += cm[2 * k + 1];
     }
+    double incl, excl, Z;
+    block_scan(wsum, incl, excl, Z);
+    int sel = 0;
+    if (!(Z > 0.0)) {
+        // A rejection implies p(x) < q(x), hence positive residual mass;
+        // none survives only through rounding: draw from p' instead.
+        sel = 1;
+        block_scan(psum, incl, excl, Z);
+    }
+    const double t = rp.u * Z;
+    int first = 0x7FFFFFFF, lastnz = -1;
+    double pre = excl, pf = 0.0, pl = 0.0;
+    for (int k = c0; k < c1; ++k) {
+        const double m = cm[2 * k + sel];
+        if (m > 0.0) {
+            if (first == 0x7FFFFFFF && pre + m > t) {
+                first = k;
+                pf = pre;
+            }
+            lastnz = k;
+            pl = pre;
+        }
+        pre += m;
+    }
+    s_pre_first[tid] = pf;
+    s_pre_last[tid] = pl;
+    const int fc = block_min_int(first);
+    const int lc = block_max_int(lastnz);
+    int ch;
+    double cpre;
+    if (fc != 0x7FFFFFFF) {
+        ch = fc;
+        cpre = s_pre_first[fc / g];
+    } else {
+        ch = lc < 0 ? 0 : lc;
+        cpre = lc < 0 ? 0.0 : s_pre_last[lc / g];
+    }
+    if (tid == 0) s_y = -1;
     __syncthreads();
+
     // Rescan the chosen chunk in id order: tile by tile, a prefix sum over
     // threads (each thread owns kResTile consecutive ids), then one thread
-    // walks its run.
-    const int sel = s_sel;
-    const double t = s_t;
-    const int64_t j0 = static_cast<int64_t>(s_chunk) * P.ce2;
-    const int64_t j1 = min<int64_t>(j0 + P.ce2, P.V);
-    double carry = s_pre;
-    int lastpos = -1;
-    for (int64_t t0 = j0; t0 < j1; t0 += tile) {
-        const int64_t id0 = t0 + static_cast<int64_t>(tid) * kResTile;
-        const int nv = static_cast<int>(min<int64_t>(max<int64_t>(j1 - id0, 0), kResTile));
-        float w[kResTile], p[kResTile];
-        double xs = 0.0;
-        if (nv > 0) {
-            eval_run<DT, TOPP>(rowT, rowD, resid, id0, nv, rp, P.c_hi, P.c_lo, invT, invD, w, p);
+    // walks its run.  Both tiles are loaded before the scans.
+    constexpr int64_t tile = static_cast<int64_t>(kThreads) * kResTile;
+    const int64_t j0 = static_cast<int64_t>(ch) * kResChunk;
+    const int64_t j1 = min<int64_t>(j0 + kResChunk, P.V);
+    float w[kResTiles][kResTile], p[kResTiles][kResTile];
+    int nvs[kResTiles];
 #pragma unroll
-            for (int i = 0; i < kResTile; ++i) {
-                const float v = sel ? p[i] : w[i];
-                w[i] = v;
-                xs += static_cast<double>(v);
-                if (v > 0.f) lastpos = static_cast<int>(id0 + i);
-            }
+    for (int tt = 0; tt < kResTiles; ++tt) {
+        const int64_t id0 = j0 + tt * tile + static_cast<int64_t>(tid) * kResTile;
+        nvs[tt] = static_cast<int>(min<int64_t>(max<int64_t>(j1 - id0, 0), kResTile));
+        eval_run<DT, TOPP>(rowT, rowD, resid, id0, nvs[tt], rp, P.c_hi, P.c_lo, invT, invD, w[tt], p[tt]);
+    }
+    double carry = cpre;
+    int lastpos = -1;
+    for (int tt = 0; tt < kResTiles; ++tt) {
+        const int64_t id0 = j0 + tt * tile + static_cast<int64_t>(tid) * kResTile;
+        float v[kResTile];
+        double xs = 0.0;
+#pragma unroll
+        for (int i = 0; i < kResTile; ++i) {
+            v[i] = sel ? p[tt][i] : w[tt][i];
+            xs += static_cast<double>(v[i]);
+            if (v[i] > 0.f) lastpos = static_cast<int>(id0 + i);
         }
-        double incl, excl, total;
-        block_scan(xs, incl, excl, total);
-        const int hit = (xs > 0.0 && carry + incl > t) ? tid : 0x7FFFFFFF;
-        const int first = block_min_int(hit);
-        if (first != 0x7FFFFFFF) {
-            if (tid == first) {
-                double run = carry + excl;
+        double ti, te, tot;
+        block_scan(xs, ti, te, tot);
+        const int hit = (xs > 0.0 && carry + ti > t) ? tid : 0x7FFFFFFF;
+        const int fh = block_min_int(hit);
+        if (fh != 0x7FFFFFFF) {
+            if (tid == fh) {
+                double run = carry + te;
                 int y = -1, lastw = -1;
-                for (int i = 0; i < nv; ++i) {
-                    if (w[i] > 0.f) {
+                for (int i = 0; i < nvs[tt]; ++i) {
+                    if (v[i] > 0.f) {
                         lastw = static_cast<int>(id0 + i);
-                        if (y < 0 && run + static_cast<double>(w[i]) > t) y = lastw;
+                        if (y < 0 && run + static_cast<double>(v[i]) > t) y = lastw;
                     }
-                    run += static_cast<double>(w[i]);
+                    run += static_cast<double>(v[i]);
                 }
                 s_y = y >= 0 ? y : lastw;
             }
             __syncthreads();
             break;
         }
-        carry += total;
+        carry += tot;
     }
     const int lp = block_max_int(lastpos);
     if (tid == 0) {
         const int y = s_y >= 0 ? s_y : (lp >= 0 ? lp : 0);
         P.out_tokens[static_cast<size_t>(b) * (P.K + 1) + rp.n] = y;
         if (P.probe_row) {
-            P.probe_row[static_cast<size_t>(b) * 4 + 0] = s_Z;
+            P.probe_row[static_cast<size_t>(b) * 4 + 0] = Z;
             P.probe_row[static_cast<size_t>(b) * 4 + 1] = t;
         }
     }
 }
 
 // ---------------------------------------------------------------------------
+// Streaming-read calibration: every 16-byte vector of a buffer read once with
+// the statistics pass's access pattern (one workgroup per kThreads*U
+// vectors), folded into an xor that is stored only if it matches a value it
+// practically never takes -- enough to keep the loads alive.
+// ---------------------------------------------------------------------------
+template <int U>
+__global__ __launch_bounds__(kThreads) void k_stream_read(const uint4* p, int64_t n16, uint32_t* sink) {
+    const int64_t base = static_cast<int64_t>(blockIdx.x) * kThreads * U;
+    uint4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int64_t k = base + u * kThreads + threadIdx.x;
+        v[u] = k < n16 ? gload16(p + k) : make_uint4(0u, 0u, 0u, 0u);
+    }
+    uint32_t acc = 0u;
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    if (acc == 0x9E3779B9u) sink[blockIdx.x & 1023] = acc;
+}
+
+hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int unroll, hipStream_t s) {
+    const int64_t n16 = bytes / 16;
+    const int64_t per = static_cast<int64_t>(kThreads) * unroll;
+    const unsigned grid = static_cast<unsigned>((n16 + per - 1) / per);
+    const uint4* p = static_cast<const uint4*>(buf);
+    if (unroll == 8) hipLaunchKernelGGL((k_stream_read<8>), dim3(grid), dim3(kThreads), 0, s, p, n16, sink);
+    else if (unroll == 2) hipLaunchKernelGGL((k_stream_read<2>), dim3(grid), dim3(kThreads), 0, s, p, n16, sink);
+    else hipLaunchKernelGGL((k_stream_read<4>), dim3(grid), dim3(kThreads), 0, s, p, n16, sink);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Launchers.
 // ---------------------------------------------------------------------------
-hipError_t launch_stats(const Params& p, int dtype, hipStream_t s) {
+hipError_t launch_stats(const Params& p, int dtype, int unroll, hipStream_t s) {
     const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(p.B) * p.nslot * p.nch);
-    if (dtype == DT_BF16) hipLaunchKernelGGL((k_stats<DT_BF16>), dim3(grid), dim3(kThreads), 0, s, p);
-    else hipLaunchKernelGGL((k_stats<DT_F32>), dim3(grid), dim3(kThreads), 0, s, p);
+    if (dtype == DT_BF16) {
+        if (unroll == 8) hipLaunchKernelGGL((k_stats<DT_BF16, 8>), dim3(grid), dim3(kThreads), 0, s, p);
+        else if (unroll == 2) hipLaunchKernelGGL((k_stats<DT_BF16, 2>), dim3(grid), dim3(kThreads), 0, s, p);
+        else hipLaunchKernelGGL((k_stats<DT_BF16, 4>), dim3(grid), dim3(kThreads), 0, s, p);
+    } else {
+        if (unroll == 8) hipLaunchKernelGGL((k_stats<DT_F32, 8>), dim3(grid), dim3(kThreads), 0, s, p);
+        else if (unroll == 2) hipLaunchKernelGGL((k_stats<DT_F32, 2>), dim3(grid), dim3(kThreads), 0, s, p);
+        else hipLaunchKernelGGL((k_stats<DT_F32, 4>), dim3(grid), dim3(kThreads), 0, s, p);
+    }
     return hipGetLastError();
 }
 

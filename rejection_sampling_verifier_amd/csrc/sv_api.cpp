@@ -70,6 +70,24 @@ int env_int(const char* name, int dflt) {
 
 bool misaligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) != 0; }
 
+// Resident statistics workgroups on the current device: CUs times the
+// kernel's occupancy (cached per device, dtype and unroll).
+int stats_resident(int dtype, int unroll) {
+    static std::mutex mu;
+    static std::map<std::pair<int, int>, int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    const std::pair<int, int> key{dev, dtype * 16 + unroll};
+    std::lock_guard<std::mutex> lk(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    const int n = cus * sv::stats_occupancy(dtype, unroll);
+    cache[key] = n;
+    return n;
+}
+
 int check_logits(const sv_logits* t) {
     if (!t || !t->data) return SV_EINVAL;
     if (t->dtype != SV_F32 && t->dtype != SV_BF16) return SV_EDTYPE;
@@ -160,11 +178,9 @@ int verify_impl(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_t
     const int64_t nvec_max = (static_cast<int64_t>(V) * E + 15) / 16 + 1;
     int unroll = env_int("SPECVERIFY_STATS_UNROLL", sv::kStatsUnroll);
     if (unroll != 2 && unroll != 8) unroll = 4;
-    // chunks are whole steps of kThreads*unroll vectors; only a row's last
-    // chunk is partial
-    const int step = sv::kThreads * unroll;
-    int cv = env_int("SPECVERIFY_STATS_VECS", step);
-    cv = ((cv < step ? step : cv) + step - 1) / step * step;
+    // an item of the persistent statistics pass is one step of
+    // kThreads*unroll vectors; only a row's last chunk is partial
+    const int cv = sv::kThreads * unroll;
     const int64_t nch64 = (nvec_max + cv - 1) / cv;
     const int nch = static_cast<int>(nch64);
     // resample pass: chunks of kResChunk ids
@@ -198,6 +214,13 @@ int verify_impl(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_t
     p.nslot = nslot;
     p.nch = nch;
     p.cv = cv;
+    {
+        const int64_t items = static_cast<int64_t>(B) * nslot * nch;
+        int64_t grid = stats_resident(dtype, unroll);
+        const int wpc = env_int("SPECVERIFY_STATS_WG", 0);  // tuning override: total workgroups
+        if (wpc > 0) grid = wpc;
+        p.stats_grid = static_cast<int>(items < grid ? items : grid);
+    }
     p.nch2 = nch2;
     // c = c_hi + c_lo with c_hi <= c rounded toward zero, so c_lo > 0.
     float c_hi = static_cast<float>(c);

@@ -21,10 +21,14 @@ enum RowMode : int { MODE_SKIP = 0, MODE_RESID = 1, MODE_BONUS = 2 };
 enum KernelKind : int { KK_STATS = 0, KK_TOPP = 1, KK_RESAMPLE = 2, KK_PICK = 3, KK_COUNT = 4 };
 
 // Statistics of one chunk of one logit row, relative to an integer offset o:
-// s = sum over the chunk of 2^(l*c - o), c = log2(e)/T; m = max logit.
+// s = sum over the chunk of 2^(l*c - o), c = log2(e)/T; m = max logit; lx =
+// the logit at the row's drafted id when that id falls in the chunk, else
+// -inf.
 struct Partial {
     float o;
     float m;
+    float lx;
+    float pad;
     double s;
 };
 
@@ -35,6 +39,8 @@ struct Partial {
 struct RvState {
     float o;
     float m;
+    float lx;
+    float pad0;
     double s;
     double kept;
     uint32_t tau;
@@ -66,6 +72,7 @@ struct Params {
     double* probe_row;            // [B, 4] or null
     int B, K, V, nslot;
     int nch, cv;                  // statistics pass: chunks per row, 16-byte vectors per chunk
+    int stats_grid;               // persistent statistics workgroups
     int nch2;                     // resample pass: chunks of kResChunk ids per row
     float c_hi, c_lo;             // c = log2(e)/T = c_hi + c_lo, c_lo > 0
     double c64;                   // (double)c_hi + (double)c_lo
@@ -79,6 +86,7 @@ struct Params {
 
 // Launchers (defined in sv_kernels.hip).
 hipError_t launch_stats(const Params& p, int dtype, int unroll, hipStream_t s);
+int stats_occupancy(int dtype, int unroll);
 hipError_t launch_topp(const Params& p, int dtype, hipStream_t s);
 hipError_t launch_resample(const Params& p, int dtype, bool topp, hipStream_t s);
 hipError_t launch_pick(const Params& p, int dtype, bool topp, hipStream_t s);

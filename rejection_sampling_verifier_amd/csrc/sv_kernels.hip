@@ -88,6 +88,7 @@ __device__ __forceinline__ void mask_edge(float* f, int64_t k, int head, int V) 
 struct RowShared {
     float o[kMaxSlots];
     float m[kMaxSlots];
+    float lx[kMaxSlots];
     double s[kMaxSlots];
     double kept[kMaxSlots];
     uint32_t tau[kMaxSlots];
@@ -108,16 +109,19 @@ __device__ __forceinline__ int rv_slot(int r, int Le, int K) { return r <= Le ? 
 
 // Combines the chunk partials of logit row `slot` of batch row b (one wave).
 __device__ __forceinline__ void combine_partials(const Params& P, int b, int slot, int lane, float& O, float& M,
-                                                 double& S) {
+                                                 float& LX, double& S) {
     const Partial* pp = P.part + (static_cast<size_t>(b) * P.nslot + slot) * P.nch;
     O = -SV_INF;
     M = -SV_INF;
+    LX = -SV_INF;
     for (int c = lane; c < P.nch; c += 64) {
         O = fmaxf(O, pp[c].o);
         M = fmaxf(M, pp[c].m);
+        LX = fmaxf(LX, pp[c].lx);
     }
     O = wave_max(O);
     M = wave_max(M);
+    LX = wave_max(LX);
     S = 0.0;
     for (int c = lane; c < P.nch; c += 64) {
         const Partial q = pp[c];
@@ -148,22 +152,16 @@ __device__ void row_decide(const Params& P, int b, RowShared& R, bool write_outp
     bool rowok;
     const int Le = row_len(P, b, rowok);
     const int nrv = 2 * Le + 1;
-    // Lanes j < Le of wave 0 start their dependent loads first (drafted id,
-    // then the two logits at it) so they overlap the statistics loads.
+    // Drafted ids (range check, tie cut); their logits come with the
+    // statistics (lx), so every load here is independent of every other.
     int x = -1;
-    float lt = 0.f, ld = 0.f;
-    if (tid < Le) {
-        x = P.tokens[static_cast<int64_t>(b) * K + tid];
-        if (x >= 0 && x < P.V) {
-            lt = load_elem<DT>(row_ptr<DT>(P, true, b, tid), x);
-            ld = load_elem<DT>(row_ptr<DT>(P, false, b, tid), x);
-        }
-    }
+    if (tid < Le) x = P.tokens[static_cast<int64_t>(b) * K + tid];
     if (TOPP) {
         for (int r = tid; r < nrv; r += kThreads) {
             const RvState q = P.rv[static_cast<size_t>(b) * P.nslot + rv_slot(r, Le, K)];
             R.o[r] = q.o;
             R.m[r] = q.m;
+            R.lx[r] = q.lx;
             R.s[r] = q.s;
             R.kept[r] = q.kept;
             R.tau[r] = q.tau;
@@ -175,7 +173,7 @@ __device__ void row_decide(const Params& P, int b, RowShared& R, bool write_outp
         int G = 64;
         while (G > 1 && G * nrv > kThreads) G >>= 1;
         const int r = tid / G, gl = tid - (tid / G) * G;
-        float O = -SV_INF, M = -SV_INF;
+        float O = -SV_INF, M = -SV_INF, LX = -SV_INF;
         double S = 0.0;
         if (r < nrv) {
             const Partial* pp = P.part + (static_cast<size_t>(b) * P.nslot + rv_slot(r, Le, K)) * P.nch;
@@ -185,20 +183,24 @@ __device__ void row_decide(const Params& P, int b, RowShared& R, bool write_outp
                 S = merge_stats(O, S, q.o, q.s, On);
                 O = On;
                 M = fmaxf(M, q.m);
+                LX = fmaxf(LX, q.lx);
             }
         }
         for (int off = G >> 1; off >= 1; off >>= 1) {
             const float O2 = __shfl_xor(O, off, 64);
             const double S2 = __shfl_xor(S, off, 64);
             const float M2 = __shfl_xor(M, off, 64);
+            const float L2 = __shfl_xor(LX, off, 64);
             float On;
             S = merge_stats(O, S, O2, S2, On);
             O = On;
             M = fmaxf(M, M2);
+            LX = fmaxf(LX, L2);
         }
         if (r < nrv && gl == 0) {
             R.o[r] = O;
             R.m[r] = M;
+            R.lx[r] = LX;
             R.s[r] = S;
             R.kept[r] = S;
             R.tau[r] = 0u;
@@ -223,6 +225,7 @@ __device__ void row_decide(const Params& P, int b, RowShared& R, bool write_outp
                     bad_tok = 1;
                 } else {
                     const int rT = lane, rD = Le + 1 + lane;
+                    const float lt = R.lx[rT], ld = R.lx[rD];
                     double pt = exp2(static_cast<double>(lt) * P.c64 - static_cast<double>(R.o[rT])) / R.kept[rT];
                     double qd = exp2(static_cast<double>(ld) * P.c64 - static_cast<double>(R.o[rD])) / R.kept[rD];
                     if (TOPP) {
@@ -306,32 +309,85 @@ __device__ void row_decide(const Params& P, int b, RowShared& R, bool write_outp
 // ---------------------------------------------------------------------------
 // Statistics pass.
 // ---------------------------------------------------------------------------
-// One step of the statistics pass: U 16-byte vectors per lane, all loads
-// issued before any use.  EDGE handles a step that touches the row's first or
-// last vector or the end of the chunk (guarded loads, masked ids).
-template <int DT, int U, bool EDGE>
-__device__ __forceinline__ void stats_step(const RowGrid& g, int64_t kb, int64_t k1, int V, float c_hi, float c_lo,
-                                           float& m_run, float& o_run, float& s_run) {
-    constexpr int VE = Fmt<DT>::VE;
-    constexpr int N = U * VE;
-    uint4 raw[U];
+// One item of the statistics pass is one chunk of one logit row: kThreads*U
+// 16-byte vectors, U per lane.
+struct StatsItem {
+    RowGrid g;
+    int64_t k0, k1;     // vector range of the chunk
+    int rvi, chunk, b, j;
+    bool tgt, drafted;  // drafted: the position has a drafted id (j < L_b)
+};
+
+__device__ __forceinline__ bool stats_needed(const Params& P, int it) {
+    const int rvi = it / P.nch;
+    const int b = rvi / P.nslot;
+    const int slot = rvi - b * P.nslot;
+    bool ok;
+    const int Le = row_len(P, b, ok);
+    const bool tgt = slot <= P.K;
+    const int j = tgt ? slot : slot - P.K - 1;
+    return tgt ? (j <= Le) : (j < Le);
+}
+// First item at or after `it` (stepping by the grid) that some row needs.
+__device__ __forceinline__ int next_item(const Params& P, int it, int total) {
+    while (it < total && !stats_needed(P, it)) it += P.stats_grid;
+    return it;
+}
+template <int DT>
+__device__ __forceinline__ StatsItem decode_item(const Params& P, int it) {
+    StatsItem t;
+    t.rvi = it / P.nch;
+    t.chunk = it - t.rvi * P.nch;
+    t.b = t.rvi / P.nslot;
+    const int slot = t.rvi - t.b * P.nslot;
+    bool ok;
+    const int Le = row_len(P, t.b, ok);
+    t.tgt = slot <= P.K;
+    t.j = t.tgt ? slot : slot - P.K - 1;
+    t.drafted = t.j < Le;
+    t.g = row_grid<DT>(row_ptr<DT>(P, t.tgt, t.b, t.j), P.V);
+    t.k0 = static_cast<int64_t>(t.chunk) * P.cv;
+    t.k1 = t.k0 + P.cv < t.g.nvec ? t.k0 + P.cv : t.g.nvec;
+    return t;
+}
+
+template <int DT, int U>
+__device__ __forceinline__ void issue_loads(const StatsItem& t, uint4* raw) {
+    constexpr int64_t STEP = static_cast<int64_t>(kThreads) * U;
+    if (t.k0 + STEP <= t.k1) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int64_t k = kb + u * kThreads + threadIdx.x;
-        if (EDGE) {
-            const uint32_t ni = Fmt<DT>::NEG_INF_WORD;
-            raw[u] = (k < k1) ? gload16(g.vp + k) : make_uint4(ni, ni, ni, ni);
-        } else {
-            raw[u] = gload16(g.vp + k);
+        for (int u = 0; u < U; ++u) raw[u] = gload16(t.g.vp + t.k0 + u * kThreads + threadIdx.x);
+    } else {
+        const uint32_t ni = Fmt<DT>::NEG_INF_WORD;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t k = t.k0 + u * kThreads + threadIdx.x;
+            raw[u] = (k < t.k1) ? gload16(t.g.vp + k) : make_uint4(ni, ni, ni, ni);
         }
     }
+}
+
+// (max, offset, sum) of one lane's U vectors; MASK handles the row's first
+// and last vector.
+// The lane holding vector kx copies element rx of it into *lx_out.
+template <int DT, int U, bool MASK>
+__device__ __forceinline__ void reduce_lane(const StatsItem& t, const uint4* raw, int V, float c_hi, float c_lo,
+                                            int64_t kx, int rx, float* lx_out, float& m, float& o, float& s) {
+    constexpr int VE = Fmt<DT>::VE;
+    constexpr int N = U * VE;
     float f[N];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         unpack<DT>(raw[u], f + u * VE);
-        if (EDGE) {
-            const int64_t k = kb + u * kThreads + threadIdx.x;
-            if (k < k1 && (k == 0 || k == g.nvec - 1)) mask_edge<DT>(f + u * VE, k, g.head, V);
+        const int64_t k = t.k0 + u * kThreads + threadIdx.x;
+        if (MASK) {
+            if (k < t.k1 && (k == 0 || k == t.g.nvec - 1)) mask_edge<DT>(f + u * VE, k, t.g.head, V);
+        }
+        if (k == kx) {
+            float v = -SV_INF;
+#pragma unroll
+            for (int i = 0; i < VE; ++i) v = (i == rx) ? f[u * VE + i] : v;
+            *lx_out = v;
         }
     }
     // N is a multiple of 4: a v_max3 tree
@@ -339,13 +395,9 @@ __device__ __forceinline__ void stats_step(const RowGrid& g, int64_t kb, int64_t
 #pragma unroll
     for (int i = 3; i + 1 < N; i += 2) bm = max3f(bm, f[i], f[i + 1]);
     bm = fmaxf(bm, f[N - 1]);
-    m_run = fmaxf(m_run, bm);
-    const float ob = ceilf(bm * c_hi);
-    if (ob > o_run) {
-        if (o_run != -SV_INF) s_run = ldexpf(s_run, static_cast<int>(fmaxf(o_run - ob, -256.f)));
-        o_run = ob;
-    }
-    const float off = (o_run == -SV_INF) ? 0.f : o_run;
+    m = bm;
+    o = ceilf(bm * c_hi);
+    const float off = (o == -SV_INF) ? 0.f : o;
     float acc[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -362,71 +414,94 @@ __device__ __forceinline__ void stats_step(const RowGrid& g, int64_t kb, int64_t
     for (int w = U / 2; w >= 1; w >>= 1)
 #pragma unroll
         for (int i = 0; i < w; ++i) acc[i] += acc[i + w];
-    s_run += acc[0];
+    s = acc[0];
 }
 
-template <int DT, int U>
-__device__ __forceinline__ void stats_chunk(const uint8_t* row, int V, int64_t k0, int64_t k1, float c_hi,
-                                            float c_lo, float& m_run, float& o_run, float& s_run) {
-    const RowGrid g = row_grid<DT>(row, V);
-    constexpr int64_t STEP = static_cast<int64_t>(kThreads) * U;
-    for (int64_t kb = k0; kb < k1; kb += STEP) {
-        // uniform across the workgroup: whole step inside the chunk and away
-        // from the row's first and last vector
-        const bool inner = kb >= 1 && kb + STEP <= k1 && kb + STEP <= g.nvec - 1;
-        if (inner) stats_step<DT, U, false>(g, kb, k1, V, c_hi, c_lo, m_run, o_run, s_run);
-        else stats_step<DT, U, true>(g, kb, k1, V, c_hi, c_lo, m_run, o_run, s_run);
-    }
-}
-
+// Statistics pass, persistent: workgroup w takes items w, w + grid, ... and
+// issues the next item's loads before reducing the current one, so that HBM
+// requests stay in flight while the VALU works.
 template <int DT, int U>
 __global__ __launch_bounds__(kThreads) void k_stats(Params P) {
-    __shared__ float sh_o[kWaves], sh_s[kWaves], sh_m[kWaves];
+    __shared__ float sh_o[2][kWaves], sh_s[2][kWaves], sh_m[2][kWaves], sh_lx[2];
+    __shared__ int sh_tag[2];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int item = blockIdx.x;
-    const int rvi = item / P.nch;
-    const int chunk = item - rvi * P.nch;
-    const int b = rvi / P.nslot;
-    const int slot = rvi - b * P.nslot;
-    bool rowok;
-    const int Le = row_len(P, b, rowok);
-    const bool tgt = slot <= P.K;
-    const int j = tgt ? slot : slot - P.K - 1;
-    if (tgt ? (j > Le) : (j >= Le)) return;  // padded position: never read
-
-    const uint8_t* row = row_ptr<DT>(P, tgt, b, j);
-    const RowGrid g = row_grid<DT>(row, P.V);
-    const int64_t k0 = static_cast<int64_t>(chunk) * P.cv;
-    const int64_t k1 = k0 + P.cv < g.nvec ? k0 + P.cv : g.nvec;
-    float m_run = -SV_INF, o_run = -SV_INF, s_run = 0.f;
-    stats_chunk<DT, U>(row, P.V, k0, k1, P.c_hi, P.c_lo, m_run, o_run, s_run);
-
-    // Workgroup combine: exact power-of-two rescaling to the largest offset.
-    const float Ow = wave_max(o_run);
-    const float sc = (o_run == -SV_INF) ? s_run : ldexpf(s_run, static_cast<int>(fmaxf(o_run - Ow, -256.f)));
-    const float Sw = wave_sum(sc);
-    const float Mw = wave_max(m_run);
-    if (lane == 0) {
-        sh_o[wv] = Ow;
-        sh_s[wv] = Sw;
-        sh_m[wv] = Mw;
-    }
+    const int total = P.B * P.nslot * P.nch;
+    int it = next_item(P, blockIdx.x, total);
+    if (it >= total) return;
+    if (tid < 2) sh_tag[tid] = -1;
     __syncthreads();
-    if (tid == 0) {
-        float O = sh_o[0], M = sh_m[0];
-        for (int w = 1; w < kWaves; ++w) {
-            O = fmaxf(O, sh_o[w]);
-            M = fmaxf(M, sh_m[w]);
+    StatsItem cur = decode_item<DT>(P, it);
+    uint4 raw[U];
+    issue_loads<DT, U>(cur, raw);
+    for (int parity = 0;; parity ^= 1) {
+        const int itn = next_item(P, it + P.stats_grid, total);
+        StatsItem nxt;
+        uint4 rawn[U];
+        if (itn < total) {
+            nxt = decode_item<DT>(P, itn);
+            issue_loads<DT, U>(nxt, rawn);
         }
-        double S = 0.0;
-        for (int w = 0; w < kWaves; ++w)
-            S += (sh_o[w] == -SV_INF) ? static_cast<double>(sh_s[w])
-                                      : ldexp(static_cast<double>(sh_s[w]), static_cast<int>(fmaxf(sh_o[w] - O, -1100.f)));
-        Partial pr;
-        pr.o = O;
-        pr.m = M;
-        pr.s = S;
-        P.part[static_cast<size_t>(rvi) * P.nch + chunk] = pr;
+        // drafted id of this logit row (uniform): the lane holding its vector
+        // records the logit there (tagged with the item)
+        int64_t kx = -1;
+        int rx = 0;
+        if (cur.drafted) {
+            const int x = P.tokens[static_cast<int64_t>(cur.b) * P.K + cur.j];
+            if (x >= 0 && x < P.V) {
+                kx = (static_cast<int64_t>(x) + cur.g.head) / Fmt<DT>::VE;
+                rx = static_cast<int>((static_cast<int64_t>(x) + cur.g.head) - kx * Fmt<DT>::VE);
+            }
+        }
+        float lxv = -SV_INF;
+        float m, o, sl;
+        const bool edge = cur.k0 == 0 || cur.k0 + static_cast<int64_t>(kThreads) * U >= cur.g.nvec - 1;
+        if (edge) reduce_lane<DT, U, true>(cur, raw, P.V, P.c_hi, P.c_lo, kx, rx, &lxv, m, o, sl);
+        else reduce_lane<DT, U, false>(cur, raw, P.V, P.c_hi, P.c_lo, kx, rx, &lxv, m, o, sl);
+        {
+            const int64_t rel = kx - cur.k0 - threadIdx.x;
+            if (kx >= cur.k0 && rel >= 0 && rel % kThreads == 0 && rel / kThreads < U) {
+                sh_lx[parity] = lxv;
+                sh_tag[parity] = it;
+            }
+        }
+
+        // workgroup combine: exact power-of-two rescaling to the largest offset
+        const float Ow = wave_max(o);
+        const float sc = (o == -SV_INF) ? sl : ldexpf(sl, static_cast<int>(fmaxf(o - Ow, -256.f)));
+        const float Sw = wave_sum(sc);
+        const float Mw = wave_max(m);
+        if (lane == 0) {
+            sh_o[parity][wv] = Ow;
+            sh_s[parity][wv] = Sw;
+            sh_m[parity][wv] = Mw;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            float O = sh_o[parity][0], M = sh_m[parity][0];
+            for (int w = 1; w < kWaves; ++w) {
+                O = fmaxf(O, sh_o[parity][w]);
+                M = fmaxf(M, sh_m[parity][w]);
+            }
+            double S = 0.0;
+            for (int w = 0; w < kWaves; ++w)
+                S += (sh_o[parity][w] == -SV_INF)
+                         ? static_cast<double>(sh_s[parity][w])
+                         : ldexp(static_cast<double>(sh_s[parity][w]),
+                                 static_cast<int>(fmaxf(sh_o[parity][w] - O, -1100.f)));
+            const float lx = (sh_tag[parity] == it) ? sh_lx[parity] : -SV_INF;
+            Partial pr;
+            pr.o = O;
+            pr.m = M;
+            pr.lx = lx;
+            pr.pad = 0.f;
+            pr.s = S;
+            P.part[static_cast<size_t>(cur.rvi) * P.nch + cur.chunk] = pr;
+        }
+        if (itn >= total) break;
+        cur = nxt;
+#pragma unroll
+        for (int u = 0; u < U; ++u) raw[u] = rawn[u];
+        it = itn;
     }
 }
 
@@ -800,7 +875,7 @@ __device__ void select_nucleus(const Params& P, const uint8_t* row, float O, dou
 template <int DT>
 __global__ __launch_bounds__(kThreads) void k_topp(Params P) {
     __shared__ SelShared sh;
-    __shared__ float s_o, s_m;
+    __shared__ float s_o, s_m, s_lx;
     __shared__ double s_s;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int rvi = blockIdx.x;
@@ -813,12 +888,13 @@ __global__ __launch_bounds__(kThreads) void k_topp(Params P) {
     if (tgt ? (j > Le) : (j >= Le)) return;
     const uint8_t* row = row_ptr<DT>(P, tgt, b, j);
     if (wv == 0) {
-        float O, M;
+        float O, M, LX;
         double S;
-        combine_partials(P, b, slot, lane, O, M, S);
+        combine_partials(P, b, slot, lane, O, M, LX, S);
         if (lane == 0) {
             s_o = O;
             s_m = M;
+            s_lx = LX;
             s_s = S;
         }
     }
@@ -828,6 +904,8 @@ __global__ __launch_bounds__(kThreads) void k_topp(Params P) {
     RvState st;
     st.o = O;
     st.m = s_m;
+    st.lx = s_lx;
+    st.pad0 = 0.f;
     st.s = S;
     st.kept = S;
     st.tau = 0u;
@@ -849,33 +927,68 @@ __global__ __launch_bounds__(kThreads) void k_topp(Params P) {
 // ---------------------------------------------------------------------------
 // Resample pass.
 // ---------------------------------------------------------------------------
+// Weights of one resample chunk [i0, i1) in id order: thread t owns ids
+// i0 + tt*tile + t*kResTile + [0, kResTile) for tiles tt.  w is the residual
+// max(0, p' - q') (or p' for the bonus), p is p'.  When the chunk is whole and
+// both rows are 16-byte aligned every load is issued before any use.
 template <int DT, bool TOPP>
-__device__ __forceinline__ void eval_run(const uint8_t* rowT, const uint8_t* rowD, bool resid, int64_t id0, int nv,
-                                         const RowParam& rp, float c_hi, float c_lo, float invT, float invD, float* w,
-                                         float* p) {
-    float lt[kResTile], ld[kResTile];
-    load8<DT>(rowT, id0, nv, lt);
-    if (resid) load8<DT>(rowD, id0, nv, ld);
-    else {
+__device__ __forceinline__ void eval_chunk(const uint8_t* rowT, const uint8_t* rowD, bool resid, int64_t i0,
+                                           int64_t i1, const RowParam& rp, float c_hi, float c_lo, float invT,
+                                           float invD, float (&w)[kResTiles][kResTile],
+                                           float (&p)[kResTiles][kResTile]) {
+    constexpr int E = Fmt<DT>::E, VE = Fmt<DT>::VE, NV = kResTile / VE;
+    constexpr int64_t tile = static_cast<int64_t>(kThreads) * kResTile;
+    float lt[kResTiles][kResTile], ld[kResTiles][kResTile];
+    const bool fast = (i1 - i0 == kResChunk) && ((reinterpret_cast<uintptr_t>(rowT + i0 * E) & 15) == 0) &&
+                      (!resid || (reinterpret_cast<uintptr_t>(rowD + i0 * E) & 15) == 0);
+    if (fast) {
+        uint4 vt[kResTiles][NV], vd[kResTiles][NV];
 #pragma unroll
-        for (int i = 0; i < kResTile; ++i) ld[i] = -SV_INF;
+        for (int tt = 0; tt < kResTiles; ++tt) {
+            const int64_t id0 = i0 + tt * tile + static_cast<int64_t>(threadIdx.x) * kResTile;
+#pragma unroll
+            for (int k = 0; k < NV; ++k) vt[tt][k] = gload16(reinterpret_cast<const uint4*>(rowT + id0 * E) + k);
+            if (resid) {
+#pragma unroll
+                for (int k = 0; k < NV; ++k) vd[tt][k] = gload16(reinterpret_cast<const uint4*>(rowD + id0 * E) + k);
+            }
+        }
+#pragma unroll
+        for (int tt = 0; tt < kResTiles; ++tt)
+#pragma unroll
+            for (int k = 0; k < NV; ++k) {
+                unpack<DT>(vt[tt][k], lt[tt] + k * VE);
+                if (resid) unpack<DT>(vd[tt][k], ld[tt] + k * VE);
+            }
+    } else {
+#pragma unroll
+        for (int tt = 0; tt < kResTiles; ++tt) {
+            const int64_t id0 = i0 + tt * tile + static_cast<int64_t>(threadIdx.x) * kResTile;
+            const int nv = static_cast<int>(min<int64_t>(max<int64_t>(i1 - id0, 0), kResTile));
+            load8<DT>(rowT, id0, nv, lt[tt]);
+            if (resid) load8<DT>(rowD, id0, nv, ld[tt]);
+        }
     }
 #pragma unroll
-    for (int i = 0; i < kResTile; ++i) {
-        float pt = tempexp(lt[i], c_hi, c_lo, rp.oT) * invT;
-        if (TOPP && !is_kept(order_key(lt[i]), id0 + i, rp.tauT, rp.cutT)) pt = 0.f;
-        float wi = pt;
-        if (resid) {
-            float qd = tempexp(ld[i], c_hi, c_lo, rp.oD) * invD;
-            if (TOPP && !is_kept(order_key(ld[i]), id0 + i, rp.tauD, rp.cutD)) qd = 0.f;
-            wi = fmaxf(pt - qd, 0.f);
+    for (int tt = 0; tt < kResTiles; ++tt) {
+        const int64_t id0 = i0 + tt * tile + static_cast<int64_t>(threadIdx.x) * kResTile;
+#pragma unroll
+        for (int i = 0; i < kResTile; ++i) {
+            float pt = tempexp(lt[tt][i], c_hi, c_lo, rp.oT) * invT;
+            if (TOPP && !is_kept(order_key(lt[tt][i]), id0 + i, rp.tauT, rp.cutT)) pt = 0.f;
+            float wi = pt;
+            if (resid) {
+                float qd = tempexp(ld[tt][i], c_hi, c_lo, rp.oD) * invD;
+                if (TOPP && !is_kept(order_key(ld[tt][i]), id0 + i, rp.tauD, rp.cutD)) qd = 0.f;
+                wi = fmaxf(pt - qd, 0.f);
+            }
+            if (id0 + i >= i1) {
+                pt = 0.f;
+                wi = 0.f;
+            }
+            w[tt][i] = wi;
+            p[tt][i] = pt;
         }
-        if (i >= nv) {
-            pt = 0.f;
-            wi = 0.f;
-        }
-        w[i] = wi;
-        p[i] = pt;
     }
 }
 
@@ -896,16 +1009,10 @@ __global__ __launch_bounds__(kThreads) void k_resample(Params P) {
     const float invD = resid ? static_cast<float>(1.0 / rp.keptD) : 0.f;
     const int64_t i0 = static_cast<int64_t>(c) * kResChunk;
     const int64_t i1 = min<int64_t>(i0 + kResChunk, P.V);
-    constexpr int64_t tile = static_cast<int64_t>(kThreads) * kResTile;
 
     double aw = 0.0, ap = 0.0;
     float w[kResTiles][kResTile], p[kResTiles][kResTile];
-#pragma unroll
-    for (int t = 0; t < kResTiles; ++t) {
-        const int64_t id0 = i0 + t * tile + static_cast<int64_t>(tid) * kResTile;
-        const int nv = static_cast<int>(min<int64_t>(max<int64_t>(i1 - id0, 0), kResTile));
-        eval_run<DT, TOPP>(rowT, rowD, resid, id0, nv, rp, P.c_hi, P.c_lo, invT, invD, w[t], p[t]);
-    }
+    eval_chunk<DT, TOPP>(rowT, rowD, resid, i0, i1, rp, P.c_hi, P.c_lo, invT, invD, w, p);
 #pragma unroll
     for (int t = 0; t < kResTiles; ++t)
 #pragma unroll
@@ -939,17 +1046,8 @@ __global__ __launch_bounds__(kThreads) void k_pick(Params P) {
     __shared__ double s_pre_first[kThreads], s_pre_last[kThreads];
     const int tid = threadIdx.x;
     const int b = blockIdx.x;
-    const RowParam rp = P.rowp[b];
-    // rowp was written by this call's resample pass; anything else is skipped
-    if ((rp.mode != MODE_RESID && rp.mode != MODE_BONUS) || rp.n < 0 || rp.n > P.K) return;
-    const bool resid = rp.mode == MODE_RESID;
-    const uint8_t* rowT = row_ptr<DT>(P, true, b, rp.n);
-    const uint8_t* rowD = resid ? row_ptr<DT>(P, false, b, rp.n) : nullptr;
-    const float invT = static_cast<float>(1.0 / rp.keptT);
-    const float invD = resid ? static_cast<float>(1.0 / rp.keptD) : 0.f;
-
     // Chunk masses: thread t owns chunks [t*g, t*g + g), summed in order; a
-    // block scan gives each thread its prefix.
+    // block scan gives each thread its prefix.  Loaded alongside rowp.
     const double* cm = P.cmass + static_cast<size_t>(b) * P.nch2 * 2;
     const int g = (P.nch2 + kThreads - 1) / kThreads;
     const int c0 = min(tid * g, P.nch2), c1 = min(c0 + g, P.nch2);
@@ -958,6 +1056,14 @@ __global__ __launch_bounds__(kThreads) void k_pick(Params P) {
         wsum += cm[2 * k];
         psum += cm[2 * k + 1];
     }
+    const RowParam rp = P.rowp[b];
+    // rowp was written by this call's resample pass; anything else is skipped
+    if ((rp.mode != MODE_RESID && rp.mode != MODE_BONUS) || rp.n < 0 || rp.n > P.K) return;
+    const bool resid = rp.mode == MODE_RESID;
+    const uint8_t* rowT = row_ptr<DT>(P, true, b, rp.n);
+    const uint8_t* rowD = resid ? row_ptr<DT>(P, false, b, rp.n) : nullptr;
+    const float invT = static_cast<float>(1.0 / rp.keptT);
+    const float invD = resid ? static_cast<float>(1.0 / rp.keptD) : 0.f;
     double incl, excl, Z;
     block_scan(wsum, incl, excl, Z);
     int sel = 0;
@@ -1005,13 +1111,7 @@ __global__ __launch_bounds__(kThreads) void k_pick(Params P) {
     const int64_t j0 = static_cast<int64_t>(ch) * kResChunk;
     const int64_t j1 = min<int64_t>(j0 + kResChunk, P.V);
     float w[kResTiles][kResTile], p[kResTiles][kResTile];
-    int nvs[kResTiles];
-#pragma unroll
-    for (int tt = 0; tt < kResTiles; ++tt) {
-        const int64_t id0 = j0 + tt * tile + static_cast<int64_t>(tid) * kResTile;
-        nvs[tt] = static_cast<int>(min<int64_t>(max<int64_t>(j1 - id0, 0), kResTile));
-        eval_run<DT, TOPP>(rowT, rowD, resid, id0, nvs[tt], rp, P.c_hi, P.c_lo, invT, invD, w[tt], p[tt]);
-    }
+    eval_chunk<DT, TOPP>(rowT, rowD, resid, j0, j1, rp, P.c_hi, P.c_lo, invT, invD, w, p);
     double carry = cpre;
     int lastpos = -1;
     for (int tt = 0; tt < kResTiles; ++tt) {
@@ -1032,7 +1132,7 @@ __global__ __launch_bounds__(kThreads) void k_pick(Params P) {
             if (tid == fh) {
                 double run = carry + te;
                 int y = -1, lastw = -1;
-                for (int i = 0; i < nvs[tt]; ++i) {
+                for (int i = 0; i < kResTile; ++i) {
                     if (v[i] > 0.f) {
                         lastw = static_cast<int>(id0 + i);
                         if (y < 0 && run + static_cast<double>(v[i]) > t) y = lastw;
@@ -1093,7 +1193,7 @@ hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, in
 // Launchers.
 // ---------------------------------------------------------------------------
 hipError_t launch_stats(const Params& p, int dtype, int unroll, hipStream_t s) {
-    const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(p.B) * p.nslot * p.nch);
+    const unsigned grid = static_cast<unsigned>(p.stats_grid);
     if (dtype == DT_BF16) {
         if (unroll == 8) hipLaunchKernelGGL((k_stats<DT_BF16, 8>), dim3(grid), dim3(kThreads), 0, s, p);
         else if (unroll == 2) hipLaunchKernelGGL((k_stats<DT_BF16, 2>), dim3(grid), dim3(kThreads), 0, s, p);
@@ -1104,6 +1204,22 @@ hipError_t launch_stats(const Params& p, int dtype, int unroll, hipStream_t s) {
         else hipLaunchKernelGGL((k_stats<DT_F32, 4>), dim3(grid), dim3(kThreads), 0, s, p);
     }
     return hipGetLastError();
+}
+
+// Workgroups of the statistics kernel that fit on one CU at once.
+int stats_occupancy(int dtype, int unroll) {
+    int n = 0;
+    hipError_t e;
+    if (dtype == DT_BF16) {
+        if (unroll == 8) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_stats<DT_BF16, 8>, kThreads, 0);
+        else if (unroll == 2) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_stats<DT_BF16, 2>, kThreads, 0);
+        else e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_stats<DT_BF16, 4>, kThreads, 0);
+    } else {
+        if (unroll == 8) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_stats<DT_F32, 8>, kThreads, 0);
+        else if (unroll == 2) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_stats<DT_F32, 2>, kThreads, 0);
+        else e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_stats<DT_F32, 4>, kThreads, 0);
+    }
+    return (e == hipSuccess && n > 0) ? n : 1;
 }
 
 hipError_t launch_topp(const Params& p, int dtype, hipStream_t s) {

@@ -184,11 +184,9 @@ def main():
     prof = binding.profile_read()
     stats_ms, stats_n = prof["stats"]
     res_ms, res_n = prof["resample"]
-    pick_ms, pick_n = prof["pick"]
     stats_avg_s = stats_ms / 1e3 / max(stats_n, 1)
     achieved = logical / stats_avg_s / 1e9
     print(f"[bench] stats kernel {stats_ms / max(stats_n, 1) * 1e3:.2f} us, resample "
-          f"{res_ms / max(res_n, 1) * 1e3:.2f} us, pick {pick_ms / max(pick_n, 1) * 1e3:.2f} us "
           f"({stats_n} launches)", file=sys.stderr, flush=True)
 
     traffic = stored_traffic()
@@ -199,10 +197,9 @@ def main():
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4),
         "traffic": traffic,
-        "kernel": "k_stats (statistics pass)",
+        "kernel": "k_stats (statistics pass + accept decision)",
         "kernel_us": round(stats_avg_s * 1e6, 3),
-        "other_kernels_us": {"resample": round(res_ms / max(res_n, 1) * 1e3, 3),
-                             "pick": round(pick_ms / max(pick_n, 1) * 1e3, 3)},
+        "other_kernels_us": {"resample": round(res_ms / max(res_n, 1) * 1e3, 3)},
         "algorithmic_bytes_per_launch": logical,
     }
 

@@ -21,8 +21,10 @@ namespace {
 using sv::Params;
 
 struct Scratch {
-    void* ptr = nullptr;
+    void* ptr = nullptr;       // per-call data, every byte rewritten before it is read
     size_t bytes = 0;
+    uint32_t* counters = nullptr;  // arrival counters: zeroed once, left at zero by every call
+    int64_t counter_rows = 0;
 };
 
 struct Layout {
@@ -70,24 +72,6 @@ int env_int(const char* name, int dflt) {
 
 bool misaligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) != 0; }
 
-// Resident statistics workgroups on the current device: CUs times the
-// kernel's occupancy (cached per device, dtype and unroll).
-int stats_resident(int dtype, int unroll) {
-    static std::mutex mu;
-    static std::map<std::pair<int, int>, int> cache;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 256;
-    const std::pair<int, int> key{dev, dtype * 16 + unroll};
-    std::lock_guard<std::mutex> lk(mu);
-    auto it = cache.find(key);
-    if (it != cache.end()) return it->second;
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-    const int n = cus * sv::stats_occupancy(dtype, unroll);
-    cache[key] = n;
-    return n;
-}
-
 int check_logits(const sv_logits* t) {
     if (!t || !t->data) return SV_EINVAL;
     if (t->dtype != SV_F32 && t->dtype != SV_BF16) return SV_EDTYPE;
@@ -96,23 +80,26 @@ int check_logits(const sv_logits* t) {
     return SV_OK;
 }
 
-// Returns the scratch for (device, stream), growing it when needed.  Every
-// byte a call reads from it is written earlier in the same call, so its
-// previous contents never matter.
-int get_scratch(hipStream_t stream, size_t bytes, void** out) {
+// Returns the scratch for (device, stream), growing it when needed.  The data
+// region is rewritten before it is read within every call.  The arrival
+// counters live in their own allocation at fixed offsets (two per batch row),
+// are zeroed when allocated, and every call leaves them at zero.
+int get_scratch(hipStream_t stream, size_t bytes, int64_t rows, void** data, uint32_t** counters) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     std::lock_guard<std::mutex> lk(g_mu);
     Scratch& s = g_scratch[{dev, stream}];
-    if (s.bytes < bytes) {
-        if (s.ptr) {
-            e = hipStreamSynchronize(stream);
-            if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
-            (void)hipFree(s.ptr);
-            s.ptr = nullptr;
-            s.bytes = 0;
-        }
+    const bool grow_data = s.bytes < bytes;
+    const bool grow_cnt = s.counter_rows < rows;
+    if ((grow_data && s.ptr) || (grow_cnt && s.counters)) {
+        e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    }
+    if (grow_data) {
+        if (s.ptr) (void)hipFree(s.ptr);
+        s.ptr = nullptr;
+        s.bytes = 0;
         void* p = nullptr;
         const size_t want = bytes + bytes / 4;
         e = hipMalloc(&p, want);
@@ -120,15 +107,31 @@ int get_scratch(hipStream_t stream, size_t bytes, void** out) {
             (void)hipGetLastError();
             return SV_ENOMEM;
         }
-        e = hipMemsetAsync(p, 0, want, stream);
+        s.ptr = p;
+        s.bytes = want;
+    }
+    if (grow_cnt) {
+        if (s.counters) (void)hipFree(s.counters);
+        s.counters = nullptr;
+        s.counter_rows = 0;
+        const int64_t want = rows < 64 ? 64 : rows * 2;
+        void* p = nullptr;
+        const size_t nb = static_cast<size_t>(want) * 2 * sv::kCounterStride * sizeof(uint32_t);
+        e = hipMalloc(&p, nb);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return SV_ENOMEM;
+        }
+        e = hipMemsetAsync(p, 0, nb, stream);
         if (e != hipSuccess) {
             (void)hipFree(p);
             return hip_fail(e, "hipMemsetAsync");
         }
-        s.ptr = p;
-        s.bytes = want;
+        s.counters = static_cast<uint32_t*>(p);
+        s.counter_rows = want;
     }
-    *out = s.ptr;
+    *data = s.ptr;
+    *counters = s.counters;
     return SV_OK;
 }
 
@@ -177,9 +180,9 @@ int verify_impl(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_t
     // statistics pass: chunks of at most `cv` 16-byte vectors per workgroup
     const int64_t nvec_max = (static_cast<int64_t>(V) * E + 15) / 16 + 1;
     int unroll = env_int("SPECVERIFY_STATS_UNROLL", sv::kStatsUnroll);
-    if (unroll != 2 && unroll != 8) unroll = 4;
-    // an item of the persistent statistics pass is one step of
-    // kThreads*unroll vectors; only a row's last chunk is partial
+    if (unroll != 8) unroll = 4;
+    // a statistics workgroup reads one chunk of kThreads*unroll vectors; only
+    // a row's last chunk is partial
     const int cv = sv::kThreads * unroll;
     const int64_t nch64 = (nvec_max + cv - 1) / cv;
     const int nch = static_cast<int>(nch64);
@@ -190,7 +193,8 @@ int verify_impl(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_t
     hipStream_t stream = static_cast<hipStream_t>(stream_v);
     const Layout lay = layout(B, nslot, nch, nch2);
     void* scratch = nullptr;
-    rc = get_scratch(stream, lay.total, &scratch);
+    uint32_t* counters = nullptr;
+    rc = get_scratch(stream, lay.total, B, &scratch, &counters);
     if (rc) return rc;
     uint8_t* base = static_cast<uint8_t*>(scratch);
 
@@ -214,13 +218,6 @@ int verify_impl(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_t
     p.nslot = nslot;
     p.nch = nch;
     p.cv = cv;
-    {
-        const int64_t items = static_cast<int64_t>(B) * nslot * nch;
-        int64_t grid = stats_resident(dtype, unroll);
-        const int wpc = env_int("SPECVERIFY_STATS_WG", 0);  // tuning override: total workgroups
-        if (wpc > 0) grid = wpc;
-        p.stats_grid = static_cast<int>(items < grid ? items : grid);
-    }
     p.nch2 = nch2;
     // c = c_hi + c_lo with c_hi <= c rounded toward zero, so c_lo > 0.
     float c_hi = static_cast<float>(c);
@@ -237,17 +234,17 @@ int verify_impl(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_t
     p.rv = reinterpret_cast<sv::RvState*>(base + lay.rv);
     p.rowp = reinterpret_cast<sv::RowParam*>(base + lay.rowp);
     p.cmass = reinterpret_cast<double*>(base + lay.cmass);
+    p.row_cnt = counters;
+    p.res_cnt = counters + static_cast<size_t>(B) * sv::kCounterStride;
 
     const bool topp = top_p < 1.f;
-    rc = timed_launch(sv::KK_STATS, stream, [&] { return sv::launch_stats(p, dtype, unroll, stream); });
+    rc = timed_launch(sv::KK_STATS, stream, [&] { return sv::launch_stats(p, dtype, unroll, topp, stream); });
     if (rc) return rc;
     if (topp) {
         rc = timed_launch(sv::KK_TOPP, stream, [&] { return sv::launch_topp(p, dtype, stream); });
         if (rc) return rc;
     }
-    rc = timed_launch(sv::KK_RESAMPLE, stream, [&] { return sv::launch_resample(p, dtype, topp, stream); });
-    if (rc) return rc;
-    return timed_launch(sv::KK_PICK, stream, [&] { return sv::launch_pick(p, dtype, topp, stream); });
+    return timed_launch(sv::KK_RESAMPLE, stream, [&] { return sv::launch_resample(p, dtype, topp, stream); });
 }
 
 }  // namespace
@@ -286,8 +283,10 @@ const char* spec_verify_strerror(int status) {
 
 void spec_verify_release(void) {
     std::lock_guard<std::mutex> lk(g_mu);
-    for (auto& kv : g_scratch)
+    for (auto& kv : g_scratch) {
         if (kv.second.ptr) (void)hipFree(kv.second.ptr);
+        if (kv.second.counters) (void)hipFree(kv.second.counters);
+    }
     g_scratch.clear();
 }
 

@@ -18,7 +18,7 @@ constexpr int kResChunk = kThreads * kResTile * kResTiles;
 
 enum DType : int { DT_F32 = 0, DT_BF16 = 1 };
 enum RowMode : int { MODE_SKIP = 0, MODE_RESID = 1, MODE_BONUS = 2 };
-enum KernelKind : int { KK_STATS = 0, KK_TOPP = 1, KK_RESAMPLE = 2, KK_PICK = 3, KK_COUNT = 4 };
+enum KernelKind : int { KK_STATS = 0, KK_TOPP = 1, KK_RESAMPLE = 2, KK_COUNT = 3 };
 
 // Statistics of one chunk of one logit row, relative to an integer offset o:
 // s = sum over the chunk of 2^(l*c - o), c = log2(e)/T; m = max logit; lx =
@@ -72,7 +72,6 @@ struct Params {
     double* probe_row;            // [B, 4] or null
     int B, K, V, nslot;
     int nch, cv;                  // statistics pass: chunks per row, 16-byte vectors per chunk
-    int stats_grid;               // persistent statistics workgroups
     int nch2;                     // resample pass: chunks of kResChunk ids per row
     float c_hi, c_lo;             // c = log2(e)/T = c_hi + c_lo, c_lo > 0
     double c64;                   // (double)c_hi + (double)c_lo
@@ -82,14 +81,16 @@ struct Params {
     RvState* rv;                  // [B, nslot]
     RowParam* rowp;               // [B]
     double* cmass;                // [B, nch2, 2]: residual (or bonus) mass, target mass
+    uint32_t* row_cnt;            // [B] arrival counters, kCounterStride words apart, zero between calls
+    uint32_t* res_cnt;            // [B] likewise, for the resample pass
 };
 
+constexpr int kCounterStride = 16;  // one 64-byte line per counter
+
 // Launchers (defined in sv_kernels.hip).
-hipError_t launch_stats(const Params& p, int dtype, int unroll, hipStream_t s);
-int stats_occupancy(int dtype, int unroll);
+hipError_t launch_stats(const Params& p, int dtype, int unroll, bool topp, hipStream_t s);
 hipError_t launch_topp(const Params& p, int dtype, hipStream_t s);
 hipError_t launch_resample(const Params& p, int dtype, bool topp, hipStream_t s);
-hipError_t launch_pick(const Params& p, int dtype, bool topp, hipStream_t s);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int unroll, hipStream_t s);
 
 }  // namespace sv

@@ -11,27 +11,26 @@
 // Speculative Decoding for LLMs", section 2 (per-sequence acceptance in a
 // batch).
 //
-// Pipeline (all on one stream, no host synchronisation, no cross-workgroup
-// atomics: every hand-off is a kernel boundary):
+// Pipeline (one stream, no host synchronisation):
 //   k_stats     one workgroup per (row b, logit row, chunk of V): streams the
-//               chunk once from HBM with 16-byte loads and reduces it to
-//               (offset o, sum 2^(l*c - o), max) -- one 16-byte partial.
-//   k_topp      (top-p only) one workgroup per logit row: combines its
-//               partials and finds the exact nucleus cut (value key tau, tie
-//               cut by id, kept mass).
-//   k_resample  one workgroup per (row b, chunk of V): first re-derives the
-//               row's decision (combine the row's partials, gather p'(x_j)
-//               and q'(x_j), Philox, accept scan -> n_b) -- a few KB of reads,
-//               cheaper than a synchronisation -- then sums the residual or
-//               bonus mass of its chunk in float64.  Chunk 0 writes the row's
-//               outputs.
-//   k_pick      one workgroup per row b: finds the chunk holding u*Z from the
-//               chunk masses and rescans it in id order for the token.
+//               chunk once from HBM with 16-byte loads and reduces it to one
+//               partial (offset o, sum 2^(l*c - o), max, logit at the drafted
+//               id).  Without top-p the last workgroup to finish a batch row
+//               makes the row's decision: combine, p'(x_j)/q'(x_j), Philox,
+//               accept scan -> n_b, outputs.
+//   k_topp      (top-p only) one workgroup per logit row: exact nucleus cut
+//               (value key tau, tie cut by id, kept mass); the last logit row
+//               of a batch row makes the decision.
+//   k_resample  one workgroup per (row b, chunk of V): residual or bonus mass
+//               of the chunk in float64; the last chunk of a row finds the
+//               chunk holding u*Z and rescans it in id order for the token.
 //
-// Everything that streams V is bandwidth-bound (no dense contraction, so no
-// MFMA).  Agent-scope release/acquire between workgroups would cost an L2
-// writeback per workgroup on this part, which is why hand-offs go through
-// kernel boundaries instead.
+// Hand-offs between workgroups of one kernel ("last one to finish does the
+// row") use agent-coherent atomic stores for the data, a wait for their
+// completion, and a relaxed agent-scope counter: on this part an agent-scope
+// release/acquire costs an L2 writeback or invalidate per workgroup, while a
+// store that is itself coherent at agent scope needs neither.  Everything that
+// streams V is bandwidth-bound (no dense contraction, so no MFMA).
 
 #include "sv_device.h"
 #include "sv_internal.h"
@@ -83,7 +82,83 @@ __device__ __forceinline__ void mask_edge(float* f, int64_t k, int head, int V) 
 }
 
 // ---------------------------------------------------------------------------
-// Row epilogue: combine, gather, Philox, accept scan, outputs.
+// Agent-coherent hand-off between workgroups of one kernel.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void st_agent(void* p, uint64_t v) {
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_agent(const void* p) {
+    return __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<void*>(p)), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+}
+// Waits until this thread's earlier stores have completed (vmcnt(0)); the
+// compiler may not move memory operations across it.
+__device__ __forceinline__ void stores_done() {
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+// Counts one arrival; true for the arrival that completes `need`.
+__device__ __forceinline__ bool arrive_last(uint32_t* cnt, uint32_t need) {
+    const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    return old + 1u == need;
+}
+__device__ __forceinline__ void counter_reset(uint32_t* cnt) {
+    __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t pack2(float a, float b) {
+    return static_cast<uint64_t>(__float_as_uint(a)) | (static_cast<uint64_t>(__float_as_uint(b)) << 32);
+}
+__device__ __forceinline__ float lo32f(uint64_t w) { return __uint_as_float(static_cast<uint32_t>(w)); }
+__device__ __forceinline__ float hi32f(uint64_t w) { return __uint_as_float(static_cast<uint32_t>(w >> 32)); }
+
+__device__ __forceinline__ void store_partial(Partial* p, float o, float m, float lx, double s) {
+    uint64_t* w = reinterpret_cast<uint64_t*>(p);
+    st_agent(w + 0, pack2(o, m));
+    st_agent(w + 1, pack2(lx, 0.f));
+    st_agent(w + 2, static_cast<uint64_t>(__double_as_longlong(s)));
+}
+__device__ __forceinline__ Partial load_partial(const Partial* p) {
+    const uint64_t* w = reinterpret_cast<const uint64_t*>(p);
+    const uint64_t a = ld_agent(w + 0), b = ld_agent(w + 1), c = ld_agent(w + 2);
+    Partial q;
+    q.o = lo32f(a);
+    q.m = hi32f(a);
+    q.lx = lo32f(b);
+    q.pad = 0.f;
+    q.s = __longlong_as_double(static_cast<long long>(c));
+    return q;
+}
+__device__ __forceinline__ void store_rvstate(RvState* p, const RvState& st) {
+    uint64_t* w = reinterpret_cast<uint64_t*>(p);
+    st_agent(w + 0, pack2(st.o, st.m));
+    st_agent(w + 1, pack2(st.lx, 0.f));
+    st_agent(w + 2, static_cast<uint64_t>(__double_as_longlong(st.s)));
+    st_agent(w + 3, static_cast<uint64_t>(__double_as_longlong(st.kept)));
+    st_agent(w + 4, static_cast<uint64_t>(st.tau) | (static_cast<uint64_t>(static_cast<uint32_t>(st.cut)) << 32));
+    st_agent(w + 5, static_cast<uint64_t>(static_cast<uint32_t>(st.valid)));
+}
+__device__ __forceinline__ RvState load_rvstate(const RvState* p) {
+    const uint64_t* w = reinterpret_cast<const uint64_t*>(p);
+    const uint64_t a = ld_agent(w + 0), b = ld_agent(w + 1), c = ld_agent(w + 2), d = ld_agent(w + 3),
+                   e = ld_agent(w + 4), f = ld_agent(w + 5);
+    RvState q;
+    q.o = lo32f(a);
+    q.m = hi32f(a);
+    q.lx = lo32f(b);
+    q.pad0 = 0.f;
+    q.s = __longlong_as_double(static_cast<long long>(c));
+    q.kept = __longlong_as_double(static_cast<long long>(d));
+    q.tau = static_cast<uint32_t>(e);
+    q.cut = static_cast<int32_t>(static_cast<uint32_t>(e >> 32));
+    q.valid = static_cast<int32_t>(static_cast<uint32_t>(f));
+    q.pad = 0;
+    return q;
+}
+
+// ---------------------------------------------------------------------------
+// Row decision: combine, gather, Philox, accept scan, outputs.
 // ---------------------------------------------------------------------------
 struct RowShared {
     float o[kMaxSlots];
@@ -107,34 +182,6 @@ struct RowShared {
 // draft j -> K + 1 + j.
 __device__ __forceinline__ int rv_slot(int r, int Le, int K) { return r <= Le ? r : K + 1 + (r - Le - 1); }
 
-// Combines the chunk partials of logit row `slot` of batch row b (one wave).
-__device__ __forceinline__ void combine_partials(const Params& P, int b, int slot, int lane, float& O, float& M,
-                                                 float& LX, double& S) {
-    const Partial* pp = P.part + (static_cast<size_t>(b) * P.nslot + slot) * P.nch;
-    O = -SV_INF;
-    M = -SV_INF;
-    LX = -SV_INF;
-    for (int c = lane; c < P.nch; c += 64) {
-        O = fmaxf(O, pp[c].o);
-        M = fmaxf(M, pp[c].m);
-        LX = fmaxf(LX, pp[c].lx);
-    }
-    O = wave_max(O);
-    M = wave_max(M);
-    LX = wave_max(LX);
-    S = 0.0;
-    for (int c = lane; c < P.nch; c += 64) {
-        const Partial q = pp[c];
-        S += (q.o == -SV_INF) ? q.s : ldexp(q.s, static_cast<int>(fmaxf(q.o - O, -1100.f)));
-    }
-    S = wave_sum(S);
-}
-
-// Re-derives the decision of batch row b into R (all threads of the
-// workgroup take part): combine (or load) the statistics of the row's logit
-// rows, check validity, gather p'(x_j), q'(x_j), draw the Philox uniforms and
-// scan for the first rejection.  With write_outputs the workgroup also writes
-// the row's outputs, its probe records and the RowParam the pick pass reads.
 // Merges two (offset, sum) statistics exactly: both sums are rescaled to the
 // larger integer offset by a power of two.  An empty side (offset -inf)
 // contributes its sum unscaled (0, or NaN from a bad logit).
@@ -145,20 +192,53 @@ __device__ __forceinline__ double merge_stats(float Oa, double Sa, float Ob, dou
     return sa + sb;
 }
 
+// Combines the chunk partials of logit row `slot` of batch row b (one wave,
+// lanes over chunks).
+__device__ __forceinline__ void combine_partials(const Params& P, int b, int slot, int lane, float& O, float& M,
+                                                 float& LX, double& S) {
+    const Partial* pp = P.part + (static_cast<size_t>(b) * P.nslot + slot) * P.nch;
+    O = -SV_INF;
+    M = -SV_INF;
+    LX = -SV_INF;
+    S = 0.0;
+    for (int c = lane; c < P.nch; c += 64) {
+        const Partial q = load_partial(pp + c);
+        float On;
+        S = merge_stats(O, S, q.o, q.s, On);
+        O = On;
+        M = fmaxf(M, q.m);
+        LX = fmaxf(LX, q.lx);
+    }
+    for (int off = 32; off >= 1; off >>= 1) {
+        const float O2 = __shfl_xor(O, off, 64);
+        const double S2 = __shfl_xor(S, off, 64);
+        const float M2 = __shfl_xor(M, off, 64);
+        const float L2 = __shfl_xor(LX, off, 64);
+        float On;
+        S = merge_stats(O, S, O2, S2, On);
+        O = On;
+        M = fmaxf(M, M2);
+        LX = fmaxf(LX, L2);
+    }
+}
+
+// The decision of batch row b, made by one workgroup (all threads take part)
+// once every logit row of b has its statistics: load the row's statistics,
+// check validity, take p'(x_j) and q'(x_j) from the logits at the drafted
+// ids, draw the Philox uniforms, scan for the first rejection, and write the
+// row's outputs, probe records and the RowParam the resample pass reads.
 template <int DT, bool TOPP>
-__device__ void row_decide(const Params& P, int b, RowShared& R, bool write_outputs) {
+__device__ void row_decide(const Params& P, int b, RowShared& R) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int K = P.K, K1 = P.K + 1;
     bool rowok;
     const int Le = row_len(P, b, rowok);
     const int nrv = 2 * Le + 1;
-    // Drafted ids (range check, tie cut); their logits come with the
-    // statistics (lx), so every load here is independent of every other.
     int x = -1;
     if (tid < Le) x = P.tokens[static_cast<int64_t>(b) * K + tid];
     if (TOPP) {
         for (int r = tid; r < nrv; r += kThreads) {
-            const RvState q = P.rv[static_cast<size_t>(b) * P.nslot + rv_slot(r, Le, K)];
+            const RvState q = load_rvstate(P.rv + static_cast<size_t>(b) * P.nslot + rv_slot(r, Le, K));
             R.o[r] = q.o;
             R.m[r] = q.m;
             R.lx[r] = q.lx;
@@ -178,7 +258,7 @@ __device__ void row_decide(const Params& P, int b, RowShared& R, bool write_outp
         if (r < nrv) {
             const Partial* pp = P.part + (static_cast<size_t>(b) * P.nslot + rv_slot(r, Le, K)) * P.nch;
             for (int c = gl; c < P.nch; c += G) {
-                const Partial q = pp[c];
+                const Partial q = load_partial(pp + c);
                 float On;
                 S = merge_stats(O, S, q.o, q.s, On);
                 O = On;
@@ -265,7 +345,6 @@ __device__ void row_decide(const Params& P, int b, RowShared& R, bool write_outp
         }
     }
     __syncthreads();
-    if (!write_outputs) return;
     const int bad = R.bad, n = R.n;
     for (int j = tid; j < K1; j += kThreads) {
         int v = -1;
@@ -307,87 +386,29 @@ __device__ void row_decide(const Params& P, int b, RowShared& R, bool write_outp
 }
 
 // ---------------------------------------------------------------------------
-// Statistics pass.
+// Statistics pass: one workgroup per chunk of kThreads*U 16-byte vectors of
+// one logit row, U per lane, all loads issued before any use.
 // ---------------------------------------------------------------------------
-// One item of the statistics pass is one chunk of one logit row: kThreads*U
-// 16-byte vectors, U per lane.
-struct StatsItem {
-    RowGrid g;
-    int64_t k0, k1;     // vector range of the chunk
-    int rvi, chunk, b, j;
-    bool tgt, drafted;  // drafted: the position has a drafted id (j < L_b)
-};
-
-__device__ __forceinline__ bool stats_needed(const Params& P, int it) {
-    const int rvi = it / P.nch;
-    const int b = rvi / P.nslot;
-    const int slot = rvi - b * P.nslot;
-    bool ok;
-    const int Le = row_len(P, b, ok);
-    const bool tgt = slot <= P.K;
-    const int j = tgt ? slot : slot - P.K - 1;
-    return tgt ? (j <= Le) : (j < Le);
-}
-// First item at or after `it` (stepping by the grid) that some row needs.
-__device__ __forceinline__ int next_item(const Params& P, int it, int total) {
-    while (it < total && !stats_needed(P, it)) it += P.stats_grid;
-    return it;
-}
-template <int DT>
-__device__ __forceinline__ StatsItem decode_item(const Params& P, int it) {
-    StatsItem t;
-    t.rvi = it / P.nch;
-    t.chunk = it - t.rvi * P.nch;
-    t.b = t.rvi / P.nslot;
-    const int slot = t.rvi - t.b * P.nslot;
-    bool ok;
-    const int Le = row_len(P, t.b, ok);
-    t.tgt = slot <= P.K;
-    t.j = t.tgt ? slot : slot - P.K - 1;
-    t.drafted = t.j < Le;
-    t.g = row_grid<DT>(row_ptr<DT>(P, t.tgt, t.b, t.j), P.V);
-    t.k0 = static_cast<int64_t>(t.chunk) * P.cv;
-    t.k1 = t.k0 + P.cv < t.g.nvec ? t.k0 + P.cv : t.g.nvec;
-    return t;
-}
-
-template <int DT, int U>
-__device__ __forceinline__ void issue_loads(const StatsItem& t, uint4* raw) {
-    constexpr int64_t STEP = static_cast<int64_t>(kThreads) * U;
-    if (t.k0 + STEP <= t.k1) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) raw[u] = gload16(t.g.vp + t.k0 + u * kThreads + threadIdx.x);
-    } else {
-        const uint32_t ni = Fmt<DT>::NEG_INF_WORD;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t k = t.k0 + u * kThreads + threadIdx.x;
-            raw[u] = (k < t.k1) ? gload16(t.g.vp + k) : make_uint4(ni, ni, ni, ni);
-        }
-    }
-}
-
-// (max, offset, sum) of one lane's U vectors; MASK handles the row's first
-// and last vector.
-// The lane holding vector kx copies element rx of it into *lx_out.
 template <int DT, int U, bool MASK>
-__device__ __forceinline__ void reduce_lane(const StatsItem& t, const uint4* raw, int V, float c_hi, float c_lo,
-                                            int64_t kx, int rx, float* lx_out, float& m, float& o, float& s) {
+__device__ __forceinline__ void reduce_lane(const RowGrid& g, const uint4* raw, int64_t k0, int64_t k1, int V,
+                                            float c_hi, float c_lo, int64_t kx, int rx, float& lx, float& m, float& o,
+                                            float& s) {
     constexpr int VE = Fmt<DT>::VE;
     constexpr int N = U * VE;
     float f[N];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         unpack<DT>(raw[u], f + u * VE);
-        const int64_t k = t.k0 + u * kThreads + threadIdx.x;
+        const int64_t k = k0 + u * kThreads + threadIdx.x;
         if (MASK) {
-            if (k < t.k1 && (k == 0 || k == t.g.nvec - 1)) mask_edge<DT>(f + u * VE, k, t.g.head, V);
+            if (k < k1 && (k == 0 || k == g.nvec - 1)) mask_edge<DT>(f + u * VE, k, g.head, V);
         }
         if (k == kx) {
+            // the lane holding the drafted id's vector records its logit
             float v = -SV_INF;
 #pragma unroll
             for (int i = 0; i < VE; ++i) v = (i == rx) ? f[u * VE + i] : v;
-            *lx_out = v;
+            lx = v;
         }
     }
     // N is a multiple of 4: a v_max3 tree
@@ -417,92 +438,91 @@ __device__ __forceinline__ void reduce_lane(const StatsItem& t, const uint4* raw
     s = acc[0];
 }
 
-// Statistics pass, persistent: workgroup w takes items w, w + grid, ... and
-// issues the next item's loads before reducing the current one, so that HBM
-// requests stay in flight while the VALU works.
-template <int DT, int U>
+template <int DT, int U, bool TOPP>
 __global__ __launch_bounds__(kThreads) void k_stats(Params P) {
-    __shared__ float sh_o[2][kWaves], sh_s[2][kWaves], sh_m[2][kWaves], sh_lx[2];
-    __shared__ int sh_tag[2];
+    __shared__ float sh_o[kWaves], sh_s[kWaves], sh_m[kWaves], sh_lx[kWaves];
+    __shared__ int s_last;
+    __shared__ RowShared R;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int total = P.B * P.nslot * P.nch;
-    int it = next_item(P, blockIdx.x, total);
-    if (it >= total) return;
-    if (tid < 2) sh_tag[tid] = -1;
-    __syncthreads();
-    StatsItem cur = decode_item<DT>(P, it);
-    uint4 raw[U];
-    issue_loads<DT, U>(cur, raw);
-    for (int parity = 0;; parity ^= 1) {
-        const int itn = next_item(P, it + P.stats_grid, total);
-        StatsItem nxt;
-        uint4 rawn[U];
-        if (itn < total) {
-            nxt = decode_item<DT>(P, itn);
-            issue_loads<DT, U>(nxt, rawn);
-        }
-        // drafted id of this logit row (uniform): the lane holding its vector
-        // records the logit there (tagged with the item)
-        int64_t kx = -1;
-        int rx = 0;
-        if (cur.drafted) {
-            const int x = P.tokens[static_cast<int64_t>(cur.b) * P.K + cur.j];
-            if (x >= 0 && x < P.V) {
-                kx = (static_cast<int64_t>(x) + cur.g.head) / Fmt<DT>::VE;
-                rx = static_cast<int>((static_cast<int64_t>(x) + cur.g.head) - kx * Fmt<DT>::VE);
-            }
-        }
-        float lxv = -SV_INF;
-        float m, o, sl;
-        const bool edge = cur.k0 == 0 || cur.k0 + static_cast<int64_t>(kThreads) * U >= cur.g.nvec - 1;
-        if (edge) reduce_lane<DT, U, true>(cur, raw, P.V, P.c_hi, P.c_lo, kx, rx, &lxv, m, o, sl);
-        else reduce_lane<DT, U, false>(cur, raw, P.V, P.c_hi, P.c_lo, kx, rx, &lxv, m, o, sl);
-        {
-            const int64_t rel = kx - cur.k0 - threadIdx.x;
-            if (kx >= cur.k0 && rel >= 0 && rel % kThreads == 0 && rel / kThreads < U) {
-                sh_lx[parity] = lxv;
-                sh_tag[parity] = it;
-            }
-        }
+    const int item = blockIdx.x;
+    const int rvi = item / P.nch;
+    const int chunk = item - rvi * P.nch;
+    const int b = rvi / P.nslot;
+    const int slot = rvi - b * P.nslot;
+    bool rowok;
+    const int Le = row_len(P, b, rowok);
+    const bool tgt = slot <= P.K;
+    const int j = tgt ? slot : slot - P.K - 1;
+    if (tgt ? (j > Le) : (j >= Le)) return;  // padded position: never read
 
-        // workgroup combine: exact power-of-two rescaling to the largest offset
-        const float Ow = wave_max(o);
-        const float sc = (o == -SV_INF) ? sl : ldexpf(sl, static_cast<int>(fmaxf(o - Ow, -256.f)));
-        const float Sw = wave_sum(sc);
-        const float Mw = wave_max(m);
-        if (lane == 0) {
-            sh_o[parity][wv] = Ow;
-            sh_s[parity][wv] = Sw;
-            sh_m[parity][wv] = Mw;
-        }
-        __syncthreads();
-        if (tid == 0) {
-            float O = sh_o[parity][0], M = sh_m[parity][0];
-            for (int w = 1; w < kWaves; ++w) {
-                O = fmaxf(O, sh_o[parity][w]);
-                M = fmaxf(M, sh_m[parity][w]);
-            }
-            double S = 0.0;
-            for (int w = 0; w < kWaves; ++w)
-                S += (sh_o[parity][w] == -SV_INF)
-                         ? static_cast<double>(sh_s[parity][w])
-                         : ldexp(static_cast<double>(sh_s[parity][w]),
-                                 static_cast<int>(fmaxf(sh_o[parity][w] - O, -1100.f)));
-            const float lx = (sh_tag[parity] == it) ? sh_lx[parity] : -SV_INF;
-            Partial pr;
-            pr.o = O;
-            pr.m = M;
-            pr.lx = lx;
-            pr.pad = 0.f;
-            pr.s = S;
-            P.part[static_cast<size_t>(cur.rvi) * P.nch + cur.chunk] = pr;
-        }
-        if (itn >= total) break;
-        cur = nxt;
+    const RowGrid g = row_grid<DT>(row_ptr<DT>(P, tgt, b, j), P.V);
+    const int64_t k0 = static_cast<int64_t>(chunk) * P.cv;
+    const int64_t k1 = k0 + P.cv < g.nvec ? k0 + P.cv : g.nvec;
+    constexpr int64_t STEP = static_cast<int64_t>(kThreads) * U;
+    uint4 raw[U];
+    if (k0 + STEP <= k1) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) raw[u] = rawn[u];
-        it = itn;
+        for (int u = 0; u < U; ++u) raw[u] = gload16(g.vp + k0 + u * kThreads + tid);
+    } else {
+        const uint32_t ni = Fmt<DT>::NEG_INF_WORD;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t k = k0 + u * kThreads + tid;
+            raw[u] = (k < k1) ? gload16(g.vp + k) : make_uint4(ni, ni, ni, ni);
+        }
     }
+    // drafted id of this logit row (uniform): its vector and position
+    int64_t kx = -1;
+    int rx = 0;
+    if (j < Le) {
+        const int x = P.tokens[static_cast<int64_t>(b) * P.K + j];
+        if (x >= 0 && x < P.V) {
+            kx = (static_cast<int64_t>(x) + g.head) / Fmt<DT>::VE;
+            rx = static_cast<int>(static_cast<int64_t>(x) + g.head - kx * Fmt<DT>::VE);
+        }
+    }
+    float lx = -SV_INF, m, o, sl;
+    if (k0 == 0 || k0 + STEP >= g.nvec - 1) reduce_lane<DT, U, true>(g, raw, k0, k1, P.V, P.c_hi, P.c_lo, kx, rx, lx, m, o, sl);
+    else reduce_lane<DT, U, false>(g, raw, k0, k1, P.V, P.c_hi, P.c_lo, kx, rx, lx, m, o, sl);
+
+    // workgroup combine: exact power-of-two rescaling to the largest offset
+    const float Ow = wave_max(o);
+    const float sc = (o == -SV_INF) ? sl : ldexpf(sl, static_cast<int>(fmaxf(o - Ow, -256.f)));
+    const float Sw = wave_sum(sc);
+    const float Mw = wave_max(m);
+    const float Lw = wave_max(lx);
+    if (lane == 0) {
+        sh_o[wv] = Ow;
+        sh_s[wv] = Sw;
+        sh_m[wv] = Mw;
+        sh_lx[wv] = Lw;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        float O = sh_o[0], M = sh_m[0], LX = sh_lx[0];
+        for (int w = 1; w < kWaves; ++w) {
+            O = fmaxf(O, sh_o[w]);
+            M = fmaxf(M, sh_m[w]);
+            LX = fmaxf(LX, sh_lx[w]);
+        }
+        double S = 0.0;
+        for (int w = 0; w < kWaves; ++w)
+            S += (sh_o[w] == -SV_INF) ? static_cast<double>(sh_s[w])
+                                      : ldexp(static_cast<double>(sh_s[w]), static_cast<int>(fmaxf(sh_o[w] - O, -1100.f)));
+        store_partial(P.part + static_cast<size_t>(rvi) * P.nch + chunk, O, M, LX, S);
+        if (!TOPP) {
+            stores_done();
+            s_last = arrive_last(P.row_cnt + static_cast<size_t>(b) * kCounterStride,
+                                 static_cast<uint32_t>((2 * Le + 1) * P.nch))
+                         ? 1
+                         : 0;
+        }
+    }
+    if (TOPP) return;
+    __syncthreads();
+    if (!s_last) return;
+    if (tid == 0) counter_reset(P.row_cnt + static_cast<size_t>(b) * kCounterStride);
+    row_decide<DT, false>(P, b, R);
 }
 
 // ---------------------------------------------------------------------------
@@ -872,61 +892,6 @@ __device__ void select_nucleus(const Params& P, const uint8_t* row, float O, dou
     }
 }
 
-template <int DT>
-__global__ __launch_bounds__(kThreads) void k_topp(Params P) {
-    __shared__ SelShared sh;
-    __shared__ float s_o, s_m, s_lx;
-    __shared__ double s_s;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int rvi = blockIdx.x;
-    const int b = rvi / P.nslot;
-    const int slot = rvi - b * P.nslot;
-    bool rowok;
-    const int Le = row_len(P, b, rowok);
-    const bool tgt = slot <= P.K;
-    const int j = tgt ? slot : slot - P.K - 1;
-    if (tgt ? (j > Le) : (j >= Le)) return;
-    const uint8_t* row = row_ptr<DT>(P, tgt, b, j);
-    if (wv == 0) {
-        float O, M, LX;
-        double S;
-        combine_partials(P, b, slot, lane, O, M, LX, S);
-        if (lane == 0) {
-            s_o = O;
-            s_m = M;
-            s_lx = LX;
-            s_s = S;
-        }
-    }
-    __syncthreads();
-    const float O = s_o;
-    const double S = s_s;
-    RvState st;
-    st.o = O;
-    st.m = s_m;
-    st.lx = s_lx;
-    st.pad0 = 0.f;
-    st.s = S;
-    st.kept = S;
-    st.tau = 0u;
-    st.cut = -1;
-    st.valid = (S > 0.0 && S < static_cast<double>(SV_INF)) ? 1 : 0;
-    st.pad = 0;
-    if (st.valid) {
-        double kept;
-        uint32_t tau;
-        int32_t cut;
-        select_nucleus<DT>(P, row, O, S, sh, kept, tau, cut);
-        st.kept = kept;
-        st.tau = tau;
-        st.cut = cut;
-    }
-    if (tid == 0) P.rv[rvi] = st;
-}
-
-// ---------------------------------------------------------------------------
-// Resample pass.
-// ---------------------------------------------------------------------------
 // Weights of one resample chunk [i0, i1) in id order: thread t owns ids
 // i0 + tt*tile + t*kResTile + [0, kResTile) for tiles tt.  w is the residual
 // max(0, p' - q') (or p' for the bonus), p is p'.  When the chunk is whole and
@@ -992,78 +957,149 @@ __device__ __forceinline__ void eval_chunk(const uint8_t* rowT, const uint8_t* r
     }
 }
 
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_topp(Params P) {
+    __shared__ SelShared sh;
+    __shared__ RowShared R;
+    __shared__ float s_o, s_m, s_lx;
+    __shared__ double s_s;
+    __shared__ int s_last;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int rvi = blockIdx.x;
+    const int b = rvi / P.nslot;
+    const int slot = rvi - b * P.nslot;
+    bool rowok;
+    const int Le = row_len(P, b, rowok);
+    const bool tgt = slot <= P.K;
+    const int j = tgt ? slot : slot - P.K - 1;
+    if (tgt ? (j > Le) : (j >= Le)) return;
+    const uint8_t* row = row_ptr<DT>(P, tgt, b, j);
+    if (wv == 0) {
+        float O, M, LX;
+        double S;
+        combine_partials(P, b, slot, lane, O, M, LX, S);
+        if (lane == 0) {
+            s_o = O;
+            s_m = M;
+            s_lx = LX;
+            s_s = S;
+        }
+    }
+    __syncthreads();
+    const float O = s_o;
+    const double S = s_s;
+    RvState st;
+    st.o = O;
+    st.m = s_m;
+    st.lx = s_lx;
+    st.pad0 = 0.f;
+    st.s = S;
+    st.kept = S;
+    st.tau = 0u;
+    st.cut = -1;
+    st.valid = (S > 0.0 && S < static_cast<double>(SV_INF)) ? 1 : 0;
+    st.pad = 0;
+    if (st.valid) {
+        double kept;
+        uint32_t tau;
+        int32_t cut;
+        select_nucleus<DT>(P, row, O, S, sh, kept, tau, cut);
+        st.kept = kept;
+        st.tau = tau;
+        st.cut = cut;
+    }
+    if (tid == 0) {
+        store_rvstate(P.rv + rvi, st);
+        stores_done();
+        s_last = arrive_last(P.row_cnt + static_cast<size_t>(b) * kCounterStride, static_cast<uint32_t>(2 * Le + 1))
+                     ? 1
+                     : 0;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    if (tid == 0) counter_reset(P.row_cnt + static_cast<size_t>(b) * kCounterStride);
+    row_decide<DT, true>(P, b, R);
+}
+
+// ---------------------------------------------------------------------------
+// Resample pass.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ double ld_agent_d(const double* p) {
+    return __longlong_as_double(static_cast<long long>(ld_agent(p)));
+}
+__device__ __forceinline__ void st_agent_d(double* p, double v) {
+    st_agent(p, static_cast<uint64_t>(__double_as_longlong(v)));
+}
+
+// One workgroup per (row b, chunk of kResChunk ids): the chunk's residual (or
+// bonus) mass and target mass in float64.  The last chunk of a row to finish
+// then draws the row's token: the chunk holding t = u*Z, rescanned in id
+// order.
 template <int DT, bool TOPP>
 __global__ __launch_bounds__(kThreads) void k_resample(Params P) {
-    __shared__ RowShared R;
     __shared__ double sh_w[kWaves], sh_p[kWaves];
+    __shared__ int s_last, s_y;
+    __shared__ double s_pre_first[kThreads], s_pre_last[kThreads];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int b = blockIdx.x / P.nch2;
     const int c = blockIdx.x - b * P.nch2;
-    row_decide<DT, TOPP>(P, b, R, c == 0);
-    const RowParam rp = R.rp;
-    if (rp.mode == MODE_SKIP) return;
-    const bool resid = rp.mode == MODE_RESID;
-    const uint8_t* rowT = row_ptr<DT>(P, true, b, rp.n);
-    const uint8_t* rowD = resid ? row_ptr<DT>(P, false, b, rp.n) : nullptr;
-    const float invT = static_cast<float>(1.0 / rp.keptT);
-    const float invD = resid ? static_cast<float>(1.0 / rp.keptD) : 0.f;
-    const int64_t i0 = static_cast<int64_t>(c) * kResChunk;
-    const int64_t i1 = min<int64_t>(i0 + kResChunk, P.V);
-
-    double aw = 0.0, ap = 0.0;
-    float w[kResTiles][kResTile], p[kResTiles][kResTile];
-    eval_chunk<DT, TOPP>(rowT, rowD, resid, i0, i1, rp, P.c_hi, P.c_lo, invT, invD, w, p);
-#pragma unroll
-    for (int t = 0; t < kResTiles; ++t)
-#pragma unroll
-        for (int i = 0; i < kResTile; ++i) {
-            aw += static_cast<double>(w[t][i]);
-            ap += static_cast<double>(p[t][i]);
-        }
-    aw = wave_sum(aw);
-    ap = wave_sum(ap);
-    if (lane == 0) {
-        sh_w[wv] = aw;
-        sh_p[wv] = ap;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        double W = 0.0, Pm = 0.0;
-        for (int w = 0; w < kWaves; ++w) {
-            W += sh_w[w];
-            Pm += sh_p[w];
-        }
-        double* cm = P.cmass + (static_cast<size_t>(b) * P.nch2 + c) * 2;
-        cm[0] = W;
-        cm[1] = Pm;
-    }
-}
-
-// Per row: the chunk holding t = u*Z, then a rescan of that chunk in id order.
-template <int DT, bool TOPP>
-__global__ __launch_bounds__(kThreads) void k_pick(Params P) {
-    __shared__ int s_y;
-    __shared__ double s_pre_first[kThreads], s_pre_last[kThreads];
-    const int tid = threadIdx.x;
-    const int b = blockIdx.x;
-    // Chunk masses: thread t owns chunks [t*g, t*g + g), summed in order; a
-    // block scan gives each thread its prefix.  Loaded alongside rowp.
-    const double* cm = P.cmass + static_cast<size_t>(b) * P.nch2 * 2;
-    const int g = (P.nch2 + kThreads - 1) / kThreads;
-    const int c0 = min(tid * g, P.nch2), c1 = min(c0 + g, P.nch2);
-    double wsum = 0.0, psum = 0.0;
-    for (int k = c0; k < c1; ++k) {
-        wsum += cm[2 * k];
-        psum += cm[2 * k + 1];
-    }
     const RowParam rp = P.rowp[b];
-    // rowp was written by this call's resample pass; anything else is skipped
+    // rowp was written by this call's decision; anything else is skipped
     if ((rp.mode != MODE_RESID && rp.mode != MODE_BONUS) || rp.n < 0 || rp.n > P.K) return;
     const bool resid = rp.mode == MODE_RESID;
     const uint8_t* rowT = row_ptr<DT>(P, true, b, rp.n);
     const uint8_t* rowD = resid ? row_ptr<DT>(P, false, b, rp.n) : nullptr;
     const float invT = static_cast<float>(1.0 / rp.keptT);
     const float invD = resid ? static_cast<float>(1.0 / rp.keptD) : 0.f;
+    double* cm = P.cmass + static_cast<size_t>(b) * P.nch2 * 2;
+    {
+        const int64_t i0 = static_cast<int64_t>(c) * kResChunk;
+        const int64_t i1 = min<int64_t>(i0 + kResChunk, P.V);
+        float w[kResTiles][kResTile], p[kResTiles][kResTile];
+        eval_chunk<DT, TOPP>(rowT, rowD, resid, i0, i1, rp, P.c_hi, P.c_lo, invT, invD, w, p);
+        double aw = 0.0, ap = 0.0;
+#pragma unroll
+        for (int t = 0; t < kResTiles; ++t)
+#pragma unroll
+            for (int i = 0; i < kResTile; ++i) {
+                aw += static_cast<double>(w[t][i]);
+                ap += static_cast<double>(p[t][i]);
+            }
+        aw = wave_sum(aw);
+        ap = wave_sum(ap);
+        if (lane == 0) {
+            sh_w[wv] = aw;
+            sh_p[wv] = ap;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            double W = 0.0, Pm = 0.0;
+            for (int k = 0; k < kWaves; ++k) {
+                W += sh_w[k];
+                Pm += sh_p[k];
+            }
+            st_agent_d(cm + 2 * c, W);
+            st_agent_d(cm + 2 * c + 1, Pm);
+            stores_done();
+            s_last = arrive_last(P.res_cnt + static_cast<size_t>(b) * kCounterStride, static_cast<uint32_t>(P.nch2))
+                         ? 1
+                         : 0;
+        }
+        __syncthreads();
+        if (!s_last) return;
+        if (tid == 0) counter_reset(P.res_cnt + static_cast<size_t>(b) * kCounterStride);
+    }
+
+    // Chunk masses: thread t owns chunks [t*g, t*g + g), summed in order; a
+    // block scan gives each thread its prefix.
+    const int g = (P.nch2 + kThreads - 1) / kThreads;
+    const int c0 = min(tid * g, P.nch2), c1 = min(c0 + g, P.nch2);
+    double wsum = 0.0, psum = 0.0;
+    for (int k = c0; k < c1; ++k) {
+        wsum += ld_agent_d(cm + 2 * k);
+        psum += ld_agent_d(cm + 2 * k + 1);
+    }
     double incl, excl, Z;
     block_scan(wsum, incl, excl, Z);
     int sel = 0;
@@ -1077,7 +1113,7 @@ __global__ __launch_bounds__(kThreads) void k_pick(Params P) {
     int first = 0x7FFFFFFF, lastnz = -1;
     double pre = excl, pf = 0.0, pl = 0.0;
     for (int k = c0; k < c1; ++k) {
-        const double m = cm[2 * k + sel];
+        const double m = ld_agent_d(cm + 2 * k + sel);
         if (m > 0.0) {
             if (first == 0x7FFFFFFF && pre + m > t) {
                 first = k;
@@ -1192,34 +1228,22 @@ hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, in
 // ---------------------------------------------------------------------------
 // Launchers.
 // ---------------------------------------------------------------------------
-hipError_t launch_stats(const Params& p, int dtype, int unroll, hipStream_t s) {
-    const unsigned grid = static_cast<unsigned>(p.stats_grid);
-    if (dtype == DT_BF16) {
-        if (unroll == 8) hipLaunchKernelGGL((k_stats<DT_BF16, 8>), dim3(grid), dim3(kThreads), 0, s, p);
-        else if (unroll == 2) hipLaunchKernelGGL((k_stats<DT_BF16, 2>), dim3(grid), dim3(kThreads), 0, s, p);
-        else hipLaunchKernelGGL((k_stats<DT_BF16, 4>), dim3(grid), dim3(kThreads), 0, s, p);
-    } else {
-        if (unroll == 8) hipLaunchKernelGGL((k_stats<DT_F32, 8>), dim3(grid), dim3(kThreads), 0, s, p);
-        else if (unroll == 2) hipLaunchKernelGGL((k_stats<DT_F32, 2>), dim3(grid), dim3(kThreads), 0, s, p);
-        else hipLaunchKernelGGL((k_stats<DT_F32, 4>), dim3(grid), dim3(kThreads), 0, s, p);
-    }
-    return hipGetLastError();
+template <int DT, int U>
+static void launch_stats_t(const Params& p, bool topp, hipStream_t s) {
+    const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(p.B) * p.nslot * p.nch);
+    if (topp) hipLaunchKernelGGL((k_stats<DT, U, true>), dim3(grid), dim3(kThreads), 0, s, p);
+    else hipLaunchKernelGGL((k_stats<DT, U, false>), dim3(grid), dim3(kThreads), 0, s, p);
 }
 
-// Workgroups of the statistics kernel that fit on one CU at once.
-int stats_occupancy(int dtype, int unroll) {
-    int n = 0;
-    hipError_t e;
+hipError_t launch_stats(const Params& p, int dtype, int unroll, bool topp, hipStream_t s) {
     if (dtype == DT_BF16) {
-        if (unroll == 8) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_stats<DT_BF16, 8>, kThreads, 0);
-        else if (unroll == 2) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_stats<DT_BF16, 2>, kThreads, 0);
-        else e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_stats<DT_BF16, 4>, kThreads, 0);
+        if (unroll == 8) launch_stats_t<DT_BF16, 8>(p, topp, s);
+        else launch_stats_t<DT_BF16, 4>(p, topp, s);
     } else {
-        if (unroll == 8) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_stats<DT_F32, 8>, kThreads, 0);
-        else if (unroll == 2) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_stats<DT_F32, 2>, kThreads, 0);
-        else e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_stats<DT_F32, 4>, kThreads, 0);
+        if (unroll == 8) launch_stats_t<DT_F32, 8>(p, topp, s);
+        else launch_stats_t<DT_F32, 4>(p, topp, s);
     }
-    return (e == hipSuccess && n > 0) ? n : 1;
+    return hipGetLastError();
 }
 
 hipError_t launch_topp(const Params& p, int dtype, hipStream_t s) {
@@ -1237,18 +1261,6 @@ hipError_t launch_resample(const Params& p, int dtype, bool topp, hipStream_t s)
     } else {
         if (topp) hipLaunchKernelGGL((k_resample<DT_F32, true>), dim3(grid), dim3(kThreads), 0, s, p);
         else hipLaunchKernelGGL((k_resample<DT_F32, false>), dim3(grid), dim3(kThreads), 0, s, p);
-    }
-    return hipGetLastError();
-}
-
-hipError_t launch_pick(const Params& p, int dtype, bool topp, hipStream_t s) {
-    const unsigned grid = static_cast<unsigned>(p.B);
-    if (dtype == DT_BF16) {
-        if (topp) hipLaunchKernelGGL((k_pick<DT_BF16, true>), dim3(grid), dim3(kThreads), 0, s, p);
-        else hipLaunchKernelGGL((k_pick<DT_BF16, false>), dim3(grid), dim3(kThreads), 0, s, p);
-    } else {
-        if (topp) hipLaunchKernelGGL((k_pick<DT_F32, true>), dim3(grid), dim3(kThreads), 0, s, p);
-        else hipLaunchKernelGGL((k_pick<DT_F32, false>), dim3(grid), dim3(kThreads), 0, s, p);
     }
     return hipGetLastError();
 }

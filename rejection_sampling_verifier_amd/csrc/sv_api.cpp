@@ -72,6 +72,21 @@ int env_int(const char* name, int dflt) {
 
 bool misaligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) != 0; }
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+    static std::mutex mu;
+    static std::map<int, int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    std::lock_guard<std::mutex> lk(mu);
+    auto it = cache.find(dev);
+    if (it != cache.end()) return it->second;
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+    return n;
+}
+
 int check_logits(const sv_logits* t) {
     if (!t || !t->data) return SV_EINVAL;
     if (t->dtype != SV_F32 && t->dtype != SV_BF16) return SV_EDTYPE;
@@ -186,8 +201,14 @@ int verify_impl(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_t
     const int cv = sv::kThreads * unroll;
     const int64_t nch64 = (nvec_max + cv - 1) / cv;
     const int nch = static_cast<int>(nch64);
-    // resample pass: chunks of kResChunk ids
-    const int nch2 = (V + sv::kResChunk - 1) / sv::kResChunk;
+    // resample pass: steps of kResStepIds ids; about one workgroup per CU
+    // over the batch, each covering res_steps consecutive steps of one row
+    const int nch2 = (V + sv::kResStepIds - 1) / sv::kResStepIds;
+    int res_split = (device_cus() + B - 1) / B;
+    if (res_split > nch2) res_split = nch2;
+    if (res_split < 1) res_split = 1;
+    const int res_steps = (nch2 + res_split - 1) / res_split;
+    res_split = (nch2 + res_steps - 1) / res_steps;
     if (static_cast<int64_t>(B) * nslot * nch >= (1ll << 31)) return SV_ESHAPE;
 
     hipStream_t stream = static_cast<hipStream_t>(stream_v);
@@ -219,6 +240,8 @@ int verify_impl(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_t
     p.nch = nch;
     p.cv = cv;
     p.nch2 = nch2;
+    p.res_split = res_split;
+    p.res_steps = res_steps;
     // c = c_hi + c_lo with c_hi <= c rounded toward zero, so c_lo > 0.
     float c_hi = static_cast<float>(c);
     if (static_cast<double>(c_hi) > c) c_hi = std::nextafter(c_hi, 0.f);

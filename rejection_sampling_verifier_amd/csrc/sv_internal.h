@@ -12,9 +12,8 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kMaxK = 16;
 constexpr int kMaxSlots = 2 * kMaxK + 1;
 constexpr int kStatsUnroll = 4;      // default 16-byte vectors in flight per lane per step
-constexpr int kResTile = 8;          // consecutive ids per lane in the resample pass
-constexpr int kResTiles = 2;         // tiles of kThreads*kResTile ids per resample chunk
-constexpr int kResChunk = kThreads * kResTile * kResTiles;
+constexpr int kResTile = 8;          // consecutive ids per thread in the id-ordered scans
+constexpr int kResStepIds = 8192;    // ids per resample step (1024 threads x 8)
 
 enum DType : int { DT_F32 = 0, DT_BF16 = 1 };
 enum RowMode : int { MODE_SKIP = 0, MODE_RESID = 1, MODE_BONUS = 2 };
@@ -72,7 +71,8 @@ struct Params {
     double* probe_row;            // [B, 4] or null
     int B, K, V, nslot;
     int nch, cv;                  // statistics pass: chunks per row, 16-byte vectors per chunk
-    int nch2;                     // resample pass: chunks of kResChunk ids per row
+    int nch2;                     // resample pass: steps of kResStepIds ids per row
+    int res_split, res_steps;     // resample workgroups per row, steps per workgroup
     float c_hi, c_lo;             // c = log2(e)/T = c_hi + c_lo, c_lo > 0
     double c64;                   // (double)c_hi + (double)c_lo
     float top_p;

@@ -169,12 +169,6 @@ struct RowShared {
     uint32_t tau[kMaxSlots];
     int32_t cut[kMaxSlots];
     int32_t valid[kMaxSlots];
-    double px[kMaxK];
-    double qx[kMaxK];
-    int bad;
-    int n;
-    double u_res;
-    RowParam rp;
 };
 
 // rv index r of a batch row: target position j -> r = j; draft position j ->
@@ -222,165 +216,183 @@ __device__ __forceinline__ void combine_partials(const Params& P, int b, int slo
     }
 }
 
-// The decision of batch row b, made by one workgroup (all threads take part)
-// once every logit row of b has its statistics: load the row's statistics,
-// check validity, take p'(x_j) and q'(x_j) from the logits at the drafted
-// ids, draw the Philox uniforms, scan for the first rejection, and write the
-// row's outputs, probe records and the RowParam the resample pass reads.
+// Partials staged in LDS by the deciding wave.
+constexpr int kStage = 256;
+struct StageShared {
+    float o[kStage];
+    float m[kStage];
+    float lx[kStage];
+    double s[kStage];
+};
+
+// The decision of batch row b, made by ONE wave (64 lanes, no workgroup
+// barrier) once every logit row of b has its statistics: load the row's
+// statistics, check validity, take p'(x_j) and q'(x_j) from the logits at the
+// drafted ids, draw the Philox uniforms, scan for the first rejection, and
+// write the row's outputs, probe records and the RowParam the resample pass
+// reads.
 template <int DT, bool TOPP>
-__device__ void row_decide(const Params& P, int b, RowShared& R) {
-    const int tid = threadIdx.x, lane = tid & 63;
+__device__ void row_decide(const Params& P, int b, RowShared& R, StageShared* stgp) {
+    const int lane = threadIdx.x & 63;
     const int K = P.K, K1 = P.K + 1;
     bool rowok;
     const int Le = row_len(P, b, rowok);
     const int nrv = 2 * Le + 1;
-    int x = -1;
-    if (tid < Le) x = P.tokens[static_cast<int64_t>(b) * K + tid];
+    const int x = (lane < Le) ? P.tokens[static_cast<int64_t>(b) * K + lane] : -1;
     if (TOPP) {
-        for (int r = tid; r < nrv; r += kThreads) {
-            const RvState q = load_rvstate(P.rv + static_cast<size_t>(b) * P.nslot + rv_slot(r, Le, K));
-            R.o[r] = q.o;
-            R.m[r] = q.m;
-            R.lx[r] = q.lx;
-            R.s[r] = q.s;
-            R.kept[r] = q.kept;
-            R.tau[r] = q.tau;
-            R.cut[r] = q.cut;
-            R.valid[r] = q.valid;
+        if (lane < nrv) {
+            const RvState q = load_rvstate(P.rv + static_cast<size_t>(b) * P.nslot + rv_slot(lane, Le, K));
+            R.o[lane] = q.o;
+            R.m[lane] = q.m;
+            R.lx[lane] = q.lx;
+            R.s[lane] = q.s;
+            R.kept[lane] = q.kept;
+            R.tau[lane] = q.tau;
+            R.cut[lane] = q.cut;
+            R.valid[lane] = q.valid;
         }
     } else {
-        // G consecutive threads per logit row (G a power of two, within a wave)
-        int G = 64;
-        while (G > 1 && G * nrv > kThreads) G >>= 1;
-        const int r = tid / G, gl = tid - (tid / G) * G;
+        // Stage the row's (logit row, chunk) partials in LDS, kStage at a
+        // time, four independent loads per lane in flight; lane r < nrv then
+        // merges logit row r's chunks in chunk order.
+        StageShared& stg = *stgp;
+        const int pairs = nrv * P.nch;
         float O = -SV_INF, M = -SV_INF, LX = -SV_INF;
         double S = 0.0;
-        if (r < nrv) {
-            const Partial* pp = P.part + (static_cast<size_t>(b) * P.nslot + rv_slot(r, Le, K)) * P.nch;
-            for (int c = gl; c < P.nch; c += G) {
-                const Partial q = load_partial(pp + c);
-                float On;
-                S = merge_stats(O, S, q.o, q.s, On);
-                O = On;
-                M = fmaxf(M, q.m);
-                LX = fmaxf(LX, q.lx);
-            }
-        }
-        for (int off = G >> 1; off >= 1; off >>= 1) {
-            const float O2 = __shfl_xor(O, off, 64);
-            const double S2 = __shfl_xor(S, off, 64);
-            const float M2 = __shfl_xor(M, off, 64);
-            const float L2 = __shfl_xor(LX, off, 64);
-            float On;
-            S = merge_stats(O, S, O2, S2, On);
-            O = On;
-            M = fmaxf(M, M2);
-            LX = fmaxf(LX, L2);
-        }
-        if (r < nrv && gl == 0) {
-            R.o[r] = O;
-            R.m[r] = M;
-            R.lx[r] = LX;
-            R.s[r] = S;
-            R.kept[r] = S;
-            R.tau[r] = 0u;
-            R.cut[r] = -1;
-            R.valid[r] = (S > 0.0 && S < static_cast<double>(SV_INF)) ? 1 : 0;
-        }
-    }
-    __syncthreads();
-    if (tid < 64) {
-        int bad = rowok ? 0 : 1;
-        for (int r = lane; r < nrv; r += 64) bad |= R.valid[r] ? 0 : 1;
-        bool rej = false;
-        double u_res = 0.0;
-        const bool rowbad = __ballot(bad) != 0ull;
-        int bad_tok = 0;
-        if (!rowbad && lane <= Le) {
-            const uint4 w = philox4x32_10(make_uint4(static_cast<uint32_t>(b), static_cast<uint32_t>(lane), 0u, 0u),
-                                          P.key0, P.key1);
-            u_res = word_uniform(w.y);
-            if (lane < Le) {
-                if (x < 0 || x >= P.V) {
-                    bad_tok = 1;
-                } else {
-                    const int rT = lane, rD = Le + 1 + lane;
-                    const float lt = R.lx[rT], ld = R.lx[rD];
-                    double pt = exp2(static_cast<double>(lt) * P.c64 - static_cast<double>(R.o[rT])) / R.kept[rT];
-                    double qd = exp2(static_cast<double>(ld) * P.c64 - static_cast<double>(R.o[rD])) / R.kept[rD];
-                    if (TOPP) {
-                        if (!is_kept(order_key(lt), x, R.tau[rT], R.cut[rT])) pt = 0.0;
-                        if (!is_kept(order_key(ld), x, R.tau[rD], R.cut[rD])) qd = 0.0;
+        for (int base = 0; base < pairs; base += kStage) {
+            const int cnt = min(kStage, pairs - base);
+            for (int q0 = 0; q0 < cnt; q0 += 4 * 64) {
+                Partial pq[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int pi = q0 + u * 64 + lane;
+                    if (pi < cnt) {
+                        const int pr = (base + pi) / P.nch, pc = (base + pi) - pr * P.nch;
+                        pq[u] = load_partial(P.part + (static_cast<size_t>(b) * P.nslot + rv_slot(pr, Le, K)) * P.nch + pc);
                     }
-                    const double r = qd > 0.0 ? pt / qd : (pt > 0.0 ? static_cast<double>(SV_INF) : 0.0);
-                    rej = !(word_uniform(w.x) < r);
-                    R.px[lane] = pt;
-                    R.qx[lane] = qd;
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int pi = q0 + u * 64 + lane;
+                    if (pi < cnt) {
+                        stg.o[pi] = pq[u].o;
+                        stg.m[pi] = pq[u].m;
+                        stg.lx[pi] = pq[u].lx;
+                        stg.s[pi] = pq[u].s;
+                    }
                 }
             }
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            if (lane < nrv) {
+                const int p0 = max(lane * P.nch, base), p1 = min((lane + 1) * P.nch, base + cnt);
+                for (int pi = p0; pi < p1; ++pi) {
+                    float On;
+                    S = merge_stats(O, S, stg.o[pi - base], stg.s[pi - base], On);
+                    O = On;
+                    M = fmaxf(M, stg.m[pi - base]);
+                    LX = fmaxf(LX, stg.lx[pi - base]);
+                }
+            }
+            __builtin_amdgcn_wave_barrier();
         }
-        const bool anybad = rowbad || (__ballot(bad_tok) != 0ull);
-        const unsigned long long rejm = __ballot(rej);
-        const int n = anybad ? 0 : (rejm ? (__ffsll(static_cast<long long>(rejm)) - 1) : Le);
-        const double un = __shfl(u_res, n, 64);
-        if (lane == 0) {
-            R.bad = anybad ? 1 : 0;
-            R.n = n;
-            R.u_res = un;
-            RowParam rp;
-            rp.mode = anybad ? MODE_SKIP : (n < Le ? MODE_RESID : MODE_BONUS);
-            rp.n = n;
-            rp.oT = R.o[n];
-            rp.keptT = R.kept[n];
-            rp.tauT = R.tau[n];
-            rp.cutT = R.cut[n];
-            const int rD = Le + 1 + n;
-            const bool resid = rp.mode == MODE_RESID;
-            rp.oD = resid ? R.o[rD] : 0.f;
-            rp.keptD = resid ? R.kept[rD] : 1.0;
-            rp.tauD = resid ? R.tau[rD] : 0u;
-            rp.cutD = resid ? R.cut[rD] : -1;
-            rp.u = un;
-            R.rp = rp;
+        if (lane < nrv) {
+            R.o[lane] = O;
+            R.m[lane] = M;
+            R.lx[lane] = LX;
+            R.s[lane] = S;
+            R.kept[lane] = S;
+            R.tau[lane] = 0u;
+            R.cut[lane] = -1;
+            R.valid[lane] = (S > 0.0 && S < static_cast<double>(SV_INF)) ? 1 : 0;
         }
     }
-    __syncthreads();
-    const int bad = R.bad, n = R.n;
-    for (int j = tid; j < K1; j += kThreads) {
+    __builtin_amdgcn_wave_barrier();
+    int bad = rowok ? 0 : 1;
+    for (int r = lane; r < nrv; r += 64) bad |= R.valid[r] ? 0 : 1;
+    const bool rowbad = __ballot(bad) != 0ull;
+    bool rej = false;
+    double u_res = 0.0, pt = nan64(), qd = nan64();
+    int bad_tok = 0;
+    if (!rowbad && lane <= Le) {
+        const uint4 w = philox4x32_10(make_uint4(static_cast<uint32_t>(b), static_cast<uint32_t>(lane), 0u, 0u),
+                                      P.key0, P.key1);
+        u_res = word_uniform(w.y);
+        if (lane < Le) {
+            if (x < 0 || x >= P.V) {
+                bad_tok = 1;
+            } else {
+                const int rT = lane, rD = Le + 1 + lane;
+                const float lt = R.lx[rT], ld = R.lx[rD];
+                pt = exp2(static_cast<double>(lt) * P.c64 - static_cast<double>(R.o[rT])) / R.kept[rT];
+                qd = exp2(static_cast<double>(ld) * P.c64 - static_cast<double>(R.o[rD])) / R.kept[rD];
+                if (TOPP) {
+                    if (!is_kept(order_key(lt), x, R.tau[rT], R.cut[rT])) pt = 0.0;
+                    if (!is_kept(order_key(ld), x, R.tau[rD], R.cut[rD])) qd = 0.0;
+                }
+                const double r = qd > 0.0 ? pt / qd : (pt > 0.0 ? static_cast<double>(SV_INF) : 0.0);
+                rej = !(word_uniform(w.x) < r);
+            }
+        }
+    }
+    const bool anybad = rowbad || (__ballot(bad_tok) != 0ull);
+    const unsigned long long rejm = __ballot(rej);
+    const int n = anybad ? 0 : (rejm ? (__ffsll(static_cast<long long>(rejm)) - 1) : Le);
+    const double un = __shfl(u_res, n, 64);
+    // outputs
+    for (int j = lane; j < K1; j += 64) {
         int v = -1;
-        if (!bad && j < n) v = P.tokens[static_cast<int64_t>(b) * K + j];
-        if (bad || j != n) P.out_tokens[static_cast<int64_t>(b) * K1 + j] = v;
+        if (!anybad && j < n) v = P.tokens[static_cast<int64_t>(b) * K + j];
+        if (anybad || j != n) P.out_tokens[static_cast<int64_t>(b) * K1 + j] = v;
     }
-    if (tid == 0) {
-        P.out_n[b] = bad ? -1 : n;
-        P.rowp[b] = R.rp;
+    if (lane == 0) {
+        P.out_n[b] = anybad ? -1 : n;
+        RowParam rp;
+        rp.mode = anybad ? MODE_SKIP : (n < Le ? MODE_RESID : MODE_BONUS);
+        rp.n = n;
+        rp.oT = R.o[n];
+        rp.keptT = R.kept[n];
+        rp.tauT = R.tau[n];
+        rp.cutT = R.cut[n];
+        const int rD = Le + 1 + n;
+        const bool resid = rp.mode == MODE_RESID;
+        rp.oD = resid ? R.o[rD] : 0.f;
+        rp.keptD = resid ? R.kept[rD] : 1.0;
+        rp.tauD = resid ? R.tau[rD] : 0u;
+        rp.cutD = resid ? R.cut[rD] : -1;
+        rp.u = un;
+        P.rowp[b] = rp;
         if (P.probe_row) {
             double* pr = P.probe_row + static_cast<size_t>(b) * 4;
             pr[0] = nan64();
             pr[1] = nan64();
-            pr[2] = bad ? nan64() : R.u_res;
-            pr[3] = bad ? -1.0 : static_cast<double>(n);
+            pr[2] = anybad ? nan64() : un;
+            pr[3] = anybad ? -1.0 : static_cast<double>(n);
         }
     }
     if (P.probe_pos) {
         double* pp = P.probe_pos + static_cast<size_t>(b) * K1 * 8;
-        for (int idx = tid; idx < K1 * 8; idx += kThreads) {
-            const int j = idx >> 3, f = idx & 7;
-            double v = nan64();
-            if (!bad) {
-                const int rD = Le + 1 + j;
-                switch (f) {
-                    case 0: if (j <= Le) v = R.m[j]; break;
-                    case 1: if (j <= Le) v = R.s[j] * exp2(static_cast<double>(R.o[j]) - static_cast<double>(R.m[j]) * P.c64); break;
-                    case 2: if (j < Le) v = R.m[rD]; break;
-                    case 3: if (j < Le) v = R.s[rD] * exp2(static_cast<double>(R.o[rD]) - static_cast<double>(R.m[rD]) * P.c64); break;
-                    case 4: if (j < Le) v = R.px[j]; break;
-                    case 5: if (j < Le) v = R.qx[j]; break;
-                    case 6: if (j <= Le) v = R.kept[j] / R.s[j]; break;
-                    default: if (j < Le) v = R.kept[rD] / R.s[rD]; break;
+        for (int j = 0; j < K1; ++j) {
+            // lane f of each group of 8 writes field f of position j
+            const double pj = __shfl(pt, j, 64), qj = __shfl(qd, j, 64);
+            if (lane < 8) {
+                const int f = lane;
+                double v = nan64();
+                if (!anybad) {
+                    const int rD = Le + 1 + j;
+                    switch (f) {
+                        case 0: if (j <= Le) v = R.m[j]; break;
+                        case 1: if (j <= Le) v = R.s[j] * exp2(static_cast<double>(R.o[j]) - static_cast<double>(R.m[j]) * P.c64); break;
+                        case 2: if (j < Le) v = R.m[rD]; break;
+                        case 3: if (j < Le) v = R.s[rD] * exp2(static_cast<double>(R.o[rD]) - static_cast<double>(R.m[rD]) * P.c64); break;
+                        case 4: if (j < Le) v = pj; break;
+                        case 5: if (j < Le) v = qj; break;
+                        case 6: if (j <= Le) v = R.kept[j] / R.s[j]; break;
+                        default: if (j < Le) v = R.kept[rD] / R.s[rD]; break;
+                    }
                 }
+                pp[j * 8 + f] = v;
             }
-            pp[idx] = v;
         }
     }
 }
@@ -441,8 +453,8 @@ __device__ __forceinline__ void reduce_lane(const RowGrid& g, const uint4* raw, 
 template <int DT, int U, bool TOPP>
 __global__ __launch_bounds__(kThreads) void k_stats(Params P) {
     __shared__ float sh_o[kWaves], sh_s[kWaves], sh_m[kWaves], sh_lx[kWaves];
-    __shared__ int s_last;
     __shared__ RowShared R;
+    __shared__ StageShared stg;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int item = blockIdx.x;
     const int rvi = item / P.nch;
@@ -498,7 +510,12 @@ __global__ __launch_bounds__(kThreads) void k_stats(Params P) {
         sh_lx[wv] = Lw;
     }
     __syncthreads();
-    if (tid == 0) {
+    // Only wave 0 goes on: it publishes the partial, counts the arrival and,
+    // for the row's last arrival, makes the decision.  The other waves leave
+    // now, so a workgroup waiting on its atomic holds one wave, not four.
+    if (wv != 0) return;
+    int last = 0;
+    if (lane == 0) {
         float O = sh_o[0], M = sh_m[0], LX = sh_lx[0];
         for (int w = 1; w < kWaves; ++w) {
             O = fmaxf(O, sh_o[w]);
@@ -512,17 +529,17 @@ __global__ __launch_bounds__(kThreads) void k_stats(Params P) {
         store_partial(P.part + static_cast<size_t>(rvi) * P.nch + chunk, O, M, LX, S);
         if (!TOPP) {
             stores_done();
-            s_last = arrive_last(P.row_cnt + static_cast<size_t>(b) * kCounterStride,
-                                 static_cast<uint32_t>((2 * Le + 1) * P.nch))
-                         ? 1
-                         : 0;
+            last = arrive_last(P.row_cnt + static_cast<size_t>(b) * kCounterStride,
+                               static_cast<uint32_t>((2 * Le + 1) * P.nch))
+                       ? 1
+                       : 0;
         }
     }
     if (TOPP) return;
-    __syncthreads();
-    if (!s_last) return;
-    if (tid == 0) counter_reset(P.row_cnt + static_cast<size_t>(b) * kCounterStride);
-    row_decide<DT, false>(P, b, R);
+    last = __shfl(last, 0, 64);
+    if (!last) return;
+    if (lane == 0) counter_reset(P.row_cnt + static_cast<size_t>(b) * kCounterStride);
+    row_decide<DT, false>(P, b, R, &stg);
 }
 
 // ---------------------------------------------------------------------------
@@ -892,78 +909,12 @@ __device__ void select_nucleus(const Params& P, const uint8_t* row, float O, dou
     }
 }
 
-// Weights of one resample chunk [i0, i1) in id order: thread t owns ids
-// i0 + tt*tile + t*kResTile + [0, kResTile) for tiles tt.  w is the residual
-// max(0, p' - q') (or p' for the bonus), p is p'.  When the chunk is whole and
-// both rows are 16-byte aligned every load is issued before any use.
-template <int DT, bool TOPP>
-__device__ __forceinline__ void eval_chunk(const uint8_t* rowT, const uint8_t* rowD, bool resid, int64_t i0,
-                                           int64_t i1, const RowParam& rp, float c_hi, float c_lo, float invT,
-                                           float invD, float (&w)[kResTiles][kResTile],
-                                           float (&p)[kResTiles][kResTile]) {
-    constexpr int E = Fmt<DT>::E, VE = Fmt<DT>::VE, NV = kResTile / VE;
-    constexpr int64_t tile = static_cast<int64_t>(kThreads) * kResTile;
-    float lt[kResTiles][kResTile], ld[kResTiles][kResTile];
-    const bool fast = (i1 - i0 == kResChunk) && ((reinterpret_cast<uintptr_t>(rowT + i0 * E) & 15) == 0) &&
-                      (!resid || (reinterpret_cast<uintptr_t>(rowD + i0 * E) & 15) == 0);
-    if (fast) {
-        uint4 vt[kResTiles][NV], vd[kResTiles][NV];
-#pragma unroll
-        for (int tt = 0; tt < kResTiles; ++tt) {
-            const int64_t id0 = i0 + tt * tile + static_cast<int64_t>(threadIdx.x) * kResTile;
-#pragma unroll
-            for (int k = 0; k < NV; ++k) vt[tt][k] = gload16(reinterpret_cast<const uint4*>(rowT + id0 * E) + k);
-            if (resid) {
-#pragma unroll
-                for (int k = 0; k < NV; ++k) vd[tt][k] = gload16(reinterpret_cast<const uint4*>(rowD + id0 * E) + k);
-            }
-        }
-#pragma unroll
-        for (int tt = 0; tt < kResTiles; ++tt)
-#pragma unroll
-            for (int k = 0; k < NV; ++k) {
-                unpack<DT>(vt[tt][k], lt[tt] + k * VE);
-                if (resid) unpack<DT>(vd[tt][k], ld[tt] + k * VE);
-            }
-    } else {
-#pragma unroll
-        for (int tt = 0; tt < kResTiles; ++tt) {
-            const int64_t id0 = i0 + tt * tile + static_cast<int64_t>(threadIdx.x) * kResTile;
-            const int nv = static_cast<int>(min<int64_t>(max<int64_t>(i1 - id0, 0), kResTile));
-            load8<DT>(rowT, id0, nv, lt[tt]);
-            if (resid) load8<DT>(rowD, id0, nv, ld[tt]);
-        }
-    }
-#pragma unroll
-    for (int tt = 0; tt < kResTiles; ++tt) {
-        const int64_t id0 = i0 + tt * tile + static_cast<int64_t>(threadIdx.x) * kResTile;
-#pragma unroll
-        for (int i = 0; i < kResTile; ++i) {
-            float pt = tempexp(lt[tt][i], c_hi, c_lo, rp.oT) * invT;
-            if (TOPP && !is_kept(order_key(lt[tt][i]), id0 + i, rp.tauT, rp.cutT)) pt = 0.f;
-            float wi = pt;
-            if (resid) {
-                float qd = tempexp(ld[tt][i], c_hi, c_lo, rp.oD) * invD;
-                if (TOPP && !is_kept(order_key(ld[tt][i]), id0 + i, rp.tauD, rp.cutD)) qd = 0.f;
-                wi = fmaxf(pt - qd, 0.f);
-            }
-            if (id0 + i >= i1) {
-                pt = 0.f;
-                wi = 0.f;
-            }
-            w[tt][i] = wi;
-            p[tt][i] = pt;
-        }
-    }
-}
-
 template <int DT>
 __global__ __launch_bounds__(kThreads) void k_topp(Params P) {
     __shared__ SelShared sh;
     __shared__ RowShared R;
     __shared__ float s_o, s_m, s_lx;
     __shared__ double s_s;
-    __shared__ int s_last;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int rvi = blockIdx.x;
     const int b = rvi / P.nslot;
@@ -1008,22 +959,105 @@ __global__ __launch_bounds__(kThreads) void k_topp(Params P) {
         st.tau = tau;
         st.cut = cut;
     }
-    if (tid == 0) {
+    if (wv != 0) return;
+    int last = 0;
+    if (lane == 0) {
         store_rvstate(P.rv + rvi, st);
         stores_done();
-        s_last = arrive_last(P.row_cnt + static_cast<size_t>(b) * kCounterStride, static_cast<uint32_t>(2 * Le + 1))
-                     ? 1
-                     : 0;
+        last = arrive_last(P.row_cnt + static_cast<size_t>(b) * kCounterStride, static_cast<uint32_t>(2 * Le + 1)) ? 1 : 0;
     }
-    __syncthreads();
-    if (!s_last) return;
-    if (tid == 0) counter_reset(P.row_cnt + static_cast<size_t>(b) * kCounterStride);
-    row_decide<DT, true>(P, b, R);
+    last = __shfl(last, 0, 64);
+    if (!last) return;
+    if (lane == 0) counter_reset(P.row_cnt + static_cast<size_t>(b) * kCounterStride);
+    row_decide<DT, true>(P, b, R, nullptr);
 }
 
 // ---------------------------------------------------------------------------
-// Resample pass.
+// Resample pass: workgroups of kRThreads threads; workgroup (b, c) covers
+// steps [c*res_steps, (c+1)*res_steps) of row b, a step being kStepIds
+// consecutive ids with kRun per thread.  It publishes the residual (or bonus)
+// mass and the target mass of every step it covers; the row's last workgroup
+// then finds the step holding t = u*Z and rescans that step alone.
 // ---------------------------------------------------------------------------
+constexpr int kRThreads = 1024;
+constexpr int kRWaves = kRThreads / 64;
+constexpr int kRun = 8;
+constexpr int kStepIds = kRThreads * kRun;
+constexpr int kGroup = 4;  // steps whose loads are in flight together
+static_assert(kStepIds == kResStepIds, "host and kernels must agree on the resample step");
+
+// ids [id0, id0 + kRun) of a row; ids at or past V read as -inf.
+template <int DT>
+__device__ __forceinline__ void load_run(const uint8_t* row, int64_t id0, int V, bool aligned, float* f) {
+    constexpr int E = Fmt<DT>::E, VE = Fmt<DT>::VE;
+    const int64_t left = static_cast<int64_t>(V) - id0;
+    if (aligned && left >= kRun) {
+        const uint4* vp = reinterpret_cast<const uint4*>(row + id0 * E);
+#pragma unroll
+        for (int k = 0; k < kRun / VE; ++k) unpack<DT>(gload16(vp + k), f + k * VE);
+    } else {
+#pragma unroll
+        for (int i = 0; i < kRun; ++i) f[i] = (i < left) ? load_elem<DT>(row, id0 + i) : -SV_INF;
+    }
+}
+
+// Residual weights w = max(0, p' - q') (or p' for the bonus) and p' of a run.
+template <bool TOPP>
+__device__ __forceinline__ void run_weights(const float* lt, const float* ld, bool resid, int64_t id0, const RowParam& rp,
+                                            float c_hi, float c_lo, float invT, float invD, float* w, float* p) {
+#pragma unroll
+    for (int i = 0; i < kRun; ++i) {
+        float pt = tempexp(lt[i], c_hi, c_lo, rp.oT) * invT;
+        if (TOPP && !is_kept(order_key(lt[i]), id0 + i, rp.tauT, rp.cutT)) pt = 0.f;
+        float wi = pt;
+        if (resid) {
+            float qd = tempexp(ld[i], c_hi, c_lo, rp.oD) * invD;
+            if (TOPP && !is_kept(order_key(ld[i]), id0 + i, rp.tauD, rp.cutD)) qd = 0.f;
+            wi = fmaxf(pt - qd, 0.f);
+        }
+        w[i] = wi;
+        p[i] = pt;
+    }
+}
+
+// Prefix sums over the kRThreads threads of a resample workgroup.
+__device__ __forceinline__ void rblock_scan(double x, double& incl, double& excl, double& total) {
+    __shared__ double ws[kRWaves];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const double wi = wave_incl_scan(x, lane);
+    double we = __shfl_up(wi, 1, 64);
+    if (lane == 0) we = 0.0;
+    if (lane == 63) ws[wv] = wi;
+    __syncthreads();
+    double off = 0.0;
+    for (int k = 0; k < wv; ++k) off += ws[k];
+    double tot = 0.0;
+    for (int k = 0; k < kRWaves; ++k) tot += ws[k];
+    incl = off + wi;
+    excl = off + we;
+    total = tot;
+    __syncthreads();
+}
+__device__ __forceinline__ int rblock_min_int(int v) {
+    __shared__ int ws[kRWaves];
+    v = wave_min_int(v);
+    if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = v;
+    __syncthreads();
+    int r = ws[0];
+    for (int k = 1; k < kRWaves; ++k) r = min(r, ws[k]);
+    __syncthreads();
+    return r;
+}
+__device__ __forceinline__ int rblock_max_int(int v) {
+    __shared__ int ws[kRWaves];
+    v = wave_max_int(v);
+    if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = v;
+    __syncthreads();
+    int r = ws[0];
+    for (int k = 1; k < kRWaves; ++k) r = max(r, ws[k]);
+    __syncthreads();
+    return r;
+}
 
 __device__ __forceinline__ double ld_agent_d(const double* p) {
     return __longlong_as_double(static_cast<long long>(ld_agent(p)));
@@ -1032,87 +1066,103 @@ __device__ __forceinline__ void st_agent_d(double* p, double v) {
     st_agent(p, static_cast<uint64_t>(__double_as_longlong(v)));
 }
 
-// One workgroup per (row b, chunk of kResChunk ids): the chunk's residual (or
-// bonus) mass and target mass in float64.  The last chunk of a row to finish
-// then draws the row's token: the chunk holding t = u*Z, rescanned in id
-// order.
 template <int DT, bool TOPP>
-__global__ __launch_bounds__(kThreads) void k_resample(Params P) {
-    __shared__ double sh_w[kWaves], sh_p[kWaves];
+__global__ __launch_bounds__(kRThreads) void k_resample(Params P) {
+    __shared__ double sw[kRWaves][kGroup], sp[kRWaves][kGroup];
     __shared__ int s_last, s_y;
-    __shared__ double s_pre_first[kThreads], s_pre_last[kThreads];
+    __shared__ double s_pre[1];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int b = blockIdx.x / P.nch2;
-    const int c = blockIdx.x - b * P.nch2;
+    const int b = blockIdx.x / P.res_split;
+    const int c = blockIdx.x - b * P.res_split;
     const RowParam rp = P.rowp[b];
     // rowp was written by this call's decision; anything else is skipped
     if ((rp.mode != MODE_RESID && rp.mode != MODE_BONUS) || rp.n < 0 || rp.n > P.K) return;
     const bool resid = rp.mode == MODE_RESID;
     const uint8_t* rowT = row_ptr<DT>(P, true, b, rp.n);
-    const uint8_t* rowD = resid ? row_ptr<DT>(P, false, b, rp.n) : nullptr;
+    const uint8_t* rowD = resid ? row_ptr<DT>(P, false, b, rp.n) : rowT;
+    const bool aligned = ((reinterpret_cast<uintptr_t>(rowT) & 15) == 0) && ((reinterpret_cast<uintptr_t>(rowD) & 15) == 0);
     const float invT = static_cast<float>(1.0 / rp.keptT);
     const float invD = resid ? static_cast<float>(1.0 / rp.keptD) : 0.f;
     double* cm = P.cmass + static_cast<size_t>(b) * P.nch2 * 2;
-    {
-        const int64_t i0 = static_cast<int64_t>(c) * kResChunk;
-        const int64_t i1 = min<int64_t>(i0 + kResChunk, P.V);
-        float w[kResTiles][kResTile], p[kResTiles][kResTile];
-        eval_chunk<DT, TOPP>(rowT, rowD, resid, i0, i1, rp, P.c_hi, P.c_lo, invT, invD, w, p);
-        double aw = 0.0, ap = 0.0;
-#pragma unroll
-        for (int t = 0; t < kResTiles; ++t)
-#pragma unroll
-            for (int i = 0; i < kResTile; ++i) {
-                aw += static_cast<double>(w[t][i]);
-                ap += static_cast<double>(p[t][i]);
-            }
-        aw = wave_sum(aw);
-        ap = wave_sum(ap);
-        if (lane == 0) {
-            sh_w[wv] = aw;
-            sh_p[wv] = ap;
-        }
-        __syncthreads();
-        if (tid == 0) {
-            double W = 0.0, Pm = 0.0;
-            for (int k = 0; k < kWaves; ++k) {
-                W += sh_w[k];
-                Pm += sh_p[k];
-            }
-            st_agent_d(cm + 2 * c, W);
-            st_agent_d(cm + 2 * c + 1, Pm);
-            stores_done();
-            s_last = arrive_last(P.res_cnt + static_cast<size_t>(b) * kCounterStride, static_cast<uint32_t>(P.nch2))
-                         ? 1
-                         : 0;
-        }
-        __syncthreads();
-        if (!s_last) return;
-        if (tid == 0) counter_reset(P.res_cnt + static_cast<size_t>(b) * kCounterStride);
-    }
 
-    // Chunk masses: thread t owns chunks [t*g, t*g + g), summed in order; a
-    // block scan gives each thread its prefix.
-    const int g = (P.nch2 + kThreads - 1) / kThreads;
-    const int c0 = min(tid * g, P.nch2), c1 = min(c0 + g, P.nch2);
+    const int s0 = c * P.res_steps;
+    const int s1 = min(s0 + P.res_steps, P.nch2);
+    bool stored = false;
+    for (int g0 = s0; g0 < s1; g0 += kGroup) {
+        const int gn = min(kGroup, s1 - g0);
+        float lt[kGroup][kRun], ld[kGroup][kRun];
+#pragma unroll
+        for (int k = 0; k < kGroup; ++k) {
+            if (k < gn) {
+                const int64_t id0 = static_cast<int64_t>(g0 + k) * kStepIds + static_cast<int64_t>(tid) * kRun;
+                load_run<DT>(rowT, id0, P.V, aligned, lt[k]);
+                if (resid) load_run<DT>(rowD, id0, P.V, aligned, ld[k]);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < kGroup; ++k) {
+            double ws = 0.0, ps = 0.0;
+            if (k < gn) {
+                const int64_t id0 = static_cast<int64_t>(g0 + k) * kStepIds + static_cast<int64_t>(tid) * kRun;
+                float w[kRun], p[kRun];
+                run_weights<TOPP>(lt[k], ld[k], resid, id0, rp, P.c_hi, P.c_lo, invT, invD, w, p);
+#pragma unroll
+                for (int i = 0; i < kRun; ++i) {
+                    ws += static_cast<double>(w[i]);
+                    ps += static_cast<double>(p[i]);
+                }
+            }
+            ws = wave_sum(ws);
+            ps = wave_sum(ps);
+            if (lane == 0) {
+                sw[wv][k] = ws;
+                sp[wv][k] = ps;
+            }
+        }
+        __syncthreads();
+        if (tid < gn) {
+            double W = 0.0, Pm = 0.0;
+            for (int w = 0; w < kRWaves; ++w) {
+                W += sw[w][tid];
+                Pm += sp[w][tid];
+            }
+            st_agent_d(cm + 2 * (g0 + tid), W);
+            st_agent_d(cm + 2 * (g0 + tid) + 1, Pm);
+            stored = true;
+        }
+        __syncthreads();
+    }
+    if (stored) stores_done();
+    __syncthreads();
+    if (tid == 0)
+        s_last = arrive_last(P.res_cnt + static_cast<size_t>(b) * kCounterStride, static_cast<uint32_t>(P.res_split)) ? 1 : 0;
+    __syncthreads();
+    if (!s_last) return;
+    if (tid == 0) counter_reset(P.res_cnt + static_cast<size_t>(b) * kCounterStride);
+
+    // Last workgroup of the row: step masses in id order (thread t owns steps
+    // [t*g, t*g + g)), a prefix scan, the step holding t, then that step alone.
+    const int ns = P.nch2;
+    const int g = (ns + kRThreads - 1) / kRThreads;
+    const int e0 = min(tid * g, ns), e1 = min(e0 + g, ns);
     double wsum = 0.0, psum = 0.0;
-    for (int k = c0; k < c1; ++k) {
+    for (int k = e0; k < e1; ++k) {
         wsum += ld_agent_d(cm + 2 * k);
         psum += ld_agent_d(cm + 2 * k + 1);
     }
     double incl, excl, Z;
-    block_scan(wsum, incl, excl, Z);
+    rblock_scan(wsum, incl, excl, Z);
     int sel = 0;
     if (!(Z > 0.0)) {
         // A rejection implies p(x) < q(x), hence positive residual mass;
         // none survives only through rounding: draw from p' instead.
         sel = 1;
-        block_scan(psum, incl, excl, Z);
+        rblock_scan(psum, incl, excl, Z);
     }
     const double t = rp.u * Z;
     int first = 0x7FFFFFFF, lastnz = -1;
     double pre = excl, pf = 0.0, pl = 0.0;
-    for (int k = c0; k < c1; ++k) {
+    for (int k = e0; k < e1; ++k) {
         const double m = ld_agent_d(cm + 2 * k + sel);
         if (m > 0.0) {
             if (first == 0x7FFFFFFF && pre + m > t) {
@@ -1124,65 +1174,48 @@ __global__ __launch_bounds__(kThreads) void k_resample(Params P) {
         }
         pre += m;
     }
-    s_pre_first[tid] = pf;
-    s_pre_last[tid] = pl;
-    const int fc = block_min_int(first);
-    const int lc = block_max_int(lastnz);
-    int ch;
-    double cpre;
-    if (fc != 0x7FFFFFFF) {
-        ch = fc;
-        cpre = s_pre_first[fc / g];
-    } else {
-        ch = lc < 0 ? 0 : lc;
-        cpre = lc < 0 ? 0.0 : s_pre_last[lc / g];
-    }
+    const int fe = rblock_min_int(first);
+    if (first == fe && fe != 0x7FFFFFFF) s_pre[0] = pf;
+    const int le = rblock_max_int(lastnz);
+    if (fe == 0x7FFFFFFF && lastnz == le && le >= 0) s_pre[0] = pl;
     if (tid == 0) s_y = -1;
     __syncthreads();
+    const int st = (fe != 0x7FFFFFFF) ? fe : (le < 0 ? 0 : le);
+    const double spre = (fe == 0x7FFFFFFF && le < 0) ? 0.0 : s_pre[0];
+    __syncthreads();
 
-    // Rescan the chosen chunk in id order: tile by tile, a prefix sum over
-    // threads (each thread owns kResTile consecutive ids), then one thread
-    // walks its run.  Both tiles are loaded before the scans.
-    constexpr int64_t tile = static_cast<int64_t>(kThreads) * kResTile;
-    const int64_t j0 = static_cast<int64_t>(ch) * kResChunk;
-    const int64_t j1 = min<int64_t>(j0 + kResChunk, P.V);
-    float w[kResTiles][kResTile], p[kResTiles][kResTile];
-    eval_chunk<DT, TOPP>(rowT, rowD, resid, j0, j1, rp, P.c_hi, P.c_lo, invT, invD, w, p);
-    double carry = cpre;
+    const int64_t id0 = static_cast<int64_t>(st) * kStepIds + static_cast<int64_t>(tid) * kRun;
+    float lt[kRun], ld[kRun], w[kRun], p[kRun];
+    load_run<DT>(rowT, id0, P.V, aligned, lt);
+    if (resid) load_run<DT>(rowD, id0, P.V, aligned, ld);
+    run_weights<TOPP>(lt, ld, resid, id0, rp, P.c_hi, P.c_lo, invT, invD, w, p);
+    double xs = 0.0;
     int lastpos = -1;
-    for (int tt = 0; tt < kResTiles; ++tt) {
-        const int64_t id0 = j0 + tt * tile + static_cast<int64_t>(tid) * kResTile;
-        float v[kResTile];
-        double xs = 0.0;
 #pragma unroll
-        for (int i = 0; i < kResTile; ++i) {
-            v[i] = sel ? p[tt][i] : w[tt][i];
-            xs += static_cast<double>(v[i]);
-            if (v[i] > 0.f) lastpos = static_cast<int>(id0 + i);
-        }
-        double ti, te, tot;
-        block_scan(xs, ti, te, tot);
-        const int hit = (xs > 0.0 && carry + ti > t) ? tid : 0x7FFFFFFF;
-        const int fh = block_min_int(hit);
-        if (fh != 0x7FFFFFFF) {
-            if (tid == fh) {
-                double run = carry + te;
-                int y = -1, lastw = -1;
-                for (int i = 0; i < kResTile; ++i) {
-                    if (v[i] > 0.f) {
-                        lastw = static_cast<int>(id0 + i);
-                        if (y < 0 && run + static_cast<double>(v[i]) > t) y = lastw;
-                    }
-                    run += static_cast<double>(v[i]);
-                }
-                s_y = y >= 0 ? y : lastw;
-            }
-            __syncthreads();
-            break;
-        }
-        carry += tot;
+    for (int i = 0; i < kRun; ++i) {
+        const float v = sel ? p[i] : w[i];
+        w[i] = v;
+        xs += static_cast<double>(v);
+        if (v > 0.f) lastpos = static_cast<int>(id0 + i);
     }
-    const int lp = block_max_int(lastpos);
+    double ti, te, tot;
+    rblock_scan(xs, ti, te, tot);
+    const int hit = (xs > 0.0 && spre + ti > t) ? tid : 0x7FFFFFFF;
+    const int fh = rblock_min_int(hit);
+    if (tid == fh && fh != 0x7FFFFFFF) {
+        double run = spre + te;
+        int y = -1, lastw = -1;
+#pragma unroll
+        for (int i = 0; i < kRun; ++i) {
+            if (w[i] > 0.f) {
+                lastw = static_cast<int>(id0 + i);
+                if (y < 0 && run + static_cast<double>(w[i]) > t) y = lastw;
+            }
+            run += static_cast<double>(w[i]);
+        }
+        s_y = y >= 0 ? y : lastw;
+    }
+    const int lp = rblock_max_int(lastpos);
     if (tid == 0) {
         const int y = s_y >= 0 ? s_y : (lp >= 0 ? lp : 0);
         P.out_tokens[static_cast<size_t>(b) * (P.K + 1) + rp.n] = y;
@@ -1254,13 +1287,13 @@ hipError_t launch_topp(const Params& p, int dtype, hipStream_t s) {
 }
 
 hipError_t launch_resample(const Params& p, int dtype, bool topp, hipStream_t s) {
-    const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(p.B) * p.nch2);
+    const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(p.B) * p.res_split);
     if (dtype == DT_BF16) {
-        if (topp) hipLaunchKernelGGL((k_resample<DT_BF16, true>), dim3(grid), dim3(kThreads), 0, s, p);
-        else hipLaunchKernelGGL((k_resample<DT_BF16, false>), dim3(grid), dim3(kThreads), 0, s, p);
+        if (topp) hipLaunchKernelGGL((k_resample<DT_BF16, true>), dim3(grid), dim3(kRThreads), 0, s, p);
+        else hipLaunchKernelGGL((k_resample<DT_BF16, false>), dim3(grid), dim3(kRThreads), 0, s, p);
     } else {
-        if (topp) hipLaunchKernelGGL((k_resample<DT_F32, true>), dim3(grid), dim3(kThreads), 0, s, p);
-        else hipLaunchKernelGGL((k_resample<DT_F32, false>), dim3(grid), dim3(kThreads), 0, s, p);
+        if (topp) hipLaunchKernelGGL((k_resample<DT_F32, true>), dim3(grid), dim3(kRThreads), 0, s, p);
+        else hipLaunchKernelGGL((k_resample<DT_F32, false>), dim3(grid), dim3(kRThreads), 0, s, p);
     }
     return hipGetLastError();
 }

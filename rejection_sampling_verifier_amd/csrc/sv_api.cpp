@@ -195,7 +195,7 @@ int verify_impl(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_t
     // statistics pass: chunks of at most `cv` 16-byte vectors per workgroup
     const int64_t nvec_max = (static_cast<int64_t>(V) * E + 15) / 16 + 1;
     int unroll = env_int("SPECVERIFY_STATS_UNROLL", sv::kStatsUnroll);
-    if (unroll != 8) unroll = 4;
+    if (unroll != 4) unroll = 8;
     // a statistics workgroup reads one chunk of kThreads*unroll vectors; only
     // a row's last chunk is partial
     const int cv = sv::kThreads * unroll;
@@ -204,7 +204,7 @@ int verify_impl(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_t
     // resample pass: steps of kResStepIds ids; about one workgroup per CU
     // over the batch, each covering res_steps consecutive steps of one row
     const int nch2 = (V + sv::kResStepIds - 1) / sv::kResStepIds;
-    int res_split = (device_cus() + B - 1) / B;
+    int res_split = (env_int("SPECVERIFY_RES_WG", device_cus()) + B - 1) / B;
     if (res_split > nch2) res_split = nch2;
     if (res_split < 1) res_split = 1;
     const int res_steps = (nch2 + res_split - 1) / res_split;

@@ -11,7 +11,7 @@ constexpr int kThreads = 256;        // every kernel runs 4 wave64s per workgrou
 constexpr int kWaves = kThreads / 64;
 constexpr int kMaxK = 16;
 constexpr int kMaxSlots = 2 * kMaxK + 1;
-constexpr int kStatsUnroll = 4;      // default 16-byte vectors in flight per lane per step
+constexpr int kStatsUnroll = 8;      // default 16-byte vectors in flight per lane per step
 constexpr int kResTile = 8;          // consecutive ids per thread in the id-ordered scans
 constexpr int kResStepIds = 8192;    // ids per resample step (1024 threads x 8)
 

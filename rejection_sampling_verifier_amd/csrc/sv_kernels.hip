@@ -452,7 +452,9 @@ __device__ __forceinline__ void reduce_lane(const RowGrid& g, const uint4* raw, 
 
 template <int DT, int U, bool TOPP>
 __global__ __launch_bounds__(kThreads) void k_stats(Params P) {
-    __shared__ float sh_o[kWaves], sh_s[kWaves], sh_m[kWaves], sh_lx[kWaves];
+    __shared__ float sh_o[kWaves], sh_s[kWaves], sh_m[kWaves];
+    __shared__ float sh_lxv;
+    __shared__ int sh_lxtag, s_last;
     __shared__ RowShared R;
     __shared__ StageShared stg;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -496,37 +498,40 @@ __global__ __launch_bounds__(kThreads) void k_stats(Params P) {
     float lx = -SV_INF, m, o, sl;
     if (k0 == 0 || k0 + STEP >= g.nvec - 1) reduce_lane<DT, U, true>(g, raw, k0, k1, P.V, P.c_hi, P.c_lo, kx, rx, lx, m, o, sl);
     else reduce_lane<DT, U, false>(g, raw, k0, k1, P.V, P.c_hi, P.c_lo, kx, rx, lx, m, o, sl);
+    // the one lane holding the drafted id's vector hands its logit over,
+    // tagged with this workgroup's id (LDS is not cleared between workgroups)
+    {
+        const int64_t rel = kx - k0 - tid;
+        if (kx >= k0 && rel >= 0 && rel % kThreads == 0 && rel / kThreads < U) {
+            sh_lxv = lx;
+            sh_lxtag = item;
+        }
+    }
 
     // workgroup combine: exact power-of-two rescaling to the largest offset
     const float Ow = wave_max(o);
     const float sc = (o == -SV_INF) ? sl : ldexpf(sl, static_cast<int>(fmaxf(o - Ow, -256.f)));
     const float Sw = wave_sum(sc);
     const float Mw = wave_max(m);
-    const float Lw = wave_max(lx);
     if (lane == 0) {
         sh_o[wv] = Ow;
         sh_s[wv] = Sw;
         sh_m[wv] = Mw;
-        sh_lx[wv] = Lw;
     }
     __syncthreads();
-    // Only wave 0 goes on: it publishes the partial, counts the arrival and,
-    // for the row's last arrival, makes the decision.  The other waves leave
-    // now, so a workgroup waiting on its atomic holds one wave, not four.
-    if (wv != 0) return;
-    int last = 0;
-    if (lane == 0) {
-        float O = sh_o[0], M = sh_m[0], LX = sh_lx[0];
+    if (tid == 0) {
+        float O = sh_o[0], M = sh_m[0];
         for (int w = 1; w < kWaves; ++w) {
             O = fmaxf(O, sh_o[w]);
             M = fmaxf(M, sh_m[w]);
-            LX = fmaxf(LX, sh_lx[w]);
         }
         double S = 0.0;
         for (int w = 0; w < kWaves; ++w)
             S += (sh_o[w] == -SV_INF) ? static_cast<double>(sh_s[w])
                                       : ldexp(static_cast<double>(sh_s[w]), static_cast<int>(fmaxf(sh_o[w] - O, -1100.f)));
+        const float LX = (kx >= k0 && kx < k0 + STEP && sh_lxtag == item) ? sh_lxv : -SV_INF;
         store_partial(P.part + static_cast<size_t>(rvi) * P.nch + chunk, O, M, LX, S);
+        int last = 0;
         if (!TOPP) {
             stores_done();
             last = arrive_last(P.row_cnt + static_cast<size_t>(b) * kCounterStride,
@@ -534,10 +539,12 @@ __global__ __launch_bounds__(kThreads) void k_stats(Params P) {
                        ? 1
                        : 0;
         }
+        s_last = last;
     }
     if (TOPP) return;
-    last = __shfl(last, 0, 64);
-    if (!last) return;
+    __syncthreads();
+    // the row's last arrival: wave 0 makes the decision
+    if (!s_last || wv != 0) return;
     if (lane == 0) counter_reset(P.row_cnt + static_cast<size_t>(b) * kCounterStride);
     row_decide<DT, false>(P, b, R, &stg);
 }
@@ -983,22 +990,67 @@ constexpr int kRThreads = 1024;
 constexpr int kRWaves = kRThreads / 64;
 constexpr int kRun = 8;
 constexpr int kStepIds = kRThreads * kRun;
-constexpr int kGroup = 4;  // steps whose loads are in flight together
+// Steps whose loads are in flight together: four 16-byte vectors per thread
+// and tensor, which keeps the unpacked runs within the 128 registers a
+// 1024-thread workgroup allows.
+template <int DT> constexpr int group_steps() { return 4 * Fmt<DT>::VE / kRun; }
 static_assert(kStepIds == kResStepIds, "host and kernels must agree on the resample step");
 
-// ids [id0, id0 + kRun) of a row; ids at or past V read as -inf.
+// A readable 16-byte vector that stands in for loads past the end of a row.
+__device__ const uint4 kPadVec = {0u, 0u, 0u, 0u};
+
+// Loading a run of ids [id0, id0 + kRun) of a row as raw 16-byte vectors
+// takes two phases so that no load waits on another: issue_run only issues
+// loads (on aligned rows a vector wholly in range is one 16-byte load and any
+// other vector loads the pad; rows not 16-byte aligned load elements at
+// clamped ids); on aligned rows, the one run whose vector straddles V is then
+// reloaded by elements (run_straddles, load_run_elems).  Values at ids >= V
+// are left undefined and become -inf in unpack_masked.
 template <int DT>
-__device__ __forceinline__ void load_run(const uint8_t* row, int64_t id0, int V, bool aligned, float* f) {
-    constexpr int E = Fmt<DT>::E, VE = Fmt<DT>::VE;
-    const int64_t left = static_cast<int64_t>(V) - id0;
-    if (aligned && left >= kRun) {
-        const uint4* vp = reinterpret_cast<const uint4*>(row + id0 * E);
+__device__ __forceinline__ void load_run_elems(const uint8_t* row, int64_t id0, int V, uint4* v) {
+    constexpr int NVR = kRun / Fmt<DT>::VE;
+    const int64_t last = static_cast<int64_t>(V) - 1;
+    uint32_t w[4 * NVR];
+    if (DT == DT_F32) {
+        const uint32_t* r = reinterpret_cast<const uint32_t*>(row);
 #pragma unroll
-        for (int k = 0; k < kRun / VE; ++k) unpack<DT>(gload16(vp + k), f + k * VE);
+        for (int i = 0; i < kRun; ++i) w[i] = r[min(id0 + i, last)];
     } else {
+        const uint16_t* r = reinterpret_cast<const uint16_t*>(row);
+        uint32_t h[kRun];
 #pragma unroll
-        for (int i = 0; i < kRun; ++i) f[i] = (i < left) ? load_elem<DT>(row, id0 + i) : -SV_INF;
+        for (int i = 0; i < kRun; ++i) h[i] = r[min(id0 + i, last)];
+#pragma unroll
+        for (int i = 0; i < kRun; i += 2) w[i / 2] = h[i] | (h[i + 1] << 16);
     }
+#pragma unroll
+    for (int q = 0; q < NVR; ++q) v[q] = make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
+}
+template <int DT>
+__device__ __forceinline__ void issue_run(const uint8_t* row, int64_t id0, int V, bool aligned, uint4* v) {
+    constexpr int E = Fmt<DT>::E, VE = Fmt<DT>::VE, NVR = kRun / VE;
+    if (aligned) {
+#pragma unroll
+        for (int q = 0; q < NVR; ++q) {
+            const int64_t vs = id0 + q * VE;
+            const uint4* a = vs + VE <= V ? reinterpret_cast<const uint4*>(row + vs * E) : &kPadVec;
+            v[q] = gload16(a);
+        }
+    } else {
+        load_run_elems<DT>(row, id0, V, v);
+    }
+}
+template <int DT> __device__ __forceinline__ bool run_straddles(int64_t id0, int V) {
+    return (V % Fmt<DT>::VE) != 0 && id0 < V && V <= id0 + kRun;
+}
+template <int DT> __device__ __forceinline__ void unpack_run(const uint4* v, float* f) {
+#pragma unroll
+    for (int q = 0; q < kRun / Fmt<DT>::VE; ++q) unpack<DT>(v[q], f + q * Fmt<DT>::VE);
+}
+template <int DT> __device__ __forceinline__ void unpack_masked(const uint4* v, int64_t id0, int V, float* f) {
+    unpack_run<DT>(v, f);
+#pragma unroll
+    for (int i = 0; i < kRun; ++i) f[i] = id0 + i < V ? f[i] : -SV_INF;
 }
 
 // Residual weights w = max(0, p' - q') (or p' for the bonus) and p' of a run.
@@ -1020,45 +1072,6 @@ __device__ __forceinline__ void run_weights(const float* lt, const float* ld, bo
     }
 }
 
-// Prefix sums over the kRThreads threads of a resample workgroup.
-__device__ __forceinline__ void rblock_scan(double x, double& incl, double& excl, double& total) {
-    __shared__ double ws[kRWaves];
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const double wi = wave_incl_scan(x, lane);
-    double we = __shfl_up(wi, 1, 64);
-    if (lane == 0) we = 0.0;
-    if (lane == 63) ws[wv] = wi;
-    __syncthreads();
-    double off = 0.0;
-    for (int k = 0; k < wv; ++k) off += ws[k];
-    double tot = 0.0;
-    for (int k = 0; k < kRWaves; ++k) tot += ws[k];
-    incl = off + wi;
-    excl = off + we;
-    total = tot;
-    __syncthreads();
-}
-__device__ __forceinline__ int rblock_min_int(int v) {
-    __shared__ int ws[kRWaves];
-    v = wave_min_int(v);
-    if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = v;
-    __syncthreads();
-    int r = ws[0];
-    for (int k = 1; k < kRWaves; ++k) r = min(r, ws[k]);
-    __syncthreads();
-    return r;
-}
-__device__ __forceinline__ int rblock_max_int(int v) {
-    __shared__ int ws[kRWaves];
-    v = wave_max_int(v);
-    if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = v;
-    __syncthreads();
-    int r = ws[0];
-    for (int k = 1; k < kRWaves; ++k) r = max(r, ws[k]);
-    __syncthreads();
-    return r;
-}
-
 __device__ __forceinline__ double ld_agent_d(const double* p) {
     return __longlong_as_double(static_cast<long long>(ld_agent(p)));
 }
@@ -1068,18 +1081,23 @@ __device__ __forceinline__ void st_agent_d(double* p, double v) {
 
 template <int DT, bool TOPP>
 __global__ __launch_bounds__(kRThreads) void k_resample(Params P) {
-    __shared__ double sw[kRWaves][kGroup], sp[kRWaves][kGroup];
-    __shared__ int s_last, s_y;
-    __shared__ double s_pre[1];
+    constexpr int NVR = kRun / Fmt<DT>::VE, G = group_steps<DT>();
+    __shared__ double sw[kRWaves][G], sp[kRWaves][G];
+    __shared__ double s_wtot[kRWaves];
+    __shared__ int s_last, s_sel, s_step, s_hit[kRWaves], s_lastpos[kRWaves];
+    __shared__ double s_spre, s_Z, s_t;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int b = blockIdx.x / P.res_split;
     const int c = blockIdx.x - b * P.res_split;
     const RowParam rp = P.rowp[b];
+    // the row's mode and n are the same for every lane: keep them scalar
+    const int mode = __builtin_amdgcn_readfirstlane(rp.mode);
+    const int rn = __builtin_amdgcn_readfirstlane(rp.n);
     // rowp was written by this call's decision; anything else is skipped
-    if ((rp.mode != MODE_RESID && rp.mode != MODE_BONUS) || rp.n < 0 || rp.n > P.K) return;
-    const bool resid = rp.mode == MODE_RESID;
-    const uint8_t* rowT = row_ptr<DT>(P, true, b, rp.n);
-    const uint8_t* rowD = resid ? row_ptr<DT>(P, false, b, rp.n) : rowT;
+    if ((mode != MODE_RESID && mode != MODE_BONUS) || rn < 0 || rn > P.K) return;
+    const bool resid = mode == MODE_RESID;
+    const uint8_t* rowT = row_ptr<DT>(P, true, b, rn);
+    const uint8_t* rowD = resid ? row_ptr<DT>(P, false, b, rn) : rowT;
     const bool aligned = ((reinterpret_cast<uintptr_t>(rowT) & 15) == 0) && ((reinterpret_cast<uintptr_t>(rowD) & 15) == 0);
     const float invT = static_cast<float>(1.0 / rp.keptT);
     const float invD = resid ? static_cast<float>(1.0 / rp.keptD) : 0.f;
@@ -1088,24 +1106,59 @@ __global__ __launch_bounds__(kRThreads) void k_resample(Params P) {
     const int s0 = c * P.res_steps;
     const int s1 = min(s0 + P.res_steps, P.nch2);
     bool stored = false;
-    for (int g0 = s0; g0 < s1; g0 += kGroup) {
-        const int gn = min(kGroup, s1 - g0);
-        float lt[kGroup][kRun], ld[kGroup][kRun];
+    for (int g0 = s0; g0 < s1; g0 += G) {
+        const int gn = min(G, s1 - g0);
+        uint4 vt[G][NVR], vd[G][NVR];
+        // uniform: a whole group of whole steps of aligned rows loads with
+        // straight-line 16-byte loads, all in flight together
+        const bool fast = aligned && gn == G && static_cast<int64_t>(g0 + G) * kStepIds <= P.V;
+        if (fast) {
 #pragma unroll
-        for (int k = 0; k < kGroup; ++k) {
-            if (k < gn) {
+            for (int k = 0; k < G; ++k) {
                 const int64_t id0 = static_cast<int64_t>(g0 + k) * kStepIds + static_cast<int64_t>(tid) * kRun;
-                load_run<DT>(rowT, id0, P.V, aligned, lt[k]);
-                if (resid) load_run<DT>(rowD, id0, P.V, aligned, ld[k]);
+                const uint4* pt = reinterpret_cast<const uint4*>(rowT + id0 * Fmt<DT>::E);
+                const uint4* pd = reinterpret_cast<const uint4*>(rowD + id0 * Fmt<DT>::E);
+#pragma unroll
+                for (int q = 0; q < NVR; ++q) vt[k][q] = gload16(pt + q);
+                if (resid) {
+#pragma unroll
+                    for (int q = 0; q < NVR; ++q) vd[k][q] = gload16(pd + q);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < G; ++k) {
+                if (k < gn) {
+                    const int64_t id0 = static_cast<int64_t>(g0 + k) * kStepIds + static_cast<int64_t>(tid) * kRun;
+                    issue_run<DT>(rowT, id0, P.V, aligned, vt[k]);
+                    if (resid) issue_run<DT>(rowD, id0, P.V, aligned, vd[k]);
+                }
+            }
+            if (aligned) {
+#pragma unroll
+                for (int k = 0; k < G; ++k) {
+                    const int64_t id0 = static_cast<int64_t>(g0 + k) * kStepIds + static_cast<int64_t>(tid) * kRun;
+                    if (k < gn && run_straddles<DT>(id0, P.V)) {
+                        load_run_elems<DT>(rowT, id0, P.V, vt[k]);
+                        if (resid) load_run_elems<DT>(rowD, id0, P.V, vd[k]);
+                    }
+                }
             }
         }
 #pragma unroll
-        for (int k = 0; k < kGroup; ++k) {
+        for (int k = 0; k < G; ++k) {
             double ws = 0.0, ps = 0.0;
             if (k < gn) {
                 const int64_t id0 = static_cast<int64_t>(g0 + k) * kStepIds + static_cast<int64_t>(tid) * kRun;
-                float w[kRun], p[kRun];
-                run_weights<TOPP>(lt[k], ld[k], resid, id0, rp, P.c_hi, P.c_lo, invT, invD, w, p);
+                float lt[kRun], ld[kRun], w[kRun], p[kRun];
+                if (fast) {
+                    unpack_run<DT>(vt[k], lt);
+                    if (resid) unpack_run<DT>(vd[k], ld);
+                } else {
+                    unpack_masked<DT>(vt[k], id0, P.V, lt);
+                    if (resid) unpack_masked<DT>(vd[k], id0, P.V, ld);
+                }
+                run_weights<TOPP>(lt, ld, resid, id0, rp, P.c_hi, P.c_lo, invT, invD, w, p);
 #pragma unroll
                 for (int i = 0; i < kRun; ++i) {
                     ws += static_cast<double>(w[i]);
@@ -1138,56 +1191,85 @@ __global__ __launch_bounds__(kRThreads) void k_resample(Params P) {
         s_last = arrive_last(P.res_cnt + static_cast<size_t>(b) * kCounterStride, static_cast<uint32_t>(P.res_split)) ? 1 : 0;
     __syncthreads();
     if (!s_last) return;
-    if (tid == 0) counter_reset(P.res_cnt + static_cast<size_t>(b) * kCounterStride);
 
-    // Last workgroup of the row: step masses in id order (thread t owns steps
-    // [t*g, t*g + g)), a prefix scan, the step holding t, then that step alone.
-    const int ns = P.nch2;
-    const int g = (ns + kRThreads - 1) / kRThreads;
-    const int e0 = min(tid * g, ns), e1 = min(e0 + g, ns);
-    double wsum = 0.0, psum = 0.0;
-    for (int k = e0; k < e1; ++k) {
-        wsum += ld_agent_d(cm + 2 * k);
-        psum += ld_agent_d(cm + 2 * k + 1);
-    }
-    double incl, excl, Z;
-    rblock_scan(wsum, incl, excl, Z);
-    int sel = 0;
-    if (!(Z > 0.0)) {
-        // A rejection implies p(x) < q(x), hence positive residual mass;
-        // none survives only through rounding: draw from p' instead.
-        sel = 1;
-        rblock_scan(psum, incl, excl, Z);
-    }
-    const double t = rp.u * Z;
-    int first = 0x7FFFFFFF, lastnz = -1;
-    double pre = excl, pf = 0.0, pl = 0.0;
-    for (int k = e0; k < e1; ++k) {
-        const double m = ld_agent_d(cm + 2 * k + sel);
-        if (m > 0.0) {
-            if (first == 0x7FFFFFFF && pre + m > t) {
-                first = k;
-                pf = pre;
-            }
-            lastnz = k;
-            pl = pre;
+    // Last workgroup of the row.  Wave 0: step masses in id order, their
+    // running sum, Z, t = u*Z and the step holding t.
+    if (wv == 0) {
+        if (lane == 0) counter_reset(P.res_cnt + static_cast<size_t>(b) * kCounterStride);
+        const int ns = P.nch2;
+        const int g = (ns + 63) / 64;
+        const int e0 = min(lane * g, ns), e1 = min(e0 + g, ns);
+        double wsum = 0.0, psum = 0.0;
+        for (int k = e0; k < e1; ++k) {
+            wsum += ld_agent_d(cm + 2 * k);
+            psum += ld_agent_d(cm + 2 * k + 1);
         }
-        pre += m;
+        double incl = wave_incl_scan(wsum, lane);
+        double Z = __shfl(incl, 63, 64);
+        int sel = 0;
+        if (!(Z > 0.0)) {
+            // A rejection implies p(x) < q(x), hence positive residual mass;
+            // none survives only through rounding: draw from p' instead.
+            sel = 1;
+            incl = wave_incl_scan(psum, lane);
+            Z = __shfl(incl, 63, 64);
+        }
+        // exclusive prefix: the previous lane's inclusive value
+        const double prev = __shfl_up(incl, 1, 64);
+        double pre = lane == 0 ? 0.0 : prev;
+        const double t = rp.u * Z;
+        int first = 0x7FFFFFFF, lastnz = -1;
+        double pf = 0.0, pl = 0.0;
+        for (int k = e0; k < e1; ++k) {
+            const double m = ld_agent_d(cm + 2 * k + sel);
+            if (m > 0.0) {
+                if (first == 0x7FFFFFFF && pre + m > t) {
+                    first = k;
+                    pf = pre;
+                }
+                lastnz = k;
+                pl = pre;
+            }
+            pre += m;
+        }
+        const int fe = wave_min_int(first);
+        const int le = wave_max_int(lastnz);
+        double spre = 0.0;
+        int stp = 0;
+        if (fe != 0x7FFFFFFF) {
+            stp = fe;
+            spre = __shfl(pf, fe / g, 64);
+        } else if (le >= 0) {
+            stp = le;
+            spre = __shfl(pl, le / g, 64);
+        }
+        if (lane == 0) {
+            s_sel = sel;
+            s_step = stp;
+            s_spre = spre;
+            s_Z = Z;
+            s_t = t;
+        }
     }
-    const int fe = rblock_min_int(first);
-    if (first == fe && fe != 0x7FFFFFFF) s_pre[0] = pf;
-    const int le = rblock_max_int(lastnz);
-    if (fe == 0x7FFFFFFF && lastnz == le && le >= 0) s_pre[0] = pl;
-    if (tid == 0) s_y = -1;
     __syncthreads();
-    const int st = (fe != 0x7FFFFFFF) ? fe : (le < 0 ? 0 : le);
-    const double spre = (fe == 0x7FFFFFFF && le < 0) ? 0.0 : s_pre[0];
-    __syncthreads();
+    const int sel = s_sel, stp = s_step;
+    const double spre = s_spre, t = s_t;
 
-    const int64_t id0 = static_cast<int64_t>(st) * kStepIds + static_cast<int64_t>(tid) * kRun;
+    // The chosen step alone, in id order: thread sums, a scan within each
+    // wave, wave totals through LDS, then the thread whose run holds t.
+    const int64_t id0 = static_cast<int64_t>(stp) * kStepIds + static_cast<int64_t>(tid) * kRun;
     float lt[kRun], ld[kRun], w[kRun], p[kRun];
-    load_run<DT>(rowT, id0, P.V, aligned, lt);
-    if (resid) load_run<DT>(rowD, id0, P.V, aligned, ld);
+    {
+        uint4 rt[NVR], rd[NVR];
+        issue_run<DT>(rowT, id0, P.V, aligned, rt);
+        if (resid) issue_run<DT>(rowD, id0, P.V, aligned, rd);
+        if (aligned && run_straddles<DT>(id0, P.V)) {
+            load_run_elems<DT>(rowT, id0, P.V, rt);
+            if (resid) load_run_elems<DT>(rowD, id0, P.V, rd);
+        }
+        unpack_masked<DT>(rt, id0, P.V, lt);
+        if (resid) unpack_masked<DT>(rd, id0, P.V, ld);
+    }
     run_weights<TOPP>(lt, ld, resid, id0, rp, P.c_hi, P.c_lo, invT, invD, w, p);
     double xs = 0.0;
     int lastpos = -1;
@@ -1198,12 +1280,35 @@ __global__ __launch_bounds__(kRThreads) void k_resample(Params P) {
         xs += static_cast<double>(v);
         if (v > 0.f) lastpos = static_cast<int>(id0 + i);
     }
-    double ti, te, tot;
-    rblock_scan(xs, ti, te, tot);
-    const int hit = (xs > 0.0 && spre + ti > t) ? tid : 0x7FFFFFFF;
-    const int fh = rblock_min_int(hit);
-    if (tid == fh && fh != 0x7FFFFFFF) {
-        double run = spre + te;
+    const double wi = wave_incl_scan(xs, lane);
+    if (lane == 63) s_wtot[wv] = wi;
+    const int wl = wave_max_int(lastpos);
+    if (lane == 0) s_lastpos[wv] = wl;
+    __syncthreads();
+    double off = spre;
+    for (int k = 0; k < wv; ++k) off += s_wtot[k];
+    const double incl = off + wi;
+    const unsigned long long hitm = __ballot(xs > 0.0 && incl > t);
+    if (lane == 0) s_hit[wv] = hitm ? (wv * 64 + __ffsll(static_cast<long long>(hitm)) - 1) : 0x7FFFFFFF;
+    __syncthreads();
+    int fh = 0x7FFFFFFF, lp = -1;
+    for (int k = 0; k < kRWaves; ++k) {
+        fh = min(fh, s_hit[k]);
+        lp = max(lp, s_lastpos[k]);
+    }
+    if (fh == 0x7FFFFFFF) {
+        // rounding put t past the step's last run: the last positive weight
+        if (tid == 0) {
+            P.out_tokens[static_cast<size_t>(b) * (P.K + 1) + rn] = lp >= 0 ? lp : 0;
+            if (P.probe_row) {
+                P.probe_row[static_cast<size_t>(b) * 4 + 0] = s_Z;
+                P.probe_row[static_cast<size_t>(b) * 4 + 1] = t;
+            }
+        }
+        return;
+    }
+    if (tid == fh) {
+        double run = incl - xs;
         int y = -1, lastw = -1;
 #pragma unroll
         for (int i = 0; i < kRun; ++i) {
@@ -1213,14 +1318,9 @@ __global__ __launch_bounds__(kRThreads) void k_resample(Params P) {
             }
             run += static_cast<double>(w[i]);
         }
-        s_y = y >= 0 ? y : lastw;
-    }
-    const int lp = rblock_max_int(lastpos);
-    if (tid == 0) {
-        const int y = s_y >= 0 ? s_y : (lp >= 0 ? lp : 0);
-        P.out_tokens[static_cast<size_t>(b) * (P.K + 1) + rp.n] = y;
+        P.out_tokens[static_cast<size_t>(b) * (P.K + 1) + rn] = y >= 0 ? y : lastw;
         if (P.probe_row) {
-            P.probe_row[static_cast<size_t>(b) * 4 + 0] = Z;
+            P.probe_row[static_cast<size_t>(b) * 4 + 0] = s_Z;
             P.probe_row[static_cast<size_t>(b) * 4 + 1] = t;
         }
     }

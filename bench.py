@@ -101,6 +101,28 @@ def cpu_baseline(sets, budget_rows):
 
 
 # ---------------------------------------------------------------------------
+# Counter calibration: kernels of known traffic
+# ---------------------------------------------------------------------------
+CALIB_BYTES = 512 << 20
+
+
+def calibrate(binding, torch, dev):
+    """A device-to-device copy (reads and writes CALIB_BYTES) and the
+    streaming-read kernel (reads CALIB_BYTES), 3 launches each."""
+    src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)
+    src.fill_(7)
+    dst = torch.empty_like(src)
+    sink = torch.zeros(1024, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    for _ in range(3):
+        binding.stream_read(src, sink, 4)
+    torch.cuda.synchronize()
+    print(f"[bench] calibration: 3 copies and 3 streaming reads of {CALIB_BYTES} bytes", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------
 # GPU timing
 # ---------------------------------------------------------------------------
 def main():
@@ -110,6 +132,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=192)
+    ap.add_argument("--calibrate", action="store_true",
+                    help="after timing, run a plain device copy and a streaming read of known sizes, the "
+                         "references that scale hardware byte counters to bytes")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the verify step is built and timed on a single MI355X "
@@ -202,6 +227,9 @@ def main():
         "other_kernels_us": {"resample": round(res_ms / max(res_n, 1) * 1e3, 3)},
         "algorithmic_bytes_per_launch": logical,
     }
+
+    if args.calibrate:
+        calibrate(binding, torch, dev)
 
     cpu = None
     if not args.no_cpu_baseline:

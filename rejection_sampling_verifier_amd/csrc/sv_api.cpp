@@ -156,12 +156,10 @@ int timed_launch(int kind, hipStream_t stream, F&& launch) {
     if (g_prof) {
         if (hipEventCreate(&ev.a) != hipSuccess || hipEventCreate(&ev.b) != hipSuccess)
             return hip_fail(hipGetLastError(), "hipEventCreate");
-        (void)hipEventRecord(ev.a, stream);
     }
-    const hipError_t e = launch();
+    const hipError_t e = launch(sv::LaunchEvents{ev.a, ev.b});
     if (e != hipSuccess) return hip_fail(e, "kernel launch");
     if (g_prof) {
-        (void)hipEventRecord(ev.b, stream);
         std::lock_guard<std::mutex> lk(g_mu);
         g_events.push_back(ev);
     }
@@ -261,13 +259,13 @@ int verify_impl(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_t
     p.res_cnt = counters + static_cast<size_t>(B) * sv::kCounterStride;
 
     const bool topp = top_p < 1.f;
-    rc = timed_launch(sv::KK_STATS, stream, [&] { return sv::launch_stats(p, dtype, unroll, topp, stream); });
+    rc = timed_launch(sv::KK_STATS, stream, [&](const sv::LaunchEvents& ev) { return sv::launch_stats(p, dtype, unroll, topp, stream, ev); });
     if (rc) return rc;
     if (topp) {
-        rc = timed_launch(sv::KK_TOPP, stream, [&] { return sv::launch_topp(p, dtype, stream); });
+        rc = timed_launch(sv::KK_TOPP, stream, [&](const sv::LaunchEvents& ev) { return sv::launch_topp(p, dtype, stream, ev); });
         if (rc) return rc;
     }
-    return timed_launch(sv::KK_RESAMPLE, stream, [&] { return sv::launch_resample(p, dtype, topp, stream); });
+    return timed_launch(sv::KK_RESAMPLE, stream, [&](const sv::LaunchEvents& ev) { return sv::launch_resample(p, dtype, topp, stream, ev); });
 }
 
 }  // namespace

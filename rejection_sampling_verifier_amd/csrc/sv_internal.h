@@ -87,10 +87,15 @@ struct Params {
 
 constexpr int kCounterStride = 16;  // one 64-byte line per counter
 
+// Timing events of one launch (both null when timing is off).
+struct LaunchEvents {
+    hipEvent_t start, stop;
+};
+
 // Launchers (defined in sv_kernels.hip).
-hipError_t launch_stats(const Params& p, int dtype, int unroll, bool topp, hipStream_t s);
-hipError_t launch_topp(const Params& p, int dtype, hipStream_t s);
-hipError_t launch_resample(const Params& p, int dtype, bool topp, hipStream_t s);
+hipError_t launch_stats(const Params& p, int dtype, int unroll, bool topp, hipStream_t s, const LaunchEvents& ev);
+hipError_t launch_topp(const Params& p, int dtype, hipStream_t s, const LaunchEvents& ev);
+hipError_t launch_resample(const Params& p, int dtype, bool topp, hipStream_t s, const LaunchEvents& ev);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int unroll, hipStream_t s);
 
 }  // namespace sv

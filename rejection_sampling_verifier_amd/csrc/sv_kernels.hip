@@ -32,6 +32,8 @@
 // store that is itself coherent at agent scope needs neither.  Everything that
 // streams V is bandwidth-bound (no dense contraction, so no MFMA).
 
+#include <hip/hip_ext.h>
+
 #include "sv_device.h"
 #include "sv_internal.h"
 
@@ -1361,39 +1363,46 @@ hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, in
 // ---------------------------------------------------------------------------
 // Launchers.
 // ---------------------------------------------------------------------------
-template <int DT, int U>
-static void launch_stats_t(const Params& p, bool topp, hipStream_t s) {
-    const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(p.B) * p.nslot * p.nch);
-    if (topp) hipLaunchKernelGGL((k_stats<DT, U, true>), dim3(grid), dim3(kThreads), 0, s, p);
-    else hipLaunchKernelGGL((k_stats<DT, U, false>), dim3(grid), dim3(kThreads), 0, s, p);
+// With profiling on, the events are attached to the kernel's own dispatch
+// (start and end of its execution); otherwise they are null.
+template <typename Kern>
+static void launch(Kern k, unsigned grid, unsigned block, hipStream_t s, const LaunchEvents& ev, const Params& p) {
+    hipExtLaunchKernelGGL(k, dim3(grid), dim3(block), 0, s, ev.start, ev.stop, 0, p);
 }
 
-hipError_t launch_stats(const Params& p, int dtype, int unroll, bool topp, hipStream_t s) {
+template <int DT, int U>
+static void launch_stats_t(const Params& p, bool topp, hipStream_t s, const LaunchEvents& ev) {
+    const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(p.B) * p.nslot * p.nch);
+    if (topp) launch(k_stats<DT, U, true>, grid, kThreads, s, ev, p);
+    else launch(k_stats<DT, U, false>, grid, kThreads, s, ev, p);
+}
+
+hipError_t launch_stats(const Params& p, int dtype, int unroll, bool topp, hipStream_t s, const LaunchEvents& ev) {
     if (dtype == DT_BF16) {
-        if (unroll == 8) launch_stats_t<DT_BF16, 8>(p, topp, s);
-        else launch_stats_t<DT_BF16, 4>(p, topp, s);
+        if (unroll == 8) launch_stats_t<DT_BF16, 8>(p, topp, s, ev);
+        else launch_stats_t<DT_BF16, 4>(p, topp, s, ev);
     } else {
-        if (unroll == 8) launch_stats_t<DT_F32, 8>(p, topp, s);
-        else launch_stats_t<DT_F32, 4>(p, topp, s);
+        if (unroll == 8) launch_stats_t<DT_F32, 8>(p, topp, s, ev);
+        else launch_stats_t<DT_F32, 4>(p, topp, s, ev);
     }
     return hipGetLastError();
 }
 
-hipError_t launch_topp(const Params& p, int dtype, hipStream_t s) {
+hipError_t launch_topp(const Params& p, int dtype, hipStream_t s, const LaunchEvents& ev) {
     const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(p.B) * p.nslot);
-    if (dtype == DT_BF16) hipLaunchKernelGGL((k_topp<DT_BF16>), dim3(grid), dim3(kThreads), 0, s, p);
-    else hipLaunchKernelGGL((k_topp<DT_F32>), dim3(grid), dim3(kThreads), 0, s, p);
+    if (dtype == DT_BF16) launch(k_topp<DT_BF16>, grid, kThreads, s, ev, p);
+    else launch(k_topp<DT_F32>, grid, kThreads, s, ev, p);
     return hipGetLastError();
 }
 
-hipError_t launch_resample(const Params& p, int dtype, bool topp, hipStream_t s) {
+hipError_t launch_resample(const Params& p, int dtype, bool topp, hipStream_t s, const LaunchEvents& ev) {
     const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(p.B) * p.res_split);
     if (dtype == DT_BF16) {
-        if (topp) hipLaunchKernelGGL((k_resample<DT_BF16, true>), dim3(grid), dim3(kRThreads), 0, s, p);
-        else hipLaunchKernelGGL((k_resample<DT_BF16, false>), dim3(grid), dim3(kRThreads), 0, s, p);
+        if (topp) launch(k_resample<DT_BF16, true>, grid, kRThreads, s, ev, p);
+        else launch(k_resample<DT_BF16, false>, grid, kRThreads, s, ev, p);
     } else {
-        if (topp) hipLaunchKernelGGL((k_resample<DT_F32, true>), dim3(grid), dim3(kRThreads), 0, s, p);
-        else hipLaunchKernelGGL((k_resample<DT_F32, false>), dim3(grid), dim3(kRThreads), 0, s, p);
+        if (topp) launch(k_resample<DT_F32, true>, grid, kRThreads, s, ev, p);
+        else launch(k_resample<DT_F32, false>, grid, kRThreads, s, ev, p);
     }
     return hipGetLastError();
 }

@@ -2,6 +2,7 @@
 // kernel dispatch and optional per-kernel timing.  The operation itself is
 // described in include/specverify.h.
 
+#include <atomic>
 #include <cfloat>
 #include <cmath>
 #include <cstdio>
@@ -21,31 +22,44 @@ namespace {
 using sv::Params;
 
 struct Scratch {
-    void* ptr = nullptr;       // per-call data, every byte rewritten before it is read
+    void* ptr = nullptr;       // records and per-row state; zeroed when allocated
     size_t bytes = 0;
     uint32_t* counters = nullptr;  // arrival counters: zeroed once, left at zero by every call
     int64_t counter_rows = 0;
 };
 
 struct Layout {
-    size_t part, rv, rowp, cmass, total;
+    size_t prec, rv, rowp, qrec, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-Layout layout(int64_t B, int nslot, int nch, int nch2) {
+// Tagged records (statistics per chunk, masses per resample item) are left
+// at zero by every call that completes; RvState and RowParam are rewritten
+// before they are read.
+Layout layout(int64_t B, int nslot, int nch, int nq) {
     Layout L;
     size_t off = 0;
-    L.part = off;
-    off = align256(off + static_cast<size_t>(B) * nslot * nch * sizeof(sv::Partial));
+    L.prec = off;
+    off = align256(off + static_cast<size_t>(B) * nslot * nch * sv::kRecWords * sizeof(uint64_t));
     L.rv = off;
     off = align256(off + static_cast<size_t>(B) * nslot * sizeof(sv::RvState));
     L.rowp = off;
     off = align256(off + static_cast<size_t>(B) * sizeof(sv::RowParam));
-    L.cmass = off;
-    off = align256(off + static_cast<size_t>(B) * nch2 * 2 * sizeof(double));
+    L.qrec = off;
+    off = align256(off + static_cast<size_t>(B) * nq * sv::kRecWords * sizeof(uint64_t));
     L.total = off;
     return L;
+}
+
+// Record tags: unique per call within the process, never 0.
+std::atomic<uint32_t> g_tag{0};
+uint32_t next_tag() {
+    uint32_t t;
+    do {
+        t = g_tag.fetch_add(1u) + 1u;
+    } while (t == 0u);
+    return t;
 }
 
 std::mutex g_mu;
@@ -95,10 +109,9 @@ int check_logits(const sv_logits* t) {
     return SV_OK;
 }
 
-// Returns the scratch for (device, stream), growing it when needed.  The data
-// region is rewritten before it is read within every call.  The arrival
-// counters live in their own allocation at fixed offsets (two per batch row),
-// are zeroed when allocated, and every call leaves them at zero.
+// Returns the scratch for (device, stream), growing it when needed.  Both
+// allocations are zeroed when made; the arrival counters (one per batch row,
+// at fixed offsets) and the tagged records are left at zero by every call.
 int get_scratch(hipStream_t stream, size_t bytes, int64_t rows, void** data, uint32_t** counters) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -121,6 +134,11 @@ int get_scratch(hipStream_t stream, size_t bytes, int64_t rows, void** data, uin
         if (e != hipSuccess) {
             (void)hipGetLastError();
             return SV_ENOMEM;
+        }
+        e = hipMemsetAsync(p, 0, want, stream);
+        if (e != hipSuccess) {
+            (void)hipFree(p);
+            return hip_fail(e, "hipMemsetAsync");
         }
         s.ptr = p;
         s.bytes = want;
@@ -199,18 +217,15 @@ int verify_impl(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_t
     const int cv = sv::kThreads * unroll;
     const int64_t nch64 = (nvec_max + cv - 1) / cv;
     const int nch = static_cast<int>(nch64);
-    // resample pass: steps of kResStepIds ids; about one workgroup per CU
-    // over the batch, each covering res_steps consecutive steps of one row
-    const int nch2 = (V + sv::kResStepIds - 1) / sv::kResStepIds;
-    int res_split = (env_int("SPECVERIFY_RES_WG", device_cus()) + B - 1) / B;
-    if (res_split > nch2) res_split = nch2;
-    if (res_split < 1) res_split = 1;
-    const int res_steps = (nch2 + res_split - 1) / res_split;
-    res_split = (nch2 + res_steps - 1) / res_steps;
-    if (static_cast<int64_t>(B) * nslot * nch >= (1ll << 31)) return SV_ESHAPE;
+    // resample: items of kItemIds ids
+    const int nq = (V + sv::kItemIds - 1) / sv::kItemIds;
+    const int64_t per_row = static_cast<int64_t>(nslot) * nch + nq;
+    if (static_cast<int64_t>(B) * per_row >= (1ll << 31)) return SV_ESHAPE;
+    // the statistics kernel clears the row pass's records, a few words each
+    if (4ll * nq > static_cast<int64_t>(sv::kThreads) * nslot * nch) return SV_ESHAPE;
 
     hipStream_t stream = static_cast<hipStream_t>(stream_v);
-    const Layout lay = layout(B, nslot, nch, nch2);
+    const Layout lay = layout(B, nslot, nch, nq);
     void* scratch = nullptr;
     uint32_t* counters = nullptr;
     rc = get_scratch(stream, lay.total, B, &scratch, &counters);
@@ -237,9 +252,8 @@ int verify_impl(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_t
     p.nslot = nslot;
     p.nch = nch;
     p.cv = cv;
-    p.nch2 = nch2;
-    p.res_split = res_split;
-    p.res_steps = res_steps;
+    p.nq = nq;
+    p.tag = next_tag();
     // c = c_hi + c_lo with c_hi <= c rounded toward zero, so c_lo > 0.
     float c_hi = static_cast<float>(c);
     if (static_cast<double>(c_hi) > c) c_hi = std::nextafter(c_hi, 0.f);
@@ -251,21 +265,23 @@ int verify_impl(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_t
     p.top_p = top_p;
     p.key0 = static_cast<uint32_t>(seed & 0xFFFFFFFFull);
     p.key1 = static_cast<uint32_t>(seed >> 32);
-    p.part = reinterpret_cast<sv::Partial*>(base + lay.part);
+    p.prec = reinterpret_cast<uint64_t*>(base + lay.prec);
     p.rv = reinterpret_cast<sv::RvState*>(base + lay.rv);
     p.rowp = reinterpret_cast<sv::RowParam*>(base + lay.rowp);
-    p.cmass = reinterpret_cast<double*>(base + lay.cmass);
+    p.qrec = reinterpret_cast<uint64_t*>(base + lay.qrec);
     p.row_cnt = counters;
-    p.res_cnt = counters + static_cast<size_t>(B) * sv::kCounterStride;
 
     const bool topp = top_p < 1.f;
-    rc = timed_launch(sv::KK_STATS, stream, [&](const sv::LaunchEvents& ev) { return sv::launch_stats(p, dtype, unroll, topp, stream, ev); });
+    rc = timed_launch(sv::KK_STATS, stream,
+                      [&](const sv::LaunchEvents& ev) { return sv::launch_stats(p, dtype, unroll, stream, ev); });
     if (rc) return rc;
     if (topp) {
-        rc = timed_launch(sv::KK_TOPP, stream, [&](const sv::LaunchEvents& ev) { return sv::launch_topp(p, dtype, stream, ev); });
+        rc = timed_launch(sv::KK_TOPP, stream,
+                          [&](const sv::LaunchEvents& ev) { return sv::launch_topp(p, dtype, stream, ev); });
         if (rc) return rc;
     }
-    return timed_launch(sv::KK_RESAMPLE, stream, [&](const sv::LaunchEvents& ev) { return sv::launch_resample(p, dtype, topp, stream, ev); });
+    return timed_launch(sv::KK_RESAMPLE, stream,
+                        [&](const sv::LaunchEvents& ev) { return sv::launch_rows(p, dtype, topp, stream, ev); });
 }
 
 }  // namespace

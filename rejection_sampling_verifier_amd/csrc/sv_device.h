@@ -152,6 +152,73 @@ __device__ __forceinline__ double wave_incl_scan(double v, int lane) {
 }
 
 // ---------------------------------------------------------------------------
+// Wave64 scans and reductions through DPP (data-parallel lane moves inside
+// the VALU, no LDS round trip): row_shr 1, 2, 4, 8 scan each row of 16 lanes,
+// then row_bcast15 and row_bcast31 carry row totals into the later rows.  A
+// lane whose source is outside its row keeps `old`, the operation's identity.
+// ---------------------------------------------------------------------------
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+constexpr int kDppWaveShr1 = 0x138;  // lane i reads lane i-1 across the whole wave
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_int(int old, int v) {
+    return __builtin_amdgcn_update_dpp(old, v, CTRL, ROWS, 0xF, false);
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_f64(double v) {
+    const long long b = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_update_dpp(0, static_cast<int>(b), CTRL, ROWS, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(b >> 32), CTRL, ROWS, 0xF, false);
+    return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned int>(lo));
+}
+// Inclusive prefix sum over the wave's lanes (fixed order of additions).
+__device__ __forceinline__ double wave_scan_dpp(double v) {
+    v += dpp_f64<kDppRowShr1, 0xF>(v);
+    v += dpp_f64<kDppRowShr2, 0xF>(v);
+    v += dpp_f64<kDppRowShr4, 0xF>(v);
+    v += dpp_f64<kDppRowShr8, 0xF>(v);
+    v += dpp_f64<kDppRowBcast15, 0xA>(v);
+    v += dpp_f64<kDppRowBcast31, 0xC>(v);
+    return v;
+}
+__device__ __forceinline__ double lane63(double v) {
+    const long long b = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_readlane(static_cast<int>(b), 63);
+    const int hi = __builtin_amdgcn_readlane(static_cast<int>(b >> 32), 63);
+    return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned int>(lo));
+}
+// Lane `l` (wave-uniform) of a double.
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+    const long long b = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_readlane(static_cast<int>(b), l);
+    const int hi = __builtin_amdgcn_readlane(static_cast<int>(b >> 32), l);
+    return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned int>(lo));
+}
+// Sum over the wave, the same in every lane.
+__device__ __forceinline__ double wave_sum_dpp(double v) { return lane63(wave_scan_dpp(v)); }
+__device__ __forceinline__ int wave_max_int_dpp(int v) {
+    constexpr int lo = static_cast<int>(0x80000000u);
+    v = max(v, dpp_int<kDppRowShr1, 0xF>(lo, v));
+    v = max(v, dpp_int<kDppRowShr2, 0xF>(lo, v));
+    v = max(v, dpp_int<kDppRowShr4, 0xF>(lo, v));
+    v = max(v, dpp_int<kDppRowShr8, 0xF>(lo, v));
+    v = max(v, dpp_int<kDppRowBcast15, 0xA>(lo, v));
+    v = max(v, dpp_int<kDppRowBcast31, 0xC>(lo, v));
+    return __builtin_amdgcn_readlane(v, 63);
+}
+__device__ __forceinline__ int wave_min_int_dpp(int v) {
+    constexpr int hi = 0x7FFFFFFF;
+    v = min(v, dpp_int<kDppRowShr1, 0xF>(hi, v));
+    v = min(v, dpp_int<kDppRowShr2, 0xF>(hi, v));
+    v = min(v, dpp_int<kDppRowShr4, 0xF>(hi, v));
+    v = min(v, dpp_int<kDppRowShr8, 0xF>(hi, v));
+    v = min(v, dpp_int<kDppRowBcast15, 0xA>(hi, v));
+    v = min(v, dpp_int<kDppRowBcast31, 0xC>(hi, v));
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
+// ---------------------------------------------------------------------------
 // Philox4x32-10 (Salmon et al., SC'11, section 3.2): per round, 32x32->64
 // products of counter words 0 and 2 with 0xD2511F53 and 0xCD9E8D57; output
 // (hi2 ^ c1 ^ k0, lo2, hi0 ^ c3 ^ k1, lo0); key bumped by the Weyl constants

@@ -13,7 +13,10 @@ constexpr int kMaxK = 16;
 constexpr int kMaxSlots = 2 * kMaxK + 1;
 constexpr int kStatsUnroll = 8;      // default 16-byte vectors in flight per lane per step
 constexpr int kResTile = 8;          // consecutive ids per thread in the id-ordered scans
-constexpr int kResStepIds = 8192;    // ids per resample step (1024 threads x 8)
+constexpr int kRun = 8;              // ids per thread per run of a resample item
+constexpr int kRuns = 4;             // runs per thread per resample item
+constexpr int kItemIds = kThreads * kRun * kRuns;  // ids per resample item (8192)
+constexpr int kRecWords = 4;         // 64-bit words per tagged record
 
 enum DType : int { DT_F32 = 0, DT_BF16 = 1 };
 enum RowMode : int { MODE_SKIP = 0, MODE_RESID = 1, MODE_BONUS = 2 };
@@ -22,13 +25,13 @@ enum KernelKind : int { KK_STATS = 0, KK_TOPP = 1, KK_RESAMPLE = 2, KK_COUNT = 3
 // Statistics of one chunk of one logit row, relative to an integer offset o:
 // s = sum over the chunk of 2^(l*c - o), c = log2(e)/T; m = max logit; lx =
 // the logit at the row's drafted id when that id falls in the chunk, else
-// -inf.
+// -inf.  In memory a chunk's statistics are a tagged record of kRecWords
+// 64-bit words (o, m, lx, s as float), each carrying the call's tag.
 struct Partial {
     float o;
     float m;
     float lx;
-    float pad;
-    double s;
+    float s;
 };
 
 // Result of the statistics pass (and, with top-p, of the nucleus selection)
@@ -70,19 +73,18 @@ struct Params {
     double* probe_pos;            // [B, K+1, 8] or null
     double* probe_row;            // [B, 4] or null
     int B, K, V, nslot;
-    int nch, cv;                  // statistics pass: chunks per row, 16-byte vectors per chunk
-    int nch2;                     // resample pass: steps of kResStepIds ids per row
-    int res_split, res_steps;     // resample workgroups per row, steps per workgroup
+    int nch, cv;                  // statistics pass: chunks per logit row, 16-byte vectors per chunk
+    int nq;                       // resample items per batch row (kItemIds ids each)
+    uint32_t tag;                 // this call's record tag (never 0)
     float c_hi, c_lo;             // c = log2(e)/T = c_hi + c_lo, c_lo > 0
     double c64;                   // (double)c_hi + (double)c_lo
     float top_p;
     uint32_t key0, key1;          // Philox key
-    Partial* part;                // [B, nslot, nch]
+    uint64_t* prec;               // [B, nslot, nch] tagged statistics records
     RvState* rv;                  // [B, nslot]
     RowParam* rowp;               // [B]
-    double* cmass;                // [B, nch2, 2]: residual (or bonus) mass, target mass
+    uint64_t* qrec;               // [B, nq] tagged resample-item mass records
     uint32_t* row_cnt;            // [B] arrival counters, kCounterStride words apart, zero between calls
-    uint32_t* res_cnt;            // [B] likewise, for the resample pass
 };
 
 constexpr int kCounterStride = 16;  // one 64-byte line per counter
@@ -93,9 +95,11 @@ struct LaunchEvents {
 };
 
 // Launchers (defined in sv_kernels.hip).
-hipError_t launch_stats(const Params& p, int dtype, int unroll, bool topp, hipStream_t s, const LaunchEvents& ev);
+// The statistics pass, then (top-p only) the nucleus pass with the decision,
+// then the row pass (decision without top-p, resample).
+hipError_t launch_stats(const Params& p, int dtype, int unroll, hipStream_t s, const LaunchEvents& ev);
 hipError_t launch_topp(const Params& p, int dtype, hipStream_t s, const LaunchEvents& ev);
-hipError_t launch_resample(const Params& p, int dtype, bool topp, hipStream_t s, const LaunchEvents& ev);
+hipError_t launch_rows(const Params& p, int dtype, bool topp, hipStream_t s, const LaunchEvents& ev);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int unroll, hipStream_t s);
 
 }  // namespace sv

@@ -115,23 +115,64 @@ __device__ __forceinline__ uint64_t pack2(float a, float b) {
 __device__ __forceinline__ float lo32f(uint64_t w) { return __uint_as_float(static_cast<uint32_t>(w)); }
 __device__ __forceinline__ float hi32f(uint64_t w) { return __uint_as_float(static_cast<uint32_t>(w >> 32)); }
 
-__device__ __forceinline__ void store_partial(Partial* p, float o, float m, float lx, double s) {
-    uint64_t* w = reinterpret_cast<uint64_t*>(p);
-    st_agent(w + 0, pack2(o, m));
-    st_agent(w + 1, pack2(lx, 0.f));
-    st_agent(w + 2, static_cast<uint64_t>(__double_as_longlong(s)));
+// ---------------------------------------------------------------------------
+// Tagged records.  A record is kRecWords 64-bit words, each holding the
+// call's 32-bit tag in its high half and 32 payload bits in its low half.
+// An aligned 64-bit store is single-copy atomic, so a reader that finds the
+// tag in every word of a record reads what this call wrote, with no fence or
+// wait on the writer's side: a producer stores its record and exits.
+// Records of earlier calls carry other tags; fresh scratch is zeroed and the
+// host never uses tag 0.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t tagged(uint32_t tag, uint32_t payload) {
+    return (static_cast<uint64_t>(tag) << 32) | payload;
 }
-__device__ __forceinline__ Partial load_partial(const Partial* p) {
-    const uint64_t* w = reinterpret_cast<const uint64_t*>(p);
-    const uint64_t a = ld_agent(w + 0), b = ld_agent(w + 1), c = ld_agent(w + 2);
+__device__ __forceinline__ bool has_tag(uint64_t w, uint32_t tag) { return static_cast<uint32_t>(w >> 32) == tag; }
+
+// Bound on the polls of one record: far beyond any wait a call can produce
+// (each poll is a memory round trip plus a short sleep), it only guarantees
+// that every wave ends.  A record still missing after it makes the row
+// invalid.
+constexpr int kPollLimit = 1 << 20;
+
+// Loads record words until all carry `tag` (true), or kPollLimit polls.
+__device__ __forceinline__ bool poll_record(const uint64_t* rec, uint32_t tag, uint32_t* pay) {
+    for (int it = 0; it < kPollLimit; ++it) {
+        uint64_t w[kRecWords];
+#pragma unroll
+        for (int k = 0; k < kRecWords; ++k) w[k] = ld_agent(rec + k);
+        bool ok = true;
+#pragma unroll
+        for (int k = 0; k < kRecWords; ++k) {
+            ok = ok && has_tag(w[k], tag);
+            pay[k] = static_cast<uint32_t>(w[k]);
+        }
+        if (ok) return true;
+        __builtin_amdgcn_s_sleep(4);
+    }
+    return false;
+}
+// A record written by an earlier kernel of this call: one plain 32-byte load
+// (cached); true if every word carries `tag`.
+__device__ __forceinline__ bool read_record(const uint64_t* rec, uint32_t tag, uint32_t* pay) {
+    static_assert(kRecWords == 4, "a record is two 16-byte vectors");
+    const uint4 a = gload16(reinterpret_cast<const uint4*>(rec));
+    const uint4 c = gload16(reinterpret_cast<const uint4*>(rec) + 1);
+    pay[0] = a.x;
+    pay[1] = a.z;
+    pay[2] = c.x;
+    pay[3] = c.z;
+    return a.y == tag && a.w == tag && c.y == tag && c.w == tag;
+}
+__device__ __forceinline__ Partial partial_from(const uint32_t* pay) {
     Partial q;
-    q.o = lo32f(a);
-    q.m = hi32f(a);
-    q.lx = lo32f(b);
-    q.pad = 0.f;
-    q.s = __longlong_as_double(static_cast<long long>(c));
+    q.o = __uint_as_float(pay[0]);
+    q.m = __uint_as_float(pay[1]);
+    q.lx = __uint_as_float(pay[2]);
+    q.s = __uint_as_float(pay[3]);
     return q;
 }
+
 __device__ __forceinline__ void store_rvstate(RvState* p, const RvState& st) {
     uint64_t* w = reinterpret_cast<uint64_t*>(p);
     st_agent(w + 0, pack2(st.o, st.m));
@@ -188,19 +229,23 @@ __device__ __forceinline__ double merge_stats(float Oa, double Sa, float Ob, dou
     return sa + sb;
 }
 
-// Combines the chunk partials of logit row `slot` of batch row b (one wave,
-// lanes over chunks).
+// Combines the chunk records of logit row `slot` of batch row b (one wave,
+// lanes over chunks, chunk order within a lane); the statistics kernel has
+// finished.  ok is false if a record lacks the call's tag.
 __device__ __forceinline__ void combine_partials(const Params& P, int b, int slot, int lane, float& O, float& M,
-                                                 float& LX, double& S) {
-    const Partial* pp = P.part + (static_cast<size_t>(b) * P.nslot + slot) * P.nch;
+                                                 float& LX, double& S, bool& ok) {
+    const uint64_t* base = P.prec + (static_cast<size_t>(b) * P.nslot + slot) * P.nch * kRecWords;
     O = -SV_INF;
     M = -SV_INF;
     LX = -SV_INF;
     S = 0.0;
+    bool good = true;
     for (int c = lane; c < P.nch; c += 64) {
-        const Partial q = load_partial(pp + c);
+        uint32_t pay[kRecWords];
+        good = read_record(base + static_cast<size_t>(c) * kRecWords, P.tag, pay) && good;
+        const Partial q = partial_from(pay);
         float On;
-        S = merge_stats(O, S, q.o, q.s, On);
+        S = merge_stats(O, S, q.o, static_cast<double>(q.s), On);
         O = On;
         M = fmaxf(M, q.m);
         LX = fmaxf(LX, q.lx);
@@ -216,100 +261,151 @@ __device__ __forceinline__ void combine_partials(const Params& P, int b, int slo
         M = fmaxf(M, M2);
         LX = fmaxf(LX, L2);
     }
+    ok = __ballot(!good) == 0ull;
 }
 
-// Partials staged in LDS by the deciding wave.
-constexpr int kStage = 256;
-struct StageShared {
-    float o[kStage];
-    float m[kStage];
-    float lx[kStage];
-    double s[kStage];
-};
+// Statistics of every logit row of batch row b into R from the chunk
+// records (the statistics kernel has finished).  The workgroup loads up to
+// kThreads records at once, stages them in LDS, and wave w merges logit rows
+// w, w+4, ... (chunk order within a lane, then a fixed wave tree, then pass
+// order).  Every thread must call it (it ends with a barrier).
+constexpr int kLaneMergeMax = 32;  // chunks per logit row merged by one lane
+static_assert(2 * kMaxK + 1 <= 64, "one lane per logit row");
+__device__ __forceinline__ void fill_row_from_partials(const Params& P, int b, int Le, RowShared& R) {
+    __shared__ Partial stage[kThreads];
+    __shared__ int stage_bad;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int nrv = 2 * Le + 1, nch = P.nch;
+    const int nrec = nrv * nch;
+    if (tid < nrv) {
+        R.o[tid] = -SV_INF;
+        R.m[tid] = -SV_INF;
+        R.lx[tid] = -SV_INF;
+        R.s[tid] = 0.0;
+        R.valid[tid] = 1;
+    }
+    if (tid == 0) stage_bad = 0;
+    __syncthreads();
+    for (int base = 0; base < nrec; base += kThreads) {
+        const int e = base + tid;
+        if (e < nrec) {
+            const int rr = e / nch, c = e - rr * nch;
+            uint32_t pay[kRecWords];
+            const bool ok = read_record(
+                P.prec + ((static_cast<size_t>(b) * P.nslot + rv_slot(rr, Le, P.K)) * nch + c) * kRecWords, P.tag, pay);
+            stage[tid] = partial_from(pay);
+            if (!ok) stage_bad = 1;
+        }
+        __syncthreads();
+        const int cnt = min(kThreads, nrec - base);
+        if (nch <= kLaneMergeMax) {
+            // few chunks per logit row: lane rr of wave 0 merges its logit
+            // row's chunks of this pass in chunk order
+            if (wv == 0 && lane < nrv) {
+                const int rr = lane;
+                const int lo = max(rr * nch, base), hi = min((rr + 1) * nch, base + cnt);
+                if (lo < hi) {
+                    float O = R.o[rr], M = R.m[rr], LX = R.lx[rr];
+                    double S = R.s[rr];
+                    for (int i = lo; i < hi; ++i) {
+                        const Partial q = stage[i - base];
+                        float On;
+                        S = merge_stats(O, S, q.o, static_cast<double>(q.s), On);
+                        O = On;
+                        M = fmaxf(M, q.m);
+                        LX = fmaxf(LX, q.lx);
+                    }
+                    R.o[rr] = O;
+                    R.m[rr] = M;
+                    R.lx[rr] = LX;
+                    R.s[rr] = S;
+                }
+            }
+            __syncthreads();
+            continue;
+        }
+        for (int rr = wv; rr < nrv; rr += kWaves) {
+            const int lo = max(rr * nch, base), hi = min((rr + 1) * nch, base + cnt);
+            if (lo >= hi) continue;
+            float O = -SV_INF, M = -SV_INF, LX = -SV_INF;
+            double S = 0.0;
+            for (int i = lo + lane; i < hi; i += 64) {
+                const Partial q = stage[i - base];
+                float On;
+                S = merge_stats(O, S, q.o, static_cast<double>(q.s), On);
+                O = On;
+                M = fmaxf(M, q.m);
+                LX = fmaxf(LX, q.lx);
+            }
+            for (int off = 32; off >= 1; off >>= 1) {
+                const float O2 = __shfl_xor(O, off, 64);
+                const double S2 = __shfl_xor(S, off, 64);
+                const float M2 = __shfl_xor(M, off, 64);
+                const float L2 = __shfl_xor(LX, off, 64);
+                float On;
+                S = merge_stats(O, S, O2, S2, On);
+                O = On;
+                M = fmaxf(M, M2);
+                LX = fmaxf(LX, L2);
+            }
+            if (lane == 0) {
+                float On;
+                R.s[rr] = merge_stats(R.o[rr], R.s[rr], O, S, On);
+                R.o[rr] = On;
+                R.m[rr] = fmaxf(R.m[rr], M);
+                R.lx[rr] = fmaxf(R.lx[rr], LX);
+            }
+        }
+        __syncthreads();
+    }
+    if (tid < nrv) {
+        const double S = R.s[tid];
+        R.kept[tid] = S;
+        R.tau[tid] = 0u;
+        R.cut[tid] = -1;
+        R.valid[tid] = (!stage_bad && S > 0.0 && S < static_cast<double>(SV_INF)) ? 1 : 0;
+    }
+    __syncthreads();
+}
 
-// The decision of batch row b, made by ONE wave (64 lanes, no workgroup
-// barrier) once every logit row of b has its statistics: load the row's
-// statistics, check validity, take p'(x_j) and q'(x_j) from the logits at the
-// drafted ids, draw the Philox uniforms, scan for the first rejection, and
-// write the row's outputs, probe records and the RowParam the resample pass
-// reads.
-template <int DT, bool TOPP>
-__device__ void row_decide(const Params& P, int b, RowShared& R, StageShared* stgp) {
+// Statistics and nucleus cuts of every logit row of batch row b into R from
+// the nucleus pass's records (one wave).
+__device__ __forceinline__ void fill_row_from_rv(const Params& P, int b, int Le, RowShared& R) {
     const int lane = threadIdx.x & 63;
-    const int K = P.K, K1 = P.K + 1;
-    bool rowok;
-    const int Le = row_len(P, b, rowok);
-    const int nrv = 2 * Le + 1;
-    const int x = (lane < Le) ? P.tokens[static_cast<int64_t>(b) * K + lane] : -1;
-    if (TOPP) {
-        if (lane < nrv) {
-            const RvState q = load_rvstate(P.rv + static_cast<size_t>(b) * P.nslot + rv_slot(lane, Le, K));
-            R.o[lane] = q.o;
-            R.m[lane] = q.m;
-            R.lx[lane] = q.lx;
-            R.s[lane] = q.s;
-            R.kept[lane] = q.kept;
-            R.tau[lane] = q.tau;
-            R.cut[lane] = q.cut;
-            R.valid[lane] = q.valid;
-        }
-    } else {
-        // Stage the row's (logit row, chunk) partials in LDS, kStage at a
-        // time, four independent loads per lane in flight; lane r < nrv then
-        // merges logit row r's chunks in chunk order.
-        StageShared& stg = *stgp;
-        const int pairs = nrv * P.nch;
-        float O = -SV_INF, M = -SV_INF, LX = -SV_INF;
-        double S = 0.0;
-        for (int base = 0; base < pairs; base += kStage) {
-            const int cnt = min(kStage, pairs - base);
-            for (int q0 = 0; q0 < cnt; q0 += 4 * 64) {
-                Partial pq[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int pi = q0 + u * 64 + lane;
-                    if (pi < cnt) {
-                        const int pr = (base + pi) / P.nch, pc = (base + pi) - pr * P.nch;
-                        pq[u] = load_partial(P.part + (static_cast<size_t>(b) * P.nslot + rv_slot(pr, Le, K)) * P.nch + pc);
-                    }
-                }
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const int pi = q0 + u * 64 + lane;
-                    if (pi < cnt) {
-                        stg.o[pi] = pq[u].o;
-                        stg.m[pi] = pq[u].m;
-                        stg.lx[pi] = pq[u].lx;
-                        stg.s[pi] = pq[u].s;
-                    }
-                }
-            }
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            if (lane < nrv) {
-                const int p0 = max(lane * P.nch, base), p1 = min((lane + 1) * P.nch, base + cnt);
-                for (int pi = p0; pi < p1; ++pi) {
-                    float On;
-                    S = merge_stats(O, S, stg.o[pi - base], stg.s[pi - base], On);
-                    O = On;
-                    M = fmaxf(M, stg.m[pi - base]);
-                    LX = fmaxf(LX, stg.lx[pi - base]);
-                }
-            }
-            __builtin_amdgcn_wave_barrier();
-        }
-        if (lane < nrv) {
-            R.o[lane] = O;
-            R.m[lane] = M;
-            R.lx[lane] = LX;
-            R.s[lane] = S;
-            R.kept[lane] = S;
-            R.tau[lane] = 0u;
-            R.cut[lane] = -1;
-            R.valid[lane] = (S > 0.0 && S < static_cast<double>(SV_INF)) ? 1 : 0;
-        }
+    if (lane < 2 * Le + 1) {
+        const RvState q = load_rvstate(P.rv + static_cast<size_t>(b) * P.nslot + rv_slot(lane, Le, P.K));
+        R.o[lane] = q.o;
+        R.m[lane] = q.m;
+        R.lx[lane] = q.lx;
+        R.s[lane] = q.s;
+        R.kept[lane] = q.kept;
+        R.tau[lane] = q.tau;
+        R.cut[lane] = q.cut;
+        R.valid[lane] = q.valid;
     }
     __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+}
+
+// The decision of batch row b, made by ONE wave from the statistics in R:
+// check validity, take p'(x_j) and q'(x_j) from the logits at the drafted
+// ids, draw the Philox uniforms, scan for the first rejection.  Lane 0 fills
+// rp (what the resample needs).  With `outputs` the wave also writes the
+// row's accepted tokens, -1 padding, n, and the probe records; the token at
+// position n is the resample's.
+// Lane j < Le's drafted id (loaded early by the callers, to overlap the load
+// with their waits).
+__device__ __forceinline__ int lane_token(const Params& P, int b, int Le) {
+    const int lane = threadIdx.x & 63;
+    return (lane < Le) ? P.tokens[static_cast<int64_t>(b) * P.K + lane] : -1;
+}
+
+template <bool TOPP>
+__device__ void decide_row(const Params& P, int b, int Le, bool rowok, const RowShared& R, bool outputs, int x,
+                           RowParam& rp) {
+    const int lane = threadIdx.x & 63;
+    const int K = P.K, K1 = P.K + 1;
+    const int nrv = 2 * Le + 1;
     int bad = rowok ? 0 : 1;
     for (int r = lane; r < nrv; r += 64) bad |= R.valid[r] ? 0 : 1;
     const bool rowbad = __ballot(bad) != 0ull;
@@ -340,16 +436,8 @@ __device__ void row_decide(const Params& P, int b, RowShared& R, StageShared* st
     const bool anybad = rowbad || (__ballot(bad_tok) != 0ull);
     const unsigned long long rejm = __ballot(rej);
     const int n = anybad ? 0 : (rejm ? (__ffsll(static_cast<long long>(rejm)) - 1) : Le);
-    const double un = __shfl(u_res, n, 64);
-    // outputs
-    for (int j = lane; j < K1; j += 64) {
-        int v = -1;
-        if (!anybad && j < n) v = P.tokens[static_cast<int64_t>(b) * K + j];
-        if (anybad || j != n) P.out_tokens[static_cast<int64_t>(b) * K1 + j] = v;
-    }
+    const double un = readlane_f64(u_res, n);
     if (lane == 0) {
-        P.out_n[b] = anybad ? -1 : n;
-        RowParam rp;
         rp.mode = anybad ? MODE_SKIP : (n < Le ? MODE_RESID : MODE_BONUS);
         rp.n = n;
         rp.oT = R.o[n];
@@ -363,11 +451,18 @@ __device__ void row_decide(const Params& P, int b, RowShared& R, StageShared* st
         rp.tauD = resid ? R.tau[rD] : 0u;
         rp.cutD = resid ? R.cut[rD] : -1;
         rp.u = un;
-        P.rowp[b] = rp;
+    }
+    if (!outputs) return;
+    for (int j = lane; j < K1; j += 64) {
+        int v = -1;
+        if (!anybad && j < n) v = P.tokens[static_cast<int64_t>(b) * K + j];
+        if (anybad || j != n) P.out_tokens[static_cast<int64_t>(b) * K1 + j] = v;
+    }
+    if (lane == 0) {
+        P.out_n[b] = anybad ? -1 : n;
         if (P.probe_row) {
+            // fields 0 and 1 (Z, t) belong to the row's last resample item
             double* pr = P.probe_row + static_cast<size_t>(b) * 4;
-            pr[0] = nan64();
-            pr[1] = nan64();
             pr[2] = anybad ? nan64() : un;
             pr[3] = anybad ? -1.0 : static_cast<double>(n);
         }
@@ -403,42 +498,93 @@ __device__ void row_decide(const Params& P, int b, RowShared& R, StageShared* st
 // Statistics pass: one workgroup per chunk of kThreads*U 16-byte vectors of
 // one logit row, U per lane, all loads issued before any use.
 // ---------------------------------------------------------------------------
-template <int DT, int U, bool MASK>
-__device__ __forceinline__ void reduce_lane(const RowGrid& g, const uint4* raw, int64_t k0, int64_t k1, int V,
+// Word q (0..3) of a 16-byte vector.
+__device__ __forceinline__ uint32_t word(const uint4& v, int q) { return q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w; }
+__device__ __forceinline__ void set_word(uint4& v, int q, uint32_t w) {
+    if (q == 0) v.x = w;
+    else if (q == 1) v.y = w;
+    else if (q == 2) v.z = w;
+    else v.w = w;
+}
+// Element i of a raw 16-byte vector as fp32 (i known at compile time after
+// unrolling: one shift or mask for bf16, nothing for fp32).
+template <int DT> __device__ __forceinline__ float elem(const uint4& v, int i) {
+    if (DT == DT_F32) return __uint_as_float(word(v, i));
+    const uint32_t w = word(v, i >> 1);
+    return __uint_as_float((i & 1) ? (w & 0xFFFF0000u) : (w << 16));
+}
+// Ids of vector k outside [0, V) become -inf, on the raw bits.
+template <int DT>
+__device__ __forceinline__ void mask_edge_raw(uint4& v, int64_t k, int head, int V) {
+    constexpr int VE = Fmt<DT>::VE;
+#pragma unroll
+    for (int i = 0; i < VE; ++i) {
+        const int64_t id = k * VE + i - head;
+        if (id < 0 || id >= V) {
+            if (DT == DT_F32) {
+                set_word(v, i, 0xFF800000u);
+            } else {
+                const uint32_t w = word(v, i >> 1);
+                set_word(v, i >> 1, (i & 1) ? ((w & 0x0000FFFFu) | 0xFF800000u) : ((w & 0xFFFF0000u) | 0x0000FF80u));
+            }
+        }
+    }
+}
+
+// Statistics of one lane's U vectors, read from the raw loaded words in two
+// passes (max, then the sum of 2^(l*c - o)) so that no unpacked copy of the
+// chunk is kept in registers.
+// Element rx (known only at run time) of a raw 16-byte vector.
+template <int DT> __device__ __forceinline__ float elem_at(const uint4& v, int rx) {
+    if (DT == DT_F32) return __uint_as_float(rx == 0 ? v.x : rx == 1 ? v.y : rx == 2 ? v.z : v.w);
+    const int q = rx >> 1;
+    const uint32_t w = q == 0 ? v.x : q == 1 ? v.y : q == 2 ? v.z : v.w;
+    return __uint_as_float((rx & 1) ? (w & 0xFFFF0000u) : (w << 16));
+}
+
+template <int DT, int U>
+__device__ __forceinline__ void reduce_lane(const RowGrid& g, uint4* raw, int64_t k0, int64_t k1, int V, bool edge,
                                             float c_hi, float c_lo, int64_t kx, int rx, float& lx, float& m, float& o,
                                             float& s) {
     constexpr int VE = Fmt<DT>::VE;
-    constexpr int N = U * VE;
-    float f[N];
+    if (edge) {
+        // the chunk holds the row's first or last vector
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        unpack<DT>(raw[u], f + u * VE);
-        const int64_t k = k0 + u * kThreads + threadIdx.x;
-        if (MASK) {
-            if (k < k1 && (k == 0 || k == g.nvec - 1)) mask_edge<DT>(f + u * VE, k, g.head, V);
-        }
-        if (k == kx) {
-            // the lane holding the drafted id's vector records its logit
-            float v = -SV_INF;
-#pragma unroll
-            for (int i = 0; i < VE; ++i) v = (i == rx) ? f[u * VE + i] : v;
-            lx = v;
+        for (int u = 0; u < U; ++u) {
+            const int64_t k = k0 + u * kThreads + threadIdx.x;
+            if (k < k1 && (k == 0 || k == g.nvec - 1)) mask_edge_raw<DT>(raw[u], k, g.head, V);
         }
     }
-    // N is a multiple of 4: a v_max3 tree
-    float bm = max3f(f[0], f[1], f[2]);
+    // the lane holding the drafted id's vector records its logit
 #pragma unroll
-    for (int i = 3; i + 1 < N; i += 2) bm = max3f(bm, f[i], f[i + 1]);
-    bm = fmaxf(bm, f[N - 1]);
-    m = bm;
-    o = ceilf(bm * c_hi);
+    for (int u = 0; u < U; ++u)
+        if (k0 + u * kThreads + threadIdx.x == kx) lx = elem_at<DT>(raw[u], rx);
+    // pass 1: the lane's max, four independent v_max3 chains
+    float bm[4] = {-SV_INF, -SV_INF, -SV_INF, -SV_INF};
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (DT == DT_F32) {
+            bm[u & 3] = max3f(bm[u & 3], elem<DT>(raw[u], 0), elem<DT>(raw[u], 1));
+            bm[(u + 2) & 3] = max3f(bm[(u + 2) & 3], elem<DT>(raw[u], 2), elem<DT>(raw[u], 3));
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) bm[q] = max3f(bm[q], elem<DT>(raw[u], 2 * q), elem<DT>(raw[u], 2 * q + 1));
+        }
+    }
+    m = max3f(bm[0], bm[1], fmaxf(bm[2], bm[3]));
+    // keep the unpacked values of pass 1 from living into pass 2: the raw
+    // words are re-read (and re-unpacked, one instruction per element)
+#pragma unroll
+    for (int u = 0; u < U; ++u) asm volatile("" : "+v"(raw[u].x), "+v"(raw[u].y), "+v"(raw[u].z), "+v"(raw[u].w));
+    o = ceilf(m * c_hi);
     const float off = (o == -SV_INF) ? 0.f : o;
+    // pass 2: the sum, a pairwise tree per vector
     float acc[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         float e[VE];
 #pragma unroll
-        for (int i = 0; i < VE; ++i) e[i] = tempexp(f[u * VE + i], c_hi, c_lo, off);
+        for (int i = 0; i < VE; ++i) e[i] = tempexp(elem<DT>(raw[u], i), c_hi, c_lo, off);
 #pragma unroll
         for (int w = VE / 2; w >= 1; w >>= 1)
 #pragma unroll
@@ -452,19 +598,16 @@ __device__ __forceinline__ void reduce_lane(const RowGrid& g, const uint4* raw, 
     s = acc[0];
 }
 
-template <int DT, int U, bool TOPP>
-__global__ __launch_bounds__(kThreads) void k_stats(Params P) {
+// One statistics item: chunk `chunk` of logit row `slot` of batch row b.
+// Streams the chunk once, reduces it to (o, m, lx, s) and publishes the
+// tagged record; nothing waits on the store.  `item` is unique to the
+// workgroup within the launch (it tags the LDS hand-over of lx).
+template <int DT, int U>
+__device__ __forceinline__ void stats_item(const Params& P, int b, int slot, int chunk, int item) {
     __shared__ float sh_o[kWaves], sh_s[kWaves], sh_m[kWaves];
     __shared__ float sh_lxv;
-    __shared__ int sh_lxtag, s_last;
-    __shared__ RowShared R;
-    __shared__ StageShared stg;
+    __shared__ int sh_lxtag;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int item = blockIdx.x;
-    const int rvi = item / P.nch;
-    const int chunk = item - rvi * P.nch;
-    const int b = rvi / P.nslot;
-    const int slot = rvi - b * P.nslot;
     bool rowok;
     const int Le = row_len(P, b, rowok);
     const bool tgt = slot <= P.K;
@@ -498,10 +641,10 @@ __global__ __launch_bounds__(kThreads) void k_stats(Params P) {
         }
     }
     float lx = -SV_INF, m, o, sl;
-    if (k0 == 0 || k0 + STEP >= g.nvec - 1) reduce_lane<DT, U, true>(g, raw, k0, k1, P.V, P.c_hi, P.c_lo, kx, rx, lx, m, o, sl);
-    else reduce_lane<DT, U, false>(g, raw, k0, k1, P.V, P.c_hi, P.c_lo, kx, rx, lx, m, o, sl);
+    reduce_lane<DT, U>(g, raw, k0, k1, P.V, k0 == 0 || k0 + STEP >= g.nvec - 1, P.c_hi, P.c_lo, kx, rx, lx, m, o, sl);
     // the one lane holding the drafted id's vector hands its logit over,
-    // tagged with this workgroup's id (LDS is not cleared between workgroups)
+    // tagged with this workgroup's item (LDS is not cleared between
+    // workgroups)
     {
         const int64_t rel = kx - k0 - tid;
         if (kx >= k0 && rel >= 0 && rel % kThreads == 0 && rel / kThreads < U) {
@@ -521,7 +664,8 @@ __global__ __launch_bounds__(kThreads) void k_stats(Params P) {
         sh_m[wv] = Mw;
     }
     __syncthreads();
-    if (tid == 0) {
+    if (tid < kRecWords) {
+        // four lanes combine the waves alike; lane k stores word k
         float O = sh_o[0], M = sh_m[0];
         for (int w = 1; w < kWaves; ++w) {
             O = fmaxf(O, sh_o[w]);
@@ -532,23 +676,29 @@ __global__ __launch_bounds__(kThreads) void k_stats(Params P) {
             S += (sh_o[w] == -SV_INF) ? static_cast<double>(sh_s[w])
                                       : ldexp(static_cast<double>(sh_s[w]), static_cast<int>(fmaxf(sh_o[w] - O, -1100.f)));
         const float LX = (kx >= k0 && kx < k0 + STEP && sh_lxtag == item) ? sh_lxv : -SV_INF;
-        store_partial(P.part + static_cast<size_t>(rvi) * P.nch + chunk, O, M, LX, S);
-        int last = 0;
-        if (!TOPP) {
-            stores_done();
-            last = arrive_last(P.row_cnt + static_cast<size_t>(b) * kCounterStride,
-                               static_cast<uint32_t>((2 * Le + 1) * P.nch))
-                       ? 1
-                       : 0;
-        }
-        s_last = last;
+        const float v = tid == 0 ? O : tid == 1 ? M : tid == 2 ? LX : static_cast<float>(S);
+        uint64_t* rec = P.prec + ((static_cast<size_t>(b) * P.nslot + slot) * P.nch + chunk) * kRecWords;
+        st_agent(rec + tid, tagged(P.tag, __float_as_uint(v)));
     }
-    if (TOPP) return;
-    __syncthreads();
-    // the row's last arrival: wave 0 makes the decision
-    if (!s_last || wv != 0) return;
-    if (lane == 0) counter_reset(P.row_cnt + static_cast<size_t>(b) * kCounterStride);
-    row_decide<DT, false>(P, b, R, &stg);
+}
+
+// Statistics pass of the top-p pipeline: one workgroup per (b, slot, chunk).
+template <int DT, int U>
+__global__ __launch_bounds__(kThreads, 8) void k_stats(Params P) {
+    const int item = blockIdx.x;
+    {
+        // clear this call's resample-item records, which the row pass polls
+        // (words [item*per, (item+1)*per), per <= kThreads by the host)
+        const int64_t words = static_cast<int64_t>(P.B) * P.nq * kRecWords;
+        const int64_t grid = static_cast<int64_t>(P.B) * P.nslot * P.nch;
+        const int per = static_cast<int>((words + grid - 1) / grid);
+        const int64_t e = static_cast<int64_t>(item) * per + threadIdx.x;
+        if (static_cast<int>(threadIdx.x) < per && e < words) P.qrec[e] = 0ull;
+    }
+    const int rvi = item / P.nch;
+    const int chunk = item - rvi * P.nch;
+    const int b = rvi / P.nslot;
+    stats_item<DT, U>(P, b, rvi - b * P.nslot, chunk, item);
 }
 
 // ---------------------------------------------------------------------------
@@ -937,12 +1087,13 @@ __global__ __launch_bounds__(kThreads) void k_topp(Params P) {
     if (wv == 0) {
         float O, M, LX;
         double S;
-        combine_partials(P, b, slot, lane, O, M, LX, S);
+        bool ok;
+        combine_partials(P, b, slot, lane, O, M, LX, S, ok);
         if (lane == 0) {
             s_o = O;
             s_m = M;
             s_lx = LX;
-            s_s = S;
+            s_s = ok ? S : nan64();
         }
     }
     __syncthreads();
@@ -978,25 +1129,30 @@ __global__ __launch_bounds__(kThreads) void k_topp(Params P) {
     last = __shfl(last, 0, 64);
     if (!last) return;
     if (lane == 0) counter_reset(P.row_cnt + static_cast<size_t>(b) * kCounterStride);
-    row_decide<DT, true>(P, b, R, nullptr);
+    bool rowok2;
+    const int Le2 = row_len(P, b, rowok2);
+    const int x = lane_token(P, b, Le2);
+    fill_row_from_rv(P, b, Le2, R);
+    RowParam rp;
+    decide_row<true>(P, b, Le2, rowok2, R, true, x, rp);
+    if (lane == 0) P.rowp[b] = rp;
 }
 
 // ---------------------------------------------------------------------------
-// Resample pass: workgroups of kRThreads threads; workgroup (b, c) covers
-// steps [c*res_steps, (c+1)*res_steps) of row b, a step being kStepIds
-// consecutive ids with kRun per thread.  It publishes the residual (or bonus)
-// mass and the target mass of every step it covers; the row's last workgroup
-// then finds the step holding t = u*Z and rescans that step alone.
+// Row pass.  Workgroup (b, r) is resample item r of batch row b: ids
+// [r*kItemIds, (r+1)*kItemIds) of the row's position n, in kRuns runs: run k
+// is the kThreads*kRun ids from r*kItemIds + k*kThreads*kRun, thread t taking
+// the kRun consecutive ids at t*kRun (16-byte loads, coalesced).  Without
+// top-p every item first makes the row's decision from the statistics
+// records (all items reach the same one; item 0 writes the outputs).  Each
+// item keeps its weights in LDS and publishes its residual (or bonus) mass W
+// and target mass as a tagged record; every item then reads all the row's
+// records, forms Z and t = u*Z, and the item holding t picks the token from
+// its weights.  The waits are on records of workgroups of the same row, which
+// are consecutive in the grid: when a row has an item still to start, all
+// earlier rows' items are running or done, so every wait ends.
 // ---------------------------------------------------------------------------
-constexpr int kRThreads = 1024;
-constexpr int kRWaves = kRThreads / 64;
-constexpr int kRun = 8;
-constexpr int kStepIds = kRThreads * kRun;
-// Steps whose loads are in flight together: four 16-byte vectors per thread
-// and tensor, which keeps the unpacked runs within the 128 registers a
-// 1024-thread workgroup allows.
-template <int DT> constexpr int group_steps() { return 4 * Fmt<DT>::VE / kRun; }
-static_assert(kStepIds == kResStepIds, "host and kernels must agree on the resample step");
+static_assert(kItemIds == kThreads * kRun * kRuns, "resample item layout");
 
 // A readable 16-byte vector that stands in for loads past the end of a row.
 __device__ const uint4 kPadVec = {0u, 0u, 0u, 0u};
@@ -1010,23 +1166,28 @@ __device__ const uint4 kPadVec = {0u, 0u, 0u, 0u};
 // are left undefined and become -inf in unpack_masked.
 template <int DT>
 __device__ __forceinline__ void load_run_elems(const uint8_t* row, int64_t id0, int V, uint4* v) {
+    // Only rows not 16-byte aligned, and a run straddling V, come here: one
+    // 32-bit word at a time keeps this rare path from setting the register
+    // budget of the whole kernel.
     constexpr int NVR = kRun / Fmt<DT>::VE;
     const int64_t last = static_cast<int64_t>(V) - 1;
-    uint32_t w[4 * NVR];
-    if (DT == DT_F32) {
-        const uint32_t* r = reinterpret_cast<const uint32_t*>(row);
 #pragma unroll
-        for (int i = 0; i < kRun; ++i) w[i] = r[min(id0 + i, last)];
-    } else {
-        const uint16_t* r = reinterpret_cast<const uint16_t*>(row);
-        uint32_t h[kRun];
-#pragma unroll
-        for (int i = 0; i < kRun; ++i) h[i] = r[min(id0 + i, last)];
-#pragma unroll
-        for (int i = 0; i < kRun; i += 2) w[i / 2] = h[i] | (h[i + 1] << 16);
+    for (int q = 0; q < NVR; ++q) {
+        uint4 x = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll 1
+        for (int c = 0; c < 4; ++c) {
+            uint32_t wd;
+            if (DT == DT_F32) {
+                wd = reinterpret_cast<const uint32_t*>(row)[min(id0 + q * 4 + c, last)];
+            } else {
+                const uint16_t* r16 = reinterpret_cast<const uint16_t*>(row);
+                const int64_t i0 = id0 + q * 8 + 2 * c;
+                wd = static_cast<uint32_t>(r16[min(i0, last)]) | (static_cast<uint32_t>(r16[min(i0 + 1, last)]) << 16);
+            }
+            set_word(x, c, wd);
+        }
+        v[q] = x;
     }
-#pragma unroll
-    for (int q = 0; q < NVR; ++q) v[q] = make_uint4(w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]);
 }
 template <int DT>
 __device__ __forceinline__ void issue_run(const uint8_t* row, int64_t id0, int V, bool aligned, uint4* v) {
@@ -1074,257 +1235,337 @@ __device__ __forceinline__ void run_weights(const float* lt, const float* ld, bo
     }
 }
 
-__device__ __forceinline__ double ld_agent_d(const double* p) {
-    return __longlong_as_double(static_cast<long long>(ld_agent(p)));
+// Raw 16-byte vectors of one item for one thread: kRuns runs of each needed
+// tensor.
+template <int DT> struct ItemRaw {
+    static constexpr int NVR = kRun / Fmt<DT>::VE;
+    uint4 t[kRuns][NVR];
+    uint4 d[kRuns][NVR];
+};
+__device__ __forceinline__ int64_t item_run_id0(int r, int k) {
+    return static_cast<int64_t>(r) * kItemIds + static_cast<int64_t>(k) * (kThreads * kRun) +
+           static_cast<int64_t>(threadIdx.x) * kRun;
 }
-__device__ __forceinline__ void st_agent_d(double* p, double v) {
-    st_agent(p, static_cast<uint64_t>(__double_as_longlong(v)));
+// Issues every load of the item, then reloads by elements a run whose vector
+// straddles V (aligned rows only).
+template <int DT>
+__device__ __forceinline__ void load_item(const uint8_t* rowT, const uint8_t* rowD, bool resid, bool aligned, int r,
+                                          int V, ItemRaw<DT>& raw) {
+#pragma unroll
+    for (int k = 0; k < kRuns; ++k) {
+        issue_run<DT>(rowT, item_run_id0(r, k), V, aligned, raw.t[k]);
+        if (resid) issue_run<DT>(rowD, item_run_id0(r, k), V, aligned, raw.d[k]);
+    }
+    if (aligned) {
+#pragma unroll
+        for (int k = 0; k < kRuns; ++k) {
+            if (run_straddles<DT>(item_run_id0(r, k), V)) {
+                load_run_elems<DT>(rowT, item_run_id0(r, k), V, raw.t[k]);
+                if (resid) load_run_elems<DT>(rowD, item_run_id0(r, k), V, raw.d[k]);
+            }
+        }
+    }
 }
-
+// Weights of run k: w = max(0, p' - q') (or p' for the bonus) and p = p'.
 template <int DT, bool TOPP>
-__global__ __launch_bounds__(kRThreads) void k_resample(Params P) {
-    constexpr int NVR = kRun / Fmt<DT>::VE, G = group_steps<DT>();
-    __shared__ double sw[kRWaves][G], sp[kRWaves][G];
-    __shared__ double s_wtot[kRWaves];
-    __shared__ int s_last, s_sel, s_step, s_hit[kRWaves], s_lastpos[kRWaves];
-    __shared__ double s_spre, s_Z, s_t;
+__device__ __forceinline__ void item_run_weights(const Params& P, const RowParam& rp, bool resid, float invT, float invD,
+                                                 const ItemRaw<DT>& raw, int r, int k, float* w, float* p) {
+    const int64_t id0 = item_run_id0(r, k);
+    float lt[kRun], ld[kRun];
+    if (static_cast<int64_t>(r + 1) * kItemIds <= P.V) {
+        // the whole item lies inside the row (uniform): nothing to mask
+        unpack_run<DT>(raw.t[k], lt);
+        if (resid) unpack_run<DT>(raw.d[k], ld);
+    } else {
+        unpack_masked<DT>(raw.t[k], id0, P.V, lt);
+        if (resid) unpack_masked<DT>(raw.d[k], id0, P.V, ld);
+    }
+    run_weights<TOPP>(lt, ld, resid, id0, rp, P.c_hi, P.c_lo, invT, invD, w, p);
+}
+__device__ __forceinline__ float run_sum(const float* v) {
+    float a = (v[0] + v[1]) + (v[2] + v[3]);
+    float c = (v[4] + v[5]) + (v[6] + v[7]);
+    return a + c;
+}
+static_assert(kRun == 8, "run_sum sums 8 values");
+
+// The resample part of batch row b for item r, given the row's decision rp
+// (the same in every item of the row).  Every thread must call it.
+template <int DT, bool TOPP>
+__device__ void resample_item(const Params& P, int b, int r, const RowParam& rp_in) {
+    __shared__ double s_w[kWaves], s_p[kWaves];
+    __shared__ double s_wt[kRuns][kWaves];
+    __shared__ int s_hit[kRuns][kWaves], s_lastpos[kWaves];
+    __shared__ int s_sel, s_item, s_ok;
+    __shared__ double s_pre, s_Z, s_t;
+    __shared__ float s_rw[kRuns][kRun][kThreads];  // this item's weights
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int b = blockIdx.x / P.res_split;
-    const int c = blockIdx.x - b * P.res_split;
-    const RowParam rp = P.rowp[b];
     // the row's mode and n are the same for every lane: keep them scalar
-    const int mode = __builtin_amdgcn_readfirstlane(rp.mode);
-    const int rn = __builtin_amdgcn_readfirstlane(rp.n);
-    // rowp was written by this call's decision; anything else is skipped
-    if ((mode != MODE_RESID && mode != MODE_BONUS) || rn < 0 || rn > P.K) return;
+    const int mode = __builtin_amdgcn_readfirstlane(rp_in.mode);
+    const int rn = __builtin_amdgcn_readfirstlane(rp_in.n);
+    if ((mode != MODE_RESID && mode != MODE_BONUS) || rn < 0 || rn > P.K) {
+        // an invalid row: the decision wrote its outputs; no item waits
+        if (r == 0 && tid == 0 && P.probe_row) {
+            P.probe_row[static_cast<size_t>(b) * 4 + 0] = nan64();
+            P.probe_row[static_cast<size_t>(b) * 4 + 1] = nan64();
+        }
+        return;
+    }
+    const RowParam& rp = rp_in;
     const bool resid = mode == MODE_RESID;
     const uint8_t* rowT = row_ptr<DT>(P, true, b, rn);
     const uint8_t* rowD = resid ? row_ptr<DT>(P, false, b, rn) : rowT;
     const bool aligned = ((reinterpret_cast<uintptr_t>(rowT) & 15) == 0) && ((reinterpret_cast<uintptr_t>(rowD) & 15) == 0);
     const float invT = static_cast<float>(1.0 / rp.keptT);
     const float invD = resid ? static_cast<float>(1.0 / rp.keptD) : 0.f;
-    double* cm = P.cmass + static_cast<size_t>(b) * P.nch2 * 2;
+    const int nq = P.nq;
+    uint64_t* qrec = P.qrec + static_cast<size_t>(b) * nq * kRecWords;
 
-    const int s0 = c * P.res_steps;
-    const int s1 = min(s0 + P.res_steps, P.nch2);
-    bool stored = false;
-    for (int g0 = s0; g0 < s1; g0 += G) {
-        const int gn = min(G, s1 - g0);
-        uint4 vt[G][NVR], vd[G][NVR];
-        // uniform: a whole group of whole steps of aligned rows loads with
-        // straight-line 16-byte loads, all in flight together
-        const bool fast = aligned && gn == G && static_cast<int64_t>(g0 + G) * kStepIds <= P.V;
-        if (fast) {
+    // 1. the item's weights (into LDS) and masses
+    double ws = 0.0, ps = 0.0;
+    {
+        ItemRaw<DT> raw;
+        load_item<DT>(rowT, rowD, resid, aligned, r, P.V, raw);
 #pragma unroll
-            for (int k = 0; k < G; ++k) {
-                const int64_t id0 = static_cast<int64_t>(g0 + k) * kStepIds + static_cast<int64_t>(tid) * kRun;
-                const uint4* pt = reinterpret_cast<const uint4*>(rowT + id0 * Fmt<DT>::E);
-                const uint4* pd = reinterpret_cast<const uint4*>(rowD + id0 * Fmt<DT>::E);
+        for (int k = 0; k < kRuns; ++k) {
+            float w[kRun], p[kRun];
+            item_run_weights<DT, TOPP>(P, rp, resid, invT, invD, raw, r, k, w, p);
 #pragma unroll
-                for (int q = 0; q < NVR; ++q) vt[k][q] = gload16(pt + q);
-                if (resid) {
-#pragma unroll
-                    for (int q = 0; q < NVR; ++q) vd[k][q] = gload16(pd + q);
-                }
-            }
-        } else {
-#pragma unroll
-            for (int k = 0; k < G; ++k) {
-                if (k < gn) {
-                    const int64_t id0 = static_cast<int64_t>(g0 + k) * kStepIds + static_cast<int64_t>(tid) * kRun;
-                    issue_run<DT>(rowT, id0, P.V, aligned, vt[k]);
-                    if (resid) issue_run<DT>(rowD, id0, P.V, aligned, vd[k]);
-                }
-            }
-            if (aligned) {
-#pragma unroll
-                for (int k = 0; k < G; ++k) {
-                    const int64_t id0 = static_cast<int64_t>(g0 + k) * kStepIds + static_cast<int64_t>(tid) * kRun;
-                    if (k < gn && run_straddles<DT>(id0, P.V)) {
-                        load_run_elems<DT>(rowT, id0, P.V, vt[k]);
-                        if (resid) load_run_elems<DT>(rowD, id0, P.V, vd[k]);
-                    }
-                }
-            }
+            for (int i = 0; i < kRun; ++i) s_rw[k][i][tid] = w[i];
+            ws += static_cast<double>(run_sum(w));
+            ps += static_cast<double>(run_sum(p));
+            // one run at a time: interleaving the runs' exponentials would
+            // multiply the registers live here
+            __builtin_amdgcn_sched_barrier(0);
         }
-#pragma unroll
-        for (int k = 0; k < G; ++k) {
-            double ws = 0.0, ps = 0.0;
-            if (k < gn) {
-                const int64_t id0 = static_cast<int64_t>(g0 + k) * kStepIds + static_cast<int64_t>(tid) * kRun;
-                float lt[kRun], ld[kRun], w[kRun], p[kRun];
-                if (fast) {
-                    unpack_run<DT>(vt[k], lt);
-                    if (resid) unpack_run<DT>(vd[k], ld);
-                } else {
-                    unpack_masked<DT>(vt[k], id0, P.V, lt);
-                    if (resid) unpack_masked<DT>(vd[k], id0, P.V, ld);
-                }
-                run_weights<TOPP>(lt, ld, resid, id0, rp, P.c_hi, P.c_lo, invT, invD, w, p);
-#pragma unroll
-                for (int i = 0; i < kRun; ++i) {
-                    ws += static_cast<double>(w[i]);
-                    ps += static_cast<double>(p[i]);
-                }
-            }
-            ws = wave_sum(ws);
-            ps = wave_sum(ps);
-            if (lane == 0) {
-                sw[wv][k] = ws;
-                sp[wv][k] = ps;
-            }
-        }
-        __syncthreads();
-        if (tid < gn) {
-            double W = 0.0, Pm = 0.0;
-            for (int w = 0; w < kRWaves; ++w) {
-                W += sw[w][tid];
-                Pm += sp[w][tid];
-            }
-            st_agent_d(cm + 2 * (g0 + tid), W);
-            st_agent_d(cm + 2 * (g0 + tid) + 1, Pm);
-            stored = true;
-        }
-        __syncthreads();
     }
-    if (stored) stores_done();
+    ws = wave_sum_dpp(ws);
+    ps = wave_sum_dpp(ps);
+    if (lane == 0) {
+        s_w[wv] = ws;
+        s_p[wv] = ps;
+    }
     __syncthreads();
-    if (tid == 0)
-        s_last = arrive_last(P.res_cnt + static_cast<size_t>(b) * kCounterStride, static_cast<uint32_t>(P.res_split)) ? 1 : 0;
-    __syncthreads();
-    if (!s_last) return;
+    const double Wown = (s_w[0] + s_w[1]) + (s_w[2] + s_w[3]);
+    const double Pown = (s_p[0] + s_p[1]) + (s_p[2] + s_p[3]);
+    // 2. publish: words W lo, W hi, Pm lo, Pm hi, each tagged
+    if (tid < kRecWords) {
+        const uint64_t bw = static_cast<uint64_t>(__double_as_longlong(Wown));
+        const uint64_t bp = static_cast<uint64_t>(__double_as_longlong(Pown));
+        const uint64_t v = tid == 0 ? bw : tid == 1 ? (bw >> 32) : tid == 2 ? bp : (bp >> 32);
+        st_agent(qrec + static_cast<size_t>(r) * kRecWords + tid, tagged(P.tag, static_cast<uint32_t>(v)));
+    }
 
-    // Last workgroup of the row.  Wave 0: step masses in id order, their
-    // running sum, Z, t = u*Z and the step holding t.
+    // 3. every item's masses in id order (wave 0; lane l takes items
+    // [l*g, (l+1)*g)): Z, t = u*Z and the item holding t
     if (wv == 0) {
-        if (lane == 0) counter_reset(P.res_cnt + static_cast<size_t>(b) * kCounterStride);
-        const int ns = P.nch2;
-        const int g = (ns + 63) / 64;
-        const int e0 = min(lane * g, ns), e1 = min(e0 + g, ns);
+        const int g = (nq + 63) / 64;
+        const int e0 = min(lane * g, nq), e1 = min(e0 + g, nq);
         double wsum = 0.0, psum = 0.0;
-        for (int k = e0; k < e1; ++k) {
-            wsum += ld_agent_d(cm + 2 * k);
-            psum += ld_agent_d(cm + 2 * k + 1);
+        bool ok = true;
+        for (int e = e0; e < e1; ++e) {
+            double W = Wown, Pm = Pown;
+            if (e != r) {
+                uint32_t pay[kRecWords];
+                ok = poll_record(qrec + static_cast<size_t>(e) * kRecWords, P.tag, pay) && ok;
+                W = __longlong_as_double(static_cast<long long>(static_cast<uint64_t>(pay[0]) | (static_cast<uint64_t>(pay[1]) << 32)));
+                Pm = __longlong_as_double(static_cast<long long>(static_cast<uint64_t>(pay[2]) | (static_cast<uint64_t>(pay[3]) << 32)));
+            }
+            wsum += W;
+            psum += Pm;
         }
-        double incl = wave_incl_scan(wsum, lane);
-        double Z = __shfl(incl, 63, 64);
+        double incl = wave_scan_dpp(wsum);
+        double Z = lane63(incl);
         int sel = 0;
         if (!(Z > 0.0)) {
             // A rejection implies p(x) < q(x), hence positive residual mass;
             // none survives only through rounding: draw from p' instead.
             sel = 1;
-            incl = wave_incl_scan(psum, lane);
-            Z = __shfl(incl, 63, 64);
+            incl = wave_scan_dpp(psum);
+            Z = lane63(incl);
         }
         // exclusive prefix: the previous lane's inclusive value
-        const double prev = __shfl_up(incl, 1, 64);
-        double pre = lane == 0 ? 0.0 : prev;
+        double pre = dpp_f64<kDppWaveShr1, 0xF>(incl);
         const double t = rp.u * Z;
         int first = 0x7FFFFFFF, lastnz = -1;
         double pf = 0.0, pl = 0.0;
-        for (int k = e0; k < e1; ++k) {
-            const double m = ld_agent_d(cm + 2 * k + sel);
+        for (int e = e0; e < e1; ++e) {
+            double m = sel ? Pown : Wown;
+            if (e != r) {
+                // the record is in memory now; read it again rather than
+                // keep g values per lane
+                uint32_t pay[kRecWords];
+                poll_record(qrec + static_cast<size_t>(e) * kRecWords, P.tag, pay);
+                const uint64_t lo = pay[sel ? 2 : 0], hi = pay[sel ? 3 : 1];
+                m = __longlong_as_double(static_cast<long long>(lo | (hi << 32)));
+            }
             if (m > 0.0) {
                 if (first == 0x7FFFFFFF && pre + m > t) {
-                    first = k;
+                    first = e;
                     pf = pre;
                 }
-                lastnz = k;
+                lastnz = e;
                 pl = pre;
             }
             pre += m;
         }
-        const int fe = wave_min_int(first);
-        const int le = wave_max_int(lastnz);
+        const int fe = wave_min_int_dpp(first);
+        const int le = wave_max_int_dpp(lastnz);
         double spre = 0.0;
-        int stp = 0;
+        int item = 0;
         if (fe != 0x7FFFFFFF) {
-            stp = fe;
-            spre = __shfl(pf, fe / g, 64);
+            item = fe;
+            spre = readlane_f64(pf, fe / g);
         } else if (le >= 0) {
-            stp = le;
-            spre = __shfl(pl, le / g, 64);
+            item = le;
+            spre = readlane_f64(pl, le / g);
         }
+        const bool allok = __ballot(!ok) == 0ull;
         if (lane == 0) {
             s_sel = sel;
-            s_step = stp;
-            s_spre = spre;
+            s_item = item;
+            s_pre = spre;
             s_Z = Z;
             s_t = t;
+            s_ok = allok ? 1 : 0;
         }
     }
     __syncthreads();
-    const int sel = s_sel, stp = s_step;
-    const double spre = s_spre, t = s_t;
-
-    // The chosen step alone, in id order: thread sums, a scan within each
-    // wave, wave totals through LDS, then the thread whose run holds t.
-    const int64_t id0 = static_cast<int64_t>(stp) * kStepIds + static_cast<int64_t>(tid) * kRun;
-    float lt[kRun], ld[kRun], w[kRun], p[kRun];
-    {
-        uint4 rt[NVR], rd[NVR];
-        issue_run<DT>(rowT, id0, P.V, aligned, rt);
-        if (resid) issue_run<DT>(rowD, id0, P.V, aligned, rd);
-        if (aligned && run_straddles<DT>(id0, P.V)) {
-            load_run_elems<DT>(rowT, id0, P.V, rt);
-            if (resid) load_run_elems<DT>(rowD, id0, P.V, rd);
-        }
-        unpack_masked<DT>(rt, id0, P.V, lt);
-        if (resid) unpack_masked<DT>(rd, id0, P.V, ld);
+    if (!s_ok) {
+        // a record never arrived: the row is reported invalid
+        if (tid == 0) P.out_n[b] = -1;
+        if (tid < P.K + 1) P.out_tokens[static_cast<size_t>(b) * (P.K + 1) + tid] = -1;
+        return;
     }
-    run_weights<TOPP>(lt, ld, resid, id0, rp, P.c_hi, P.c_lo, invT, invD, w, p);
-    double xs = 0.0;
+    if (s_item != r) return;
+    const int sel = s_sel;
+    const double t = s_t;
+
+    // 4. this item holds t: its weights in id order, run-major, then thread,
+    // then id.  Drawing from p' (sel) is the rare rounding fallback: its
+    // weights replace w in LDS.
+    if (sel) {
+        ItemRaw<DT> raw;
+        load_item<DT>(rowT, rowD, resid, aligned, r, P.V, raw);
+#pragma unroll
+        for (int k = 0; k < kRuns; ++k) {
+            float w[kRun], p[kRun];
+            item_run_weights<DT, TOPP>(P, rp, resid, invT, invD, raw, r, k, w, p);
+#pragma unroll
+            for (int i = 0; i < kRun; ++i) s_rw[k][i][tid] = p[i];
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    double xs[kRuns], wi[kRuns];
     int lastpos = -1;
 #pragma unroll
-    for (int i = 0; i < kRun; ++i) {
-        const float v = sel ? p[i] : w[i];
-        w[i] = v;
-        xs += static_cast<double>(v);
-        if (v > 0.f) lastpos = static_cast<int>(id0 + i);
+    for (int k = 0; k < kRuns; ++k) {
+        float v[kRun];
+#pragma unroll
+        for (int i = 0; i < kRun; ++i) v[i] = s_rw[k][i][tid];
+        xs[k] = static_cast<double>(run_sum(v));
+        const int64_t id0 = item_run_id0(r, k);
+#pragma unroll
+        for (int i = 0; i < kRun; ++i)
+            if (v[i] > 0.f) lastpos = static_cast<int>(id0 + i);
+        wi[k] = wave_scan_dpp(xs[k]);
+        if (lane == 63) s_wt[k][wv] = wi[k];
     }
-    const double wi = wave_incl_scan(xs, lane);
-    if (lane == 63) s_wtot[wv] = wi;
-    const int wl = wave_max_int(lastpos);
+    const int wl = wave_max_int_dpp(lastpos);
     if (lane == 0) s_lastpos[wv] = wl;
     __syncthreads();
-    double off = spre;
-    for (int k = 0; k < wv; ++k) off += s_wtot[k];
-    const double incl = off + wi;
-    const unsigned long long hitm = __ballot(xs > 0.0 && incl > t);
-    if (lane == 0) s_hit[wv] = hitm ? (wv * 64 + __ffsll(static_cast<long long>(hitm)) - 1) : 0x7FFFFFFF;
-    __syncthreads();
-    int fh = 0x7FFFFFFF, lp = -1;
-    for (int k = 0; k < kRWaves; ++k) {
-        fh = min(fh, s_hit[k]);
-        lp = max(lp, s_lastpos[k]);
+    double base = s_pre;
+#pragma unroll
+    for (int k = 0; k < kRuns; ++k) {
+        double off = base;
+        for (int w2 = 0; w2 < wv; ++w2) off += s_wt[k][w2];
+        const double incl = off + wi[k];
+        const unsigned long long hm = __ballot(xs[k] > 0.0 && incl > t);
+        if (lane == 0) s_hit[k][wv] = hm ? (wv * 64 + __ffsll(static_cast<long long>(hm)) - 1) : 0x7FFFFFFF;
+        for (int w2 = 0; w2 < kWaves; ++w2) base += s_wt[k][w2];
     }
-    if (fh == 0x7FFFFFFF) {
-        // rounding put t past the step's last run: the last positive weight
+    __syncthreads();
+    int hk = -1, ht = 0x7FFFFFFF, lp = -1;
+    for (int k = kRuns - 1; k >= 0; --k) {
+        int h = 0x7FFFFFFF;
+        for (int w2 = 0; w2 < kWaves; ++w2) h = min(h, s_hit[k][w2]);
+        if (h != 0x7FFFFFFF) {
+            hk = k;
+            ht = h;
+        }
+    }
+    for (int w2 = 0; w2 < kWaves; ++w2) lp = max(lp, s_lastpos[w2]);
+    double* pr = P.probe_row ? P.probe_row + static_cast<size_t>(b) * 4 : nullptr;
+    int32_t* outp = P.out_tokens + static_cast<size_t>(b) * (P.K + 1) + rn;
+    if (hk < 0) {
+        // rounding put t past the item's last positive weight
         if (tid == 0) {
-            P.out_tokens[static_cast<size_t>(b) * (P.K + 1) + rn] = lp >= 0 ? lp : 0;
-            if (P.probe_row) {
-                P.probe_row[static_cast<size_t>(b) * 4 + 0] = s_Z;
-                P.probe_row[static_cast<size_t>(b) * 4 + 1] = t;
+            *outp = lp >= 0 ? lp : 0;
+            if (pr) {
+                pr[0] = s_Z;
+                pr[1] = t;
             }
         }
         return;
     }
-    if (tid == fh) {
-        double run = incl - xs;
-        int y = -1, lastw = -1;
+    if (tid == ht) {
+        // this thread's run hk holds t: walk its weights in id order from
+        // the exclusive prefix the scan formed
+        double xk = xs[0], wk = wi[0];
 #pragma unroll
-        for (int i = 0; i < kRun; ++i) {
-            if (w[i] > 0.f) {
-                lastw = static_cast<int>(id0 + i);
-                if (y < 0 && run + static_cast<double>(w[i]) > t) y = lastw;
+        for (int k = 1; k < kRuns; ++k)
+            if (k == hk) {
+                xk = xs[k];
+                wk = wi[k];
             }
-            run += static_cast<double>(w[i]);
+        double off = s_pre;
+        for (int k = 0; k < hk; ++k)
+            for (int w2 = 0; w2 < kWaves; ++w2) off += s_wt[k][w2];
+        for (int w2 = 0; w2 < wv; ++w2) off += s_wt[hk][w2];
+        double run = off + wk - xk;
+        const int64_t id0 = item_run_id0(r, hk);
+        int y = -1, lastw = -1;
+        for (int i = 0; i < kRun; ++i) {
+            const float v = s_rw[hk][i][tid];
+            if (v > 0.f) {
+                lastw = static_cast<int>(id0 + i);
+                if (y < 0 && run + static_cast<double>(v) > t) y = lastw;
+            }
+            run += static_cast<double>(v);
         }
-        P.out_tokens[static_cast<size_t>(b) * (P.K + 1) + rn] = y >= 0 ? y : lastw;
-        if (P.probe_row) {
-            P.probe_row[static_cast<size_t>(b) * 4 + 0] = s_Z;
-            P.probe_row[static_cast<size_t>(b) * 4 + 1] = t;
+        *outp = y >= 0 ? y : lastw;
+        if (pr) {
+            pr[0] = s_Z;
+            pr[1] = t;
         }
+    }
+}
+
+// Row pass: one workgroup per (b, item).  With top-p the decision was made by
+// the nucleus pass; without, every item makes it from the statistics records
+// (the statistics kernel has finished, so no record is waited for).
+template <int DT, bool TOPP>
+__global__ __launch_bounds__(kThreads) void k_rows(Params P) {
+    __shared__ RowShared R;
+    __shared__ RowParam s_rp;
+    const int b = blockIdx.x / P.nq;
+    const int r = blockIdx.x - b * P.nq;
+    if (TOPP) {
+        const RowParam rp = P.rowp[b];
+        resample_item<DT, true>(P, b, r, rp);
+    } else {
+        bool rowok;
+        const int Le = row_len(P, b, rowok);
+        const int x = lane_token(P, b, Le);
+        fill_row_from_partials(P, b, Le, R);
+        if ((threadIdx.x >> 6) == 0) {
+            RowParam rp;
+            decide_row<false>(P, b, Le, rowok, R, r == 0, x, rp);
+            if ((threadIdx.x & 63) == 0) s_rp = rp;
+        }
+        __syncthreads();
+        const RowParam rp = s_rp;
+        resample_item<DT, false>(P, b, r, rp);
     }
 }
 
@@ -1370,20 +1611,14 @@ static void launch(Kern k, unsigned grid, unsigned block, hipStream_t s, const L
     hipExtLaunchKernelGGL(k, dim3(grid), dim3(block), 0, s, ev.start, ev.stop, 0, p);
 }
 
-template <int DT, int U>
-static void launch_stats_t(const Params& p, bool topp, hipStream_t s, const LaunchEvents& ev) {
+hipError_t launch_stats(const Params& p, int dtype, int unroll, hipStream_t s, const LaunchEvents& ev) {
     const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(p.B) * p.nslot * p.nch);
-    if (topp) launch(k_stats<DT, U, true>, grid, kThreads, s, ev, p);
-    else launch(k_stats<DT, U, false>, grid, kThreads, s, ev, p);
-}
-
-hipError_t launch_stats(const Params& p, int dtype, int unroll, bool topp, hipStream_t s, const LaunchEvents& ev) {
     if (dtype == DT_BF16) {
-        if (unroll == 8) launch_stats_t<DT_BF16, 8>(p, topp, s, ev);
-        else launch_stats_t<DT_BF16, 4>(p, topp, s, ev);
+        if (unroll == 8) launch(k_stats<DT_BF16, 8>, grid, kThreads, s, ev, p);
+        else launch(k_stats<DT_BF16, 4>, grid, kThreads, s, ev, p);
     } else {
-        if (unroll == 8) launch_stats_t<DT_F32, 8>(p, topp, s, ev);
-        else launch_stats_t<DT_F32, 4>(p, topp, s, ev);
+        if (unroll == 8) launch(k_stats<DT_F32, 8>, grid, kThreads, s, ev, p);
+        else launch(k_stats<DT_F32, 4>, grid, kThreads, s, ev, p);
     }
     return hipGetLastError();
 }
@@ -1395,14 +1630,14 @@ hipError_t launch_topp(const Params& p, int dtype, hipStream_t s, const LaunchEv
     return hipGetLastError();
 }
 
-hipError_t launch_resample(const Params& p, int dtype, bool topp, hipStream_t s, const LaunchEvents& ev) {
-    const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(p.B) * p.res_split);
+hipError_t launch_rows(const Params& p, int dtype, bool topp, hipStream_t s, const LaunchEvents& ev) {
+    const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(p.B) * p.nq);
     if (dtype == DT_BF16) {
-        if (topp) launch(k_resample<DT_BF16, true>, grid, kRThreads, s, ev, p);
-        else launch(k_resample<DT_BF16, false>, grid, kRThreads, s, ev, p);
+        if (topp) launch(k_rows<DT_BF16, true>, grid, kThreads, s, ev, p);
+        else launch(k_rows<DT_BF16, false>, grid, kThreads, s, ev, p);
     } else {
-        if (topp) launch(k_resample<DT_F32, true>, grid, kRThreads, s, ev, p);
-        else launch(k_resample<DT_F32, false>, grid, kRThreads, s, ev, p);
+        if (topp) launch(k_rows<DT_F32, true>, grid, kThreads, s, ev, p);
+        else launch(k_rows<DT_F32, false>, grid, kThreads, s, ev, p);
     }
     return hipGetLastError();
 }

@@ -1266,21 +1266,21 @@ __device__ __forceinline__ void load_item(const uint8_t* rowT, const uint8_t* ro
         }
     }
 }
-// Weights of run k: w = max(0, p' - q') (or p' for the bonus) and p = p'.
-template <int DT, bool TOPP>
-__device__ __forceinline__ void item_run_weights(const Params& P, const RowParam& rp, bool resid, float invT, float invD,
-                                                 const ItemRaw<DT>& raw, int r, int k, float* w, float* p) {
+// Weights of run k of item r: w = max(0, p' - q') (or p' for the bonus) and
+// p = p'.  `interior`: the whole item lies inside the row (nothing to mask).
+template <int DT, bool TOPP, bool RESID>
+__device__ __forceinline__ void item_run(const Params& P, const RowParam& rp, float invT, float invD,
+                                         const ItemRaw<DT>& raw, int r, int k, bool interior, float* w, float* p) {
     const int64_t id0 = item_run_id0(r, k);
     float lt[kRun], ld[kRun];
-    if (static_cast<int64_t>(r + 1) * kItemIds <= P.V) {
-        // the whole item lies inside the row (uniform): nothing to mask
+    if (interior) {
         unpack_run<DT>(raw.t[k], lt);
-        if (resid) unpack_run<DT>(raw.d[k], ld);
+        if (RESID) unpack_run<DT>(raw.d[k], ld);
     } else {
         unpack_masked<DT>(raw.t[k], id0, P.V, lt);
-        if (resid) unpack_masked<DT>(raw.d[k], id0, P.V, ld);
+        if (RESID) unpack_masked<DT>(raw.d[k], id0, P.V, ld);
     }
-    run_weights<TOPP>(lt, ld, resid, id0, rp, P.c_hi, P.c_lo, invT, invD, w, p);
+    run_weights<TOPP>(lt, ld, RESID, id0, rp, P.c_hi, P.c_lo, invT, invD, w, p);
 }
 __device__ __forceinline__ float run_sum(const float* v) {
     float a = (v[0] + v[1]) + (v[2] + v[3]);
@@ -1289,50 +1289,39 @@ __device__ __forceinline__ float run_sum(const float* v) {
 }
 static_assert(kRun == 8, "run_sum sums 8 values");
 
-// The resample part of batch row b for item r, given the row's decision rp
-// (the same in every item of the row).  Every thread must call it.
-template <int DT, bool TOPP>
-__device__ void resample_item(const Params& P, int b, int r, const RowParam& rp_in) {
+// The resample part of batch row b for item r, given the row's decision (the
+// same in every item of the row) with n = rn and the mode's RESID.  Every
+// thread must call it.
+template <int DT, bool TOPP, bool RESID>
+__device__ void resample_body(const Params& P, int b, int r, const RowParam& rp, int rn) {
     __shared__ double s_w[kWaves], s_p[kWaves];
     __shared__ double s_wt[kRuns][kWaves];
-    __shared__ int s_hit[kRuns][kWaves], s_lastpos[kWaves];
+    __shared__ int s_lastpos[kWaves];
     __shared__ int s_sel, s_item, s_ok;
     __shared__ double s_pre, s_Z, s_t;
-    __shared__ float s_rw[kRuns][kRun][kThreads];  // this item's weights
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    // the row's mode and n are the same for every lane: keep them scalar
-    const int mode = __builtin_amdgcn_readfirstlane(rp_in.mode);
-    const int rn = __builtin_amdgcn_readfirstlane(rp_in.n);
-    if ((mode != MODE_RESID && mode != MODE_BONUS) || rn < 0 || rn > P.K) {
-        // an invalid row: the decision wrote its outputs; no item waits
-        if (r == 0 && tid == 0 && P.probe_row) {
-            P.probe_row[static_cast<size_t>(b) * 4 + 0] = nan64();
-            P.probe_row[static_cast<size_t>(b) * 4 + 1] = nan64();
-        }
-        return;
-    }
-    const RowParam& rp = rp_in;
-    const bool resid = mode == MODE_RESID;
     const uint8_t* rowT = row_ptr<DT>(P, true, b, rn);
-    const uint8_t* rowD = resid ? row_ptr<DT>(P, false, b, rn) : rowT;
+    const uint8_t* rowD = RESID ? row_ptr<DT>(P, false, b, rn) : rowT;
     const bool aligned = ((reinterpret_cast<uintptr_t>(rowT) & 15) == 0) && ((reinterpret_cast<uintptr_t>(rowD) & 15) == 0);
     const float invT = static_cast<float>(1.0 / rp.keptT);
-    const float invD = resid ? static_cast<float>(1.0 / rp.keptD) : 0.f;
+    const float invD = RESID ? static_cast<float>(1.0 / rp.keptD) : 0.f;
+    const bool interior = static_cast<int64_t>(r + 1) * kItemIds <= P.V;
     const int nq = P.nq;
     uint64_t* qrec = P.qrec + static_cast<size_t>(b) * nq * kRecWords;
 
-    // 1. the item's weights (into LDS) and masses
+    // 1. the item's weights (kept in registers) and masses
+    float w[kRuns][kRun];
+    float xs[kRuns];
     double ws = 0.0, ps = 0.0;
     {
         ItemRaw<DT> raw;
-        load_item<DT>(rowT, rowD, resid, aligned, r, P.V, raw);
+        load_item<DT>(rowT, rowD, RESID, aligned, r, P.V, raw);
 #pragma unroll
         for (int k = 0; k < kRuns; ++k) {
-            float w[kRun], p[kRun];
-            item_run_weights<DT, TOPP>(P, rp, resid, invT, invD, raw, r, k, w, p);
-#pragma unroll
-            for (int i = 0; i < kRun; ++i) s_rw[k][i][tid] = w[i];
-            ws += static_cast<double>(run_sum(w));
+            float p[kRun];
+            item_run<DT, TOPP, RESID>(P, rp, invT, invD, raw, r, k, interior, w[k], p);
+            xs[k] = run_sum(w[k]);
+            ws += static_cast<double>(xs[k]);
             ps += static_cast<double>(run_sum(p));
             // one run at a time: interleaving the runs' exponentials would
             // multiply the registers live here
@@ -1438,62 +1427,52 @@ __device__ void resample_item(const Params& P, int b, int r, const RowParam& rp_
         return;
     }
     if (s_item != r) return;
-    const int sel = s_sel;
-    const double t = s_t;
 
-    // 4. this item holds t: its weights in id order, run-major, then thread,
-    // then id.  Drawing from p' (sel) is the rare rounding fallback: its
-    // weights replace w in LDS.
-    if (sel) {
+    // 4. this item holds t.  Id order is run-major, then thread, then id.
+    // Drawing from p' (sel) is the rare rounding fallback: its weights
+    // replace w.
+    const double t = s_t;
+    if (s_sel) {
         ItemRaw<DT> raw;
-        load_item<DT>(rowT, rowD, resid, aligned, r, P.V, raw);
+        load_item<DT>(rowT, rowD, RESID, aligned, r, P.V, raw);
 #pragma unroll
         for (int k = 0; k < kRuns; ++k) {
-            float w[kRun], p[kRun];
-            item_run_weights<DT, TOPP>(P, rp, resid, invT, invD, raw, r, k, w, p);
-#pragma unroll
-            for (int i = 0; i < kRun; ++i) s_rw[k][i][tid] = p[i];
+            float wk[kRun];
+            item_run<DT, TOPP, RESID>(P, rp, invT, invD, raw, r, k, interior, wk, w[k]);
+            xs[k] = run_sum(w[k]);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    double xs[kRuns], wi[kRuns];
+    double wi[kRuns];
     int lastpos = -1;
 #pragma unroll
     for (int k = 0; k < kRuns; ++k) {
-        float v[kRun];
-#pragma unroll
-        for (int i = 0; i < kRun; ++i) v[i] = s_rw[k][i][tid];
-        xs[k] = static_cast<double>(run_sum(v));
+        wi[k] = wave_scan_dpp(static_cast<double>(xs[k]));
+        if (lane == 63) s_wt[k][wv] = wi[k];
         const int64_t id0 = item_run_id0(r, k);
 #pragma unroll
         for (int i = 0; i < kRun; ++i)
-            if (v[i] > 0.f) lastpos = static_cast<int>(id0 + i);
-        wi[k] = wave_scan_dpp(xs[k]);
-        if (lane == 63) s_wt[k][wv] = wi[k];
+            if (w[k][i] > 0.f) lastpos = static_cast<int>(id0 + i);
     }
-    const int wl = wave_max_int_dpp(lastpos);
-    if (lane == 0) s_lastpos[wv] = wl;
+    lastpos = wave_max_int_dpp(lastpos);
+    if (lane == 0) s_lastpos[wv] = lastpos;
     __syncthreads();
-    double base = s_pre;
+    // the (run, wave) holding t, from the 16 totals in id order
+    double base = s_pre, hoff = 0.0;
+    int hk = -1, hw = -1, lp = -1;
 #pragma unroll
-    for (int k = 0; k < kRuns; ++k) {
-        double off = base;
-        for (int w2 = 0; w2 < wv; ++w2) off += s_wt[k][w2];
-        const double incl = off + wi[k];
-        const unsigned long long hm = __ballot(xs[k] > 0.0 && incl > t);
-        if (lane == 0) s_hit[k][wv] = hm ? (wv * 64 + __ffsll(static_cast<long long>(hm)) - 1) : 0x7FFFFFFF;
-        for (int w2 = 0; w2 < kWaves; ++w2) base += s_wt[k][w2];
-    }
-    __syncthreads();
-    int hk = -1, ht = 0x7FFFFFFF, lp = -1;
-    for (int k = kRuns - 1; k >= 0; --k) {
-        int h = 0x7FFFFFFF;
-        for (int w2 = 0; w2 < kWaves; ++w2) h = min(h, s_hit[k][w2]);
-        if (h != 0x7FFFFFFF) {
-            hk = k;
-            ht = h;
+    for (int k = 0; k < kRuns; ++k)
+#pragma unroll
+        for (int w2 = 0; w2 < kWaves; ++w2) {
+            const double tot = s_wt[k][w2];
+            if (hk < 0 && tot > 0.0 && base + tot > t) {
+                hk = k;
+                hw = w2;
+                hoff = base;
+            }
+            base += tot;
         }
-    }
+#pragma unroll
     for (int w2 = 0; w2 < kWaves; ++w2) lp = max(lp, s_lastpos[w2]);
     double* pr = P.probe_row ? P.probe_row + static_cast<size_t>(b) * 4 : nullptr;
     int32_t* outp = P.out_tokens + static_cast<size_t>(b) * (P.K + 1) + rn;
@@ -1508,37 +1487,56 @@ __device__ void resample_item(const Params& P, int b, int r, const RowParam& rp_
         }
         return;
     }
-    if (tid == ht) {
-        // this thread's run hk holds t: walk its weights in id order from
-        // the exclusive prefix the scan formed
-        double xk = xs[0], wk = wi[0];
+    if (wv != hw) return;
+    // wave hw: the first lane of run hk whose inclusive prefix passes t
+    float v[kRun];
+    double myx = 0.0, myw = 0.0;
 #pragma unroll
-        for (int k = 1; k < kRuns; ++k)
-            if (k == hk) {
-                xk = xs[k];
-                wk = wi[k];
-            }
-        double off = s_pre;
-        for (int k = 0; k < hk; ++k)
-            for (int w2 = 0; w2 < kWaves; ++w2) off += s_wt[k][w2];
-        for (int w2 = 0; w2 < wv; ++w2) off += s_wt[hk][w2];
-        double run = off + wk - xk;
+    for (int k = 0; k < kRuns; ++k)
+        if (k == hk) {
+#pragma unroll
+            for (int i = 0; i < kRun; ++i) v[i] = w[k][i];
+            myx = static_cast<double>(xs[k]);
+            myw = wi[k];
+        }
+    const double incl = hoff + myw;
+    const unsigned long long hm = __ballot(myx > 0.0 && incl > t);
+    const int hl = hm ? __ffsll(static_cast<long long>(hm)) - 1 : 63;
+    if (lane == hl) {
+        double run = incl - myx;  // exclusive prefix of this thread's run
         const int64_t id0 = item_run_id0(r, hk);
         int y = -1, lastw = -1;
+#pragma unroll
         for (int i = 0; i < kRun; ++i) {
-            const float v = s_rw[hk][i][tid];
-            if (v > 0.f) {
+            if (v[i] > 0.f) {
                 lastw = static_cast<int>(id0 + i);
-                if (y < 0 && run + static_cast<double>(v) > t) y = lastw;
+                if (y < 0 && run + static_cast<double>(v[i]) > t) y = lastw;
             }
-            run += static_cast<double>(v);
+            run += static_cast<double>(v[i]);
         }
-        *outp = y >= 0 ? y : lastw;
+        *outp = y >= 0 ? y : (lastw >= 0 ? lastw : (lp >= 0 ? lp : 0));
         if (pr) {
             pr[0] = s_Z;
             pr[1] = t;
         }
     }
+}
+
+template <int DT, bool TOPP>
+__device__ __forceinline__ void resample_item(const Params& P, int b, int r, const RowParam& rp) {
+    // the row's mode and n are the same for every lane: keep them scalar
+    const int mode = __builtin_amdgcn_readfirstlane(rp.mode);
+    const int rn = __builtin_amdgcn_readfirstlane(rp.n);
+    if ((mode != MODE_RESID && mode != MODE_BONUS) || rn < 0 || rn > P.K) {
+        // an invalid row: the decision wrote its outputs; no item waits
+        if (r == 0 && threadIdx.x == 0 && P.probe_row) {
+            P.probe_row[static_cast<size_t>(b) * 4 + 0] = nan64();
+            P.probe_row[static_cast<size_t>(b) * 4 + 1] = nan64();
+        }
+        return;
+    }
+    if (mode == MODE_RESID) resample_body<DT, TOPP, true>(P, b, r, rp, rn);
+    else resample_body<DT, TOPP, false>(P, b, r, rp, rn);
 }
 
 // Row pass: one workgroup per (b, item).  With top-p the decision was made by

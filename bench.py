@@ -1,14 +1,15 @@
 """Benchmark of the batched speculative-sampling verify step on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--calibrate]
 
 Workload: B=64 rows, K=5 drafted tokens, V=128256 (Llama-3 vocabulary),
 bfloat16 logits, temperature 0.7, top-p off -- the batched workload of the
 seeded generator.  Three distinct input sets (3 x 180.6 MB, more than the
 256 MB Infinity Cache) are resident in HBM and rotated call by call, so no
 call finds its inputs in the cache.  A step is one spec_verify call: the
-statistics pass over every needed logit row, the accept scan and the
-residual/bonus resample.
+statistics pass over every needed logit row (k_stats), then the row pass
+(k_rows): acceptance decision, residual or bonus masses, inverse-CDF draw.
 
 Prints one JSON line.  `value` is verified draft positions per second; the
 roofline object prices the dominant kernel (the statistics pass) against
@@ -208,11 +209,11 @@ def main():
     binding.profile_enable(False)
     prof = binding.profile_read()
     stats_ms, stats_n = prof["stats"]
-    res_ms, res_n = prof["resample"]
+    res_ms, res_n = prof["rows"]
     stats_avg_s = stats_ms / 1e3 / max(stats_n, 1)
     achieved = logical / stats_avg_s / 1e9
-    print(f"[bench] stats kernel {stats_ms / max(stats_n, 1) * 1e3:.2f} us, resample "
-          f"({stats_n} launches)", file=sys.stderr, flush=True)
+    print(f"[bench] statistics kernel {stats_ms / max(stats_n, 1) * 1e3:.2f} us, row kernel "
+          f"{res_ms / max(res_n, 1) * 1e3:.2f} us ({stats_n} launches)", file=sys.stderr, flush=True)
 
     traffic = stored_traffic()
     roofline = {
@@ -222,9 +223,9 @@ def main():
         "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4),
         "traffic": traffic,
-        "kernel": "k_stats (statistics pass + accept decision)",
+        "kernel": "k_stats (statistics pass: every needed logit row read once)",
         "kernel_us": round(stats_avg_s * 1e6, 3),
-        "other_kernels_us": {"resample": round(res_ms / max(res_n, 1) * 1e3, 3)},
+        "other_kernels_us": {"k_rows": round(res_ms / max(res_n, 1) * 1e3, 3)},
         "algorithmic_bytes_per_launch": logical,
     }
 

@@ -37,7 +37,10 @@
  * The library owns a small scratch buffer per (device, stream), grown on first
  * use and kept until spec_verify_release().  Calls are asynchronous on the
  * given stream and never synchronise the host (except a first call on a
- * stream, or a call that outgrows the cached scratch, which allocates).
+ * stream, or a call that outgrows the cached scratch, which allocates).  A
+ * call that does not allocate may be captured into a HIP graph: each kernel
+ * of a call rewrites, before any reader needs it, all scratch that later
+ * kernels of the same call read, so replays are independent.
  * Concurrent calls on the same stream from several host threads are not
  * supported; calls on different streams may run concurrently.
  */
@@ -145,12 +148,13 @@ void spec_verify_release(void);
 /* Returns SPECVERIFY_ABI_VERSION. */
 int spec_verify_abi_version(void);
 
-/* Kernel timing for measurement.  While enabled, every launch is bracketed by
- * HIP events on its stream.  spec_verify_profile_read synchronises those
- * events and writes, for each of the n kernel kinds (0 statistics pass,
- * 1 nucleus selection, 2 resample), the summed duration in milliseconds and
- * the number of launches since the last read; it returns the number of kinds
- * written.  Host arrays ms[n], launches[n]. */
+/* Kernel timing for measurement.  While enabled, every launch carries a pair
+ * of HIP events on its stream, attached to the kernel's dispatch.
+ * spec_verify_profile_read synchronises those events and writes, for each of
+ * the n kernel kinds (0 statistics pass, 1 nucleus selection, 2 row pass:
+ * the decision when top-p is off, and the resample), the summed duration in
+ * milliseconds and the number of launches since the last read; it returns
+ * the number of kinds written.  Host arrays ms[n], launches[n]. */
 int spec_verify_profile_enable(int enable);
 int spec_verify_profile_read(double* ms, int64_t* launches, int n);
 

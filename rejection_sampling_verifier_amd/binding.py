@@ -18,7 +18,7 @@ SV_F32, SV_BF16 = 0, 1
 PROBE_POS, PROBE_ROW = 8, 4
 STATUS = {0: "SV_OK", -1: "SV_EINVAL", -2: "SV_ESHAPE", -3: "SV_EDTYPE", -4: "SV_EHIP", -5: "SV_ENOMEM",
           -6: "SV_EALIGN"}
-KERNEL_KINDS = ("stats", "topp", "resample")
+KERNEL_KINDS = ("stats", "topp", "rows")
 
 EXPORTS = ("spec_verify", "spec_verify_probe", "spec_verify_strerror", "spec_verify_release",
            "spec_verify_abi_version", "spec_verify_profile_enable", "spec_verify_profile_read",

@@ -214,3 +214,42 @@ def test_stream_argument_and_plain_entry_point():
     ref = run_gpu(inp, probe=True, tensors=(t, d, x, dl))
     np.testing.assert_array_equal(tok.cpu().numpy(), ref[0])
     np.testing.assert_array_equal(n.cpu().numpy(), ref[1])
+
+
+@pytest.mark.parametrize("top_p", [1.0, 0.6])
+def test_graph_capture_replays(top_p):
+    """One call captured into a HIP graph and replayed on new inputs copied
+    into the captured buffers gives, replay after replay, the outputs of the
+    same call made eagerly (the replays reuse the captured record tag, so
+    this also checks that every call leaves the scratch ready for the next)."""
+    cfg = 4 if top_p < 1.0 else 2
+    sets = [W.make_inputs(cfg, s, B=12, V=9000) for s in range(3)]
+    T = float(sets[0].temperature)
+    seed = 0x5EEDF00D
+    stream = torch.cuda.Stream()
+    t, d, x, _ = to_device(sets[0])
+    out_t = torch.empty((t.shape[0], t.shape[1]), dtype=torch.int32, device="cuda")
+    out_n = torch.empty((t.shape[0],), dtype=torch.int32, device="cuda")
+    with torch.cuda.stream(stream):
+        # first call on this stream allocates the scratch: outside capture
+        binding.verify(t, d, x, None, T, top_p, seed, stream=stream, out_tokens=out_t, out_n_accepted=out_n)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        binding.verify(t, d, x, None, T, top_p, seed, stream=stream, out_tokens=out_t, out_n_accepted=out_n)
+    torch.cuda.synchronize()
+    for rep in range(6):
+        inp = sets[rep % 3]
+        nt, nd, nx, _ = to_device(inp)
+        t.copy_(nt)
+        d.copy_(nd)
+        x.copy_(nx)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        got_t, got_n = out_t.cpu().numpy(), out_n.cpu().numpy()
+        ref_t, ref_n = binding.verify(nt, nd, nx, None, T, top_p, seed)
+        torch.cuda.synchronize()
+        say(f"[graph] top_p={top_p} replay {rep}: accepted {got_n.tolist()}")
+        np.testing.assert_array_equal(got_n, ref_n.cpu().numpy(), err_msg=f"replay {rep}")
+        np.testing.assert_array_equal(got_t, ref_t.cpu().numpy(), err_msg=f"replay {rep}")

@@ -217,8 +217,16 @@ int verify_impl(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_t
     const int cv = sv::kThreads * unroll;
     const int64_t nch64 = (nvec_max + cv - 1) / cv;
     const int nch = static_cast<int>(nch64);
-    // resample: items of kItemIds ids
-    const int nq = (V + sv::kItemIds - 1) / sv::kItemIds;
+    // row pass: items of runs*kRunIds ids; one-run items when the batch would
+    // otherwise give fewer than two workgroups per CU
+    int runs = sv::kRunsMax;
+    {
+        const int64_t big = static_cast<int64_t>(B) * ((V + runs * sv::kRunIds - 1) / (runs * sv::kRunIds));
+        if (big < 2ll * device_cus()) runs = 1;
+        const int forced = env_int("SPECVERIFY_ROW_RUNS", 0);
+        if (forced == 1 || forced == 2 || forced == sv::kRunsMax) runs = forced;
+    }
+    const int nq = (V + runs * sv::kRunIds - 1) / (runs * sv::kRunIds);
     const int64_t per_row = static_cast<int64_t>(nslot) * nch + nq;
     if (static_cast<int64_t>(B) * per_row >= (1ll << 31)) return SV_ESHAPE;
     // the statistics kernel clears the row pass's records, a few words each
@@ -253,6 +261,7 @@ int verify_impl(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_t
     p.nch = nch;
     p.cv = cv;
     p.nq = nq;
+    p.runs = runs;
     p.tag = next_tag();
     // c = c_hi + c_lo with c_hi <= c rounded toward zero, so c_lo > 0.
     float c_hi = static_cast<float>(c);

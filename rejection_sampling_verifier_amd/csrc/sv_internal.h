@@ -14,8 +14,8 @@ constexpr int kMaxSlots = 2 * kMaxK + 1;
 constexpr int kStatsUnroll = 8;      // default 16-byte vectors in flight per lane per step
 constexpr int kResTile = 8;          // consecutive ids per thread in the id-ordered scans
 constexpr int kRun = 8;              // ids per thread per run of a resample item
-constexpr int kRuns = 4;             // runs per thread per resample item
-constexpr int kItemIds = kThreads * kRun * kRuns;  // ids per resample item (8192)
+constexpr int kRunsMax = 4;          // runs per thread per resample item, large batches
+constexpr int kRunIds = kThreads * kRun;  // ids per run of an item (2048)
 constexpr int kRecWords = 4;         // 64-bit words per tagged record
 
 enum DType : int { DT_F32 = 0, DT_BF16 = 1 };
@@ -74,7 +74,8 @@ struct Params {
     double* probe_row;            // [B, 4] or null
     int B, K, V, nslot;
     int nch, cv;                  // statistics pass: chunks per logit row, 16-byte vectors per chunk
-    int nq;                       // resample items per batch row (kItemIds ids each)
+    int nq;                       // resample items per batch row (runs*kRunIds ids each)
+    int runs;                     // runs per resample item: 1, 2 or kRunsMax
     uint32_t tag;                 // this call's record tag (never 0)
     float c_hi, c_lo;             // c = log2(e)/T = c_hi + c_lo, c_lo > 0
     double c64;                   // (double)c_hi + (double)c_lo

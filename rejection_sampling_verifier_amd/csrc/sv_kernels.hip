@@ -733,6 +733,28 @@ __device__ __forceinline__ int block_min_int(int v) {
     __syncthreads();
     return r;
 }
+// Unsigned minimum, maximum and sum over the workgroup (every thread calls).
+template <typename Op>
+__device__ __forceinline__ uint32_t block_reduce_u32(uint32_t v, Op op) {
+    __shared__ uint32_t ws[kWaves];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = op(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), o, 64)));
+    if ((threadIdx.x & 63) == 0) ws[threadIdx.x >> 6] = v;
+    __syncthreads();
+    uint32_t r = ws[0];
+    for (int k = 1; k < kWaves; ++k) r = op(r, ws[k]);
+    __syncthreads();
+    return r;
+}
+__device__ __forceinline__ uint32_t block_min_u32(uint32_t v) {
+    return block_reduce_u32(v, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+}
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v) {
+    return block_reduce_u32(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+__device__ __forceinline__ uint32_t block_sum_u32(uint32_t v) {
+    return block_reduce_u32(v, [](uint32_t a, uint32_t b) { return a + b; });
+}
 __device__ __forceinline__ int block_max_int(int v) {
     __shared__ int ws[kWaves];
     v = wave_max_int(v);
@@ -791,16 +813,33 @@ struct SelShared {
     int r_keepall;
 };
 
+// Calls fn(logit, id) for every element of a row, the workgroup's threads
+// taking 16-byte vectors in turn; kSweep vectors per thread are loaded
+// before any is used, so a pass over a row costs few memory round trips.
+// Ids outside [0, V) (edges of unaligned rows) come with -inf.
+constexpr int kSweep = 8;
 template <int DT, typename F>
 __device__ __forceinline__ void for_each_vec(const uint8_t* row, int V, F&& fn) {
     constexpr int VE = Fmt<DT>::VE;
     const RowGrid g = row_grid<DT>(row, V);
-    for (int64_t k = threadIdx.x; k < g.nvec; k += kThreads) {
-        float f[VE];
-        unpack<DT>(g.vp[k], f);
-        if (k == 0 || k == g.nvec - 1) mask_edge<DT>(f, k, g.head, V);
+    constexpr int64_t STEP = static_cast<int64_t>(kThreads) * kSweep;
+    for (int64_t k0 = 0; k0 < g.nvec; k0 += STEP) {
+        uint4 raw[kSweep];
+        const uint32_t ni = Fmt<DT>::NEG_INF_WORD;
 #pragma unroll
-        for (int i = 0; i < VE; ++i) fn(f[i], k * VE + i - g.head);
+        for (int u = 0; u < kSweep; ++u) {
+            const int64_t k = k0 + u * kThreads + threadIdx.x;
+            raw[u] = k < g.nvec ? gload16(g.vp + k) : make_uint4(ni, ni, ni, ni);
+        }
+#pragma unroll
+        for (int u = 0; u < kSweep; ++u) {
+            const int64_t k = k0 + u * kThreads + threadIdx.x;
+            float f[VE];
+            unpack<DT>(raw[u], f);
+            if (k == 0 || k >= g.nvec - 1) mask_edge<DT>(f, k, g.head, V);
+#pragma unroll
+            for (int i = 0; i < VE; ++i) fn(f[i], k * VE + i - g.head);
+        }
     }
 }
 
@@ -812,28 +851,25 @@ __device__ void select_nucleus(const Params& P, const uint8_t* row, float O, dou
     const float c_hi = P.c_hi, c_lo = P.c_lo;
     const double Tm = static_cast<double>(P.top_p) * S;
 
-    for (int i = tid; i < kGapBins; i += kThreads) {
-        sh.mass[i] = 0.0;
-        sh.cnt[i] = 0u;
-        sh.kmin[i] = 0xFFFFFFFFu;
-        sh.kmax[i] = 0u;
+    for (int i = tid; i < kGapBins; i += kThreads) sh.mass[i] = 0.0;
+    if (tid == 0) {
+        sh.r_keepall = 0;
+        sh.nlist = 0u;
     }
-    if (tid == 0) sh.r_keepall = 0;
     __syncthreads();
-    // Pass A: gap histogram.
+    // Pass A: gap histogram (mass only; a bin is a monotone function of the
+    // logit, so its key interval and count are found again in pass B), and
+    // the smallest key within 16 bits of the offset.
+    uint32_t kin = 0xFFFFFFFFu;
     for_each_vec<DT>(row, V, [&](float l, int64_t id) {
         const float a = fmaf(l, c_lo, fmaf(l, c_hi, -O));
         if (a > -16.f && id >= 0 && id < V) {
-            const float e = exp2f(a);
             const int bin = max(0, static_cast<int>(floorf(-a * kGapPerBit)));
-            const uint32_t key = order_key(l);
-            atomicAdd(&sh.mass[bin], static_cast<double>(e));
-            atomicAdd(&sh.cnt[bin], 1u);
-            atomicMin(&sh.kmin[bin], key);
-            atomicMax(&sh.kmax[bin], key);
+            atomicAdd(&sh.mass[bin], static_cast<double>(exp2f(a)));
+            kin = min(kin, order_key(l));
         }
     });
-    __syncthreads();
+    kin = block_min_u32(kin);
     // Crossing bin: the smallest bin whose running mass from bin 0 reaches Tm.
     {
         constexpr int PER = kGapBins / kThreads;
@@ -846,7 +882,7 @@ __device__ void select_nucleus(const Params& P, const uint8_t* row, float O, dou
         for (int i = 0; i < PER; ++i) {
             const int bin = tid * PER + i;
             const double m = sh.mass[bin];
-            if (found == 0x7FFFFFFF && sh.cnt[bin] > 0 && pre + m >= Tm) {
+            if (found == 0x7FFFFFFF && m > 0.0 && pre + m >= Tm) {
                 found = bin;
                 fpre = pre;
             }
@@ -857,31 +893,60 @@ __device__ void select_nucleus(const Params& P, const uint8_t* row, float O, dou
             sh.sel_bin = fb;
             sh.sel_pre = fpre;
         }
-        // smallest key among non-empty bins, for the overflow case
         if (tid == 0 && fb == 0x7FFFFFFF) {
-            uint32_t kf = 0xFFFFFFFFu;
-            bool any = false;
-            for (int i = 0; i < kGapBins; ++i)
-                if (sh.cnt[i]) {
-                    kf = min(kf, sh.kmin[i]);
-                    any = true;
-                }
+            // no bin reaches Tm: the cut lies below every histogrammed key
             sh.sel_bin = kGapBins;
             sh.sel_pre = total;
-            sh.r_klo = 0u;
-            sh.r_khi = any ? kf - 1u : 0xFFFFFFFFu;
-            sh.r_cnt = 0xFFFFFFFFu;  // unknown: forces a radix pass
         }
-        __syncthreads();
-        if (tid == 0 && sh.sel_bin < kGapBins) {
-            const int sb = sh.sel_bin;
-            sh.r_klo = sh.kmin[sb];
-            sh.r_khi = sh.kmax[sb];
-            sh.r_cnt = sh.cnt[sb];
-        }
-        if (tid == 0) sh.r_A = sh.sel_pre;
         __syncthreads();
     }
+    const int sb = sh.sel_bin;
+    if (sb < kGapBins) {
+        // Pass B: the crossing bin's count and key interval, from registers,
+        // and its tokens collected while they fit (one LDS counter update per
+        // wave per vector)
+        uint32_t cnt = 0u, kmn = 0xFFFFFFFFu, kmx = 0u;
+        const int lane = tid & 63;
+        for_each_vec<DT>(row, V, [&](float l, int64_t id) {
+            const float a = fmaf(l, c_lo, fmaf(l, c_hi, -O));
+            const bool in = a > -16.f && id >= 0 && id < V &&
+                            max(0, static_cast<int>(floorf(-a * kGapPerBit))) == sb;
+            const uint32_t key = order_key(l);
+            if (in) {
+                ++cnt;
+                kmn = min(kmn, key);
+                kmx = max(kmx, key);
+            }
+            const unsigned long long m = __ballot(in);
+            if (m) {
+                const int nb = __popcll(m);
+                uint32_t base = 0u;
+                const int leader = __ffsll(static_cast<long long>(m)) - 1;
+                if (lane == leader) base = atomicAdd(&sh.nlist, static_cast<uint32_t>(nb));
+                base = __shfl(base, leader, 64);
+                if (in) {
+                    const uint32_t at = base + static_cast<uint32_t>(__popcll(m & ((1ull << lane) - 1ull)));
+                    if (at < static_cast<uint32_t>(kCollect))
+                        sh.list[at] = (static_cast<unsigned long long>(~key) << 32) | static_cast<uint32_t>(id);
+                }
+            }
+        });
+        cnt = block_sum_u32(cnt);
+        kmn = block_min_u32(kmn);
+        kmx = block_max_u32(kmx);
+        if (tid == 0) {
+            sh.r_klo = kmn;
+            sh.r_khi = kmx;
+            sh.r_cnt = cnt;
+        }
+    } else if (tid == 0) {
+        sh.r_klo = 0u;
+        sh.r_khi = kin == 0xFFFFFFFFu ? 0xFFFFFFFFu : kin - 1u;
+        sh.r_cnt = 0xFFFFFFFFu;  // unknown: forces a radix pass
+    }
+    if (tid == 0) sh.r_A = sh.sel_pre;
+    __syncthreads();
+    bool collected = sb < kGapBins && sh.r_cnt <= static_cast<uint32_t>(kCollect);
     // Refinement.
     for (;;) {
         const uint32_t klo = sh.r_klo, khi = sh.r_khi, rc = sh.r_cnt;
@@ -894,52 +959,10 @@ __device__ void select_nucleus(const Params& P, const uint8_t* row, float O, dou
             kept = S;
             return;
         }
-        if (klo == khi) {
-            // one key: a tie group of rc tokens of equal mass e
-            const float e = tempexp(key_value(klo), c_hi, c_lo, O);
-            const double need = (Tm - A) / static_cast<double>(e);
-            double rr = ceil(need);
-            if (!(rr >= 1.0)) rr = 1.0;
-            if (rr > static_cast<double>(rc)) rr = static_cast<double>(rc);
-            const uint32_t r = static_cast<uint32_t>(rr);
-            tau = klo;
-            kept = A + static_cast<double>(r) * static_cast<double>(e);
-            if (r >= rc) {
-                cut = 0x7FFFFFFF;
-                return;
-            }
-            // id of the r-th tied token in id order
-            int carry = 0;
-            if (tid == 0) sh.r_cut = -1;
-            __syncthreads();
-            for (int64_t t0 = 0; t0 < V; t0 += static_cast<int64_t>(kThreads) * kResTile) {
-                const int64_t id0 = t0 + static_cast<int64_t>(tid) * kResTile;
-                const int nv = static_cast<int>(min<int64_t>(max<int64_t>(V - id0, 0), kResTile));
-                float f[kResTile];
-                if (nv > 0) load8<DT>(row, id0, nv, f);
-                int cntl = 0;
-                for (int i = 0; i < nv; ++i) cntl += order_key(f[i]) == klo;
-                // exclusive prefix count of ties over threads
-                double ie, ee, te;
-                block_scan(static_cast<double>(cntl), ie, ee, te);
-                const int ex = carry + static_cast<int>(ee);
-                if (cntl > 0 && ex < static_cast<int>(r) && ex + cntl >= static_cast<int>(r)) {
-                    int c2 = ex;
-                    for (int i = 0; i < nv; ++i)
-                        if (order_key(f[i]) == klo && ++c2 == static_cast<int>(r)) {
-                            sh.r_cut = static_cast<int>(id0 + i);
-                            break;
-                        }
-                }
-                __syncthreads();
-                carry += static_cast<int>(te);
-                if (sh.r_cut >= 0) break;
-            }
-            cut = sh.r_cut;
-            return;
-        }
         if (rc <= static_cast<uint32_t>(kCollect)) {
-            // collect, sort by (key desc, id asc), walk the running mass
+            // collect (unless pass B already did), sort by (key desc, id
+            // asc), walk the running mass
+            if (!collected) {
             if (tid == 0) sh.nlist = 0u;
             __syncthreads();
             for_each_vec<DT>(row, V, [&](float l, int64_t id) {
@@ -952,6 +975,8 @@ __device__ void select_nucleus(const Params& P, const uint8_t* row, float O, dou
                     }
                 }
             });
+            }
+            collected = false;
             __syncthreads();
             const int n = static_cast<int>(min(sh.nlist, static_cast<uint32_t>(kCollect)));
             int np2 = 1;
@@ -1011,6 +1036,51 @@ __device__ void select_nucleus(const Params& P, const uint8_t* row, float O, dou
             tau = ~static_cast<uint32_t>(e >> 32);
             cut = static_cast<int32_t>(static_cast<uint32_t>(e));
             kept = sh.r_A;
+            return;
+        }
+        if (klo == khi) {
+            // one key, more tokens than the collect list holds: a tie group of
+            // rc tokens of equal mass e
+            const float e = tempexp(key_value(klo), c_hi, c_lo, O);
+            const double need = (Tm - A) / static_cast<double>(e);
+            double rr = ceil(need);
+            if (!(rr >= 1.0)) rr = 1.0;
+            if (rr > static_cast<double>(rc)) rr = static_cast<double>(rc);
+            const uint32_t r = static_cast<uint32_t>(rr);
+            tau = klo;
+            kept = A + static_cast<double>(r) * static_cast<double>(e);
+            if (r >= rc) {
+                cut = 0x7FFFFFFF;
+                return;
+            }
+            // id of the r-th tied token in id order
+            int carry = 0;
+            if (tid == 0) sh.r_cut = -1;
+            __syncthreads();
+            for (int64_t t0 = 0; t0 < V; t0 += static_cast<int64_t>(kThreads) * kResTile) {
+                const int64_t id0 = t0 + static_cast<int64_t>(tid) * kResTile;
+                const int nv = static_cast<int>(min<int64_t>(max<int64_t>(V - id0, 0), kResTile));
+                float f[kResTile];
+                if (nv > 0) load8<DT>(row, id0, nv, f);
+                int cntl = 0;
+                for (int i = 0; i < nv; ++i) cntl += order_key(f[i]) == klo;
+                // exclusive prefix count of ties over threads
+                double ie, ee, te;
+                block_scan(static_cast<double>(cntl), ie, ee, te);
+                const int ex = carry + static_cast<int>(ee);
+                if (cntl > 0 && ex < static_cast<int>(r) && ex + cntl >= static_cast<int>(r)) {
+                    int c2 = ex;
+                    for (int i = 0; i < nv; ++i)
+                        if (order_key(f[i]) == klo && ++c2 == static_cast<int>(r)) {
+                            sh.r_cut = static_cast<int>(id0 + i);
+                            break;
+                        }
+                }
+                __syncthreads();
+                carry += static_cast<int>(te);
+                if (sh.r_cut >= 0) break;
+            }
+            cut = sh.r_cut;
             return;
         }
         // radix pass: split [klo, khi] by the next 8 bits
@@ -1140,8 +1210,10 @@ __global__ __launch_bounds__(kThreads) void k_topp(Params P) {
 
 // ---------------------------------------------------------------------------
 // Row pass.  Workgroup (b, r) is resample item r of batch row b: ids
-// [r*kItemIds, (r+1)*kItemIds) of the row's position n, in kRuns runs: run k
-// is the kThreads*kRun ids from r*kItemIds + k*kThreads*kRun, thread t taking
+// [r*I, (r+1)*I) of the row's position n, I = R*kThreads*kRun (R runs, 4 for
+// large batches, 1 when the batch has few items, which quadruples the
+// workgroups).  Run k is the kThreads*kRun ids from r*I + k*kThreads*kRun,
+// thread t taking
 // the kRun consecutive ids at t*kRun (16-byte loads, coalesced).  Without
 // top-p every item first makes the row's decision from the statistics
 // records (all items reach the same one; item 0 writes the outputs).  Each
@@ -1152,7 +1224,6 @@ __global__ __launch_bounds__(kThreads) void k_topp(Params P) {
 // are consecutive in the grid: when a row has an item still to start, all
 // earlier rows' items are running or done, so every wait ends.
 // ---------------------------------------------------------------------------
-static_assert(kItemIds == kThreads * kRun * kRuns, "resample item layout");
 
 // A readable 16-byte vector that stands in for loads past the end of a row.
 __device__ const uint4 kPadVec = {0u, 0u, 0u, 0u};
@@ -1235,43 +1306,43 @@ __device__ __forceinline__ void run_weights(const float* lt, const float* ld, bo
     }
 }
 
-// Raw 16-byte vectors of one item for one thread: kRuns runs of each needed
+// Raw 16-byte vectors of one item for one thread: R runs of each needed
 // tensor.
-template <int DT> struct ItemRaw {
+template <int DT, int R> struct ItemRaw {
     static constexpr int NVR = kRun / Fmt<DT>::VE;
-    uint4 t[kRuns][NVR];
-    uint4 d[kRuns][NVR];
+    uint4 t[R][NVR];
+    uint4 d[R][NVR];
 };
-__device__ __forceinline__ int64_t item_run_id0(int r, int k) {
-    return static_cast<int64_t>(r) * kItemIds + static_cast<int64_t>(k) * (kThreads * kRun) +
+template <int R> __device__ __forceinline__ int64_t item_run_id0(int r, int k) {
+    return static_cast<int64_t>(r) * (R * kThreads * kRun) + static_cast<int64_t>(k) * (kThreads * kRun) +
            static_cast<int64_t>(threadIdx.x) * kRun;
 }
 // Issues every load of the item, then reloads by elements a run whose vector
 // straddles V (aligned rows only).
-template <int DT>
+template <int DT, int R>
 __device__ __forceinline__ void load_item(const uint8_t* rowT, const uint8_t* rowD, bool resid, bool aligned, int r,
-                                          int V, ItemRaw<DT>& raw) {
+                                          int V, ItemRaw<DT, R>& raw) {
 #pragma unroll
-    for (int k = 0; k < kRuns; ++k) {
-        issue_run<DT>(rowT, item_run_id0(r, k), V, aligned, raw.t[k]);
-        if (resid) issue_run<DT>(rowD, item_run_id0(r, k), V, aligned, raw.d[k]);
+    for (int k = 0; k < R; ++k) {
+        issue_run<DT>(rowT, item_run_id0<R>(r, k), V, aligned, raw.t[k]);
+        if (resid) issue_run<DT>(rowD, item_run_id0<R>(r, k), V, aligned, raw.d[k]);
     }
     if (aligned) {
 #pragma unroll
-        for (int k = 0; k < kRuns; ++k) {
-            if (run_straddles<DT>(item_run_id0(r, k), V)) {
-                load_run_elems<DT>(rowT, item_run_id0(r, k), V, raw.t[k]);
-                if (resid) load_run_elems<DT>(rowD, item_run_id0(r, k), V, raw.d[k]);
+        for (int k = 0; k < R; ++k) {
+            if (run_straddles<DT>(item_run_id0<R>(r, k), V)) {
+                load_run_elems<DT>(rowT, item_run_id0<R>(r, k), V, raw.t[k]);
+                if (resid) load_run_elems<DT>(rowD, item_run_id0<R>(r, k), V, raw.d[k]);
             }
         }
     }
 }
 // Weights of run k of item r: w = max(0, p' - q') (or p' for the bonus) and
 // p = p'.  `interior`: the whole item lies inside the row (nothing to mask).
-template <int DT, bool TOPP, bool RESID>
+template <int DT, bool TOPP, bool RESID, int R>
 __device__ __forceinline__ void item_run(const Params& P, const RowParam& rp, float invT, float invD,
-                                         const ItemRaw<DT>& raw, int r, int k, bool interior, float* w, float* p) {
-    const int64_t id0 = item_run_id0(r, k);
+                                         const ItemRaw<DT, R>& raw, int r, int k, bool interior, float* w, float* p) {
+    const int64_t id0 = item_run_id0<R>(r, k);
     float lt[kRun], ld[kRun];
     if (interior) {
         unpack_run<DT>(raw.t[k], lt);
@@ -1292,10 +1363,10 @@ static_assert(kRun == 8, "run_sum sums 8 values");
 // The resample part of batch row b for item r, given the row's decision (the
 // same in every item of the row) with n = rn and the mode's RESID.  Every
 // thread must call it.
-template <int DT, bool TOPP, bool RESID>
+template <int DT, bool TOPP, bool RESID, int R>
 __device__ void resample_body(const Params& P, int b, int r, const RowParam& rp, int rn) {
     __shared__ double s_w[kWaves], s_p[kWaves];
-    __shared__ double s_wt[kRuns][kWaves];
+    __shared__ double s_wt[R][kWaves];
     __shared__ int s_lastpos[kWaves];
     __shared__ int s_sel, s_item, s_ok;
     __shared__ double s_pre, s_Z, s_t;
@@ -1305,21 +1376,21 @@ __device__ void resample_body(const Params& P, int b, int r, const RowParam& rp,
     const bool aligned = ((reinterpret_cast<uintptr_t>(rowT) & 15) == 0) && ((reinterpret_cast<uintptr_t>(rowD) & 15) == 0);
     const float invT = static_cast<float>(1.0 / rp.keptT);
     const float invD = RESID ? static_cast<float>(1.0 / rp.keptD) : 0.f;
-    const bool interior = static_cast<int64_t>(r + 1) * kItemIds <= P.V;
+    const bool interior = static_cast<int64_t>(r + 1) * (R * kThreads * kRun) <= P.V;
     const int nq = P.nq;
     uint64_t* qrec = P.qrec + static_cast<size_t>(b) * nq * kRecWords;
 
     // 1. the item's weights (kept in registers) and masses
-    float w[kRuns][kRun];
-    float xs[kRuns];
+    float w[R][kRun];
+    float xs[R];
     double ws = 0.0, ps = 0.0;
     {
-        ItemRaw<DT> raw;
+        ItemRaw<DT, R> raw;
         load_item<DT>(rowT, rowD, RESID, aligned, r, P.V, raw);
 #pragma unroll
-        for (int k = 0; k < kRuns; ++k) {
+        for (int k = 0; k < R; ++k) {
             float p[kRun];
-            item_run<DT, TOPP, RESID>(P, rp, invT, invD, raw, r, k, interior, w[k], p);
+            item_run<DT, TOPP, RESID, R>(P, rp, invT, invD, raw, r, k, interior, w[k], p);
             xs[k] = run_sum(w[k]);
             ws += static_cast<double>(xs[k]);
             ps += static_cast<double>(run_sum(p));
@@ -1433,23 +1504,23 @@ __device__ void resample_body(const Params& P, int b, int r, const RowParam& rp,
     // replace w.
     const double t = s_t;
     if (s_sel) {
-        ItemRaw<DT> raw;
+        ItemRaw<DT, R> raw;
         load_item<DT>(rowT, rowD, RESID, aligned, r, P.V, raw);
 #pragma unroll
-        for (int k = 0; k < kRuns; ++k) {
+        for (int k = 0; k < R; ++k) {
             float wk[kRun];
-            item_run<DT, TOPP, RESID>(P, rp, invT, invD, raw, r, k, interior, wk, w[k]);
+            item_run<DT, TOPP, RESID, R>(P, rp, invT, invD, raw, r, k, interior, wk, w[k]);
             xs[k] = run_sum(w[k]);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
-    double wi[kRuns];
+    double wi[R];
     int lastpos = -1;
 #pragma unroll
-    for (int k = 0; k < kRuns; ++k) {
+    for (int k = 0; k < R; ++k) {
         wi[k] = wave_scan_dpp(static_cast<double>(xs[k]));
         if (lane == 63) s_wt[k][wv] = wi[k];
-        const int64_t id0 = item_run_id0(r, k);
+        const int64_t id0 = item_run_id0<R>(r, k);
 #pragma unroll
         for (int i = 0; i < kRun; ++i)
             if (w[k][i] > 0.f) lastpos = static_cast<int>(id0 + i);
@@ -1461,7 +1532,7 @@ __device__ void resample_body(const Params& P, int b, int r, const RowParam& rp,
     double base = s_pre, hoff = 0.0;
     int hk = -1, hw = -1, lp = -1;
 #pragma unroll
-    for (int k = 0; k < kRuns; ++k)
+    for (int k = 0; k < R; ++k)
 #pragma unroll
         for (int w2 = 0; w2 < kWaves; ++w2) {
             const double tot = s_wt[k][w2];
@@ -1492,7 +1563,7 @@ __device__ void resample_body(const Params& P, int b, int r, const RowParam& rp,
     float v[kRun];
     double myx = 0.0, myw = 0.0;
 #pragma unroll
-    for (int k = 0; k < kRuns; ++k)
+    for (int k = 0; k < R; ++k)
         if (k == hk) {
 #pragma unroll
             for (int i = 0; i < kRun; ++i) v[i] = w[k][i];
@@ -1504,7 +1575,7 @@ __device__ void resample_body(const Params& P, int b, int r, const RowParam& rp,
     const int hl = hm ? __ffsll(static_cast<long long>(hm)) - 1 : 63;
     if (lane == hl) {
         double run = incl - myx;  // exclusive prefix of this thread's run
-        const int64_t id0 = item_run_id0(r, hk);
+        const int64_t id0 = item_run_id0<R>(r, hk);
         int y = -1, lastw = -1;
 #pragma unroll
         for (int i = 0; i < kRun; ++i) {
@@ -1522,7 +1593,7 @@ __device__ void resample_body(const Params& P, int b, int r, const RowParam& rp,
     }
 }
 
-template <int DT, bool TOPP>
+template <int DT, bool TOPP, int R>
 __device__ __forceinline__ void resample_item(const Params& P, int b, int r, const RowParam& rp) {
     // the row's mode and n are the same for every lane: keep them scalar
     const int mode = __builtin_amdgcn_readfirstlane(rp.mode);
@@ -1535,35 +1606,35 @@ __device__ __forceinline__ void resample_item(const Params& P, int b, int r, con
         }
         return;
     }
-    if (mode == MODE_RESID) resample_body<DT, TOPP, true>(P, b, r, rp, rn);
-    else resample_body<DT, TOPP, false>(P, b, r, rp, rn);
+    if (mode == MODE_RESID) resample_body<DT, TOPP, true, R>(P, b, r, rp, rn);
+    else resample_body<DT, TOPP, false, R>(P, b, r, rp, rn);
 }
 
 // Row pass: one workgroup per (b, item).  With top-p the decision was made by
 // the nucleus pass; without, every item makes it from the statistics records
 // (the statistics kernel has finished, so no record is waited for).
-template <int DT, bool TOPP>
+template <int DT, bool TOPP, int R>
 __global__ __launch_bounds__(kThreads) void k_rows(Params P) {
-    __shared__ RowShared R;
+    __shared__ RowShared RS;
     __shared__ RowParam s_rp;
     const int b = blockIdx.x / P.nq;
     const int r = blockIdx.x - b * P.nq;
     if (TOPP) {
         const RowParam rp = P.rowp[b];
-        resample_item<DT, true>(P, b, r, rp);
+        resample_item<DT, true, R>(P, b, r, rp);
     } else {
         bool rowok;
         const int Le = row_len(P, b, rowok);
         const int x = lane_token(P, b, Le);
-        fill_row_from_partials(P, b, Le, R);
+        fill_row_from_partials(P, b, Le, RS);
         if ((threadIdx.x >> 6) == 0) {
             RowParam rp;
-            decide_row<false>(P, b, Le, rowok, R, r == 0, x, rp);
+            decide_row<false>(P, b, Le, rowok, RS, r == 0, x, rp);
             if ((threadIdx.x & 63) == 0) s_rp = rp;
         }
         __syncthreads();
         const RowParam rp = s_rp;
-        resample_item<DT, false>(P, b, r, rp);
+        resample_item<DT, false, R>(P, b, r, rp);
     }
 }
 
@@ -1628,15 +1699,22 @@ hipError_t launch_topp(const Params& p, int dtype, hipStream_t s, const LaunchEv
     return hipGetLastError();
 }
 
-hipError_t launch_rows(const Params& p, int dtype, bool topp, hipStream_t s, const LaunchEvents& ev) {
+template <int R>
+static void launch_rows_r(const Params& p, int dtype, bool topp, hipStream_t s, const LaunchEvents& ev) {
     const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(p.B) * p.nq);
     if (dtype == DT_BF16) {
-        if (topp) launch(k_rows<DT_BF16, true>, grid, kThreads, s, ev, p);
-        else launch(k_rows<DT_BF16, false>, grid, kThreads, s, ev, p);
+        if (topp) launch(k_rows<DT_BF16, true, R>, grid, kThreads, s, ev, p);
+        else launch(k_rows<DT_BF16, false, R>, grid, kThreads, s, ev, p);
     } else {
-        if (topp) launch(k_rows<DT_F32, true>, grid, kThreads, s, ev, p);
-        else launch(k_rows<DT_F32, false>, grid, kThreads, s, ev, p);
+        if (topp) launch(k_rows<DT_F32, true, R>, grid, kThreads, s, ev, p);
+        else launch(k_rows<DT_F32, false, R>, grid, kThreads, s, ev, p);
     }
+}
+
+hipError_t launch_rows(const Params& p, int dtype, bool topp, hipStream_t s, const LaunchEvents& ev) {
+    if (p.runs == 1) launch_rows_r<1>(p, dtype, topp, s, ev);
+    else if (p.runs == 2) launch_rows_r<2>(p, dtype, topp, s, ev);
+    else launch_rows_r<kRunsMax>(p, dtype, topp, s, ev);
     return hipGetLastError();
 }
 

@@ -796,13 +796,15 @@ __device__ __forceinline__ int block_sum_int(int v) {
 // ---------------------------------------------------------------------------
 constexpr int kGapBins = 1024;          // 16 bits of gap at 64 bins per bit
 constexpr float kGapPerBit = 64.f;
-constexpr int kCollect = 2048;
+constexpr int kRadixBins = 256;         // a radix pass splits a key interval by 8 bits
+constexpr int kCollect = 512;           // tokens a collect-and-sort step takes
 
+// Small enough that every logit row's workgroup is resident at once.
 struct SelShared {
-    double mass[kGapBins];
-    uint32_t cnt[kGapBins];
-    uint32_t kmin[kGapBins];
-    uint32_t kmax[kGapBins];
+    double mass[kGapBins];              // gap histogram; radix masses in [0, kRadixBins)
+    uint32_t cnt[kRadixBins];
+    uint32_t kmin[kRadixBins];
+    uint32_t kmax[kRadixBins];
     unsigned long long list[kCollect];
     uint32_t nlist;
     int sel_bin;
@@ -817,7 +819,7 @@ struct SelShared {
 // taking 16-byte vectors in turn; kSweep vectors per thread are loaded
 // before any is used, so a pass over a row costs few memory round trips.
 // Ids outside [0, V) (edges of unaligned rows) come with -inf.
-constexpr int kSweep = 8;
+constexpr int kSweep = 4;
 template <int DT, typename F>
 __device__ __forceinline__ void for_each_vec(const uint8_t* row, int V, F&& fn) {
     constexpr int VE = Fmt<DT>::VE;
@@ -843,6 +845,9 @@ __device__ __forceinline__ void for_each_vec(const uint8_t* row, int V, F&& fn) 
     }
 }
 
+// Gap bin of a token with exponent a = l*c - O > -16 (a <= 0 up to rounding).
+__device__ __forceinline__ int gap_bin(float a) { return max(0, static_cast<int>(-a * kGapPerBit)); }
+
 template <int DT>
 __device__ void select_nucleus(const Params& P, const uint8_t* row, float O, double S, SelShared& sh, double& kept,
                                uint32_t& tau, int32_t& cut) {
@@ -858,18 +863,13 @@ __device__ void select_nucleus(const Params& P, const uint8_t* row, float O, dou
     }
     __syncthreads();
     // Pass A: gap histogram (mass only; a bin is a monotone function of the
-    // logit, so its key interval and count are found again in pass B), and
-    // the smallest key within 16 bits of the offset.
-    uint32_t kin = 0xFFFFFFFFu;
-    for_each_vec<DT>(row, V, [&](float l, int64_t id) {
+    // logit, so its key interval and count are found again in pass B).  Ids
+    // outside [0, V) arrive as -inf and fail the gap test.
+    for_each_vec<DT>(row, V, [&](float l, int64_t) {
         const float a = fmaf(l, c_lo, fmaf(l, c_hi, -O));
-        if (a > -16.f && id >= 0 && id < V) {
-            const int bin = max(0, static_cast<int>(floorf(-a * kGapPerBit)));
-            atomicAdd(&sh.mass[bin], static_cast<double>(exp2f(a)));
-            kin = min(kin, order_key(l));
-        }
+        if (a > -16.f) atomicAdd(&sh.mass[gap_bin(a)], static_cast<double>(hw_exp2(a)));
     });
-    kin = block_min_u32(kin);
+    __syncthreads();
     // Crossing bin: the smallest bin whose running mass from bin 0 reaches Tm.
     {
         constexpr int PER = kGapBins / kThreads;
@@ -900,35 +900,31 @@ __device__ void select_nucleus(const Params& P, const uint8_t* row, float O, dou
         }
         __syncthreads();
     }
+    uint32_t kin = 0xFFFFFFFFu;  // smallest key within 16 bits (overflow case only)
+    if (sh.sel_bin == kGapBins) {
+        for_each_vec<DT>(row, V, [&](float l, int64_t) {
+            const float a = fmaf(l, c_lo, fmaf(l, c_hi, -O));
+            if (a > -16.f) kin = min(kin, order_key(l));
+        });
+        kin = block_min_u32(kin);
+    }
     const int sb = sh.sel_bin;
     if (sb < kGapBins) {
         // Pass B: the crossing bin's count and key interval, from registers,
         // and its tokens collected while they fit (one LDS counter update per
         // wave per vector)
         uint32_t cnt = 0u, kmn = 0xFFFFFFFFu, kmx = 0u;
-        const int lane = tid & 63;
         for_each_vec<DT>(row, V, [&](float l, int64_t id) {
             const float a = fmaf(l, c_lo, fmaf(l, c_hi, -O));
-            const bool in = a > -16.f && id >= 0 && id < V &&
-                            max(0, static_cast<int>(floorf(-a * kGapPerBit))) == sb;
-            const uint32_t key = order_key(l);
-            if (in) {
+            if (a > -16.f && gap_bin(a) == sb) {
+                // rare: the crossing bin holds few tokens of a row
+                const uint32_t key = order_key(l);
                 ++cnt;
                 kmn = min(kmn, key);
                 kmx = max(kmx, key);
-            }
-            const unsigned long long m = __ballot(in);
-            if (m) {
-                const int nb = __popcll(m);
-                uint32_t base = 0u;
-                const int leader = __ffsll(static_cast<long long>(m)) - 1;
-                if (lane == leader) base = atomicAdd(&sh.nlist, static_cast<uint32_t>(nb));
-                base = __shfl(base, leader, 64);
-                if (in) {
-                    const uint32_t at = base + static_cast<uint32_t>(__popcll(m & ((1ull << lane) - 1ull)));
-                    if (at < static_cast<uint32_t>(kCollect))
-                        sh.list[at] = (static_cast<unsigned long long>(~key) << 32) | static_cast<uint32_t>(id);
-                }
+                const uint32_t at = atomicAdd(&sh.nlist, 1u);
+                if (at < static_cast<uint32_t>(kCollect))
+                    sh.list[at] = (static_cast<unsigned long long>(~key) << 32) | static_cast<uint32_t>(id);
             }
         });
         cnt = block_sum_u32(cnt);

@@ -29,15 +29,16 @@ struct Scratch {
 };
 
 struct Layout {
-    size_t prec, rv, rowp, qrec, total;
+    size_t prec, rv, rowp, qrec, chdr, cand, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
 // Tagged records (statistics per chunk, masses per resample item) are left
 // at zero by every call that completes; RvState and RowParam are rewritten
-// before they are read.
-Layout layout(int64_t B, int nslot, int nch, int nq) {
+// before they are read.  The top-p candidate headers and lists (present only
+// when `topp`) are rewritten by the statistics pass of every top-p call.
+Layout layout(int64_t B, int nslot, int nch, int nq, bool topp) {
     Layout L;
     size_t off = 0;
     L.prec = off;
@@ -48,6 +49,11 @@ Layout layout(int64_t B, int nslot, int nch, int nq) {
     off = align256(off + static_cast<size_t>(B) * sizeof(sv::RowParam));
     L.qrec = off;
     off = align256(off + static_cast<size_t>(B) * nq * sv::kRecWords * sizeof(uint64_t));
+    const size_t chunks = topp ? static_cast<size_t>(B) * nslot * nch : 0;
+    L.chdr = off;
+    off = align256(off + chunks * sv::kWaves * 2 * sizeof(uint64_t));
+    L.cand = off;
+    off = align256(off + chunks * sv::kCand * sizeof(uint64_t));
     L.total = off;
     return L;
 }
@@ -233,7 +239,8 @@ int verify_impl(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_t
     if (4ll * nq > static_cast<int64_t>(sv::kThreads) * nslot * nch) return SV_ESHAPE;
 
     hipStream_t stream = static_cast<hipStream_t>(stream_v);
-    const Layout lay = layout(B, nslot, nch, nq);
+    const bool topp = top_p < 1.f;
+    const Layout lay = layout(B, nslot, nch, nq, topp);
     void* scratch = nullptr;
     uint32_t* counters = nullptr;
     rc = get_scratch(stream, lay.total, B, &scratch, &counters);
@@ -271,6 +278,7 @@ int verify_impl(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_t
     p.c_hi = c_hi;
     p.c_lo = c_lo;
     p.c64 = static_cast<double>(c_hi) + static_cast<double>(c_lo);
+    p.inv_c = static_cast<float>(1.0 / c);
     p.top_p = top_p;
     p.key0 = static_cast<uint32_t>(seed & 0xFFFFFFFFull);
     p.key1 = static_cast<uint32_t>(seed >> 32);
@@ -278,11 +286,13 @@ int verify_impl(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_t
     p.rv = reinterpret_cast<sv::RvState*>(base + lay.rv);
     p.rowp = reinterpret_cast<sv::RowParam*>(base + lay.rowp);
     p.qrec = reinterpret_cast<uint64_t*>(base + lay.qrec);
+    p.chdr = topp ? reinterpret_cast<uint64_t*>(base + lay.chdr) : nullptr;
+    p.cand = topp ? reinterpret_cast<uint64_t*>(base + lay.cand) : nullptr;
     p.row_cnt = counters;
 
-    const bool topp = top_p < 1.f;
-    rc = timed_launch(sv::KK_STATS, stream,
-                      [&](const sv::LaunchEvents& ev) { return sv::launch_stats(p, dtype, unroll, stream, ev); });
+    rc = timed_launch(sv::KK_STATS, stream, [&](const sv::LaunchEvents& ev) {
+        return sv::launch_stats(p, dtype, unroll, topp, stream, ev);
+    });
     if (rc) return rc;
     if (topp) {
         rc = timed_launch(sv::KK_TOPP, stream,

@@ -207,6 +207,17 @@ __device__ __forceinline__ int wave_max_int_dpp(int v) {
     v = max(v, dpp_int<kDppRowBcast31, 0xC>(lo, v));
     return __builtin_amdgcn_readlane(v, 63);
 }
+// Maximum over the wave, the same in every lane (-inf is the identity).
+__device__ __forceinline__ float wave_max_dpp(float v) {
+    constexpr int ninf = static_cast<int>(0xFF800000u);
+    v = fmaxf(v, __int_as_float(dpp_int<kDppRowShr1, 0xF>(ninf, __float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_int<kDppRowShr2, 0xF>(ninf, __float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_int<kDppRowShr4, 0xF>(ninf, __float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_int<kDppRowShr8, 0xF>(ninf, __float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_int<kDppRowBcast15, 0xA>(ninf, __float_as_int(v))));
+    v = fmaxf(v, __int_as_float(dpp_int<kDppRowBcast31, 0xC>(ninf, __float_as_int(v))));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
 __device__ __forceinline__ int wave_min_int_dpp(int v) {
     constexpr int hi = 0x7FFFFFFF;
     v = min(v, dpp_int<kDppRowShr1, 0xF>(hi, v));

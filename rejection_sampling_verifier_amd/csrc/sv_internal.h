@@ -17,6 +17,8 @@ constexpr int kRun = 8;              // ids per thread per run of a resample ite
 constexpr int kRunsMax = 4;          // runs per thread per resample item, large batches
 constexpr int kRunIds = kThreads * kRun;  // ids per run of an item (2048)
 constexpr int kRecWords = 4;         // 64-bit words per tagged record
+constexpr int kCand = 256;           // nucleus candidates a statistics chunk lists at most
+constexpr uint32_t kNoCover = 0xFFFFFFFFu;  // candidate header: the chunk's list covers nothing
 
 enum DType : int { DT_F32 = 0, DT_BF16 = 1 };
 enum RowMode : int { MODE_SKIP = 0, MODE_RESID = 1, MODE_BONUS = 2 };
@@ -79,12 +81,15 @@ struct Params {
     uint32_t tag;                 // this call's record tag (never 0)
     float c_hi, c_lo;             // c = log2(e)/T = c_hi + c_lo, c_lo > 0
     double c64;                   // (double)c_hi + (double)c_lo
+    float inv_c;                  // 1/c, rounded (thresholds only)
     float top_p;
     uint32_t key0, key1;          // Philox key
     uint64_t* prec;               // [B, nslot, nch] tagged statistics records
     RvState* rv;                  // [B, nslot]
     RowParam* rowp;               // [B]
     uint64_t* qrec;               // [B, nq] tagged resample-item mass records
+    uint64_t* chdr;               // top-p: [B, nslot, nch, kWaves, 2] tagged candidate headers (count, key bound)
+    uint64_t* cand;               // top-p: [B, nslot, nch, kCand] candidates (~key << 32 | id), kCand/kWaves per wave
     uint32_t* row_cnt;            // [B] arrival counters, kCounterStride words apart, zero between calls
 };
 
@@ -96,9 +101,10 @@ struct LaunchEvents {
 };
 
 // Launchers (defined in sv_kernels.hip).
-// The statistics pass, then (top-p only) the nucleus pass with the decision,
-// then the row pass (decision without top-p, resample).
-hipError_t launch_stats(const Params& p, int dtype, int unroll, hipStream_t s, const LaunchEvents& ev);
+// The statistics pass (with top-p it also lists each chunk's nucleus
+// candidates), then (top-p only) the nucleus pass with the decision, then the
+// row pass (decision without top-p, resample).
+hipError_t launch_stats(const Params& p, int dtype, int unroll, bool topp, hipStream_t s, const LaunchEvents& ev);
 hipError_t launch_topp(const Params& p, int dtype, hipStream_t s, const LaunchEvents& ev);
 hipError_t launch_rows(const Params& p, int dtype, bool topp, hipStream_t s, const LaunchEvents& ev);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int unroll, hipStream_t s);

@@ -14,23 +14,26 @@
 // Pipeline (one stream, no host synchronisation):
 //   k_stats     one workgroup per (row b, logit row, chunk of V): streams the
 //               chunk once from HBM with 16-byte loads and reduces it to one
-//               partial (offset o, sum 2^(l*c - o), max, logit at the drafted
-//               id).  Without top-p the last workgroup to finish a batch row
-//               makes the row's decision: combine, p'(x_j)/q'(x_j), Philox,
-//               accept scan -> n_b, outputs.
+//               tagged partial record (offset o, sum 2^(l*c - o), max, logit
+//               at the drafted id).  With top-p every wave also lists its
+//               share's largest logits (nucleus candidates) with a key bound
+//               above which the list is complete.
 //   k_topp      (top-p only) one workgroup per logit row: exact nucleus cut
-//               (value key tau, tie cut by id, kept mass); the last logit row
-//               of a batch row makes the decision.
-//   k_resample  one workgroup per (row b, chunk of V): residual or bonus mass
-//               of the chunk in float64; the last chunk of a row finds the
-//               chunk holding u*Z and rescans it in id order for the token.
+//               (value key tau, tie cut by id, kept mass), from the candidate
+//               lists when they reach it, else from passes over the row; the
+//               last logit row of a batch row makes the decision.
+//   k_rows      one workgroup per (row b, item of V): combines the row's
+//               partials and makes the decision (without top-p: every item
+//               alike), then computes the residual or bonus weights of its
+//               ids, exchanges item masses through tagged records and lets
+//               the item holding u*Z pick the token by an in-order scan.
 //
-// Hand-offs between workgroups of one kernel ("last one to finish does the
-// row") use agent-coherent atomic stores for the data, a wait for their
-// completion, and a relaxed agent-scope counter: on this part an agent-scope
-// release/acquire costs an L2 writeback or invalidate per workgroup, while a
-// store that is itself coherent at agent scope needs neither.  Everything that
-// streams V is bandwidth-bound (no dense contraction, so no MFMA).
+// Hand-offs between workgroups use tagged 64-bit records: an aligned 64-bit
+// store is single-copy atomic, so a producer stores and exits, and a consumer
+// polls (bounded) until every word carries the call's tag.  Across a kernel
+// boundary plain loads suffice.  Only the top-p decision uses a counter (the
+// last logit row of a batch row to finish decides).  Everything that streams V
+// is bandwidth-bound (no dense contraction, so no MFMA).
 
 #include <hip/hip_ext.h>
 
@@ -531,6 +534,21 @@ __device__ __forceinline__ void mask_edge_raw(uint4& v, int64_t k, int head, int
     }
 }
 
+// Nucleus candidates (top-p).  Each wave of a statistics workgroup lists the
+// tokens of its share of the chunk whose logit is at least a threshold thr,
+// chosen from the wave's own count histogram so that at most kCandW -
+// kCandSlack tokens pass.  The wave's header records the count and the key
+// bound order_key(thr): every finite-logit token of its share with a key at
+// or above the bound is in its list.  The nucleus pass can therefore take the
+// cut from the lists whenever it lies above every wave's bound.  A wave whose
+// top bin alone holds too many tokens, or whose list overflows, records
+// kNoCover.
+constexpr uint32_t kCandLowBits = 448u << 21;  // e >= 2^-15
+constexpr int kCandW = kCand / kWaves;         // list slots per wave
+constexpr int kCandSlack = 8;
+constexpr int kCandHist = 64;                  // per-wave bins: top 9 bits of e in [448, 512)
+static_assert(kCandW == 64 && kCandHist == 64, "one lane per list slot and per bin");
+
 // Statistics of one lane's U vectors, read from the raw loaded words in two
 // passes (max, then the sum of 2^(l*c - o)) so that no unpacked copy of the
 // chunk is kept in registers.
@@ -542,10 +560,15 @@ template <int DT> __device__ __forceinline__ float elem_at(const uint4& v, int r
     return __uint_as_float((rx & 1) ? (w & 0xFFFF0000u) : (w << 16));
 }
 
-template <int DT, int U>
+// With top-p (CAND) the exponents are taken against the wave's offset
+// instead of the lane's, and every element with e = 2^(l*c - o) >= 2^-15
+// also counts into the wave's histogram `hist` by the top 9 bits of e
+// (exponent and two mantissa bits: quarter-octave bins of the mass, a
+// monotone function of l within the wave; the 64 bins cover [2^-15, 2)).
+template <int DT, int U, bool CAND>
 __device__ __forceinline__ void reduce_lane(const RowGrid& g, uint4* raw, int64_t k0, int64_t k1, int V, bool edge,
-                                            float c_hi, float c_lo, int64_t kx, int rx, float& lx, float& m, float& o,
-                                            float& s) {
+                                            float c_hi, float c_lo, int64_t kx, int rx, uint32_t* hist, float& lx,
+                                            float& m, float& o, float& s) {
     constexpr int VE = Fmt<DT>::VE;
     if (edge) {
         // the chunk holds the row's first or last vector
@@ -576,7 +599,7 @@ __device__ __forceinline__ void reduce_lane(const RowGrid& g, uint4* raw, int64_
     // words are re-read (and re-unpacked, one instruction per element)
 #pragma unroll
     for (int u = 0; u < U; ++u) asm volatile("" : "+v"(raw[u].x), "+v"(raw[u].y), "+v"(raw[u].z), "+v"(raw[u].w));
-    o = ceilf(m * c_hi);
+    o = ceilf((CAND ? wave_max_dpp(m) : m) * c_hi);
     const float off = (o == -SV_INF) ? 0.f : o;
     // pass 2: the sum, a pairwise tree per vector
     float acc[U];
@@ -584,12 +607,24 @@ __device__ __forceinline__ void reduce_lane(const RowGrid& g, uint4* raw, int64_
     for (int u = 0; u < U; ++u) {
         float e[VE];
 #pragma unroll
-        for (int i = 0; i < VE; ++i) e[i] = tempexp(elem<DT>(raw[u], i), c_hi, c_lo, off);
+        for (int i = 0; i < VE; ++i) {
+            e[i] = tempexp(elem<DT>(raw[u], i), c_hi, c_lo, off);
+            if (CAND) {
+                // NaN and inf (invalid rows) land in some bin, never outside
+                const uint32_t eb = __float_as_uint(e[i]);
+                if (eb >= kCandLowBits)
+                    __hip_atomic_fetch_add(hist + __builtin_amdgcn_ubfe(eb, 21, 6), 1u, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_WORKGROUP);
+            }
+        }
 #pragma unroll
         for (int w = VE / 2; w >= 1; w >>= 1)
 #pragma unroll
             for (int i = 0; i < w; ++i) e[i] += e[i + w];
         acc[u] = e[0];
+        // with the histogram updates in between, the instruction order would
+        // keep every vector's exponentials alive until the end: pin the sum
+        if (CAND) asm volatile("" : "+v"(acc[u]));
     }
 #pragma unroll
     for (int w = U / 2; w >= 1; w >>= 1)
@@ -598,15 +633,81 @@ __device__ __forceinline__ void reduce_lane(const RowGrid& g, uint4* raw, int64_
     s = acc[0];
 }
 
+// The wave's candidate list (see above): threshold from the wave's histogram
+// (bins against the wave's offset o), then one pass over the registers that
+// appends every token with l >= thr to the wave's LDS stage, copied out with
+// one store per lane to list slot `slot0` + position; the header (count, key
+// bound) goes to header `hdr`.
+template <int DT, int U>
+__device__ __forceinline__ void list_wave_candidates(const Params& P, const RowGrid& g, uint4* raw, int64_t k0, float o,
+                                                     const uint32_t* hist, uint64_t* stage, size_t slot0, size_t hdr) {
+    const int tid = threadIdx.x, lane = tid & 63;
+    // top bins first: lane i counts the 9-bit value 511 - i of e
+    const double incl = wave_scan_dpp(static_cast<double>(hist[kCandHist - 1 - lane]));
+    const int t = __popcll(__ballot(incl <= static_cast<double>(kCandW - kCandSlack)));
+    float thr = SV_INF;
+    uint32_t kw = kNoCover;
+    if (o == -SV_INF) {
+        kw = 0u;  // no finite logit: nothing to list
+    } else if (t > 0) {
+        // the listed bins hold e >= 2^(E-127) * (1 + q/4): l >= (o + log2 of that) / c
+        const int eb = 512 - t;
+        const int q = eb & 3;
+        const float lg1p = q == 0 ? 0.f : q == 1 ? 0.32192809f : q == 2 ? 0.5849625f : 0.80735492f;
+        thr = (o + static_cast<float>((eb >> 2) - 127) + lg1p) * P.inv_c;
+        kw = order_key(thr);
+    }
+    // nothing unpacked by the sum pass lives until here
+#pragma unroll
+    for (int u = 0; u < U; ++u) asm volatile("" : "+v"(raw[u].x), "+v"(raw[u].y), "+v"(raw[u].z), "+v"(raw[u].w));
+    // base counts every passing token (wave-uniform); slots past kCandW are
+    // not written, and a count above kCandW marks the list incomplete
+    uint32_t base = 0u;
+    const int id0 = static_cast<int>((k0 + tid) * Fmt<DT>::VE) - g.head;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < Fmt<DT>::VE; ++i) {
+            const float l = elem<DT>(raw[u], i);
+            const bool take = l >= thr;
+            const uint64_t bal = __ballot(take);
+            if (bal != 0ull) {
+                const uint32_t at = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), base));
+                if (take && at < static_cast<uint32_t>(kCandW))
+                    stage[at] = (static_cast<uint64_t>(__float_as_uint(l)) << 32) |
+                                static_cast<uint32_t>(id0 + (u * kThreads) * Fmt<DT>::VE + i);
+                base = __builtin_amdgcn_readfirstlane(base + static_cast<uint32_t>(__popcll(bal)));
+            }
+        }
+    }
+    const bool over = base > static_cast<uint32_t>(kCandW);
+    // same-wave LDS order: the stage is complete for this wave's lanes; the
+    // entries leave as (~key << 32 | id)
+    if (!over && static_cast<uint32_t>(lane) < base) {
+        const uint64_t st = stage[lane];
+        const uint32_t key = order_key(__uint_as_float(static_cast<uint32_t>(st >> 32)));
+        P.cand[slot0 + lane] = (static_cast<uint64_t>(~key) << 32) | static_cast<uint32_t>(st);
+    }
+    if (lane == 0) {
+        P.chdr[2 * hdr] = tagged(P.tag, over ? 0u : base);
+        P.chdr[2 * hdr + 1] = tagged(P.tag, over ? kNoCover : kw);
+    }
+}
+
 // One statistics item: chunk `chunk` of logit row `slot` of batch row b.
 // Streams the chunk once, reduces it to (o, m, lx, s) and publishes the
 // tagged record; nothing waits on the store.  `item` is unique to the
-// workgroup within the launch (it tags the LDS hand-over of lx).
-template <int DT, int U>
+// workgroup within the launch (it tags the LDS hand-over of lx).  With CAND
+// (top-p) each wave also lists its share's nucleus candidates.
+template <int DT, int U, bool CAND>
 __device__ __forceinline__ void stats_item(const Params& P, int b, int slot, int chunk, int item) {
     __shared__ float sh_o[kWaves], sh_s[kWaves], sh_m[kWaves];
     __shared__ float sh_lxv;
     __shared__ int sh_lxtag;
+    __shared__ uint32_t sh_hist[kWaves][kCandHist];
+    __shared__ uint64_t sh_stage[kWaves][kCandW];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     bool rowok;
     const int Le = row_len(P, b, rowok);
@@ -640,8 +741,18 @@ __device__ __forceinline__ void stats_item(const Params& P, int b, int slot, int
             rx = static_cast<int>(static_cast<int64_t>(x) + g.head - kx * Fmt<DT>::VE);
         }
     }
+    uint32_t* hist = nullptr;
+    if (CAND) {
+        hist = sh_hist[wv];
+        hist[lane] = 0u;  // each wave clears its own histogram (same-wave LDS order)
+    }
     float lx = -SV_INF, m, o, sl;
-    reduce_lane<DT, U>(g, raw, k0, k1, P.V, k0 == 0 || k0 + STEP >= g.nvec - 1, P.c_hi, P.c_lo, kx, rx, lx, m, o, sl);
+    reduce_lane<DT, U, CAND>(g, raw, k0, k1, P.V, k0 == 0 || k0 + STEP >= g.nvec - 1, P.c_hi, P.c_lo, kx, rx, hist,
+                             lx, m, o, sl);
+    if (CAND) {
+        const size_t ci = (static_cast<size_t>(b) * P.nslot + slot) * P.nch + chunk;
+        list_wave_candidates<DT, U>(P, g, raw, k0, o, hist, sh_stage[wv], ci * kCand + wv * kCandW, ci * kWaves + wv);
+    }
     // the one lane holding the drafted id's vector hands its logit over,
     // tagged with this workgroup's item (LDS is not cleared between
     // workgroups)
@@ -683,7 +794,7 @@ __device__ __forceinline__ void stats_item(const Params& P, int b, int slot, int
 }
 
 // Statistics pass of the top-p pipeline: one workgroup per (b, slot, chunk).
-template <int DT, int U>
+template <int DT, int U, bool CAND>
 __global__ __launch_bounds__(kThreads, 8) void k_stats(Params P) {
     const int item = blockIdx.x;
     {
@@ -698,7 +809,7 @@ __global__ __launch_bounds__(kThreads, 8) void k_stats(Params P) {
     const int rvi = item / P.nch;
     const int chunk = item - rvi * P.nch;
     const int b = rvi / P.nslot;
-    stats_item<DT, U>(P, b, rvi - b * P.nslot, chunk, item);
+    stats_item<DT, U, CAND>(P, b, rvi - b * P.nslot, chunk, item);
 }
 
 // ---------------------------------------------------------------------------
@@ -848,6 +959,108 @@ __device__ __forceinline__ void for_each_vec(const uint8_t* row, int V, F&& fn) 
 // Gap bin of a token with exponent a = l*c - O > -16 (a <= 0 up to rounding).
 __device__ __forceinline__ int gap_bin(float a) { return max(0, static_cast<int>(-a * kGapPerBit)); }
 
+// Crossing bin of the gap histogram sh.mass: the smallest bin whose running
+// mass from bin 0 reaches Tm (sh.sel_bin, with the mass of the bins before it
+// in sh.sel_pre), or kGapBins with the total when no bin does.
+__device__ void find_crossing(SelShared& sh, double Tm) {
+    const int tid = threadIdx.x;
+    constexpr int PER = kGapBins / kThreads;
+    double tsum = 0.0;
+    for (int i = 0; i < PER; ++i) tsum += sh.mass[tid * PER + i];
+    double incl, excl, total;
+    block_scan(tsum, incl, excl, total);
+    int found = 0x7FFFFFFF;
+    double pre = excl, fpre = 0.0;
+    for (int i = 0; i < PER; ++i) {
+        const int bin = tid * PER + i;
+        const double m = sh.mass[bin];
+        if (found == 0x7FFFFFFF && m > 0.0 && pre + m >= Tm) {
+            found = bin;
+            fpre = pre;
+        }
+        pre += m;
+    }
+    const int fb = block_min_int(found);
+    if (found == fb && fb != 0x7FFFFFFF) {
+        sh.sel_bin = fb;
+        sh.sel_pre = fpre;
+    }
+    if (tid == 0 && fb == 0x7FFFFFFF) {
+        // no bin reaches Tm: the cut lies below every histogrammed key
+        sh.sel_bin = kGapBins;
+        sh.sel_pre = total;
+    }
+    __syncthreads();
+}
+
+// Sorts the n collected entries (~key << 32 | id) of sh.list ascending -- key
+// descending, id ascending -- and walks the running mass from A in that
+// order.  Returns true with the first entry whose running mass reaches Tm
+// (tau, cut) and that running mass (kept).  Returns false when no running sum
+// reaches Tm (rounding), with the last entry and A plus the entries' mass.
+__device__ bool sort_walk(SelShared& sh, int n, double A, double Tm, float O, float c_hi, float c_lo, uint32_t& tau,
+                          int32_t& cut, double& kept) {
+    const int tid = threadIdx.x;
+    int np2 = 1;
+    while (np2 < n) np2 <<= 1;
+    for (int i = n + tid; i < np2; i += kThreads) sh.list[i] = ~0ull;
+    __syncthreads();
+    // bitonic sort, ascending
+    for (int kk = 2; kk <= np2; kk <<= 1) {
+        for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+            for (int i = tid; i < np2; i += kThreads) {
+                const int ij = i ^ jj;
+                if (ij > i) {
+                    const unsigned long long a = sh.list[i], c = sh.list[ij];
+                    const bool up = (i & kk) == 0;
+                    if ((a > c) == up) {
+                        sh.list[i] = c;
+                        sh.list[ij] = a;
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+    // running mass in sorted order: each thread a run of `per`, then a scan
+    const int per = (n + kThreads - 1) / kThreads;
+    const int s0 = tid * per, s1 = min(s0 + per, n);
+    double ts = 0.0;
+    for (int i = s0; i < s1; ++i)
+        ts += static_cast<double>(tempexp(key_value(~static_cast<uint32_t>(sh.list[i] >> 32)), c_hi, c_lo, O));
+    double incl, excl, total;
+    block_scan(ts, incl, excl, total);
+    int found = 0x7FFFFFFF;
+    double fk = 0.0;
+    double run = A + excl;
+    for (int i = s0; i < s1; ++i) {
+        run += static_cast<double>(tempexp(key_value(~static_cast<uint32_t>(sh.list[i] >> 32)), c_hi, c_lo, O));
+        if (run >= Tm) {
+            found = i;
+            fk = run;
+            break;
+        }
+    }
+    const int fi = block_min_int(found);
+    if (fi == 0x7FFFFFFF) {
+        // rounding: no running sum reached Tm; keep the whole interval
+        if (tid == 0) {
+            sh.r_A = A + total;
+            sh.r_cut = n - 1;
+        }
+    } else if (found == fi) {
+        sh.r_A = fk;
+        sh.r_cut = fi;
+    }
+    __syncthreads();
+    const int at = sh.r_cut;
+    const unsigned long long e = sh.list[at < 0 ? 0 : at];
+    tau = ~static_cast<uint32_t>(e >> 32);
+    cut = static_cast<int32_t>(static_cast<uint32_t>(e));
+    kept = sh.r_A;
+    return fi != 0x7FFFFFFF;
+}
+
 template <int DT>
 __device__ void select_nucleus(const Params& P, const uint8_t* row, float O, double S, SelShared& sh, double& kept,
                                uint32_t& tau, int32_t& cut) {
@@ -870,36 +1083,7 @@ __device__ void select_nucleus(const Params& P, const uint8_t* row, float O, dou
         if (a > -16.f) atomicAdd(&sh.mass[gap_bin(a)], static_cast<double>(hw_exp2(a)));
     });
     __syncthreads();
-    // Crossing bin: the smallest bin whose running mass from bin 0 reaches Tm.
-    {
-        constexpr int PER = kGapBins / kThreads;
-        double tsum = 0.0;
-        for (int i = 0; i < PER; ++i) tsum += sh.mass[tid * PER + i];
-        double incl, excl, total;
-        block_scan(tsum, incl, excl, total);
-        int found = 0x7FFFFFFF;
-        double pre = excl, fpre = 0.0;
-        for (int i = 0; i < PER; ++i) {
-            const int bin = tid * PER + i;
-            const double m = sh.mass[bin];
-            if (found == 0x7FFFFFFF && m > 0.0 && pre + m >= Tm) {
-                found = bin;
-                fpre = pre;
-            }
-            pre += m;
-        }
-        const int fb = block_min_int(found);
-        if (found == fb && fb != 0x7FFFFFFF) {
-            sh.sel_bin = fb;
-            sh.sel_pre = fpre;
-        }
-        if (tid == 0 && fb == 0x7FFFFFFF) {
-            // no bin reaches Tm: the cut lies below every histogrammed key
-            sh.sel_bin = kGapBins;
-            sh.sel_pre = total;
-        }
-        __syncthreads();
-    }
+    find_crossing(sh, Tm);
     uint32_t kin = 0xFFFFFFFFu;  // smallest key within 16 bits (overflow case only)
     if (sh.sel_bin == kGapBins) {
         for_each_vec<DT>(row, V, [&](float l, int64_t) {
@@ -975,63 +1159,7 @@ __device__ void select_nucleus(const Params& P, const uint8_t* row, float O, dou
             collected = false;
             __syncthreads();
             const int n = static_cast<int>(min(sh.nlist, static_cast<uint32_t>(kCollect)));
-            int np2 = 1;
-            while (np2 < n) np2 <<= 1;
-            for (int i = n + tid; i < np2; i += kThreads) sh.list[i] = ~0ull;
-            __syncthreads();
-            // bitonic sort, ascending
-            for (int kk = 2; kk <= np2; kk <<= 1) {
-                for (int jj = kk >> 1; jj > 0; jj >>= 1) {
-                    for (int i = tid; i < np2; i += kThreads) {
-                        const int ij = i ^ jj;
-                        if (ij > i) {
-                            const unsigned long long a = sh.list[i], c = sh.list[ij];
-                            const bool up = (i & kk) == 0;
-                            if ((a > c) == up) {
-                                sh.list[i] = c;
-                                sh.list[ij] = a;
-                            }
-                        }
-                    }
-                    __syncthreads();
-                }
-            }
-            // running mass in sorted order: each thread a run of 8, then a scan
-            const int per = (n + kThreads - 1) / kThreads;
-            const int s0 = tid * per, s1 = min(s0 + per, n);
-            double ts = 0.0;
-            for (int i = s0; i < s1; ++i)
-                ts += static_cast<double>(tempexp(key_value(~static_cast<uint32_t>(sh.list[i] >> 32)), c_hi, c_lo, O));
-            double incl, excl, total;
-            block_scan(ts, incl, excl, total);
-            int found = 0x7FFFFFFF;
-            double fk = 0.0;
-            double run = A + excl;
-            for (int i = s0; i < s1; ++i) {
-                run += static_cast<double>(tempexp(key_value(~static_cast<uint32_t>(sh.list[i] >> 32)), c_hi, c_lo, O));
-                if (run >= Tm) {
-                    found = i;
-                    fk = run;
-                    break;
-                }
-            }
-            const int fi = block_min_int(found);
-            if (fi == 0x7FFFFFFF) {
-                // rounding: no running sum reached Tm; keep the whole interval
-                if (tid == 0) {
-                    sh.r_A = A + total;
-                    sh.r_cut = n - 1;
-                }
-            } else if (found == fi) {
-                sh.r_A = fk;
-                sh.r_cut = fi;
-            }
-            __syncthreads();
-            const int at = sh.r_cut;
-            const unsigned long long e = sh.list[at < 0 ? 0 : at];
-            tau = ~static_cast<uint32_t>(e >> 32);
-            cut = static_cast<int32_t>(static_cast<uint32_t>(e));
-            kept = sh.r_A;
+            (void)sort_walk(sh, n, A, Tm, O, c_hi, c_lo, tau, cut, kept);
             return;
         }
         if (klo == khi) {
@@ -1134,6 +1262,98 @@ __device__ void select_nucleus(const Params& P, const uint8_t* row, float O, dou
     }
 }
 
+// Gap bin of a listed candidate (any finite exponent a = l*c - O): the bins
+// of the row pass below, with everything deeper than 16 bits in the last.
+__device__ __forceinline__ int cand_gap_bin(float a) {
+    return static_cast<int>(fminf(fmaxf(-a * kGapPerBit, 0.f), static_cast<float>(kGapBins - 1)));
+}
+
+// Nucleus cut from the statistics pass's candidate lists, without reading the
+// logit row.  The lists hold, for every chunk, all tokens with a key at or
+// above the chunk's bound; above the largest bound kth the union of the lists
+// is therefore the row's whole set of tokens.  The gap histogram of that set
+// gives the crossing bin; every bin before it lies above kth, and the tokens
+// of the crossing bin missing from the lists (keys below kth) sort after all
+// listed ones, so walking the listed tokens of the crossing bin finds the cut
+// whenever the listed mass reaches top_p * S.  Returns false (block-uniform)
+// when it cannot decide: a chunk's list is incomplete, the listed mass does
+// not reach top_p * S, the crossing bin overflows the sort list, or rounding
+// stops the walk short.
+__device__ bool select_from_candidates(const Params& P, int rvi, uint32_t kth, float O, double S, SelShared& sh,
+                                       double& kept, uint32_t& tau, int32_t& cut) {
+    const int tid = threadIdx.x;
+    const float c_hi = P.c_hi, c_lo = P.c_lo;
+    const double Tm = static_cast<double>(P.top_p) * S;
+    // thread tid reads slot tid of every chunk's list: slot tid & 63 of the
+    // list of statistics wave tid >> 6
+    const uint64_t* hdr = P.chdr + (static_cast<size_t>(rvi) * P.nch * kWaves + (tid >> 6)) * 2;
+    const uint64_t* lst = P.cand + static_cast<size_t>(rvi) * P.nch * kCand;
+    const uint32_t slot = static_cast<uint32_t>(tid & 63);
+    for (int i = tid; i < kGapBins; i += kThreads) sh.mass[i] = 0.0;
+    if (tid == 0) sh.nlist = 0u;
+    __syncthreads();
+    // two passes over the lists: the gap histogram of the listed tokens at
+    // or above kth, then the crossing bin's tokens.  Entry `tid` of
+    // kCandBatch chunks is loaded at once (every list slot is in bounds;
+    // slots past a chunk's count are masked).
+    constexpr int kCandBatch = 8;
+    int sb = 0;
+    double A = 0.0;
+    for (int pass = 0; pass < 2; ++pass) {
+        for (int c0 = 0; c0 < P.nch; c0 += kCandBatch) {
+            unsigned long long e[kCandBatch];
+            uint32_t n[kCandBatch];
+#pragma unroll
+            for (int q = 0; q < kCandBatch; ++q) {
+                const int c = min(c0 + q, P.nch - 1);
+                n[q] = c0 + q < P.nch ? static_cast<uint32_t>(hdr[static_cast<size_t>(c) * kWaves * 2]) : 0u;
+                e[q] = lst[static_cast<size_t>(c) * kCand + tid];
+            }
+#pragma unroll
+            for (int q = 0; q < kCandBatch; ++q) {
+                const uint32_t key = ~static_cast<uint32_t>(e[q] >> 32);
+                if (slot < n[q] && key >= kth) {
+                    const float l = key_value(key);
+                    const float a = fmaf(l, c_lo, fmaf(l, c_hi, -O));
+                    const int bin = cand_gap_bin(a);
+                    if (pass == 0) {
+                        atomicAdd(&sh.mass[bin], static_cast<double>(hw_exp2(a)));
+                    } else if (bin == sb) {
+                        const uint32_t at = atomicAdd(&sh.nlist, 1u);
+                        if (at < static_cast<uint32_t>(kCollect)) sh.list[at] = e[q];
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        if (pass == 0) {
+            find_crossing(sh, Tm);
+            sb = sh.sel_bin;
+            A = sh.sel_pre;
+            if (sb == kGapBins) return false;
+        }
+    }
+    const uint32_t nl = sh.nlist;
+    if (nl > static_cast<uint32_t>(kCollect)) return false;
+    return sort_walk(sh, static_cast<int>(nl), A, Tm, O, c_hi, c_lo, tau, cut, kept);
+}
+
+// Largest candidate key bound of logit row rvi over its chunks, or kNoCover
+// when a chunk's list is incomplete or its header is not this call's.
+__device__ uint32_t candidate_bound(const Params& P, int rvi, int lane) {
+    const uint64_t* hdr = P.chdr + static_cast<size_t>(rvi) * P.nch * kWaves * 2;
+    uint32_t kth = 0u;
+    int bad = 0;
+    for (int c = lane; c < P.nch * kWaves; c += 64) {
+        const uint64_t w0 = hdr[2 * c], w1 = hdr[2 * c + 1];
+        if (!has_tag(w0, P.tag) || !has_tag(w1, P.tag) || static_cast<uint32_t>(w1) == kNoCover) bad = 1;
+        kth = max(kth, static_cast<uint32_t>(w1));
+    }
+    bad = wave_max_int(bad);
+    kth = static_cast<uint32_t>(wave_max_int_dpp(static_cast<int>(kth ^ 0x80000000u))) ^ 0x80000000u;
+    return bad ? kNoCover : kth;
+}
+
 template <int DT>
 __global__ __launch_bounds__(kThreads) void k_topp(Params P) {
     __shared__ SelShared sh;
@@ -1150,6 +1370,7 @@ __global__ __launch_bounds__(kThreads) void k_topp(Params P) {
     const int j = tgt ? slot : slot - P.K - 1;
     if (tgt ? (j > Le) : (j >= Le)) return;
     const uint8_t* row = row_ptr<DT>(P, tgt, b, j);
+    __shared__ uint32_t s_kth;
     if (wv == 0) {
         float O, M, LX;
         double S;
@@ -1161,6 +1382,10 @@ __global__ __launch_bounds__(kThreads) void k_topp(Params P) {
             s_lx = LX;
             s_s = ok ? S : nan64();
         }
+    } else if (wv == 1) {
+        // the candidate headers, in parallel with the combine
+        const uint32_t kth = candidate_bound(P, rvi, lane);
+        if (lane == 0) s_kth = kth;
     }
     __syncthreads();
     const float O = s_o;
@@ -1180,7 +1405,11 @@ __global__ __launch_bounds__(kThreads) void k_topp(Params P) {
         double kept;
         uint32_t tau;
         int32_t cut;
-        select_nucleus<DT>(P, row, O, S, sh, kept, tau, cut);
+        const uint32_t kth = s_kth;
+        if (kth == kNoCover || !select_from_candidates(P, rvi, kth, O, S, sh, kept, tau, cut)) {
+            __syncthreads();
+            select_nucleus<DT>(P, row, O, S, sh, kept, tau, cut);
+        }
         st.kept = kept;
         st.tau = tau;
         st.cut = cut;
@@ -1676,15 +1905,21 @@ static void launch(Kern k, unsigned grid, unsigned block, hipStream_t s, const L
     hipExtLaunchKernelGGL(k, dim3(grid), dim3(block), 0, s, ev.start, ev.stop, 0, p);
 }
 
-hipError_t launch_stats(const Params& p, int dtype, int unroll, hipStream_t s, const LaunchEvents& ev) {
-    const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(p.B) * p.nslot * p.nch);
+template <bool CAND>
+static void launch_stats_c(const Params& p, int dtype, int unroll, unsigned grid, hipStream_t s, const LaunchEvents& ev) {
     if (dtype == DT_BF16) {
-        if (unroll == 8) launch(k_stats<DT_BF16, 8>, grid, kThreads, s, ev, p);
-        else launch(k_stats<DT_BF16, 4>, grid, kThreads, s, ev, p);
+        if (unroll == 8) launch(k_stats<DT_BF16, 8, CAND>, grid, kThreads, s, ev, p);
+        else launch(k_stats<DT_BF16, 4, CAND>, grid, kThreads, s, ev, p);
     } else {
-        if (unroll == 8) launch(k_stats<DT_F32, 8>, grid, kThreads, s, ev, p);
-        else launch(k_stats<DT_F32, 4>, grid, kThreads, s, ev, p);
+        if (unroll == 8) launch(k_stats<DT_F32, 8, CAND>, grid, kThreads, s, ev, p);
+        else launch(k_stats<DT_F32, 4, CAND>, grid, kThreads, s, ev, p);
     }
+}
+
+hipError_t launch_stats(const Params& p, int dtype, int unroll, bool topp, hipStream_t s, const LaunchEvents& ev) {
+    const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(p.B) * p.nslot * p.nch);
+    if (topp) launch_stats_c<true>(p, dtype, unroll, grid, s, ev);
+    else launch_stats_c<false>(p, dtype, unroll, grid, s, ev);
     return hipGetLastError();
 }
 

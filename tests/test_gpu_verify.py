@@ -138,6 +138,48 @@ def test_top_p_coarse_logits_many_ties():
     _parity(inp, label="coarse logits, top_p=0.8")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_top_p_several_chunks(dtype):
+    # V = 40009: three (bf16) or five (fp32) statistics chunks, each listing
+    # its own nucleus candidates
+    inp = W.make_inputs(4, 31, B=6, V=40009, dtype=dtype)
+    _parity(inp, label=f"filtered V=40009 {dtype}")
+
+
+def test_top_p_candidates_skewed_chunks():
+    # row 0 has its largest logits in the first statistics chunk, row 1 in
+    # the last: the chunks' candidate bounds differ widely
+    V = 3 * 16384 + 123
+    inp = W.make_inputs(4, 32, B=4, V=V)
+    t = W.bf16_bits_to_f32(inp.target).copy()
+    d = W.bf16_bits_to_f32(inp.draft).copy()
+    t[0, :, :16384] += 2.5
+    d[0, :, :16384] += 2.5
+    t[1, :, -16000:] += 2.5
+    d[1, :, -16000:] += 2.5
+    inp.target[:] = W.f32_to_bf16_bits(t)
+    inp.draft[:] = W.f32_to_bf16_bits(d)
+    _parity(inp, label="filtered, skewed chunks")
+
+
+def test_top_p_tie_group_larger_than_sort_list():
+    # 600 tokens share the largest logit, 200 in each statistics chunk: every
+    # chunk lists its share, but the cut falls inside a tie group larger than
+    # one sort list holds; the lowest ids of the group are kept
+    V = 3 * 16384
+    rng = np.random.default_rng(17)
+    inp = W.synthetic(3, 2, V, dtype="bf16", temperature=1.0, top_p=0.5, seed=17, gen_seed=17)
+    t = rng.normal(0, 1, size=(3, 3, V)).astype(np.float32)
+    d = (t[:, :2] + rng.normal(0, 0.5, size=(3, 2, V))).astype(np.float32)
+    for c in range(3):
+        ids = c * 16384 + rng.choice(16384, 200, replace=False)
+        t[:, :, ids] = 6.0
+        d[:, :, ids] = 6.0
+    inp.target[:] = W.f32_to_bf16_bits(t)
+    inp.draft[:] = W.f32_to_bf16_bits(d)
+    _parity(inp, label="600-way tie at the top, top_p=0.5")
+
+
 def test_extreme_and_masked_logits():
     inp = W.synthetic(6, 3, 3000, dtype="f32", temperature=0.5, seed=11, gen_seed=11)
     inp.target[0] *= 3000.0            # logits of order 1e4

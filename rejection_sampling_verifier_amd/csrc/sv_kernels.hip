@@ -1297,17 +1297,20 @@ __device__ bool select_from_candidates(const Params& P, int rvi, uint32_t kth, f
     // kCandBatch chunks is loaded at once (every list slot is in bounds;
     // slots past a chunk's count are masked).
     constexpr int kCandBatch = 8;
+    const bool one_batch = P.nch <= kCandBatch;  // then pass 1 reuses pass 0's registers
     int sb = 0;
     double A = 0.0;
+    unsigned long long e[kCandBatch];
+    uint32_t n[kCandBatch];
     for (int pass = 0; pass < 2; ++pass) {
         for (int c0 = 0; c0 < P.nch; c0 += kCandBatch) {
-            unsigned long long e[kCandBatch];
-            uint32_t n[kCandBatch];
+            if (pass == 0 || !one_batch) {
 #pragma unroll
-            for (int q = 0; q < kCandBatch; ++q) {
-                const int c = min(c0 + q, P.nch - 1);
-                n[q] = c0 + q < P.nch ? static_cast<uint32_t>(hdr[static_cast<size_t>(c) * kWaves * 2]) : 0u;
-                e[q] = lst[static_cast<size_t>(c) * kCand + tid];
+                for (int q = 0; q < kCandBatch; ++q) {
+                    const int c = min(c0 + q, P.nch - 1);
+                    n[q] = c0 + q < P.nch ? static_cast<uint32_t>(hdr[static_cast<size_t>(c) * kWaves * 2]) : 0u;
+                    e[q] = lst[static_cast<size_t>(c) * kCand + tid];
+                }
             }
 #pragma unroll
             for (int q = 0; q < kCandBatch; ++q) {
@@ -1512,22 +1515,45 @@ template <int DT> __device__ __forceinline__ void unpack_masked(const uint4* v, 
     for (int i = 0; i < kRun; ++i) f[i] = id0 + i < V ? f[i] : -SV_INF;
 }
 
+// The nucleus test on the logit itself: key(l) > tau, or key(l) == tau with
+// id <= cut, is l > tv, or l == tv with id <= cut, for tv the logit of key
+// tau (order keys are monotone in the value, -0 and +0 sharing one).  tau = 0
+// (every token kept) maps to tv = -inf: every finite logit passes and -inf
+// tokens carry no mass either way.
+__device__ __forceinline__ float kept_bound(uint32_t tau) { return tau == 0u ? -SV_INF : key_value(tau); }
+__device__ __forceinline__ bool kept_l(float l, float tv, int64_t id, int32_t cut) {
+    return l > tv || (l == tv && id <= cut);
+}
+
 // Residual weights w = max(0, p' - q') (or p' for the bonus) and p' of a run.
+// With top-p both are 0 wherever the target token is outside its nucleus.
 template <bool TOPP>
 __device__ __forceinline__ void run_weights(const float* lt, const float* ld, bool resid, int64_t id0, const RowParam& rp,
                                             float c_hi, float c_lo, float invT, float invD, float* w, float* p) {
+    const float tvT = TOPP ? kept_bound(rp.tauT) : 0.f;
+    const float tvD = TOPP ? kept_bound(rp.tauD) : 0.f;
 #pragma unroll
     for (int i = 0; i < kRun; ++i) {
-        float pt = tempexp(lt[i], c_hi, c_lo, rp.oT) * invT;
-        if (TOPP && !is_kept(order_key(lt[i]), id0 + i, rp.tauT, rp.cutT)) pt = 0.f;
-        float wi = pt;
-        if (resid) {
-            float qd = tempexp(ld[i], c_hi, c_lo, rp.oD) * invD;
-            if (TOPP && !is_kept(order_key(ld[i]), id0 + i, rp.tauD, rp.cutD)) qd = 0.f;
-            wi = fmaxf(pt - qd, 0.f);
+        if (TOPP) {
+            const bool kt = kept_l(lt[i], tvT, id0 + i, rp.cutT);
+            const float pt = kt ? tempexp(lt[i], c_hi, c_lo, rp.oT) * invT : 0.f;
+            float wi = pt;
+            if (resid) {
+                const float qd = kept_l(ld[i], tvD, id0 + i, rp.cutD) ? tempexp(ld[i], c_hi, c_lo, rp.oD) * invD : 0.f;
+                wi = fmaxf(pt - qd, 0.f);
+            }
+            w[i] = wi;
+            p[i] = pt;
+        } else {
+            const float pt = tempexp(lt[i], c_hi, c_lo, rp.oT) * invT;
+            float wi = pt;
+            if (resid) {
+                const float qd = tempexp(ld[i], c_hi, c_lo, rp.oD) * invD;
+                wi = fmaxf(pt - qd, 0.f);
+            }
+            w[i] = wi;
+            p[i] = pt;
         }
-        w[i] = wi;
-        p[i] = pt;
     }
 }
 

@@ -24,19 +24,16 @@ using sv::Params;
 struct Scratch {
     void* ptr = nullptr;       // records and per-row state; zeroed when allocated
     size_t bytes = 0;
-    uint32_t* counters = nullptr;  // arrival counters: zeroed once, left at zero by every call
-    int64_t counter_rows = 0;
 };
 
 struct Layout {
-    size_t prec, rv, rowp, qrec, chdr, cand, total;
+    size_t prec, rv, qrec, chdr, cand, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-// Tagged records (statistics per chunk, masses per resample item) are left
-// at zero by every call that completes; RvState and RowParam are rewritten
-// before they are read.  The top-p candidate headers and lists (present only
+// Tagged records (statistics per chunk, masses per resample item) carry the
+// call's tag; RvState is rewritten before it is read.  The top-p candidate headers and lists (present only
 // when `topp`) are rewritten by the statistics pass of every top-p call.
 Layout layout(int64_t B, int nslot, int nch, int nq, bool topp) {
     Layout L;
@@ -45,8 +42,6 @@ Layout layout(int64_t B, int nslot, int nch, int nq, bool topp) {
     off = align256(off + static_cast<size_t>(B) * nslot * nch * sv::kRecWords * sizeof(uint64_t));
     L.rv = off;
     off = align256(off + static_cast<size_t>(B) * nslot * sizeof(sv::RvState));
-    L.rowp = off;
-    off = align256(off + static_cast<size_t>(B) * sizeof(sv::RowParam));
     L.qrec = off;
     off = align256(off + static_cast<size_t>(B) * nq * sv::kRecWords * sizeof(uint64_t));
     const size_t chunks = topp ? static_cast<size_t>(B) * nslot * nch : 0;
@@ -115,18 +110,15 @@ int check_logits(const sv_logits* t) {
     return SV_OK;
 }
 
-// Returns the scratch for (device, stream), growing it when needed.  Both
-// allocations are zeroed when made; the arrival counters (one per batch row,
-// at fixed offsets) and the tagged records are left at zero by every call.
-int get_scratch(hipStream_t stream, size_t bytes, int64_t rows, void** data, uint32_t** counters) {
+// Returns the scratch for (device, stream), growing it (zeroed) when needed.
+int get_scratch(hipStream_t stream, size_t bytes, void** data) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     std::lock_guard<std::mutex> lk(g_mu);
     Scratch& s = g_scratch[{dev, stream}];
     const bool grow_data = s.bytes < bytes;
-    const bool grow_cnt = s.counter_rows < rows;
-    if ((grow_data && s.ptr) || (grow_cnt && s.counters)) {
+    if (grow_data && s.ptr) {
         e = hipStreamSynchronize(stream);
         if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
     }
@@ -149,28 +141,7 @@ int get_scratch(hipStream_t stream, size_t bytes, int64_t rows, void** data, uin
         s.ptr = p;
         s.bytes = want;
     }
-    if (grow_cnt) {
-        if (s.counters) (void)hipFree(s.counters);
-        s.counters = nullptr;
-        s.counter_rows = 0;
-        const int64_t want = rows < 64 ? 64 : rows * 2;
-        void* p = nullptr;
-        const size_t nb = static_cast<size_t>(want) * 2 * sv::kCounterStride * sizeof(uint32_t);
-        e = hipMalloc(&p, nb);
-        if (e != hipSuccess) {
-            (void)hipGetLastError();
-            return SV_ENOMEM;
-        }
-        e = hipMemsetAsync(p, 0, nb, stream);
-        if (e != hipSuccess) {
-            (void)hipFree(p);
-            return hip_fail(e, "hipMemsetAsync");
-        }
-        s.counters = static_cast<uint32_t*>(p);
-        s.counter_rows = want;
-    }
     *data = s.ptr;
-    *counters = s.counters;
     return SV_OK;
 }
 
@@ -242,8 +213,7 @@ int verify_impl(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_t
     const bool topp = top_p < 1.f;
     const Layout lay = layout(B, nslot, nch, nq, topp);
     void* scratch = nullptr;
-    uint32_t* counters = nullptr;
-    rc = get_scratch(stream, lay.total, B, &scratch, &counters);
+    rc = get_scratch(stream, lay.total, &scratch);
     if (rc) return rc;
     uint8_t* base = static_cast<uint8_t*>(scratch);
 
@@ -284,11 +254,9 @@ int verify_impl(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_t
     p.key1 = static_cast<uint32_t>(seed >> 32);
     p.prec = reinterpret_cast<uint64_t*>(base + lay.prec);
     p.rv = reinterpret_cast<sv::RvState*>(base + lay.rv);
-    p.rowp = reinterpret_cast<sv::RowParam*>(base + lay.rowp);
     p.qrec = reinterpret_cast<uint64_t*>(base + lay.qrec);
     p.chdr = topp ? reinterpret_cast<uint64_t*>(base + lay.chdr) : nullptr;
     p.cand = topp ? reinterpret_cast<uint64_t*>(base + lay.cand) : nullptr;
-    p.row_cnt = counters;
 
     rc = timed_launch(sv::KK_STATS, stream, [&](const sv::LaunchEvents& ev) {
         return sv::launch_stats(p, dtype, unroll, topp, stream, ev);
@@ -341,7 +309,6 @@ void spec_verify_release(void) {
     std::lock_guard<std::mutex> lk(g_mu);
     for (auto& kv : g_scratch) {
         if (kv.second.ptr) (void)hipFree(kv.second.ptr);
-        if (kv.second.counters) (void)hipFree(kv.second.counters);
     }
     g_scratch.clear();
 }

@@ -86,14 +86,10 @@ struct Params {
     uint32_t key0, key1;          // Philox key
     uint64_t* prec;               // [B, nslot, nch] tagged statistics records
     RvState* rv;                  // [B, nslot]
-    RowParam* rowp;               // [B]
     uint64_t* qrec;               // [B, nq] tagged resample-item mass records
     uint64_t* chdr;               // top-p: [B, nslot, nch, kWaves, 2] tagged candidate headers (count, key bound)
     uint64_t* cand;               // top-p: [B, nslot, nch, kCand] candidates (~key << 32 | id), kCand/kWaves per wave
-    uint32_t* row_cnt;            // [B] arrival counters, kCounterStride words apart, zero between calls
 };
-
-constexpr int kCounterStride = 16;  // one 64-byte line per counter
 
 // Timing events of one launch (both null when timing is off).
 struct LaunchEvents {

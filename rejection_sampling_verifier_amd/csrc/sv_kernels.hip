@@ -20,20 +20,19 @@
 //               above which the list is complete.
 //   k_topp      (top-p only) one workgroup per logit row: exact nucleus cut
 //               (value key tau, tie cut by id, kept mass), from the candidate
-//               lists when they reach it, else from passes over the row; the
-//               last logit row of a batch row makes the decision.
+//               lists when they reach it, else from passes over the row.
 //   k_rows      one workgroup per (row b, item of V): combines the row's
-//               partials and makes the decision (without top-p: every item
-//               alike), then computes the residual or bonus weights of its
-//               ids, exchanges item masses through tagged records and lets
-//               the item holding u*Z pick the token by an in-order scan.
+//               partials (or, with top-p, its nucleus states) and makes the
+//               decision (every item alike), then computes the residual or
+//               bonus weights of its ids, exchanges item masses through
+//               tagged records and lets the item holding u*Z pick the token
+//               by an in-order scan.
 //
-// Hand-offs between workgroups use tagged 64-bit records: an aligned 64-bit
-// store is single-copy atomic, so a producer stores and exits, and a consumer
-// polls (bounded) until every word carries the call's tag.  Across a kernel
-// boundary plain loads suffice.  Only the top-p decision uses a counter (the
-// last logit row of a batch row to finish decides).  Everything that streams V
-// is bandwidth-bound (no dense contraction, so no MFMA).
+// Hand-offs between workgroups of one kernel use tagged 64-bit records: an
+// aligned 64-bit store is single-copy atomic, so a producer stores and exits,
+// and a consumer polls (bounded) until every word carries the call's tag.
+// Across a kernel boundary plain loads suffice.  Everything that streams V is
+// bandwidth-bound (no dense contraction, so no MFMA).
 
 #include <hip/hip_ext.h>
 
@@ -95,22 +94,6 @@ __device__ __forceinline__ void st_agent(void* p, uint64_t v) {
 __device__ __forceinline__ uint64_t ld_agent(const void* p) {
     return __hip_atomic_load(reinterpret_cast<uint64_t*>(const_cast<void*>(p)), __ATOMIC_RELAXED,
                              __HIP_MEMORY_SCOPE_AGENT);
-}
-// Waits until this thread's earlier stores have completed (vmcnt(0)); the
-// compiler may not move memory operations across it.
-__device__ __forceinline__ void stores_done() {
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0x0F70);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-// Counts one arrival; true for the arrival that completes `need`.
-__device__ __forceinline__ bool arrive_last(uint32_t* cnt, uint32_t need) {
-    const uint32_t old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    return old + 1u == need;
-}
-__device__ __forceinline__ void counter_reset(uint32_t* cnt) {
-    __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ uint64_t pack2(float a, float b) {
     return static_cast<uint64_t>(__float_as_uint(a)) | (static_cast<uint64_t>(__float_as_uint(b)) << 32);
@@ -1417,23 +1400,7 @@ __global__ __launch_bounds__(kThreads) void k_topp(Params P) {
         st.tau = tau;
         st.cut = cut;
     }
-    if (wv != 0) return;
-    int last = 0;
-    if (lane == 0) {
-        store_rvstate(P.rv + rvi, st);
-        stores_done();
-        last = arrive_last(P.row_cnt + static_cast<size_t>(b) * kCounterStride, static_cast<uint32_t>(2 * Le + 1)) ? 1 : 0;
-    }
-    last = __shfl(last, 0, 64);
-    if (!last) return;
-    if (lane == 0) counter_reset(P.row_cnt + static_cast<size_t>(b) * kCounterStride);
-    bool rowok2;
-    const int Le2 = row_len(P, b, rowok2);
-    const int x = lane_token(P, b, Le2);
-    fill_row_from_rv(P, b, Le2, R);
-    RowParam rp;
-    decide_row<true>(P, b, Le2, rowok2, R, true, x, rp);
-    if (lane == 0) P.rowp[b] = rp;
+    if (tid == 0) store_rvstate(P.rv + rvi, st);
 }
 
 // ---------------------------------------------------------------------------
@@ -1521,7 +1488,7 @@ template <int DT> __device__ __forceinline__ void unpack_masked(const uint4* v, 
 // (every token kept) maps to tv = -inf: every finite logit passes and -inf
 // tokens carry no mass either way.
 __device__ __forceinline__ float kept_bound(uint32_t tau) { return tau == 0u ? -SV_INF : key_value(tau); }
-__device__ __forceinline__ bool kept_l(float l, float tv, int64_t id, int32_t cut) {
+__device__ __forceinline__ bool kept_l(float l, float tv, int id, int32_t cut) {
     return l > tv || (l == tv && id <= cut);
 }
 
@@ -1532,14 +1499,15 @@ __device__ __forceinline__ void run_weights(const float* lt, const float* ld, bo
                                             float c_hi, float c_lo, float invT, float invD, float* w, float* p) {
     const float tvT = TOPP ? kept_bound(rp.tauT) : 0.f;
     const float tvD = TOPP ? kept_bound(rp.tauD) : 0.f;
+    const int i0 = static_cast<int>(id0);  // ids < 2^24
 #pragma unroll
     for (int i = 0; i < kRun; ++i) {
         if (TOPP) {
-            const bool kt = kept_l(lt[i], tvT, id0 + i, rp.cutT);
+            const bool kt = kept_l(lt[i], tvT, i0 + i, rp.cutT);
             const float pt = kt ? tempexp(lt[i], c_hi, c_lo, rp.oT) * invT : 0.f;
             float wi = pt;
             if (resid) {
-                const float qd = kept_l(ld[i], tvD, id0 + i, rp.cutD) ? tempexp(ld[i], c_hi, c_lo, rp.oD) * invD : 0.f;
+                const float qd = kept_l(ld[i], tvD, i0 + i, rp.cutD) ? tempexp(ld[i], c_hi, c_lo, rp.oD) * invD : 0.f;
                 wi = fmaxf(pt - qd, 0.f);
             }
             w[i] = wi;
@@ -1861,32 +1829,32 @@ __device__ __forceinline__ void resample_item(const Params& P, int b, int r, con
     else resample_body<DT, TOPP, false, R>(P, b, r, rp, rn);
 }
 
-// Row pass: one workgroup per (b, item).  With top-p the decision was made by
-// the nucleus pass; without, every item makes it from the statistics records
-// (the statistics kernel has finished, so no record is waited for).
+// Row pass: one workgroup per (b, item).  Every item makes the row's decision
+// from the statistics records (without top-p) or the nucleus pass's row
+// states (with top-p): the kernels before have finished, so nothing is
+// waited for; all items reach the same decision and item 0 writes it out.
 template <int DT, bool TOPP, int R>
 __global__ __launch_bounds__(kThreads) void k_rows(Params P) {
     __shared__ RowShared RS;
     __shared__ RowParam s_rp;
     const int b = blockIdx.x / P.nq;
     const int r = blockIdx.x - b * P.nq;
+    bool rowok;
+    const int Le = row_len(P, b, rowok);
+    const int x = lane_token(P, b, Le);
     if (TOPP) {
-        const RowParam rp = P.rowp[b];
-        resample_item<DT, true, R>(P, b, r, rp);
+        if ((threadIdx.x >> 6) == 0) fill_row_from_rv(P, b, Le, RS);
     } else {
-        bool rowok;
-        const int Le = row_len(P, b, rowok);
-        const int x = lane_token(P, b, Le);
         fill_row_from_partials(P, b, Le, RS);
-        if ((threadIdx.x >> 6) == 0) {
-            RowParam rp;
-            decide_row<false>(P, b, Le, rowok, RS, r == 0, x, rp);
-            if ((threadIdx.x & 63) == 0) s_rp = rp;
-        }
-        __syncthreads();
-        const RowParam rp = s_rp;
-        resample_item<DT, false, R>(P, b, r, rp);
     }
+    if ((threadIdx.x >> 6) == 0) {
+        RowParam rp;
+        decide_row<TOPP>(P, b, Le, rowok, RS, r == 0, x, rp);
+        if ((threadIdx.x & 63) == 0) s_rp = rp;
+    }
+    __syncthreads();
+    const RowParam rp = s_rp;
+    resample_item<DT, TOPP, R>(P, b, r, rp);
 }
 
 // ---------------------------------------------------------------------------

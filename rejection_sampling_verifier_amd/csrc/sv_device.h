@@ -52,6 +52,11 @@ __device__ __forceinline__ uint4 gload16(const uint4* p) {
     const sv_u32x4 v = *(sv_g_u32x4*)(p);
     return make_uint4(v.x, v.y, v.z, v.w);
 }
+// The same with the nontemporal hint (data read once).
+__device__ __forceinline__ uint4 gload16_nt(const uint4* p) {
+    const sv_u32x4 v = __builtin_nontemporal_load((sv_g_u32x4*)(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 template <int DT> __device__ __forceinline__ float load_elem(const uint8_t* row, int64_t i);
 template <> __device__ __forceinline__ float load_elem<DT_F32>(const uint8_t* row, int64_t i) {

@@ -704,8 +704,9 @@ __device__ __forceinline__ void stats_item(const Params& P, int b, int slot, int
     constexpr int64_t STEP = static_cast<int64_t>(kThreads) * U;
     uint4 raw[U];
     if (k0 + STEP <= k1) {
+        // streamed once: nontemporal loads
 #pragma unroll
-        for (int u = 0; u < U; ++u) raw[u] = gload16(g.vp + k0 + u * kThreads + tid);
+        for (int u = 0; u < U; ++u) raw[u] = gload16_nt(g.vp + k0 + u * kThreads + tid);
     } else {
         const uint32_t ni = Fmt<DT>::NEG_INF_WORD;
 #pragma unroll
@@ -1860,7 +1861,7 @@ __global__ __launch_bounds__(kThreads) void k_rows(Params P) {
 // ---------------------------------------------------------------------------
 // Streaming-read calibration: every 16-byte vector of a buffer read once with
 // the statistics pass's access pattern (one workgroup per kThreads*U
-// vectors), folded into an xor that is stored only if it matches a value it
+// vectors, nontemporal loads), folded into an xor that is stored only if it matches a value it
 // practically never takes -- enough to keep the loads alive.
 // ---------------------------------------------------------------------------
 template <int U>
@@ -1870,7 +1871,7 @@ __global__ __launch_bounds__(kThreads) void k_stream_read(const uint4* p, int64_
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         const int64_t k = base + u * kThreads + threadIdx.x;
-        v[u] = k < n16 ? gload16(p + k) : make_uint4(0u, 0u, 0u, 0u);
+        v[u] = k < n16 ? gload16_nt(p + k) : make_uint4(0u, 0u, 0u, 0u);
     }
     uint32_t acc = 0u;
 #pragma unroll

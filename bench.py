@@ -107,9 +107,13 @@ def cpu_baseline(sets, budget_rows, workload_name):
 CALIB_BYTES = 512 << 20
 
 
-def calibrate(binding, torch, dev):
+def calibrate(binding, torch, dev, logical):
     """A device-to-device copy (reads and writes CALIB_BYTES) and the
-    streaming-read kernel (reads CALIB_BYTES), 3 launches each."""
+    streaming-read kernel (reads CALIB_BYTES), 3 launches each: the
+    references that scale byte counters.  Then the streaming-read ceiling
+    for the statistics pass's own byte count: the streaming-read kernel with
+    its access pattern (8 vectors per lane) over three rotated buffers of
+    `logical` bytes, timed with events."""
     src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device=dev)
     src.fill_(7)
     dst = torch.empty_like(src)
@@ -121,6 +125,24 @@ def calibrate(binding, torch, dev):
         binding.stream_read(src, sink, 4)
     torch.cuda.synchronize()
     print(f"[bench] calibration: 3 copies and 3 streaming reads of {CALIB_BYTES} bytes", file=sys.stderr, flush=True)
+    del src, dst
+    nbytes = int(logical) // 16 * 16
+    bufs = [torch.full((nbytes,), 3, dtype=torch.uint8, device=dev) for _ in range(N_SETS)]
+    stream = torch.cuda.current_stream(dev)
+    for i in range(300):
+        binding.stream_read(bufs[i % N_SETS], sink, 8, stream=stream)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    reps = 600
+    e0.record(stream)
+    for i in range(reps):
+        binding.stream_read(bufs[i % N_SETS], sink, 8, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / reps * 1e3
+    print(f"[bench] streaming read of {nbytes} bytes: {us:.2f} us", file=sys.stderr, flush=True)
+    return {"stream_read_bytes": nbytes, "stream_read_us": round(us, 3),
+            "stream_read_GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
 
 
 # ---------------------------------------------------------------------------
@@ -233,8 +255,10 @@ def main():
         "algorithmic_bytes_per_launch": logical,
     }
 
+    calib = None
     if args.calibrate:
-        calibrate(binding, torch, dev)
+        calib = calibrate(binding, torch, dev, logical)
+        roofline["frac_of_stream_read"] = round(calib["stream_read_us"] / (stats_avg_s * 1e6), 4)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -269,6 +293,7 @@ def main():
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
+        **({"calibration": calib} if calib else {}),
     }
     print(json.dumps(line), flush=True)
 

@@ -17,9 +17,12 @@ Modules:
   philox  -- Philox4x32-10 counter-based generator (Salmon et al., SC'11).
   verify  -- softmax, nucleus filter, accept/first-reject scan, residual and
              bonus inverse-CDF sample, decision margins.
+  smc     -- one SMC-SD step: importance log-weights from target and draft
+             probabilities, bonus draw, ESS and systematic resampling.
 """
 
 from .philox import philox4x32_10, uniforms  # noqa: F401
+from .smc import SmcResult, ess, log_weight_increment, smc_step, systematic, systematic_uniform  # noqa: F401
 from .verify import (  # noqa: F401
     FLAG_BAND,
     OracleResult,

@@ -138,6 +138,50 @@ int spec_verify_probe(const sv_logits* target_logits, const sv_logits* draft_log
                       int32_t* out_tokens, int32_t* out_n_accepted,
                       double* probe_pos, double* probe_row, void* stream);
 
+/*
+ * spec_smc_step -- one reweight-and-resample step of SMC-SD over N particles
+ * (page "Faster LLM Inference via Sequential Monte Carlo", section 2: every
+ * particle is extended by K draft tokens and scored by the target, which also
+ * yields one bonus token per particle; importance weights follow the ratio of
+ * target to draft probabilities; when the effective sample size falls below a
+ * threshold the particles are resampled).
+ *
+ * target_logits   [N, K+1, V] target logits, bf16 or fp32 (B of the
+ *                 descriptor = N particles).
+ * draft_logits    [N, K, V] draft logits, same dtype, N and V; 1 <= K <= 16.
+ * draft_tokens    device int32 [N, K], contiguous: each particle's K drafted ids.
+ * logw_in         device float64 [N]: log-weights before the step (any
+ *                 common offset; -inf marks a dead particle).
+ * temperature     > 0, finite; divides both models' logits (no top-p).
+ * ess_fraction    resample when ESS < ess_fraction * N (0.5 is the usual
+ *                 choice; <= 0 never, > 1 always resamples); not NaN.
+ * seed            64-bit Philox key.  Bonus draw of particle i: word 1 of
+ *                 counter (i, K, 0, 0), as the verify step's bonus; systematic
+ *                 resampling offset u0: word 0 of counter (0, 0, 1, 0).
+ * out_bonus       device int32 [N]: the bonus token drawn from the target at
+ *                 position K by inverse CDF; -1 for an invalid particle.
+ * out_logw        device float64 [N]: logw_in + sum_j (log p_j(x_j) -
+ *                 log q_j(x_j)); all 0 after a resampling; -inf for an invalid
+ *                 particle.  May be the same buffer as logw_in.
+ * out_ancestor    device int32 [N]: the particle that slot k continues (k
+ *                 itself without resampling; systematic: the first particle
+ *                 whose cumulative normalised weight exceeds (k + u0)/N).
+ * out_ess         device float64 [1]: (sum w)^2 / sum w^2 before resampling,
+ *                 w = exp(logw - max); 0 when no particle is valid.
+ * out_resampled   device int32 [1]: 1 if the step resampled.
+ * stream          hipStream_t to run on (NULL = the default stream).
+ *
+ * A particle is invalid when a drafted id lies outside [0, V), a needed logit
+ * row holds a NaN, a +inf or only -inf, or its input log-weight is NaN or
+ * +inf; it never becomes an ancestor.  Host-checkable errors return
+ * SV_EINVAL / SV_ESHAPE / SV_EDTYPE / SV_EALIGN and launch nothing.
+ */
+int spec_smc_step(const sv_logits* target_logits, const sv_logits* draft_logits,
+                  const int32_t* draft_tokens, const double* logw_in,
+                  float temperature, double ess_fraction, uint64_t seed,
+                  int32_t* out_bonus, double* out_logw, int32_t* out_ancestor,
+                  double* out_ess, int32_t* out_resampled, void* stream);
+
 /* Human-readable text for a status code (for SV_EHIP, the last HIP error). */
 const char* spec_verify_strerror(int status);
 
@@ -152,9 +196,10 @@ int spec_verify_abi_version(void);
  * of HIP events on its stream, attached to the kernel's dispatch.
  * spec_verify_profile_read synchronises those events and writes, for each of
  * the n kernel kinds (0 statistics pass, 1 nucleus selection, 2 row pass:
- * the decision when top-p is off, and the resample), the summed duration in
- * milliseconds and the number of launches since the last read; it returns
- * the number of kinds written.  Host arrays ms[n], launches[n]. */
+ * decision and resample, or the SMC particle pass, 3 SMC resampling), the
+ * summed duration in milliseconds and the number of launches since the last
+ * read; it returns the number of kinds written.  Host arrays ms[n],
+ * launches[n]. */
 int spec_verify_profile_enable(int enable);
 int spec_verify_profile_read(double* ms, int64_t* launches, int n);
 

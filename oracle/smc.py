@@ -97,6 +97,9 @@ class SmcResult:
     min_margin: float        # smallest decision margin of the step
     n_decisions: int
     n_flagged: int
+    bonus_margin: np.ndarray = None  # [N] margin of each bonus draw (inf if invalid)
+    ess_margin: float = np.inf       # |ESS - ess_fraction * N| / N
+    resample_margin: float = np.inf  # smallest point-to-boundary distance when resampling
 
     @property
     def flagged(self):
@@ -120,6 +123,8 @@ def smc_step(target, draft, draft_tokens, logw_in, temperature, ess_fraction, se
     bonus = np.full(N, -1, dtype=np.int64)
     inc = np.full(N, np.nan)
     lw = np.full(N, -np.inf)
+    bm = np.full(N, np.inf)
+    em, rm = np.inf, np.inf
     margins = []
     for i in range(N):
         x = tok[i]
@@ -134,17 +139,19 @@ def smc_step(target, draft, draft_tokens, logw_in, temperature, ess_fraction, se
         _, u_res = uniforms(seed, i, K)
         y, _, _, m = inverse_cdf(p[K], u_res)
         bonus[i] = y
+        bm[i] = m
         margins.append(m)
     e = ess(lw)
     resampled = False
     anc = np.arange(N, dtype=np.int64)
     if e > 0.0:
-        margins.append(abs(e - ess_fraction * N) / N)
+        em = abs(e - ess_fraction * N) / N
+        margins.append(em)
         if e < ess_fraction * N:
             resampled = True
-            anc, m = systematic(lw, systematic_uniform(seed))
-            margins.append(m)
+            anc, rm = systematic(lw, systematic_uniform(seed))
+            margins.append(rm)
             lw = np.zeros(N)
     mm = min(margins) if margins else np.inf
     return SmcResult(bonus, lw, inc, anc, e, resampled, mm, len(margins),
-                     sum(1 for m in margins if m < FLAG_BAND))
+                     sum(1 for m in margins if m < FLAG_BAND), bm, em, rm)

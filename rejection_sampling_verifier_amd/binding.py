@@ -18,9 +18,9 @@ SV_F32, SV_BF16 = 0, 1
 PROBE_POS, PROBE_ROW = 8, 4
 STATUS = {0: "SV_OK", -1: "SV_EINVAL", -2: "SV_ESHAPE", -3: "SV_EDTYPE", -4: "SV_EHIP", -5: "SV_ENOMEM",
           -6: "SV_EALIGN"}
-KERNEL_KINDS = ("stats", "topp", "rows")
+KERNEL_KINDS = ("stats", "topp", "rows", "smc")
 
-EXPORTS = ("spec_verify", "spec_verify_probe", "spec_verify_strerror", "spec_verify_release",
+EXPORTS = ("spec_verify", "spec_verify_probe", "spec_smc_step", "spec_verify_strerror", "spec_verify_release",
            "spec_verify_abi_version", "spec_verify_profile_enable", "spec_verify_profile_read",
            "spec_verify_stream_read")
 
@@ -60,6 +60,9 @@ def load(path=LIB_PATH):
     lib.spec_verify.restype = ctypes.c_int
     lib.spec_verify_probe.argtypes = lib.spec_verify.argtypes[:9] + [ctypes.c_void_p] * 3
     lib.spec_verify_probe.restype = ctypes.c_int
+    lib.spec_smc_step.argtypes = [P(SvLogits), P(SvLogits), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,
+                                  ctypes.c_double, ctypes.c_uint64] + [ctypes.c_void_p] * 6
+    lib.spec_smc_step.restype = ctypes.c_int
     lib.spec_verify_strerror.argtypes = [ctypes.c_int]
     lib.spec_verify_strerror.restype = ctypes.c_char_p
     lib.spec_verify_release.argtypes = []
@@ -136,6 +139,40 @@ def verify(target, draft, draft_tokens, draft_len=None, temperature=1.0, top_p=1
         return out_tokens, out_n_accepted, pp, pr
     _check(lib, lib.spec_verify(*args, sh))
     return out_tokens, out_n_accepted
+
+
+def smc_step(target, draft, draft_tokens, logw_in, temperature=1.0, ess_fraction=0.5, seed=0, *, stream=None,
+             out_bonus=None, out_logw=None, out_ancestor=None):
+    """One SMC-SD reweight-and-resample step on device tensors.
+
+    target [N, K+1, V], draft [N, K, V]: bfloat16 or float32, V contiguous;
+    draft_tokens [N, K] int32 contiguous; logw_in [N] float64 contiguous.
+    Returns (bonus [N] int32, logw [N] float64, ancestor [N] int32,
+    ess [1] float64, resampled [1] int32), all on the device.
+    """
+    lib = load()
+    if draft_tokens.dtype != torch.int32 or not draft_tokens.is_contiguous():
+        raise ValueError("draft_tokens must be contiguous int32")
+    if logw_in.dtype != torch.float64 or not logw_in.is_contiguous():
+        raise ValueError("logw_in must be contiguous float64")
+    dev = target.device
+    N = target.shape[0]
+    if out_bonus is None:
+        out_bonus = torch.empty((N,), dtype=torch.int32, device=dev)
+    if out_logw is None:
+        out_logw = torch.empty((N,), dtype=torch.float64, device=dev)
+    if out_ancestor is None:
+        out_ancestor = torch.empty((N,), dtype=torch.int32, device=dev)
+    ess = torch.empty((1,), dtype=torch.float64, device=dev)
+    resampled = torch.empty((1,), dtype=torch.int32, device=dev)
+    td, dd = _desc(target, "target"), _desc(draft, "draft")
+    _check(lib, lib.spec_smc_step(ctypes.byref(td), ctypes.byref(dd), ctypes.c_void_p(draft_tokens.data_ptr()),
+                                  ctypes.c_void_p(logw_in.data_ptr()), ctypes.c_float(temperature),
+                                  ctypes.c_double(ess_fraction), ctypes.c_uint64(int(seed) & (2 ** 64 - 1)),
+                                  ctypes.c_void_p(out_bonus.data_ptr()), ctypes.c_void_p(out_logw.data_ptr()),
+                                  ctypes.c_void_p(out_ancestor.data_ptr()), ctypes.c_void_p(ess.data_ptr()),
+                                  ctypes.c_void_p(resampled.data_ptr()), _stream_handle(stream, dev)))
+    return out_bonus, out_logw, out_ancestor, ess, resampled
 
 
 def profile_enable(on=True):

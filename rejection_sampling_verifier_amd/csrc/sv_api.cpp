@@ -27,7 +27,7 @@ struct Scratch {
 };
 
 struct Layout {
-    size_t prec, rv, qrec, chdr, cand, total;
+    size_t prec, rv, qrec, chdr, cand, cum, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -35,7 +35,7 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 // Tagged records (statistics per chunk, masses per resample item) carry the
 // call's tag; RvState is rewritten before it is read.  The top-p candidate headers and lists (present only
 // when `topp`) are rewritten by the statistics pass of every top-p call.
-Layout layout(int64_t B, int nslot, int nch, int nq, bool topp) {
+Layout layout(int64_t B, int nslot, int nch, int nq, bool topp, bool smc) {
     Layout L;
     size_t off = 0;
     L.prec = off;
@@ -49,6 +49,8 @@ Layout layout(int64_t B, int nslot, int nch, int nq, bool topp) {
     off = align256(off + chunks * sv::kWaves * 2 * sizeof(uint64_t));
     L.cand = off;
     off = align256(off + chunks * sv::kCand * sizeof(uint64_t));
+    L.cum = off;
+    off = align256(off + (smc ? static_cast<size_t>(B) * sizeof(double) : 0));
     L.total = off;
     return L;
 }
@@ -161,17 +163,25 @@ int timed_launch(int kind, hipStream_t stream, F&& launch) {
     return SV_OK;
 }
 
-int verify_impl(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_tokens, const int32_t* draft_len,
-                float temperature, float top_p, uint64_t seed, int32_t* out_tokens, int32_t* out_n,
-                double* probe_pos, double* probe_row, void* stream_v) {
+// What every entry point shares: argument checks, chunking, scratch and the
+// kernel parameters.  `smc`: an SMC-SD step (no draft lengths, no top-p, the
+// resampling kernel's scratch).
+struct Setup {
+    Params p;
+    int dtype = 0;
+    int unroll = 0;
+    bool topp = false;
+    hipStream_t stream = nullptr;
+};
+
+int prepare(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_tokens, const int32_t* draft_len,
+            float temperature, float top_p, uint64_t seed, bool smc, void* stream_v, Setup& S) {
     int rc = check_logits(tl);
     if (rc) return rc;
     rc = check_logits(dl);
     if (rc) return rc;
-    if (!draft_tokens || !out_tokens || !out_n) return SV_EINVAL;
-    if (misaligned(draft_tokens, 4) || misaligned(out_tokens, 4) || misaligned(out_n, 4) ||
-        (draft_len && misaligned(draft_len, 4)))
-        return SV_EALIGN;
+    if (!draft_tokens) return SV_EINVAL;
+    if (misaligned(draft_tokens, 4) || (draft_len && misaligned(draft_len, 4))) return SV_EALIGN;
     if (tl->dtype != dl->dtype) return SV_EDTYPE;
     const int B = tl->B, V = tl->V, K = tl->P - 1;
     if (B <= 0 || V <= 0 || K < 1 || K > SPECVERIFY_MAX_K) return SV_ESHAPE;
@@ -211,13 +221,13 @@ int verify_impl(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_t
 
     hipStream_t stream = static_cast<hipStream_t>(stream_v);
     const bool topp = top_p < 1.f;
-    const Layout lay = layout(B, nslot, nch, nq, topp);
+    const Layout lay = layout(B, nslot, nch, nq, topp, smc);
     void* scratch = nullptr;
     rc = get_scratch(stream, lay.total, &scratch);
     if (rc) return rc;
     uint8_t* base = static_cast<uint8_t*>(scratch);
 
-    Params p;
+    Params& p = S.p;
     std::memset(&p, 0, sizeof(p));
     p.tgt = static_cast<const uint8_t*>(tl->data);
     p.dft = static_cast<const uint8_t*>(dl->data);
@@ -227,10 +237,6 @@ int verify_impl(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_t
     p.dsp = dl->stride_p;
     p.tokens = draft_tokens;
     p.dlen = draft_len;
-    p.out_tokens = out_tokens;
-    p.out_n = out_n;
-    p.probe_pos = probe_pos;
-    p.probe_row = probe_row;
     p.B = B;
     p.K = K;
     p.V = V;
@@ -257,18 +263,71 @@ int verify_impl(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_t
     p.qrec = reinterpret_cast<uint64_t*>(base + lay.qrec);
     p.chdr = topp ? reinterpret_cast<uint64_t*>(base + lay.chdr) : nullptr;
     p.cand = topp ? reinterpret_cast<uint64_t*>(base + lay.cand) : nullptr;
+    p.smc = smc ? 1 : 0;
+    p.smc_cum = smc ? reinterpret_cast<double*>(base + lay.cum) : nullptr;
+    S.dtype = dtype;
+    S.unroll = unroll;
+    S.topp = topp;
+    S.stream = stream;
+    return SV_OK;
+}
 
+int verify_impl(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_tokens, const int32_t* draft_len,
+                float temperature, float top_p, uint64_t seed, int32_t* out_tokens, int32_t* out_n,
+                double* probe_pos, double* probe_row, void* stream_v) {
+    if (!out_tokens || !out_n) return SV_EINVAL;
+    if (misaligned(out_tokens, 4) || misaligned(out_n, 4)) return SV_EALIGN;
+    Setup S;
+    int rc = prepare(tl, dl, draft_tokens, draft_len, temperature, top_p, seed, false, stream_v, S);
+    if (rc) return rc;
+    Params& p = S.p;
+    p.out_tokens = out_tokens;
+    p.out_n = out_n;
+    p.probe_pos = probe_pos;
+    p.probe_row = probe_row;
+    const hipStream_t stream = S.stream;
     rc = timed_launch(sv::KK_STATS, stream, [&](const sv::LaunchEvents& ev) {
-        return sv::launch_stats(p, dtype, unroll, topp, stream, ev);
+        return sv::launch_stats(p, S.dtype, S.unroll, S.topp, stream, ev);
     });
     if (rc) return rc;
-    if (topp) {
+    if (S.topp) {
         rc = timed_launch(sv::KK_TOPP, stream,
-                          [&](const sv::LaunchEvents& ev) { return sv::launch_topp(p, dtype, stream, ev); });
+                          [&](const sv::LaunchEvents& ev) { return sv::launch_topp(p, S.dtype, stream, ev); });
         if (rc) return rc;
     }
     return timed_launch(sv::KK_RESAMPLE, stream,
-                        [&](const sv::LaunchEvents& ev) { return sv::launch_rows(p, dtype, topp, stream, ev); });
+                        [&](const sv::LaunchEvents& ev) { return sv::launch_rows(p, S.dtype, S.topp, stream, ev); });
+}
+
+int smc_impl(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_tokens, const double* logw_in,
+             float temperature, double ess_fraction, uint64_t seed, int32_t* out_bonus, double* out_logw,
+             int32_t* out_ancestor, double* out_ess, int32_t* out_resampled, void* stream_v) {
+    if (!logw_in || !out_bonus || !out_logw || !out_ancestor || !out_ess || !out_resampled) return SV_EINVAL;
+    if (misaligned(logw_in, 8) || misaligned(out_logw, 8) || misaligned(out_ess, 8) || misaligned(out_bonus, 4) ||
+        misaligned(out_ancestor, 4) || misaligned(out_resampled, 4))
+        return SV_EALIGN;
+    if (std::isnan(ess_fraction)) return SV_EINVAL;
+    Setup S;
+    int rc = prepare(tl, dl, draft_tokens, nullptr, temperature, 1.f, seed, true, stream_v, S);
+    if (rc) return rc;
+    Params& p = S.p;
+    p.out_tokens = out_bonus;
+    p.ess_frac = ess_fraction;
+    p.logw_in = logw_in;
+    p.logw_out = out_logw;
+    p.out_ancestor = out_ancestor;
+    p.out_ess = out_ess;
+    p.out_resampled = out_resampled;
+    const hipStream_t stream = S.stream;
+    rc = timed_launch(sv::KK_STATS, stream, [&](const sv::LaunchEvents& ev) {
+        return sv::launch_stats(p, S.dtype, S.unroll, false, stream, ev);
+    });
+    if (rc) return rc;
+    rc = timed_launch(sv::KK_RESAMPLE, stream,
+                      [&](const sv::LaunchEvents& ev) { return sv::launch_smc_rows(p, S.dtype, stream, ev); });
+    if (rc) return rc;
+    return timed_launch(sv::KK_SMC, stream,
+                        [&](const sv::LaunchEvents& ev) { return sv::launch_smc_resample(p, stream, ev); });
 }
 
 }  // namespace
@@ -290,6 +349,13 @@ int spec_verify_probe(const sv_logits* target_logits, const sv_logits* draft_log
     if (misaligned(probe_pos, 8) || misaligned(probe_row, 8)) return SV_EALIGN;
     return verify_impl(target_logits, draft_logits, draft_tokens, draft_len, temperature, top_p, seed, out_tokens,
                        out_n_accepted, probe_pos, probe_row, stream);
+}
+
+int spec_smc_step(const sv_logits* target_logits, const sv_logits* draft_logits, const int32_t* draft_tokens,
+                  const double* logw_in, float temperature, double ess_fraction, uint64_t seed, int32_t* out_bonus,
+                  double* out_logw, int32_t* out_ancestor, double* out_ess, int32_t* out_resampled, void* stream) {
+    return smc_impl(target_logits, draft_logits, draft_tokens, logw_in, temperature, ess_fraction, seed, out_bonus,
+                    out_logw, out_ancestor, out_ess, out_resampled, stream);
 }
 
 const char* spec_verify_strerror(int status) {

@@ -22,7 +22,7 @@ constexpr uint32_t kNoCover = 0xFFFFFFFFu;  // candidate header: the chunk's lis
 
 enum DType : int { DT_F32 = 0, DT_BF16 = 1 };
 enum RowMode : int { MODE_SKIP = 0, MODE_RESID = 1, MODE_BONUS = 2 };
-enum KernelKind : int { KK_STATS = 0, KK_TOPP = 1, KK_RESAMPLE = 2, KK_COUNT = 3 };
+enum KernelKind : int { KK_STATS = 0, KK_TOPP = 1, KK_RESAMPLE = 2, KK_SMC = 3, KK_COUNT = 4 };
 
 // Statistics of one chunk of one logit row, relative to an integer offset o:
 // s = sum over the chunk of 2^(l*c - o), c = log2(e)/T; m = max logit; lx =
@@ -87,6 +87,15 @@ struct Params {
     uint64_t* prec;               // [B, nslot, nch] tagged statistics records
     RvState* rv;                  // [B, nslot]
     uint64_t* qrec;               // [B, nq] tagged resample-item mass records
+    // SMC-SD step (smc = 1): B particles, every one with K drafted tokens
+    int smc;
+    double ess_frac;              // resample when ESS < ess_frac * B
+    const double* logw_in;        // [B]
+    double* logw_out;             // [B] (may alias logw_in)
+    int32_t* out_ancestor;        // [B]
+    double* out_ess;              // [1]
+    int32_t* out_resampled;       // [1]
+    double* smc_cum;              // [B] scratch: cumulative normalised weights
     uint64_t* chdr;               // top-p: [B, nslot, nch, kWaves, 2] tagged candidate headers (count, key bound)
     uint64_t* cand;               // top-p: [B, nslot, nch, kCand] candidates (~key << 32 | id), kCand/kWaves per wave
 };
@@ -103,6 +112,10 @@ struct LaunchEvents {
 hipError_t launch_stats(const Params& p, int dtype, int unroll, bool topp, hipStream_t s, const LaunchEvents& ev);
 hipError_t launch_topp(const Params& p, int dtype, hipStream_t s, const LaunchEvents& ev);
 hipError_t launch_rows(const Params& p, int dtype, bool topp, hipStream_t s, const LaunchEvents& ev);
+// SMC-SD step: the statistics pass, then the particle pass (log-weight
+// increments and the bonus draw), then the resampling kernel.
+hipError_t launch_smc_rows(const Params& p, int dtype, hipStream_t s, const LaunchEvents& ev);
+hipError_t launch_smc_resample(const Params& p, hipStream_t s, const LaunchEvents& ev);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int unroll, hipStream_t s);
 
 }  // namespace sv

@@ -1713,8 +1713,12 @@ __device__ void resample_body(const Params& P, int b, int r, const RowParam& rp,
     __syncthreads();
     if (!s_ok) {
         // a record never arrived: the row is reported invalid
-        if (tid == 0) P.out_n[b] = -1;
-        if (tid < P.K + 1) P.out_tokens[static_cast<size_t>(b) * (P.K + 1) + tid] = -1;
+        if (P.smc) {
+            if (tid == 0) P.out_tokens[b] = -1;
+        } else {
+            if (tid == 0) P.out_n[b] = -1;
+            if (tid < P.K + 1) P.out_tokens[static_cast<size_t>(b) * (P.K + 1) + tid] = -1;
+        }
         return;
     }
     if (s_item != r) return;
@@ -1766,7 +1770,8 @@ __device__ void resample_body(const Params& P, int b, int r, const RowParam& rp,
 #pragma unroll
     for (int w2 = 0; w2 < kWaves; ++w2) lp = max(lp, s_lastpos[w2]);
     double* pr = P.probe_row ? P.probe_row + static_cast<size_t>(b) * 4 : nullptr;
-    int32_t* outp = P.out_tokens + static_cast<size_t>(b) * (P.K + 1) + rn;
+    // the verify step's token at position n, or an SMC particle's bonus
+    int32_t* outp = P.smc ? P.out_tokens + b : P.out_tokens + static_cast<size_t>(b) * (P.K + 1) + rn;
     if (hk < 0) {
         // rounding put t past the item's last positive weight
         if (tid == 0) {
@@ -1859,6 +1864,165 @@ __global__ __launch_bounds__(kThreads) void k_rows(Params P) {
 }
 
 // ---------------------------------------------------------------------------
+// SMC-SD step (page "Faster LLM Inference via Sequential Monte Carlo",
+// section 2): every particle is scored at its K drafted tokens and draws a
+// bonus token from the target at position K; its log-weight grows by
+// sum_j log p_j(x_j) - log q_j(x_j); when the effective sample size falls
+// below ess_frac * B the particles are resampled systematically.
+// ---------------------------------------------------------------------------
+
+constexpr double kLn2 = 0.693147180559945309417232121458176568;
+
+// The particle's validity, log-weight increment and bonus parameters, by
+// ONE wave from the statistics in R (lane j < K takes position j).  With
+// `outputs` lane 0 writes the new log-weight (-inf for an invalid particle,
+// whose bonus is -1).
+__device__ void smc_particle(const Params& P, int b, const RowShared& R, bool outputs, int x, RowParam& rp) {
+    const int lane = threadIdx.x & 63;
+    const int K = P.K;
+    int bad = 0;
+    for (int r = lane; r < 2 * K + 1; r += 64) bad |= R.valid[r] ? 0 : 1;
+    double term = 0.0;
+    if (lane < K) {
+        if (x < 0 || x >= P.V) {
+            bad = 1;
+        } else {
+            // ln p(x) = ln2 * (l(x) c - o) - ln S, the same for q
+            const int rT = lane, rD = K + 1 + lane;
+            const double lp = kLn2 * (static_cast<double>(R.lx[rT]) * P.c64 - static_cast<double>(R.o[rT])) - log(R.s[rT]);
+            const double lq = kLn2 * (static_cast<double>(R.lx[rD]) * P.c64 - static_cast<double>(R.o[rD])) - log(R.s[rD]);
+            term = lp - lq;
+        }
+    }
+    const double lw_in = P.logw_in[b];
+    const bool valid = __ballot(bad) == 0ull && !__builtin_isnan(lw_in) && lw_in != static_cast<double>(SV_INF);
+    const double inc = wave_sum_dpp(term);
+    if (lane == 0) {
+        rp.mode = valid ? MODE_BONUS : MODE_SKIP;
+        rp.n = K;
+        rp.oT = R.o[K];
+        rp.keptT = R.kept[K];
+        rp.tauT = 0u;
+        rp.cutT = -1;
+        rp.oD = 0.f;
+        rp.keptD = 1.0;
+        rp.tauD = 0u;
+        rp.cutD = -1;
+        const uint4 w = philox4x32_10(make_uint4(static_cast<uint32_t>(b), static_cast<uint32_t>(K), 0u, 0u), P.key0,
+                                      P.key1);
+        rp.u = word_uniform(w.y);
+        if (outputs) {
+            P.logw_out[b] = valid ? lw_in + inc : -static_cast<double>(SV_INF);
+            if (!valid) P.out_tokens[b] = -1;
+        }
+    }
+}
+
+// Particle pass: one workgroup per (particle, item), as the verify step's
+// row pass with every particle in bonus mode at position K.
+template <int DT, int R>
+__global__ __launch_bounds__(kThreads) void k_smc_rows(Params P) {
+    __shared__ RowShared RS;
+    __shared__ RowParam s_rp;
+    const int b = blockIdx.x / P.nq;
+    const int r = blockIdx.x - b * P.nq;
+    const int x = lane_token(P, b, P.K);
+    fill_row_from_partials(P, b, P.K, RS);
+    if ((threadIdx.x >> 6) == 0) {
+        RowParam rp;
+        smc_particle(P, b, RS, r == 0, x, rp);
+        if ((threadIdx.x & 63) == 0) s_rp = rp;
+    }
+    __syncthreads();
+    const RowParam rp = s_rp;
+    resample_item<DT, false, R>(P, b, r, rp);
+}
+
+// Resampling: one workgroup over the B particles' new log-weights.  ESS =
+// (sum w)^2 / sum w^2 with w = exp(logw - max); below ess_frac * B the
+// ancestors follow systematic resampling with u0 = word 0 of Philox at
+// counter (0, 0, 1, 0): a_k = the number of particles whose cumulative
+// normalised weight is at most s_k = (k + u0)/B (capped at the last particle
+// of positive weight), and every log-weight becomes 0; otherwise a_k = k.
+__global__ __launch_bounds__(kThreads) void k_smc_resample(Params P) {
+    __shared__ double s_red[kWaves];
+    __shared__ double s_m, s_W;
+    __shared__ int s_last;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int N = P.B;
+    // max log-weight (NaN cannot occur: invalid particles hold -inf)
+    double m = -static_cast<double>(SV_INF);
+    for (int i = tid; i < N; i += kThreads) m = fmax(m, P.logw_out[i]);
+    for (int o = 32; o >= 1; o >>= 1) m = fmax(m, __shfl_xor(m, o, 64));
+    if (lane == 0) s_red[wv] = m;
+    __syncthreads();
+    if (tid == 0) s_m = fmax(fmax(s_red[0], s_red[1]), fmax(s_red[2], s_red[3]));
+    __syncthreads();
+    m = s_m;
+    if (m == -static_cast<double>(SV_INF)) {
+        // no valid particle: nothing to resample
+        for (int i = tid; i < N; i += kThreads) P.out_ancestor[i] = i;
+        if (tid == 0) {
+            *P.out_ess = 0.0;
+            *P.out_resampled = 0;
+        }
+        return;
+    }
+    // each thread a contiguous segment: sums, then the cumulative weights
+    const int per = (N + kThreads - 1) / kThreads;
+    const int i0 = min(tid * per, N), i1 = min(i0 + per, N);
+    double w1 = 0.0, w2 = 0.0;
+    int last = -1;
+    for (int i = i0; i < i1; ++i) {
+        const double w = exp(P.logw_out[i] - m);
+        w1 += w;
+        w2 += w * w;
+        if (w > 0.0) last = i;
+    }
+    double incl, excl, W;
+    block_scan(w1, incl, excl, W);
+    double ig, eg, W2;
+    block_scan(w2, ig, eg, W2);
+    last = block_max_int(last);
+    const double e = W * W / W2;
+    const bool resample = e < P.ess_frac * static_cast<double>(N);
+    if (tid == 0) {
+        *P.out_ess = e;
+        *P.out_resampled = resample ? 1 : 0;
+    }
+    if (!resample) {
+        for (int i = tid; i < N; i += kThreads) P.out_ancestor[i] = i;
+        return;
+    }
+    {
+        double c = excl;
+        for (int i = i0; i < i1; ++i) {
+            c += exp(P.logw_out[i] - m);
+            P.smc_cum[i] = c / W;
+        }
+    }
+    __syncthreads();  // the cumulative weights are written (workgroup scope)
+    const uint4 pw = philox4x32_10(make_uint4(0u, 0u, 1u, 0u), P.key0, P.key1);
+    const double u0 = word_uniform(pw.x);
+    for (int k = tid; k < N; k += kThreads) {
+        const double sk = (static_cast<double>(k) + u0) / static_cast<double>(N);
+        // smallest i with cum[i] > sk
+        int lo = 0, hi = N;
+        while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (P.smc_cum[mid] > sk) hi = mid;
+            else lo = mid + 1;
+        }
+        P.out_ancestor[k] = min(lo, last);
+    }
+    __syncthreads();  // every read of the log-weights is done
+    for (int i = tid; i < N; i += kThreads) P.logw_out[i] = 0.0;
+}
+
+hipError_t launch_smc_rows(const Params& p, int dtype, hipStream_t s, const LaunchEvents& ev);
+hipError_t launch_smc_resample(const Params& p, hipStream_t s, const LaunchEvents& ev);
+
+// ---------------------------------------------------------------------------
 // Streaming-read calibration: every 16-byte vector of a buffer read once with
 // the statistics pass's access pattern (one workgroup per kThreads*U
 // vectors, nontemporal loads), folded into an xor that is stored only if it matches a value it
@@ -1935,6 +2099,25 @@ static void launch_rows_r(const Params& p, int dtype, bool topp, hipStream_t s, 
         if (topp) launch(k_rows<DT_F32, true, R>, grid, kThreads, s, ev, p);
         else launch(k_rows<DT_F32, false, R>, grid, kThreads, s, ev, p);
     }
+}
+
+template <int R>
+static void launch_smc_rows_r(const Params& p, int dtype, hipStream_t s, const LaunchEvents& ev) {
+    const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(p.B) * p.nq);
+    if (dtype == DT_BF16) launch(k_smc_rows<DT_BF16, R>, grid, kThreads, s, ev, p);
+    else launch(k_smc_rows<DT_F32, R>, grid, kThreads, s, ev, p);
+}
+
+hipError_t launch_smc_rows(const Params& p, int dtype, hipStream_t s, const LaunchEvents& ev) {
+    if (p.runs == 1) launch_smc_rows_r<1>(p, dtype, s, ev);
+    else if (p.runs == 2) launch_smc_rows_r<2>(p, dtype, s, ev);
+    else launch_smc_rows_r<kRunsMax>(p, dtype, s, ev);
+    return hipGetLastError();
+}
+
+hipError_t launch_smc_resample(const Params& p, hipStream_t s, const LaunchEvents& ev) {
+    launch(k_smc_resample, 1u, kThreads, s, ev, p);
+    return hipGetLastError();
 }
 
 hipError_t launch_rows(const Params& p, int dtype, bool topp, hipStream_t s, const LaunchEvents& ev) {

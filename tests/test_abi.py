@@ -26,12 +26,12 @@ def lib():
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(spec_verify\w*)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(spec_\w+)\s*\(", src)))
 
 
 def test_header_declares_the_interface():
     names = declared_functions()
-    assert "spec_verify" in names and "spec_verify_probe" in names
+    assert "spec_verify" in names and "spec_verify_probe" in names and "spec_smc_step" in names
     assert set(names) == set(binding.EXPORTS)
 
 
@@ -76,3 +76,22 @@ def _call(lib, B=2, K=3, V=100, dtype=0, T=1.0, top_p=1.0, tP=None, dP=None, tda
 ])
 def test_host_validation(lib, kw, code):
     assert _call(lib, **kw) == code
+
+
+def _smc(lib, N=4, K=2, V=64, T=1.0, ess=0.5, tdata=0x1000, ddata=0x2000, tokens=0x3000, lw=0x4000, bonus=0x5000,
+         lwo=0x6000, anc=0x7000, e=0x8000, rs=0x9000, tP=None):
+    t = binding.SvLogits(tdata, 0, N, K + 1 if tP is None else tP, V, (K + 1) * V, V)
+    d = binding.SvLogits(ddata, 0, N, K, V, K * V, V)
+    v = ctypes.c_void_p
+    return lib.spec_smc_step(ctypes.byref(t), ctypes.byref(d), v(tokens), v(lw), ctypes.c_float(T),
+                             ctypes.c_double(ess), ctypes.c_uint64(0), v(bonus), v(lwo), v(anc), v(e), v(rs), v(None))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(lw=0), -1), (dict(bonus=0), -1), (dict(lwo=0), -1), (dict(anc=0), -1), (dict(e=0), -1), (dict(rs=0), -1),
+    (dict(tokens=0), -1), (dict(ess=float("nan")), -1), (dict(T=0.0), -1),
+    (dict(lw=0x4004), -6), (dict(lwo=0x6004), -6), (dict(e=0x8004), -6), (dict(anc=0x7002), -6),
+    (dict(K=0), -2), (dict(K=17), -2), (dict(N=0), -2), (dict(tP=2), -2),
+])
+def test_smc_host_validation(lib, kw, code):
+    assert _smc(lib, **kw) == code

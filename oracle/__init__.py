@@ -19,8 +19,11 @@ Modules:
              bonus inverse-CDF sample, decision margins.
   smc     -- one SMC-SD step: importance log-weights from target and draft
              probabilities, bonus draw, ESS and systematic resampling.
+  hispec  -- the two-stage (hierarchical) verify: the verify rule applied
+             draft -> intermediate layer -> final layer.
 """
 
+from .hispec import HispecResult, hispec_verify  # noqa: F401
 from .philox import philox4x32_10, uniforms  # noqa: F401
 from .smc import SmcResult, ess, log_weight_increment, smc_step, systematic, systematic_uniform  # noqa: F401
 from .verify import (  # noqa: F401

@@ -66,7 +66,8 @@ def word_to_uniform(w):
     return (np.asarray(w, dtype=np.uint64) >> np.uint64(8)).astype(np.float64) * 2.0 ** -24
 
 
-def uniforms(seed, row, pos):
-    """The (acceptance, resampling) uniforms for one (row, pos) counter."""
-    out = philox4x32_10(np.array([row, pos, 0, 0], dtype=np.uint64), seed_key(seed))
+def uniforms(seed, row, pos, stage=0):
+    """The (acceptance, resampling) uniforms for counter (row, pos, stage, 0);
+    stage 0 is the verify step's own stream."""
+    out = philox4x32_10(np.array([row, pos, stage, 0], dtype=np.uint64), seed_key(seed))
     return float(word_to_uniform(out[0])), float(word_to_uniform(out[1]))

@@ -218,7 +218,7 @@ def _row_is_bad(l):
     return bool(np.any(np.isnan(l)) or np.any(l == np.inf) or np.all(l == -np.inf))
 
 
-def verify(target, draft, draft_tokens, draft_len, temperature, top_p, seed, rows=None):
+def verify(target, draft, draft_tokens, draft_len, temperature, top_p, seed, rows=None, stage=0):
     """The verify step on a batch.
 
     target: [B, K+1, V] logits (float32/float64 values, or uint16 bfloat16
@@ -227,7 +227,9 @@ def verify(target, draft, draft_tokens, draft_len, temperature, top_p, seed, row
     are taken as float32, the precision the library's interface carries;
     top_p >= 1 switches the filter off.  seed: 64-bit Philox key.
     rows: optional subset of batch rows to compute (rows are independent);
-    the other rows of the result are left at -1 / NaN.
+    the other rows of the result are left at -1 / NaN.  stage: the third
+    Philox counter word (0 for the verify step; a second verification of the
+    same rows, as in the hierarchical step, draws from stage 1).
     """
     tl = _widen(target)
     dl = _widen(draft)
@@ -284,7 +286,7 @@ def verify(target, draft, draft_tokens, draft_len, temperature, top_p, seed, row
         for j in range(L):
             probe_pos[b, j, 4] = p[j][x[j]]
             probe_pos[b, j, 5] = q[j][x[j]]
-        ua, ur = zip(*(uniforms(seed, b, j) for j in range(L + 1)))
+        ua, ur = zip(*(uniforms(seed, b, j, stage) for j in range(L + 1)))
         d = decide_row(p, q, x, ua, ur)
         n_acc[b] = d.n
         tokens[b, : d.n + 1] = d.tokens

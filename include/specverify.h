@@ -139,6 +139,36 @@ int spec_verify_probe(const sv_logits* target_logits, const sv_logits* draft_log
                       double* probe_pos, double* probe_row, void* stream);
 
 /*
+ * spec_hispec_verify -- the two-stage (hierarchical) verify step (page
+ * "HiSpec: Hierarchical Speculative Decoding for LLMs", section 2: an
+ * early-exit model's intermediate layer verifies the drafts first and rejects
+ * early; the final layer verifies what passed; applying the lossless rule in
+ * both stages makes the output follow the final layer exactly).
+ *
+ * final_logits    [B, K+2, V] final-layer logits at the positions of the
+ *                 provisional sequence (positions past n1 + 1 are not read).
+ * inter_logits    [B, K+1, V] intermediate-layer logits.
+ * draft_logits    [B, K, V] draft-layer logits; all three the same dtype, B
+ *                 and V; 1 <= K <= 15.
+ * draft_tokens, draft_len, temperature, top_p, seed: as for spec_verify.
+ * out_tokens      device int32 [B, K+2]: the n accepted tokens, then the
+ *                 final layer's corrected or bonus token, then -1.
+ * out_n_accepted  device int32 [B]: n (stage 2's accepted count), -1 for an
+ *                 invalid row.
+ * out_n_stage1    device int32 [B] or NULL: n1, the drafts the intermediate
+ *                 layer accepted.
+ *
+ * Stage 1 is spec_verify(inter, draft): n1 accepted drafts and one token.
+ * Stage 2 is spec_verify(final, inter) on those n1 + 1 tokens, with its
+ * uniforms from Philox counter (row, position, 1, 0).  Errors as spec_verify.
+ */
+int spec_hispec_verify(const sv_logits* final_logits, const sv_logits* inter_logits,
+                       const sv_logits* draft_logits, const int32_t* draft_tokens,
+                       const int32_t* draft_len, float temperature, float top_p,
+                       uint64_t seed, int32_t* out_tokens, int32_t* out_n_accepted,
+                       int32_t* out_n_stage1, void* stream);
+
+/*
  * spec_smc_step -- one reweight-and-resample step of SMC-SD over N particles
  * (page "Faster LLM Inference via Sequential Monte Carlo", section 2: every
  * particle is extended by K draft tokens and scored by the target, which also

@@ -20,7 +20,8 @@ STATUS = {0: "SV_OK", -1: "SV_EINVAL", -2: "SV_ESHAPE", -3: "SV_EDTYPE", -4: "SV
           -6: "SV_EALIGN"}
 KERNEL_KINDS = ("stats", "topp", "rows", "smc")
 
-EXPORTS = ("spec_verify", "spec_verify_probe", "spec_smc_step", "spec_verify_strerror", "spec_verify_release",
+EXPORTS = ("spec_verify", "spec_verify_probe", "spec_hispec_verify", "spec_smc_step", "spec_verify_strerror",
+           "spec_verify_release",
            "spec_verify_abi_version", "spec_verify_profile_enable", "spec_verify_profile_read",
            "spec_verify_stream_read")
 
@@ -60,6 +61,9 @@ def load(path=LIB_PATH):
     lib.spec_verify.restype = ctypes.c_int
     lib.spec_verify_probe.argtypes = lib.spec_verify.argtypes[:9] + [ctypes.c_void_p] * 3
     lib.spec_verify_probe.restype = ctypes.c_int
+    lib.spec_hispec_verify.argtypes = [P(SvLogits)] * 3 + [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,
+                                                            ctypes.c_float, ctypes.c_uint64] + [ctypes.c_void_p] * 4
+    lib.spec_hispec_verify.restype = ctypes.c_int
     lib.spec_smc_step.argtypes = [P(SvLogits), P(SvLogits), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,
                                   ctypes.c_double, ctypes.c_uint64] + [ctypes.c_void_p] * 6
     lib.spec_smc_step.restype = ctypes.c_int
@@ -139,6 +143,34 @@ def verify(target, draft, draft_tokens, draft_len=None, temperature=1.0, top_p=1
         return out_tokens, out_n_accepted, pp, pr
     _check(lib, lib.spec_verify(*args, sh))
     return out_tokens, out_n_accepted
+
+
+def hispec_verify(final, inter, draft, draft_tokens, draft_len=None, temperature=1.0, top_p=1.0, seed=0, *,
+                  stream=None, out_tokens=None, out_n_accepted=None, out_n_stage1=None):
+    """The two-stage verify on device tensors: final [B, K+2, V], inter
+    [B, K+1, V], draft [B, K, V] logits (same dtype, V contiguous).  Returns
+    (tokens [B, K+2] int32, n_accepted [B] int32, n_stage1 [B] int32)."""
+    lib = load()
+    if draft_tokens.dtype != torch.int32 or not draft_tokens.is_contiguous():
+        raise ValueError("draft_tokens must be contiguous int32")
+    if draft_len is not None and (draft_len.dtype != torch.int32 or not draft_len.is_contiguous()):
+        raise ValueError("draft_len must be contiguous int32")
+    dev = final.device
+    B, K2 = final.shape[0], final.shape[1]
+    if out_tokens is None:
+        out_tokens = torch.empty((B, K2), dtype=torch.int32, device=dev)
+    if out_n_accepted is None:
+        out_n_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    if out_n_stage1 is None:
+        out_n_stage1 = torch.empty((B,), dtype=torch.int32, device=dev)
+    fd, idd, dd = _desc(final, "final"), _desc(inter, "inter"), _desc(draft, "draft")
+    _check(lib, lib.spec_hispec_verify(
+        ctypes.byref(fd), ctypes.byref(idd), ctypes.byref(dd), ctypes.c_void_p(draft_tokens.data_ptr()),
+        ctypes.c_void_p(draft_len.data_ptr() if draft_len is not None else None), ctypes.c_float(temperature),
+        ctypes.c_float(top_p), ctypes.c_uint64(int(seed) & (2 ** 64 - 1)), ctypes.c_void_p(out_tokens.data_ptr()),
+        ctypes.c_void_p(out_n_accepted.data_ptr()), ctypes.c_void_p(out_n_stage1.data_ptr()),
+        _stream_handle(stream, dev)))
+    return out_tokens, out_n_accepted, out_n_stage1
 
 
 def smc_step(target, draft, draft_tokens, logw_in, temperature=1.0, ess_fraction=0.5, seed=0, *, stream=None,

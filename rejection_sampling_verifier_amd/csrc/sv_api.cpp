@@ -163,19 +163,20 @@ int timed_launch(int kind, hipStream_t stream, F&& launch) {
     return SV_OK;
 }
 
-// What every entry point shares: argument checks, chunking, scratch and the
-// kernel parameters.  `smc`: an SMC-SD step (no draft lengths, no top-p, the
-// resampling kernel's scratch).
+// What every entry point shares: argument checks, chunking and the kernel
+// parameters (plan), then the scratch pointers (bind).  `smc`: an SMC-SD step
+// (no draft lengths, no top-p, the resampling kernel's scratch).
 struct Setup {
     Params p;
     int dtype = 0;
     int unroll = 0;
     bool topp = false;
     hipStream_t stream = nullptr;
+    Layout lay;
 };
 
-int prepare(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_tokens, const int32_t* draft_len,
-            float temperature, float top_p, uint64_t seed, bool smc, void* stream_v, Setup& S) {
+int plan(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_tokens, const int32_t* draft_len,
+         float temperature, float top_p, uint64_t seed, bool smc, void* stream_v, Setup& S) {
     int rc = check_logits(tl);
     if (rc) return rc;
     rc = check_logits(dl);
@@ -219,13 +220,8 @@ int prepare(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_token
     // the statistics kernel clears the row pass's records, a few words each
     if (4ll * nq > static_cast<int64_t>(sv::kThreads) * nslot * nch) return SV_ESHAPE;
 
-    hipStream_t stream = static_cast<hipStream_t>(stream_v);
     const bool topp = top_p < 1.f;
-    const Layout lay = layout(B, nslot, nch, nq, topp, smc);
-    void* scratch = nullptr;
-    rc = get_scratch(stream, lay.total, &scratch);
-    if (rc) return rc;
-    uint8_t* base = static_cast<uint8_t*>(scratch);
+    S.lay = layout(B, nslot, nch, nq, topp, smc);
 
     Params& p = S.p;
     std::memset(&p, 0, sizeof(p));
@@ -258,35 +254,42 @@ int prepare(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_token
     p.top_p = top_p;
     p.key0 = static_cast<uint32_t>(seed & 0xFFFFFFFFull);
     p.key1 = static_cast<uint32_t>(seed >> 32);
-    p.prec = reinterpret_cast<uint64_t*>(base + lay.prec);
-    p.rv = reinterpret_cast<sv::RvState*>(base + lay.rv);
-    p.qrec = reinterpret_cast<uint64_t*>(base + lay.qrec);
-    p.chdr = topp ? reinterpret_cast<uint64_t*>(base + lay.chdr) : nullptr;
-    p.cand = topp ? reinterpret_cast<uint64_t*>(base + lay.cand) : nullptr;
     p.smc = smc ? 1 : 0;
-    p.smc_cum = smc ? reinterpret_cast<double*>(base + lay.cum) : nullptr;
     S.dtype = dtype;
     S.unroll = unroll;
     S.topp = topp;
-    S.stream = stream;
+    S.stream = static_cast<hipStream_t>(stream_v);
     return SV_OK;
 }
 
-int verify_impl(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_tokens, const int32_t* draft_len,
-                float temperature, float top_p, uint64_t seed, int32_t* out_tokens, int32_t* out_n,
-                double* probe_pos, double* probe_row, void* stream_v) {
-    if (!out_tokens || !out_n) return SV_EINVAL;
-    if (misaligned(out_tokens, 4) || misaligned(out_n, 4)) return SV_EALIGN;
-    Setup S;
-    int rc = prepare(tl, dl, draft_tokens, draft_len, temperature, top_p, seed, false, stream_v, S);
-    if (rc) return rc;
+void bind(Setup& S, uint8_t* base) {
     Params& p = S.p;
-    p.out_tokens = out_tokens;
-    p.out_n = out_n;
-    p.probe_pos = probe_pos;
-    p.probe_row = probe_row;
+    const Layout& lay = S.lay;
+    p.prec = reinterpret_cast<uint64_t*>(base + lay.prec);
+    p.rv = reinterpret_cast<sv::RvState*>(base + lay.rv);
+    p.qrec = reinterpret_cast<uint64_t*>(base + lay.qrec);
+    p.chdr = S.topp ? reinterpret_cast<uint64_t*>(base + lay.chdr) : nullptr;
+    p.cand = S.topp ? reinterpret_cast<uint64_t*>(base + lay.cand) : nullptr;
+    p.smc_cum = p.smc ? reinterpret_cast<double*>(base + lay.cum) : nullptr;
+}
+
+// plan + scratch + bind for a single pass.
+int prepare(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_tokens, const int32_t* draft_len,
+            float temperature, float top_p, uint64_t seed, bool smc, void* stream_v, Setup& S) {
+    int rc = plan(tl, dl, draft_tokens, draft_len, temperature, top_p, seed, smc, stream_v, S);
+    if (rc) return rc;
+    void* scratch = nullptr;
+    rc = get_scratch(S.stream, S.lay.total, &scratch);
+    if (rc) return rc;
+    bind(S, static_cast<uint8_t*>(scratch));
+    return SV_OK;
+}
+
+// The verify step's kernels for one planned and bound pass.
+int launch_verify(Setup& S) {
+    Params& p = S.p;
     const hipStream_t stream = S.stream;
-    rc = timed_launch(sv::KK_STATS, stream, [&](const sv::LaunchEvents& ev) {
+    int rc = timed_launch(sv::KK_STATS, stream, [&](const sv::LaunchEvents& ev) {
         return sv::launch_stats(p, S.dtype, S.unroll, S.topp, stream, ev);
     });
     if (rc) return rc;
@@ -297,6 +300,68 @@ int verify_impl(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_t
     }
     return timed_launch(sv::KK_RESAMPLE, stream,
                         [&](const sv::LaunchEvents& ev) { return sv::launch_rows(p, S.dtype, S.topp, stream, ev); });
+}
+
+int verify_impl(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_tokens, const int32_t* draft_len,
+                float temperature, float top_p, uint64_t seed, int32_t* out_tokens, int32_t* out_n,
+                double* probe_pos, double* probe_row, void* stream_v) {
+    if (!out_tokens || !out_n) return SV_EINVAL;
+    if (misaligned(out_tokens, 4) || misaligned(out_n, 4)) return SV_EALIGN;
+    Setup S;
+    int rc = prepare(tl, dl, draft_tokens, draft_len, temperature, top_p, seed, false, stream_v, S);
+    if (rc) return rc;
+    S.p.out_tokens = out_tokens;
+    S.p.out_n = out_n;
+    S.p.probe_pos = probe_pos;
+    S.p.probe_row = probe_row;
+    return launch_verify(S);
+}
+
+// Two-stage verify: stage 1 verifies the drafts against the intermediate
+// layer, stage 2 the n1 + 1 tokens it emitted against the final layer (the
+// intermediate layer as their proposal, Philox stream 1).  One scratch
+// allocation holds both passes' regions and stage 1's outputs.
+int hispec_impl(const sv_logits* fl, const sv_logits* il, const sv_logits* dl, const int32_t* draft_tokens,
+                const int32_t* draft_len, float temperature, float top_p, uint64_t seed, int32_t* out_tokens,
+                int32_t* out_n, int32_t* out_n_stage1, void* stream_v) {
+    if (!out_tokens || !out_n) return SV_EINVAL;
+    if (misaligned(out_tokens, 4) || misaligned(out_n, 4) || (out_n_stage1 && misaligned(out_n_stage1, 4)))
+        return SV_EALIGN;
+    if (!fl || !il) return SV_EINVAL;
+    if (fl->B != il->B || fl->V != il->V || fl->P != il->P + 1) return SV_ESHAPE;
+    Setup S1, S2;
+    int rc = plan(il, dl, draft_tokens, draft_len, temperature, top_p, seed, false, stream_v, S1);
+    if (rc) return rc;
+    // stage 2's drafts are device scratch bound below; the caller's ids stand
+    // in for the host checks
+    rc = plan(fl, il, draft_tokens, nullptr, temperature, top_p, seed, false, stream_v, S2);
+    if (rc) return rc;
+    const int B = S1.p.B, K1 = S1.p.K + 1;
+    const size_t tok_bytes = align256(static_cast<size_t>(B) * K1 * sizeof(int32_t));
+    const size_t vec_bytes = align256(static_cast<size_t>(B) * sizeof(int32_t));
+    const size_t total = S1.lay.total + S2.lay.total + tok_bytes + 2 * vec_bytes;
+    void* scratch = nullptr;
+    rc = get_scratch(S1.stream, total, &scratch);
+    if (rc) return rc;
+    uint8_t* base = static_cast<uint8_t*>(scratch);
+    bind(S1, base);
+    bind(S2, base + S1.lay.total);
+    uint8_t* extra = base + S1.lay.total + S2.lay.total;
+    int32_t* tok1 = reinterpret_cast<int32_t*>(extra);
+    int32_t* n1 = reinterpret_cast<int32_t*>(extra + tok_bytes);
+    int32_t* len2 = reinterpret_cast<int32_t*>(extra + tok_bytes + vec_bytes);
+    S1.p.out_tokens = tok1;
+    S1.p.out_n = n1;
+    S2.p.tokens = tok1;
+    S2.p.dlen = len2;
+    S2.p.stage = 1;
+    S2.p.out_tokens = out_tokens;
+    S2.p.out_n = out_n;
+    rc = launch_verify(S1);
+    if (rc) return rc;
+    const hipError_t e = sv::launch_hispec_link(n1, len2, out_n_stage1, B, S1.stream);
+    if (e != hipSuccess) return hip_fail(e, "kernel launch");
+    return launch_verify(S2);
 }
 
 int smc_impl(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_tokens, const double* logw_in,
@@ -349,6 +414,14 @@ int spec_verify_probe(const sv_logits* target_logits, const sv_logits* draft_log
     if (misaligned(probe_pos, 8) || misaligned(probe_row, 8)) return SV_EALIGN;
     return verify_impl(target_logits, draft_logits, draft_tokens, draft_len, temperature, top_p, seed, out_tokens,
                        out_n_accepted, probe_pos, probe_row, stream);
+}
+
+int spec_hispec_verify(const sv_logits* final_logits, const sv_logits* inter_logits, const sv_logits* draft_logits,
+                       const int32_t* draft_tokens, const int32_t* draft_len, float temperature, float top_p,
+                       uint64_t seed, int32_t* out_tokens, int32_t* out_n_accepted, int32_t* out_n_stage1,
+                       void* stream) {
+    return hispec_impl(final_logits, inter_logits, draft_logits, draft_tokens, draft_len, temperature, top_p, seed,
+                       out_tokens, out_n_accepted, out_n_stage1, stream);
 }
 
 int spec_smc_step(const sv_logits* target_logits, const sv_logits* draft_logits, const int32_t* draft_tokens,

@@ -84,6 +84,7 @@ struct Params {
     float inv_c;                  // 1/c, rounded (thresholds only)
     float top_p;
     uint32_t key0, key1;          // Philox key
+    uint32_t stage;               // Philox counter word 2 of the decision (0; 1 for a second verification)
     uint64_t* prec;               // [B, nslot, nch] tagged statistics records
     RvState* rv;                  // [B, nslot]
     uint64_t* qrec;               // [B, nq] tagged resample-item mass records
@@ -116,6 +117,8 @@ hipError_t launch_rows(const Params& p, int dtype, bool topp, hipStream_t s, con
 // increments and the bonus draw), then the resampling kernel.
 hipError_t launch_smc_rows(const Params& p, int dtype, hipStream_t s, const LaunchEvents& ev);
 hipError_t launch_smc_resample(const Params& p, hipStream_t s, const LaunchEvents& ev);
+// Two-stage verify: stage 2's draft lengths (n1 + 1) from stage 1's counts.
+hipError_t launch_hispec_link(const int32_t* n1, int32_t* len2, int32_t* out_n1, int B, hipStream_t s);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int unroll, hipStream_t s);
 
 }  // namespace sv

@@ -399,7 +399,7 @@ __device__ void decide_row(const Params& P, int b, int Le, bool rowok, const Row
     double u_res = 0.0, pt = nan64(), qd = nan64();
     int bad_tok = 0;
     if (!rowbad && lane <= Le) {
-        const uint4 w = philox4x32_10(make_uint4(static_cast<uint32_t>(b), static_cast<uint32_t>(lane), 0u, 0u),
+        const uint4 w = philox4x32_10(make_uint4(static_cast<uint32_t>(b), static_cast<uint32_t>(lane), P.stage, 0u),
                                       P.key0, P.key1);
         u_res = word_uniform(w.y);
         if (lane < Le) {
@@ -2021,6 +2021,26 @@ __global__ __launch_bounds__(kThreads) void k_smc_resample(Params P) {
 
 hipError_t launch_smc_rows(const Params& p, int dtype, hipStream_t s, const LaunchEvents& ev);
 hipError_t launch_smc_resample(const Params& p, hipStream_t s, const LaunchEvents& ev);
+
+// ---------------------------------------------------------------------------
+// Two-stage (hierarchical) verify (page "HiSpec: Hierarchical Speculative
+// Decoding for LLMs", section 2): between the two verify passes, the tokens
+// stage 1 emitted become stage 2's drafts, n1 + 1 of them per row (a row
+// invalid in stage 1 gets an invalid length and stays invalid).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void k_hispec_link(const int32_t* n1, int32_t* len2, int32_t* out_n1, int B) {
+    const int b = blockIdx.x * kThreads + threadIdx.x;
+    if (b >= B) return;
+    const int n = n1[b];
+    len2[b] = n >= 0 ? n + 1 : -1;
+    if (out_n1) out_n1[b] = n;
+}
+
+hipError_t launch_hispec_link(const int32_t* n1, int32_t* len2, int32_t* out_n1, int B, hipStream_t s) {
+    const unsigned grid = static_cast<unsigned>((B + kThreads - 1) / kThreads);
+    hipLaunchKernelGGL(k_hispec_link, dim3(grid), dim3(kThreads), 0, s, n1, len2, out_n1, B);
+    return hipGetLastError();
+}
 
 // ---------------------------------------------------------------------------
 // Streaming-read calibration: every 16-byte vector of a buffer read once with

@@ -32,6 +32,7 @@ def declared_functions():
 def test_header_declares_the_interface():
     names = declared_functions()
     assert "spec_verify" in names and "spec_verify_probe" in names and "spec_smc_step" in names
+    assert "spec_hispec_verify" in names
     assert set(names) == set(binding.EXPORTS)
 
 
@@ -95,3 +96,23 @@ def _smc(lib, N=4, K=2, V=64, T=1.0, ess=0.5, tdata=0x1000, ddata=0x2000, tokens
 ])
 def test_smc_host_validation(lib, kw, code):
     assert _smc(lib, **kw) == code
+
+
+def _hispec(lib, B=3, K=2, V=64, fP=None, iP=None, T=1.0, fdata=0x1000, idata=0x2000, ddata=0x3000, tokens=0x4000,
+            out=0x5000, outn=0x6000, outn1=0x7000, dtype_f=0):
+    f = binding.SvLogits(fdata, dtype_f, B, K + 2 if fP is None else fP, V, (K + 2) * V, V)
+    i = binding.SvLogits(idata, 0, B, K + 1 if iP is None else iP, V, (K + 1) * V, V)
+    d = binding.SvLogits(ddata, 0, B, K, V, K * V, V)
+    v = ctypes.c_void_p
+    return lib.spec_hispec_verify(ctypes.byref(f), ctypes.byref(i), ctypes.byref(d), v(tokens), v(None),
+                                  ctypes.c_float(T), ctypes.c_float(1.0), ctypes.c_uint64(0), v(out), v(outn),
+                                  v(outn1), v(None))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(out=0), -1), (dict(outn=0), -1), (dict(tokens=0), -1), (dict(fdata=0), -1), (dict(T=0.0), -1),
+    (dict(fP=3), -2), (dict(iP=2), -2), (dict(K=15 + 1), -2), (dict(dtype_f=1), -3),
+    (dict(out=0x5002), -6), (dict(outn1=0x7002), -6),
+])
+def test_hispec_host_validation(lib, kw, code):
+    assert _hispec(lib, **kw) == code

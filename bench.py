@@ -269,6 +269,106 @@ def smc_bench(args, binding, torch, dev, sets, dsets, logical, stream):
 
 
 # ---------------------------------------------------------------------------
+# Two-stage verify timing (--hispec): three exit layers of one synthetic
+# early-exit model, B=64, K=5, V=128256, bf16, T=0.7
+# ---------------------------------------------------------------------------
+def _oracle_hispec(args):
+    import oracle
+
+    si, r0, r1 = args
+    h = _SAMPLE[si]
+    oracle.hispec_verify(h.final[r0:r1], h.inter[r0:r1], h.draft[r0:r1], h.draft_tokens[r0:r1], None,
+                         h.temperature, h.top_p, h.seed)
+    return (r1 - r0) * h.draft.shape[1]
+
+
+def hispec_bench(args, binding, torch, dev):
+    import numpy as np
+
+    from rejection_sampling_verifier_amd import workloads
+
+    B, K, V = 64, 5, workloads.V_LLAMA3
+    print(f"[bench] generating {N_SETS} three-layer input sets", file=sys.stderr, flush=True)
+    hs = [workloads.make_hispec_inputs(B, K, V, dtype="bf16", step=s, temperature=0.7) for s in range(N_SETS)]
+
+    def put(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    ds = [(put(h.final), put(h.inter), put(h.draft), torch.from_numpy(h.draft_tokens).to(dev), float(h.temperature),
+           h.seed) for h in hs]
+    outs = [(torch.empty((B, K + 2), dtype=torch.int32, device=dev), torch.empty((B,), dtype=torch.int32, device=dev),
+             torch.empty((B,), dtype=torch.int32, device=dev)) for _ in range(N_SETS)]
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        f, it, d, x, T, seed = ds[i % N_SETS]
+        o = outs[i % N_SETS]
+        binding.hispec_verify(f, it, d, x, None, T, 1.0, seed, stream=stream, out_tokens=o[0], out_n_accepted=o[1],
+                              out_n_stage1=o[2])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # logical bytes: stage 1 reads 2K + 1 rows per batch row, stage 2
+    # 2 (n1 + 1) + 1 rows (n1 from each set's own result)
+    rows = []
+    for s in range(N_SETS):
+        n1 = outs[s][2].cpu().numpy()
+        rows.append(B * (2 * K + 1) + int(np.sum(2 * (n1 + 1) + 1)))
+    logical = sum(rows) / N_SETS * V * 2
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    binding.profile_read()
+    binding.profile_enable(True)
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    binding.profile_enable(False)
+    prof = binding.profile_read()
+    us = {k: prof[k][0] / prof[k][1] * 1e3 for k in ("stats", "rows") if prof[k][1]}
+    print(f"[bench] hispec {args.steps} steps: {ms_step * 1e3:.2f} us/step; per-kernel averages over both stages "
+          f"{us}", file=sys.stderr, flush=True)
+    cpu = None
+    if not args.no_cpu_baseline:
+        global _SAMPLE
+        _SAMPLE = hs
+        cores = max(1, min(16, os.cpu_count() or 1))
+        work = [(s, r, r + 1) for s in range(N_SETS) for r in range(B)]
+        positions, dt, passes = _timed_passes(_oracle_hispec, work, cores)
+        cpu = {"value": positions / dt, "unit": "positions/s", "cores": cores, "kind": "oracle",
+               "sample": f"{len(work)} rows of the three-layer workload, {passes} passes ({positions} draft "
+                         f"positions), float64 NumPy oracle, one row per task over {cores} processes, "
+                         f"{dt:.1f} s wall"}
+    line = {
+        "metric": "two-stage verify: draft positions/sec + logits HBM GB/s (% of peak) at B=64,K=5,V=128256",
+        "value": round(B * K / (ms_step / 1e3), 1),
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "two-stage verify B=64 K=5 V=128256 bf16 T=0.7 (final, intermediate, draft layers)",
+                   "B": B, "K": K, "V": V, "logical_bytes_per_step": logical,
+                   "logits_GBps": round(logical / (ms_step / 1e3) / 1e9, 1),
+                   "logits_frac_of_peak": round(logical / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "kernels_us": {"k_stats (per stage)": round(us["stats"], 3), "k_rows (per stage)": round(us["rows"], 3)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+# ---------------------------------------------------------------------------
 # GPU timing
 # ---------------------------------------------------------------------------
 def main():
@@ -280,6 +380,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=192)
     ap.add_argument("--workload", type=int, default=WORKLOAD_CFG,
                     help="seeded workload to time (default: the batched B=64 K=5 V=128256 bf16 one)")
+    ap.add_argument("--hispec", action="store_true",
+                    help="time the two-stage verify (spec_hispec_verify) on three synthetic exit layers")
     ap.add_argument("--smc", action="store_true",
                     help="time the SMC-SD step (spec_smc_step) on the same inputs instead of the verify step")
     ap.add_argument("--calibrate", action="store_true",
@@ -300,6 +402,10 @@ def main():
     binding.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    if args.hispec:
+        hispec_bench(args, binding, torch, dev)
+        return
 
     print(f"[bench] generating {N_SETS} input sets of workload {args.workload}", file=sys.stderr, flush=True)
     sets = [workloads.make_inputs(args.workload, s) for s in range(N_SETS)]

@@ -205,3 +205,40 @@ def synthetic(B, K, V, *, dtype="f32", temperature=1.0, top_p=1.0, sigma=1.0, sc
     dl = None if draft_len is None else np.asarray(draft_len, np.int32)
     return Inputs(CONFIGS[0], 0, np.ascontiguousarray(ts), np.ascontiguousarray(ds), tokens, dl, T,
                   np.float32(top_p), int(seed))
+
+
+@dataclass
+class HispecInputs:
+    final: np.ndarray        # [B, K+2, V] float32 or bfloat16 bits
+    inter: np.ndarray        # [B, K+1, V]
+    draft: np.ndarray        # [B, K, V]
+    draft_tokens: np.ndarray # [B, K] int32
+    draft_len: Optional[np.ndarray]
+    temperature: np.float32
+    top_p: np.float32
+    seed: int
+
+
+def make_hispec_inputs(B, K, V, *, dtype="bf16", step=0, temperature=0.7, top_p=1.0, sig_inter=0.7,
+                       sig_draft=1.0, ragged=False):
+    """Three exit layers of one early-exit model (page "HiSpec", section 2):
+    final-layer logits N(0, 3^2) over [B, K+2, V]; intermediate layer = final
+    + N(0, sig_inter^2) at positions 0..K; draft layer = intermediate +
+    N(0, sig_draft^2) at positions 0..K-1; drafted tokens sampled from the
+    draft layer's softmax at the temperature (Gumbel-max); with `ragged`,
+    per-row draft lengths uniform in 0..K.  Seeded by SeedSequence([0x5EED2000,
+    step])."""
+    rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence([0x5EED2000, step])))
+    f = rng.standard_normal((B, K + 2, V), dtype=np.float32) * np.float32(3.0)
+    i = f[:, : K + 1] + rng.standard_normal((B, K + 1, V), dtype=np.float32) * np.float32(sig_inter)
+    d = i[:, :K] + rng.standard_normal((B, K, V), dtype=np.float32) * np.float32(sig_draft)
+    if dtype == "bf16":
+        f, i, d = f32_to_bf16_bits(f), f32_to_bf16_bits(i), f32_to_bf16_bits(d)
+        dv = bf16_bits_to_f32(d)
+    else:
+        dv = d
+    T = np.float32(temperature)
+    tokens = _gumbel_argmax(rng, dv, float(T)).astype(np.int32)
+    dl = rng.integers(0, K + 1, size=B).astype(np.int32) if ragged else None
+    return HispecInputs(np.ascontiguousarray(f), np.ascontiguousarray(i), np.ascontiguousarray(d), tokens, dl, T,
+                        np.float32(top_p), (0x5EED2 << 32) | step)

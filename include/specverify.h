@@ -139,6 +139,33 @@ int spec_verify_probe(const sv_logits* target_logits, const sv_logits* draft_log
                       double* probe_pos, double* probe_row, void* stream);
 
 /*
+ * spec_greedy_verify -- greedy verify: the temperature -> 0 limit of
+ * spec_verify (page "Speculative Decoding للمحترف", section "المفهوم بالتقريب":
+ * accept the drafted tokens the target agrees with, take the target's token at
+ * the first disagreement), plus the k ids that rank after the emitted token
+ * in the logits it came from (the LogitSpec page, gist.science 2507.01449,
+ * section 2: candidates for the token after next; the page uses k = 60).
+ *
+ * target_logits   [B, K+1, V] target logits, bf16 or fp32; 1 <= K <= 16.
+ * draft_tokens, draft_len: as for spec_verify (no draft logits are needed).
+ * k               0 <= k <= 64.
+ * out_tokens      device int32 [B, K+1]: the n accepted ids, the target's
+ *                 argmax at position n (ties to the lower id), then -1.
+ * out_n_accepted  device int32 [B]: n = the first j < L_b whose drafted id is
+ *                 not the target's argmax (L_b if none), -1 for an invalid row.
+ * out_topk        device int32 [B, k] (NULL when k = 0): the ids ranked 2..k+1
+ *                 by logit at position n (descending, ties to the lower id),
+ *                 -1 past V.
+ *
+ * Invalid rows (as for spec_verify, on the target rows 0..L_b) give n = -1
+ * and -1 in every output.  Errors as spec_verify, SV_EINVAL for k outside
+ * [0, 64] or out_topk NULL with k > 0.
+ */
+int spec_greedy_verify(const sv_logits* target_logits, const int32_t* draft_tokens,
+                       const int32_t* draft_len, int32_t k, int32_t* out_tokens,
+                       int32_t* out_n_accepted, int32_t* out_topk, void* stream);
+
+/*
  * spec_hispec_verify -- the two-stage (hierarchical) verify step (page
  * "HiSpec: Hierarchical Speculative Decoding for LLMs", section 2: an
  * early-exit model's intermediate layer verifies the drafts first and rejects

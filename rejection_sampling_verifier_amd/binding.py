@@ -20,7 +20,8 @@ STATUS = {0: "SV_OK", -1: "SV_EINVAL", -2: "SV_ESHAPE", -3: "SV_EDTYPE", -4: "SV
           -6: "SV_EALIGN"}
 KERNEL_KINDS = ("stats", "topp", "rows", "smc")
 
-EXPORTS = ("spec_verify", "spec_verify_probe", "spec_hispec_verify", "spec_smc_step", "spec_verify_strerror",
+EXPORTS = ("spec_verify", "spec_verify_probe", "spec_greedy_verify", "spec_hispec_verify", "spec_smc_step",
+           "spec_verify_strerror",
            "spec_verify_release",
            "spec_verify_abi_version", "spec_verify_profile_enable", "spec_verify_profile_read",
            "spec_verify_stream_read")
@@ -61,6 +62,9 @@ def load(path=LIB_PATH):
     lib.spec_verify.restype = ctypes.c_int
     lib.spec_verify_probe.argtypes = lib.spec_verify.argtypes[:9] + [ctypes.c_void_p] * 3
     lib.spec_verify_probe.restype = ctypes.c_int
+    lib.spec_greedy_verify.argtypes = [P(SvLogits), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32] + \
+        [ctypes.c_void_p] * 4
+    lib.spec_greedy_verify.restype = ctypes.c_int
     lib.spec_hispec_verify.argtypes = [P(SvLogits)] * 3 + [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,
                                                             ctypes.c_float, ctypes.c_uint64] + [ctypes.c_void_p] * 4
     lib.spec_hispec_verify.restype = ctypes.c_int
@@ -143,6 +147,33 @@ def verify(target, draft, draft_tokens, draft_len=None, temperature=1.0, top_p=1
         return out_tokens, out_n_accepted, pp, pr
     _check(lib, lib.spec_verify(*args, sh))
     return out_tokens, out_n_accepted
+
+
+def greedy_verify(target, draft_tokens, draft_len=None, k=0, *, stream=None, out_tokens=None, out_n_accepted=None,
+                  out_topk=None):
+    """Greedy verify on device tensors: target [B, K+1, V] (bfloat16 or
+    float32, V contiguous), draft_tokens [B, K] int32.  Returns (tokens
+    [B, K+1] int32, n_accepted [B] int32, topk [B, k] int32)."""
+    lib = load()
+    if draft_tokens.dtype != torch.int32 or not draft_tokens.is_contiguous():
+        raise ValueError("draft_tokens must be contiguous int32")
+    if draft_len is not None and (draft_len.dtype != torch.int32 or not draft_len.is_contiguous()):
+        raise ValueError("draft_len must be contiguous int32")
+    dev = target.device
+    B, K1 = target.shape[0], target.shape[1]
+    if out_tokens is None:
+        out_tokens = torch.empty((B, K1), dtype=torch.int32, device=dev)
+    if out_n_accepted is None:
+        out_n_accepted = torch.empty((B,), dtype=torch.int32, device=dev)
+    if out_topk is None:
+        out_topk = torch.empty((B, max(k, 1)), dtype=torch.int32, device=dev)
+    td = _desc(target, "target")
+    _check(lib, lib.spec_greedy_verify(ctypes.byref(td), ctypes.c_void_p(draft_tokens.data_ptr()),
+                                       ctypes.c_void_p(draft_len.data_ptr() if draft_len is not None else None),
+                                       ctypes.c_int32(k), ctypes.c_void_p(out_tokens.data_ptr()),
+                                       ctypes.c_void_p(out_n_accepted.data_ptr()),
+                                       ctypes.c_void_p(out_topk.data_ptr()), _stream_handle(stream, dev)))
+    return out_tokens, out_n_accepted, out_topk[:, :k]
 
 
 def hispec_verify(final, inter, draft, draft_tokens, draft_len=None, temperature=1.0, top_p=1.0, seed=0, *,

@@ -175,18 +175,23 @@ struct Setup {
     Layout lay;
 };
 
+enum Mode { MODE_VERIFY = 0, MODE_SMC = 1, MODE_GREEDY = 2 };
+
 int plan(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_tokens, const int32_t* draft_len,
-         float temperature, float top_p, uint64_t seed, bool smc, void* stream_v, Setup& S) {
+         float temperature, float top_p, uint64_t seed, int mode, void* stream_v, Setup& S) {
+    const bool smc = mode == MODE_SMC, greedy = mode == MODE_GREEDY;
     int rc = check_logits(tl);
     if (rc) return rc;
-    rc = check_logits(dl);
-    if (rc) return rc;
+    if (!greedy) {
+        rc = check_logits(dl);
+        if (rc) return rc;
+    }
     if (!draft_tokens) return SV_EINVAL;
     if (misaligned(draft_tokens, 4) || (draft_len && misaligned(draft_len, 4))) return SV_EALIGN;
-    if (tl->dtype != dl->dtype) return SV_EDTYPE;
+    if (!greedy && tl->dtype != dl->dtype) return SV_EDTYPE;
     const int B = tl->B, V = tl->V, K = tl->P - 1;
     if (B <= 0 || V <= 0 || K < 1 || K > SPECVERIFY_MAX_K) return SV_ESHAPE;
-    if (dl->B != B || dl->V != V || dl->P != K) return SV_ESHAPE;
+    if (!greedy && (dl->B != B || dl->V != V || dl->P != K)) return SV_ESHAPE;
     if (B > (1 << 22) || V > (1 << 24)) return SV_ESHAPE;
     if (!(temperature > 0.f) || !std::isfinite(temperature)) return SV_EINVAL;
     if (!(top_p > 0.f && top_p <= 1.f)) return SV_EINVAL;
@@ -195,7 +200,8 @@ int plan(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_tokens, 
 
     const int dtype = tl->dtype == SV_BF16 ? sv::DT_BF16 : sv::DT_F32;
     const int E = dtype == sv::DT_BF16 ? 2 : 4;
-    const int nslot = 2 * K + 1;
+    // greedy verify reads the target rows only
+    const int nslot = greedy ? K + 1 : 2 * K + 1;
     // statistics pass: chunks of at most `cv` 16-byte vectors per workgroup
     const int64_t nvec_max = (static_cast<int64_t>(V) * E + 15) / 16 + 1;
     int unroll = env_int("SPECVERIFY_STATS_UNROLL", sv::kStatsUnroll);
@@ -214,23 +220,26 @@ int plan(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_tokens, 
         const int forced = env_int("SPECVERIFY_ROW_RUNS", 0);
         if (forced == 1 || forced == 2 || forced == sv::kRunsMax) runs = forced;
     }
-    const int nq = (V + runs * sv::kRunIds - 1) / (runs * sv::kRunIds);
+    const int nq = greedy ? 0 : (V + runs * sv::kRunIds - 1) / (runs * sv::kRunIds);
     const int64_t per_row = static_cast<int64_t>(nslot) * nch + nq;
     if (static_cast<int64_t>(B) * per_row >= (1ll << 31)) return SV_ESHAPE;
     // the statistics kernel clears the row pass's records, a few words each
     if (4ll * nq > static_cast<int64_t>(sv::kThreads) * nslot * nch) return SV_ESHAPE;
 
-    const bool topp = top_p < 1.f;
+    // greedy verify takes its argmaxes and top-k from the candidate lists
+    const bool topp = top_p < 1.f || greedy;
     S.lay = layout(B, nslot, nch, nq, topp, smc);
 
     Params& p = S.p;
     std::memset(&p, 0, sizeof(p));
     p.tgt = static_cast<const uint8_t*>(tl->data);
-    p.dft = static_cast<const uint8_t*>(dl->data);
     p.tsb = tl->stride_b;
     p.tsp = tl->stride_p;
-    p.dsb = dl->stride_b;
-    p.dsp = dl->stride_p;
+    if (!greedy) {
+        p.dft = static_cast<const uint8_t*>(dl->data);
+        p.dsb = dl->stride_b;
+        p.dsp = dl->stride_p;
+    }
     p.tokens = draft_tokens;
     p.dlen = draft_len;
     p.B = B;
@@ -275,8 +284,8 @@ void bind(Setup& S, uint8_t* base) {
 
 // plan + scratch + bind for a single pass.
 int prepare(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_tokens, const int32_t* draft_len,
-            float temperature, float top_p, uint64_t seed, bool smc, void* stream_v, Setup& S) {
-    int rc = plan(tl, dl, draft_tokens, draft_len, temperature, top_p, seed, smc, stream_v, S);
+            float temperature, float top_p, uint64_t seed, int mode, void* stream_v, Setup& S) {
+    int rc = plan(tl, dl, draft_tokens, draft_len, temperature, top_p, seed, mode, stream_v, S);
     if (rc) return rc;
     void* scratch = nullptr;
     rc = get_scratch(S.stream, S.lay.total, &scratch);
@@ -308,7 +317,7 @@ int verify_impl(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_t
     if (!out_tokens || !out_n) return SV_EINVAL;
     if (misaligned(out_tokens, 4) || misaligned(out_n, 4)) return SV_EALIGN;
     Setup S;
-    int rc = prepare(tl, dl, draft_tokens, draft_len, temperature, top_p, seed, false, stream_v, S);
+    int rc = prepare(tl, dl, draft_tokens, draft_len, temperature, top_p, seed, MODE_VERIFY, stream_v, S);
     if (rc) return rc;
     S.p.out_tokens = out_tokens;
     S.p.out_n = out_n;
@@ -330,11 +339,11 @@ int hispec_impl(const sv_logits* fl, const sv_logits* il, const sv_logits* dl, c
     if (!fl || !il) return SV_EINVAL;
     if (fl->B != il->B || fl->V != il->V || fl->P != il->P + 1) return SV_ESHAPE;
     Setup S1, S2;
-    int rc = plan(il, dl, draft_tokens, draft_len, temperature, top_p, seed, false, stream_v, S1);
+    int rc = plan(il, dl, draft_tokens, draft_len, temperature, top_p, seed, MODE_VERIFY, stream_v, S1);
     if (rc) return rc;
     // stage 2's drafts are device scratch bound below; the caller's ids stand
     // in for the host checks
-    rc = plan(fl, il, draft_tokens, nullptr, temperature, top_p, seed, false, stream_v, S2);
+    rc = plan(fl, il, draft_tokens, nullptr, temperature, top_p, seed, MODE_VERIFY, stream_v, S2);
     if (rc) return rc;
     const int B = S1.p.B, K1 = S1.p.K + 1;
     const size_t tok_bytes = align256(static_cast<size_t>(B) * K1 * sizeof(int32_t));
@@ -364,6 +373,31 @@ int hispec_impl(const sv_logits* fl, const sv_logits* il, const sv_logits* dl, c
     return launch_verify(S2);
 }
 
+// Greedy verify: the statistics pass over the target rows with candidate
+// lists (at T = 1, which only scales the list bins), then one workgroup per
+// batch row for the argmaxes, the decision and the top-k.
+int greedy_impl(const sv_logits* tl, const int32_t* draft_tokens, const int32_t* draft_len, int32_t k,
+                int32_t* out_tokens, int32_t* out_n, int32_t* out_topk, void* stream_v) {
+    if (!out_tokens || !out_n || (k > 0 && !out_topk)) return SV_EINVAL;
+    if (k < 0 || k > sv::kMaxTopK) return SV_EINVAL;
+    if (misaligned(out_tokens, 4) || misaligned(out_n, 4) || (out_topk && misaligned(out_topk, 4))) return SV_EALIGN;
+    Setup S;
+    int rc = prepare(tl, nullptr, draft_tokens, draft_len, 1.f, 1.f, 0, MODE_GREEDY, stream_v, S);
+    if (rc) return rc;
+    Params& p = S.p;
+    p.out_tokens = out_tokens;
+    p.out_n = out_n;
+    p.topk = k;
+    p.out_topk = out_topk;
+    const hipStream_t stream = S.stream;
+    rc = timed_launch(sv::KK_STATS, stream, [&](const sv::LaunchEvents& ev) {
+        return sv::launch_stats(p, S.dtype, S.unroll, true, stream, ev);
+    });
+    if (rc) return rc;
+    return timed_launch(sv::KK_RESAMPLE, stream,
+                        [&](const sv::LaunchEvents& ev) { return sv::launch_greedy_rows(p, S.dtype, stream, ev); });
+}
+
 int smc_impl(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_tokens, const double* logw_in,
              float temperature, double ess_fraction, uint64_t seed, int32_t* out_bonus, double* out_logw,
              int32_t* out_ancestor, double* out_ess, int32_t* out_resampled, void* stream_v) {
@@ -373,7 +407,7 @@ int smc_impl(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_toke
         return SV_EALIGN;
     if (std::isnan(ess_fraction)) return SV_EINVAL;
     Setup S;
-    int rc = prepare(tl, dl, draft_tokens, nullptr, temperature, 1.f, seed, true, stream_v, S);
+    int rc = prepare(tl, dl, draft_tokens, nullptr, temperature, 1.f, seed, MODE_SMC, stream_v, S);
     if (rc) return rc;
     Params& p = S.p;
     p.out_tokens = out_bonus;
@@ -414,6 +448,11 @@ int spec_verify_probe(const sv_logits* target_logits, const sv_logits* draft_log
     if (misaligned(probe_pos, 8) || misaligned(probe_row, 8)) return SV_EALIGN;
     return verify_impl(target_logits, draft_logits, draft_tokens, draft_len, temperature, top_p, seed, out_tokens,
                        out_n_accepted, probe_pos, probe_row, stream);
+}
+
+int spec_greedy_verify(const sv_logits* target_logits, const int32_t* draft_tokens, const int32_t* draft_len,
+                       int32_t k, int32_t* out_tokens, int32_t* out_n_accepted, int32_t* out_topk, void* stream) {
+    return greedy_impl(target_logits, draft_tokens, draft_len, k, out_tokens, out_n_accepted, out_topk, stream);
 }
 
 int spec_hispec_verify(const sv_logits* final_logits, const sv_logits* inter_logits, const sv_logits* draft_logits,

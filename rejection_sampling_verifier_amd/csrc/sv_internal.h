@@ -18,6 +18,7 @@ constexpr int kRunsMax = 4;          // runs per thread per resample item, large
 constexpr int kRunIds = kThreads * kRun;  // ids per run of an item (2048)
 constexpr int kRecWords = 4;         // 64-bit words per tagged record
 constexpr int kCand = 256;           // nucleus candidates a statistics chunk lists at most
+constexpr int kMaxTopK = 64;         // greedy verify: largest top-k
 constexpr uint32_t kNoCover = 0xFFFFFFFFu;  // candidate header: the chunk's list covers nothing
 
 enum DType : int { DT_F32 = 0, DT_BF16 = 1 };
@@ -97,6 +98,9 @@ struct Params {
     double* out_ess;              // [1]
     int32_t* out_resampled;       // [1]
     double* smc_cum;              // [B] scratch: cumulative normalised weights
+    // greedy verify: the top-k ids after the emitted token
+    int topk;
+    int32_t* out_topk;            // [B, topk]
     uint64_t* chdr;               // top-p: [B, nslot, nch, kWaves, 2] tagged candidate headers (count, key bound)
     uint64_t* cand;               // top-p: [B, nslot, nch, kCand] candidates (~key << 32 | id), kCand/kWaves per wave
 };
@@ -117,6 +121,9 @@ hipError_t launch_rows(const Params& p, int dtype, bool topp, hipStream_t s, con
 // increments and the bonus draw), then the resampling kernel.
 hipError_t launch_smc_rows(const Params& p, int dtype, hipStream_t s, const LaunchEvents& ev);
 hipError_t launch_smc_resample(const Params& p, hipStream_t s, const LaunchEvents& ev);
+// Greedy verify: one workgroup per batch row after a statistics pass over the
+// target rows (nslot = K + 1) with candidate lists.
+hipError_t launch_greedy_rows(const Params& p, int dtype, hipStream_t s, const LaunchEvents& ev);
 // Two-stage verify: stage 2's draft lengths (n1 + 1) from stage 1's counts.
 hipError_t launch_hispec_link(const int32_t* n1, int32_t* len2, int32_t* out_n1, int B, hipStream_t s);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int unroll, hipStream_t s);

@@ -628,11 +628,14 @@ __device__ __forceinline__ void list_wave_candidates(const Params& P, const RowG
     // top bins first: lane i counts the 9-bit value 511 - i of e
     const double incl = wave_scan_dpp(static_cast<double>(hist[kCandHist - 1 - lane]));
     const int t = __popcll(__ballot(incl <= static_cast<double>(kCandW - kCandSlack)));
+    // tokens in the listed bins: none means the wave's top bin alone holds too
+    // many (the bins above the top one are empty)
+    const double nlisted = t > 0 ? readlane_f64(incl, t - 1) : 0.0;
     float thr = SV_INF;
     uint32_t kw = kNoCover;
     if (o == -SV_INF) {
         kw = 0u;  // no finite logit: nothing to list
-    } else if (t > 0) {
+    } else if (nlisted > 0.0) {
         // the listed bins hold e >= 2^(E-127) * (1 + q/4): l >= (o + log2 of that) / c
         const int eb = 512 - t;
         const int q = eb & 3;
@@ -2023,6 +2026,283 @@ hipError_t launch_smc_rows(const Params& p, int dtype, hipStream_t s, const Laun
 hipError_t launch_smc_resample(const Params& p, hipStream_t s, const LaunchEvents& ev);
 
 // ---------------------------------------------------------------------------
+// Greedy verify (the temperature -> 0 limit of the verify step on the page
+// "Speculative Decoding للمحترف", section "المفهوم بالتقريب": accept drafted
+// tokens the target agrees with, take the target's token at the first
+// disagreement) with the top-k of the last logits after the emitted token
+// (the LogitSpec page, section 2: candidates for the token after next).
+// The statistics pass runs over the target rows only, at T = 1, listing
+// every wave's largest logits with a completeness bound (as for top-p); one
+// workgroup per batch row then takes each row's argmax, the decision and the
+// top-k from those lists.  Where a list cannot decide (a wave's top bin held
+// too many tokens, or the lists hold fewer than k + 1 tokens above their
+// bounds) the workgroup scans the logit row itself.
+// ---------------------------------------------------------------------------
+constexpr int kGreedySel = 1024;  // tokens a top-k selection sorts in LDS
+constexpr int kDistBins = 264;    // log-scaled key distances below the row max
+
+struct GreedyShared {
+    float M[kMaxK + 1];
+    int valid[kMaxK + 1];
+    uint32_t kth[kMaxK + 1];
+    int nocover[kMaxK + 1];
+    int amin[kMaxK + 1];
+    uint32_t hist[kDistBins];
+    unsigned long long list[kGreedySel];
+    uint32_t nlist;
+    int n, bad, tbin, mode;
+    float bv;
+    int bid;
+};
+
+// Monotone log-scaled bin of a key distance d: 0 for d = 0, else 8 bins per
+// octave of d.
+__device__ __forceinline__ int dist_bin(uint32_t d) {
+    if (d == 0u) return 0;
+    const int lz = __clz(d);
+    const int hb = 32 - lz;
+    const uint32_t frac = (d << lz) << 1;  // bits after the leading one
+    return hb * 8 + static_cast<int>(frac >> 29);
+}
+
+// (v, id) comes before (w, jd) in the order logit descending, id ascending.
+__device__ __forceinline__ bool ranks_before(float v, int id, float w, int jd) {
+    return v > w || (v == w && id < jd);
+}
+
+// Block-wide first element in (logit desc, id asc) order of a row among those
+// strictly after (pv, pid) in that order (pass pv = +inf, pid = -1 for the
+// first); returns its id in every thread (-1 if none).  One pass over the row.
+template <int DT>
+__device__ int row_next_ranked(const uint8_t* row, int V, float pv, int pid, GreedyShared& sh) {
+    float bv = -SV_INF;
+    int bid = 0x7FFFFFFF;
+    for_each_vec<DT>(row, V, [&](float l, int64_t id64) {
+        const int id = static_cast<int>(id64);
+        if (id >= 0 && id < V && ranks_before(pv, pid, l, id) && ranks_before(l, id, bv, bid)) {
+            bv = l;
+            bid = id;
+        }
+    });
+    // wave, then block
+    for (int o = 32; o >= 1; o >>= 1) {
+        const float ov = __shfl_xor(bv, o, 64);
+        const int oi = __shfl_xor(bid, o, 64);
+        if (ranks_before(ov, oi, bv, bid)) {
+            bv = ov;
+            bid = oi;
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        sh.bv = -SV_INF;
+        sh.bid = 0x7FFFFFFF;
+    }
+    __syncthreads();
+    for (int w = 0; w < kWaves; ++w) {
+        if ((threadIdx.x >> 6) == w && (threadIdx.x & 63) == 0 && ranks_before(bv, bid, sh.bv, sh.bid)) {
+            sh.bv = bv;
+            sh.bid = bid;
+        }
+        __syncthreads();
+    }
+    const int r = sh.bid;
+    __syncthreads();
+    return r == 0x7FFFFFFF ? -1 : r;
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_greedy_rows(Params P) {
+    __shared__ GreedyShared sh;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int b = blockIdx.x;
+    const int K1 = P.K + 1;
+    bool rowok;
+    const int L = row_len(P, b, rowok);
+    const int x = lane_token(P, b, L);
+    const size_t row0 = static_cast<size_t>(b) * P.nslot;  // logit row j of b is row0 + j
+    if (wv == 0) {
+        // row maxima and validity from the statistics records (lane j)
+        if (lane <= L) {
+            float M = -SV_INF;
+            bool ok = true;
+            for (int c = 0; c < P.nch; ++c) {
+                uint32_t pay[kRecWords];
+                ok = read_record(P.prec + ((row0 + lane) * P.nch + c) * kRecWords, P.tag, pay) && ok;
+                const Partial q = partial_from(pay);
+                M = fmaxf(M, q.m);
+                if (!(q.s < SV_INF) || __builtin_isnan(q.s)) ok = false;
+            }
+            sh.M[lane] = M;
+            sh.valid[lane] = (ok && M > -SV_INF) ? 1 : 0;
+            sh.kth[lane] = 0u;
+            sh.nocover[lane] = 0;
+            sh.amin[lane] = 0x7FFFFFFF;
+        }
+        int bad = rowok ? 0 : 1;
+        if (lane < L && (x < 0 || x >= P.V)) bad = 1;
+        if (lane <= L && !sh.valid[lane]) bad = 1;
+        bad = __ballot(bad) != 0ull ? 1 : 0;
+        if (lane == 0) sh.bad = bad;
+    }
+    __syncthreads();
+    const bool rowbad = sh.bad != 0;
+    if (rowbad) {
+        for (int i = tid; i < K1; i += kThreads) P.out_tokens[static_cast<size_t>(b) * K1 + i] = -1;
+        for (int i = tid; i < P.topk; i += kThreads) P.out_topk[static_cast<size_t>(b) * P.topk + i] = -1;
+        if (tid == 0) P.out_n[b] = -1;
+        return;
+    }
+    // the candidate headers of every row j <= L: bound kth_j, coverage
+    const int nh = (L + 1) * P.nch * kWaves;
+    for (int h = tid; h < nh; h += kThreads) {
+        const int j = h / (P.nch * kWaves);
+        const uint64_t* hw = P.chdr + (row0 * P.nch * kWaves + static_cast<size_t>(h)) * 2;
+        const uint64_t w0 = hw[0], w1 = hw[1];
+        if (!has_tag(w0, P.tag) || !has_tag(w1, P.tag) || static_cast<uint32_t>(w1) == kNoCover)
+            atomicOr(&sh.nocover[j], 1);
+        else
+            atomicMax(&sh.kth[j], static_cast<uint32_t>(w1));
+    }
+    __syncthreads();
+    // a row whose max lies below a bound (a threshold rounded just above a
+    // wave's max) is not covered either
+    if (tid <= L && order_key(sh.M[tid]) < sh.kth[tid]) sh.nocover[tid] = 1;
+    __syncthreads();
+    // argmax of every covered row: the lowest listed id with the max's key
+    // (the max's key is at or above every bound, so all such ids are listed)
+    for (int j = 0; j <= L; ++j) {
+        if (sh.nocover[j]) continue;
+        const uint32_t km = order_key(sh.M[j]);
+        const uint64_t* hdr = P.chdr + ((row0 + j) * P.nch * kWaves + wv) * 2;
+        const uint64_t* lst = P.cand + (row0 + j) * P.nch * kCand;
+        for (int c = 0; c < P.nch; ++c) {
+            const uint32_t n = static_cast<uint32_t>(hdr[static_cast<size_t>(c) * kWaves * 2]);
+            if (static_cast<uint32_t>(lane) < n) {
+                const unsigned long long e = lst[static_cast<size_t>(c) * kCand + tid];
+                if (~static_cast<uint32_t>(e >> 32) == km) atomicMin(&sh.amin[j], static_cast<int>(static_cast<uint32_t>(e)));
+            }
+        }
+    }
+    __syncthreads();
+    // rows a list could not decide: one exact pass each
+    for (int j = 0; j <= L; ++j) {
+        if (!sh.nocover[j]) continue;
+        const int g = row_next_ranked<DT>(row_ptr<DT>(P, true, b, j), P.V, SV_INF, -1, sh);
+        if (tid == 0) sh.amin[j] = g;
+        __syncthreads();
+    }
+    // decision
+    if (wv == 0) {
+        const bool mism = lane < L && x != sh.amin[lane];
+        const unsigned long long mm = __ballot(mism);
+        const int n = mm ? __ffsll(static_cast<long long>(mm)) - 1 : L;
+        for (int i = lane; i < K1; i += 64) {
+            int v = -1;
+            if (i < n) v = P.tokens[static_cast<size_t>(b) * P.K + i];
+            else if (i == n) v = sh.amin[n];
+            P.out_tokens[static_cast<size_t>(b) * K1 + i] = v;
+        }
+        if (lane == 0) {
+            P.out_n[b] = n;
+            sh.n = n;
+        }
+    }
+    __syncthreads();
+    const int k = P.topk;
+    if (k == 0) return;
+    const int n = sh.n;
+    int32_t* out = P.out_topk + static_cast<size_t>(b) * k;
+    // top-(k+1) of row n from its lists: count the listed tokens at or above
+    // the bound by log-scaled key distance below the max, find the bin where
+    // the count reaches k + 1, sort everything up to that bin
+    bool listed = !sh.nocover[n];
+    if (listed) {
+        for (int i = tid; i < kDistBins; i += kThreads) sh.hist[i] = 0u;
+        if (tid == 0) sh.nlist = 0u;
+        __syncthreads();
+        const uint32_t km = order_key(sh.M[n]), kt = sh.kth[n];
+        const uint64_t* hdr = P.chdr + ((row0 + n) * P.nch * kWaves + wv) * 2;
+        const uint64_t* lst = P.cand + (row0 + n) * P.nch * kCand;
+        for (int c = 0; c < P.nch; ++c) {
+            const uint32_t cn = static_cast<uint32_t>(hdr[static_cast<size_t>(c) * kWaves * 2]);
+            if (static_cast<uint32_t>(lane) < cn) {
+                const uint32_t key = ~static_cast<uint32_t>(lst[static_cast<size_t>(c) * kCand + tid] >> 32);
+                if (key >= kt) atomicAdd(&sh.hist[dist_bin(km - key)], 1u);
+            }
+        }
+        __syncthreads();
+        if (tid == 0) {
+            uint32_t cum = 0u;
+            int t = -1;
+            for (int i = 0; i < kDistBins; ++i) {
+                cum += sh.hist[i];
+                if (cum >= static_cast<uint32_t>(k + 1)) {
+                    t = i;
+                    break;
+                }
+            }
+            sh.tbin = (t >= 0 && cum <= static_cast<uint32_t>(kGreedySel)) ? t : -1;
+        }
+        __syncthreads();
+        const int tb = sh.tbin;
+        listed = tb >= 0;
+        if (listed) {
+            for (int c = 0; c < P.nch; ++c) {
+                const uint32_t cn = static_cast<uint32_t>(hdr[static_cast<size_t>(c) * kWaves * 2]);
+                if (static_cast<uint32_t>(lane) < cn) {
+                    const unsigned long long e = lst[static_cast<size_t>(c) * kCand + tid];
+                    const uint32_t key = ~static_cast<uint32_t>(e >> 32);
+                    if (key >= kt && dist_bin(km - key) <= tb) {
+                        const uint32_t at = atomicAdd(&sh.nlist, 1u);
+                        if (at < static_cast<uint32_t>(kGreedySel)) sh.list[at] = e;
+                    }
+                }
+            }
+            __syncthreads();
+            const int cnt = static_cast<int>(min(sh.nlist, static_cast<uint32_t>(kGreedySel)));
+            int np2 = 1;
+            while (np2 < cnt) np2 <<= 1;
+            for (int i = cnt + tid; i < np2; i += kThreads) sh.list[i] = ~0ull;
+            __syncthreads();
+            for (int kk = 2; kk <= np2; kk <<= 1) {
+                for (int jj = kk >> 1; jj > 0; jj >>= 1) {
+                    for (int i = tid; i < np2; i += kThreads) {
+                        const int ij = i ^ jj;
+                        if (ij > i) {
+                            const unsigned long long a = sh.list[i], c2 = sh.list[ij];
+                            const bool up = (i & kk) == 0;
+                            if ((a > c2) == up) {
+                                sh.list[i] = c2;
+                                sh.list[ij] = a;
+                            }
+                        }
+                    }
+                    __syncthreads();
+                }
+            }
+            for (int i = tid; i < k; i += kThreads)
+                out[i] = i + 1 < cnt ? static_cast<int32_t>(static_cast<uint32_t>(sh.list[i + 1])) : -1;
+            return;
+        }
+    }
+    // exact passes over row n: rank by rank
+    const uint8_t* rown = row_ptr<DT>(P, true, b, n);
+    float pv = SV_INF;
+    int pid = -1;
+    for (int r = 0; r <= k; ++r) {
+        const int id = row_next_ranked<DT>(rown, P.V, pv, pid, sh);
+        if (id < 0) {
+            for (int i = max(r - 1, 0) + tid; i < k; i += kThreads) out[i] = -1;
+            break;
+        }
+        if (r > 0 && tid == 0) out[r - 1] = id;
+        pv = load_elem<DT>(rown, id);
+        pid = id;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Two-stage (hierarchical) verify (page "HiSpec: Hierarchical Speculative
 // Decoding for LLMs", section 2): between the two verify passes, the tokens
 // stage 1 emitted become stage 2's drafts, n1 + 1 of them per row (a row
@@ -2132,6 +2412,13 @@ hipError_t launch_smc_rows(const Params& p, int dtype, hipStream_t s, const Laun
     if (p.runs == 1) launch_smc_rows_r<1>(p, dtype, s, ev);
     else if (p.runs == 2) launch_smc_rows_r<2>(p, dtype, s, ev);
     else launch_smc_rows_r<kRunsMax>(p, dtype, s, ev);
+    return hipGetLastError();
+}
+
+hipError_t launch_greedy_rows(const Params& p, int dtype, hipStream_t s, const LaunchEvents& ev) {
+    const unsigned grid = static_cast<unsigned>(p.B);
+    if (dtype == DT_BF16) launch(k_greedy_rows<DT_BF16>, grid, kThreads, s, ev, p);
+    else launch(k_greedy_rows<DT_F32>, grid, kThreads, s, ev, p);
     return hipGetLastError();
 }
 

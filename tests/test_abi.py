@@ -32,7 +32,7 @@ def declared_functions():
 def test_header_declares_the_interface():
     names = declared_functions()
     assert "spec_verify" in names and "spec_verify_probe" in names and "spec_smc_step" in names
-    assert "spec_hispec_verify" in names
+    assert "spec_hispec_verify" in names and "spec_greedy_verify" in names
     assert set(names) == set(binding.EXPORTS)
 
 
@@ -116,3 +116,19 @@ def _hispec(lib, B=3, K=2, V=64, fP=None, iP=None, T=1.0, fdata=0x1000, idata=0x
 ])
 def test_hispec_host_validation(lib, kw, code):
     assert _hispec(lib, **kw) == code
+
+
+def _greedy(lib, B=3, K=2, V=64, k=5, tdata=0x1000, tokens=0x4000, out=0x5000, outn=0x6000, topk=0x7000, dtype=0):
+    t = binding.SvLogits(tdata, dtype, B, K + 1, V, (K + 1) * V, V)
+    v = ctypes.c_void_p
+    return lib.spec_greedy_verify(ctypes.byref(t), v(tokens), v(None), ctypes.c_int32(k), v(out), v(outn), v(topk),
+                                  v(None))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(out=0), -1), (dict(outn=0), -1), (dict(tokens=0), -1), (dict(tdata=0), -1), (dict(topk=0), -1),
+    (dict(k=-1), -1), (dict(k=65), -1), (dict(K=0), -2), (dict(K=17), -2), (dict(dtype=5), -3),
+    (dict(out=0x5002), -6), (dict(topk=0x7001), -6),
+])
+def test_greedy_host_validation(lib, kw, code):
+    assert _greedy(lib, **kw) == code

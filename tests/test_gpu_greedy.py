@@ -1,0 +1,110 @@
+"""GPU parity of greedy verify with the next-next-token top-k:
+spec_greedy_verify against the float64 oracle (oracle.greedy_verify) on the
+same seeded inputs, through the C ABI.  Greedy decisions are exact
+comparisons, so every row must match exactly: accepted counts, emitted
+tokens and the top-k ids."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import dev_array, say
+from rejection_sampling_verifier_amd import binding
+from rejection_sampling_verifier_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    binding.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def _drafts(target_f32, s, agree=0.7):
+    """Drafts that agree with the target's argmax with probability `agree`."""
+    rng = np.random.default_rng(4000 + s)
+    B, K1, V = target_f32.shape
+    am = np.argmax(target_f32[:, : K1 - 1], axis=-1)
+    rnd = rng.integers(0, V, size=am.shape)
+    return np.where(rng.random(am.shape) < agree, am, rnd).astype(np.int32)
+
+
+def _check(t, x, dl, k, label):
+    B, K1 = t.shape[0], t.shape[1]
+    say(f"[greedy] {label} B={B} K={K1 - 1} V={t.shape[2]} {t.dtype} k={k}")
+    xt = torch.from_numpy(np.ascontiguousarray(x, dtype=np.int32)).cuda()
+    dlt = None if dl is None else torch.from_numpy(np.ascontiguousarray(dl, dtype=np.int32)).cuda()
+    tok, n, tk = binding.greedy_verify(dev_array(t), xt, dlt, k)
+    torch.cuda.synchronize()
+    tok, n, tk = tok.cpu().numpy(), n.cpu().numpy(), tk.cpu().numpy()
+    r = oracle.greedy_verify(t, x, dl, k)
+    assert np.array_equal(n, r.n_accepted), (label, n, r.n_accepted)
+    assert np.array_equal(tok, r.tokens), label
+    if k:
+        bad = np.nonzero(np.any(tk != r.topk, axis=1))[0]
+        assert bad.size == 0, (label, bad[:4], tk[bad[:1]], r.topk[bad[:1]])
+    say(f"    mean n={np.mean(r.n_accepted):.2f}")
+    return r
+
+
+def _f32(t):
+    return W.bf16_bits_to_f32(t) if t.dtype == np.uint16 else t
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("k", [10, 60])
+def test_greedy_small(dtype, k):
+    for s in range(3):
+        inp = W.synthetic(16, 4, 1000, dtype=dtype, seed=s, gen_seed=6000 + s)
+        x = _drafts(_f32(inp.target), s)
+        _check(inp.target, x, None, k, f"small s={s}")
+
+
+def test_greedy_several_chunks_ragged():
+    for s in range(2):
+        # padded positions hold NaN and are never read; their drafted ids are -1
+        inp = W.make_inputs(3, 20 + s, B=24, V=40009)
+        x = _drafts(np.nan_to_num(W.bf16_bits_to_f32(inp.target), nan=-1e30), s)
+        x = np.where(inp.draft_tokens >= 0, x, -1)
+        _check(inp.target, x, inp.draft_len, 60, f"ragged V=40009 s={s}")
+
+
+def test_greedy_ties_and_flat_rows():
+    rng = np.random.default_rng(9)
+    B, K, V = 6, 3, 3000
+    t = (np.round(rng.normal(0, 1.5, size=(B, K + 1, V)) * 2) / 2).astype(np.float32)  # heavy ties
+    t[4] = 0.0                      # flat rows: every list overflows
+    t[5, :, :] = -1.0
+    t[5, :, 2500:2600] = 2.0        # a 100-way tie at the top of one wave
+    x = _drafts(t, 9, agree=0.8)
+    _check(W.f32_to_bf16_bits(t), x, None, 60, "ties and flat rows, bf16")
+    _check(t, x, None, 17, "ties and flat rows, fp32")
+
+
+def test_greedy_small_vocabulary_and_k0():
+    inp = W.synthetic(5, 2, 40, dtype="f32", seed=3, gen_seed=6100)
+    x = _drafts(inp.target, 3)
+    _check(inp.target, x, None, 60, "V=40 < k+1")
+    _check(inp.target, x, None, 0, "k=0")
+
+
+def test_greedy_invalid_rows():
+    inp = W.synthetic(6, 3, 700, dtype="f32", seed=4, gen_seed=6200)
+    t = inp.target.copy()
+    x = _drafts(t, 4)
+    x[1, 0] = 700
+    t[2, 1, 5] = np.nan
+    t[3, 0, :] = -np.inf
+    dl = np.array([3, 3, 3, 3, 4, -1], np.int32)
+    r = _check(t, x, dl, 8, "invalid rows")
+    assert list(r.n_accepted[[1, 2, 3, 4, 5]]) == [-1] * 5
+
+
+def test_greedy_full_size():
+    inp = W.make_inputs(2, 11)
+    x = _drafts(W.bf16_bits_to_f32(inp.target), 11)
+    _check(inp.target, x, None, 60, "full size")

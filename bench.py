@@ -269,6 +269,111 @@ def smc_bench(args, binding, torch, dev, sets, dsets, logical, stream):
 
 
 # ---------------------------------------------------------------------------
+# Greedy verify timing (--greedy): the batched workload's target logits, drafts
+# that agree with the target's argmax at 70 % of positions, top-60
+# ---------------------------------------------------------------------------
+GREEDY_TOPK = 60
+
+
+def _greedy_drafts(inp, s):
+    import numpy as np
+
+    from rejection_sampling_verifier_amd import workloads
+
+    rng = np.random.default_rng(0x6EED + s)
+    t = workloads.bf16_bits_to_f32(inp.target[:, : inp.K])
+    am = np.argmax(t, axis=-1)
+    return np.where(rng.random(am.shape) < 0.7, am, rng.integers(0, inp.V, size=am.shape)).astype(np.int32)
+
+
+def _oracle_greedy(args):
+    import oracle
+
+    si, r0, r1 = args
+    inp, x = _SAMPLE[si]
+    oracle.greedy_verify(inp.target[r0:r1], x[r0:r1], None, GREEDY_TOPK)
+    return (r1 - r0) * inp.K
+
+
+def greedy_bench(args, binding, torch, dev, sets):
+    import numpy as np
+
+    B, K, V = sets[0].B, sets[0].K, sets[0].V
+    xs = [_greedy_drafts(inp, s) for s, inp in enumerate(sets)]
+
+    def put(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    ds = [(put(inp.target), torch.from_numpy(x).to(dev)) for inp, x in zip(sets, xs)]
+    outs = [(torch.empty((B, K + 1), dtype=torch.int32, device=dev), torch.empty((B,), dtype=torch.int32, device=dev),
+             torch.empty((B, GREEDY_TOPK), dtype=torch.int32, device=dev)) for _ in range(N_SETS)]
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        t, x = ds[i % N_SETS]
+        o = outs[i % N_SETS]
+        binding.greedy_verify(t, x, None, GREEDY_TOPK, stream=stream, out_tokens=o[0], out_n_accepted=o[1],
+                              out_topk=o[2])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = ev0.elapsed_time(ev1) / args.steps
+    binding.profile_read()
+    binding.profile_enable(True)
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    binding.profile_enable(False)
+    prof = binding.profile_read()
+    us = {k: prof[k][0] / prof[k][1] * 1e3 for k in ("stats", "rows") if prof[k][1]}
+    logical = B * (K + 1) * V * 2  # target rows only
+    print(f"[bench] greedy {args.steps} steps: {ms_step * 1e3:.2f} us/step; kernels {us}", file=sys.stderr,
+          flush=True)
+    cpu = None
+    if not args.no_cpu_baseline:
+        global _SAMPLE
+        _SAMPLE = list(zip(sets, xs))
+        cores = max(1, min(16, os.cpu_count() or 1))
+        work = [(s, r, r + 1) for s in range(N_SETS) for r in range(B)]
+        positions, dt, passes = _timed_passes(_oracle_greedy, work, cores)
+        cpu = {"value": positions / dt, "unit": "positions/s", "cores": cores, "kind": "oracle",
+               "sample": f"{len(work)} rows of the batched workload, {passes} passes ({positions} draft positions), "
+                         f"float64 NumPy oracle, one row per task over {cores} processes, {dt:.1f} s wall"}
+    stats_s = us["stats"] * 1e-6
+    line = {
+        "metric": "greedy verify + top-60: draft positions/sec + logits HBM GB/s (% of peak) at B=64,K=5,V=128256",
+        "value": round(B * K / (ms_step / 1e3), 1),
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "greedy verify, batched B=64 K=5 V=128256 bf16 target logits, top-60",
+                   "B": B, "K": K, "V": V, "k": GREEDY_TOPK, "logical_bytes_per_step": logical,
+                   "logits_GBps": round(logical / (ms_step / 1e3) / 1e9, 1)},
+        "roofline": {"bound": "hbm", "achieved": round(logical / stats_s / 1e9, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(logical / stats_s / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "k_stats<…, true> over the target rows", "kernel_us": round(us["stats"], 3),
+                     "other_kernels_us": {"k_greedy_rows": round(us["rows"], 3)}},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+# ---------------------------------------------------------------------------
 # Two-stage verify timing (--hispec): three exit layers of one synthetic
 # early-exit model, B=64, K=5, V=128256, bf16, T=0.7
 # ---------------------------------------------------------------------------
@@ -380,6 +485,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=192)
     ap.add_argument("--workload", type=int, default=WORKLOAD_CFG,
                     help="seeded workload to time (default: the batched B=64 K=5 V=128256 bf16 one)")
+    ap.add_argument("--greedy", action="store_true",
+                    help="time greedy verify with the top-60 (spec_greedy_verify) on the batched target logits")
     ap.add_argument("--hispec", action="store_true",
                     help="time the two-stage verify (spec_hispec_verify) on three synthetic exit layers")
     ap.add_argument("--smc", action="store_true",
@@ -431,6 +538,9 @@ def main():
 
     if args.smc:
         smc_bench(args, binding, torch, dev, sets, dsets, logical, stream)
+        return
+    if args.greedy:
+        greedy_bench(args, binding, torch, dev, sets)
         return
 
     def step(i):

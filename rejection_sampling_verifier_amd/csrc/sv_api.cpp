@@ -46,7 +46,7 @@ Layout layout(int64_t B, int nslot, int nch, int nq, bool topp, bool smc) {
     off = align256(off + static_cast<size_t>(B) * nq * sv::kRecWords * sizeof(uint64_t));
     const size_t chunks = topp ? static_cast<size_t>(B) * nslot * nch : 0;
     L.chdr = off;
-    off = align256(off + chunks * sv::kWaves * 2 * sizeof(uint64_t));
+    off = align256(off + chunks * sv::kWaves * 4 * sizeof(uint64_t));  // four tagged words per wave
     L.cand = off;
     off = align256(off + chunks * sv::kCand * sizeof(uint64_t));
     L.cum = off;

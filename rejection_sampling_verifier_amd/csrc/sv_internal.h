@@ -101,7 +101,8 @@ struct Params {
     // greedy verify: the top-k ids after the emitted token
     int topk;
     int32_t* out_topk;            // [B, topk]
-    uint64_t* chdr;               // top-p: [B, nslot, nch, kWaves, 2] tagged candidate headers (count, key bound)
+    uint64_t* chdr;               // top-p: [B, nslot, nch, kWaves, 4] tagged candidate headers (count, key bound,
+                                  // key of the wave's max, lowest listed id holding it)
     uint64_t* cand;               // top-p: [B, nslot, nch, kCand] candidates (~key << 32 | id), kCand/kWaves per wave
 };
 

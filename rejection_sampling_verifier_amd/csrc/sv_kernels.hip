@@ -527,6 +527,9 @@ __device__ __forceinline__ void mask_edge_raw(uint4& v, int64_t k, int head, int
 // top bin alone holds too many tokens, or whose list overflows, records
 // kNoCover.
 constexpr uint32_t kCandLowBits = 448u << 21;  // e >= 2^-15
+// 64-bit words of a wave's candidate header: count, key bound, the key of the
+// wave's max logit, the lowest listed id holding it (each tagged)
+constexpr int kHdrWords = 4;
 constexpr int kCandW = kCand / kWaves;         // list slots per wave
 constexpr int kCandSlack = 8;
 constexpr int kCandHist = 64;                  // per-wave bins: top 9 bits of e in [448, 512)
@@ -623,7 +626,8 @@ __device__ __forceinline__ void reduce_lane(const RowGrid& g, uint4* raw, int64_
 // bound) goes to header `hdr`.
 template <int DT, int U>
 __device__ __forceinline__ void list_wave_candidates(const Params& P, const RowGrid& g, uint4* raw, int64_t k0, float o,
-                                                     const uint32_t* hist, uint64_t* stage, size_t slot0, size_t hdr) {
+                                                     float m, const uint32_t* hist, uint64_t* stage, size_t slot0,
+                                                     size_t hdr) {
     const int tid = threadIdx.x, lane = tid & 63;
     // top bins first: lane i counts the 9-bit value 511 - i of e
     const double incl = wave_scan_dpp(static_cast<double>(hist[kCandHist - 1 - lane]));
@@ -670,15 +674,24 @@ __device__ __forceinline__ void list_wave_candidates(const Params& P, const RowG
     }
     const bool over = base > static_cast<uint32_t>(kCandW);
     // same-wave LDS order: the stage is complete for this wave's lanes; the
-    // entries leave as (~key << 32 | id)
+    // entries leave as (~key << 32 | id).  The wave's max logit and the lowest
+    // listed id holding it go into the header too.
+    const float mw = wave_max_dpp(m);
+    int amax = 0x7FFFFFFF;
     if (!over && static_cast<uint32_t>(lane) < base) {
         const uint64_t st = stage[lane];
-        const uint32_t key = order_key(__uint_as_float(static_cast<uint32_t>(st >> 32)));
+        const float v = __uint_as_float(static_cast<uint32_t>(st >> 32));
+        const uint32_t key = order_key(v);
         P.cand[slot0 + lane] = (static_cast<uint64_t>(~key) << 32) | static_cast<uint32_t>(st);
+        if (v == mw) amax = static_cast<int>(static_cast<uint32_t>(st));
     }
-    if (lane == 0) {
-        P.chdr[2 * hdr] = tagged(P.tag, over ? 0u : base);
-        P.chdr[2 * hdr + 1] = tagged(P.tag, over ? kNoCover : kw);
+    amax = wave_min_int_dpp(amax);
+    if (lane < kHdrWords) {
+        const uint32_t v = lane == 0 ? (over ? 0u : base)
+                           : lane == 1 ? (over ? kNoCover : kw)
+                           : lane == 2 ? order_key(mw)
+                                       : static_cast<uint32_t>(amax);
+        P.chdr[kHdrWords * hdr + lane] = tagged(P.tag, v);
     }
 }
 
@@ -738,7 +751,8 @@ __device__ __forceinline__ void stats_item(const Params& P, int b, int slot, int
                              lx, m, o, sl);
     if (CAND) {
         const size_t ci = (static_cast<size_t>(b) * P.nslot + slot) * P.nch + chunk;
-        list_wave_candidates<DT, U>(P, g, raw, k0, o, hist, sh_stage[wv], ci * kCand + wv * kCandW, ci * kWaves + wv);
+        list_wave_candidates<DT, U>(P, g, raw, k0, o, m, hist, sh_stage[wv], ci * kCand + wv * kCandW,
+                                    ci * kWaves + wv);
     }
     // the one lane holding the drafted id's vector hands its logit over,
     // tagged with this workgroup's item (LDS is not cleared between
@@ -1273,7 +1287,7 @@ __device__ bool select_from_candidates(const Params& P, int rvi, uint32_t kth, f
     const double Tm = static_cast<double>(P.top_p) * S;
     // thread tid reads slot tid of every chunk's list: slot tid & 63 of the
     // list of statistics wave tid >> 6
-    const uint64_t* hdr = P.chdr + (static_cast<size_t>(rvi) * P.nch * kWaves + (tid >> 6)) * 2;
+    const uint64_t* hdr = P.chdr + (static_cast<size_t>(rvi) * P.nch * kWaves + (tid >> 6)) * kHdrWords;
     const uint64_t* lst = P.cand + static_cast<size_t>(rvi) * P.nch * kCand;
     const uint32_t slot = static_cast<uint32_t>(tid & 63);
     for (int i = tid; i < kGapBins; i += kThreads) sh.mass[i] = 0.0;
@@ -1295,7 +1309,7 @@ __device__ bool select_from_candidates(const Params& P, int rvi, uint32_t kth, f
 #pragma unroll
                 for (int q = 0; q < kCandBatch; ++q) {
                     const int c = min(c0 + q, P.nch - 1);
-                    n[q] = c0 + q < P.nch ? static_cast<uint32_t>(hdr[static_cast<size_t>(c) * kWaves * 2]) : 0u;
+                    n[q] = c0 + q < P.nch ? static_cast<uint32_t>(hdr[static_cast<size_t>(c) * kWaves * kHdrWords]) : 0u;
                     e[q] = lst[static_cast<size_t>(c) * kCand + tid];
                 }
             }
@@ -1331,11 +1345,11 @@ __device__ bool select_from_candidates(const Params& P, int rvi, uint32_t kth, f
 // Largest candidate key bound of logit row rvi over its chunks, or kNoCover
 // when a chunk's list is incomplete or its header is not this call's.
 __device__ uint32_t candidate_bound(const Params& P, int rvi, int lane) {
-    const uint64_t* hdr = P.chdr + static_cast<size_t>(rvi) * P.nch * kWaves * 2;
+    const uint64_t* hdr = P.chdr + static_cast<size_t>(rvi) * P.nch * kWaves * kHdrWords;
     uint32_t kth = 0u;
     int bad = 0;
     for (int c = lane; c < P.nch * kWaves; c += 64) {
-        const uint64_t w0 = hdr[2 * c], w1 = hdr[2 * c + 1];
+        const uint64_t w0 = hdr[kHdrWords * c], w1 = hdr[kHdrWords * c + 1];
         if (!has_tag(w0, P.tag) || !has_tag(w1, P.tag) || static_cast<uint32_t>(w1) == kNoCover) bad = 1;
         kth = max(kth, static_cast<uint32_t>(w1));
     }
@@ -2121,11 +2135,16 @@ __global__ __launch_bounds__(kThreads) void k_greedy_rows(Params P) {
     const int L = row_len(P, b, rowok);
     const int x = lane_token(P, b, L);
     const size_t row0 = static_cast<size_t>(b) * P.nslot;  // logit row j of b is row0 + j
+    if (tid <= L) {
+        sh.kth[tid] = 0u;
+        sh.nocover[tid] = 0;
+        sh.amin[tid] = 0x7FFFFFFF;
+    }
     if (wv == 0) {
         // row maxima and validity from the statistics records (lane j)
+        bool ok = true;
+        float M = -SV_INF;
         if (lane <= L) {
-            float M = -SV_INF;
-            bool ok = true;
             for (int c = 0; c < P.nch; ++c) {
                 uint32_t pay[kRecWords];
                 ok = read_record(P.prec + ((row0 + lane) * P.nch + c) * kRecWords, P.tag, pay) && ok;
@@ -2134,55 +2153,58 @@ __global__ __launch_bounds__(kThreads) void k_greedy_rows(Params P) {
                 if (!(q.s < SV_INF) || __builtin_isnan(q.s)) ok = false;
             }
             sh.M[lane] = M;
-            sh.valid[lane] = (ok && M > -SV_INF) ? 1 : 0;
-            sh.kth[lane] = 0u;
-            sh.nocover[lane] = 0;
-            sh.amin[lane] = 0x7FFFFFFF;
         }
         int bad = rowok ? 0 : 1;
         if (lane < L && (x < 0 || x >= P.V)) bad = 1;
-        if (lane <= L && !sh.valid[lane]) bad = 1;
+        if (lane <= L && !(ok && M > -SV_INF)) bad = 1;
         bad = __ballot(bad) != 0ull ? 1 : 0;
         if (lane == 0) sh.bad = bad;
     }
     __syncthreads();
-    const bool rowbad = sh.bad != 0;
-    if (rowbad) {
+    if (sh.bad) {
         for (int i = tid; i < K1; i += kThreads) P.out_tokens[static_cast<size_t>(b) * K1 + i] = -1;
         for (int i = tid; i < P.topk; i += kThreads) P.out_topk[static_cast<size_t>(b) * P.topk + i] = -1;
         if (tid == 0) P.out_n[b] = -1;
         return;
     }
-    // the candidate headers of every row j <= L: bound kth_j, coverage
-    const int nh = (L + 1) * P.nch * kWaves;
-    for (int h = tid; h < nh; h += kThreads) {
-        const int j = h / (P.nch * kWaves);
-        const uint64_t* hw = P.chdr + (row0 * P.nch * kWaves + static_cast<size_t>(h)) * 2;
-        const uint64_t w0 = hw[0], w1 = hw[1];
-        if (!has_tag(w0, P.tag) || !has_tag(w1, P.tag) || static_cast<uint32_t>(w1) == kNoCover)
-            atomicOr(&sh.nocover[j], 1);
-        else
-            atomicMax(&sh.kth[j], static_cast<uint32_t>(w1));
-    }
-    __syncthreads();
-    // a row whose max lies below a bound (a threshold rounded just above a
-    // wave's max) is not covered either
-    if (tid <= L && order_key(sh.M[tid]) < sh.kth[tid]) sh.nocover[tid] = 1;
-    __syncthreads();
-    // argmax of every covered row: the lowest listed id with the max's key
-    // (the max's key is at or above every bound, so all such ids are listed)
-    for (int j = 0; j <= L; ++j) {
-        if (sh.nocover[j]) continue;
-        const uint32_t km = order_key(sh.M[j]);
-        const uint64_t* hdr = P.chdr + ((row0 + j) * P.nch * kWaves + wv) * 2;
-        const uint64_t* lst = P.cand + (row0 + j) * P.nch * kCand;
-        for (int c = 0; c < P.nch; ++c) {
-            const uint32_t n = static_cast<uint32_t>(hdr[static_cast<size_t>(c) * kWaves * 2]);
-            if (static_cast<uint32_t>(lane) < n) {
-                const unsigned long long e = lst[static_cast<size_t>(c) * kCand + tid];
-                if (~static_cast<uint32_t>(e >> 32) == km) atomicMin(&sh.amin[j], static_cast<int>(static_cast<uint32_t>(e)));
+    // the wave headers of every row j <= L: coverage, bound, max key and the
+    // lowest listed id holding it
+    const int per_row = P.nch * kWaves;
+    const int nh = (L + 1) * per_row;
+    uint32_t hkey[3];
+    int hid[3], hj[3];
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+        const int h = tid + q * kThreads;
+        hj[q] = -1;
+        if (h < nh) {
+            const uint64_t* hw = P.chdr + (row0 * per_row + static_cast<size_t>(h)) * kHdrWords;
+            const uint64_t w0 = hw[0], w1 = hw[1], w2 = hw[2], w3 = hw[3];
+            const int j = h / per_row;
+            hj[q] = j;
+            hkey[q] = static_cast<uint32_t>(w2);
+            hid[q] = static_cast<int>(static_cast<uint32_t>(w3));
+            if (!has_tag(w0, P.tag) || !has_tag(w1, P.tag) || !has_tag(w2, P.tag) || !has_tag(w3, P.tag) ||
+                static_cast<uint32_t>(w1) == kNoCover) {
+                atomicOr(&sh.nocover[j], 1);
+            } else {
+                atomicMax(&sh.kth[j], static_cast<uint32_t>(w1));
             }
         }
+    }
+    for (int h = tid + 3 * kThreads; h < nh; h += kThreads) {
+        // more than 3 headers per thread (very large vocabularies): coverage only
+        atomicOr(&sh.nocover[h / per_row], 1);
+    }
+    __syncthreads();
+    // argmax of a covered row: every wave lists its max, so the row's argmax
+    // is the lowest header id among the headers carrying the row's max key
+    if (tid <= L && order_key(sh.M[tid]) < sh.kth[tid]) sh.nocover[tid] = 1;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+        const int j = hj[q];
+        if (j >= 0 && !sh.nocover[j] && hkey[q] == order_key(sh.M[j])) atomicMin(&sh.amin[j], hid[q]);
     }
     __syncthreads();
     // rows a list could not decide: one exact pass each
@@ -2215,51 +2237,63 @@ __global__ __launch_bounds__(kThreads) void k_greedy_rows(Params P) {
     int32_t* out = P.out_topk + static_cast<size_t>(b) * k;
     // top-(k+1) of row n from its lists: count the listed tokens at or above
     // the bound by log-scaled key distance below the max, find the bin where
-    // the count reaches k + 1, sort everything up to that bin
+    // the count reaches k + 1, sort everything up to that bin.  Slot tid of
+    // each chunk's list (slot tid & 63 of wave tid >> 6), eight chunks per
+    // batch of loads.
     bool listed = !sh.nocover[n];
     if (listed) {
         for (int i = tid; i < kDistBins; i += kThreads) sh.hist[i] = 0u;
         if (tid == 0) sh.nlist = 0u;
         __syncthreads();
         const uint32_t km = order_key(sh.M[n]), kt = sh.kth[n];
-        const uint64_t* hdr = P.chdr + ((row0 + n) * P.nch * kWaves + wv) * 2;
+        const uint64_t* hdr = P.chdr + ((row0 + n) * per_row + wv) * kHdrWords;
         const uint64_t* lst = P.cand + (row0 + n) * P.nch * kCand;
-        for (int c = 0; c < P.nch; ++c) {
-            const uint32_t cn = static_cast<uint32_t>(hdr[static_cast<size_t>(c) * kWaves * 2]);
-            if (static_cast<uint32_t>(lane) < cn) {
-                const uint32_t key = ~static_cast<uint32_t>(lst[static_cast<size_t>(c) * kCand + tid] >> 32);
-                if (key >= kt) atomicAdd(&sh.hist[dist_bin(km - key)], 1u);
-            }
-        }
-        __syncthreads();
-        if (tid == 0) {
-            uint32_t cum = 0u;
-            int t = -1;
-            for (int i = 0; i < kDistBins; ++i) {
-                cum += sh.hist[i];
-                if (cum >= static_cast<uint32_t>(k + 1)) {
-                    t = i;
-                    break;
+        // pass 0 counts, pass 1 collects up to the chosen bin
+        for (int pass = 0; pass < 2; ++pass) {
+            const int tb = sh.tbin;
+            for (int c0 = 0; c0 < P.nch; c0 += 8) {
+                unsigned long long e[8];
+                uint32_t cn[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const int cc = min(c0 + q, P.nch - 1);
+                    cn[q] = c0 + q < P.nch ? static_cast<uint32_t>(hdr[static_cast<size_t>(cc) * kWaves * kHdrWords]) : 0u;
+                    e[q] = lst[static_cast<size_t>(cc) * kCand + tid];
                 }
-            }
-            sh.tbin = (t >= 0 && cum <= static_cast<uint32_t>(kGreedySel)) ? t : -1;
-        }
-        __syncthreads();
-        const int tb = sh.tbin;
-        listed = tb >= 0;
-        if (listed) {
-            for (int c = 0; c < P.nch; ++c) {
-                const uint32_t cn = static_cast<uint32_t>(hdr[static_cast<size_t>(c) * kWaves * 2]);
-                if (static_cast<uint32_t>(lane) < cn) {
-                    const unsigned long long e = lst[static_cast<size_t>(c) * kCand + tid];
-                    const uint32_t key = ~static_cast<uint32_t>(e >> 32);
-                    if (key >= kt && dist_bin(km - key) <= tb) {
-                        const uint32_t at = atomicAdd(&sh.nlist, 1u);
-                        if (at < static_cast<uint32_t>(kGreedySel)) sh.list[at] = e;
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    const uint32_t key = ~static_cast<uint32_t>(e[q] >> 32);
+                    if (static_cast<uint32_t>(lane) < cn[q] && key >= kt) {
+                        const int db = dist_bin(km - key);
+                        if (pass == 0) {
+                            atomicAdd(&sh.hist[db], 1u);
+                        } else if (db <= tb) {
+                            const uint32_t at = atomicAdd(&sh.nlist, 1u);
+                            if (at < static_cast<uint32_t>(kGreedySel)) sh.list[at] = e[q];
+                        }
                     }
                 }
             }
             __syncthreads();
+            if (pass == 0) {
+                if (tid == 0) {
+                    uint32_t cum = 0u;
+                    int t = -1;
+                    for (int i = 0; i < kDistBins; ++i) {
+                        cum += sh.hist[i];
+                        if (cum >= static_cast<uint32_t>(k + 1)) {
+                            t = i;
+                            break;
+                        }
+                    }
+                    sh.tbin = (t >= 0 && cum <= static_cast<uint32_t>(kGreedySel)) ? t : -1;
+                }
+                __syncthreads();
+                if (sh.tbin < 0) break;  // too few listed, or too many to sort: exact passes
+            }
+        }
+        listed = sh.tbin >= 0;
+        if (listed) {
             const int cnt = static_cast<int>(min(sh.nlist, static_cast<uint32_t>(kGreedySel)));
             int np2 = 1;
             while (np2 < cnt) np2 <<= 1;

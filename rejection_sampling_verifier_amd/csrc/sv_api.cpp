@@ -391,7 +391,7 @@ int greedy_impl(const sv_logits* tl, const int32_t* draft_tokens, const int32_t*
     p.out_topk = out_topk;
     const hipStream_t stream = S.stream;
     rc = timed_launch(sv::KK_STATS, stream, [&](const sv::LaunchEvents& ev) {
-        return sv::launch_stats(p, S.dtype, S.unroll, true, stream, ev);
+        return sv::launch_greedy_stats(p, S.dtype, S.unroll, stream, ev);
     });
     if (rc) return rc;
     return timed_launch(sv::KK_RESAMPLE, stream,

@@ -124,6 +124,7 @@ hipError_t launch_smc_rows(const Params& p, int dtype, hipStream_t s, const Laun
 hipError_t launch_smc_resample(const Params& p, hipStream_t s, const LaunchEvents& ev);
 // Greedy verify: one workgroup per batch row after a statistics pass over the
 // target rows (nslot = K + 1) with candidate lists.
+hipError_t launch_greedy_stats(const Params& p, int dtype, int unroll, hipStream_t s, const LaunchEvents& ev);
 hipError_t launch_greedy_rows(const Params& p, int dtype, hipStream_t s, const LaunchEvents& ev);
 // Two-stage verify: stage 2's draft lengths (n1 + 1) from stage 1's counts.
 hipError_t launch_hispec_link(const int32_t* n1, int32_t* len2, int32_t* out_n1, int B, hipStream_t s);

@@ -814,6 +814,169 @@ __global__ __launch_bounds__(kThreads, 8) void k_stats(Params P) {
 }
 
 // ---------------------------------------------------------------------------
+// Statistics pass of greedy verify: no temperature, no sum, no histogram.
+// Each wave lists the tokens of its share at or above thr0, the smallest of
+// its eight 8-lane group maxima (groups with no finite logit left out): at
+// least one token per such group, a few dozen on smooth rows.  Up to
+// 2 * kCandW takers are staged; when more than kCandW took part the list is
+// cut back to those at or above thr1, the second smallest group maximum.  The
+// header then holds the count, the bound (the threshold used: every token of
+// the share at or above it is listed), the wave's max key and the lowest
+// listed id holding it.  NaN logits pass the listing compare; a wave that
+// saw one records the key of NaN, above that of +inf, as its max key, so a
+// row's largest max key tells its validity (NaN or +inf: invalid; the key of
+// -inf: no finite logit).  No statistics records are written.
+// ---------------------------------------------------------------------------
+constexpr int kGreedyStage = 2 * kCandW;
+constexpr uint32_t kKeyNaN = 0xFFC00000u;  // order key of the quiet NaN 0x7FC00000
+
+template <int DT, int U>
+__device__ __forceinline__ void greedy_stats_item(const Params& P, int b, int j, int chunk) {
+    __shared__ uint64_t sh_stage[kWaves][kGreedyStage];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    bool rowok;
+    const int Le = row_len(P, b, rowok);
+    if (j > Le) return;  // padded position: never read
+    const RowGrid g = row_grid<DT>(row_ptr<DT>(P, true, b, j), P.V);
+    const int64_t k0 = static_cast<int64_t>(chunk) * P.cv;
+    const int64_t k1 = k0 + P.cv < g.nvec ? k0 + P.cv : g.nvec;
+    constexpr int64_t STEP = static_cast<int64_t>(kThreads) * U;
+    constexpr int VE = Fmt<DT>::VE;
+    uint4 raw[U];
+    if (k0 + STEP <= k1) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) raw[u] = gload16_nt(g.vp + k0 + u * kThreads + tid);
+    } else {
+        const uint32_t ni = Fmt<DT>::NEG_INF_WORD;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t k = k0 + u * kThreads + tid;
+            raw[u] = (k < k1) ? gload16(g.vp + k) : make_uint4(ni, ni, ni, ni);
+        }
+    }
+    if (k0 == 0 || k0 + STEP >= g.nvec - 1) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t k = k0 + u * kThreads + tid;
+            if (k < k1 && (k == 0 || k == g.nvec - 1)) mask_edge_raw<DT>(raw[u], k, g.head, P.V);
+        }
+    }
+    // the lane's max
+    float bm[4] = {-SV_INF, -SV_INF, -SV_INF, -SV_INF};
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (DT == DT_F32) {
+            bm[u & 3] = max3f(bm[u & 3], elem<DT>(raw[u], 0), elem<DT>(raw[u], 1));
+            bm[(u + 2) & 3] = max3f(bm[(u + 2) & 3], elem<DT>(raw[u], 2), elem<DT>(raw[u], 3));
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) bm[q] = max3f(bm[q], elem<DT>(raw[u], 2 * q), elem<DT>(raw[u], 2 * q + 1));
+        }
+    }
+    const float m = max3f(bm[0], bm[1], fmaxf(bm[2], bm[3]));
+#pragma unroll
+    for (int u = 0; u < U; ++u) asm volatile("" : "+v"(raw[u].x), "+v"(raw[u].y), "+v"(raw[u].z), "+v"(raw[u].w));
+    const float mw = wave_max_dpp(m);
+    // group maxima: after shifts of 1, 2 and 4 within a 16-lane row, lane i
+    // holds the max over lanes i-7..i of its row; lanes 7, 15, ... hold the
+    // eight groups' maxima.  The two smallest come from their order keys
+    // (groups with no finite logit count as +inf).
+    constexpr int ninf = static_cast<int>(0xFF800000u);
+    float gm = m;
+    gm = fmaxf(gm, __int_as_float(dpp_int<kDppRowShr1, 0xF>(ninf, __float_as_int(gm))));
+    gm = fmaxf(gm, __int_as_float(dpp_int<kDppRowShr2, 0xF>(ninf, __float_as_int(gm))));
+    gm = fmaxf(gm, __int_as_float(dpp_int<kDppRowShr4, 0xF>(ninf, __float_as_int(gm))));
+    const uint32_t kinf = order_key(SV_INF);
+    const uint32_t gk = gm > -SV_INF ? order_key(gm) : kinf;
+    uint32_t k1st = kinf, k2nd = kinf;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const uint32_t v = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(gk), 8 * q + 7));
+        k2nd = min(k2nd, max(k1st, v));
+        k1st = min(k1st, v);
+    }
+    const float thr0 = key_value(k1st), thr1 = key_value(k2nd);
+    // listing: every token with !(l < thr0) (NaN included), staged in LDS
+    uint64_t* stage = sh_stage[wv];
+    uint32_t base = 0u;
+    bool nan = false;
+    const int id0 = static_cast<int>((k0 + tid) * VE) - g.head;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < VE; ++i) {
+            const float l = elem<DT>(raw[u], i);
+            const bool take = !(l < thr0);
+            const uint64_t bal = __ballot(take);
+            if (bal != 0ull) {
+                const uint32_t at = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32),
+                                                              __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), base));
+                if (take) {
+                    nan = nan || __builtin_isnan(l);
+                    if (at < static_cast<uint32_t>(kGreedyStage))
+                        stage[at] = (static_cast<uint64_t>(__float_as_uint(l)) << 32) |
+                                    static_cast<uint32_t>(id0 + (u * kThreads) * VE + i);
+                }
+                base = __builtin_amdgcn_readfirstlane(base + static_cast<uint32_t>(__popcll(bal)));
+            }
+        }
+    }
+    // same-wave LDS order: the stage is complete.  Each lane holds up to two
+    // staged entries; keep all of them, or those at or above thr1.
+    const bool cut = base > static_cast<uint32_t>(kCandW);
+    const float thr = cut ? thr1 : thr0;
+    const uint64_t s0 = stage[lane], s1 = stage[kCandW + lane];
+    const float v0 = __uint_as_float(static_cast<uint32_t>(s0 >> 32));
+    const float v1 = __uint_as_float(static_cast<uint32_t>(s1 >> 32));
+    const bool staged = base <= static_cast<uint32_t>(kGreedyStage);
+    const bool keep0 = staged && static_cast<uint32_t>(lane) < base && !(v0 < thr);
+    const bool keep1 = staged && static_cast<uint32_t>(kCandW + lane) < base && !(v1 < thr);
+    const uint64_t b0 = __ballot(keep0), b1 = __ballot(keep1);
+    const uint32_t n0 = static_cast<uint32_t>(__popcll(b0));
+    const uint32_t count = n0 + static_cast<uint32_t>(__popcll(b1));
+    const bool over = !staged || count > static_cast<uint32_t>(kCandW);
+    const size_t ci = (static_cast<size_t>(b) * P.nslot + j) * P.nch + chunk;
+    const size_t slot0 = ci * kCand + wv * kCandW;
+    int amax = 0x7FFFFFFF;
+    if (!over) {
+        const uint32_t p0 = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(b0 >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(b0), 0u));
+        const uint32_t p1 = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(b1 >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(b1), n0));
+        if (keep0) {
+            P.cand[slot0 + p0] = (static_cast<uint64_t>(~order_key(v0)) << 32) | static_cast<uint32_t>(s0);
+            if (v0 == mw) amax = static_cast<int>(static_cast<uint32_t>(s0));
+        }
+        if (keep1) {
+            P.cand[slot0 + p1] = (static_cast<uint64_t>(~order_key(v1)) << 32) | static_cast<uint32_t>(s1);
+            if (v1 == mw) amax = min(amax, static_cast<int>(static_cast<uint32_t>(s1)));
+        }
+    }
+    amax = wave_min_int_dpp(amax);
+    const bool nanw = __ballot(nan) != 0ull;
+    if (lane < kHdrWords) {
+        // a wave with no logit above -inf lists nothing and bounds nothing
+        const uint32_t kw = !(mw > -SV_INF) ? 0u : over ? kNoCover : order_key(thr);
+        const uint32_t v = lane == 0 ? (over ? 0u : count)
+                           : lane == 1 ? kw
+                           : lane == 2 ? (nanw ? kKeyNaN : order_key(mw))
+                                       : static_cast<uint32_t>(amax);
+        P.chdr[kHdrWords * (ci * kWaves + wv) + lane] = tagged(P.tag, v);
+    }
+}
+
+// Greedy statistics pass: one workgroup per (b, j, chunk) of the target rows.
+template <int DT, int U>
+__global__ __launch_bounds__(kThreads, 8) void k_greedy_stats(Params P) {
+    const int item = blockIdx.x;
+    const int rvi = item / P.nch;
+    const int chunk = item - rvi * P.nch;
+    const int b = rvi / P.nslot;
+    greedy_stats_item<DT, U>(P, b, rvi - b * P.nslot, chunk);
+}
+
+// ---------------------------------------------------------------------------
 // Block-wide helpers for the selection and resample passes.
 // ---------------------------------------------------------------------------
 // Inclusive/exclusive prefix sums over the workgroup's threads in thread
@@ -2055,16 +2218,19 @@ hipError_t launch_smc_resample(const Params& p, hipStream_t s, const LaunchEvent
 constexpr int kGreedySel = 1024;  // tokens a top-k selection sorts in LDS
 constexpr int kDistBins = 264;    // log-scaled key distances below the row max
 
+constexpr int kReread = 16;  // shares re-read for the argmaxes of one batch row
+constexpr int kRerTop = 8;   // shares re-read for the top-k of row n
 struct GreedyShared {
     float M[kMaxK + 1];
-    int valid[kMaxK + 1];
-    uint32_t kth[kMaxK + 1];
+    uint32_t Mk[kMaxK + 1];
     int nocover[kMaxK + 1];
     int amin[kMaxK + 1];
     uint32_t hist[kDistBins];
     unsigned long long list[kGreedySel];
-    uint32_t nlist;
-    int n, bad, tbin, mode;
+    unsigned long long top[kMaxTopK + 1];
+    int rq[kReread], rset[kRerTop];
+    uint32_t nlist, nrq, nr;
+    int n, bad, tbin;
     float bv;
     int bid;
 };
@@ -2125,6 +2291,54 @@ __device__ int row_next_ranked(const uint8_t* row, int V, float pv, int pid, Gre
     return r == 0x7FFFFFFF ? -1 : r;
 }
 
+// Every element of share h (wave h % kWaves of chunk h / kWaves: the ids one
+// statistics wave read) of a logit row, across the workgroup: f(l, id).
+template <int DT, typename F>
+__device__ __forceinline__ void for_each_in_share(const Params& P, const uint8_t* row, int h, F&& f) {
+    constexpr int VE = Fmt<DT>::VE;
+    const RowGrid g = row_grid<DT>(row, P.V);
+    const int c = h / kWaves, w = h - c * kWaves;
+    const int U = P.cv / kThreads;
+    const int lane = threadIdx.x & 63;
+    for (int u = threadIdx.x >> 6; u < U; u += kWaves) {
+        const int64_t k = static_cast<int64_t>(c) * P.cv + static_cast<int64_t>(u) * kThreads + w * 64 + lane;
+        if (k < g.nvec) {
+            const uint4 v = gload16(g.vp + k);
+#pragma unroll
+            for (int i = 0; i < VE; ++i) {
+                const int64_t id = k * VE + i - g.head;
+                if (id >= 0 && id < P.V) f(elem<DT>(v, i), static_cast<int>(id));
+            }
+        }
+    }
+}
+
+// The k+1 first of the cnt distinct entries sh.list[0, cnt) in ascending
+// order (key descending, id ascending), by counting each entry's rank, into
+// sh.top[0, k].  Every thread calls.
+__device__ void greedy_rank(GreedyShared& sh, int cnt, int k) {
+    for (int i = threadIdx.x; i < cnt; i += kThreads) {
+        const unsigned long long e = sh.list[i];
+        int r = 0;
+        int q = 0;
+        for (; q + 4 <= cnt; q += 4)
+            r += (sh.list[q] < e) + (sh.list[q + 1] < e) + (sh.list[q + 2] < e) + (sh.list[q + 3] < e);
+        for (; q < cnt; ++q) r += sh.list[q] < e;
+        if (r <= k) sh.top[r] = e;
+    }
+    __syncthreads();
+}
+
+// Greedy decision and top-k, one workgroup per batch row, from the headers
+// and lists of the greedy statistics pass.  A list is complete at or above
+// its bound, so
+// * the argmax of row j is the lowest id holding the row max among the
+//   shares whose max it is: the header's id for a listed share, a re-read
+//   of the share for one whose list overflowed;
+// * with theta the (k+1)-th largest listed key of row n, every token at or
+//   above theta is listed, except in shares whose bound lies above theta
+//   and whose max reaches it: those few shares are re-read.
+// Rows beyond these limits take exact passes over the whole row.
 template <int DT>
 __global__ __launch_bounds__(kThreads) void k_greedy_rows(Params P) {
     __shared__ GreedyShared sh;
@@ -2136,27 +2350,54 @@ __global__ __launch_bounds__(kThreads) void k_greedy_rows(Params P) {
     const int x = lane_token(P, b, L);
     const size_t row0 = static_cast<size_t>(b) * P.nslot;  // logit row j of b is row0 + j
     if (tid <= L) {
-        sh.kth[tid] = 0u;
+        sh.Mk[tid] = 0u;
         sh.nocover[tid] = 0;
         sh.amin[tid] = 0x7FFFFFFF;
     }
-    if (wv == 0) {
-        // row maxima and validity from the statistics records (lane j)
-        bool ok = true;
-        float M = -SV_INF;
-        if (lane <= L) {
-            for (int c = 0; c < P.nch; ++c) {
-                uint32_t pay[kRecWords];
-                ok = read_record(P.prec + ((row0 + lane) * P.nch + c) * kRecWords, P.tag, pay) && ok;
-                const Partial q = partial_from(pay);
-                M = fmaxf(M, q.m);
-                if (!(q.s < SV_INF) || __builtin_isnan(q.s)) ok = false;
+    if (tid == 0) sh.nrq = 0u;
+    __syncthreads();
+    // every header of the rows j <= L: the row's largest max key (NaN's key
+    // above +inf's), the first kHR per thread kept for the argmax pass
+    const int per_row = P.nch * kWaves;
+    const int nh = (L + 1) * per_row;
+    constexpr int kHR = 2;
+    uint32_t hb[kHR], hm[kHR], ha[kHR];
+    int hj[kHR];
+#pragma unroll
+    for (int q = 0; q < kHR; ++q) {
+        const int h = tid + q * kThreads;
+        hj[q] = -1;
+        if (h < nh) {
+            const uint64_t* hw = P.chdr + (row0 * per_row + static_cast<size_t>(h)) * kHdrWords;
+            const uint64_t w1 = hw[1], w2 = hw[2], w3 = hw[3];
+            const int j = h / per_row;
+            if (has_tag(w1, P.tag) && has_tag(w2, P.tag) && has_tag(w3, P.tag)) {
+                hj[q] = j;
+                hb[q] = static_cast<uint32_t>(w1);
+                hm[q] = static_cast<uint32_t>(w2);
+                ha[q] = static_cast<uint32_t>(w3);
+                atomicMax(&sh.Mk[j], hm[q]);
+            } else {
+                atomicOr(&sh.nocover[j], 1);
             }
-            sh.M[lane] = M;
         }
+    }
+    for (int h = tid + kHR * kThreads; h < nh; h += kThreads) {
+        const uint64_t w2 = P.chdr[(row0 * per_row + static_cast<size_t>(h)) * kHdrWords + 2];
+        const int j = h / per_row;
+        if (has_tag(w2, P.tag)) atomicMax(&sh.Mk[j], static_cast<uint32_t>(w2));
+        else atomicOr(&sh.nocover[j], 1);
+    }
+    __syncthreads();
+    if (wv == 0) {
         int bad = rowok ? 0 : 1;
         if (lane < L && (x < 0 || x >= P.V)) bad = 1;
-        if (lane <= L && !(ok && M > -SV_INF)) bad = 1;
+        if (lane <= L) {
+            // NaN or +inf anywhere, or no logit above -inf: invalid
+            const uint32_t mk = sh.Mk[lane];
+            if (mk >= order_key(SV_INF) || mk <= order_key(-SV_INF)) bad = 1;
+            sh.M[lane] = key_value(mk);
+        }
         bad = __ballot(bad) != 0ull ? 1 : 0;
         if (lane == 0) sh.bad = bad;
     }
@@ -2167,47 +2408,48 @@ __global__ __launch_bounds__(kThreads) void k_greedy_rows(Params P) {
         if (tid == 0) P.out_n[b] = -1;
         return;
     }
-    // the wave headers of every row j <= L: coverage, bound, max key and the
-    // lowest listed id holding it
-    const int per_row = P.nch * kWaves;
-    const int nh = (L + 1) * per_row;
-    uint32_t hkey[3];
-    int hid[3], hj[3];
+    // argmax candidates: shares whose max is the row's
+    auto argmax_candidate = [&](int j, uint32_t bound, uint32_t mkey, uint32_t amax, int h) {
+        if (mkey != sh.Mk[j]) return;
+        if (bound != kNoCover) {
+            atomicMin(&sh.amin[j], static_cast<int>(amax));
+        } else {
+            const uint32_t at = atomicAdd(&sh.nrq, 1u);
+            if (at < static_cast<uint32_t>(kReread)) sh.rq[at] = h;
+            else atomicOr(&sh.nocover[j], 1);
+        }
+    };
 #pragma unroll
-    for (int q = 0; q < 3; ++q) {
-        const int h = tid + q * kThreads;
-        hj[q] = -1;
-        if (h < nh) {
-            const uint64_t* hw = P.chdr + (row0 * per_row + static_cast<size_t>(h)) * kHdrWords;
-            const uint64_t w0 = hw[0], w1 = hw[1], w2 = hw[2], w3 = hw[3];
+    for (int q = 0; q < kHR; ++q)
+        if (hj[q] >= 0) argmax_candidate(hj[q], hb[q], hm[q], ha[q], tid + q * kThreads);
+    for (int h = tid + kHR * kThreads; h < nh; h += kThreads) {
+        const uint64_t* hw = P.chdr + (row0 * per_row + static_cast<size_t>(h)) * kHdrWords;
+        const uint64_t w1 = hw[1], w3 = hw[3];
+        const int j = h / per_row;
+        if (has_tag(w1, P.tag) && has_tag(w3, P.tag))
+            argmax_candidate(j, static_cast<uint32_t>(w1), static_cast<uint32_t>(hw[2]), static_cast<uint32_t>(w3), h);
+        else
+            atomicOr(&sh.nocover[j], 1);
+    }
+    __syncthreads();
+    // overflowed shares holding their row's max: the lowest id holding it
+    {
+        const int nrq = static_cast<int>(min(sh.nrq, static_cast<uint32_t>(kReread)));
+        for (int q = 0; q < nrq; ++q) {
+            const int h = sh.rq[q];
             const int j = h / per_row;
-            hj[q] = j;
-            hkey[q] = static_cast<uint32_t>(w2);
-            hid[q] = static_cast<int>(static_cast<uint32_t>(w3));
-            if (!has_tag(w0, P.tag) || !has_tag(w1, P.tag) || !has_tag(w2, P.tag) || !has_tag(w3, P.tag) ||
-                static_cast<uint32_t>(w1) == kNoCover) {
-                atomicOr(&sh.nocover[j], 1);
-            } else {
-                atomicMax(&sh.kth[j], static_cast<uint32_t>(w1));
-            }
+            if (sh.nocover[j]) continue;  // uniform
+            const float Mj = sh.M[j];
+            int best = 0x7FFFFFFF;
+            for_each_in_share<DT>(P, row_ptr<DT>(P, true, b, j), h - j * per_row, [&](float l, int id) {
+                if (l == Mj) best = min(best, id);
+            });
+            best = wave_min_int(best);
+            if (lane == 0 && best != 0x7FFFFFFF) atomicMin(&sh.amin[j], best);
         }
     }
-    for (int h = tid + 3 * kThreads; h < nh; h += kThreads) {
-        // more than 3 headers per thread (very large vocabularies): coverage only
-        atomicOr(&sh.nocover[h / per_row], 1);
-    }
     __syncthreads();
-    // argmax of a covered row: every wave lists its max, so the row's argmax
-    // is the lowest header id among the headers carrying the row's max key
-    if (tid <= L && order_key(sh.M[tid]) < sh.kth[tid]) sh.nocover[tid] = 1;
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < 3; ++q) {
-        const int j = hj[q];
-        if (j >= 0 && !sh.nocover[j] && hkey[q] == order_key(sh.M[j])) atomicMin(&sh.amin[j], hid[q]);
-    }
-    __syncthreads();
-    // rows a list could not decide: one exact pass each
+    // rows the headers could not decide: one exact pass each
     for (int j = 0; j <= L; ++j) {
         if (!sh.nocover[j]) continue;
         const int g = row_next_ranked<DT>(row_ptr<DT>(P, true, b, j), P.V, SV_INF, -1, sh);
@@ -2235,36 +2477,40 @@ __global__ __launch_bounds__(kThreads) void k_greedy_rows(Params P) {
     if (k == 0) return;
     const int n = sh.n;
     int32_t* out = P.out_topk + static_cast<size_t>(b) * k;
-    // top-(k+1) of row n from its lists: count the listed tokens at or above
-    // the bound by log-scaled key distance below the max, find the bin where
-    // the count reaches k + 1, sort everything up to that bin.  Slot tid of
-    // each chunk's list (slot tid & 63 of wave tid >> 6), eight chunks per
-    // batch of loads.
-    bool listed = !sh.nocover[n];
-    if (listed) {
+    const uint64_t* hdr = P.chdr + ((row0 + n) * per_row + wv) * kHdrWords;
+    const uint64_t* lst = P.cand + (row0 + n) * P.nch * kCand;
+    if (!sh.nocover[n]) {
+        // the k+1 largest listed entries of row n: count by log-scaled key
+        // distance below the max, find the bin where the count reaches k + 1,
+        // collect up to it and rank.  Slot tid of each chunk's list (slot
+        // tid & 63 of wave tid >> 6), eight chunks per batch of loads; the
+        // first batch stays in registers for the collect pass.
         for (int i = tid; i < kDistBins; i += kThreads) sh.hist[i] = 0u;
-        if (tid == 0) sh.nlist = 0u;
+        if (tid == 0) {
+            sh.nlist = 0u;
+            sh.nr = 0u;
+        }
         __syncthreads();
-        const uint32_t km = order_key(sh.M[n]), kt = sh.kth[n];
-        const uint64_t* hdr = P.chdr + ((row0 + n) * per_row + wv) * kHdrWords;
-        const uint64_t* lst = P.cand + (row0 + n) * P.nch * kCand;
-        // pass 0 counts, pass 1 collects up to the chosen bin
+        const uint32_t km = sh.Mk[n];
+        unsigned long long e[8];
+        uint32_t cn[8];
+        auto load_batch = [&](int c0) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int cc = min(c0 + q, P.nch - 1);
+                cn[q] = c0 + q < P.nch ? static_cast<uint32_t>(hdr[static_cast<size_t>(cc) * kWaves * kHdrWords]) : 0u;
+                e[q] = lst[static_cast<size_t>(cc) * kCand + tid];
+            }
+        };
+        load_batch(0);
         for (int pass = 0; pass < 2; ++pass) {
             const int tb = sh.tbin;
             for (int c0 = 0; c0 < P.nch; c0 += 8) {
-                unsigned long long e[8];
-                uint32_t cn[8];
+                if (c0 > 0 || (pass == 1 && P.nch > 8)) load_batch(c0);
 #pragma unroll
                 for (int q = 0; q < 8; ++q) {
-                    const int cc = min(c0 + q, P.nch - 1);
-                    cn[q] = c0 + q < P.nch ? static_cast<uint32_t>(hdr[static_cast<size_t>(cc) * kWaves * kHdrWords]) : 0u;
-                    e[q] = lst[static_cast<size_t>(cc) * kCand + tid];
-                }
-#pragma unroll
-                for (int q = 0; q < 8; ++q) {
-                    const uint32_t key = ~static_cast<uint32_t>(e[q] >> 32);
-                    if (static_cast<uint32_t>(lane) < cn[q] && key >= kt) {
-                        const int db = dist_bin(km - key);
+                    if (static_cast<uint32_t>(lane) < cn[q]) {
+                        const int db = dist_bin(km - ~static_cast<uint32_t>(e[q] >> 32));
                         if (pass == 0) {
                             atomicAdd(&sh.hist[db], 1u);
                         } else if (db <= tb) {
@@ -2276,48 +2522,82 @@ __global__ __launch_bounds__(kThreads) void k_greedy_rows(Params P) {
             }
             __syncthreads();
             if (pass == 0) {
-                if (tid == 0) {
-                    uint32_t cum = 0u;
+                if (wv == 0) {
+                    // first bin where the running count reaches k + 1
+                    double base = 0.0, ct = 0.0;
                     int t = -1;
-                    for (int i = 0; i < kDistBins; ++i) {
-                        cum += sh.hist[i];
-                        if (cum >= static_cast<uint32_t>(k + 1)) {
-                            t = i;
+                    for (int i0 = 0; i0 < kDistBins; i0 += 64) {
+                        const double v = i0 + lane < kDistBins ? static_cast<double>(sh.hist[i0 + lane]) : 0.0;
+                        const double inc = wave_scan_dpp(v) + base;
+                        const unsigned long long bal = __ballot(inc >= static_cast<double>(k + 1));
+                        if (bal) {
+                            const int f = __ffsll(static_cast<long long>(bal)) - 1;
+                            t = i0 + f;
+                            ct = readlane_f64(inc, f);
                             break;
                         }
+                        base = lane63(inc);
                     }
-                    sh.tbin = (t >= 0 && cum <= static_cast<uint32_t>(kGreedySel)) ? t : -1;
+                    if (lane == 0) sh.tbin = (t >= 0 && ct <= static_cast<double>(kGreedySel)) ? t : -1;
                 }
                 __syncthreads();
-                if (sh.tbin < 0) break;  // too few listed, or too many to sort: exact passes
+                if (sh.tbin < 0) break;  // too few listed, or too many to rank: exact passes
             }
         }
-        listed = sh.tbin >= 0;
-        if (listed) {
-            const int cnt = static_cast<int>(min(sh.nlist, static_cast<uint32_t>(kGreedySel)));
-            int np2 = 1;
-            while (np2 < cnt) np2 <<= 1;
-            for (int i = cnt + tid; i < np2; i += kThreads) sh.list[i] = ~0ull;
-            __syncthreads();
-            for (int kk = 2; kk <= np2; kk <<= 1) {
-                for (int jj = kk >> 1; jj > 0; jj >>= 1) {
-                    for (int i = tid; i < np2; i += kThreads) {
-                        const int ij = i ^ jj;
-                        if (ij > i) {
-                            const unsigned long long a = sh.list[i], c2 = sh.list[ij];
-                            const bool up = (i & kk) == 0;
-                            if ((a > c2) == up) {
-                                sh.list[i] = c2;
-                                sh.list[ij] = a;
-                            }
-                        }
-                    }
-                    __syncthreads();
+        if (sh.tbin >= 0) {
+            greedy_rank(sh, static_cast<int>(sh.nlist), k);
+            const uint32_t theta = ~static_cast<uint32_t>(sh.top[k] >> 32);
+            // shares that may hold unlisted tokens at or above theta
+            for (int h = tid; h < per_row; h += kThreads) {
+                const uint64_t* hw = P.chdr + ((row0 + n) * per_row + static_cast<size_t>(h)) * kHdrWords;
+                if (static_cast<uint32_t>(hw[1]) > theta && static_cast<uint32_t>(hw[2]) >= theta) {
+                    const uint32_t at = atomicAdd(&sh.nr, 1u);
+                    if (at < static_cast<uint32_t>(kRerTop)) sh.rset[at] = h;
                 }
             }
-            for (int i = tid; i < k; i += kThreads)
-                out[i] = i + 1 < cnt ? static_cast<int32_t>(static_cast<uint32_t>(sh.list[i + 1])) : -1;
-            return;
+            __syncthreads();
+            const int nr = static_cast<int>(sh.nr);
+            if (nr == 0) {
+                for (int i = tid; i < k; i += kThreads) out[i] = static_cast<int32_t>(static_cast<uint32_t>(sh.top[i + 1]));
+                return;
+            }
+            if (nr <= kRerTop) {
+                // every token at or above theta: the listed ones of the other
+                // shares, then the re-read shares
+                if (tid == 0) sh.nlist = 0u;
+                __syncthreads();
+                for (int c = 0; c < P.nch; ++c) {
+                    const int h = c * kWaves + wv;
+                    bool mine = false;
+                    for (int r = 0; r < nr; ++r) mine = mine || sh.rset[r] == h;
+                    const uint32_t cnt = static_cast<uint32_t>(hdr[static_cast<size_t>(c) * kWaves * kHdrWords]);
+                    if (!mine && static_cast<uint32_t>(lane) < cnt) {
+                        const unsigned long long en = lst[static_cast<size_t>(c) * kCand + tid];
+                        if (~static_cast<uint32_t>(en >> 32) >= theta) {
+                            const uint32_t at = atomicAdd(&sh.nlist, 1u);
+                            if (at < static_cast<uint32_t>(kGreedySel)) sh.list[at] = en;
+                        }
+                    }
+                }
+                const uint8_t* rown = row_ptr<DT>(P, true, b, n);
+                for (int r = 0; r < nr; ++r) {
+                    for_each_in_share<DT>(P, rown, sh.rset[r], [&](float l, int id) {
+                        const uint32_t key = order_key(l);
+                        if (key >= theta) {
+                            const uint32_t at = atomicAdd(&sh.nlist, 1u);
+                            if (at < static_cast<uint32_t>(kGreedySel))
+                                sh.list[at] = (static_cast<unsigned long long>(~key) << 32) | static_cast<uint32_t>(id);
+                        }
+                    });
+                }
+                __syncthreads();
+                if (sh.nlist <= static_cast<uint32_t>(kGreedySel)) {
+                    greedy_rank(sh, static_cast<int>(sh.nlist), k);
+                    for (int i = tid; i < k; i += kThreads)
+                        out[i] = static_cast<int32_t>(static_cast<uint32_t>(sh.top[i + 1]));
+                    return;
+                }
+            }
         }
     }
     // exact passes over row n: rank by rank
@@ -2413,6 +2693,18 @@ hipError_t launch_stats(const Params& p, int dtype, int unroll, bool topp, hipSt
     const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(p.B) * p.nslot * p.nch);
     if (topp) launch_stats_c<true>(p, dtype, unroll, grid, s, ev);
     else launch_stats_c<false>(p, dtype, unroll, grid, s, ev);
+    return hipGetLastError();
+}
+
+hipError_t launch_greedy_stats(const Params& p, int dtype, int unroll, hipStream_t s, const LaunchEvents& ev) {
+    const unsigned grid = static_cast<unsigned>(static_cast<int64_t>(p.B) * p.nslot * p.nch);
+    if (dtype == DT_BF16) {
+        if (unroll == 8) launch(k_greedy_stats<DT_BF16, 8>, grid, kThreads, s, ev, p);
+        else launch(k_greedy_stats<DT_BF16, 4>, grid, kThreads, s, ev, p);
+    } else {
+        if (unroll == 8) launch(k_greedy_stats<DT_F32, 8>, grid, kThreads, s, ev, p);
+        else launch(k_greedy_stats<DT_F32, 4>, grid, kThreads, s, ev, p);
+    }
     return hipGetLastError();
 }
 

@@ -108,3 +108,52 @@ def test_greedy_full_size():
     inp = W.make_inputs(2, 11)
     x = _drafts(W.bf16_bits_to_f32(inp.target), 11)
     _check(inp.target, x, None, 60, "full size")
+
+
+def _wave0_ids(V, n_per_lane, lanes):
+    """Ids that a 256-thread statistics workgroup with 16-byte loads of
+    8 bf16 values gives to the given lanes of its first wave in the first
+    chunk: vector u * 256 + lane, element i.  (A different split only moves
+    the pattern between lists; the parity check holds either way.)"""
+    ids = []
+    for lane in lanes:
+        for u in range(n_per_lane):
+            ids.append((u * 256 + lane) * 8)
+    return np.array(ids)
+
+
+def test_greedy_list_cut_back_and_overflow():
+    rng = np.random.default_rng(21)
+    B, K, V = 4, 2, 40000
+    t = (rng.standard_normal((B, K + 1, V)) - 10.0).astype(np.float32)
+    # row 0: group g (lanes 8g..8g+7) of the first wave holds a few tokens at
+    # 1 + g, group 0 thirty of them: more than one list's worth at the
+    # smallest group max, few enough at the second smallest
+    for j in range(K + 1):
+        for g in range(8):
+            lanes = range(8 * g, 8 * g + 8)
+            ids = _wave0_ids(V, 8, lanes)
+            take = ids[: (30 if g == 0 else 6)]
+            t[0, j, take] = 1.0 + g
+    # row 1: too many takers even at the second smallest group max
+    for j in range(K + 1):
+        ids = _wave0_ids(V, 8, range(64))
+        t[1, j, ids[:200]] = 3.0
+    # row 2: whole chunks of -inf (a masked vocabulary tail)
+    t[2, :, 9000:] = -np.inf
+    # row 3: logits rising with the id (one wave holds every top token)
+    t[3] = np.linspace(-5.0, 5.0, V, dtype=np.float32)[None, :] + 0.01 * t[3]
+    x = _drafts(t, 21, agree=0.8)
+    _check(W.f32_to_bf16_bits(t), x, None, 60, "cut-back, overflow, masked tail, sorted, bf16")
+    _check(t, x, None, 33, "cut-back, overflow, masked tail, sorted, fp32")
+
+
+def test_greedy_nan_and_inf_in_a_full_chunk():
+    inp = W.make_inputs(2, 12, B=6)
+    t = inp.target.copy()
+    x = _drafts(W.bf16_bits_to_f32(t), 12)
+    t[1, 3, 70000] = W.NAN_BF16                     # NaN inside a full chunk
+    t[2, 0, 5] = W.f32_to_bf16_bits(np.float32(np.inf)).item()  # +inf: invalid too
+    t[3, 5, 128255] = W.f32_to_bf16_bits(np.float32(-np.inf)).item()
+    r = _check(t, x, None, 60, "NaN / +inf / -inf in full rows")
+    assert r.n_accepted[1] == -1 and r.n_accepted[2] == -1 and r.n_accepted[3] >= 0

@@ -815,11 +815,12 @@ __global__ __launch_bounds__(kThreads, 8) void k_stats(Params P) {
 
 // ---------------------------------------------------------------------------
 // Statistics pass of greedy verify: no temperature, no sum, no histogram.
-// Each wave lists the tokens of its share at or above thr0, the smallest of
-// its eight 8-lane group maxima (groups with no finite logit left out): at
-// least one token per such group, a few dozen on smooth rows.  Up to
+// Each wave lists the tokens of its share at or above thr0, the second
+// smallest of its eight 8-lane group maxima (groups with no finite logit
+// left out; the smallest when only one group has one): at least seven tokens
+// on a share of finite logits, about fifteen on smooth rows.  Up to
 // 2 * kCandW takers are staged; when more than kCandW took part the list is
-// cut back to those at or above thr1, the second smallest group maximum.  The
+// cut back to those at or above thr1, the third smallest group maximum.  The
 // header then holds the count, the bound (the threshold used: every token of
 // the share at or above it is listed), the wave's max key and the lowest
 // listed id holding it.  NaN logits pass the listing compare; a wave that
@@ -879,7 +880,7 @@ __device__ __forceinline__ void greedy_stats_item(const Params& P, int b, int j,
     const float mw = wave_max_dpp(m);
     // group maxima: after shifts of 1, 2 and 4 within a 16-lane row, lane i
     // holds the max over lanes i-7..i of its row; lanes 7, 15, ... hold the
-    // eight groups' maxima.  The two smallest come from their order keys
+    // eight groups' maxima.  The three smallest come from their order keys
     // (groups with no finite logit count as +inf).
     constexpr int ninf = static_cast<int>(0xFF800000u);
     float gm = m;
@@ -888,18 +889,24 @@ __device__ __forceinline__ void greedy_stats_item(const Params& P, int b, int j,
     gm = fmaxf(gm, __int_as_float(dpp_int<kDppRowShr4, 0xF>(ninf, __float_as_int(gm))));
     const uint32_t kinf = order_key(SV_INF);
     const uint32_t gk = gm > -SV_INF ? order_key(gm) : kinf;
-    uint32_t k1st = kinf, k2nd = kinf;
+    uint32_t k1st = kinf, k2nd = kinf, k3rd = kinf;
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
         const uint32_t v = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(gk), 8 * q + 7));
+        k3rd = min(k3rd, max(k2nd, v));
         k2nd = min(k2nd, max(k1st, v));
         k1st = min(k1st, v);
     }
-    const float thr0 = key_value(k1st), thr1 = key_value(k2nd);
-    // listing: every token with !(l < thr0) (NaN included), staged in LDS
+    // fewer than two (three) finite groups: fall back to the next smaller
+    if (k2nd == kinf) k2nd = k1st;
+    if (k3rd == kinf) k3rd = k2nd;
+    const float thr0 = key_value(k2nd), thr1 = key_value(k3rd);
+    // listing: every token with !(l < thr0) (NaN included), staged in LDS;
+    // takers past the stage all land on its last slot (the list is then
+    // dropped anyway)
     uint64_t* stage = sh_stage[wv];
     uint32_t base = 0u;
-    bool nan = false;
+    uint64_t nanbal = 0ull;
     const int id0 = static_cast<int>((k0 + tid) * VE) - g.head;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -912,12 +919,11 @@ __device__ __forceinline__ void greedy_stats_item(const Params& P, int b, int j,
             if (bal != 0ull) {
                 const uint32_t at = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(bal >> 32),
                                                               __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(bal), base));
-                if (take) {
-                    nan = nan || __builtin_isnan(l);
-                    if (at < static_cast<uint32_t>(kGreedyStage))
-                        stage[at] = (static_cast<uint64_t>(__float_as_uint(l)) << 32) |
-                                    static_cast<uint32_t>(id0 + (u * kThreads) * VE + i);
-                }
+                if (take)
+                    stage[min(at, static_cast<uint32_t>(kGreedyStage - 1))] =
+                        (static_cast<uint64_t>(__float_as_uint(l)) << 32) |
+                        static_cast<uint32_t>(id0 + (u * kThreads) * VE + i);
+                nanbal |= __ballot(__builtin_isnan(l));
                 base = __builtin_amdgcn_readfirstlane(base + static_cast<uint32_t>(__popcll(bal)));
             }
         }
@@ -954,7 +960,7 @@ __device__ __forceinline__ void greedy_stats_item(const Params& P, int b, int j,
         }
     }
     amax = wave_min_int_dpp(amax);
-    const bool nanw = __ballot(nan) != 0ull;
+    const bool nanw = nanbal != 0ull;
     if (lane < kHdrWords) {
         // a wave with no logit above -inf lists nothing and bounds nothing
         const uint32_t kw = !(mw > -SV_INF) ? 0u : over ? kNoCover : order_key(thr);
@@ -2333,8 +2339,9 @@ __device__ void greedy_rank(GreedyShared& sh, int cnt, int k) {
 // and lists of the greedy statistics pass.  A list is complete at or above
 // its bound, so
 // * the argmax of row j is the lowest id holding the row max among the
-//   shares whose max it is: the header's id for a listed share, a re-read
-//   of the share for one whose list overflowed;
+//   shares whose max it is: the header's id for a share whose max is at or
+//   above its bound (so listed), a re-read of the share otherwise (its list
+//   overflowed);
 // * with theta the (k+1)-th largest listed key of row n, every token at or
 //   above theta is listed, except in shares whose bound lies above theta
 //   and whose max reaches it: those few shares are re-read.
@@ -2411,7 +2418,7 @@ __global__ __launch_bounds__(kThreads) void k_greedy_rows(Params P) {
     // argmax candidates: shares whose max is the row's
     auto argmax_candidate = [&](int j, uint32_t bound, uint32_t mkey, uint32_t amax, int h) {
         if (mkey != sh.Mk[j]) return;
-        if (bound != kNoCover) {
+        if (bound <= mkey) {
             atomicMin(&sh.amin[j], static_cast<int>(amax));
         } else {
             const uint32_t at = atomicAdd(&sh.nrq, 1u);

@@ -23,11 +23,13 @@ Modules:
              draft -> intermediate layer -> final layer.
   greedy  -- greedy verify (argmax acceptance) and the top-k of the last
              logits after the emitted token.
+  produce -- the synthetic draft producer of the two-batch schedule.
 """
 
 from .greedy import GreedyResult, argmax_lowest, greedy_verify, top_k_after_first  # noqa: F401
 from .hispec import HispecResult, hispec_verify  # noqa: F401
 from .philox import philox4x32_10, uniforms  # noqa: F401
+from .produce import produce_drafts  # noqa: F401
 from .smc import SmcResult, ess, log_weight_increment, smc_step, systematic, systematic_uniform  # noqa: F401
 from .verify import (  # noqa: F401
     FLAG_BAND,

@@ -374,6 +374,174 @@ def greedy_bench(args, binding, torch, dev, sets):
 
 
 # ---------------------------------------------------------------------------
+# Two-batch schedule (--overlap): batch X is verified on one stream while the
+# synthetic draft producer drafts batch Y on a second stream; the roles swap
+# every step.  Timed alone, one after the other on one stream, and overlapped.
+# ---------------------------------------------------------------------------
+def _oracle_overlap(args):
+    import oracle
+
+    si, r0, r1 = args
+    inp = _SAMPLE[si]
+    d, x = oracle.produce_drafts(inp.target[r0:r1], inp.K, 1000 + si)
+    oracle.verify(inp.target[r0:r1], d, x, None, inp.temperature, 1.0, inp.seed)
+    return (r1 - r0) * inp.K
+
+
+def overlap_bench(args, binding, torch, dev, sets):
+    import numpy as np
+
+    B, K, V = sets[0].B, sets[0].K, sets[0].V
+    T = float(sets[0].temperature)
+
+    def put(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    tgt = [put(sets[i].target) for i in range(2)]
+    drafts = [torch.empty((B, K, V), dtype=torch.bfloat16, device=dev) for _ in range(2)]
+    toks = [torch.empty((B, K), dtype=torch.int32, device=dev) for _ in range(2)]
+    outs = [(torch.empty((B, K + 1), dtype=torch.int32, device=dev), torch.empty((B,), dtype=torch.int32, device=dev))
+            for _ in range(2)]
+    s0 = torch.cuda.Stream(dev)
+    s1 = torch.cuda.Stream(dev)
+    produced = [None, None]
+    verified = [None, None]
+
+    def produce(y, i, st):
+        binding.draft_produce(tgt[y], K, 1000 + i, stream=st, out=drafts[y], out_tokens=toks[y])
+
+    def verify(x, i, st):
+        binding.verify(tgt[x], drafts[x], toks[x], None, T, 1.0, 5000 + i, stream=st, out_tokens=outs[x][0],
+                       out_n_accepted=outs[x][1])
+
+    def run(mode, n, base, ev=None):
+        """Issue n steps.  In the overlapped mode, step i verifies batch i % 2
+        on s0 after its drafts exist and drafts batch (i + 1) % 2 on s1 after
+        its previous verify; `ev` holds the (produced, verified) events."""
+        produced_, verified_ = ev if ev is not None else (produced, verified)
+        for i in range(base, base + n):
+            x, y = i % 2, (i + 1) % 2
+            if mode == "verify":
+                verify(x, i, s0)
+            elif mode == "produce":
+                produce(y, i, s0)
+            elif mode == "serial":
+                produce(y, i, s0)
+                verify(x, i, s0)
+            else:
+                if produced_[x] is not None:
+                    s0.wait_event(produced_[x])
+                verify(x, i, s0)
+                verified_[x] = torch.cuda.Event()
+                verified_[x].record(s0)
+                if verified_[y] is not None:
+                    s1.wait_event(verified_[y])
+                produce(y, i, s1)
+                produced_[y] = torch.cuda.Event()
+                produced_[y].record(s1)
+
+    # The host needs tens of microseconds to issue one step through the
+    # Python binding, so each mode is captured as a HIP graph of GSTEPS steps
+    # (the second stream forked from and joined back to the first) and the
+    # graph is replayed: the GPU then sees every launch as soon as its
+    # dependencies allow.
+    GSTEPS = 10
+
+    def graph(mode):
+        torch.cuda.synchronize()
+        produce(0, 0, s0)
+        produce(1, 0, s0)
+        run(mode, 2, 0, ([None, None], [None, None]))  # scratch sized on both streams
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s0):
+            fork = torch.cuda.Event()
+            fork.record(s0)
+            s1.wait_event(fork)
+            run(mode, GSTEPS, 0, ([None, None], [None, None]))
+            join = torch.cuda.Event()
+            join.record(s1)
+            s0.wait_event(join)
+        torch.cuda.synchronize()
+        return g
+
+    def timed(mode):
+        g = graph(mode)
+        reps = max(1, args.steps // GSTEPS)
+        for _ in range(max(1, args.warmup // GSTEPS)):
+            g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(s0)
+        for _ in range(reps):
+            g.replay()
+        e1.record(s0)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * GSTEPS) * 1e3
+
+    with torch.cuda.stream(s0):
+        us = {m: timed(m) for m in ("verify", "produce", "serial", "overlap")}
+        # the overlapped graph's last verify (step GSTEPS - 1, batch 1) against
+        # the same call issued eagerly
+        last = GSTEPS - 1
+        got = (outs[last % 2][0].clone(), outs[last % 2][1].clone())
+        ref = binding.verify(tgt[last % 2], drafts[last % 2], toks[last % 2], None, T, 1.0, 5000 + last, stream=s0)
+        torch.cuda.synchronize()
+        replay_ok = bool(torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1]))
+    # kernel durations inside the overlapped schedule, issued eagerly
+    binding.profile_read()
+    binding.profile_enable(True)
+    run("overlap", args.steps, 1, ([None, None], [None, None]))
+    torch.cuda.synchronize()
+    binding.profile_enable(False)
+    prof = binding.profile_read()
+    kus = {k: round(prof[k][0] / prof[k][1] * 1e3, 3) for k in ("stats", "rows", "produce") if prof[k][1]}
+    print(f"[bench] two-batch schedule, {args.steps} steps each: {us}; kernels in the overlapped run {kus}",
+          file=sys.stderr, flush=True)
+    hidden = us["serial"] - us["overlap"]
+    prod_bytes = 2 * B * K * V * 2  # the producer reads K target rows and writes K draft rows
+    cpu = None
+    if not args.no_cpu_baseline:
+        global _SAMPLE
+        _SAMPLE = sets[:2]
+        cores = max(1, min(16, os.cpu_count() or 1))
+        work = [(s, r, r + 1) for s in range(2) for r in range(B)]
+        positions, dt, passes = _timed_passes(_oracle_overlap, work, cores)
+        cpu = {"value": positions / dt, "unit": "positions/s", "cores": cores, "kind": "oracle",
+               "sample": f"{len(work)} rows of two batches, {passes} passes ({positions} draft positions), "
+                         f"float oracle of the producer then the verify step, one row per task over {cores} "
+                         f"processes, {dt:.1f} s wall"}
+    line = {
+        "metric": "two-batch schedule (verify one batch while drafting the other): draft positions verified/sec "
+                  "at B=64,K=5,V=128256",
+        "value": round(B * K / (us["overlap"] * 1e-6), 1),
+        "unit": "positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(us["overlap"] / 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": "two batches of B=64 K=5 V=128256 bf16 T=0.7; verify on stream 0, the synthetic "
+                               "draft producer on stream 1, roles swapped every step",
+                   "B": B, "K": K, "V": V},
+        "overlap": {"verify_alone_us": round(us["verify"], 3), "produce_alone_us": round(us["produce"], 3),
+                    "serial_us": round(us["serial"], 3), "overlapped_us": round(us["overlap"], 3),
+                    "hidden_us": round(hidden, 3),
+                    "hidden_frac_of_shorter": round(hidden / min(us["verify"], us["produce"]), 4)},
+        "kernels_us": kus,
+        "graph_replay_matches_eager": replay_ok,
+        "producer_GBps_alone": round(prod_bytes / (us["produce"] * 1e-6) / 1e9, 1),
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+# ---------------------------------------------------------------------------
 # Two-stage verify timing (--hispec): three exit layers of one synthetic
 # early-exit model, B=64, K=5, V=128256, bf16, T=0.7
 # ---------------------------------------------------------------------------
@@ -487,6 +655,8 @@ def main():
                     help="seeded workload to time (default: the batched B=64 K=5 V=128256 bf16 one)")
     ap.add_argument("--greedy", action="store_true",
                     help="time greedy verify with the top-60 (spec_greedy_verify) on the batched target logits")
+    ap.add_argument("--overlap", action="store_true",
+                    help="time the two-batch schedule: verify on one stream, the synthetic draft producer on another")
     ap.add_argument("--hispec", action="store_true",
                     help="time the two-stage verify (spec_hispec_verify) on three synthetic exit layers")
     ap.add_argument("--smc", action="store_true",
@@ -541,6 +711,9 @@ def main():
         return
     if args.greedy:
         greedy_bench(args, binding, torch, dev, sets)
+        return
+    if args.overlap:
+        overlap_bench(args, binding, torch, dev, sets)
         return
 
     def step(i):

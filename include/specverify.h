@@ -239,6 +239,38 @@ int spec_smc_step(const sv_logits* target_logits, const sv_logits* draft_logits,
                   int32_t* out_bonus, double* out_logw, int32_t* out_ancestor,
                   double* out_ess, int32_t* out_resampled, void* stream);
 
+/*
+ * spec_draft_produce -- the synthetic draft producer of the two-batch
+ * schedule (page "MineDraft: A Framework for Batch Parallel Speculative
+ * Decoding", section 2: two batches alternate, one verified while the other
+ * is drafted, roles swapping every step).  The pages give no drafter; this
+ * stand-in derives a batch's drafts from its target logits so that a caller
+ * can run it on one stream while spec_verify runs on another:
+ *
+ *   draft[b, j, v] = round(float32(target[b, j, v]) + delta(b, j, v)), j < K,
+ *   delta = ((h >> 5) - 1024) / 512 with h the 16-bit half (v & 1; 0 = low)
+ *   of word (v & 7) >> 1 of Philox4x32-10 at counter (v >> 3, b, j, 3), key
+ *   (seed low, seed high); round = round to nearest even into the logits'
+ *   format (NaN stays NaN);
+ *   out_tokens[b, j] = the lowest id holding the largest draft[b, j, :], or
+ *   -1 when that row holds a NaN (a greedy drafter).
+ *
+ * target_logits  [B, P, V], bf16 or fp32; positions 0..K-1 are read.
+ * K              1 <= K <= P.
+ * draft_out      device buffer of the target's dtype, written at element
+ *                b*out_stride_b + j*out_stride_p + v (strides in elements,
+ *                >= 0); must not overlap the target.
+ * out_tokens     device int32 [B, K], contiguous.
+ *
+ * Errors as spec_verify: SV_EINVAL (NULL pointer, negative stride),
+ * SV_ESHAPE (K outside [1, P], B or V out of range), SV_EDTYPE, SV_EALIGN,
+ * SV_ENOMEM, SV_EHIP; nothing is launched on a host-checked error.  Uses the
+ * stream's scratch like every other call: calls on one stream run in order.
+ */
+int spec_draft_produce(const sv_logits* target_logits, int32_t K, uint64_t seed,
+                       void* draft_out, int64_t out_stride_b, int64_t out_stride_p,
+                       int32_t* out_tokens, void* stream);
+
 /* Human-readable text for a status code (for SV_EHIP, the last HIP error). */
 const char* spec_verify_strerror(int status);
 
@@ -253,7 +285,8 @@ int spec_verify_abi_version(void);
  * of HIP events on its stream, attached to the kernel's dispatch.
  * spec_verify_profile_read synchronises those events and writes, for each of
  * the n kernel kinds (0 statistics pass, 1 nucleus selection, 2 row pass:
- * decision and resample, or the SMC particle pass, 3 SMC resampling), the
+ * decision and resample, or the SMC particle pass, 3 SMC resampling, 4 the
+ * synthetic draft producer), the
  * summed duration in milliseconds and the number of launches since the last
  * read; it returns the number of kinds written.  Host arrays ms[n],
  * launches[n]. */

@@ -18,9 +18,10 @@ SV_F32, SV_BF16 = 0, 1
 PROBE_POS, PROBE_ROW = 8, 4
 STATUS = {0: "SV_OK", -1: "SV_EINVAL", -2: "SV_ESHAPE", -3: "SV_EDTYPE", -4: "SV_EHIP", -5: "SV_ENOMEM",
           -6: "SV_EALIGN"}
-KERNEL_KINDS = ("stats", "topp", "rows", "smc")
+KERNEL_KINDS = ("stats", "topp", "rows", "smc", "produce")
 
 EXPORTS = ("spec_verify", "spec_verify_probe", "spec_greedy_verify", "spec_hispec_verify", "spec_smc_step",
+           "spec_draft_produce",
            "spec_verify_strerror",
            "spec_verify_release",
            "spec_verify_abi_version", "spec_verify_profile_enable", "spec_verify_profile_read",
@@ -71,6 +72,9 @@ def load(path=LIB_PATH):
     lib.spec_smc_step.argtypes = [P(SvLogits), P(SvLogits), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,
                                   ctypes.c_double, ctypes.c_uint64] + [ctypes.c_void_p] * 6
     lib.spec_smc_step.restype = ctypes.c_int
+    lib.spec_draft_produce.argtypes = [P(SvLogits), ctypes.c_int32, ctypes.c_uint64, ctypes.c_void_p,
+                                       ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p]
+    lib.spec_draft_produce.restype = ctypes.c_int
     lib.spec_verify_strerror.argtypes = [ctypes.c_int]
     lib.spec_verify_strerror.restype = ctypes.c_char_p
     lib.spec_verify_release.argtypes = []
@@ -174,6 +178,29 @@ def greedy_verify(target, draft_tokens, draft_len=None, k=0, *, stream=None, out
                                        ctypes.c_void_p(out_n_accepted.data_ptr()),
                                        ctypes.c_void_p(out_topk.data_ptr()), _stream_handle(stream, dev)))
     return out_tokens, out_n_accepted, out_topk[:, :k]
+
+
+def draft_produce(target, K, seed=0, *, stream=None, out=None, out_tokens=None):
+    """The synthetic draft producer on device tensors: target [B, P, V]
+    (bfloat16 or float32, V contiguous), K <= P.  Returns (draft [B, K, V] of
+    the target's dtype, tokens [B, K] int32); `out` may be any [B, K, V] view
+    of that dtype with V contiguous."""
+    lib = load()
+    dev = target.device
+    B, _, V = target.shape
+    if out is None:
+        out = torch.empty((B, K, V), dtype=target.dtype, device=dev)
+    if out.dim() != 3 or tuple(out.shape) != (B, K, V) or out.dtype != target.dtype or out.stride(2) != 1:
+        raise ValueError("out must be [B, K, V] of the target's dtype, contiguous along V")
+    if out_tokens is None:
+        out_tokens = torch.empty((B, K), dtype=torch.int32, device=dev)
+    if out_tokens.dtype != torch.int32 or not out_tokens.is_contiguous() or tuple(out_tokens.shape) != (B, K):
+        raise ValueError("out_tokens must be contiguous int32 [B, K]")
+    td = _desc(target, "target")
+    _check(lib, lib.spec_draft_produce(ctypes.byref(td), ctypes.c_int32(K), ctypes.c_uint64(seed & (2**64 - 1)),
+                                       ctypes.c_void_p(out.data_ptr()), out.stride(0), out.stride(1),
+                                       ctypes.c_void_p(out_tokens.data_ptr()), _stream_handle(stream, dev)))
+    return out, out_tokens
 
 
 def hispec_verify(final, inter, draft, draft_tokens, draft_len=None, temperature=1.0, top_p=1.0, seed=0, *,

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libspecverify.so")
 ARCH = "gfx950"
 
-SOURCES = ["sv_kernels.hip", "sv_api.cpp"]
+SOURCES = ["sv_kernels.hip", "sv_produce.hip", "sv_api.cpp"]
 DEPS = ["sv_internal.h", "sv_device.h"]
 
 

@@ -429,6 +429,52 @@ int smc_impl(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_toke
                         [&](const sv::LaunchEvents& ev) { return sv::launch_smc_resample(p, stream, ev); });
 }
 
+// Synthetic draft producer of the two-batch schedule: drafts and chunk
+// records, then the tokens.  Its chunk records use the (device, stream)
+// scratch like every other call on that stream.
+int produce_impl(const sv_logits* tl, int32_t K, uint64_t seed, void* out, int64_t osb, int64_t osp,
+                 int32_t* out_tokens, void* stream_v) {
+    int rc = check_logits(tl);
+    if (rc) return rc;
+    if (!out || !out_tokens) return SV_EINVAL;
+    const int E = tl->dtype == SV_BF16 ? 2 : 4;
+    if (misaligned(out, E) || misaligned(out_tokens, 4)) return SV_EALIGN;
+    if (osb < 0 || osp < 0) return SV_EINVAL;
+    const int B = tl->B, V = tl->V;
+    if (B <= 0 || V <= 0 || K < 1 || K > tl->P || B > (1 << 22) || V > (1 << 24)) return SV_ESHAPE;
+    const int64_t groups = (static_cast<int64_t>(V) + 7) / 8;
+    const int64_t per = static_cast<int64_t>(sv::kThreads) * sv::kProdU;
+    const int nchp = static_cast<int>((groups + per - 1) / per);
+    if (static_cast<int64_t>(B) * K * nchp >= (1ll << 31)) return SV_ESHAPE;
+    const hipStream_t stream = static_cast<hipStream_t>(stream_v);
+    void* base = nullptr;
+    rc = get_scratch(stream, static_cast<size_t>(B) * K * nchp * 2 * sizeof(uint64_t), &base);
+    if (rc) return rc;
+    sv::ProduceParams p;
+    std::memset(&p, 0, sizeof(p));
+    p.tgt = static_cast<const uint8_t*>(tl->data);
+    p.tsb = tl->stride_b;
+    p.tsp = tl->stride_p;
+    p.out = static_cast<uint8_t*>(out);
+    p.osb = osb;
+    p.osp = osp;
+    p.tokens = out_tokens;
+    p.rec = static_cast<uint64_t*>(base);
+    p.B = B;
+    p.K = K;
+    p.V = V;
+    p.nchp = nchp;
+    p.k0 = static_cast<uint32_t>(seed);
+    p.k1 = static_cast<uint32_t>(seed >> 32);
+    p.tag = next_tag();
+    const int dtype = tl->dtype == SV_BF16 ? sv::DT_BF16 : sv::DT_F32;
+    rc = timed_launch(sv::KK_PRODUCE, stream,
+                      [&](const sv::LaunchEvents& ev) { return sv::launch_produce(p, dtype, stream, ev); });
+    if (rc) return rc;
+    return timed_launch(sv::KK_PRODUCE, stream,
+                        [&](const sv::LaunchEvents& ev) { return sv::launch_produce_tokens(p, stream, ev); });
+}
+
 }  // namespace
 
 extern "C" {
@@ -468,6 +514,11 @@ int spec_smc_step(const sv_logits* target_logits, const sv_logits* draft_logits,
                   double* out_logw, int32_t* out_ancestor, double* out_ess, int32_t* out_resampled, void* stream) {
     return smc_impl(target_logits, draft_logits, draft_tokens, logw_in, temperature, ess_fraction, seed, out_bonus,
                     out_logw, out_ancestor, out_ess, out_resampled, stream);
+}
+
+int spec_draft_produce(const sv_logits* target_logits, int32_t K, uint64_t seed, void* draft_out,
+                       int64_t out_stride_b, int64_t out_stride_p, int32_t* out_tokens, void* stream) {
+    return produce_impl(target_logits, K, seed, draft_out, out_stride_b, out_stride_p, out_tokens, stream);
 }
 
 const char* spec_verify_strerror(int status) {

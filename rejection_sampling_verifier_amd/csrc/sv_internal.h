@@ -23,7 +23,7 @@ constexpr uint32_t kNoCover = 0xFFFFFFFFu;  // candidate header: the chunk's lis
 
 enum DType : int { DT_F32 = 0, DT_BF16 = 1 };
 enum RowMode : int { MODE_SKIP = 0, MODE_RESID = 1, MODE_BONUS = 2 };
-enum KernelKind : int { KK_STATS = 0, KK_TOPP = 1, KK_RESAMPLE = 2, KK_SMC = 3, KK_COUNT = 4 };
+enum KernelKind : int { KK_STATS = 0, KK_TOPP = 1, KK_RESAMPLE = 2, KK_SMC = 3, KK_PRODUCE = 4, KK_COUNT = 5 };
 
 // Statistics of one chunk of one logit row, relative to an integer offset o:
 // s = sum over the chunk of 2^(l*c - o), c = log2(e)/T; m = max logit; lx =
@@ -101,9 +101,23 @@ struct Params {
     // greedy verify: the top-k ids after the emitted token
     int topk;
     int32_t* out_topk;            // [B, topk]
-    uint64_t* chdr;               // top-p: [B, nslot, nch, kWaves, 4] tagged candidate headers (count, key bound,
-                                  // key of the wave's max, lowest listed id holding it)
-    uint64_t* cand;               // top-p: [B, nslot, nch, kCand] candidates (~key << 32 | id), kCand/kWaves per wave
+    uint64_t* chdr;               // top-p and greedy: [B, nslot, nch, kWaves, 4] tagged candidate headers (count,
+                                  // key bound, key of the wave's max, lowest listed id holding it)
+    uint64_t* cand;               // top-p and greedy: [B, nslot, nch, kCand] candidates (~key << 32 | id),
+                                  // kCand/kWaves per wave
+};
+
+// The synthetic draft producer of the two-batch schedule (sv_produce.hip).
+constexpr int kProdU = 4;  // groups of 8 ids per thread per producer workgroup
+struct ProduceParams {
+    const uint8_t* tgt;           // target logits [B, >= K, V]
+    int64_t tsb, tsp;             // its strides (elements)
+    uint8_t* out;                 // draft logits written [B, K, V], same dtype
+    int64_t osb, osp;
+    int32_t* tokens;              // [B, K] greedy draft tokens
+    uint64_t* rec;                // [B, K, nchp, 2] scratch: tagged (key, id) per chunk
+    int B, K, V, nchp;
+    uint32_t k0, k1, tag;
 };
 
 // Timing events of one launch (both null when timing is off).
@@ -122,12 +136,16 @@ hipError_t launch_rows(const Params& p, int dtype, bool topp, hipStream_t s, con
 // increments and the bonus draw), then the resampling kernel.
 hipError_t launch_smc_rows(const Params& p, int dtype, hipStream_t s, const LaunchEvents& ev);
 hipError_t launch_smc_resample(const Params& p, hipStream_t s, const LaunchEvents& ev);
-// Greedy verify: one workgroup per batch row after a statistics pass over the
-// target rows (nslot = K + 1) with candidate lists.
+// Greedy verify: a statistics pass of its own over the target rows (nslot =
+// K + 1) that lists each wave's largest logits, then one workgroup per batch
+// row.
 hipError_t launch_greedy_stats(const Params& p, int dtype, int unroll, hipStream_t s, const LaunchEvents& ev);
 hipError_t launch_greedy_rows(const Params& p, int dtype, hipStream_t s, const LaunchEvents& ev);
 // Two-stage verify: stage 2's draft lengths (n1 + 1) from stage 1's counts.
 hipError_t launch_hispec_link(const int32_t* n1, int32_t* len2, int32_t* out_n1, int B, hipStream_t s);
 hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, int unroll, hipStream_t s);
+// Synthetic draft producer: drafts and chunk records, then the tokens.
+hipError_t launch_produce(const ProduceParams& p, int dtype, hipStream_t s, const LaunchEvents& ev);
+hipError_t launch_produce_tokens(const ProduceParams& p, hipStream_t s, const LaunchEvents& ev);
 
 }  // namespace sv

@@ -1530,7 +1530,6 @@ __device__ uint32_t candidate_bound(const Params& P, int rvi, int lane) {
 template <int DT>
 __global__ __launch_bounds__(kThreads) void k_topp(Params P) {
     __shared__ SelShared sh;
-    __shared__ RowShared R;
     __shared__ float s_o, s_m, s_lx;
     __shared__ double s_s;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -2132,8 +2131,7 @@ __global__ __launch_bounds__(kThreads) void k_smc_rows(Params P) {
 // of positive weight), and every log-weight becomes 0; otherwise a_k = k.
 __global__ __launch_bounds__(kThreads) void k_smc_resample(Params P) {
     __shared__ double s_red[kWaves];
-    __shared__ double s_m, s_W;
-    __shared__ int s_last;
+    __shared__ double s_m;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int N = P.B;
     // max log-weight (NaN cannot occur: invalid particles hold -inf)

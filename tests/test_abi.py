@@ -132,3 +132,20 @@ def _greedy(lib, B=3, K=2, V=64, k=5, tdata=0x1000, tokens=0x4000, out=0x5000, o
 ])
 def test_greedy_host_validation(lib, kw, code):
     assert _greedy(lib, **kw) == code
+
+
+def _produce(lib, B=3, P=4, K=2, V=64, tdata=0x1000, out=0x5000, osb=None, osp=None, tokens=0x6000, dtype=1):
+    t = binding.SvLogits(tdata, dtype, B, P, V, P * V, V)
+    v = ctypes.c_void_p
+    return lib.spec_draft_produce(ctypes.byref(t), ctypes.c_int32(K), ctypes.c_uint64(1), v(out),
+                                  ctypes.c_int64(K * V if osb is None else osb), ctypes.c_int64(V if osp is None else osp),
+                                  v(tokens), v(None))
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(out=0), -1), (dict(tokens=0), -1), (dict(tdata=0), -1), (dict(osb=-1), -1), (dict(osp=-5), -1),
+    (dict(K=0), -2), (dict(K=5), -2), (dict(B=0), -2), (dict(V=0), -2), (dict(dtype=7), -3),
+    (dict(out=0x5001), -6), (dict(tokens=0x6002), -6), (dict(tdata=0x1001), -6),
+])
+def test_produce_host_validation(lib, kw, code):
+    assert _produce(lib, **kw) == code

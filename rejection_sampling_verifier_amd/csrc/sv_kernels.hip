@@ -527,8 +527,9 @@ __device__ __forceinline__ void mask_edge_raw(uint4& v, int64_t k, int head, int
 // top bin alone holds too many tokens, or whose list overflows, records
 // kNoCover.
 constexpr uint32_t kCandLowBits = 448u << 21;  // e >= 2^-15
-// 64-bit words of a wave's candidate header: count, key bound, the key of the
-// wave's max logit, the lowest listed id holding it (each tagged)
+// 64-bit words of a wave's candidate header: count, key bound (both lists),
+// the key of the wave's max logit and the lowest listed id holding it (greedy
+// lists only), each tagged
 constexpr int kHdrWords = 4;
 constexpr int kCandW = kCand / kWaves;         // list slots per wave
 constexpr int kCandSlack = 8;
@@ -626,8 +627,7 @@ __device__ __forceinline__ void reduce_lane(const RowGrid& g, uint4* raw, int64_
 // bound) goes to header `hdr`.
 template <int DT, int U>
 __device__ __forceinline__ void list_wave_candidates(const Params& P, const RowGrid& g, uint4* raw, int64_t k0, float o,
-                                                     float m, const uint32_t* hist, uint64_t* stage, size_t slot0,
-                                                     size_t hdr) {
+                                                     const uint32_t* hist, uint64_t* stage, size_t slot0, size_t hdr) {
     const int tid = threadIdx.x, lane = tid & 63;
     // top bins first: lane i counts the 9-bit value 511 - i of e
     const double incl = wave_scan_dpp(static_cast<double>(hist[kCandHist - 1 - lane]));
@@ -674,23 +674,15 @@ __device__ __forceinline__ void list_wave_candidates(const Params& P, const RowG
     }
     const bool over = base > static_cast<uint32_t>(kCandW);
     // same-wave LDS order: the stage is complete for this wave's lanes; the
-    // entries leave as (~key << 32 | id).  The wave's max logit and the lowest
-    // listed id holding it go into the header too.
-    const float mw = wave_max_dpp(m);
-    int amax = 0x7FFFFFFF;
+    // entries leave as (~key << 32 | id).  The nucleus pass reads the count
+    // and the bound (header words 0 and 1).
     if (!over && static_cast<uint32_t>(lane) < base) {
         const uint64_t st = stage[lane];
-        const float v = __uint_as_float(static_cast<uint32_t>(st >> 32));
-        const uint32_t key = order_key(v);
+        const uint32_t key = order_key(__uint_as_float(static_cast<uint32_t>(st >> 32)));
         P.cand[slot0 + lane] = (static_cast<uint64_t>(~key) << 32) | static_cast<uint32_t>(st);
-        if (v == mw) amax = static_cast<int>(static_cast<uint32_t>(st));
     }
-    amax = wave_min_int_dpp(amax);
-    if (lane < kHdrWords) {
-        const uint32_t v = lane == 0 ? (over ? 0u : base)
-                           : lane == 1 ? (over ? kNoCover : kw)
-                           : lane == 2 ? order_key(mw)
-                                       : static_cast<uint32_t>(amax);
+    if (lane < 2) {
+        const uint32_t v = lane == 0 ? (over ? 0u : base) : (over ? kNoCover : kw);
         P.chdr[kHdrWords * hdr + lane] = tagged(P.tag, v);
     }
 }
@@ -751,7 +743,7 @@ __device__ __forceinline__ void stats_item(const Params& P, int b, int slot, int
                              lx, m, o, sl);
     if (CAND) {
         const size_t ci = (static_cast<size_t>(b) * P.nslot + slot) * P.nch + chunk;
-        list_wave_candidates<DT, U>(P, g, raw, k0, o, m, hist, sh_stage[wv], ci * kCand + wv * kCandW,
+        list_wave_candidates<DT, U>(P, g, raw, k0, o, hist, sh_stage[wv], ci * kCand + wv * kCandW,
                                     ci * kWaves + wv);
     }
     // the one lane holding the drafted id's vector hands its logit over,

@@ -259,7 +259,8 @@ int spec_smc_step(const sv_logits* target_logits, const sv_logits* draft_logits,
  * K              1 <= K <= P.
  * draft_out      device buffer of the target's dtype, written at element
  *                b*out_stride_b + j*out_stride_p + v (strides in elements,
- *                >= 0); must not overlap the target.
+ *                >= 0); its rows must not overlap one another or the
+ *                target (the library does not check this).
  * out_tokens     device int32 [B, K], contiguous.
  *
  * Errors as spec_verify: SV_EINVAL (NULL pointer, negative stride),

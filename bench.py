@@ -757,6 +757,37 @@ def main():
     print(f"[bench] statistics kernel {stats_ms / max(stats_n, 1) * 1e3:.2f} us, row kernel "
           f"{res_ms / max(res_n, 1) * 1e3:.2f} us ({stats_n} launches)", file=sys.stderr, flush=True)
 
+    # timed region 3: the same calls with two independent batches in flight
+    # (calls alternate between two streams, nothing orders them), as a
+    # serving loop that keeps two batches (MineDraft's batch-parallel
+    # schedule) would issue them.  Reported beside the sequential figure.
+    stream_b = torch.cuda.Stream(dev)
+    outs2 = [(torch.empty((B, K + 1), dtype=torch.int32, device=dev), torch.empty((B,), dtype=torch.int32, device=dev))
+             for _ in range(2 * N_SETS)]
+
+    def step2(i):
+        t, d, x, dl, T, tp, seed = dsets[i % N_SETS]
+        o = outs2[i % (2 * N_SETS)]
+        binding.verify(t, d, x, dl, T, tp, seed, stream=stream if i % 2 == 0 else stream_b, out_tokens=o[0],
+                       out_n_accepted=o[1])
+
+    for i in range(min(args.warmup, 200)):
+        step2(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    stream_b.wait_event(e0)
+    for i in range(args.steps):
+        step2(i)
+    joined = torch.cuda.Event()
+    joined.record(stream_b)
+    stream.wait_event(joined)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step2 = e0.elapsed_time(e1) / args.steps
+    print(f"[bench] two batches in flight: {ms_step2 * 1e3:.2f} us per call", file=sys.stderr, flush=True)
+
     traffic = stored_traffic()
     roofline = {
         "bound": "hbm",
@@ -811,6 +842,12 @@ def main():
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "two_batches_in_flight": {
+            "us_per_call": round(ms_step2 * 1e3, 3),
+            "positions_per_s": round(positions / (ms_step2 / 1e3), 1),
+            "logits_GBps": round(logical / (ms_step2 / 1e3) / 1e9, 1),
+            "logits_frac_of_peak": round(logical / (ms_step2 / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
+        },
         **({"calibration": calib} if calib else {}),
     }
     print(json.dumps(line), flush=True)

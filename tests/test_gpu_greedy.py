@@ -157,3 +157,29 @@ def test_greedy_nan_and_inf_in_a_full_chunk():
     t[3, 5, 128255] = W.f32_to_bf16_bits(np.float32(-np.inf)).item()
     r = _check(t, x, None, 60, "NaN / +inf / -inf in full rows")
     assert r.n_accepted[1] == -1 and r.n_accepted[2] == -1 and r.n_accepted[3] >= 0
+
+
+def test_greedy_large_ragged_full_size():
+    """The large ragged batch's shape (B=256, K=8, V=128256 bf16, ragged
+    lengths, padded positions NaN and never read): every row's decision
+    against the oracle, the top-60 on a sample of rows."""
+    inp = W.make_inputs(3, 5)
+    t = inp.target
+    tf = np.nan_to_num(W.bf16_bits_to_f32(t), nan=-1e30)
+    x = _drafts(tf, 5)
+    x = np.where(inp.draft_tokens >= 0, x, -1).astype(np.int32)
+    say(f"[greedy] large ragged B={t.shape[0]} K={t.shape[1] - 1} V={t.shape[2]}")
+    xt = torch.from_numpy(x).cuda()
+    dlt = torch.from_numpy(inp.draft_len.astype(np.int32)).cuda()
+    tok, n, tk = binding.greedy_verify(dev_array(t), xt, dlt, 60)
+    torch.cuda.synchronize()
+    tok, n, tk = tok.cpu().numpy(), n.cpu().numpy(), tk.cpu().numpy()
+    rows = list(range(0, t.shape[0], 16)) + [t.shape[0] - 1]
+    for b in range(t.shape[0]):
+        L = int(inp.draft_len[b])
+        am = [oracle.argmax_lowest(W.bf16_bits_to_f32(t[b, j])) for j in range(L + 1)]
+        nb = next((j for j in range(L) if x[b, j] != am[j]), L)
+        assert n[b] == nb, (b, n[b], nb)
+        assert np.array_equal(tok[b, :nb], x[b, :nb]) and tok[b, nb] == am[nb] and np.all(tok[b, nb + 1:] == -1), b
+        if b in rows:
+            assert np.array_equal(tk[b], oracle.top_k_after_first(W.bf16_bits_to_f32(t[b, nb]), 60)), b

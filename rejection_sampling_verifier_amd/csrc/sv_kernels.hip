@@ -2544,13 +2544,20 @@ __global__ __launch_bounds__(kThreads) void k_greedy_rows(Params P) {
         if (sh.tbin >= 0) {
             greedy_rank(sh, static_cast<int>(sh.nlist), k);
             const uint32_t theta = ~static_cast<uint32_t>(sh.top[k] >> 32);
-            // shares that may hold unlisted tokens at or above theta
-            for (int h = tid; h < per_row; h += kThreads) {
-                const uint64_t* hw = P.chdr + ((row0 + n) * per_row + static_cast<size_t>(h)) * kHdrWords;
-                if (static_cast<uint32_t>(hw[1]) > theta && static_cast<uint32_t>(hw[2]) >= theta) {
+            // shares that may hold unlisted tokens at or above theta: from
+            // the headers this thread kept in registers, the rest re-read
+            auto reread_candidate = [&](uint32_t bound, uint32_t mkey, int hr) {
+                if (bound > theta && mkey >= theta) {
                     const uint32_t at = atomicAdd(&sh.nr, 1u);
-                    if (at < static_cast<uint32_t>(kRerTop)) sh.rset[at] = h;
+                    if (at < static_cast<uint32_t>(kRerTop)) sh.rset[at] = hr;
                 }
+            };
+#pragma unroll
+            for (int q = 0; q < kHR; ++q)
+                if (hj[q] == n) reread_candidate(hb[q], hm[q], tid + q * kThreads - n * per_row);
+            for (int h = max(n * per_row, kHR * kThreads) + tid; h < (n + 1) * per_row; h += kThreads) {
+                const uint64_t* hw = P.chdr + (row0 * per_row + static_cast<size_t>(h)) * kHdrWords;
+                reread_candidate(static_cast<uint32_t>(hw[1]), static_cast<uint32_t>(hw[2]), h - n * per_row);
             }
             __syncthreads();
             const int nr = static_cast<int>(sh.nr);

@@ -183,3 +183,15 @@ def test_greedy_large_ragged_full_size():
         assert np.array_equal(tok[b, :nb], x[b, :nb]) and tok[b, nb] == am[nb] and np.all(tok[b, nb + 1:] == -1), b
         if b in rows:
             assert np.array_equal(tk[b], oracle.top_k_after_first(W.bf16_bits_to_f32(t[b, nb]), 60)), b
+
+
+@pytest.mark.parametrize("unroll", [4, 8])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_greedy_statistics_variants(unroll, dtype, monkeypatch):
+    """Both compiled statistics variants (4 or 8 vectors per lane; with 4, a
+    V = 128256 bf16 row has 16 chunks, so the row kernel reads the lists in
+    two batches of eight chunks)."""
+    monkeypatch.setenv("SPECVERIFY_STATS_UNROLL", str(unroll))
+    inp = W.make_inputs(2, 13, B=6, dtype=dtype)
+    x = _drafts(_f32(inp.target), 13)
+    _check(inp.target, x, None, 60, f"unroll={unroll} {dtype}")

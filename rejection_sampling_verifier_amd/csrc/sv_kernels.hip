@@ -28,6 +28,17 @@
 //               tagged records and lets the item holding u*Z pick the token
 //               by an in-order scan.
 //
+// The other entry points reuse these pieces:
+//   SMC-SD step       k_stats, then k_smc_rows (per particle: log-weight
+//                     increment and bonus draw) and k_smc_resample (ESS,
+//                     systematic resampling in one workgroup).
+//   two-stage verify  the verify pipeline twice, linked by k_hispec_link.
+//   greedy verify     k_greedy_stats (max and candidate lists of the target
+//                     rows, no exponentials), then k_greedy_rows (one
+//                     workgroup per batch row: argmaxes, decision, top-k).
+// The synthetic draft producer of the two-batch schedule is in
+// sv_produce.hip.
+//
 // Hand-offs between workgroups of one kernel use tagged 64-bit records: an
 // aligned 64-bit store is single-copy atomic, so a producer stores and exits,
 // and a consumer polls (bounded) until every word carries the call's tag.

@@ -667,7 +667,8 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the verify step is built and timed on a single MI355X "
-              "(batch rows shard across GPUs with no exchange; see the design notes).", file=sys.stderr)
+              "(batch rows shard across GPUs with no exchange: each GPU runs this step on its own rows).",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np

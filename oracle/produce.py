@@ -9,8 +9,8 @@ draft model drafts the other, and the roles swap at the end of every step.
 On one GPU the verify step of one batch runs on one stream while a producer
 of the other batch's drafts runs on a second stream.
 
-The pages give no drafter, so the producer is defined here (a reading listed
-in the design notes).  For every batch row b and draft position j < K:
+The pages give no drafter, so the producer is defined here.  For every
+batch row b and draft position j < K:
 
   * delta(b, j, v) = ((h >> 5) - 1024) * 2^-9, where h is the 16-bit half
     (v & 1: 0 = low, 1 = high) of word (v & 7) >> 1 of Philox4x32-10 at

@@ -177,6 +177,24 @@ def calibrate(binding, torch, dev, logical):
     torch.cuda.synchronize()
     print(f"[bench] calibration: 3 copies and 3 streaming reads of {CALIB_BYTES} bytes", file=sys.stderr, flush=True)
     del src, dst
+    # the streaming-read ceiling over 1 GiB, and the device's own figures
+    big = torch.full((1 << 30,), 5, dtype=torch.uint8, device=dev)
+    for _ in range(5):
+        binding.stream_read(big, sink, 8)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(20):
+        binding.stream_read(big, sink, 8)
+    e1.record()
+    torch.cuda.synchronize()
+    big_GBps = (1 << 30) / (e0.elapsed_time(e1) / 20 * 1e-3) / 1e9
+    del big
+    props = torch.cuda.get_device_properties(dev)
+    device = {"name": props.name, "arch": getattr(props, "gcnArchName", ""), "compute_units": props.multi_processor_count,
+              "memory_GiB": round(props.total_memory / 2 ** 30, 1),
+              "l2_MiB": round(getattr(props, "L2_cache_size", 0) / 2 ** 20, 1)}
+    print(f"[bench] streaming read of 1 GiB: {big_GBps:.0f} GB/s; device {device}", file=sys.stderr, flush=True)
     nbytes = int(logical) // 16 * 16
     bufs = [torch.full((nbytes,), 3, dtype=torch.uint8, device=dev) for _ in range(N_SETS)]
     stream = torch.cuda.current_stream(dev)
@@ -193,7 +211,8 @@ def calibrate(binding, torch, dev, logical):
     us = e0.elapsed_time(e1) / reps * 1e3
     print(f"[bench] streaming read of {nbytes} bytes: {us:.2f} us", file=sys.stderr, flush=True)
     return {"stream_read_bytes": nbytes, "stream_read_us": round(us, 3),
-            "stream_read_GBps": round(nbytes / (us * 1e-6) / 1e9, 1)}
+            "stream_read_GBps": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "stream_read_1GiB_GBps": round(big_GBps, 1), "device": device}
 
 
 # ---------------------------------------------------------------------------

@@ -1824,12 +1824,31 @@ __device__ void resample_body(const Params& P, int b, int r, const RowParam& rp,
         st_agent(qrec + static_cast<size_t>(r) * kRecWords + tid, tagged(P.tag, static_cast<uint32_t>(v)));
     }
 
+    // the item's per-run wave totals and last positive id, while the other
+    // items' masses arrive (only the item holding t uses them)
+    auto item_scans = [&]() {
+        int lastpos = -1;
+#pragma unroll
+        for (int k = 0; k < R; ++k) {
+            const double wik = wave_scan_dpp(static_cast<double>(xs[k]));
+            if (lane == 63) s_wt[k][wv] = wik;
+            const int64_t id0 = item_run_id0<R>(r, k);
+#pragma unroll
+            for (int i = 0; i < kRun; ++i)
+                if (w[k][i] > 0.f) lastpos = static_cast<int>(id0 + i);
+        }
+        lastpos = wave_max_int_dpp(lastpos);
+        if (lane == 0) s_lastpos[wv] = lastpos;
+    };
+    item_scans();
+
     // 3. every item's masses in id order (wave 0; lane l takes items
     // [l*g, (l+1)*g)): Z, t = u*Z and the item holding t
     if (wv == 0) {
         const int g = (nq + 63) / 64;
         const int e0 = min(lane * g, nq), e1 = min(e0 + g, nq);
         double wsum = 0.0, psum = 0.0;
+        double W1 = 0.0, P1 = 0.0;  // the lane's one item when g == 1
         bool ok = true;
         for (int e = e0; e < e1; ++e) {
             double W = Wown, Pm = Pown;
@@ -1841,6 +1860,8 @@ __device__ void resample_body(const Params& P, int b, int r, const RowParam& rp,
             }
             wsum += W;
             psum += Pm;
+            W1 = W;
+            P1 = Pm;
         }
         double incl = wave_scan_dpp(wsum);
         double Z = lane63(incl);
@@ -1859,9 +1880,11 @@ __device__ void resample_body(const Params& P, int b, int r, const RowParam& rp,
         double pf = 0.0, pl = 0.0;
         for (int e = e0; e < e1; ++e) {
             double m = sel ? Pown : Wown;
-            if (e != r) {
-                // the record is in memory now; read it again rather than
-                // keep g values per lane
+            if (g == 1) {
+                m = sel ? P1 : W1;
+            } else if (e != r) {
+                // several items per lane: the record is in memory now; read
+                // it again rather than keep g values per lane
                 uint32_t pay[kRecWords];
                 poll_record(qrec + static_cast<size_t>(e) * kRecWords, P.tag, pay);
                 const uint64_t lo = pay[sel ? 2 : 0], hi = pay[sel ? 3 : 1];
@@ -1925,21 +1948,9 @@ __device__ void resample_body(const Params& P, int b, int r, const RowParam& rp,
             xs[k] = run_sum(w[k]);
             __builtin_amdgcn_sched_barrier(0);
         }
+        item_scans();
+        __syncthreads();
     }
-    double wi[R];
-    int lastpos = -1;
-#pragma unroll
-    for (int k = 0; k < R; ++k) {
-        wi[k] = wave_scan_dpp(static_cast<double>(xs[k]));
-        if (lane == 63) s_wt[k][wv] = wi[k];
-        const int64_t id0 = item_run_id0<R>(r, k);
-#pragma unroll
-        for (int i = 0; i < kRun; ++i)
-            if (w[k][i] > 0.f) lastpos = static_cast<int>(id0 + i);
-    }
-    lastpos = wave_max_int_dpp(lastpos);
-    if (lane == 0) s_lastpos[wv] = lastpos;
-    __syncthreads();
     // the (run, wave) holding t, from the 16 totals in id order
     double base = s_pre, hoff = 0.0;
     int hk = -1, hw = -1, lp = -1;
@@ -1974,15 +1985,16 @@ __device__ void resample_body(const Params& P, int b, int r, const RowParam& rp,
     if (wv != hw) return;
     // wave hw: the first lane of run hk whose inclusive prefix passes t
     float v[kRun];
-    double myx = 0.0, myw = 0.0;
+    double myx = 0.0;
 #pragma unroll
     for (int k = 0; k < R; ++k)
         if (k == hk) {
 #pragma unroll
             for (int i = 0; i < kRun; ++i) v[i] = w[k][i];
             myx = static_cast<double>(xs[k]);
-            myw = wi[k];
         }
+    // the run's wave scan again (the same additions as for its total)
+    const double myw = wave_scan_dpp(myx);
     const double incl = hoff + myw;
     const unsigned long long hm = __ballot(myx > 0.0 && incl > t);
     const int hl = hm ? __ffsll(static_cast<long long>(hm)) - 1 : 63;

@@ -674,6 +674,8 @@ def main():
                     help="seeded workload to time (default: the batched B=64 K=5 V=128256 bf16 one)")
     ap.add_argument("--greedy", action="store_true",
                     help="time greedy verify with the top-60 (spec_greedy_verify) on the batched target logits")
+    ap.add_argument("--two-batches", action="store_true",
+                    help="also time the batched calls with two independent batches in flight on two streams")
     ap.add_argument("--overlap", action="store_true",
                     help="time the two-batch schedule: verify on one stream, the synthetic draft producer on another")
     ap.add_argument("--hispec", action="store_true",
@@ -777,36 +779,44 @@ def main():
     print(f"[bench] statistics kernel {stats_ms / max(stats_n, 1) * 1e3:.2f} us, row kernel "
           f"{res_ms / max(res_n, 1) * 1e3:.2f} us ({stats_n} launches)", file=sys.stderr, flush=True)
 
-    # timed region 3: the same calls with two independent batches in flight
-    # (calls alternate between two streams, nothing orders them), as a
-    # serving loop that keeps two batches (MineDraft's batch-parallel
-    # schedule) would issue them.  Reported beside the sequential figure.
-    stream_b = torch.cuda.Stream(dev)
-    outs2 = [(torch.empty((B, K + 1), dtype=torch.int32, device=dev), torch.empty((B,), dtype=torch.int32, device=dev))
-             for _ in range(2 * N_SETS)]
+    # timed region 3 (--two-batches): the same calls with two independent
+    # batches in flight (calls alternate between two streams, nothing orders
+    # them), as a serving loop that keeps two batches (MineDraft's
+    # batch-parallel schedule) would issue them.  Reported beside the
+    # sequential figure; off by default so that a kernel trace of the default
+    # run holds sequential calls only.
+    two = None
+    if args.two_batches:
+        stream_b = torch.cuda.Stream(dev)
+        outs2 = [(torch.empty((B, K + 1), dtype=torch.int32, device=dev),
+                  torch.empty((B,), dtype=torch.int32, device=dev)) for _ in range(2 * N_SETS)]
 
-    def step2(i):
-        t, d, x, dl, T, tp, seed = dsets[i % N_SETS]
-        o = outs2[i % (2 * N_SETS)]
-        binding.verify(t, d, x, dl, T, tp, seed, stream=stream if i % 2 == 0 else stream_b, out_tokens=o[0],
-                       out_n_accepted=o[1])
+        def step2(i):
+            t, d, x, dl, T, tp, seed = dsets[i % N_SETS]
+            o = outs2[i % (2 * N_SETS)]
+            binding.verify(t, d, x, dl, T, tp, seed, stream=stream if i % 2 == 0 else stream_b, out_tokens=o[0],
+                           out_n_accepted=o[1])
 
-    for i in range(min(args.warmup, 200)):
-        step2(i)
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    stream_b.wait_event(e0)
-    for i in range(args.steps):
-        step2(i)
-    joined = torch.cuda.Event()
-    joined.record(stream_b)
-    stream.wait_event(joined)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms_step2 = e0.elapsed_time(e1) / args.steps
-    print(f"[bench] two batches in flight: {ms_step2 * 1e3:.2f} us per call", file=sys.stderr, flush=True)
+        for i in range(min(args.warmup, 200)):
+            step2(i)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        stream_b.wait_event(e0)
+        for i in range(args.steps):
+            step2(i)
+        joined = torch.cuda.Event()
+        joined.record(stream_b)
+        stream.wait_event(joined)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_step2 = e0.elapsed_time(e1) / args.steps
+        print(f"[bench] two batches in flight: {ms_step2 * 1e3:.2f} us per call", file=sys.stderr, flush=True)
+        two = {"us_per_call": round(ms_step2 * 1e3, 3),
+               "positions_per_s": round(positions / (ms_step2 / 1e3), 1),
+               "logits_GBps": round(logical / (ms_step2 / 1e3) / 1e9, 1),
+               "logits_frac_of_peak": round(logical / (ms_step2 / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
 
     traffic = stored_traffic()
     roofline = {
@@ -862,12 +872,7 @@ def main():
         },
         "roofline": roofline,
         "cpu_baseline": cpu,
-        "two_batches_in_flight": {
-            "us_per_call": round(ms_step2 * 1e3, 3),
-            "positions_per_s": round(positions / (ms_step2 / 1e3), 1),
-            "logits_GBps": round(logical / (ms_step2 / 1e3) / 1e9, 1),
-            "logits_frac_of_peak": round(logical / (ms_step2 / 1e3) / 1e9 / HBM_PEAK_GBS, 4),
-        },
+        **({"two_batches_in_flight": two} if two else {}),
         **({"calibration": calib} if calib else {}),
     }
     print(json.dumps(line), flush=True)

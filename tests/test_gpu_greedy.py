@@ -195,3 +195,9 @@ def test_greedy_statistics_variants(unroll, dtype, monkeypatch):
     inp = W.make_inputs(2, 13, B=6, dtype=dtype)
     x = _drafts(_f32(inp.target), 13)
     _check(inp.target, x, None, 60, f"unroll={unroll} {dtype}")
+
+
+def test_greedy_large_vocabulary():
+    inp = W.make_inputs(2, 14, B=6, V=262147)
+    x = _drafts(_f32(inp.target), 14)
+    _check(inp.target, x, None, 64, "V=262147 k=64")

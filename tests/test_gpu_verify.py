@@ -309,3 +309,13 @@ def test_kernel_variants(runs, unroll, monkeypatch):
     for cfg, top_p in ((2, None), (4, 0.6)):
         inp = W.make_inputs(cfg, 5, B=6, V=20011, top_p=top_p)
         _parity(inp, label=f"variant unroll={unroll} runs={runs} cfg={cfg}")
+
+
+@pytest.mark.parametrize("top_p", [1.0, 0.9])
+def test_large_vocabulary(top_p):
+    """A vocabulary twice the batched workload's and not a multiple of the
+    chunk (V = 262147: 17 statistics chunks per bf16 row, a ragged last
+    vector), with and without top-p."""
+    cfg = 4 if top_p < 1.0 else 2
+    for step in range(2):
+        _parity(W.make_inputs(cfg, 200 + step, B=6, V=262147), label=f"V=262147 top_p={top_p} step {step}")

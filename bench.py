@@ -45,15 +45,16 @@ def kernel_source_sha():
     return h.hexdigest()[:16]
 
 
-def stored_traffic():
+def stored_traffic(workload_name):
     """HBM bytes per statistics-pass launch from the committed counter runs,
-    or None when the kernel sources changed since they were taken."""
+    or None when they were taken on another workload or the kernel sources
+    changed since."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_sha") != kernel_source_sha():
+    if t.get("kernel_source_sha") != kernel_source_sha() or t.get("workload") != workload_name:
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -818,7 +819,7 @@ def main():
                "logits_GBps": round(logical / (ms_step2 / 1e3) / 1e9, 1),
                "logits_frac_of_peak": round(logical / (ms_step2 / 1e3) / 1e9 / HBM_PEAK_GBS, 4)}
 
-    traffic = stored_traffic()
+    traffic = stored_traffic(w.name)
     roofline = {
         "bound": "hbm",
         "achieved": round(achieved, 1),

@@ -1681,36 +1681,31 @@ __device__ __forceinline__ bool kept_l(float l, float tv, int id, int32_t cut) {
     return l > tv || (l == tv && id <= cut);
 }
 
-// Residual weights w = max(0, p' - q') (or p' for the bonus) and p' of a run.
-// With top-p both are 0 wherever the target token is outside its nucleus.
+// Residual weights of a run in units of the target's kept mass: with
+// eT = 2^(lT*c - oT) and eD = 2^(lD*c - oD), p' = eT/keptT and q' =
+// eD/keptD, so max(0, p' - q') = max(0, eT - rho*eD)/keptT for rho =
+// keptT/keptD.  w gets max(0, eT - rho*eD) (eT for the bonus) and p gets eT;
+// the caller scales sums by 1/keptT when it widens them to float64, so no
+// per-id multiply by a kept mass is needed.  With top-p, eT and eD are 0
+// wherever their token is outside its nucleus.
 template <bool TOPP>
 __device__ __forceinline__ void run_weights(const float* lt, const float* ld, bool resid, int64_t id0, const RowParam& rp,
-                                            float c_hi, float c_lo, float invT, float invD, float* w, float* p) {
+                                            float c_hi, float c_lo, float rho, float* w, float* p) {
     const float tvT = TOPP ? kept_bound(rp.tauT) : 0.f;
     const float tvD = TOPP ? kept_bound(rp.tauD) : 0.f;
     const int i0 = static_cast<int>(id0);  // ids < 2^24
 #pragma unroll
     for (int i = 0; i < kRun; ++i) {
-        if (TOPP) {
-            const bool kt = kept_l(lt[i], tvT, i0 + i, rp.cutT);
-            const float pt = kt ? tempexp(lt[i], c_hi, c_lo, rp.oT) * invT : 0.f;
-            float wi = pt;
-            if (resid) {
-                const float qd = kept_l(ld[i], tvD, i0 + i, rp.cutD) ? tempexp(ld[i], c_hi, c_lo, rp.oD) * invD : 0.f;
-                wi = fmaxf(pt - qd, 0.f);
-            }
-            w[i] = wi;
-            p[i] = pt;
-        } else {
-            const float pt = tempexp(lt[i], c_hi, c_lo, rp.oT) * invT;
-            float wi = pt;
-            if (resid) {
-                const float qd = tempexp(ld[i], c_hi, c_lo, rp.oD) * invD;
-                wi = fmaxf(pt - qd, 0.f);
-            }
-            w[i] = wi;
-            p[i] = pt;
+        float eT = tempexp(lt[i], c_hi, c_lo, rp.oT);
+        if (TOPP && !kept_l(lt[i], tvT, i0 + i, rp.cutT)) eT = 0.f;
+        float wi = eT;
+        if (resid) {
+            float eD = tempexp(ld[i], c_hi, c_lo, rp.oD);
+            if (TOPP && !kept_l(ld[i], tvD, i0 + i, rp.cutD)) eD = 0.f;
+            wi = fmaxf(fmaf(-rho, eD, eT), 0.f);
         }
+        w[i] = wi;
+        p[i] = eT;
     }
 }
 
@@ -1748,7 +1743,7 @@ __device__ __forceinline__ void load_item(const uint8_t* rowT, const uint8_t* ro
 // Weights of run k of item r: w = max(0, p' - q') (or p' for the bonus) and
 // p = p'.  `interior`: the whole item lies inside the row (nothing to mask).
 template <int DT, bool TOPP, bool RESID, int R>
-__device__ __forceinline__ void item_run(const Params& P, const RowParam& rp, float invT, float invD,
+__device__ __forceinline__ void item_run(const Params& P, const RowParam& rp, float rho,
                                          const ItemRaw<DT, R>& raw, int r, int k, bool interior, float* w, float* p) {
     const int64_t id0 = item_run_id0<R>(r, k);
     float lt[kRun], ld[kRun];
@@ -1759,7 +1754,7 @@ __device__ __forceinline__ void item_run(const Params& P, const RowParam& rp, fl
         unpack_masked<DT>(raw.t[k], id0, P.V, lt);
         if (RESID) unpack_masked<DT>(raw.d[k], id0, P.V, ld);
     }
-    run_weights<TOPP>(lt, ld, RESID, id0, rp, P.c_hi, P.c_lo, invT, invD, w, p);
+    run_weights<TOPP>(lt, ld, RESID, id0, rp, P.c_hi, P.c_lo, rho, w, p);
 }
 __device__ __forceinline__ float run_sum(const float* v) {
     float a = (v[0] + v[1]) + (v[2] + v[3]);
@@ -1782,8 +1777,10 @@ __device__ void resample_body(const Params& P, int b, int r, const RowParam& rp,
     const uint8_t* rowT = row_ptr<DT>(P, true, b, rn);
     const uint8_t* rowD = RESID ? row_ptr<DT>(P, false, b, rn) : rowT;
     const bool aligned = ((reinterpret_cast<uintptr_t>(rowT) & 15) == 0) && ((reinterpret_cast<uintptr_t>(rowD) & 15) == 0);
-    const float invT = static_cast<float>(1.0 / rp.keptT);
-    const float invD = RESID ? static_cast<float>(1.0 / rp.keptD) : 0.f;
+    // weights are kept in units of the target's kept mass (see run_weights);
+    // sT scales them to p' units wherever they are widened to float64
+    const float rho = RESID ? static_cast<float>(rp.keptT / rp.keptD) : 0.f;
+    const double sT = 1.0 / rp.keptT;
     const bool interior = static_cast<int64_t>(r + 1) * (R * kThreads * kRun) <= P.V;
     const int nq = P.nq;
     uint64_t* qrec = P.qrec + static_cast<size_t>(b) * nq * kRecWords;
@@ -1798,10 +1795,10 @@ __device__ void resample_body(const Params& P, int b, int r, const RowParam& rp,
 #pragma unroll
         for (int k = 0; k < R; ++k) {
             float p[kRun];
-            item_run<DT, TOPP, RESID, R>(P, rp, invT, invD, raw, r, k, interior, w[k], p);
+            item_run<DT, TOPP, RESID, R>(P, rp, rho, raw, r, k, interior, w[k], p);
             xs[k] = run_sum(w[k]);
-            ws += static_cast<double>(xs[k]);
-            ps += static_cast<double>(run_sum(p));
+            ws += static_cast<double>(xs[k]) * sT;
+            ps += static_cast<double>(run_sum(p)) * sT;
             // one run at a time: interleaving the runs' exponentials would
             // multiply the registers live here
             __builtin_amdgcn_sched_barrier(0);
@@ -1830,7 +1827,7 @@ __device__ void resample_body(const Params& P, int b, int r, const RowParam& rp,
         int lastpos = -1;
 #pragma unroll
         for (int k = 0; k < R; ++k) {
-            const double wik = wave_scan_dpp(static_cast<double>(xs[k]));
+            const double wik = wave_scan_dpp(static_cast<double>(xs[k]) * sT);
             if (lane == 63) s_wt[k][wv] = wik;
             const int64_t id0 = item_run_id0<R>(r, k);
 #pragma unroll
@@ -1944,7 +1941,7 @@ __device__ void resample_body(const Params& P, int b, int r, const RowParam& rp,
 #pragma unroll
         for (int k = 0; k < R; ++k) {
             float wk[kRun];
-            item_run<DT, TOPP, RESID, R>(P, rp, invT, invD, raw, r, k, interior, wk, w[k]);
+            item_run<DT, TOPP, RESID, R>(P, rp, rho, raw, r, k, interior, wk, w[k]);
             xs[k] = run_sum(w[k]);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -1991,7 +1988,7 @@ __device__ void resample_body(const Params& P, int b, int r, const RowParam& rp,
         if (k == hk) {
 #pragma unroll
             for (int i = 0; i < kRun; ++i) v[i] = w[k][i];
-            myx = static_cast<double>(xs[k]);
+            myx = static_cast<double>(xs[k]) * sT;
         }
     // the run's wave scan again (the same additions as for its total)
     const double myw = wave_scan_dpp(myx);
@@ -2006,9 +2003,9 @@ __device__ void resample_body(const Params& P, int b, int r, const RowParam& rp,
         for (int i = 0; i < kRun; ++i) {
             if (v[i] > 0.f) {
                 lastw = static_cast<int>(id0 + i);
-                if (y < 0 && run + static_cast<double>(v[i]) > t) y = lastw;
+                if (y < 0 && run + static_cast<double>(v[i]) * sT > t) y = lastw;
             }
-            run += static_cast<double>(v[i]);
+            run += static_cast<double>(v[i]) * sT;
         }
         *outp = y >= 0 ? y : (lastw >= 0 ? lastw : (lp >= 0 ? lp : 0));
         if (pr) {

@@ -97,6 +97,18 @@ def test_small_vocabularies(dtype, V):
         _parity(inp, label=f"V={V} {dtype}")
 
 
+@pytest.mark.parametrize("top_p", [1.0, 0.8])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("V", [16384, 32768])
+def test_vocabularies_filling_whole_chunks(V, dtype, top_p):
+    """Aligned rows whose 16-byte vector count is a multiple of the
+    statistics chunk (2048 vectors): each row's last chunk is empty, and the
+    row is the last thing in its buffer, so a load past it can leave the
+    allocation."""
+    inp = W.synthetic(3, 2, V, dtype=dtype, temperature=0.7, top_p=top_p, seed=31 + V, gen_seed=V + int(top_p * 10))
+    _parity(inp, label=f"V={V} {dtype} top_p={top_p}")
+
+
 @pytest.mark.parametrize("K", [1, 2, 16])
 def test_draft_lengths(K):
     inp = W.synthetic(9, K, 3001, dtype="bf16", temperature=0.7, sigma=0.3, seed=77 + K, gen_seed=K)

@@ -55,6 +55,12 @@ extern "C" {
 
 #define SPECVERIFY_ABI_VERSION 1
 #define SPECVERIFY_MAX_K 16
+/* Largest vocabulary of the calls that draw a token (spec_verify,
+ * spec_verify_probe, spec_smc_step, spec_hispec_verify): their row pass
+ * splits a logit row over workgroups that wait for one another, so all of a
+ * row's workgroups must fit on the device at once.  Greedy verify and the
+ * draft producer take V up to 2^24. */
+#define SPECVERIFY_MAX_V (1 << 21)
 
 /* Element type of a logits tensor. */
 typedef enum { SV_F32 = 0, SV_BF16 = 1 } sv_dtype;
@@ -100,7 +106,8 @@ enum {
 /*
  * spec_verify -- the verify step (steps 1-4 above) for B rows.
  *
- * target_logits   [B, K+1, V] target logits, bf16 or fp32.
+ * target_logits   [B, K+1, V] target logits, bf16 or fp32;
+ *                 1 <= B <= 2^22, 1 <= V <= SPECVERIFY_MAX_V.
  * draft_logits    [B, K, V] draft logits, same dtype, B and V; 1 <= K <= 16.
  * draft_tokens    device int32 [B, K], contiguous; entry (b, j) is the drafted
  *                 id at position j, read only for j < L_b.

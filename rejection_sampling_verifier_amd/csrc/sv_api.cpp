@@ -192,7 +192,8 @@ int plan(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_tokens, 
     const int B = tl->B, V = tl->V, K = tl->P - 1;
     if (B <= 0 || V <= 0 || K < 1 || K > SPECVERIFY_MAX_K) return SV_ESHAPE;
     if (!greedy && (dl->B != B || dl->V != V || dl->P != K)) return SV_ESHAPE;
-    if (B > (1 << 22) || V > (1 << 24)) return SV_ESHAPE;
+    // the calls that draw a token need a row's items resident together
+    if (B > (1 << 22) || V > (greedy ? (1 << 24) : SPECVERIFY_MAX_V)) return SV_ESHAPE;
     if (!(temperature > 0.f) || !std::isfinite(temperature)) return SV_EINVAL;
     if (!(top_p > 0.f && top_p <= 1.f)) return SV_EINVAL;
     const double c = 1.4426950408889634074 / static_cast<double>(temperature);  // log2(e)/T

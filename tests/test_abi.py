@@ -74,6 +74,7 @@ def _call(lib, B=2, K=3, V=100, dtype=0, T=1.0, top_p=1.0, tP=None, dP=None, tda
     (dict(top_p=0.0), -1), (dict(top_p=1.5), -1), (dict(top_p=float("nan")), -1),
     (dict(tdata=0x1002), -6), (dict(dtype=1, dtype_d=1, tdata=0x1001), -6), (dict(tokens=0x3002), -6),
     (dict(stride=(-2 * 400, 0)), -1),
+    (dict(V=(1 << 21) + 1), -2), (dict(V=(1 << 24) + 1), -2),
 ])
 def test_host_validation(lib, kw, code):
     assert _call(lib, **kw) == code
@@ -92,7 +93,7 @@ def _smc(lib, N=4, K=2, V=64, T=1.0, ess=0.5, tdata=0x1000, ddata=0x2000, tokens
     (dict(lw=0), -1), (dict(bonus=0), -1), (dict(lwo=0), -1), (dict(anc=0), -1), (dict(e=0), -1), (dict(rs=0), -1),
     (dict(tokens=0), -1), (dict(ess=float("nan")), -1), (dict(T=0.0), -1),
     (dict(lw=0x4004), -6), (dict(lwo=0x6004), -6), (dict(e=0x8004), -6), (dict(anc=0x7002), -6),
-    (dict(K=0), -2), (dict(K=17), -2), (dict(N=0), -2), (dict(tP=2), -2),
+    (dict(K=0), -2), (dict(K=17), -2), (dict(N=0), -2), (dict(tP=2), -2), (dict(V=(1 << 21) + 1), -2),
 ])
 def test_smc_host_validation(lib, kw, code):
     assert _smc(lib, **kw) == code
@@ -111,7 +112,7 @@ def _hispec(lib, B=3, K=2, V=64, fP=None, iP=None, T=1.0, fdata=0x1000, idata=0x
 
 @pytest.mark.parametrize("kw,code", [
     (dict(out=0), -1), (dict(outn=0), -1), (dict(tokens=0), -1), (dict(fdata=0), -1), (dict(T=0.0), -1),
-    (dict(fP=3), -2), (dict(iP=2), -2), (dict(K=15 + 1), -2), (dict(dtype_f=1), -3),
+    (dict(fP=3), -2), (dict(iP=2), -2), (dict(K=15 + 1), -2), (dict(dtype_f=1), -3), (dict(V=(1 << 21) + 1), -2),
     (dict(out=0x5002), -6), (dict(outn1=0x7002), -6),
 ])
 def test_hispec_host_validation(lib, kw, code):
@@ -128,6 +129,7 @@ def _greedy(lib, B=3, K=2, V=64, k=5, tdata=0x1000, tokens=0x4000, out=0x5000, o
 @pytest.mark.parametrize("kw,code", [
     (dict(out=0), -1), (dict(outn=0), -1), (dict(tokens=0), -1), (dict(tdata=0), -1), (dict(topk=0), -1),
     (dict(k=-1), -1), (dict(k=65), -1), (dict(K=0), -2), (dict(K=17), -2), (dict(dtype=5), -3),
+    (dict(V=(1 << 24) + 1), -2),
     (dict(out=0x5002), -6), (dict(topk=0x7001), -6),
 ])
 def test_greedy_host_validation(lib, kw, code):

@@ -209,7 +209,22 @@ struct RowShared {
     uint32_t tau[kMaxSlots];
     int32_t cut[kMaxSlots];
     int32_t valid[kMaxSlots];
+    uint32_t wacc[kMaxK + 1];   // Philox word 0 (acceptance) of position j
+    uint32_t wres[kMaxK + 1];   // Philox word 1 (resample) of position j
 };
+
+// The row's Philox words, one lane per position (counter (b, j, stage, 0)),
+// into R; the row pass has one wave compute them while others wait for the
+// statistics, so the decision does not.
+__device__ __forceinline__ void row_uniform_words(const Params& P, int b, RowShared& R) {
+    const int lane = threadIdx.x & 63;
+    if (lane <= P.K) {
+        const uint4 w = philox4x32_10(make_uint4(static_cast<uint32_t>(b), static_cast<uint32_t>(lane), P.stage, 0u),
+                                      P.key0, P.key1);
+        R.wacc[lane] = w.x;
+        R.wres[lane] = w.y;
+    }
+}
 
 // rv index r of a batch row: target position j -> r = j; draft position j ->
 // r = Le + 1 + j.  Slot in the [B, 2K+1] scratch layout: target j -> j,
@@ -410,23 +425,29 @@ __device__ void decide_row(const Params& P, int b, int Le, bool rowok, const Row
     double u_res = 0.0, pt = nan64(), qd = nan64();
     int bad_tok = 0;
     if (!rowbad && lane <= Le) {
-        const uint4 w = philox4x32_10(make_uint4(static_cast<uint32_t>(b), static_cast<uint32_t>(lane), P.stage, 0u),
-                                      P.key0, P.key1);
-        u_res = word_uniform(w.y);
+        u_res = word_uniform(R.wres[lane]);
         if (lane < Le) {
             if (x < 0 || x >= P.V) {
                 bad_tok = 1;
             } else {
                 const int rT = lane, rD = Le + 1 + lane;
                 const float lt = R.lx[rT], ld = R.lx[rD];
-                pt = exp2(static_cast<double>(lt) * P.c64 - static_cast<double>(R.o[rT])) / R.kept[rT];
-                qd = exp2(static_cast<double>(ld) * P.c64 - static_cast<double>(R.o[rD])) / R.kept[rD];
-                if (TOPP) {
-                    if (!is_kept(order_key(lt), x, R.tau[rT], R.cut[rT])) pt = 0.0;
-                    if (!is_kept(order_key(ld), x, R.tau[rD], R.cut[rD])) qd = 0.0;
+                // log2 of the unnormalised masses at x: p'(x) = 2^aT/keptT
+                const double aT = static_cast<double>(lt) * P.c64 - static_cast<double>(R.o[rT]);
+                const double aD = static_cast<double>(ld) * P.c64 - static_cast<double>(R.o[rD]);
+                const bool kT = !TOPP || is_kept(order_key(lt), x, R.tau[rT], R.cut[rT]);
+                const bool kD = !TOPP || is_kept(order_key(ld), x, R.tau[rD], R.cut[rD]);
+                // r = p'(x)/q'(x) = 2^(aT - aD) * keptD/keptT, one exponential;
+                // a token outside a nucleus, or at -inf, has no mass
+                double r;
+                if (!kT || lt == -SV_INF) r = 0.0;
+                else if (!kD || ld == -SV_INF) r = static_cast<double>(SV_INF);
+                else r = exp2(aT - aD) * (R.kept[rD] / R.kept[rT]);
+                rej = !(word_uniform(R.wacc[lane]) < r);
+                if (P.probe_pos) {
+                    pt = (kT && lt != -SV_INF) ? exp2(aT) / R.kept[rT] : 0.0;
+                    qd = (kD && ld != -SV_INF) ? exp2(aD) / R.kept[rD] : 0.0;
                 }
-                const double r = qd > 0.0 ? pt / qd : (pt > 0.0 ? static_cast<double>(SV_INF) : 0.0);
-                rej = !(word_uniform(w.x) < r);
             }
         }
     }
@@ -2045,8 +2066,11 @@ __global__ __launch_bounds__(kThreads) void k_rows(Params P) {
     bool rowok;
     const int Le = row_len(P, b, rowok);
     const int x = lane_token(P, b, Le);
+    // the last wave loads no statistics records for K < 12
+    if ((threadIdx.x >> 6) == kWaves - 1) row_uniform_words(P, b, RS);
     if (TOPP) {
         if ((threadIdx.x >> 6) == 0) fill_row_from_rv(P, b, Le, RS);
+        __syncthreads();
     } else {
         fill_row_from_partials(P, b, Le, RS);
     }

@@ -331,3 +331,15 @@ def test_large_vocabulary(top_p):
     cfg = 4 if top_p < 1.0 else 2
     for step in range(2):
         _parity(W.make_inputs(cfg, 200 + step, B=6, V=262147), label=f"V=262147 top_p={top_p} step {step}")
+
+
+@pytest.mark.parametrize("dtype,top_p", [("bf16", 1.0), ("f32", 1.0), ("bf16", 0.9)])
+def test_largest_accepted_vocabulary(dtype, top_p):
+    """V = 2^21, the largest vocabulary the row pass accepts: a small batch
+    splits each row into 1024 row-pass items of 2048 ids, all of which must
+    be resident together.  (With 2^21 tokens a row's decisions often fall in
+    the flag band; four rows leave some unflagged.)"""
+    V = 1 << 21
+    inp = W.synthetic(4, 2, V, dtype=dtype, temperature=0.7, top_p=top_p, seed=90 + int(top_p * 10),
+                      gen_seed=V + (dtype == "f32"))
+    _parity(inp, label=f"V=2^21 {dtype} top_p={top_p}")

@@ -109,6 +109,20 @@ def test_vocabularies_filling_whole_chunks(V, dtype, top_p):
     _parity(inp, label=f"V={V} {dtype} top_p={top_p}")
 
 
+def test_many_rows_small_vocabulary():
+    """4096 rows of 64 ids: tens of thousands of statistics workgroups, one
+    row-pass item per row (rows sampled for the oracle)."""
+    inp = W.synthetic(4096, 3, 64, dtype="f32", temperature=0.9, seed=4096, gen_seed=4096)
+    _parity(inp, rows=np.arange(0, inp.B, 61), label="B=4096 V=64")
+
+
+def test_large_batch_full_vocabulary():
+    """384 rows of the batched recipe at V = 128256: 6144 row-pass items, six
+    rounds of the resident workgroups (rows sampled for the oracle)."""
+    inp = W.make_inputs(2, 7, B=384)
+    _parity(inp, rows=np.arange(0, inp.B, 24), label="batched recipe B=384")
+
+
 @pytest.mark.parametrize("K", [1, 2, 16])
 def test_draft_lengths(K):
     inp = W.synthetic(9, K, 3001, dtype="bf16", temperature=0.7, sigma=0.3, seed=77 + K, gen_seed=K)

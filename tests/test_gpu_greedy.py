@@ -201,3 +201,12 @@ def test_greedy_large_vocabulary():
     inp = W.make_inputs(2, 14, B=6, V=262147)
     x = _drafts(_f32(inp.target), 14)
     _check(inp.target, x, None, 64, "V=262147 k=64")
+
+
+def test_greedy_largest_vocabulary():
+    """V = 2^24, the largest vocabulary greedy verify accepts: 1024
+    statistics chunks and 4096 wave lists per logit row."""
+    V = 1 << 24
+    inp = W.synthetic(2, 2, V, dtype="bf16", seed=5, gen_seed=V)
+    x = _drafts(_f32(inp.target), 15)
+    _check(inp.target, x, None, 64, "V=2^24 k=64")

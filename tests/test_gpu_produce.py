@@ -146,3 +146,10 @@ def test_two_stream_schedule_matches_standalone_calls():
     x, _, d, t, _, _ = outs[-1]
     rd, rt = oracle.produce_drafts(sets[x].target, K, 1001 + len(outs) - 2)
     assert np.array_equal(_bits(d), rd) and np.array_equal(t.cpu().numpy(), rt)
+
+
+def test_produce_largest_vocabulary_sampled_rows():
+    """V = 2^24, the largest vocabulary the producer accepts (2048 chunk
+    records per row for the token kernel); two rows checked."""
+    inp = W.synthetic(2, 2, 1 << 24, dtype="bf16", seed=3, gen_seed=1 << 24)
+    _check(inp.target, 2, 0x5EED, "V=2^24 bf16", rows=[(0, 0), (1, 1)])

@@ -41,7 +41,11 @@ notes):
 Decision margins: each evaluated acceptance test, each sample and each nucleus
 cut records its distance to the decision boundary.  A row holding a decision
 whose margin is below FLAG_BAND is "flagged": any correct finite-precision
-implementation may legitimately decide it either way.
+implementation may legitimately decide it either way.  Besides the margins the
+result keeps what a caller needs to judge a decision it takes differently:
+the (u, r) pair of every evaluated acceptance test, and, for a draw whose
+margin is below SAMPLE_KEEP_BAND, the draw's running sums divided by Z, so
+that any token can be placed against u.
 """
 
 from dataclasses import dataclass, field
@@ -51,6 +55,8 @@ import numpy as np
 from .philox import uniforms
 
 FLAG_BAND = 1e-6
+# draws this close to a boundary keep their normalised running sums
+SAMPLE_KEEP_BAND = 1e-5
 
 # probe layout per position j (float64):
 #   0 target max logit   1 target sum exp((l-max)/T)
@@ -163,6 +169,8 @@ class RowDecision:
     t: float = np.nan
     u_res: float = np.nan
     margins: list = field(default_factory=list)  # (kind, position, margin)
+    accepts: list = field(default_factory=list)  # (u, r) of each evaluated acceptance test
+    cdf: np.ndarray = None                       # running sums / Z of the draw
 
 
 def decide_row(p, q, x, u_acc, u_res):
@@ -176,10 +184,12 @@ def decide_row(p, q, x, u_acc, u_res):
     """
     L = len(q)
     margins = []
+    accepts = []
     n = L
     for j in range(L):
         r = ratio(p[j][x[j]], q[j][x[j]])
         margins.append(("accept", j, abs(u_acc[j] - r)))
+        accepts.append((float(u_acc[j]), float(r)))
         if not accept(u_acc[j], r):
             n = j
             break
@@ -195,7 +205,9 @@ def decide_row(p, q, x, u_acc, u_res):
         w = np.array(p[L], dtype=np.float64)
     y, z, t, m = inverse_cdf(w, u_res[n])
     margins.append(("sample", n, m))
-    return RowDecision(n=n, tokens=list(x[:n]) + [y], z=z, t=t, u_res=u_res[n], margins=margins)
+    cdf = np.cumsum(np.asarray(w, dtype=np.float64)) / z if m < SAMPLE_KEEP_BAND else None
+    return RowDecision(n=n, tokens=list(x[:n]) + [y], z=z, t=t, u_res=u_res[n], margins=margins,
+                       accepts=accepts, cdf=cdf)
 
 
 @dataclass
@@ -208,6 +220,10 @@ class OracleResult:
     n_decisions: np.ndarray   # [B] decisions taken in the row
     n_flagged: np.ndarray     # [B] decisions with margin below FLAG_BAND
     rows: np.ndarray          # the rows computed
+    margins: dict = field(default_factory=dict)   # b -> [(kind, position, margin)]
+    accepts: dict = field(default_factory=dict)   # b -> [(u, r)] in position order
+    sample_cdf: dict = field(default_factory=dict)  # b -> running sums / Z (near-boundary draws)
+    u_res: np.ndarray = None  # [B, K+1] resampling uniforms of the evaluated positions
 
     @property
     def flagged(self):
@@ -218,7 +234,7 @@ def _row_is_bad(l):
     return bool(np.any(np.isnan(l)) or np.any(l == np.inf) or np.all(l == -np.inf))
 
 
-def verify(target, draft, draft_tokens, draft_len, temperature, top_p, seed, rows=None, stage=0):
+def verify(target, draft, draft_tokens, draft_len, temperature, top_p, seed, rows=None, stage=0, forced=None):
     """The verify step on a batch.
 
     target: [B, K+1, V] logits (float32/float64 values, or uint16 bfloat16
@@ -230,6 +246,11 @@ def verify(target, draft, draft_tokens, draft_len, temperature, top_p, seed, row
     the other rows of the result are left at -1 / NaN.  stage: the third
     Philox counter word (0 for the verify step; a second verification of the
     same rows, as in the hierarchical step, draws from stage 1).
+    forced: optional {row: {position: accept}} that replaces the uniform
+    comparison at those acceptance tests (accept: u taken as 0, which accepts
+    any r > 0; reject: u taken as 1, which no r <= 1 passes).  A caller that
+    sees another implementation decide a near-boundary test the other way
+    uses it to follow that branch; such a test's margin is meaningless.
     """
     tl = _widen(target)
     dl = _widen(draft)
@@ -251,6 +272,8 @@ def verify(target, draft, draft_tokens, draft_len, temperature, top_p, seed, row
     min_margin = np.full(B, np.inf)
     n_dec = np.zeros(B, dtype=np.int64)
     n_flag = np.zeros(B, dtype=np.int64)
+    margins, accepts, sample_cdf = {}, {}, {}
+    u_res_all = np.full((B, K1), np.nan)
 
     for b in rows:
         L = int(lens[b])
@@ -287,6 +310,10 @@ def verify(target, draft, draft_tokens, draft_len, temperature, top_p, seed, row
             probe_pos[b, j, 4] = p[j][x[j]]
             probe_pos[b, j, 5] = q[j][x[j]]
         ua, ur = zip(*(uniforms(seed, b, j, stage) for j in range(L + 1)))
+        if forced and int(b) in forced:
+            ua = list(ua)
+            for j, acc in forced[int(b)].items():
+                ua[j] = 0.0 if acc else 1.0
         d = decide_row(p, q, x, ua, ur)
         n_acc[b] = d.n
         tokens[b, : d.n + 1] = d.tokens
@@ -295,4 +322,10 @@ def verify(target, draft, draft_tokens, draft_len, temperature, top_p, seed, row
         n_dec[b] = len(all_m)
         min_margin[b] = min(m for _, _, m in all_m)
         n_flag[b] = sum(1 for _, _, m in all_m if m < FLAG_BAND)
-    return OracleResult(tokens, n_acc, probe_pos, probe_row, min_margin, n_dec, n_flag, rows)
+        margins[b] = all_m
+        accepts[b] = d.accepts
+        u_res_all[b, : L + 1] = ur
+        if d.cdf is not None:
+            sample_cdf[b] = d.cdf
+    return OracleResult(tokens, n_acc, probe_pos, probe_row, min_margin, n_dec, n_flag, rows,
+                        margins, accepts, sample_cdf, u_res_all)

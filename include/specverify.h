@@ -30,19 +30,45 @@
  * gives the acceptance uniform, word 1 the resampling uniform, each as
  * (word >> 8) * 2^-24.  Any implementation following that contract reproduces
  * the outputs bit for bit, decisions lying within rounding of a boundary
- * aside.
+ * aside.  Precision: the softmax normalisers behind the acceptance tests are
+ * float32 exponentials summed per lane and wave in float32 (relative error
+ * below 1.2e-6 each, so below 2.4e-6 on p'(x)/q'(x)); the draw of step 4 is
+ * float64 throughout (its own normalisers of the two rows at n, float64
+ * exponentials and masses), so its token is the exact inverse-CDF token
+ * unless u*Z lies within about 1e-13*Z of a boundary.
  *
  * Memory: every pointer argument is caller-owned device memory unless stated
  * otherwise.  Inputs are only read; outputs are written in full for every row.
  * The library owns a small scratch buffer per (device, stream), grown on first
  * use and kept until spec_verify_release().  Calls are asynchronous on the
  * given stream and never synchronise the host (except a first call on a
- * stream, or a call that outgrows the cached scratch, which allocates).  A
- * call that does not allocate may be captured into a HIP graph: each kernel
- * of a call rewrites, before any reader needs it, all scratch that later
- * kernels of the same call read, so replays are independent.
- * Concurrent calls on the same stream from several host threads are not
- * supported; calls on different streams may run concurrently.
+ * stream, or a call that outgrows the cached scratch, which allocates).
+ *
+ * Graphs: a call that does not allocate may be captured into a HIP graph:
+ * each kernel of a call rewrites, before any reader needs it, all scratch
+ * that later kernels of the same call read, so replays are independent.  A
+ * call that would have to grow the scratch while its stream is being
+ * captured returns SV_ECAPTURE and enqueues nothing (make one call of the
+ * largest shape on that stream before capturing).  A buffer outgrown later
+ * is kept, not freed, so graphs captured earlier stay valid;
+ * spec_verify_release() frees every buffer and so invalidates every graph
+ * that holds a call of this library.
+ *
+ * Concurrency: concurrent calls on the same stream from several host threads
+ * are not supported.  Calls on different streams may run concurrently, up to
+ * four executing at once (the hardware queues a process gets by default,
+ * GPU_MAX_HW_QUEUES = 4): the row pass splits a logit row over workgroups
+ * that wait for one another, and the library sizes them so that one row's
+ * workgroups take at most a quarter of the device's resident slots for that
+ * kernel, which keeps every wait finite with four calls in flight (a
+ * vocabulary too large for that returns SV_ESHAPE).  Work of other processes
+ * on the same device is outside this guarantee; should a row's workgroups
+ * still give up waiting (after about a second), that row reports
+ * out_n_accepted = -2 and every token -1 (an SMC particle: bonus -2).
+ *
+ * Testing: with the environment variable SPECVERIFY_FAIL_LAUNCH set to a
+ * non-zero value every call fails as a failed kernel launch does (SV_EHIP,
+ * message through spec_verify_strerror) before touching the device.
  */
 #ifndef SPECVERIFY_H
 #define SPECVERIFY_H
@@ -57,9 +83,11 @@ extern "C" {
 #define SPECVERIFY_MAX_K 16
 /* Largest vocabulary of the calls that draw a token (spec_verify,
  * spec_verify_probe, spec_smc_step, spec_hispec_verify): their row pass
- * splits a logit row over workgroups that wait for one another, so all of a
- * row's workgroups must fit on the device at once.  Greedy verify and the
- * draft producer take V up to 2^24. */
+ * splits a logit row over workgroups that wait for one another, so a row's
+ * workgroups must fit in a quarter of the device's resident slots (see
+ * Concurrency above; on MI355X bf16 rows reach 2^21, float32 rows with four
+ * calls in flight somewhat less, beyond which SV_ESHAPE).  Greedy verify and
+ * the draft producer take V up to 2^24. */
 #define SPECVERIFY_MAX_V (1 << 21)
 
 /* Element type of a logits tensor. */
@@ -85,7 +113,8 @@ enum {
     SV_EDTYPE = -3,   /* unknown dtype, or target and draft dtypes differ */
     SV_EHIP = -4,     /* a HIP runtime call failed; see spec_verify_strerror */
     SV_ENOMEM = -5,   /* scratch allocation failed */
-    SV_EALIGN = -6    /* a pointer is not aligned to its element size */
+    SV_EALIGN = -6,   /* a pointer is not aligned to its element size */
+    SV_ECAPTURE = -7  /* the stream is being captured and the scratch would have to grow */
 };
 
 /* Probe record layout (float64), per row b and position j in [0, K]:
@@ -118,11 +147,14 @@ enum {
  * seed            64-bit Philox key.
  * out_tokens      device int32 [B, K+1], contiguous: the n_b accepted drafted
  *                 ids, then the resampled or bonus token, then -1.
- * out_n_accepted  device int32 [B]: n_b in [0, L_b], or -1 for an invalid row.
+ * out_n_accepted  device int32 [B]: n_b in [0, L_b], or -1 for an invalid row
+ *                 (-2: see Concurrency above).
  * stream          hipStream_t to run on (NULL = the default stream).
  *
  * Errors: arguments the host can check return SV_EINVAL / SV_ESHAPE /
- * SV_EDTYPE / SV_EALIGN and launch nothing.  Data errors cannot be reported
+ * SV_EDTYPE / SV_EALIGN and launch nothing (SV_ESHAPE also for a vocabulary
+ * whose rows the row pass cannot keep resident, see Concurrency above);
+ * SV_ECAPTURE as described under Graphs.  Data errors cannot be reported
  * synchronously: a row whose L_b lies outside [0, K], whose drafted id at some
  * j < L_b lies outside [0, V), or one of whose needed logit rows holds a NaN, a
  * +inf or only -inf, gets out_n_accepted = -1 and out_tokens = -1 throughout.

@@ -11,6 +11,7 @@
 #include <map>
 #include <mutex>
 #include <string>
+#include <tuple>
 #include <utility>
 #include <vector>
 
@@ -43,7 +44,7 @@ Layout layout(int64_t B, int nslot, int nch, int nq, bool topp, bool smc) {
     L.rv = off;
     off = align256(off + static_cast<size_t>(B) * nslot * sizeof(sv::RvState));
     L.qrec = off;
-    off = align256(off + static_cast<size_t>(B) * nq * sv::kRecWords * sizeof(uint64_t));
+    off = align256(off + static_cast<size_t>(B) * nq * sv::kQRecWords * sizeof(uint64_t));
     const size_t chunks = topp ? static_cast<size_t>(B) * nslot * nch : 0;
     L.chdr = off;
     off = align256(off + chunks * sv::kWaves * 4 * sizeof(uint64_t));  // four tagged words per wave
@@ -104,6 +105,30 @@ int device_cus() {
     return n;
 }
 
+// Calls that may execute at once on one device: the hardware queues a
+// process gets (HIP's default, GPU_MAX_HW_QUEUES = 4).
+constexpr int kConcurrentCalls = 4;
+
+// Resident row-pass workgroups on the current device for a variant (cached).
+int64_t resident_row_slots(int dtype, bool topp, bool smc, int runs, int cus) {
+    static std::mutex mu;
+    static std::map<std::tuple<int, int, int, int, int>, int> cache;
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    const auto key = std::make_tuple(dev, dtype, topp ? 1 : 0, smc ? 1 : 0, runs);
+    std::lock_guard<std::mutex> lk(mu);
+    auto it = cache.find(key);
+    int per_cu;
+    if (it != cache.end()) {
+        per_cu = it->second;
+    } else {
+        per_cu = sv::rows_blocks_per_cu(dtype, topp, smc, runs);
+        if (per_cu <= 0) per_cu = 1;  // unknown: assume one per CU
+        cache[key] = per_cu;
+    }
+    return static_cast<int64_t>(per_cu) * cus;
+}
+
 int check_logits(const sv_logits* t) {
     if (!t || !t->data) return SV_EINVAL;
     if (t->dtype != SV_F32 && t->dtype != SV_BF16) return SV_EDTYPE;
@@ -112,37 +137,53 @@ int check_logits(const sv_logits* t) {
     return SV_OK;
 }
 
+// Test-only fault injection: with SPECVERIFY_FAIL_LAUNCH set to a non-zero
+// value every call fails where it would first touch the device, as a failed
+// launch does (SV_EHIP and its message), so that the error path can be
+// tested without a GPU.
+bool fail_launch_forced() { return env_int("SPECVERIFY_FAIL_LAUNCH", 0) != 0; }
+
+// Buffers replaced by larger ones.  A HIP graph captured from an earlier
+// call may still use them, so they are freed only by spec_verify_release.
+std::vector<void*> g_retired;
+
 // Returns the scratch for (device, stream), growing it (zeroed) when needed.
+// Growing allocates and synchronises the stream, which a stream being
+// captured into a graph cannot do: then SV_ECAPTURE, and nothing changes.
 int get_scratch(hipStream_t stream, size_t bytes, void** data) {
+    if (fail_launch_forced()) return hip_fail(hipErrorLaunchFailure, "kernel launch (forced by SPECVERIFY_FAIL_LAUNCH)");
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
     std::lock_guard<std::mutex> lk(g_mu);
     Scratch& s = g_scratch[{dev, stream}];
-    const bool grow_data = s.bytes < bytes;
-    if (grow_data && s.ptr) {
+    if (s.bytes >= bytes) {
+        *data = s.ptr;
+        return SV_OK;
+    }
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    e = hipStreamIsCapturing(stream, &cap);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamIsCapturing");
+    if (cap != hipStreamCaptureStatusNone) return SV_ECAPTURE;
+    if (s.ptr) {
         e = hipStreamSynchronize(stream);
         if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
     }
-    if (grow_data) {
-        if (s.ptr) (void)hipFree(s.ptr);
-        s.ptr = nullptr;
-        s.bytes = 0;
-        void* p = nullptr;
-        const size_t want = bytes + bytes / 4;
-        e = hipMalloc(&p, want);
-        if (e != hipSuccess) {
-            (void)hipGetLastError();
-            return SV_ENOMEM;
-        }
-        e = hipMemsetAsync(p, 0, want, stream);
-        if (e != hipSuccess) {
-            (void)hipFree(p);
-            return hip_fail(e, "hipMemsetAsync");
-        }
-        s.ptr = p;
-        s.bytes = want;
+    void* p = nullptr;
+    const size_t want = bytes + bytes / 4;
+    e = hipMalloc(&p, want);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return SV_ENOMEM;
     }
+    e = hipMemsetAsync(p, 0, want, stream);
+    if (e != hipSuccess) {
+        (void)hipFree(p);
+        return hip_fail(e, "hipMemsetAsync");
+    }
+    if (s.ptr) g_retired.push_back(s.ptr);
+    s.ptr = p;
+    s.bytes = want;
     *data = s.ptr;
     return SV_OK;
 }
@@ -154,6 +195,7 @@ int timed_launch(int kind, hipStream_t stream, F&& launch) {
         if (hipEventCreate(&ev.a) != hipSuccess || hipEventCreate(&ev.b) != hipSuccess)
             return hip_fail(hipGetLastError(), "hipEventCreate");
     }
+    if (fail_launch_forced()) return hip_fail(hipErrorLaunchFailure, "kernel launch (forced by SPECVERIFY_FAIL_LAUNCH)");
     const hipError_t e = launch(sv::LaunchEvents{ev.a, ev.b});
     if (e != hipSuccess) return hip_fail(e, "kernel launch");
     if (g_prof) {
@@ -215,17 +257,30 @@ int plan(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_tokens, 
     // row pass: items of runs*kRunIds ids; one-run items when the batch would
     // otherwise give fewer than two workgroups per CU
     int runs = sv::kRunsMax;
-    {
+    if (!greedy) {
+        const int cus = device_cus();
         const int64_t big = static_cast<int64_t>(B) * ((V + runs * sv::kRunIds - 1) / (runs * sv::kRunIds));
-        if (big < 2ll * device_cus()) runs = 1;
+        if (big < 2ll * cus) runs = 1;
         const int forced = env_int("SPECVERIFY_ROW_RUNS", 0);
         if (forced == 1 || forced == 2 || forced == sv::kRunsMax) runs = forced;
+        // The items of a row wait for one another, so a row progresses only
+        // once all of its items are resident.  Each call has at most one
+        // partly resident row at a time (items start in grid order), and at
+        // most kConcurrentCalls calls execute at once; with a row's items
+        // within 1/kConcurrentCalls of the resident slots, some slot is always
+        // free of waiting items and every wait ends.  Larger items if needed.
+        for (;;) {
+            const int64_t nqr = (V + runs * sv::kRunIds - 1) / (runs * sv::kRunIds);
+            if (nqr * kConcurrentCalls <= resident_row_slots(dtype, top_p < 1.f, smc, runs, cus)) break;
+            if (runs == sv::kRunsMax) return SV_ESHAPE;
+            runs = runs == 1 ? 2 : sv::kRunsMax;
+        }
     }
     const int nq = greedy ? 0 : (V + runs * sv::kRunIds - 1) / (runs * sv::kRunIds);
     const int64_t per_row = static_cast<int64_t>(nslot) * nch + nq;
     if (static_cast<int64_t>(B) * per_row >= (1ll << 31)) return SV_ESHAPE;
     // the statistics kernel clears the row pass's records, a few words each
-    if (4ll * nq > static_cast<int64_t>(sv::kThreads) * nslot * nch) return SV_ESHAPE;
+    if (static_cast<int64_t>(sv::kQRecWords) * nq > static_cast<int64_t>(sv::kThreads) * nslot * nch) return SV_ESHAPE;
 
     // greedy verify takes its argmaxes and top-k from the candidate lists
     const bool topp = top_p < 1.f || greedy;
@@ -259,7 +314,11 @@ int plan(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_tokens, 
     if (!(c_lo >= FLT_MIN)) c_lo = FLT_MIN;
     p.c_hi = c_hi;
     p.c_lo = c_lo;
-    p.c64 = static_cast<double>(c_hi) + static_cast<double>(c_lo);
+    p.c64 = c;
+    // relative error bound of keptT/keptD as the statistics (and nucleus)
+    // passes compute them: float32 exponentials and float32 lane and wave
+    // sums, below 1.2e-6 per normaliser (below 2e-6 per kept mass)
+    p.amb_band = top_p < 1.f ? 4e-6 : 2.5e-6;
     p.inv_c = static_cast<float>(1.0 / c);
     p.top_p = top_p;
     p.key0 = static_cast<uint32_t>(seed & 0xFFFFFFFFull);
@@ -531,6 +590,7 @@ const char* spec_verify_strerror(int status) {
         case SV_EHIP: return g_hip_msg.empty() ? "HIP runtime error" : g_hip_msg.c_str();
         case SV_ENOMEM: return "scratch allocation failed";
         case SV_EALIGN: return "pointer not aligned to its element size";
+        case SV_ECAPTURE: return "the stream is being captured and the call would have to grow its scratch";
         default: return "unknown status";
     }
 }
@@ -541,6 +601,8 @@ void spec_verify_release(void) {
         if (kv.second.ptr) (void)hipFree(kv.second.ptr);
     }
     g_scratch.clear();
+    for (void* p : g_retired) (void)hipFree(p);
+    g_retired.clear();
 }
 
 int spec_verify_abi_version(void) { return SPECVERIFY_ABI_VERSION; }

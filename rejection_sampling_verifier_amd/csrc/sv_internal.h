@@ -16,7 +16,8 @@ constexpr int kResTile = 8;          // consecutive ids per thread in the id-ord
 constexpr int kRun = 8;              // ids per thread per run of a resample item
 constexpr int kRunsMax = 4;          // runs per thread per resample item, large batches
 constexpr int kRunIds = kThreads * kRun;  // ids per run of an item (2048)
-constexpr int kRecWords = 4;         // 64-bit words per tagged record
+constexpr int kRecWords = 4;         // 64-bit words per tagged statistics record
+constexpr int kQRecWords = 24;       // 64-bit words per row-pass item record (and the row flag)
 constexpr int kCand = 256;           // nucleus candidates a statistics chunk lists at most
 constexpr int kMaxTopK = 64;         // greedy verify: largest top-k
 constexpr uint32_t kNoCover = 0xFFFFFFFFu;  // candidate header: the chunk's list covers nothing
@@ -80,15 +81,16 @@ struct Params {
     int nq;                       // resample items per batch row (runs*kRunIds ids each)
     int runs;                     // runs per resample item: 1, 2 or kRunsMax
     uint32_t tag;                 // this call's record tag (never 0)
-    float c_hi, c_lo;             // c = log2(e)/T = c_hi + c_lo, c_lo > 0
-    double c64;                   // (double)c_hi + (double)c_lo
+    float c_hi, c_lo;             // c = log2(e)/T = c_hi + c_lo, c_lo > 0 (float32 exponentials)
+    double c64;                   // log2(e)/T in float64 (float64 exponentials and decisions)
+    double amb_band;              // bound on the relative error of keptT/keptD from the earlier passes
     float inv_c;                  // 1/c, rounded (thresholds only)
     float top_p;
     uint32_t key0, key1;          // Philox key
     uint32_t stage;               // Philox counter word 2 of the decision (0; 1 for a second verification)
     uint64_t* prec;               // [B, nslot, nch] tagged statistics records
     RvState* rv;                  // [B, nslot]
-    uint64_t* qrec;               // [B, nq] tagged resample-item mass records
+    uint64_t* qrec;               // [B, nq, kQRecWords] tagged row-pass item records
     // SMC-SD step (smc = 1): B particles, every one with K drafted tokens
     int smc;
     double ess_frac;              // resample when ESS < ess_frac * B
@@ -132,6 +134,9 @@ struct LaunchEvents {
 hipError_t launch_stats(const Params& p, int dtype, int unroll, bool topp, hipStream_t s, const LaunchEvents& ev);
 hipError_t launch_topp(const Params& p, int dtype, hipStream_t s, const LaunchEvents& ev);
 hipError_t launch_rows(const Params& p, int dtype, bool topp, hipStream_t s, const LaunchEvents& ev);
+// Resident workgroups per CU of the row pass (smc: the SMC particle pass)
+// with `runs` runs per item; 0 when unknown.
+int rows_blocks_per_cu(int dtype, bool topp, bool smc, int runs);
 // SMC-SD step: the statistics pass, then the particle pass (log-weight
 // increments and the bonus draw), then the resampling kernel.
 hipError_t launch_smc_rows(const Params& p, int dtype, hipStream_t s, const LaunchEvents& ev);

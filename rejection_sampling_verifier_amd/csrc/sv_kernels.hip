@@ -413,7 +413,7 @@ __device__ __forceinline__ int lane_token(const Params& P, int b, int Le) {
 }
 
 template <bool TOPP>
-__device__ void decide_row(const Params& P, int b, int Le, bool rowok, const RowShared& R, bool outputs, int x,
+__device__ __forceinline__ void decide_row(const Params& P, int b, int Le, bool rowok, const RowShared& R, bool outputs, int x,
                            RowParam& rp) {
     const int lane = threadIdx.x & 63;
     const int K = P.K, K1 = P.K + 1;
@@ -825,7 +825,7 @@ __global__ __launch_bounds__(kThreads, 8) void k_stats(Params P) {
     {
         // clear this call's resample-item records, which the row pass polls
         // (words [item*per, (item+1)*per), per <= kThreads by the host)
-        const int64_t words = static_cast<int64_t>(P.B) * P.nq * kRecWords;
+        const int64_t words = static_cast<int64_t>(P.B) * P.nq * kQRecWords;
         const int64_t grid = static_cast<int64_t>(P.B) * P.nslot * P.nch;
         const int per = static_cast<int>((words + grid - 1) / grid);
         const int64_t e = static_cast<int64_t>(item) * per + threadIdx.x;
@@ -1692,6 +1692,101 @@ template <int DT> __device__ __forceinline__ void unpack_masked(const uint4* v, 
     for (int i = 0; i < kRun; ++i) f[i] = id0 + i < V ? f[i] : -SV_INF;
 }
 
+// ---------------------------------------------------------------------------
+// Float64 exponentials of the draw.  2^x = 2^floor(k/64) * 2^((k mod 64)/64)
+// * 2^r with k = round(64 x) and |r| <= 1/128: the middle factor from a
+// 64-entry table in LDS (each workgroup fills it with the library's float64
+// exp2), 2^r - 1 by its Taylor series in r*ln2 to degree 5 (the remainder is
+// below 4e-17), the power of two by ldexp.  Relative error a few units of
+// 2^-53.  Arguments are clamped to >= -1100, below which 2^x is 0 in float64:
+// a logit of -inf gives 0.
+// ---------------------------------------------------------------------------
+constexpr double kLn2 = 0.693147180559945309417232121458176568;
+constexpr double kTay1 = kLn2;
+constexpr double kTay2 = kTay1 * kLn2 / 2.0;
+constexpr double kTay3 = kTay2 * kLn2 / 3.0;
+constexpr double kTay4 = kTay3 * kLn2 / 4.0;
+constexpr double kTay5 = kTay4 * kLn2 / 5.0;
+// x + 1.5 * 2^46 lies in [2^46, 2^47), where doubles are spaced 2^-6 apart:
+// the sum rounds x to the nearest multiple of 1/64, and its low 32 bits hold
+// that multiple times 64 as a two's-complement integer.
+constexpr double kRound64 = 105553116266496.0;
+constexpr int kExpTab = 64;
+
+__device__ __forceinline__ void exp2_table_fill(double* tab) {
+    if (threadIdx.x < kExpTab) tab[threadIdx.x] = exp2(static_cast<double>(threadIdx.x) * (1.0 / kExpTab));
+}
+__device__ __forceinline__ double exp2_f64(double x, const double* tab) {
+    x = fmax(x, -1100.0);
+    const double kd = x + kRound64;
+    const int k = static_cast<int>(static_cast<uint32_t>(__double_as_longlong(kd)));
+    const double r = x - (kd - kRound64);
+    double p = fma(r, kTay5, kTay4);
+    p = fma(p, r, kTay3);
+    p = fma(p, r, kTay2);
+    p = fma(p, r, kTay1);
+    p *= r;
+    const double t = tab[k & (kExpTab - 1)];
+    return ldexp(fma(t, p, t), k >> 6);
+}
+
+// ---------------------------------------------------------------------------
+// Row pass, the draw (see the section header above k_rows).  Everything that
+// decides the drawn token is float64: per id eT = 2^(lT*c - oT) and eD =
+// 2^(lD*c - oD) (0 outside the id's nucleus), the row's normalisers ST = sum
+// eT and SD = sum eD taken in this pass itself, and the weights in units of
+// eT: w = max(0, eT - rho*eD) with rho = ST/SD on a rejection (the corrected
+// distribution max(0, p' - q') times ST), w = eT for the bonus.
+//
+// rho is only known once every item of the row has published its sums, so
+// an item classifies its ids against rho~ = keptT/keptD of the earlier
+// passes, whose relative error is below P.amb_band: in d = lT - lD, an id
+// has w > 0 iff d > d*, and d~* (from rho~) lies within Delta of d*.  Ids
+// with |d - d~*| > Delta are classified for certain and enter the sums A = sum
+// eT and B = sum eD of the ids with w > 0, so that the item's mass is A -
+// rho*B once rho is known.  Ids within Delta ("ambiguous") are carried
+// exactly: ids with equal d have equal eT/eD, so each group of equal d
+// contributes max(0, GT - rho*GD) from its sums; an item publishes up to
+// kAmbGroups groups.  An item with more (a rare event: the band holds well
+// under one id per row on smooth rows) sends its row into a second round, in
+// which every item recomputes its mass with rho and publishes it again.
+// ---------------------------------------------------------------------------
+constexpr int kAmbGroups = 3;
+// Record of an item (tagged 64-bit words, 32 payload bits each): word 0 the
+// group count (bits 0-7) and the overflow flag (bit 8); then ST, SD, A, B as
+// float64 (two words each); then the groups' GT, GD.  The second round's
+// record (the item's mass W, two words) follows.
+constexpr int kQHdr = 9;
+constexpr int kQRound1 = kQHdr + 4 * kAmbGroups;   // 21
+constexpr int kQRound2 = kQRound1;                 // word offset of the second round
+static_assert(kQRound2 + 2 < kQRecWords, "record layout: the last word is the row flag");
+
+// Loads n record words until all carry `tag` (true), or kPollLimit polls.
+template <int N>
+__device__ __forceinline__ bool poll_words(const uint64_t* rec, uint32_t tag, uint32_t* pay) {
+    for (int it = 0; it < kPollLimit; ++it) {
+        uint64_t w[N];
+#pragma unroll
+        for (int k = 0; k < N; ++k) w[k] = ld_agent(rec + k);
+        bool ok = true;
+#pragma unroll
+        for (int k = 0; k < N; ++k) {
+            ok = ok && has_tag(w[k], tag);
+            pay[k] = static_cast<uint32_t>(w[k]);
+        }
+        if (ok) return true;
+        __builtin_amdgcn_s_sleep(4);
+    }
+    return false;
+}
+__device__ __forceinline__ double f64_of(uint32_t lo, uint32_t hi) {
+    return __longlong_as_double(static_cast<long long>(static_cast<uint64_t>(lo) | (static_cast<uint64_t>(hi) << 32)));
+}
+__device__ __forceinline__ uint32_t f64_word(double v, int half) {
+    const uint64_t b = static_cast<uint64_t>(__double_as_longlong(v));
+    return static_cast<uint32_t>(half ? (b >> 32) : b);
+}
+
 // The nucleus test on the logit itself: key(l) > tau, or key(l) == tau with
 // id <= cut, is l > tv, or l == tv with id <= cut, for tv the logit of key
 // tau (order keys are monotone in the value, -0 and +0 sharing one).  tau = 0
@@ -1700,34 +1795,6 @@ template <int DT> __device__ __forceinline__ void unpack_masked(const uint4* v, 
 __device__ __forceinline__ float kept_bound(uint32_t tau) { return tau == 0u ? -SV_INF : key_value(tau); }
 __device__ __forceinline__ bool kept_l(float l, float tv, int id, int32_t cut) {
     return l > tv || (l == tv && id <= cut);
-}
-
-// Residual weights of a run in units of the target's kept mass: with
-// eT = 2^(lT*c - oT) and eD = 2^(lD*c - oD), p' = eT/keptT and q' =
-// eD/keptD, so max(0, p' - q') = max(0, eT - rho*eD)/keptT for rho =
-// keptT/keptD.  w gets max(0, eT - rho*eD) (eT for the bonus) and p gets eT;
-// the caller scales sums by 1/keptT when it widens them to float64, so no
-// per-id multiply by a kept mass is needed.  With top-p, eT and eD are 0
-// wherever their token is outside its nucleus.
-template <bool TOPP>
-__device__ __forceinline__ void run_weights(const float* lt, const float* ld, bool resid, int64_t id0, const RowParam& rp,
-                                            float c_hi, float c_lo, float rho, float* w, float* p) {
-    const float tvT = TOPP ? kept_bound(rp.tauT) : 0.f;
-    const float tvD = TOPP ? kept_bound(rp.tauD) : 0.f;
-    const int i0 = static_cast<int>(id0);  // ids < 2^24
-#pragma unroll
-    for (int i = 0; i < kRun; ++i) {
-        float eT = tempexp(lt[i], c_hi, c_lo, rp.oT);
-        if (TOPP && !kept_l(lt[i], tvT, i0 + i, rp.cutT)) eT = 0.f;
-        float wi = eT;
-        if (resid) {
-            float eD = tempexp(ld[i], c_hi, c_lo, rp.oD);
-            if (TOPP && !kept_l(ld[i], tvD, i0 + i, rp.cutD)) eD = 0.f;
-            wi = fmaxf(fmaf(-rho, eD, eT), 0.f);
-        }
-        w[i] = wi;
-        p[i] = eT;
-    }
 }
 
 // Raw 16-byte vectors of one item for one thread: R runs of each needed
@@ -1761,153 +1828,493 @@ __device__ __forceinline__ void load_item(const uint8_t* rowT, const uint8_t* ro
         }
     }
 }
-// Weights of run k of item r: w = max(0, p' - q') (or p' for the bonus) and
-// p = p'.  `interior`: the whole item lies inside the row (nothing to mask).
-template <int DT, bool TOPP, bool RESID, int R>
-__device__ __forceinline__ void item_run(const Params& P, const RowParam& rp, float rho,
-                                         const ItemRaw<DT, R>& raw, int r, int k, bool interior, float* w, float* p) {
+
+// What every id of the draw needs, uniform over the row (kept in scalar
+// registers).
+struct DrawParam {
+    double c, oT, oD;          // exponent scale and offsets
+    float tvT, tvD;            // nucleus bounds (top-p)
+    int32_t cutT, cutD;
+    double dstar, delta;       // classification of residual ids (see above)
+    double rho;                // exact ST/SD, known after the exchange
+};
+__device__ __forceinline__ double sgpr_f64(double v) {
+    const long long b = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_readfirstlane(static_cast<int>(b));
+    const int hi = __builtin_amdgcn_readfirstlane(static_cast<int>(b >> 32));
+    return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned int>(lo));
+}
+__device__ __forceinline__ float sgpr_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
+
+// Orders the exponentials of consecutive pairs of ids: the next pair's
+// inputs are tied to this pair's results, so the scheduler cannot start the
+// next pair's table lookups early (each exponential in flight holds half a
+// dozen registers, and 32 of them would cost the occupancy).
+template <bool RESID>
+__device__ __forceinline__ void pair_fence(double& a0, double& a1, double& b0, double& b1, float& n0, float& n1,
+                                           float& m0, float& m1) {
+    if (RESID) asm volatile("" : "+v"(a0), "+v"(a1), "+v"(b0), "+v"(b1), "+v"(n0), "+v"(n1), "+v"(m0), "+v"(m1));
+    else asm volatile("" : "+v"(a0), "+v"(a1), "+v"(n0), "+v"(n1));
+}
+
+// eT (and eD) of one id: 0 outside the id's nucleus (top-p) and at -inf.
+template <bool TOPP, bool RESID>
+__device__ __forceinline__ void id_exps(float lt, float ld, int id, const DrawParam& dp, const double* tab, double& eT,
+                                        double& eD) {
+    eT = exp2_f64(fma(static_cast<double>(lt), dp.c, -dp.oT), tab);
+    if (TOPP && !kept_l(lt, dp.tvT, id, dp.cutT)) eT = 0.0;
+    eD = 0.0;
+    if (RESID) {
+        eD = exp2_f64(fma(static_cast<double>(ld), dp.c, -dp.oD), tab);
+        if (TOPP && !kept_l(ld, dp.tvD, id, dp.cutD)) eD = 0.0;
+    }
+}
+
+template <int DT, int R>
+__device__ __forceinline__ void unpack_item_run(const Params& P, const ItemRaw<DT, R>& raw, int r, int k, bool interior,
+                                                bool resid, float* lt, float* ld) {
     const int64_t id0 = item_run_id0<R>(r, k);
-    float lt[kRun], ld[kRun];
     if (interior) {
         unpack_run<DT>(raw.t[k], lt);
-        if (RESID) unpack_run<DT>(raw.d[k], ld);
+        if (resid) unpack_run<DT>(raw.d[k], ld);
     } else {
         unpack_masked<DT>(raw.t[k], id0, P.V, lt);
-        if (RESID) unpack_masked<DT>(raw.d[k], id0, P.V, ld);
+        if (resid) unpack_masked<DT>(raw.d[k], id0, P.V, ld);
     }
-    run_weights<TOPP>(lt, ld, RESID, id0, rp, P.c_hi, P.c_lo, rho, w, p);
 }
-__device__ __forceinline__ float run_sum(const float* v) {
-    float a = (v[0] + v[1]) + (v[2] + v[3]);
-    float c = (v[4] + v[5]) + (v[6] + v[7]);
-    return a + c;
-}
-static_assert(kRun == 8, "run_sum sums 8 values");
 
-// The resample part of batch row b for item r, given the row's decision (the
-// same in every item of the row) with n = rn and the mode's RESID.  Every
-// thread must call it.
+// Calls f(k, lt, ld, i0) for the runs k = 0..R-1 of item r (lt, ld: the
+// run's logits, i0 its first id), loading run k+1 while run k is processed.
+// The loop stays rolled: one copy of the float64 body keeps the registers of
+// one run live, whatever R.
+template <int DT, int R, bool RD, typename F>
+__device__ __forceinline__ void for_item_runs(const Params& P, const uint8_t* rowT, const uint8_t* rowD, bool aligned,
+                                              int r, bool interior, F&& f) {
+    constexpr int NVR = kRun / Fmt<DT>::VE;
+    uint4 ct[NVR], cd[NVR], nt[NVR], nd[NVR];
+    issue_run<DT>(rowT, item_run_id0<R>(r, 0), P.V, aligned, ct);
+    if (RD) issue_run<DT>(rowD, item_run_id0<R>(r, 0), P.V, aligned, cd);
+#pragma unroll 1
+    for (int k = 0; k < R; ++k) {
+        const int64_t id0 = item_run_id0<R>(r, k);
+        if (k + 1 < R) {
+            issue_run<DT>(rowT, id0 + kRunIds, P.V, aligned, nt);
+            if (RD) issue_run<DT>(rowD, id0 + kRunIds, P.V, aligned, nd);
+        }
+        if (aligned && run_straddles<DT>(id0, P.V)) {
+            load_run_elems<DT>(rowT, id0, P.V, ct);
+            if (RD) load_run_elems<DT>(rowD, id0, P.V, cd);
+        }
+        float lt[kRun], ld[kRun];
+        if (interior) {
+            unpack_run<DT>(ct, lt);
+            if (RD) unpack_run<DT>(cd, ld);
+        } else {
+            unpack_masked<DT>(ct, id0, P.V, lt);
+            if (RD) unpack_masked<DT>(cd, id0, P.V, ld);
+        }
+        f(k, lt, ld, static_cast<int>(id0));  // ids < 2^24
+#pragma unroll
+        for (int q = 0; q < NVR; ++q) {
+            ct[q] = nt[q];
+            if (RD) cd[q] = nd[q];
+        }
+    }
+}
+
+// Per-thread sums of one item's first pass (rho~ classification); the
+// per-run sums A and B of the thread go to LDS (sA[k][tid], sB[k][tid]).
+struct ItemSums {
+    double ST, SD;          // all ids
+    double sT, sD, skey;    // one stashed group of ambiguous ids (equal d, run srun)
+    int srun;
+    bool shas, sover;
+};
+
 template <int DT, bool TOPP, bool RESID, int R>
-__device__ void resample_body(const Params& P, int b, int r, const RowParam& rp, int rn) {
-    __shared__ double s_w[kWaves], s_p[kWaves];
-    __shared__ double s_wt[R][kWaves];
-    __shared__ int s_lastpos[kWaves];
-    __shared__ int s_sel, s_item, s_ok;
-    __shared__ double s_pre, s_Z, s_t;
+__device__ __forceinline__ void item_first_pass(const Params& P, const uint8_t* rowT, const uint8_t* rowD, bool aligned,
+                                                int r, bool interior, const DrawParam& dp, const double* tab,
+                                                double (*sA)[kThreads], double (*sB)[kThreads], ItemSums& s) {
+    s.ST = 0.0;
+    s.SD = 0.0;
+    s.sT = s.sD = s.skey = 0.0;
+    s.srun = -1;
+    s.shas = s.sover = false;
+    const int tid = threadIdx.x;
+    for_item_runs<DT, R, RESID>(P, rowT, rowD, aligned, r, interior, [&](int k, float* lt, float* ld, int i0) {
+        double a = 0.0, bsum = 0.0;
+#pragma unroll
+        for (int i = 0; i < kRun; i += 2) {
+            double eT[2], eD[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                id_exps<TOPP, RESID>(lt[i + h], RESID ? ld[i + h] : 0.f, i0 + i + h, dp, tab, eT[h], eD[h]);
+            if (i + 2 < kRun)
+                pair_fence<RESID>(eT[0], eT[1], eD[0], eD[1], lt[i + 2], lt[i + 3], ld[i + 2], ld[i + 3]);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                s.ST += eT[h];
+                if (RESID) {
+                    s.SD += eD[h];
+                    // w > 0 iff d > d*: certain beyond Delta of d~*; an id
+                    // outside the draft nucleus (eD = 0) keeps eT, one outside
+                    // the target's (eT = 0) has none
+                    const double key = static_cast<double>(lt[i + h]) - static_cast<double>(ld[i + h]);
+                    const double dd = key - dp.dstar;
+                    const bool inT = eT[h] > 0.0;
+                    const bool in = inT && (eD[h] == 0.0 || dd > dp.delta);
+                    const double m = in ? 1.0 : 0.0;
+                    a = fma(m, eT[h], a);
+                    bsum = fma(m, eD[h], bsum);
+                    if (inT && eD[h] > 0.0 && fabs(dd) <= dp.delta) {
+                        if (!s.shas) {
+                            s.shas = true;
+                            s.sT = eT[h];
+                            s.sD = eD[h];
+                            s.skey = key;
+                            s.srun = k;
+                        } else if (s.skey == key && s.srun == k) {
+                            s.sT += eT[h];
+                            s.sD += eD[h];
+                        } else {
+                            s.sover = true;
+                        }
+                    }
+                } else {
+                    a += eT[h];
+                }
+            }
+        }
+        sA[k][tid] = a;
+        sB[k][tid] = bsum;
+    });
+}
+
+// Per-run weight totals of a second, exact pass (rho known; `bonus`: w = eT,
+// the draw from p' when the residual vanished): sA[k][tid] = sum w over run
+// k, sB = 0.
+template <int DT, bool TOPP, bool RESID, int R>
+__device__ __forceinline__ void item_exact_pass(const Params& P, const uint8_t* rowT, const uint8_t* rowD, bool aligned,
+                                                int r, bool interior, const DrawParam& dp, const double* tab,
+                                                bool bonus, double (*sA)[kThreads], double (*sB)[kThreads]) {
+    const int tid = threadIdx.x;
+    auto body = [&](auto resid_c, int k, float* lt, float* ld, int i0) {
+        constexpr bool RS = decltype(resid_c)::value;
+        double a = 0.0;
+#pragma unroll
+        for (int i = 0; i < kRun; i += 2) {
+            double eT[2], eD[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                id_exps<TOPP, RS>(lt[i + h], RS ? ld[i + h] : 0.f, i0 + i + h, dp, tab, eT[h], eD[h]);
+            if (i + 2 < kRun) pair_fence<RS>(eT[0], eT[1], eD[0], eD[1], lt[i + 2], lt[i + 3], ld[i + 2], ld[i + 3]);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) a += RS ? fmax(fma(-dp.rho, eD[h], eT[h]), 0.0) : eT[h];
+        }
+        sA[k][tid] = a;
+        sB[k][tid] = 0.0;
+    };
+    if (RESID && !bonus)
+        for_item_runs<DT, R, true>(P, rowT, rowD, aligned, r, interior, [&](int k, float* lt, float* ld, int i0) {
+            body(std::integral_constant<bool, true>(), k, lt, ld, i0);
+        });
+    else
+        for_item_runs<DT, R, false>(P, rowT, rowD, aligned, r, interior, [&](int k, float* lt, float* ld, int i0) {
+            body(std::integral_constant<bool, false>(), k, lt, ld, i0);
+        });
+}
+
+// One item's record as read back: ST, SD, A, B, its groups, its flags.
+struct ItemRec {
+    double ST, SD, A, B;
+    double gT[kAmbGroups], gD[kAmbGroups];
+    int n, over;
+};
+__device__ __forceinline__ bool read_item_record(const uint64_t* rec, uint32_t tag, ItemRec& q) {
+    uint32_t h[kQHdr];
+    bool ok = poll_words<kQHdr>(rec, tag, h);
+    q.n = min(static_cast<int>(h[0] & 0xFFu), kAmbGroups);
+    q.over = static_cast<int>((h[0] >> 8) & 1u);
+    q.ST = f64_of(h[1], h[2]);
+    q.SD = f64_of(h[3], h[4]);
+    q.A = f64_of(h[5], h[6]);
+    q.B = f64_of(h[7], h[8]);
+#pragma unroll
+    for (int g = 0; g < kAmbGroups; ++g) {
+        q.gT[g] = 0.0;
+        q.gD[g] = 0.0;
+        if (ok && g < q.n) {
+            uint32_t w[4];
+            ok = poll_words<4>(rec + kQHdr + 4 * g, tag, w);
+            q.gT[g] = f64_of(w[0], w[1]);
+            q.gD[g] = f64_of(w[2], w[3]);
+        }
+    }
+    return ok;
+}
+// The item's mass in eT units: A - rho*B plus its groups (the residual),
+// ST for the bonus or the draw from p'.
+__device__ __forceinline__ double item_mass(const ItemRec& q, double rho, bool resid) {
+    if (!resid) return q.ST;
+    double W = fma(-rho, q.B, q.A);
+#pragma unroll
+    for (int g = 0; g < kAmbGroups; ++g)
+        if (g < q.n) W += fmax(fma(-rho, q.gD[g], q.gT[g]), 0.0);
+    return W;
+}
+
+// A row some of whose items stopped polling (a record that never arrived:
+// the row's items were not all resident) is reported with n = -2 and every
+// token -1.  The item that gives up first marks the row in a flag word (the
+// last word of item 0's record, cleared with the records); the writers of
+// the row's ordinary outputs check it, so that an item that only ran after
+// the others gave up does not overwrite the sentinel.
+__device__ __forceinline__ uint64_t* row_flag(const Params& P, int b) {
+    return P.qrec + static_cast<size_t>(b) * P.nq * kQRecWords + (kQRecWords - 1);
+}
+__device__ __forceinline__ void row_timed_out(const Params& P, int b) {
+    const int tid = threadIdx.x;
+    if (tid == 0) st_agent(row_flag(P, b), tagged(P.tag, 1u));
+    if (P.smc) {
+        if (tid == 0) P.out_tokens[b] = -2;
+        return;
+    }
+    if (tid == 0) P.out_n[b] = -2;
+    if (tid < P.K + 1) P.out_tokens[static_cast<size_t>(b) * (P.K + 1) + tid] = -1;
+}
+
+// The draw of batch row b for item r, given the row's decision (the same in
+// every item of the row) with n = rn and the mode's RESID.  Every thread must
+// call it.
+// The draw's LDS (one instance per workgroup, shared by the residual and
+// bonus variants of the kernel).
+template <int R> struct DrawShared {
+    double tab[kExpTab];
+    double red[4][kWaves];
+    double wt[R][kWaves];
+    double A[R][kThreads], B[R][kThreads];  // per (run, thread) sums
+    int item, mode, ok, hk, hw, last;
+    double pre, Z, t, rho, hoff, ST;
+    // ambiguous groups of the item (key, GT, GD), their count and overflow
+    double gkey[kAmbGroups], gT[kAmbGroups], gD[kAmbGroups];
+    int gn, gover;
+};
+
+template <int DT, bool TOPP, bool RESID, int R>
+__device__ __forceinline__ void resample_body(const Params& P, int b, int r, const RowParam& rp, int rn,
+                                              DrawShared<R>* sh_) {
+    DrawShared<R>& sh = *sh_;
+    double* const s_tab = sh.tab;
+    double (*const s_red)[kWaves] = sh.red;
+    double (*const s_wt)[kWaves] = sh.wt;
+    double (*const s_A)[kThreads] = sh.A;
+    double (*const s_B)[kThreads] = sh.B;
+    int &s_item = sh.item, &s_mode = sh.mode, &s_ok = sh.ok, &s_hk = sh.hk, &s_hw = sh.hw, &s_last = sh.last;
+    double &s_pre = sh.pre, &s_Z = sh.Z, &s_t = sh.t, &s_rho = sh.rho, &s_hoff = sh.hoff, &s_ST = sh.ST;
+    double* const s_gkey = sh.gkey;
+    double* const s_gT = sh.gT;
+    double* const s_gD = sh.gD;
+    int &s_gn = sh.gn, &s_gover = sh.gover;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const uint8_t* rowT = row_ptr<DT>(P, true, b, rn);
     const uint8_t* rowD = RESID ? row_ptr<DT>(P, false, b, rn) : rowT;
     const bool aligned = ((reinterpret_cast<uintptr_t>(rowT) & 15) == 0) && ((reinterpret_cast<uintptr_t>(rowD) & 15) == 0);
-    // weights are kept in units of the target's kept mass (see run_weights);
-    // sT scales them to p' units wherever they are widened to float64
-    const float rho = RESID ? static_cast<float>(rp.keptT / rp.keptD) : 0.f;
-    const double sT = 1.0 / rp.keptT;
     const bool interior = static_cast<int64_t>(r + 1) * (R * kThreads * kRun) <= P.V;
     const int nq = P.nq;
-    uint64_t* qrec = P.qrec + static_cast<size_t>(b) * nq * kRecWords;
+    uint64_t* qrec = P.qrec + static_cast<size_t>(b) * nq * kQRecWords;
 
-    // 1. the item's weights (kept in registers) and masses
-    float w[R][kRun];
-    float xs[R];
-    double ws = 0.0, ps = 0.0;
-    {
-        ItemRaw<DT, R> raw;
-        load_item<DT>(rowT, rowD, RESID, aligned, r, P.V, raw);
-#pragma unroll
-        for (int k = 0; k < R; ++k) {
-            float p[kRun];
-            item_run<DT, TOPP, RESID, R>(P, rp, rho, raw, r, k, interior, w[k], p);
-            xs[k] = run_sum(w[k]);
-            ws += static_cast<double>(xs[k]) * sT;
-            ps += static_cast<double>(run_sum(p)) * sT;
-            // one run at a time: interleaving the runs' exponentials would
-            // multiply the registers live here
-            __builtin_amdgcn_sched_barrier(0);
-        }
+    DrawParam dp;
+    dp.c = P.c64;
+    dp.oT = sgpr_f64(static_cast<double>(rp.oT));
+    dp.oD = sgpr_f64(static_cast<double>(rp.oD));
+    dp.tvT = TOPP ? sgpr_f32(kept_bound(rp.tauT)) : 0.f;
+    dp.tvD = TOPP ? sgpr_f32(kept_bound(rp.tauD)) : 0.f;
+    dp.cutT = __builtin_amdgcn_readfirstlane(rp.cutT);
+    dp.cutD = __builtin_amdgcn_readfirstlane(rp.cutD);
+    dp.rho = 0.0;
+    dp.dstar = 0.0;
+    dp.delta = 0.0;
+    const double rtil = sgpr_f64(rp.keptT / rp.keptD);  // rho~
+    if (RESID) {
+        // d~* from rho~: eT > rho~ eD iff (lT - lD) c - oT + oD > log2 rho~;
+        // Delta covers the relative error P.amb_band of rho~ plus the float64
+        // rounding of d and d~*
+        dp.dstar = sgpr_f64((log2(rtil) + dp.oT - dp.oD) / dp.c);
+        dp.delta = sgpr_f64(1.01 * P.amb_band / (dp.c * kLn2) + 1e-12 * (fabs(dp.dstar) + 1.0));
     }
-    ws = wave_sum_dpp(ws);
-    ps = wave_sum_dpp(ps);
-    if (lane == 0) {
-        s_w[wv] = ws;
-        s_p[wv] = ps;
+    exp2_table_fill(s_tab);
+    if (tid == 0) {
+        s_gn = 0;
+        s_gover = 0;
     }
     __syncthreads();
-    const double Wown = (s_w[0] + s_w[1]) + (s_w[2] + s_w[3]);
-    const double Pown = (s_p[0] + s_p[1]) + (s_p[2] + s_p[3]);
-    // 2. publish: words W lo, W hi, Pm lo, Pm hi, each tagged
-    if (tid < kRecWords) {
-        const uint64_t bw = static_cast<uint64_t>(__double_as_longlong(Wown));
-        const uint64_t bp = static_cast<uint64_t>(__double_as_longlong(Pown));
-        const uint64_t v = tid == 0 ? bw : tid == 1 ? (bw >> 32) : tid == 2 ? bp : (bp >> 32);
-        st_agent(qrec + static_cast<size_t>(r) * kRecWords + tid, tagged(P.tag, static_cast<uint32_t>(v)));
-    }
 
-    // the item's per-run wave totals and last positive id, while the other
-    // items' masses arrive (only the item holding t uses them)
-    auto item_scans = [&]() {
-        int lastpos = -1;
+    // 1. the item's float64 sums (one pass over its ids)
+    ItemSums s;
+    item_first_pass<DT, TOPP, RESID, R>(P, rowT, rowD, aligned, r, interior, dp, s_tab, s_A, s_B, s);
+    {
+        double Aall = 0.0, Ball = 0.0;
 #pragma unroll
         for (int k = 0; k < R; ++k) {
-            const double wik = wave_scan_dpp(static_cast<double>(xs[k]) * sT);
-            if (lane == 63) s_wt[k][wv] = wik;
-            const int64_t id0 = item_run_id0<R>(r, k);
-#pragma unroll
-            for (int i = 0; i < kRun; ++i)
-                if (w[k][i] > 0.f) lastpos = static_cast<int>(id0 + i);
+            Aall += s_A[k][tid];
+            Ball += s_B[k][tid];
         }
-        lastpos = wave_max_int_dpp(lastpos);
-        if (lane == 0) s_lastpos[wv] = lastpos;
-    };
-    item_scans();
-
-    // 3. every item's masses in id order (wave 0; lane l takes items
-    // [l*g, (l+1)*g)): Z, t = u*Z and the item holding t
-    if (wv == 0) {
-        const int g = (nq + 63) / 64;
-        const int e0 = min(lane * g, nq), e1 = min(e0 + g, nq);
-        double wsum = 0.0, psum = 0.0;
-        double W1 = 0.0, P1 = 0.0;  // the lane's one item when g == 1
-        bool ok = true;
-        for (int e = e0; e < e1; ++e) {
-            double W = Wown, Pm = Pown;
-            if (e != r) {
-                uint32_t pay[kRecWords];
-                ok = poll_record(qrec + static_cast<size_t>(e) * kRecWords, P.tag, pay) && ok;
-                W = __longlong_as_double(static_cast<long long>(static_cast<uint64_t>(pay[0]) | (static_cast<uint64_t>(pay[1]) << 32)));
-                Pm = __longlong_as_double(static_cast<long long>(static_cast<uint64_t>(pay[2]) | (static_cast<uint64_t>(pay[3]) << 32)));
+        const double v0 = wave_sum_dpp(s.ST), v1 = wave_sum_dpp(s.SD);
+        const double v2 = wave_sum_dpp(Aall), v3 = wave_sum_dpp(Ball);
+        if (lane == 0) {
+            s_red[0][wv] = v0;
+            s_red[1][wv] = v1;
+            s_red[2][wv] = v2;
+            s_red[3][wv] = v3;
+        }
+    }
+    // ambiguous ids (rare): merge the threads' groups, wave by wave
+    if (RESID && __syncthreads_or(s.shas || s.sover)) {
+        for (int w2 = 0; w2 < kWaves; ++w2) {
+            if (wv == w2) {
+                unsigned long long m = __ballot(s.shas);
+                if (__ballot(s.sover) && lane == 0) s_gover = 1;
+                while (m) {
+                    const int l = __ffsll(static_cast<long long>(m)) - 1;
+                    m &= m - 1;
+                    const double key = readlane_f64(s.skey, l), gT = readlane_f64(s.sT, l), gD = readlane_f64(s.sD, l);
+                    if (lane == 0) {
+                        int g = 0;
+                        while (g < s_gn && s_gkey[g] != key) ++g;
+                        if (g < s_gn) {
+                            s_gT[g] += gT;
+                            s_gD[g] += gD;
+                        } else if (s_gn < kAmbGroups) {
+                            s_gkey[g] = key;
+                            s_gT[g] = gT;
+                            s_gD[g] = gD;
+                            s_gn = g + 1;
+                        } else {
+                            s_gover = 1;
+                        }
+                    }
+                }
             }
-            wsum += W;
-            psum += Pm;
-            W1 = W;
-            P1 = Pm;
+            __syncthreads();
         }
+    } else {
+        __syncthreads();
+    }
+    ItemRec own;
+    own.ST = (s_red[0][0] + s_red[0][1]) + (s_red[0][2] + s_red[0][3]);
+    own.SD = (s_red[1][0] + s_red[1][1]) + (s_red[1][2] + s_red[1][3]);
+    own.A = (s_red[2][0] + s_red[2][1]) + (s_red[2][2] + s_red[2][3]);
+    own.B = (s_red[3][0] + s_red[3][1]) + (s_red[3][2] + s_red[3][3]);
+    own.n = s_gn;
+    own.over = s_gover;
+#pragma unroll
+    for (int g = 0; g < kAmbGroups; ++g) {
+        own.gT[g] = g < own.n ? s_gT[g] : 0.0;
+        own.gD[g] = g < own.n ? s_gD[g] : 0.0;
+    }
+
+    // 2. publish: the header, ST, SD, A, B, the groups
+    if (tid < kQHdr + 4 * own.n) {
+        uint32_t v;
+        if (tid == 0) {
+            v = static_cast<uint32_t>(own.n) | (static_cast<uint32_t>(own.over) << 8);
+        } else if (tid < kQHdr) {
+            const int f = (tid - 1) >> 1;
+            const double x = f == 0 ? own.ST : f == 1 ? own.SD : f == 2 ? own.A : own.B;
+            v = f64_word(x, (tid - 1) & 1);
+        } else {
+            const int g = (tid - kQHdr) >> 2, f = ((tid - kQHdr) >> 1) & 1;
+            v = f64_word(f == 0 ? s_gT[g] : s_gD[g], (tid - kQHdr) & 1);
+        }
+        st_agent(qrec + static_cast<size_t>(r) * kQRecWords + tid, tagged(P.tag, v));
+    }
+
+    // 3. every item's record in id order (wave 0; lane l takes items
+    // [l*g, (l+1)*g)): exact rho, the items' masses, Z, t = u*Z and the item
+    // holding t.  Each item sees the same records and makes the same sums.
+    const int gper = (nq + 63) / 64;
+    const int e0 = min(lane * gper, nq), e1 = min(e0 + gper, nq);
+    if (wv == 0) {
+        bool ok = true;
+        double sts = 0.0, sds = 0.0;
+        int over = 0;
+        for (int e = e0; e < e1; ++e) {
+            ItemRec q = own;
+            if (e != r) ok = read_item_record(qrec + static_cast<size_t>(e) * kQRecWords, P.tag, q) && ok;
+            sts += q.ST;
+            sds += q.SD;
+            over |= q.over;
+        }
+        const double ST = lane63(wave_scan_dpp(sts));
+        const double SD = lane63(wave_scan_dpp(sds));
+        const double rho = RESID ? ST / SD : 0.0;
+        // rho~ outside its assumed band of rho would misclassify: redo exactly
+        const bool inband = fabs(rho / rtil - 1.0) <= P.amb_band;
+        const bool rowover = RESID && (!inband || __ballot(over != 0) != 0ull);
+        const bool allok = __ballot(!ok) == 0ull;
+        if (lane == 0) {
+            s_rho = rho;
+            s_ST = ST;
+            s_ok = allok ? 1 : 0;
+            s_mode = rowover ? 2 : 0;
+        }
+    }
+    __syncthreads();
+    if (!s_ok) {
+        row_timed_out(P, b);
+        return;
+    }
+    dp.rho = sgpr_f64(s_rho);
+    const bool round2 = s_mode == 2;
+    // per-run masses of this item's threads (in s_A, s_B): an exact pass
+    // when the row goes to a second round, else from the first pass
+    if (round2) {
+        item_exact_pass<DT, TOPP, RESID, R>(P, rowT, rowD, aligned, r, interior, dp, s_tab, false, s_A, s_B);
+        double w = 0.0;
+#pragma unroll
+        for (int k = 0; k < R; ++k) w += s_A[k][tid];
+        w = wave_sum_dpp(w);
+        if (lane == 0) s_red[0][wv] = w;
+        __syncthreads();
+        const double Wown = (s_red[0][0] + s_red[0][1]) + (s_red[0][2] + s_red[0][3]);
+        if (tid < 2)
+            st_agent(qrec + static_cast<size_t>(r) * kQRecWords + kQRound2 + tid, tagged(P.tag, f64_word(Wown, tid)));
+    }
+    if (wv == 0) {
+        // the masses in id order, Z, t and the holding item
+        bool ok = true;
+        auto mass_of = [&](int e, bool sel) {
+            if (round2 && !sel) {
+                uint32_t pay[2];
+                ok = poll_words<2>(qrec + static_cast<size_t>(e) * kQRecWords + kQRound2, P.tag, pay) && ok;
+                return f64_of(pay[0], pay[1]);
+            }
+            ItemRec q = own;
+            if (e != r) ok = read_item_record(qrec + static_cast<size_t>(e) * kQRecWords, P.tag, q) && ok;
+            return item_mass(q, dp.rho, RESID && !sel);
+        };
+        double wsum = 0.0;
+        for (int e = e0; e < e1; ++e) wsum += mass_of(e, false);
         double incl = wave_scan_dpp(wsum);
         double Z = lane63(incl);
-        int sel = 0;
+        bool sel = false;
         if (!(Z > 0.0)) {
             // A rejection implies p(x) < q(x), hence positive residual mass;
             // none survives only through rounding: draw from p' instead.
-            sel = 1;
-            incl = wave_scan_dpp(psum);
+            sel = true;
+            wsum = 0.0;
+            for (int e = e0; e < e1; ++e) wsum += mass_of(e, true);
+            incl = wave_scan_dpp(wsum);
             Z = lane63(incl);
         }
-        // exclusive prefix: the previous lane's inclusive value
         double pre = dpp_f64<kDppWaveShr1, 0xF>(incl);
         const double t = rp.u * Z;
         int first = 0x7FFFFFFF, lastnz = -1;
         double pf = 0.0, pl = 0.0;
         for (int e = e0; e < e1; ++e) {
-            double m = sel ? Pown : Wown;
-            if (g == 1) {
-                m = sel ? P1 : W1;
-            } else if (e != r) {
-                // several items per lane: the record is in memory now; read
-                // it again rather than keep g values per lane
-                uint32_t pay[kRecWords];
-                poll_record(qrec + static_cast<size_t>(e) * kRecWords, P.tag, pay);
-                const uint64_t lo = pay[sel ? 2 : 0], hi = pay[sel ? 3 : 1];
-                m = __longlong_as_double(static_cast<long long>(lo | (hi << 32)));
-            }
+            const double m = gper == 1 ? wsum : mass_of(e, sel);
             if (m > 0.0) {
                 if (first == 0x7FFFFFFF && pre + m > t) {
                     first = e;
@@ -1921,123 +2328,152 @@ __device__ void resample_body(const Params& P, int b, int r, const RowParam& rp,
         const int fe = wave_min_int_dpp(first);
         const int le = wave_max_int_dpp(lastnz);
         double spre = 0.0;
-        int item = 0;
+        int item = 0, last = 0;
         if (fe != 0x7FFFFFFF) {
             item = fe;
-            spre = readlane_f64(pf, fe / g);
+            spre = readlane_f64(pf, fe / gper);
         } else if (le >= 0) {
             item = le;
-            spre = readlane_f64(pl, le / g);
+            spre = readlane_f64(pl, le / gper);
+            last = 1;
         }
         const bool allok = __ballot(!ok) == 0ull;
         if (lane == 0) {
-            s_sel = sel;
             s_item = item;
             s_pre = spre;
             s_Z = Z;
             s_t = t;
+            s_last = last;
             s_ok = allok ? 1 : 0;
+            if (sel) s_mode = 1;
         }
     }
     __syncthreads();
     if (!s_ok) {
-        // a record never arrived: the row is reported invalid
-        if (P.smc) {
-            if (tid == 0) P.out_tokens[b] = -1;
-        } else {
-            if (tid == 0) P.out_n[b] = -1;
-            if (tid < P.K + 1) P.out_tokens[static_cast<size_t>(b) * (P.K + 1) + tid] = -1;
-        }
+        row_timed_out(P, b);
         return;
     }
     if (s_item != r) return;
 
     // 4. this item holds t.  Id order is run-major, then thread, then id.
-    // Drawing from p' (sel) is the rare rounding fallback: its weights
-    // replace w.
+    const bool sel = s_mode == 1;
+    if (sel) item_exact_pass<DT, TOPP, RESID, R>(P, rowT, rowD, aligned, r, interior, dp, s_tab, true, s_A, s_B);
     const double t = s_t;
-    if (s_sel) {
-        ItemRaw<DT, R> raw;
-        load_item<DT>(rowT, rowD, RESID, aligned, r, P.V, raw);
+    // the mass of this thread's run k (the stash, with the first pass's
+    // sums: its ambiguous ids, now with the exact rho)
+    auto run_mass = [&](int k) {
+        if (!RESID || sel || round2) return s_A[k][tid];
+        double w = fma(-dp.rho, s_B[k][tid], s_A[k][tid]);
+        if (s.shas && s.srun == k) w += fmax(fma(-dp.rho, s.sD, s.sT), 0.0);
+        return w;
+    };
 #pragma unroll
-        for (int k = 0; k < R; ++k) {
-            float wk[kRun];
-            item_run<DT, TOPP, RESID, R>(P, rp, rho, raw, r, k, interior, wk, w[k]);
-            xs[k] = run_sum(w[k]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        item_scans();
-        __syncthreads();
+    for (int k = 0; k < R; ++k) {
+        const double wik = wave_scan_dpp(run_mass(k));
+        if (lane == 63) s_wt[k][wv] = wik;
     }
-    // the (run, wave) holding t, from the 16 totals in id order
-    double base = s_pre, hoff = 0.0;
-    int hk = -1, hw = -1, lp = -1;
-#pragma unroll
-    for (int k = 0; k < R; ++k)
-#pragma unroll
-        for (int w2 = 0; w2 < kWaves; ++w2) {
-            const double tot = s_wt[k][w2];
-            if (hk < 0 && tot > 0.0 && base + tot > t) {
-                hk = k;
-                hw = w2;
-                hoff = base;
+    __syncthreads();
+    if (tid == 0) {
+        // the (run, wave) holding t, from the R*4 totals in id order; past
+        // the item's total (rounding, or t beyond every item: s_last), the
+        // last (run, wave) with mass
+        double base = s_pre;
+        int hk = -1, hw = -1, lk = -1, lw = -1;
+        double hoff = 0.0, loff = 0.0;
+        for (int k = 0; k < R; ++k)
+            for (int w2 = 0; w2 < kWaves; ++w2) {
+                const double tot = s_wt[k][w2];
+                if (tot > 0.0) {
+                    if (hk < 0 && !s_last && base + tot > t) {
+                        hk = k;
+                        hw = w2;
+                        hoff = base;
+                    }
+                    lk = k;
+                    lw = w2;
+                    loff = base;
+                }
+                base += tot;
             }
-            base += tot;
+        if (hk < 0) {
+            hk = lk;
+            hw = lw;
+            hoff = loff;
+            s_last = 1;
         }
-#pragma unroll
-    for (int w2 = 0; w2 < kWaves; ++w2) lp = max(lp, s_lastpos[w2]);
+        s_hk = hk;
+        s_hw = hw;
+        s_hoff = hoff;
+    }
+    __syncthreads();
+    const int hk = s_hk, hw = s_hw;
     double* pr = P.probe_row ? P.probe_row + static_cast<size_t>(b) * 4 : nullptr;
     // the verify step's token at position n, or an SMC particle's bonus
     int32_t* outp = P.smc ? P.out_tokens + b : P.out_tokens + static_cast<size_t>(b) * (P.K + 1) + rn;
     if (hk < 0) {
-        // rounding put t past the item's last positive weight
-        if (tid == 0) {
-            *outp = lp >= 0 ? lp : 0;
-            if (pr) {
-                pr[0] = s_Z;
-                pr[1] = t;
-            }
-        }
+        // no id of the item has mass (cannot happen for the holding item)
+        if (tid == 0) *outp = static_cast<int>(item_run_id0<R>(r, 0));
         return;
     }
     if (wv != hw) return;
-    // wave hw: the first lane of run hk whose inclusive prefix passes t
-    float v[kRun];
-    double myx = 0.0;
-#pragma unroll
-    for (int k = 0; k < R; ++k)
-        if (k == hk) {
-#pragma unroll
-            for (int i = 0; i < kRun; ++i) v[i] = w[k][i];
-            myx = static_cast<double>(xs[k]) * sT;
-        }
-    // the run's wave scan again (the same additions as for its total)
-    const double myw = wave_scan_dpp(myx);
-    const double incl = hoff + myw;
-    const unsigned long long hm = __ballot(myx > 0.0 && incl > t);
-    const int hl = hm ? __ffsll(static_cast<long long>(hm)) - 1 : 63;
+    // wave hw: the first lane of run hk whose inclusive prefix passes t (or
+    // the last lane with mass)
+    const double myx = run_mass(hk);
+    const double incl = s_hoff + wave_scan_dpp(myx);
+    bool last = s_last != 0;
+    unsigned long long hm = __ballot(myx > 0.0 && (last || incl > t));
+    if (hm == 0ull) {
+        // rounding: the wave's total passed t, no lane's prefix does
+        last = true;
+        hm = __ballot(myx > 0.0);
+    }
+    const int hl = last ? 63 - __clzll(static_cast<long long>(hm)) : __ffsll(static_cast<long long>(hm)) - 1;
     if (lane == hl) {
-        double run = incl - myx;  // exclusive prefix of this thread's run
+        // a row some item gave up on keeps its sentinel
+        const bool dead = has_tag(ld_agent(row_flag(P, b)), P.tag);
+        // this thread's run hk: its ids' weights again, exactly as summed
         const int64_t id0 = item_run_id0<R>(r, hk);
+        const bool resid = RESID && !sel;
+        uint4 vt[ItemRaw<DT, 1>::NVR], vd[ItemRaw<DT, 1>::NVR];
+        issue_run<DT>(rowT, id0, P.V, aligned, vt);
+        if (resid) issue_run<DT>(rowD, id0, P.V, aligned, vd);
+        if (aligned && run_straddles<DT>(id0, P.V)) {
+            load_run_elems<DT>(rowT, id0, P.V, vt);
+            if (resid) load_run_elems<DT>(rowD, id0, P.V, vd);
+        }
+        float lt[kRun], ld[kRun];
+        unpack_masked<DT>(vt, id0, P.V, lt);
+        if (resid) unpack_masked<DT>(vd, id0, P.V, ld);
+        double run = incl - myx;  // exclusive prefix of this thread's run
         int y = -1, lastw = -1;
 #pragma unroll
         for (int i = 0; i < kRun; ++i) {
-            if (v[i] > 0.f) {
-                lastw = static_cast<int>(id0 + i);
-                if (y < 0 && run + static_cast<double>(v[i]) * sT > t) y = lastw;
+            double eT, eD, wi;
+            if (resid) {
+                id_exps<TOPP, true>(lt[i], ld[i], static_cast<int>(id0) + i, dp, s_tab, eT, eD);
+                wi = fmax(fma(-dp.rho, eD, eT), 0.0);
+            } else {
+                id_exps<TOPP, false>(lt[i], 0.f, static_cast<int>(id0) + i, dp, s_tab, eT, eD);
+                wi = eT;
             }
-            run += static_cast<double>(v[i]) * sT;
+            if (wi > 0.0) {
+                lastw = static_cast<int>(id0 + i);
+                if (y < 0 && !last && run + wi > t) y = lastw;
+            }
+            run += wi;
         }
-        *outp = y >= 0 ? y : (lastw >= 0 ? lastw : (lp >= 0 ? lp : 0));
-        if (pr) {
-            pr[0] = s_Z;
-            pr[1] = t;
+        if (!dead) *outp = y >= 0 ? y : (lastw >= 0 ? lastw : static_cast<int>(id0));
+        if (pr && !dead) {
+            // Z and t in units of p' (the target's kept mass ST)
+            pr[0] = s_Z / s_ST;
+            pr[1] = t / s_ST;
         }
     }
 }
 
 template <int DT, bool TOPP, int R>
 __device__ __forceinline__ void resample_item(const Params& P, int b, int r, const RowParam& rp) {
+    __shared__ DrawShared<R> sh;
     // the row's mode and n are the same for every lane: keep them scalar
     const int mode = __builtin_amdgcn_readfirstlane(rp.mode);
     const int rn = __builtin_amdgcn_readfirstlane(rp.n);
@@ -2049,8 +2485,8 @@ __device__ __forceinline__ void resample_item(const Params& P, int b, int r, con
         }
         return;
     }
-    if (mode == MODE_RESID) resample_body<DT, TOPP, true, R>(P, b, r, rp, rn);
-    else resample_body<DT, TOPP, false, R>(P, b, r, rp, rn);
+    if (mode == MODE_RESID) resample_body<DT, TOPP, true, R>(P, b, r, rp, rn, &sh);
+    else resample_body<DT, TOPP, false, R>(P, b, r, rp, rn, &sh);
 }
 
 // Row pass: one workgroup per (b, item).  Every item makes the row's decision
@@ -2092,13 +2528,11 @@ __global__ __launch_bounds__(kThreads) void k_rows(Params P) {
 // below ess_frac * B the particles are resampled systematically.
 // ---------------------------------------------------------------------------
 
-constexpr double kLn2 = 0.693147180559945309417232121458176568;
-
 // The particle's validity, log-weight increment and bonus parameters, by
 // ONE wave from the statistics in R (lane j < K takes position j).  With
 // `outputs` lane 0 writes the new log-weight (-inf for an invalid particle,
 // whose bonus is -1).
-__device__ void smc_particle(const Params& P, int b, const RowShared& R, bool outputs, int x, RowParam& rp) {
+__device__ __forceinline__ void smc_particle(const Params& P, int b, const RowShared& R, bool outputs, int x, RowParam& rp) {
     const int lane = threadIdx.x & 63;
     const int K = P.K;
     int bad = 0;
@@ -2799,6 +3233,30 @@ hipError_t launch_greedy_rows(const Params& p, int dtype, hipStream_t s, const L
 hipError_t launch_smc_resample(const Params& p, hipStream_t s, const LaunchEvents& ev) {
     launch(k_smc_resample, 1u, kThreads, s, ev, p);
     return hipGetLastError();
+}
+
+// Resident workgroups per CU of the row pass (or the SMC particle pass) for
+// a dtype, top-p flag and run count; 0 if the runtime cannot tell.
+template <int R>
+static int rows_blocks_r(int dtype, bool topp, bool smc) {
+    int n = 0;
+    hipError_t e;
+    if (smc) {
+        e = dtype == DT_BF16 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_smc_rows<DT_BF16, R>, kThreads, 0)
+                             : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_smc_rows<DT_F32, R>, kThreads, 0);
+    } else if (dtype == DT_BF16) {
+        e = topp ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_rows<DT_BF16, true, R>, kThreads, 0)
+                 : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_rows<DT_BF16, false, R>, kThreads, 0);
+    } else {
+        e = topp ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_rows<DT_F32, true, R>, kThreads, 0)
+                 : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_rows<DT_F32, false, R>, kThreads, 0);
+    }
+    return e == hipSuccess ? n : 0;
+}
+int rows_blocks_per_cu(int dtype, bool topp, bool smc, int runs) {
+    if (runs == 1) return rows_blocks_r<1>(dtype, topp, smc);
+    if (runs == 2) return rows_blocks_r<2>(dtype, topp, smc);
+    return rows_blocks_r<kRunsMax>(dtype, topp, smc);
 }
 
 hipError_t launch_rows(const Params& p, int dtype, bool topp, hipStream_t s, const LaunchEvents& ev) {

@@ -1,7 +1,39 @@
 """Shared helpers of the GPU tests: move seeded inputs to the device, run the
-library through its binding, run the oracle on the same inputs, compare."""
+library through its binding, run the oracle on the same inputs, compare
+decision by decision.
 
+The bar (the exactness claim of the page "Speculative Decoding للمحترف: ضاعف
+سرعة Llama 70B لـ 2.4x بدون فقد token واحد", section "التعريف الرياضي من
+Leviathan et al.", turned into a finite-precision check): accepted counts and
+emitted tokens equal the oracle's except at decisions that lie within the
+library's own rounding bound of their boundary ("flagged").  Each decision
+kind has its band, the rigorous error bound of the kernel arithmetic that
+takes it (the derivations are in the design notes):
+
+  accept   |u - r| < BAND_ACCEPT.  r comes from the statistics pass's
+           normalisers, float32 exponentials summed in float32 per lane and
+           per wave: relative error below 1.2e-6 each, so below 2.4e-6 on r;
+           with top-p the kept masses (below 1.6e-6 each) replace them.
+  sample   |C - t|/Z < BAND_SAMPLE (plus float64 rounding relative to the
+           row's Z) at the token's interval: the draw is float64 throughout.
+  nucleus  the running mass at the cut within BAND_NUCLEUS of top_p: float32
+           exponentials of the kept tokens against top_p times the float32
+           normaliser.
+
+What is checked at a flagged decision instead of equality:
+  * an acceptance test decided the other way: everything before it matches,
+    and the rest of the row must match the oracle's run forced down the
+    library's branch;
+  * a draw: the library's token has positive weight and its running-sum
+    interval lies within the band of u (a valid neighbour of the oracle's);
+  * a nucleus cut: the distribution itself may differ, so from that position
+    on only the output's structure is checked (drafted ids, then one token
+    in [0, V), then -1).
+"""
+
+import math
 import sys
+from dataclasses import dataclass, field
 
 import numpy as np
 import torch
@@ -10,6 +42,16 @@ import oracle
 from rejection_sampling_verifier_amd import binding
 
 PROBE_RTOL = 1e-5  # probabilities and residual masses (spec tolerance)
+
+BAND_ACCEPT = 2.5e-6
+BAND_ACCEPT_TOPP = 3.5e-6
+BAND_SAMPLE = 1e-10
+# float64 rounding of Z = A - rho*B and of the exponentials, relative to Z
+# (in units of the target's kept mass): added to BAND_SAMPLE per row
+SAMPLE_REL_EPS = 2e-13
+BAND_NUCLEUS = 3e-6
+BANDS = {"accept": BAND_ACCEPT, "sample": BAND_SAMPLE, "nucleus_t": BAND_NUCLEUS, "nucleus_d": BAND_NUCLEUS,
+         "degenerate": math.inf}
 
 
 def dev_array(a, device="cuda"):
@@ -33,9 +75,9 @@ def run_gpu(inp, probe=True, tensors=None):
     return [o.cpu().numpy() for o in out]
 
 
-def run_oracle(inp, rows=None):
+def run_oracle(inp, rows=None, forced=None):
     return oracle.verify(inp.target, inp.draft, inp.draft_tokens, inp.draft_len, inp.temperature, inp.top_p,
-                         inp.seed, rows=rows)
+                         inp.seed, rows=rows, forced=forced)
 
 
 def say(*a):
@@ -43,32 +85,158 @@ def say(*a):
     sys.stdout.flush()
 
 
-def check_parity(inp, res, gpu, rows=None, check_probes=True):
-    """Element-by-element comparison on the rows the oracle computed.
+def sample_band(res, b):
+    """The draw's band for row b: BAND_SAMPLE plus the float64 rounding of
+    the library's mass arithmetic relative to this row's Z (Z is in units of
+    the target mass, 1 for a bonus draw)."""
+    z = res.probe_row[b, 0]
+    return BAND_SAMPLE + (SAMPLE_REL_EPS / z if z > 0 else math.inf)
 
-    Tokens and accepted counts must be identical on every row without a
-    flagged decision.  Probe values (max logit, softmax normalisers, p'(x_j),
-    q'(x_j), kept masses, Z, t) must agree to PROBE_RTOL relative.
-    Returns (rows compared, rows flagged, decisions, flagged decisions)."""
+
+def accept_band(inp):
+    return BAND_ACCEPT_TOPP if float(inp.top_p) < 1.0 else BAND_ACCEPT
+
+
+def band_of(kind, res, b, inp):
+    if kind == "sample":
+        return sample_band(res, b)
+    if kind == "accept":
+        return accept_band(inp)
+    if kind.startswith("nucleus"):
+        return BAND_NUCLEUS
+    return BANDS[kind]
+
+
+@dataclass
+class ParityStats:
+    rows: int = 0                 # rows compared
+    decisions: int = 0            # oracle decisions on those rows
+    flagged: dict = field(default_factory=dict)  # kind -> decisions within their band
+    branch_switches: int = 0      # flagged acceptance tests the library took the other way
+    neighbour_draws: int = 0      # flagged draws where the library drew a valid neighbour
+    structural_rows: int = 0      # rows past a flagged nucleus cut (structure checked only)
+    exact_rows: int = 0           # rows equal to the oracle's outputs bit for bit
+
+    @property
+    def n_flagged(self):
+        return sum(self.flagged.values())
+
+    @property
+    def flagged_fraction(self):
+        return self.n_flagged / max(1, self.decisions)
+
+    def add(self, o):
+        self.rows += o.rows
+        self.decisions += o.decisions
+        for k, v in o.flagged.items():
+            self.flagged[k] = self.flagged.get(k, 0) + v
+        self.branch_switches += o.branch_switches
+        self.neighbour_draws += o.neighbour_draws
+        self.structural_rows += o.structural_rows
+        self.exact_rows += o.exact_rows
+        return self
+
+    def __str__(self):
+        kinds = " ".join(f"{k}={v}" for k, v in sorted(self.flagged.items()))
+        return (f"rows={self.rows} exact={self.exact_rows} decisions={self.decisions} flagged={self.n_flagged} "
+                f"({self.flagged_fraction:.2e}) [{kinds}] switches={self.branch_switches} "
+                f"neighbours={self.neighbour_draws} structural={self.structural_rows}")
+
+
+def _structure_ok(inp, b, n, toks):
+    L = int(inp.lengths()[b])
+    K1 = inp.K + 1
+    assert 0 <= n <= L, (b, n, L)
+    assert list(toks[:n]) == list(inp.draft_tokens[b, :n]), (b, toks, inp.draft_tokens[b])
+    assert 0 <= toks[n] < inp.V, (b, toks)
+    assert np.all(toks[n + 1:K1] == -1), (b, toks)
+
+
+def _check_draw(inp, res, b, g_tok, stats):
+    """The draw at the row's n: equal to the oracle's token outside the band;
+    inside it, a positive-weight token whose interval lies within the band."""
+    m = [mg for k, _, mg in res.margins[b] if k == "sample"][0]
+    band = sample_band(res, b)
+    o_tok = int(res.tokens[b, res.n_accepted[b]])
+    if m >= band:
+        assert g_tok == o_tok, (b, g_tok, o_tok, m)
+        return
+    if g_tok == o_tok:
+        return
+    cdf = res.sample_cdf.get(b)
+    assert cdf is not None, (b, m)
+    u = res.probe_row[b, 2]
+    lo = cdf[g_tok - 1] if g_tok > 0 else 0.0
+    hi = cdf[g_tok]
+    assert hi > lo, (b, g_tok, "zero weight")
+    assert lo <= u + band and hi >= u - band, (b, g_tok, o_tok, lo, hi, u, band)
+    stats.neighbour_draws += 1
+
+
+def _check_row(inp, res, b, n_g, toks, stats, depth=0):
+    """Compares row b of the library's output with the oracle's result `res`
+    (decision by decision); returns True when they are equal bit for bit."""
+    n_o = int(res.n_accepted[b])
+    if n_o < 0:
+        assert n_g == n_o and np.all(toks == -1), (b, n_g, toks)
+        return True
+    L = int(inp.lengths()[b])
+    margins = res.margins[b]
+    # a flagged nucleus cut at a position the row's decisions use: the
+    # distribution there is not pinned; structure from that position on
+    cut_flag = sorted(j for k, j, mg in margins if k.startswith("nucleus") and mg < BAND_NUCLEUS)
+    first_cut = cut_flag[0] if cut_flag else L + 1
+    accepts = res.accepts[b]
+    j0 = min(n_g, n_o)
+    if first_cut <= j0:
+        stats.structural_rows += 1
+        _structure_ok(inp, b, n_g, toks)
+        return False
+    if n_g != n_o:
+        # the test at j0 went the other way: it must lie within its band
+        u, r = accepts[j0]
+        assert abs(u - r) < accept_band(inp) and depth == 0, (b, n_g, n_o, u, r)
+        stats.branch_switches += 1
+        alt = run_oracle(inp, rows=[b], forced={int(b): {j0: n_g > j0}})
+        _check_row(inp, alt, b, n_g, toks, stats, depth + 1)
+        return False
+    assert list(toks[:n_g]) == list(res.tokens[b, :n_g]), (b, toks, res.tokens[b])
+    assert np.all(toks[n_g + 1:] == -1), (b, toks)
+    if first_cut <= n_g:
+        stats.structural_rows += 1
+        _structure_ok(inp, b, n_g, toks)
+        return False
+    if any(k == "degenerate" for k, _, _ in margins):
+        _structure_ok(inp, b, n_g, toks)
+        return False
+    _check_draw(inp, res, b, int(toks[n_g]), stats)
+    return bool(toks[n_g] == res.tokens[b, n_g])
+
+
+def check_parity(inp, res, gpu, rows=None, check_probes=True):
+    """Decision-by-decision comparison on the rows the oracle computed (see
+    the module docstring).  Probe values (max logit, softmax normalisers,
+    p'(x_j), q'(x_j), kept masses, and Z, t, u where the row's n agrees)
+    must agree to PROBE_RTOL relative.  Returns ParityStats."""
     tokens, n_acc = gpu[0], gpu[1]
     rows = res.rows if rows is None else rows
-    checked = flagged = 0
+    st = ParityStats()
     for b in rows:
-        if res.flagged[b]:
-            flagged += 1
-            continue
-        checked += 1
-        assert n_acc[b] == res.n_accepted[b], (b, int(n_acc[b]), int(res.n_accepted[b]))
-        np.testing.assert_array_equal(tokens[b], res.tokens[b], err_msg=f"row {b}")
+        st.rows += 1
+        ms = res.margins.get(b, [])
+        st.decisions += len(ms)
+        for k, _, mg in ms:
+            if mg < band_of(k, res, b, inp):
+                st.flagged[k] = st.flagged.get(k, 0) + 1
+        exact = _check_row(inp, res, b, int(n_acc[b]), tokens[b], st)
+        st.exact_rows += int(exact)
         if check_probes and len(gpu) > 2 and res.n_accepted[b] >= 0:
             pp, pr = gpu[2], gpu[3]
             ok = ~np.isnan(res.probe_pos[b])
             np.testing.assert_array_equal(np.isnan(pp[b]), ~ok, err_msg=f"probe NaN pattern, row {b}")
             np.testing.assert_allclose(pp[b][ok], res.probe_pos[b][ok], rtol=PROBE_RTOL, atol=0,
                                        err_msg=f"probe_pos row {b}")
-            np.testing.assert_allclose(pr[b][:3], res.probe_row[b][:3], rtol=PROBE_RTOL, atol=0,
-                                       err_msg=f"probe_row row {b}")
-            assert pr[b][3] == res.n_accepted[b]
-    dec = int(np.sum(res.n_decisions[rows]))
-    fdec = int(np.sum(res.n_flagged[rows]))
-    return checked, flagged, dec, fdec
+            if int(n_acc[b]) == int(res.n_accepted[b]) and pr[b][3] == res.n_accepted[b]:
+                np.testing.assert_allclose(pr[b][:3], res.probe_row[b][:3], rtol=PROBE_RTOL, atol=0,
+                                           err_msg=f"probe_row row {b}")
+    return st

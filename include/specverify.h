@@ -114,7 +114,8 @@ enum {
     SV_EHIP = -4,     /* a HIP runtime call failed; see spec_verify_strerror */
     SV_ENOMEM = -5,   /* scratch allocation failed */
     SV_EALIGN = -6,   /* a pointer is not aligned to its element size */
-    SV_ECAPTURE = -7  /* the stream is being captured and the scratch would have to grow */
+    SV_ECAPTURE = -7, /* the stream is being captured and the scratch would have to grow */
+    SV_ETOOBIG = -8   /* spec_verify_noalloc: the call needs more than its fixed scratch */
 };
 
 /* Probe record layout (float64), per row b and position j in [0, K]:
@@ -164,6 +165,27 @@ int spec_verify(const sv_logits* target_logits, const sv_logits* draft_logits,
                 const int32_t* draft_tokens, const int32_t* draft_len,
                 float temperature, float top_p, uint64_t seed,
                 int32_t* out_tokens, int32_t* out_n_accepted, void* stream);
+
+/*
+ * spec_verify_noalloc -- spec_verify for callers that cannot allocate device
+ * memory (code being captured into a HIP graph, tight serving loops, hosts
+ * that forbid allocation).  Same arguments, kernels and outputs as
+ * spec_verify, but the scratch (statistics records, row states, candidate
+ * lists, row-pass records) lives in one fixed device array of
+ * SPECVERIFY_NOALLOC_SCRATCH_BYTES per device, held until the process ends,
+ * so no call allocates or frees anything.  A call needing more scratch
+ * returns SV_ETOOBIG and launches nothing (B = 64, K = 5, V = 128256 needs
+ * about 0.4 MiB, 12.5 MiB with top-p).  Every call on a device shares that
+ * device's array: calls that overlap on one device (different streams, or
+ * threads) race and must not be issued; each call rewrites, before reading,
+ * all the scratch it uses, so nothing needs clearing between calls.  Errors
+ * otherwise as spec_verify.
+ */
+#define SPECVERIFY_NOALLOC_SCRATCH_BYTES (16 << 20)
+int spec_verify_noalloc(const sv_logits* target_logits, const sv_logits* draft_logits,
+                        const int32_t* draft_tokens, const int32_t* draft_len,
+                        float temperature, float top_p, uint64_t seed,
+                        int32_t* out_tokens, int32_t* out_n_accepted, void* stream);
 
 /*
  * spec_verify_probe -- spec_verify plus the intermediate values behind each

@@ -17,10 +17,10 @@ LIB_PATH = os.path.join(_HERE, "libspecverify.so")
 SV_F32, SV_BF16 = 0, 1
 PROBE_POS, PROBE_ROW = 8, 4
 STATUS = {0: "SV_OK", -1: "SV_EINVAL", -2: "SV_ESHAPE", -3: "SV_EDTYPE", -4: "SV_EHIP", -5: "SV_ENOMEM",
-          -6: "SV_EALIGN", -7: "SV_ECAPTURE"}
+          -6: "SV_EALIGN", -7: "SV_ECAPTURE", -8: "SV_ETOOBIG"}
 KERNEL_KINDS = ("stats", "topp", "rows", "smc", "produce")
 
-EXPORTS = ("spec_verify", "spec_verify_probe", "spec_greedy_verify", "spec_hispec_verify", "spec_smc_step",
+EXPORTS = ("spec_verify", "spec_verify_noalloc", "spec_verify_probe", "spec_greedy_verify", "spec_hispec_verify", "spec_smc_step",
            "spec_draft_produce",
            "spec_verify_strerror",
            "spec_verify_release",
@@ -61,6 +61,8 @@ def load(path=LIB_PATH):
     lib.spec_verify.argtypes = [P(SvLogits), P(SvLogits), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_float,
                                 ctypes.c_float, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
     lib.spec_verify.restype = ctypes.c_int
+    lib.spec_verify_noalloc.argtypes = lib.spec_verify.argtypes
+    lib.spec_verify_noalloc.restype = ctypes.c_int
     lib.spec_verify_probe.argtypes = lib.spec_verify.argtypes[:9] + [ctypes.c_void_p] * 3
     lib.spec_verify_probe.restype = ctypes.c_int
     lib.spec_greedy_verify.argtypes = [P(SvLogits), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32] + \
@@ -119,19 +121,24 @@ def _check(lib, rc):
 
 
 def verify(target, draft, draft_tokens, draft_len=None, temperature=1.0, top_p=1.0, seed=0, *, stream=None,
-           out_tokens=None, out_n_accepted=None, probe=False):
+           out_tokens=None, out_n_accepted=None, probe=False, noalloc=False):
     """The verify step on device tensors.
 
     target [B, K+1, V] and draft [B, K, V]: bfloat16 or float32, V contiguous.
     draft_tokens [B, K] int32 contiguous; draft_len [B] int32 or None.
     Returns (tokens [B, K+1] int32, n_accepted [B] int32), plus
     (probe_pos [B, K+1, 8], probe_row [B, 4]) float64 when probe is set.
+    noalloc: call spec_verify_noalloc (no device allocation by the library;
+    the caller passes out_tokens and out_n_accepted to allocate nothing at
+    all).
     """
     lib = load()
     if draft_tokens.dtype != torch.int32 or not draft_tokens.is_contiguous():
         raise ValueError("draft_tokens must be contiguous int32")
     if draft_len is not None and (draft_len.dtype != torch.int32 or not draft_len.is_contiguous()):
         raise ValueError("draft_len must be contiguous int32")
+    if noalloc and probe:
+        raise ValueError("the no-allocation entry point has no probe")
     dev = target.device
     B, K1 = target.shape[0], target.shape[1]
     if out_tokens is None:
@@ -149,7 +156,10 @@ def verify(target, draft, draft_tokens, draft_len=None, temperature=1.0, top_p=1
         pr = torch.empty((B, PROBE_ROW), dtype=torch.float64, device=dev)
         _check(lib, lib.spec_verify_probe(*args, ctypes.c_void_p(pp.data_ptr()), ctypes.c_void_p(pr.data_ptr()), sh))
         return out_tokens, out_n_accepted, pp, pr
-    _check(lib, lib.spec_verify(*args, sh))
+    if noalloc:
+        _check(lib, lib.spec_verify_noalloc(*args, sh))
+    else:
+        _check(lib, lib.spec_verify(*args, sh))
     return out_tokens, out_n_accepted
 
 

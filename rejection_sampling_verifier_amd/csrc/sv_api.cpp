@@ -143,6 +143,32 @@ int check_logits(const sv_logits* t) {
 // tested without a GPU.
 bool fail_launch_forced() { return env_int("SPECVERIFY_FAIL_LAUNCH", 0) != 0; }
 
+// Scratch of spec_verify_noalloc: one fixed array per device, held until the
+// process ends.  Host code never uses the array's name as an address (on the
+// host it is only a stand-in): each device's address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+constexpr size_t kNoAllocBytes = static_cast<size_t>(SPECVERIFY_NOALLOC_SCRATCH_BYTES);
+static __device__ __align__(256) uint8_t scratch[kNoAllocBytes];
+std::mutex g_noalloc_mu;
+std::map<int, void*> g_noalloc_ptr;
+
+int noalloc_scratch(void** out) {
+    if (fail_launch_forced()) return hip_fail(hipErrorLaunchFailure, "kernel launch (forced by SPECVERIFY_FAIL_LAUNCH)");
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lk(g_noalloc_mu);
+    auto it = g_noalloc_ptr.find(dev);
+    if (it == g_noalloc_ptr.end()) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || ptr == nullptr) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        it = g_noalloc_ptr.emplace(dev, ptr).first;
+    }
+    *out = it->second;
+    return SV_OK;
+}
+
 // Buffers replaced by larger ones.  A HIP graph captured from an earlier
 // call may still use them, so they are freed only by spec_verify_release.
 std::vector<void*> g_retired;
@@ -386,6 +412,26 @@ int verify_impl(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_t
     return launch_verify(S);
 }
 
+// spec_verify on the fixed per-device scratch: the same kernels, no
+// allocation; calls needing more than the array holds are refused.
+int verify_noalloc_impl(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_tokens,
+                        const int32_t* draft_len, float temperature, float top_p, uint64_t seed, int32_t* out_tokens,
+                        int32_t* out_n, void* stream_v) {
+    if (!out_tokens || !out_n) return SV_EINVAL;
+    if (misaligned(out_tokens, 4) || misaligned(out_n, 4)) return SV_EALIGN;
+    Setup S;
+    int rc = plan(tl, dl, draft_tokens, draft_len, temperature, top_p, seed, MODE_VERIFY, stream_v, S);
+    if (rc) return rc;
+    if (S.lay.total > kNoAllocBytes) return SV_ETOOBIG;
+    void* base = nullptr;
+    rc = noalloc_scratch(&base);
+    if (rc) return rc;
+    bind(S, static_cast<uint8_t*>(base));
+    S.p.out_tokens = out_tokens;
+    S.p.out_n = out_n;
+    return launch_verify(S);
+}
+
 // Two-stage verify: stage 1 verifies the drafts against the intermediate
 // layer, stage 2 the n1 + 1 tokens it emitted against the final layer (the
 // intermediate layer as their proposal, Philox stream 1).  One scratch
@@ -546,6 +592,13 @@ int spec_verify(const sv_logits* target_logits, const sv_logits* draft_logits, c
                        out_n_accepted, nullptr, nullptr, stream);
 }
 
+int spec_verify_noalloc(const sv_logits* target_logits, const sv_logits* draft_logits, const int32_t* draft_tokens,
+                        const int32_t* draft_len, float temperature, float top_p, uint64_t seed, int32_t* out_tokens,
+                        int32_t* out_n_accepted, void* stream) {
+    return verify_noalloc_impl(target_logits, draft_logits, draft_tokens, draft_len, temperature, top_p, seed,
+                               out_tokens, out_n_accepted, stream);
+}
+
 int spec_verify_probe(const sv_logits* target_logits, const sv_logits* draft_logits, const int32_t* draft_tokens,
                       const int32_t* draft_len, float temperature, float top_p, uint64_t seed,
                       int32_t* out_tokens, int32_t* out_n_accepted, double* probe_pos, double* probe_row,
@@ -591,6 +644,7 @@ const char* spec_verify_strerror(int status) {
         case SV_ENOMEM: return "scratch allocation failed";
         case SV_EALIGN: return "pointer not aligned to its element size";
         case SV_ECAPTURE: return "the stream is being captured and the call would have to grow its scratch";
+        case SV_ETOOBIG: return "the call needs more scratch than spec_verify_noalloc's fixed array holds";
         default: return "unknown status";
     }
 }

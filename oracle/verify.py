@@ -99,7 +99,7 @@ def softmax(logits, temperature):
     return e / s, m, s
 
 
-def nucleus(p, top_p):
+def nucleus(p, top_p, keep=None):
     """Top-p filter by its sorting definition.
 
     Sort tokens by probability, descending, ties by the lower id (stable
@@ -107,20 +107,42 @@ def nucleus(p, top_p):
     renormalise by the kept mass.  Returns (filtered p, kept mass, margin):
     the margin is the distance of the two running sums around the cut from
     top_p.  When no running sum reaches top_p (rounding with top_p near 1)
-    every token is kept.
+    every token is kept.  `keep` (a count) replaces the cut: the prefix of
+    that many tokens is kept instead, the margin still being that of the
+    defined cut.
     """
+    p, k, c, margin = _nucleus_cut(p, top_p)
+    if keep is not None:
+        k = int(keep)
+    order = np.argsort(-p, kind="stable")
+    kept = float(c[k - 1])
+    out = np.zeros_like(p)
+    out[order[:k]] = p[order[:k]] / kept
+    return out, kept, float(margin)
+
+
+def _nucleus_cut(p, top_p):
+    """(p as float64, kept count, running sums in sorted order, margin)."""
     p = np.asarray(p, dtype=np.float64)
     order = np.argsort(-p, kind="stable")
     c = np.cumsum(p[order])
     hit = np.nonzero(c >= top_p)[0]
     k = int(hit[0]) + 1 if hit.size else p.size
-    kept = float(c[k - 1])
     margin = abs(c[k - 1] - top_p)
     if k >= 2:
         margin = min(margin, abs(c[k - 2] - top_p))
-    out = np.zeros_like(p)
-    out[order[:k]] = p[order[:k]] / kept
-    return out, kept, float(margin)
+    return p, k, c, float(margin)
+
+
+def nucleus_neighbours(p, top_p):
+    """The defined cut's kept count k and the kept masses of the prefixes of
+    k-1, k and k+1 tokens (NaN where no such prefix exists): what another
+    implementation keeps when it takes a near-boundary cut one token to
+    either side."""
+    _, k, c, _ = _nucleus_cut(p, top_p)
+    prev = float(c[k - 2]) if k >= 2 else np.nan
+    nxt = float(c[k]) if k < c.size else np.nan
+    return k, (prev, float(c[k - 1]), nxt)
 
 
 def ratio(p_x, q_x):
@@ -224,6 +246,9 @@ class OracleResult:
     accepts: dict = field(default_factory=dict)   # b -> [(u, r)] in position order
     sample_cdf: dict = field(default_factory=dict)  # b -> running sums / Z (near-boundary draws)
     u_res: np.ndarray = None  # [B, K+1] resampling uniforms of the evaluated positions
+    # b -> {(side "t"/"d", position): (k, (kept of k-1, k, k+1 tokens))} for
+    # the nucleus cuts within SAMPLE_KEEP_BAND of top_p
+    cuts: dict = field(default_factory=dict)
 
     @property
     def flagged(self):
@@ -234,7 +259,8 @@ def _row_is_bad(l):
     return bool(np.any(np.isnan(l)) or np.any(l == np.inf) or np.all(l == -np.inf))
 
 
-def verify(target, draft, draft_tokens, draft_len, temperature, top_p, seed, rows=None, stage=0, forced=None):
+def verify(target, draft, draft_tokens, draft_len, temperature, top_p, seed, rows=None, stage=0, forced=None,
+           forced_cuts=None):
     """The verify step on a batch.
 
     target: [B, K+1, V] logits (float32/float64 values, or uint16 bfloat16
@@ -251,6 +277,10 @@ def verify(target, draft, draft_tokens, draft_len, temperature, top_p, seed, row
     any r > 0; reject: u taken as 1, which no r <= 1 passes).  A caller that
     sees another implementation decide a near-boundary test the other way
     uses it to follow that branch; such a test's margin is meaningless.
+    forced_cuts: optional {row: {(side, position): count}} with side "t"
+    (target) or "d" (draft) that keeps that many tokens at that nucleus cut
+    instead of the defined count (see nucleus); the same use for a cut that
+    lies within rounding of top_p.  Its margin is reported as infinite.
     """
     tl = _widen(target)
     dl = _widen(draft)
@@ -272,7 +302,7 @@ def verify(target, draft, draft_tokens, draft_len, temperature, top_p, seed, row
     min_margin = np.full(B, np.inf)
     n_dec = np.zeros(B, dtype=np.int64)
     n_flag = np.zeros(B, dtype=np.int64)
-    margins, accepts, sample_cdf = {}, {}, {}
+    margins, accepts, sample_cdf, cuts = {}, {}, {}, {}
     u_res_all = np.full((B, K1), np.nan)
 
     for b in rows:
@@ -288,13 +318,25 @@ def verify(target, draft, draft_tokens, draft_len, temperature, top_p, seed, row
             continue
         extra = []
         p, q = [], []
+        fc = (forced_cuts or {}).get(int(b), {})
+        row_cuts = {}
+
+        def filtered(pj, side, j):
+            keep = fc.get((side, j))
+            out, kept, mg = nucleus(pj, tp, keep=keep)
+            if keep is not None:
+                mg = np.inf
+            if mg < SAMPLE_KEEP_BAND:
+                row_cuts[(side, j)] = nucleus_neighbours(pj, tp)
+            extra.append(("nucleus_" + side, j, mg))
+            return out, kept
+
         for j in range(L + 1):
             pj, m, s = softmax(tl[b, j], T)
             probe_pos[b, j, 0:2] = (m, s)
             kept = 1.0
             if use_topp:
-                pj, kept, mg = nucleus(pj, tp)
-                extra.append(("nucleus_t", j, mg))
+                pj, kept = filtered(pj, "t", j)
             probe_pos[b, j, 6] = kept
             p.append(pj)
         for j in range(L):
@@ -302,8 +344,7 @@ def verify(target, draft, draft_tokens, draft_len, temperature, top_p, seed, row
             probe_pos[b, j, 2:4] = (m, s)
             kept = 1.0
             if use_topp:
-                qj, kept, mg = nucleus(qj, tp)
-                extra.append(("nucleus_d", j, mg))
+                qj, kept = filtered(qj, "d", j)
             probe_pos[b, j, 7] = kept
             q.append(qj)
         for j in range(L):
@@ -327,5 +368,7 @@ def verify(target, draft, draft_tokens, draft_len, temperature, top_p, seed, row
         u_res_all[b, : L + 1] = ur
         if d.cdf is not None:
             sample_cdf[b] = d.cdf
+        if row_cuts:
+            cuts[b] = row_cuts
     return OracleResult(tokens, n_acc, probe_pos, probe_row, min_margin, n_dec, n_flag, rows,
-                        margins, accepts, sample_cdf, u_res_all)
+                        margins, accepts, sample_cdf, u_res_all, cuts)

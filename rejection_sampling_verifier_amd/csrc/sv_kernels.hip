@@ -1693,41 +1693,38 @@ template <int DT> __device__ __forceinline__ void unpack_masked(const uint4* v, 
 }
 
 // ---------------------------------------------------------------------------
-// Float64 exponentials of the draw.  2^x = 2^floor(k/64) * 2^((k mod 64)/64)
-// * 2^r with k = round(64 x) and |r| <= 1/128: the middle factor from a
-// 64-entry table in LDS (each workgroup fills it with the library's float64
-// exp2), 2^r - 1 by its Taylor series in r*ln2 to degree 5 (the remainder is
-// below 4e-17), the power of two by ldexp.  Relative error a few units of
-// 2^-53.  Arguments are clamped to >= -1100, below which 2^x is 0 in float64:
-// a logit of -inf gives 0.
+// Float64 exponentials of the draw.  2^x = 2^floor(k/256) * 2^((k mod 256)/256)
+// * 2^r with k = round(256 x) and |r| <= 1/512: the middle factor from a
+// 256-entry table in LDS (each workgroup fills it with the library's float64
+// exp2), 2^r - 1 by its Taylor series in r*ln2 to degree 3 (the remainder is
+// below 1.5e-13 relative), the power of two by ldexp.  Arguments are clamped
+// to >= -1100, below which 2^x is 0 in float64: a logit of -inf gives 0.
 // ---------------------------------------------------------------------------
 constexpr double kLn2 = 0.693147180559945309417232121458176568;
 constexpr double kTay1 = kLn2;
 constexpr double kTay2 = kTay1 * kLn2 / 2.0;
 constexpr double kTay3 = kTay2 * kLn2 / 3.0;
-constexpr double kTay4 = kTay3 * kLn2 / 4.0;
-constexpr double kTay5 = kTay4 * kLn2 / 5.0;
-// x + 1.5 * 2^46 lies in [2^46, 2^47), where doubles are spaced 2^-6 apart:
-// the sum rounds x to the nearest multiple of 1/64, and its low 32 bits hold
-// that multiple times 64 as a two's-complement integer.
-constexpr double kRound64 = 105553116266496.0;
-constexpr int kExpTab = 64;
+constexpr int kExpTabBits = 8;
+constexpr int kExpTab = 1 << kExpTabBits;
+// x + 1.5 * 2^44 lies in [2^44, 2^45), where doubles are spaced 2^-8 apart:
+// the sum rounds x to the nearest multiple of 1/256, and its low 32 bits hold
+// that multiple times 256 as a two's-complement integer.
+constexpr double kRoundTab = 26388279066624.0;
 
 __device__ __forceinline__ void exp2_table_fill(double* tab) {
-    if (threadIdx.x < kExpTab) tab[threadIdx.x] = exp2(static_cast<double>(threadIdx.x) * (1.0 / kExpTab));
+    for (int j = threadIdx.x; j < kExpTab; j += kThreads)
+        tab[j] = exp2(static_cast<double>(j) * (1.0 / kExpTab));
 }
 __device__ __forceinline__ double exp2_f64(double x, const double* tab) {
     x = fmax(x, -1100.0);
-    const double kd = x + kRound64;
+    const double kd = x + kRoundTab;
     const int k = static_cast<int>(static_cast<uint32_t>(__double_as_longlong(kd)));
-    const double r = x - (kd - kRound64);
-    double p = fma(r, kTay5, kTay4);
-    p = fma(p, r, kTay3);
-    p = fma(p, r, kTay2);
+    const double r = x - (kd - kRoundTab);
+    double p = fma(r, kTay3, kTay2);
     p = fma(p, r, kTay1);
     p *= r;
     const double t = tab[k & (kExpTab - 1)];
-    return ldexp(fma(t, p, t), k >> 6);
+    return ldexp(fma(t, p, t), k >> kExpTabBits);
 }
 
 // ---------------------------------------------------------------------------
@@ -2144,7 +2141,7 @@ __device__ __forceinline__ void resample_body(const Params& P, int b, int r, con
         dp.dstar = sgpr_f64((log2(rtil) + dp.oT - dp.oD) / dp.c);
         dp.delta = sgpr_f64(1.01 * P.amb_band / (dp.c * kLn2) + 1e-12 * (fabs(dp.dstar) + 1.0));
     }
-    exp2_table_fill(s_tab);
+    // (the exponential table was filled at the kernel's start)
     if (tid == 0) {
         s_gn = 0;
         s_gover = 0;
@@ -2472,8 +2469,7 @@ __device__ __forceinline__ void resample_body(const Params& P, int b, int r, con
 }
 
 template <int DT, bool TOPP, int R>
-__device__ __forceinline__ void resample_item(const Params& P, int b, int r, const RowParam& rp) {
-    __shared__ DrawShared<R> sh;
+__device__ __forceinline__ void resample_item(const Params& P, int b, int r, const RowParam& rp, DrawShared<R>& sh) {
     // the row's mode and n are the same for every lane: keep them scalar
     const int mode = __builtin_amdgcn_readfirstlane(rp.mode);
     const int rn = __builtin_amdgcn_readfirstlane(rp.n);
@@ -2497,6 +2493,10 @@ template <int DT, bool TOPP, int R>
 __global__ __launch_bounds__(kThreads) void k_rows(Params P) {
     __shared__ RowShared RS;
     __shared__ RowParam s_rp;
+    __shared__ DrawShared<R> DS;
+    // the draw's exponential table, filled while the records load (the
+    // barriers of the decision order it before any use)
+    exp2_table_fill(DS.tab);
     const int b = blockIdx.x / P.nq;
     const int r = blockIdx.x - b * P.nq;
     bool rowok;
@@ -2517,7 +2517,7 @@ __global__ __launch_bounds__(kThreads) void k_rows(Params P) {
     }
     __syncthreads();
     const RowParam rp = s_rp;
-    resample_item<DT, TOPP, R>(P, b, r, rp);
+    resample_item<DT, TOPP, R>(P, b, r, rp, DS);
 }
 
 // ---------------------------------------------------------------------------
@@ -2579,6 +2579,8 @@ template <int DT, int R>
 __global__ __launch_bounds__(kThreads) void k_smc_rows(Params P) {
     __shared__ RowShared RS;
     __shared__ RowParam s_rp;
+    __shared__ DrawShared<R> DS;
+    exp2_table_fill(DS.tab);
     const int b = blockIdx.x / P.nq;
     const int r = blockIdx.x - b * P.nq;
     const int x = lane_token(P, b, P.K);
@@ -2590,7 +2592,7 @@ __global__ __launch_bounds__(kThreads) void k_smc_rows(Params P) {
     }
     __syncthreads();
     const RowParam rp = s_rp;
-    resample_item<DT, false, R>(P, b, r, rp);
+    resample_item<DT, false, R>(P, b, r, rp, DS);
 }
 
 // Resampling: one workgroup over the B particles' new log-weights.  ESS =

@@ -26,9 +26,14 @@ What is checked at a flagged decision instead of equality:
     library's branch;
   * a draw: the library's token has positive weight and its running-sum
     interval lies within the band of u (a valid neighbour of the oracle's);
-  * a nucleus cut: the distribution itself may differ, so from that position
-    on only the output's structure is checked (drafted ids, then one token
-    in [0, V), then -1).
+  * a nucleus cut: the library's kept mass (a probe value, float32-exact to
+    KEPT_TOL) tells which of the prefixes of k-1, k or k+1 tokens it kept; a
+    different count than the oracle's is followed by forcing the oracle's cut
+    to it, and the row must then match that run.  Only when two prefixes lie
+    within KEPT_TOL of the library's mass (the token at the cut carries less
+    than that) is the cut undetermined, and from that position on only the
+    output's structure is checked (drafted ids, then one token in [0, V),
+    then -1).
 """
 
 import math
@@ -48,8 +53,11 @@ BAND_ACCEPT_TOPP = 3.5e-6
 BAND_SAMPLE = 1e-10
 # float64 rounding of Z = A - rho*B and of the exponentials, relative to Z
 # (in units of the target's kept mass): added to BAND_SAMPLE per row
-SAMPLE_REL_EPS = 2e-13
+SAMPLE_REL_EPS = 4e-13
 BAND_NUCLEUS = 3e-6
+# the library's kept masses: float32 exponentials of the kept tokens over the
+# float32 normaliser (relative error below 1.6e-6; kept masses are <= 1)
+KEPT_TOL = 2e-6
 BANDS = {"accept": BAND_ACCEPT, "sample": BAND_SAMPLE, "nucleus_t": BAND_NUCLEUS, "nucleus_d": BAND_NUCLEUS,
          "degenerate": math.inf}
 
@@ -75,9 +83,9 @@ def run_gpu(inp, probe=True, tensors=None):
     return [o.cpu().numpy() for o in out]
 
 
-def run_oracle(inp, rows=None, forced=None):
+def run_oracle(inp, rows=None, forced=None, forced_cuts=None):
     return oracle.verify(inp.target, inp.draft, inp.draft_tokens, inp.draft_len, inp.temperature, inp.top_p,
-                         inp.seed, rows=rows, forced=forced)
+                         inp.seed, rows=rows, forced=forced, forced_cuts=forced_cuts)
 
 
 def say(*a):
@@ -113,6 +121,7 @@ class ParityStats:
     decisions: int = 0            # oracle decisions on those rows
     flagged: dict = field(default_factory=dict)  # kind -> decisions within their band
     branch_switches: int = 0      # flagged acceptance tests the library took the other way
+    cut_switches: int = 0         # flagged nucleus cuts the library took one token to the other side
     neighbour_draws: int = 0      # flagged draws where the library drew a valid neighbour
     structural_rows: int = 0      # rows past a flagged nucleus cut (structure checked only)
     exact_rows: int = 0           # rows equal to the oracle's outputs bit for bit
@@ -131,6 +140,7 @@ class ParityStats:
         for k, v in o.flagged.items():
             self.flagged[k] = self.flagged.get(k, 0) + v
         self.branch_switches += o.branch_switches
+        self.cut_switches += o.cut_switches
         self.neighbour_draws += o.neighbour_draws
         self.structural_rows += o.structural_rows
         self.exact_rows += o.exact_rows
@@ -139,7 +149,7 @@ class ParityStats:
     def __str__(self):
         kinds = " ".join(f"{k}={v}" for k, v in sorted(self.flagged.items()))
         return (f"rows={self.rows} exact={self.exact_rows} decisions={self.decisions} flagged={self.n_flagged} "
-                f"({self.flagged_fraction:.2e}) [{kinds}] switches={self.branch_switches} "
+                f"({self.flagged_fraction:.2e}) [{kinds}] switches={self.branch_switches} cut_switches={self.cut_switches} "
                 f"neighbours={self.neighbour_draws} structural={self.structural_rows}")
 
 
@@ -173,52 +183,90 @@ def _check_draw(inp, res, b, g_tok, stats):
     stats.neighbour_draws += 1
 
 
-def _check_row(inp, res, b, n_g, toks, stats, depth=0):
-    """Compares row b of the library's output with the oracle's result `res`
-    (decision by decision); returns True when they are equal bit for bit."""
+def _library_cuts(res, b, pp):
+    """The library's count at each nucleus cut of row b within BAND_NUCLEUS
+    of top_p, read from its kept mass pp[j, 6|7] against the oracle's
+    prefixes of k-1, k and k+1 tokens.  Returns ({(side, j): count} for the
+    cuts it took differently, the smallest position of a cut it cannot
+    determine, or None)."""
+    flips, unknown = {}, None
+    for kind, j, mg in res.margins[b]:
+        if not kind.startswith("nucleus") or mg >= BAND_NUCLEUS:
+            continue
+        side = kind[-1]
+        k, kept3 = res.cuts[b][(side, j)]
+        lib = float(pp[j, 6 if side == "t" else 7])
+        d = np.array([abs(lib - v) if np.isfinite(v) else np.inf for v in kept3])
+        near = np.sort(d)
+        if not near[0] <= KEPT_TOL or near[1] <= KEPT_TOL:
+            unknown = j if unknown is None else min(unknown, j)
+            continue
+        best = int(np.argmin(d))
+        if best != 1:
+            flips[(side, j)] = k - 1 + best
+    return flips, unknown
+
+
+def _check_row(inp, res, b, gpu_row, stats, forced=None, cuts=None, depth=0):
+    """Compares row b of the library's output (n, tokens, probe_pos or None)
+    with the oracle's result `res`, decision by decision.  Returns (True when
+    equal bit for bit, the oracle result the row was finally compared to)."""
+    n_g, toks, pp = gpu_row
     n_o = int(res.n_accepted[b])
     if n_o < 0:
         assert n_g == n_o and np.all(toks == -1), (b, n_g, toks)
-        return True
+        return True, res
+    assert depth < 6, (b, "too many near-boundary switches")
     L = int(inp.lengths()[b])
     margins = res.margins[b]
-    # a flagged nucleus cut at a position the row's decisions use: the
-    # distribution there is not pinned; structure from that position on
-    cut_flag = sorted(j for k, j, mg in margins if k.startswith("nucleus") and mg < BAND_NUCLEUS)
-    first_cut = cut_flag[0] if cut_flag else L + 1
+    first_cut = L + 1
+    if pp is not None:
+        flips, unknown = _library_cuts(res, b, pp)
+        if flips:
+            stats.cut_switches += len(flips)
+            cuts = {**(cuts or {}), **flips}
+            alt = run_oracle(inp, rows=[b], forced={b: forced} if forced else None, forced_cuts={b: cuts})
+            return _check_row(inp, alt, b, gpu_row, stats, forced, cuts, depth + 1)
+        if unknown is not None:
+            first_cut = unknown
+    else:
+        cut_flag = [j for k, j, mg in margins if k.startswith("nucleus") and mg < BAND_NUCLEUS]
+        first_cut = min(cut_flag, default=L + 1)
     accepts = res.accepts[b]
     j0 = min(n_g, n_o)
     if first_cut <= j0:
         stats.structural_rows += 1
         _structure_ok(inp, b, n_g, toks)
-        return False
+        return False, res
     if n_g != n_o:
         # the test at j0 went the other way: it must lie within its band
         u, r = accepts[j0]
-        assert abs(u - r) < accept_band(inp) and depth == 0, (b, n_g, n_o, u, r)
+        assert abs(u - r) < accept_band(inp) and j0 not in (forced or {}), (b, n_g, n_o, u, r)
         stats.branch_switches += 1
-        alt = run_oracle(inp, rows=[b], forced={int(b): {j0: n_g > j0}})
-        _check_row(inp, alt, b, n_g, toks, stats, depth + 1)
-        return False
+        forced = {**(forced or {}), j0: n_g > j0}
+        alt = run_oracle(inp, rows=[b], forced={b: forced}, forced_cuts={b: cuts} if cuts else None)
+        return _check_row(inp, alt, b, gpu_row, stats, forced, cuts, depth + 1)
     assert list(toks[:n_g]) == list(res.tokens[b, :n_g]), (b, toks, res.tokens[b])
     assert np.all(toks[n_g + 1:] == -1), (b, toks)
     if first_cut <= n_g:
         stats.structural_rows += 1
         _structure_ok(inp, b, n_g, toks)
-        return False
+        return False, res
     if any(k == "degenerate" for k, _, _ in margins):
         _structure_ok(inp, b, n_g, toks)
-        return False
+        return False, res
     _check_draw(inp, res, b, int(toks[n_g]), stats)
-    return bool(toks[n_g] == res.tokens[b, n_g])
+    return bool(toks[n_g] == res.tokens[b, n_g]), res
 
 
 def check_parity(inp, res, gpu, rows=None, check_probes=True):
     """Decision-by-decision comparison on the rows the oracle computed (see
     the module docstring).  Probe values (max logit, softmax normalisers,
     p'(x_j), q'(x_j), kept masses, and Z, t, u where the row's n agrees)
-    must agree to PROBE_RTOL relative.  Returns ParityStats."""
+    must agree to PROBE_RTOL relative with the oracle run the row was
+    compared to.  Returns ParityStats."""
     tokens, n_acc = gpu[0], gpu[1]
+    has_probes = len(gpu) > 2
     rows = res.rows if rows is None else rows
     st = ParityStats()
     for b in rows:
@@ -228,15 +276,16 @@ def check_parity(inp, res, gpu, rows=None, check_probes=True):
         for k, _, mg in ms:
             if mg < band_of(k, res, b, inp):
                 st.flagged[k] = st.flagged.get(k, 0) + 1
-        exact = _check_row(inp, res, b, int(n_acc[b]), tokens[b], st)
+        row = (int(n_acc[b]), tokens[b], gpu[2][b] if has_probes else None)
+        exact, ref = _check_row(inp, res, b, row, st)
         st.exact_rows += int(exact)
-        if check_probes and len(gpu) > 2 and res.n_accepted[b] >= 0:
+        if check_probes and has_probes and ref.n_accepted[b] >= 0:
             pp, pr = gpu[2], gpu[3]
-            ok = ~np.isnan(res.probe_pos[b])
+            ok = ~np.isnan(ref.probe_pos[b])
             np.testing.assert_array_equal(np.isnan(pp[b]), ~ok, err_msg=f"probe NaN pattern, row {b}")
-            np.testing.assert_allclose(pp[b][ok], res.probe_pos[b][ok], rtol=PROBE_RTOL, atol=0,
+            np.testing.assert_allclose(pp[b][ok], ref.probe_pos[b][ok], rtol=PROBE_RTOL, atol=0,
                                        err_msg=f"probe_pos row {b}")
-            if int(n_acc[b]) == int(res.n_accepted[b]) and pr[b][3] == res.n_accepted[b]:
-                np.testing.assert_allclose(pr[b][:3], res.probe_row[b][:3], rtol=PROBE_RTOL, atol=0,
+            if int(n_acc[b]) == int(ref.n_accepted[b]) and pr[b][3] == ref.n_accepted[b]:
+                np.testing.assert_allclose(pr[b][:3], ref.probe_row[b][:3], rtol=PROBE_RTOL, atol=0,
                                            err_msg=f"probe_row row {b}")
     return st

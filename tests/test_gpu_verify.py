@@ -355,16 +355,16 @@ def test_largest_accepted_vocabulary(dtype, top_p):
     for one another, so the library sizes them to take at most a quarter of
     the device's resident row-pass slots (four calls may run at once).  In
     bf16 that reaches V = 2^21 (256 items of 8192 ids at four workgroups per
-    CU); float32 items need more registers (three per CU), so float32 stops at
-    192 items, V = 1.5 * 2^20, and V = 2^21 is refused with SV_ESHAPE.  (With
-    millions of tokens a row's decisions often fall in the flag band; four
-    rows leave some unflagged.)"""
-    V = 1 << 21 if dtype == "bf16" else 3 << 19
+    CU); float32 items and the top-p variant need more registers (three per
+    CU), so they stop at 192 items, V = 1.5 * 2^20, and V = 2^21 is refused
+    with SV_ESHAPE."""
+    full = dtype == "bf16" and top_p == 1.0
+    V = 1 << 21 if full else 3 << 19
     inp = W.synthetic(4, 2, V, dtype=dtype, temperature=0.7, top_p=top_p, seed=90 + int(top_p * 10),
                       gen_seed=V + (dtype == "f32"))
     _parity(inp, label=f"V={V} {dtype} top_p={top_p}")
-    if dtype == "f32":
-        big = W.synthetic(2, 2, 1 << 21, dtype="f32", temperature=0.7, seed=91, gen_seed=91)
+    if not full:
+        big = W.synthetic(2, 2, 1 << 21, dtype=dtype, temperature=0.7, top_p=top_p, seed=91, gen_seed=91)
         with pytest.raises(binding.SpecVerifyError) as err:
             run_gpu(big)
         assert err.value.status == -2

@@ -115,3 +115,44 @@ def test_structure_after_flagged_nucleus_cut(monkeypatch):
     bad[0][0, int(bad[1][0])] = inp.V  # out of range
     with pytest.raises(AssertionError):
         gh.check_parity(inp, res, bad)
+
+
+def _fake_probed(res):
+    return _fake(res) + [res.probe_pos.copy(), res.probe_row.copy()]
+
+
+def test_nucleus_cut_read_from_kept_mass(monkeypatch):
+    # every cut counts as near top_p; the library's kept mass shows which
+    # prefix it kept: a row that took k+1 tokens at one cut must match the
+    # oracle forced to that count, and fails when its tokens do not
+    monkeypatch.setattr(gh, "BAND_NUCLEUS", 1.0)
+    monkeypatch.setattr(ov, "SAMPLE_KEEP_BAND", 2.0)
+    inp = W.synthetic(12, 3, 60, dtype="f32", temperature=0.8, top_p=0.7, seed=3, gen_seed=5)
+    res = gh.run_oracle(inp)
+    st = gh.check_parity(inp, res, _fake_probed(res))
+    assert st.cut_switches == 0 and st.structural_rows == 0 and st.exact_rows == inp.B
+    switched = 0
+    for b in range(inp.B):
+        n = int(res.n_accepted[b])
+        k, kept3 = res.cuts[b][("t", n)]
+        if not np.isfinite(kept3[2]):
+            continue
+        alt = gh.run_oracle(inp, rows=[b], forced_cuts={b: {("t", n): k + 1}})
+        g = _fake_probed(res)
+        g[0][b], g[1][b], g[2][b], g[3][b] = alt.tokens[b], alt.n_accepted[b], alt.probe_pos[b], alt.probe_row[b]
+        assert g[2][b, n, 6] == kept3[2]
+        st = gh.check_parity(inp, res, g, rows=[b])
+        assert st.cut_switches == 1 and st.structural_rows == 0
+        if alt.tokens[b, int(alt.n_accepted[b])] != res.tokens[b, n]:
+            # the kept mass says k+1: the unforced oracle's tokens do not pass
+            g2 = _fake_probed(res)
+            g2[2][b] = alt.probe_pos[b]
+            g2[3][b] = alt.probe_row[b]
+            with pytest.raises(AssertionError):
+                gh.check_parity(inp, res, g2, rows=[b])
+            switched += 1
+        nb = int(alt.n_accepted[b])
+        g[0][b, nb] = (g[0][b, nb] + 7) % inp.V
+        with pytest.raises(AssertionError):
+            gh.check_parity(inp, res, g, rows=[b])
+    assert switched >= 2

@@ -55,20 +55,23 @@
  * that holds a call of this library.
  *
  * Concurrency: concurrent calls on the same stream from several host threads
- * are not supported.  Calls on different streams may run concurrently, up to
- * four executing at once (the hardware queues a process gets by default,
- * GPU_MAX_HW_QUEUES = 4): the row pass splits a logit row over workgroups
- * that wait for one another, and the library sizes them so that one row's
- * workgroups take at most a quarter of the device's resident slots for that
- * kernel, which keeps every wait finite with four calls in flight (a
- * vocabulary too large for that returns SV_ESHAPE).  Work of other processes
- * on the same device is outside this guarantee; should a row's workgroups
- * still give up waiting (after about a second), that row reports
- * out_n_accepted = -2 and every token -1 (an SMC particle: bonus -2).
+ * are not supported.  Calls on different streams may run concurrently, each
+ * on its stream's own scratch.  No workgroup of a call waits for another
+ * workgroup to start: the row pass splits a logit row over workgroups, and
+ * the one that completes the row's arrival count draws the token from the
+ * records the others left, so any number of calls, and any other work on the
+ * device, can share it.  A row whose record is found missing or foreign (a
+ * corrupted scratch; not otherwise possible) reports out_n_accepted = -2 and
+ * every token -1 (an SMC particle: bonus -2).
  *
  * Testing: with the environment variable SPECVERIFY_FAIL_LAUNCH set to a
  * non-zero value every call fails as a failed kernel launch does (SV_EHIP,
  * message through spec_verify_strerror) before touching the device.
+ * SPECVERIFY_AMB_BAND (a number) replaces the relative error the row pass
+ * assumes for the float32 kept-mass ratio when it classifies ids before the
+ * exact ratio is known: 0 sends every row through the exact second round, a
+ * wide band fills the ambiguous groups.  The result is the same either way;
+ * only the path (and its time) changes.
  */
 #ifndef SPECVERIFY_H
 #define SPECVERIFY_H
@@ -82,12 +85,8 @@ extern "C" {
 #define SPECVERIFY_ABI_VERSION 1
 #define SPECVERIFY_MAX_K 16
 /* Largest vocabulary of the calls that draw a token (spec_verify,
- * spec_verify_probe, spec_smc_step, spec_hispec_verify): their row pass
- * splits a logit row over workgroups that wait for one another, so a row's
- * workgroups must fit in a quarter of the device's resident slots (see
- * Concurrency above; on MI355X bf16 rows reach 2^21, float32 rows with four
- * calls in flight somewhat less, beyond which SV_ESHAPE).  Greedy verify and
- * the draft producer take V up to 2^24. */
+ * spec_verify_probe, spec_smc_step, spec_hispec_verify; beyond it SV_ESHAPE).
+ * Greedy verify and the draft producer take V up to 2^24. */
 #define SPECVERIFY_MAX_V (1 << 21)
 
 /* Element type of a logits tensor. */
@@ -149,12 +148,11 @@ enum {
  * out_tokens      device int32 [B, K+1], contiguous: the n_b accepted drafted
  *                 ids, then the resampled or bonus token, then -1.
  * out_n_accepted  device int32 [B]: n_b in [0, L_b], or -1 for an invalid row
- *                 (-2: see Concurrency above).
+ *                 (-2: see Concurrency above; not otherwise possible).
  * stream          hipStream_t to run on (NULL = the default stream).
  *
  * Errors: arguments the host can check return SV_EINVAL / SV_ESHAPE /
- * SV_EDTYPE / SV_EALIGN and launch nothing (SV_ESHAPE also for a vocabulary
- * whose rows the row pass cannot keep resident, see Concurrency above);
+ * SV_EDTYPE / SV_EALIGN and launch nothing;
  * SV_ECAPTURE as described under Graphs.  Data errors cannot be reported
  * synchronously: a row whose L_b lies outside [0, K], whose drafted id at some
  * j < L_b lies outside [0, V), or one of whose needed logit rows holds a NaN, a

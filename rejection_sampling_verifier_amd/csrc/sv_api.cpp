@@ -27,6 +27,8 @@ struct Scratch {
     size_t bytes = 0;
 };
 
+static_assert(SPECVERIFY_MAX_V == sv::kMaxV, "vocabulary limit");
+
 struct Layout {
     size_t prec, rv, qrec, chdr, cand, cum, total;
 };
@@ -88,6 +90,12 @@ int env_int(const char* name, int dflt) {
     return std::atoi(s);
 }
 
+double env_double(const char* name, double dflt) {
+    const char* s = std::getenv(name);
+    if (!s || !*s) return dflt;
+    return std::atof(s);
+}
+
 bool misaligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) != 0; }
 
 // Compute units of the current device (cached per device).
@@ -103,30 +111,6 @@ int device_cus() {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
     cache[dev] = n;
     return n;
-}
-
-// Calls that may execute at once on one device: the hardware queues a
-// process gets (HIP's default, GPU_MAX_HW_QUEUES = 4).
-constexpr int kConcurrentCalls = 4;
-
-// Resident row-pass workgroups on the current device for a variant (cached).
-int64_t resident_row_slots(int dtype, bool topp, bool smc, int runs, int cus) {
-    static std::mutex mu;
-    static std::map<std::tuple<int, int, int, int, int>, int> cache;
-    int dev = 0;
-    (void)hipGetDevice(&dev);
-    const auto key = std::make_tuple(dev, dtype, topp ? 1 : 0, smc ? 1 : 0, runs);
-    std::lock_guard<std::mutex> lk(mu);
-    auto it = cache.find(key);
-    int per_cu;
-    if (it != cache.end()) {
-        per_cu = it->second;
-    } else {
-        per_cu = sv::rows_blocks_per_cu(dtype, topp, smc, runs);
-        if (per_cu <= 0) per_cu = 1;  // unknown: assume one per CU
-        cache[key] = per_cu;
-    }
-    return static_cast<int64_t>(per_cu) * cus;
 }
 
 int check_logits(const sv_logits* t) {
@@ -260,7 +244,6 @@ int plan(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_tokens, 
     const int B = tl->B, V = tl->V, K = tl->P - 1;
     if (B <= 0 || V <= 0 || K < 1 || K > SPECVERIFY_MAX_K) return SV_ESHAPE;
     if (!greedy && (dl->B != B || dl->V != V || dl->P != K)) return SV_ESHAPE;
-    // the calls that draw a token need a row's items resident together
     if (B > (1 << 22) || V > (greedy ? (1 << 24) : SPECVERIFY_MAX_V)) return SV_ESHAPE;
     if (!(temperature > 0.f) || !std::isfinite(temperature)) return SV_EINVAL;
     if (!(top_p > 0.f && top_p <= 1.f)) return SV_EINVAL;
@@ -289,24 +272,10 @@ int plan(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_tokens, 
         if (big < 2ll * cus) runs = 1;
         const int forced = env_int("SPECVERIFY_ROW_RUNS", 0);
         if (forced == 1 || forced == 2 || forced == sv::kRunsMax) runs = forced;
-        // The items of a row wait for one another, so a row progresses only
-        // once all of its items are resident.  Each call has at most one
-        // partly resident row at a time (items start in grid order), and at
-        // most kConcurrentCalls calls execute at once; with a row's items
-        // within 1/kConcurrentCalls of the resident slots, some slot is always
-        // free of waiting items and every wait ends.  Larger items if needed.
-        for (;;) {
-            const int64_t nqr = (V + runs * sv::kRunIds - 1) / (runs * sv::kRunIds);
-            if (nqr * kConcurrentCalls <= resident_row_slots(dtype, top_p < 1.f, smc, runs, cus)) break;
-            if (runs == sv::kRunsMax) return SV_ESHAPE;
-            runs = runs == 1 ? 2 : sv::kRunsMax;
-        }
     }
     const int nq = greedy ? 0 : (V + runs * sv::kRunIds - 1) / (runs * sv::kRunIds);
     const int64_t per_row = static_cast<int64_t>(nslot) * nch + nq;
     if (static_cast<int64_t>(B) * per_row >= (1ll << 31)) return SV_ESHAPE;
-    // the statistics kernel clears the row pass's records, a few words each
-    if (static_cast<int64_t>(sv::kQRecWords) * nq > static_cast<int64_t>(sv::kThreads) * nslot * nch) return SV_ESHAPE;
 
     // greedy verify takes its argmaxes and top-k from the candidate lists
     const bool topp = top_p < 1.f || greedy;
@@ -344,7 +313,9 @@ int plan(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_tokens, 
     // relative error bound of keptT/keptD as the statistics (and nucleus)
     // passes compute them: float32 exponentials and float32 lane and wave
     // sums, below 1.2e-6 per normaliser (below 2e-6 per kept mass)
-    p.amb_band = top_p < 1.f ? 4e-6 : 2.5e-6;
+    // SPECVERIFY_AMB_BAND replaces it (tests: 0 sends every row to the exact
+    // second round, a wide band fills the items' ambiguous groups)
+    p.amb_band = env_double("SPECVERIFY_AMB_BAND", top_p < 1.f ? 4e-6 : 2.5e-6);
     p.inv_c = static_cast<float>(1.0 / c);
     p.top_p = top_p;
     p.key0 = static_cast<uint32_t>(seed & 0xFFFFFFFFull);

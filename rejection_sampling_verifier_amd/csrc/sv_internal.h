@@ -17,7 +17,9 @@ constexpr int kRun = 8;              // ids per thread per run of a resample ite
 constexpr int kRunsMax = 4;          // runs per thread per resample item, large batches
 constexpr int kRunIds = kThreads * kRun;  // ids per run of an item (2048)
 constexpr int kRecWords = 4;         // 64-bit words per tagged statistics record
-constexpr int kQRecWords = 24;       // 64-bit words per row-pass item record (and the row flag)
+constexpr int kQRecWords = 88;       // 64-bit words per row-pass item record
+constexpr int kQCnt = 21;            // word of item 0's record: the row's arrival count
+constexpr int kMaxV = 1 << 21;       // largest vocabulary of the sampling entry points
 constexpr int kCand = 256;           // nucleus candidates a statistics chunk lists at most
 constexpr int kMaxTopK = 64;         // greedy verify: largest top-k
 constexpr uint32_t kNoCover = 0xFFFFFFFFu;  // candidate header: the chunk's list covers nothing
@@ -134,9 +136,6 @@ struct LaunchEvents {
 hipError_t launch_stats(const Params& p, int dtype, int unroll, bool topp, hipStream_t s, const LaunchEvents& ev);
 hipError_t launch_topp(const Params& p, int dtype, hipStream_t s, const LaunchEvents& ev);
 hipError_t launch_rows(const Params& p, int dtype, bool topp, hipStream_t s, const LaunchEvents& ev);
-// Resident workgroups per CU of the row pass (smc: the SMC particle pass)
-// with `runs` runs per item; 0 when unknown.
-int rows_blocks_per_cu(int dtype, bool topp, bool smc, int runs);
 // SMC-SD step: the statistics pass, then the particle pass (log-weight
 // increments and the bonus draw), then the resampling kernel.
 hipError_t launch_smc_rows(const Params& p, int dtype, hipStream_t s, const LaunchEvents& ev);

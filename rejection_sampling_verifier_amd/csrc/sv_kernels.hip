@@ -822,15 +822,9 @@ __device__ __forceinline__ void stats_item(const Params& P, int b, int slot, int
 template <int DT, int U, bool CAND>
 __global__ __launch_bounds__(kThreads, 8) void k_stats(Params P) {
     const int item = blockIdx.x;
-    {
-        // clear this call's resample-item records, which the row pass polls
-        // (words [item*per, (item+1)*per), per <= kThreads by the host)
-        const int64_t words = static_cast<int64_t>(P.B) * P.nq * kQRecWords;
-        const int64_t grid = static_cast<int64_t>(P.B) * P.nslot * P.nch;
-        const int per = static_cast<int>((words + grid - 1) / grid);
-        const int64_t e = static_cast<int64_t>(item) * per + threadIdx.x;
-        if (static_cast<int>(threadIdx.x) < per && e < words) P.qrec[e] = 0ull;
-    }
+    // the row pass's arrival count of batch row `item` starts at 0 (the grid
+    // has at least B workgroups)
+    if (threadIdx.x == 0 && item < P.B && P.nq > 0) P.qrec[static_cast<size_t>(item) * P.nq * kQRecWords + kQCnt] = 0ull;
     const int rvi = item / P.nch;
     const int chunk = item - rvi * P.nch;
     const int b = rvi / P.nslot;
@@ -1679,6 +1673,11 @@ __device__ __forceinline__ void issue_run(const uint8_t* row, int64_t id0, int V
         load_run_elems<DT>(row, id0, V, v);
     }
 }
+// One logit (id < V) as float32, by a 2- or 4-byte load.
+template <int DT> __device__ __forceinline__ float load_logit(const uint8_t* row, int64_t id) {
+    if (DT == DT_F32) return reinterpret_cast<const float*>(row)[id];
+    return __uint_as_float(static_cast<uint32_t>(reinterpret_cast<const uint16_t*>(row)[id]) << 16);
+}
 template <int DT> __device__ __forceinline__ bool run_straddles(int64_t id0, int V) {
     return (V % Fmt<DT>::VE) != 0 && id0 < V && V <= id0 + kRun;
 }
@@ -1751,12 +1750,15 @@ __device__ __forceinline__ double exp2_f64(double x, const double* tab) {
 constexpr int kAmbGroups = 3;
 // Record of an item (tagged 64-bit words, 32 payload bits each): word 0 the
 // group count (bits 0-7) and the overflow flag (bit 8); then ST, SD, A, B as
-// float64 (two words each); then the groups' GT, GD.  The second round's
-// record (the item's mass W, two words) follows.
+// float64 (two words each); then the groups' GT, GD.  Word kQCnt of item 0's
+// record is the row's arrival count; from word kQKw on, the item's sums per
+// (run, wave) -- A then B, [R][kWaves] each -- as float64 (two words each).
 constexpr int kQHdr = 9;
 constexpr int kQRound1 = kQHdr + 4 * kAmbGroups;   // 21
-constexpr int kQRound2 = kQRound1;                 // word offset of the second round
-static_assert(kQRound2 + 2 < kQRecWords, "record layout: the last word is the row flag");
+static_assert(kQCnt == kQRound1, "record layout");
+constexpr int kQKw = 24;
+static_assert(kQKw + 4 * kRunsMax * kWaves <= kQRecWords, "record layout");
+constexpr int kMaxItems = kMaxV / kRunIds;  // items of a row at most (one-run items)
 
 // Loads n record words until all carry `tag` (true), or kPollLimit polls.
 template <int N>
@@ -2062,18 +2064,11 @@ __device__ __forceinline__ double item_mass(const ItemRec& q, double rho, bool r
     return W;
 }
 
-// A row some of whose items stopped polling (a record that never arrived:
-// the row's items were not all resident) is reported with n = -2 and every
-// token -1.  The item that gives up first marks the row in a flag word (the
-// last word of item 0's record, cleared with the records); the writers of
-// the row's ordinary outputs check it, so that an item that only ran after
-// the others gave up does not overwrite the sentinel.
-__device__ __forceinline__ uint64_t* row_flag(const Params& P, int b) {
-    return P.qrec + static_cast<size_t>(b) * P.nq * kQRecWords + (kQRecWords - 1);
-}
-__device__ __forceinline__ void row_timed_out(const Params& P, int b) {
+// A row whose last item finds another item's record missing (its tag is
+// not this call's: only a corrupted scratch can cause it) is reported with
+// n = -2 and every token -1.
+__device__ __forceinline__ void row_failed(const Params& P, int b) {
     const int tid = threadIdx.x;
-    if (tid == 0) st_agent(row_flag(P, b), tagged(P.tag, 1u));
     if (P.smc) {
         if (tid == 0) P.out_tokens[b] = -2;
         return;
@@ -2082,21 +2077,30 @@ __device__ __forceinline__ void row_timed_out(const Params& P, int b) {
     if (tid < P.K + 1) P.out_tokens[static_cast<size_t>(b) * (P.K + 1) + tid] = -1;
 }
 
-// The draw of batch row b for item r, given the row's decision (the same in
-// every item of the row) with n = rn and the mode's RESID.  Every thread must
-// call it.
-// The draw's LDS (one instance per workgroup, shared by the residual and
-// bonus variants of the kernel).
+// Arrival of one item of a row at the row's count, which the statistics
+// kernel of the call set to 0 (relaxed: the records are tagged words, which
+// the winner polls for).  True for the item that completes the count.  One
+// atomic add per item: no retries under contention.
+__device__ __forceinline__ bool row_arrive(uint64_t* cnt, int nq) {
+    const uint64_t old = __hip_atomic_fetch_add(cnt, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return old + 1u == static_cast<uint64_t>(nq);
+}
+
 template <int R> struct DrawShared {
     double tab[kExpTab];
     double red[4][kWaves];
     double wt[R][kWaves];
     double A[R][kThreads], B[R][kThreads];  // per (run, thread) sums
-    int item, mode, ok, hk, hw, last;
+    int item, mode, ok, hk, hw, last, fin, whole;
     double pre, Z, t, rho, hoff, ST;
     // ambiguous groups of the item (key, GT, GD), their count and overflow
     double gkey[kAmbGroups], gT[kAmbGroups], gD[kAmbGroups];
     int gn, gover;
+    double kw[2 * R * kWaves];  // the holding item's per-(run, wave) sums
+    union {
+        double qm[kMaxItems];       // exact item masses (second round)
+        double kwall[kMaxItems];    // every item's per-(run, wave) sums, when they fit
+    };
 };
 
 template <int DT, bool TOPP, bool RESID, int R>
@@ -2152,11 +2156,23 @@ __device__ __forceinline__ void resample_body(const Params& P, int b, int r, con
     ItemSums s;
     item_first_pass<DT, TOPP, RESID, R>(P, rowT, rowD, aligned, r, interior, dp, s_tab, s_A, s_B, s);
     {
+        // the item's totals, and its sums per (run, wave) straight to the
+        // record (lane 0 of each wave)
+        uint64_t* kw = qrec + static_cast<size_t>(r) * kQRecWords + kQKw;
         double Aall = 0.0, Ball = 0.0;
 #pragma unroll
         for (int k = 0; k < R; ++k) {
-            Aall += s_A[k][tid];
-            Ball += s_B[k][tid];
+            const double a = s_A[k][tid], bk = s_B[k][tid];
+            Aall += a;
+            Ball += bk;
+            const double wa = wave_sum_dpp(a);
+            const double wb = RESID ? wave_sum_dpp(bk) : 0.0;
+            if (lane < 4) {
+                // two tagged words per sum: A_kw, then B_kw
+                const double x = lane < 2 ? wa : wb;
+                const int slot = lane < 2 ? k * kWaves + wv : (R + k) * kWaves + wv;
+                st_agent(kw + 2 * slot + (lane & 1), tagged(P.tag, f64_word(x, lane & 1)));
+            }
         }
         const double v0 = wave_sum_dpp(s.ST), v1 = wave_sum_dpp(s.SD);
         const double v2 = wave_sum_dpp(Aall), v3 = wave_sum_dpp(Ball);
@@ -2228,25 +2244,60 @@ __device__ __forceinline__ void resample_body(const Params& P, int b, int r, con
         st_agent(qrec + static_cast<size_t>(r) * kQRecWords + tid, tagged(P.tag, v));
     }
 
-    // 3. every item's record in id order (wave 0; lane l takes items
+    // 3. arrival: the item that completes the row's count finishes the draw;
+    // the others are done.  Nothing waits on another workgroup: the finisher
+    // reads the records it needs by their tags (every item stored its record
+    // before arriving, so a word still in flight lands within its polls).
+    __syncthreads();
+    if (tid == 0) {
+        sh.fin = row_arrive(qrec + kQCnt, nq) ? 1 : 0;
+        s_ok = 1;
+    }
+    __syncthreads();
+    if (!sh.fin) return;
+
+    // 4. every item's record in id order (wave 0; lane l takes items
     // [l*g, (l+1)*g)): exact rho, the items' masses, Z, t = u*Z and the item
-    // holding t.  Each item sees the same records and makes the same sums.
+    // holding t.
     const int gper = (nq + 63) / 64;
     const int e0 = min(lane * gper, nq), e1 = min(e0 + gper, nq);
+    // one item per lane (nq <= 64): its record is read once, and its masses
+    // kept once rho is known
+    double m1 = 0.0, mST = 0.0;
+    int ng1 = 0;
+    // the other waves meanwhile fetch every item's per-(run, wave) sums
+    constexpr int kKw = 2 * R * kWaves;
+    const bool kwpre = nq * kKw <= kMaxItems;
+    if (wv > 0 && kwpre) {
+        bool okk = true;
+        for (int i = tid - 64; i < nq * kKw; i += kThreads - 64) {
+            uint32_t w[2];
+            okk = poll_words<2>(qrec + static_cast<size_t>(i / kKw) * kQRecWords + kQKw + 2 * (i % kKw), P.tag, w) && okk;
+            sh.kwall[i] = f64_of(w[0], w[1]);
+        }
+        if (!okk) s_ok = 0;
+    }
     if (wv == 0) {
         bool ok = true;
         double sts = 0.0, sds = 0.0;
         int over = 0;
+        ItemRec q1 = own;
         for (int e = e0; e < e1; ++e) {
             ItemRec q = own;
             if (e != r) ok = read_item_record(qrec + static_cast<size_t>(e) * kQRecWords, P.tag, q) && ok;
             sts += q.ST;
             sds += q.SD;
             over |= q.over;
+            q1 = q;
         }
         const double ST = lane63(wave_scan_dpp(sts));
         const double SD = lane63(wave_scan_dpp(sds));
         const double rho = RESID ? ST / SD : 0.0;
+        if (gper == 1 && e0 < e1) {
+            m1 = item_mass(q1, rho, RESID);
+            mST = q1.ST;
+            ng1 = q1.n;
+        }
         // rho~ outside its assumed band of rho would misclassify: redo exactly
         const bool inband = fabs(rho / rtil - 1.0) <= P.amb_band;
         const bool rowover = RESID && (!inband || __ballot(over != 0) != 0ull);
@@ -2254,46 +2305,56 @@ __device__ __forceinline__ void resample_body(const Params& P, int b, int r, con
         if (lane == 0) {
             s_rho = rho;
             s_ST = ST;
-            s_ok = allok ? 1 : 0;
+            if (!allok) s_ok = 0;
             s_mode = rowover ? 2 : 0;
         }
     }
     __syncthreads();
     if (!s_ok) {
-        row_timed_out(P, b);
+        row_failed(P, b);
         return;
     }
     dp.rho = sgpr_f64(s_rho);
     const bool round2 = s_mode == 2;
-    // per-run masses of this item's threads (in s_A, s_B): an exact pass
-    // when the row goes to a second round, else from the first pass
     if (round2) {
-        item_exact_pass<DT, TOPP, RESID, R>(P, rowT, rowD, aligned, r, interior, dp, s_tab, false, s_A, s_B);
-        double w = 0.0;
+        // some ids could not be classified against rho~ (rare): every item's
+        // exact mass, one item after another
+        for (int e = 0; e < nq; ++e) {
+            const bool in_e = static_cast<int64_t>(e + 1) * (R * kRunIds) <= P.V;
+            item_exact_pass<DT, TOPP, RESID, R>(P, rowT, rowD, aligned, e, in_e, dp, s_tab, false, s_A, s_B);
+            double w = 0.0;
 #pragma unroll
-        for (int k = 0; k < R; ++k) w += s_A[k][tid];
-        w = wave_sum_dpp(w);
-        if (lane == 0) s_red[0][wv] = w;
-        __syncthreads();
-        const double Wown = (s_red[0][0] + s_red[0][1]) + (s_red[0][2] + s_red[0][3]);
-        if (tid < 2)
-            st_agent(qrec + static_cast<size_t>(r) * kQRecWords + kQRound2 + tid, tagged(P.tag, f64_word(Wown, tid)));
+            for (int k = 0; k < R; ++k) w += s_A[k][tid];
+            w = wave_sum_dpp(w);
+            if (lane == 0) s_red[0][wv] = w;
+            __syncthreads();
+            if (tid == 0) sh.qm[e] = (s_red[0][0] + s_red[0][1]) + (s_red[0][2] + s_red[0][3]);
+            __syncthreads();
+        }
     }
     if (wv == 0) {
-        // the masses in id order, Z, t and the holding item
+        // the masses in id order, Z, t and the holding item (with its group
+        // count: an item with ambiguous ids is recomputed whole)
         bool ok = true;
-        auto mass_of = [&](int e, bool sel) {
-            if (round2 && !sel) {
-                uint32_t pay[2];
-                ok = poll_words<2>(qrec + static_cast<size_t>(e) * kQRecWords + kQRound2, P.tag, pay) && ok;
-                return f64_of(pay[0], pay[1]);
+        auto mass_of = [&](int e, bool sel, int& ng) {
+            ng = 0;
+            if (round2 && !sel) return sh.qm[e];
+            if (gper == 1) {
+                ng = ng1;
+                return (RESID && !sel) ? m1 : mST;
             }
             ItemRec q = own;
             if (e != r) ok = read_item_record(qrec + static_cast<size_t>(e) * kQRecWords, P.tag, q) && ok;
+            ng = q.n;
             return item_mass(q, dp.rho, RESID && !sel);
         };
+        int ngw = 0;
         double wsum = 0.0;
-        for (int e = e0; e < e1; ++e) wsum += mass_of(e, false);
+        for (int e = e0; e < e1; ++e) {
+            int ng;
+            wsum += mass_of(e, false, ng);
+            ngw = ng;
+        }
         double incl = wave_scan_dpp(wsum);
         double Z = lane63(incl);
         bool sel = false;
@@ -2302,36 +2363,44 @@ __device__ __forceinline__ void resample_body(const Params& P, int b, int r, con
             // none survives only through rounding: draw from p' instead.
             sel = true;
             wsum = 0.0;
-            for (int e = e0; e < e1; ++e) wsum += mass_of(e, true);
+            for (int e = e0; e < e1; ++e) {
+                int ng;
+                wsum += mass_of(e, true, ng);
+            }
             incl = wave_scan_dpp(wsum);
             Z = lane63(incl);
         }
         double pre = dpp_f64<kDppWaveShr1, 0xF>(incl);
         const double t = rp.u * Z;
-        int first = 0x7FFFFFFF, lastnz = -1;
+        int first = 0x7FFFFFFF, lastnz = -1, fng = 0, lng = 0;
         double pf = 0.0, pl = 0.0;
         for (int e = e0; e < e1; ++e) {
-            const double m = gper == 1 ? wsum : mass_of(e, sel);
+            int ng = ngw;
+            const double m = gper == 1 ? wsum : mass_of(e, sel, ng);
             if (m > 0.0) {
                 if (first == 0x7FFFFFFF && pre + m > t) {
                     first = e;
                     pf = pre;
+                    fng = ng;
                 }
                 lastnz = e;
                 pl = pre;
+                lng = ng;
             }
             pre += m;
         }
         const int fe = wave_min_int_dpp(first);
         const int le = wave_max_int_dpp(lastnz);
         double spre = 0.0;
-        int item = 0, last = 0;
+        int item = 0, last = 0, hng = 0;
         if (fe != 0x7FFFFFFF) {
             item = fe;
             spre = readlane_f64(pf, fe / gper);
+            hng = __shfl(fng, fe / gper, 64);
         } else if (le >= 0) {
             item = le;
             spre = readlane_f64(pl, le / gper);
+            hng = __shfl(lng, le / gper, 64);
             last = 1;
         }
         const bool allok = __ballot(!ok) == 0ull;
@@ -2343,37 +2412,141 @@ __device__ __forceinline__ void resample_body(const Params& P, int b, int r, con
             s_last = last;
             s_ok = allok ? 1 : 0;
             if (sel) s_mode = 1;
+            sh.whole = (round2 || sel || hng > 0) ? 1 : 0;
         }
     }
     __syncthreads();
     if (!s_ok) {
-        row_timed_out(P, b);
+        row_failed(P, b);
         return;
     }
-    if (s_item != r) return;
-
-    // 4. this item holds t.  Id order is run-major, then thread, then id.
-    const bool sel = s_mode == 1;
-    if (sel) item_exact_pass<DT, TOPP, RESID, R>(P, rowT, rowD, aligned, r, interior, dp, s_tab, true, s_A, s_B);
+    const int h = s_item;
     const double t = s_t;
-    // the mass of this thread's run k (the stash, with the first pass's
-    // sums: its ambiguous ids, now with the exact rho)
-    auto run_mass = [&](int k) {
-        if (!RESID || sel || round2) return s_A[k][tid];
-        double w = fma(-dp.rho, s_B[k][tid], s_A[k][tid]);
-        if (s.shas && s.srun == k) w += fmax(fma(-dp.rho, s.sD, s.sT), 0.0);
-        return w;
-    };
+    double* pr = P.probe_row ? P.probe_row + static_cast<size_t>(b) * 4 : nullptr;
+    // the verify step's token at position n, or an SMC particle's bonus
+    int32_t* outp = P.smc ? P.out_tokens + b : P.out_tokens + static_cast<size_t>(b) * (P.K + 1) + rn;
+    const bool sel = s_mode == 1;
+    const bool resid = RESID && !sel;
+    if (!sh.whole) {
+        // 5a. the (run, wave) of item h holding t, from its published sums in
+        // id order (run-major, then wave), then its kRun*64 ids, two per
+        // thread: their exact weights, a block scan, the token
+        if (tid < kKw) {
+            if (kwpre) {
+                sh.kw[tid] = sh.kwall[h * kKw + tid];
+            } else {
+                uint32_t w[2];
+                if (!poll_words<2>(qrec + static_cast<size_t>(h) * kQRecWords + kQKw + 2 * tid, P.tag, w)) s_ok = 0;
+                sh.kw[tid] = f64_of(w[0], w[1]);
+            }
+        }
+        __syncthreads();
+        if (!s_ok) {
+            row_failed(P, b);
+            return;
+        }
+        if (tid == 0) {
+            double base = s_pre;
+            int hk = -1, hw = -1, lk = -1, lw = -1;
+            double hoff = 0.0, loff = 0.0;
+            for (int k = 0; k < R; ++k)
+                for (int w2 = 0; w2 < kWaves; ++w2) {
+                    const double a = sh.kw[k * kWaves + w2];
+                    const double tot = resid ? fma(-dp.rho, sh.kw[(R + k) * kWaves + w2], a) : a;
+                    if (tot > 0.0) {
+                        if (hk < 0 && !s_last && base + tot > t) {
+                            hk = k;
+                            hw = w2;
+                            hoff = base;
+                        }
+                        lk = k;
+                        lw = w2;
+                        loff = base;
+                    }
+                    base += tot;
+                }
+            if (hk < 0) {
+                hk = lk;
+                hw = lw;
+                hoff = loff;
+                s_last = 1;
+            }
+            s_hk = hk;
+            s_hw = hw;
+            s_hoff = hoff;
+        }
+        __syncthreads();
+        const int hk = s_hk, hw = s_hw;
+        if (hk < 0) {
+            // no (run, wave) of the item has mass (cannot happen for the
+            // holding item): its first id
+            if (tid == 0) *outp = static_cast<int>(static_cast<int64_t>(h) * (R * kRunIds));
+            return;
+        }
+        const int64_t id0 = static_cast<int64_t>(h) * (R * kRunIds) + static_cast<int64_t>(hk) * kRunIds +
+                            static_cast<int64_t>(hw) * (64 * kRun) + 2 * tid;
+        double w2v[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int64_t id = id0 + i;
+            float lt = -SV_INF, ld = -SV_INF;
+            if (id < P.V) {
+                lt = load_logit<DT>(rowT, id);
+                if (resid) ld = load_logit<DT>(rowD, id);
+            }
+            double eT, eD;
+            if (resid) {
+                id_exps<TOPP, true>(lt, ld, static_cast<int>(id), dp, s_tab, eT, eD);
+                w2v[i] = fmax(fma(-dp.rho, eD, eT), 0.0);
+            } else {
+                id_exps<TOPP, false>(lt, 0.f, static_cast<int>(id), dp, s_tab, eT, eD);
+                w2v[i] = eT;
+            }
+        }
+        const double mine = w2v[0] + w2v[1];
+        double incl, excl, total;
+        block_scan(mine, incl, excl, total);
+        const bool last = s_last != 0;
+        const int cross = block_min_int((mine > 0.0 && !last && s_hoff + incl > t) ? tid : 0x7FFFFFFF);
+        int who = cross;
+        bool lastmode = last;
+        if (cross == 0x7FFFFFFF) {
+            // past the (run, wave)'s total (rounding, or t beyond every
+            // item): the last id with mass
+            who = block_max_int(mine > 0.0 ? tid : -1);
+            lastmode = true;
+        }
+        if (tid == who) {
+            int y;
+            if (lastmode) {
+                y = static_cast<int>(w2v[1] > 0.0 ? id0 + 1 : id0);
+            } else {
+                const double run0 = s_hoff + excl;
+                y = static_cast<int>((w2v[0] > 0.0 && run0 + w2v[0] > t) || !(w2v[1] > 0.0) ? id0 : id0 + 1);
+            }
+            *outp = y;
+            if (pr) {
+                // Z and t in units of p' (the target's kept mass ST)
+                pr[0] = s_Z / s_ST;
+                pr[1] = t / s_ST;
+            }
+        }
+        if (who < 0 && tid == 0) *outp = static_cast<int>(id0);
+        return;
+    }
+
+    // 5b. the holding item recomputed whole (a second round, the draw from
+    // p', or ambiguous ids in it): exact weights per (run, thread), then the
+    // (run, wave), the lane and its run's ids in order.
+    const bool interior_h = static_cast<int64_t>(h + 1) * (R * kRunIds) <= P.V;
+    item_exact_pass<DT, TOPP, RESID, R>(P, rowT, rowD, aligned, h, interior_h, dp, s_tab, sel, s_A, s_B);
 #pragma unroll
     for (int k = 0; k < R; ++k) {
-        const double wik = wave_scan_dpp(run_mass(k));
+        const double wik = wave_scan_dpp(s_A[k][tid]);
         if (lane == 63) s_wt[k][wv] = wik;
     }
     __syncthreads();
     if (tid == 0) {
-        // the (run, wave) holding t, from the R*4 totals in id order; past
-        // the item's total (rounding, or t beyond every item: s_last), the
-        // last (run, wave) with mass
         double base = s_pre;
         int hk = -1, hw = -1, lk = -1, lw = -1;
         double hoff = 0.0, loff = 0.0;
@@ -2404,33 +2577,25 @@ __device__ __forceinline__ void resample_body(const Params& P, int b, int r, con
     }
     __syncthreads();
     const int hk = s_hk, hw = s_hw;
-    double* pr = P.probe_row ? P.probe_row + static_cast<size_t>(b) * 4 : nullptr;
-    // the verify step's token at position n, or an SMC particle's bonus
-    int32_t* outp = P.smc ? P.out_tokens + b : P.out_tokens + static_cast<size_t>(b) * (P.K + 1) + rn;
     if (hk < 0) {
-        // no id of the item has mass (cannot happen for the holding item)
-        if (tid == 0) *outp = static_cast<int>(item_run_id0<R>(r, 0));
+        if (tid == 0) *outp = static_cast<int>(item_run_id0<R>(h, 0));
         return;
     }
     if (wv != hw) return;
     // wave hw: the first lane of run hk whose inclusive prefix passes t (or
     // the last lane with mass)
-    const double myx = run_mass(hk);
+    const double myx = s_A[hk][tid];
     const double incl = s_hoff + wave_scan_dpp(myx);
     bool last = s_last != 0;
     unsigned long long hm = __ballot(myx > 0.0 && (last || incl > t));
     if (hm == 0ull) {
-        // rounding: the wave's total passed t, no lane's prefix does
         last = true;
         hm = __ballot(myx > 0.0);
     }
     const int hl = last ? 63 - __clzll(static_cast<long long>(hm)) : __ffsll(static_cast<long long>(hm)) - 1;
     if (lane == hl) {
-        // a row some item gave up on keeps its sentinel
-        const bool dead = has_tag(ld_agent(row_flag(P, b)), P.tag);
         // this thread's run hk: its ids' weights again, exactly as summed
-        const int64_t id0 = item_run_id0<R>(r, hk);
-        const bool resid = RESID && !sel;
+        const int64_t id0 = item_run_id0<R>(h, hk);
         uint4 vt[ItemRaw<DT, 1>::NVR], vd[ItemRaw<DT, 1>::NVR];
         issue_run<DT>(rowT, id0, P.V, aligned, vt);
         if (resid) issue_run<DT>(rowD, id0, P.V, aligned, vd);
@@ -2459,9 +2624,8 @@ __device__ __forceinline__ void resample_body(const Params& P, int b, int r, con
             }
             run += wi;
         }
-        if (!dead) *outp = y >= 0 ? y : (lastw >= 0 ? lastw : static_cast<int>(id0));
-        if (pr && !dead) {
-            // Z and t in units of p' (the target's kept mass ST)
+        *outp = y >= 0 ? y : (lastw >= 0 ? lastw : static_cast<int>(id0));
+        if (pr) {
             pr[0] = s_Z / s_ST;
             pr[1] = t / s_ST;
         }
@@ -3235,30 +3399,6 @@ hipError_t launch_greedy_rows(const Params& p, int dtype, hipStream_t s, const L
 hipError_t launch_smc_resample(const Params& p, hipStream_t s, const LaunchEvents& ev) {
     launch(k_smc_resample, 1u, kThreads, s, ev, p);
     return hipGetLastError();
-}
-
-// Resident workgroups per CU of the row pass (or the SMC particle pass) for
-// a dtype, top-p flag and run count; 0 if the runtime cannot tell.
-template <int R>
-static int rows_blocks_r(int dtype, bool topp, bool smc) {
-    int n = 0;
-    hipError_t e;
-    if (smc) {
-        e = dtype == DT_BF16 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_smc_rows<DT_BF16, R>, kThreads, 0)
-                             : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_smc_rows<DT_F32, R>, kThreads, 0);
-    } else if (dtype == DT_BF16) {
-        e = topp ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_rows<DT_BF16, true, R>, kThreads, 0)
-                 : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_rows<DT_BF16, false, R>, kThreads, 0);
-    } else {
-        e = topp ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_rows<DT_F32, true, R>, kThreads, 0)
-                 : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_rows<DT_F32, false, R>, kThreads, 0);
-    }
-    return e == hipSuccess ? n : 0;
-}
-int rows_blocks_per_cu(int dtype, bool topp, bool smc, int runs) {
-    if (runs == 1) return rows_blocks_r<1>(dtype, topp, smc);
-    if (runs == 2) return rows_blocks_r<2>(dtype, topp, smc);
-    return rows_blocks_r<kRunsMax>(dtype, topp, smc);
 }
 
 hipError_t launch_rows(const Params& p, int dtype, bool topp, hipStream_t s, const LaunchEvents& ev) {

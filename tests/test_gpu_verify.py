@@ -349,22 +349,33 @@ def test_large_vocabulary(top_p):
         _parity(W.make_inputs(cfg, 200 + step, B=6, V=262147), label=f"V=262147 top_p={top_p} step {step}")
 
 
+@pytest.mark.parametrize("band", ["0", "1e-3", "0.05"])
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_draw_paths_second_round_and_groups(cfg, band, monkeypatch):
+    """The exact draw through its rarer paths, forced by SPECVERIFY_AMB_BAND
+    (the assumed relative error of the earlier passes' kept-mass ratio):
+    0 sends every row to the second round (the row's last item recomputes
+    every item's exact mass), 1e-3 leaves ambiguous groups of equal d in many
+    items (a holding item with groups is recomputed whole), 0.05 overflows
+    the groups (second round again).  The draw is exact on every path."""
+    monkeypatch.setenv("SPECVERIFY_AMB_BAND", band)
+    for step in range(2):
+        inp = W.make_inputs(cfg, 300 + step, B=12, V=30011)
+        _parity(inp, label=f"cfg {cfg} SPECVERIFY_AMB_BAND={band}")
+
+
 @pytest.mark.parametrize("dtype,top_p", [("bf16", 1.0), ("f32", 1.0), ("bf16", 0.9)])
 def test_largest_accepted_vocabulary(dtype, top_p):
-    """The largest vocabularies the row pass accepts: a row's workgroups wait
-    for one another, so the library sizes them to take at most a quarter of
-    the device's resident row-pass slots (four calls may run at once).  In
-    bf16 that reaches V = 2^21 (256 items of 8192 ids at four workgroups per
-    CU); float32 items and the top-p variant need more registers (three per
-    CU), so they stop at 192 items, V = 1.5 * 2^20, and V = 2^21 is refused
-    with SV_ESHAPE."""
-    full = dtype == "bf16" and top_p == 1.0
-    V = 1 << 21 if full else 3 << 19
+    """The largest vocabulary, V = 2^21: 256 row-pass items per row (1024 in
+    the one-run items of a small batch), whose last arrival finishes the
+    draw; no item waits for another, so no residency limit applies.  One
+    more id is refused with SV_ESHAPE."""
+    V = 1 << 21
     inp = W.synthetic(4, 2, V, dtype=dtype, temperature=0.7, top_p=top_p, seed=90 + int(top_p * 10),
                       gen_seed=V + (dtype == "f32"))
     _parity(inp, label=f"V={V} {dtype} top_p={top_p}")
-    if not full:
-        big = W.synthetic(2, 2, 1 << 21, dtype=dtype, temperature=0.7, top_p=top_p, seed=91, gen_seed=91)
+    if dtype == "f32":
+        big = W.synthetic(1, 1, V + 1, dtype="f32", temperature=0.7, seed=91, gen_seed=91)
         with pytest.raises(binding.SpecVerifyError) as err:
             run_gpu(big)
         assert err.value.status == -2

@@ -276,6 +276,8 @@ int plan(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_tokens, 
     const int nq = greedy ? 0 : (V + runs * sv::kRunIds - 1) / (runs * sv::kRunIds);
     const int64_t per_row = static_cast<int64_t>(nslot) * nch + nq;
     if (static_cast<int64_t>(B) * per_row >= (1ll << 31)) return SV_ESHAPE;
+    // the statistics kernel clears the row pass's records, a few words each
+    if (static_cast<int64_t>(sv::kQRecWords) * nq > static_cast<int64_t>(sv::kThreads) * nslot * nch) return SV_ESHAPE;
 
     // greedy verify takes its argmaxes and top-k from the candidate lists
     const bool topp = top_p < 1.f || greedy;

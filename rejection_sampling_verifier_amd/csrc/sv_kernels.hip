@@ -822,9 +822,18 @@ __device__ __forceinline__ void stats_item(const Params& P, int b, int slot, int
 template <int DT, int U, bool CAND>
 __global__ __launch_bounds__(kThreads, 8) void k_stats(Params P) {
     const int item = blockIdx.x;
-    // the row pass's arrival count of batch row `item` starts at 0 (the grid
-    // has at least B workgroups)
-    if (threadIdx.x == 0 && item < P.B && P.nq > 0) P.qrec[static_cast<size_t>(item) * P.nq * kQRecWords + kQCnt] = 0ull;
+    {
+        // clear this call's row-pass records (the arrival counts with them):
+        // the row pass reads them within its own kernel, where a record left
+        // by an earlier call under the same tag (a replayed graph) would pass
+        // for this call's (words [item*per, (item+1)*per), per <= kThreads by
+        // the host)
+        const int64_t words = static_cast<int64_t>(P.B) * P.nq * kQRecWords;
+        const int64_t grid = static_cast<int64_t>(P.B) * P.nslot * P.nch;
+        const int per = static_cast<int>((words + grid - 1) / grid);
+        const int64_t e = static_cast<int64_t>(item) * per + threadIdx.x;
+        if (static_cast<int>(threadIdx.x) < per && e < words) P.qrec[e] = 0ull;
+    }
     const int rvi = item / P.nch;
     const int chunk = item - rvi * P.nch;
     const int b = rvi / P.nslot;
@@ -2078,9 +2087,10 @@ __device__ __forceinline__ void row_failed(const Params& P, int b) {
 }
 
 // Arrival of one item of a row at the row's count, which the statistics
-// kernel of the call set to 0 (relaxed: the records are tagged words, which
-// the winner polls for).  True for the item that completes the count.  One
-// atomic add per item: no retries under contention.
+// kernel of the call cleared with the records (relaxed: the records are
+// tagged words, which the winner polls for).  True for the item that
+// completes the count.  One atomic add per item: no retries under
+// contention.
 __device__ __forceinline__ bool row_arrive(uint64_t* cnt, int nq) {
     const uint64_t old = __hip_atomic_fetch_add(cnt, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return old + 1u == static_cast<uint64_t>(nq);

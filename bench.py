@@ -94,7 +94,7 @@ def cpu_baseline_smc(sets, budget_particles, workload_name):
     """The SMC oracle on sub-batches of 4 particles (each a valid step)."""
     global _SAMPLE
     _SAMPLE = sets
-    cores = max(1, min(16, os.cpu_count() or 1))
+    cores = max(1, min(POOL, os.cpu_count() or 1))
     work, n = [], 0
     for si, inp in enumerate(sets):
         for i0 in range(0, inp.B, 4):
@@ -114,10 +114,29 @@ def cpu_baseline_smc(sets, budget_particles, workload_name):
     }
 
 
+def host_cpu():
+    """The host's CPU model and logical CPU count."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, os.cpu_count() or 1
+
+
+# worker processes of the oracle pool: the GPU box's CPU share is 16
+POOL = 16
+
+
 def cpu_baseline(sets, budget_rows, workload_name):
     global _SAMPLE
     _SAMPLE = sets
-    cores = max(1, min(16, os.cpu_count() or 1))
+    model, logical = host_cpu()
+    cores = max(1, min(POOL, logical))
     work = []
     n = 0
     for si, inp in enumerate(sets):
@@ -127,30 +146,80 @@ def cpu_baseline(sets, budget_rows, workload_name):
             work.append((si, [b]))
             n += 1
     positions, dt, passes = _timed_passes(_oracle_rows, work, cores)
+    # one worker on a sixteenth of the sample: the single-core rate
+    p1, dt1, passes1 = _timed_passes(_oracle_rows, work[: max(1, len(work) // 16)], 1, wall=CPU_WALL_S)
     return {
         "value": positions / dt,
         "unit": "positions/s",
         "cores": cores,
         "kind": "oracle",
+        "value_1_worker": p1 / dt1,
+        "host_cpu": model,
+        "host_logical_cpus": logical,
         "sample": f"{len(work)} batch rows of the {workload_name} workload, {passes} passes ({positions} draft "
-                  f"positions), float64 NumPy oracle, one row per task over {cores} processes, {dt:.1f} s wall",
+                  f"positions), float64 NumPy oracle, one row per task over {cores} processes, {dt:.1f} s wall; "
+                  f"one process: {len(work[: max(1, len(work) // 16)])} rows, {passes1} passes ({p1} positions), "
+                  f"{dt1:.1f} s",
     }
 
 
 CPU_WALL_S = 1.5  # about 10-30 s of CPU work over the pool
 
 
-def _timed_passes(fn, work, cores):
+def _timed_passes(fn, work, cores, wall=None):
     """Passes over the sample until CPU_WALL_S of wall time (at most 20)."""
+    wall = CPU_WALL_S if wall is None else wall
     ctx = mp.get_context("fork")
     positions, passes = 0, 0
     with ctx.Pool(cores) as pool:
         t0 = time.perf_counter()
-        while passes < 20 and (passes == 0 or time.perf_counter() - t0 < CPU_WALL_S):
+        while passes < 20 and (passes == 0 or time.perf_counter() - t0 < wall):
             positions += sum(pool.map(fn, work, chunksize=1))
             passes += 1
         dt = time.perf_counter() - t0
     return positions, dt, passes
+
+
+# ---------------------------------------------------------------------------
+# GPU clocks and the per-call distribution
+# ---------------------------------------------------------------------------
+WARMUP_SPIN_S = 0.3
+
+
+def device_warmup(binding, torch, dev, dsets):
+    """Streams the input sets with the streaming-read kernel for about
+    WARMUP_SPIN_S so that the clocks reach their steady state before the
+    warmup steps (an idle GPU runs its first tens of milliseconds slower);
+    no verify call is made."""
+    sink = torch.empty(1024, dtype=torch.int32, device=dev)
+    bufs = [t for ds in dsets for t in ds[:2]]
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < WARMUP_SPIN_S:
+        for b in bufs:
+            binding.stream_read(b, sink, unroll=8)
+            n += 1
+        torch.cuda.synchronize()
+    print(f"[bench] device warm-up: {n} streaming reads in {time.perf_counter() - t0:.2f} s", file=sys.stderr,
+          flush=True)
+
+
+def per_call_distribution(torch, stream, step, n):
+    """Each of n more calls between its own pair of events on the launch
+    stream: median, p10 and p90 of the per-call times (the events sit between
+    calls, not inside them)."""
+    import numpy as np
+
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for i in range(n):
+        evs[i][0].record(stream)
+        step(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) * 1e3 for a, b in evs])
+    return {"median_us": round(float(np.median(us)), 3), "p10_us": round(float(np.percentile(us, 10)), 3),
+            "p90_us": round(float(np.percentile(us, 90)), 3), "calls": n}
 
 
 # ---------------------------------------------------------------------------
@@ -272,7 +341,7 @@ def smc_bench(args, binding, torch, dev, sets, dsets, logical, stream):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f32+f64",
         "data": "synthetic",
         "config": {"workload": f"SMC-SD step over the {sets[0].workload.name} inputs as {N} particles",
                    "N": N, "K": K, "V": sets[0].V, "ess_fraction": SMC_ESS_FRACTION,
@@ -283,6 +352,7 @@ def smc_bench(args, binding, torch, dev, sets, dsets, logical, stream):
                      "kernel": "k_stats (statistics pass)", "kernel_us": round(us["stats"], 3),
                      "other_kernels_us": {"k_smc_rows": round(us["rows"], 3),
                                           "k_smc_resample": round(us["smc"], 3)}},
+        "per_call": dist,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -388,6 +458,7 @@ def greedy_bench(args, binding, torch, dev, sets):
                      "unit": "GB/s", "frac": round(logical / stats_s / 1e9 / HBM_PEAK_GBS, 4), "traffic": None,
                      "kernel": "k_stats<…, true> over the target rows", "kernel_us": round(us["stats"], 3),
                      "other_kernels_us": {"k_greedy_rows": round(us["rows"], 3)}},
+        "per_call": dist,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -556,6 +627,7 @@ def overlap_bench(args, binding, torch, dev, sets):
         "kernels_us": kus,
         "graph_replay_matches_eager": replay_ok,
         "producer_GBps_alone": round(prod_bytes / (us["produce"] * 1e-6) / 1e9, 1),
+        "per_call": dist,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -649,13 +721,14 @@ def hispec_bench(args, binding, torch, dev):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f32+f64",
         "data": "synthetic",
         "config": {"workload": "two-stage verify B=64 K=5 V=128256 bf16 T=0.7 (final, intermediate, draft layers)",
                    "B": B, "K": K, "V": V, "logical_bytes_per_step": logical,
                    "logits_GBps": round(logical / (ms_step / 1e3) / 1e9, 1),
                    "logits_frac_of_peak": round(logical / (ms_step / 1e3) / 1e9 / HBM_PEAK_GBS, 4)},
         "kernels_us": {"k_stats (per stage)": round(us["stats"], 3), "k_rows (per stage)": round(us["rows"], 3)},
+        "per_call": dist,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -745,6 +818,7 @@ def main():
         binding.verify(t, d, x, dl, T, tp, seed, stream=stream, out_tokens=o[0],
                        out_n_accepted=o[1])
 
+    device_warmup(binding, torch, dev, dsets)
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for i in range(args.warmup):
         step(i)
@@ -762,6 +836,9 @@ def main():
     ms_total = ev0.elapsed_time(ev1)
     ms_step = ms_total / args.steps
     print(f"[bench] {args.steps} steps: {ms_step * 1e3:.2f} us/step", file=sys.stderr, flush=True)
+    dist = per_call_distribution(torch, stream, step, args.steps)
+    print(f"[bench] per call: median {dist['median_us']} us, p10 {dist['p10_us']}, p90 {dist['p90_us']}",
+          file=sys.stderr, flush=True)
 
     # timed region 2: per-kernel HIP events recorded by the library on the
     # launch stream around every kernel
@@ -779,6 +856,7 @@ def main():
     achieved = logical / stats_avg_s / 1e9
     print(f"[bench] statistics kernel {stats_ms / max(stats_n, 1) * 1e3:.2f} us, row kernel "
           f"{res_ms / max(res_n, 1) * 1e3:.2f} us ({stats_n} launches)", file=sys.stderr, flush=True)
+    kernels_sum_us = (stats_ms + res_ms + prof["topp"][0]) / max(stats_n, 1) * 1e3
 
     # timed region 3 (--two-batches): the same calls with two independent
     # batches in flight (calls alternate between two streams, nothing orders
@@ -829,6 +907,8 @@ def main():
         "traffic": traffic,
         "kernel": "k_stats (statistics pass: every needed logit row read once)",
         "kernel_us": round(stats_avg_s * 1e6, 3),
+        "kernels_sum_us": round(kernels_sum_us, 3),
+        "timing": "per-dispatch HIP events on the launch stream over a second region of the same calls",
         "other_kernels_us": dict({"k_rows": round(res_ms / max(res_n, 1) * 1e3, 3)},
                                  **({"k_topp": round(prof["topp"][0] / prof["topp"][1] * 1e3, 3)}
                                     if prof["topp"][1] else {})),
@@ -857,13 +937,14 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f32+f64",
         "data": "synthetic",
         "config": {
             "workload": w.name,
             "B": B, "K": K, "V": sets[0].V, "temperature": float(sets[0].temperature),
             "top_p": float(sets[0].top_p), "logits_dtype": w.dtype,
-            "arithmetic": "fp32 per element (exp2, weights), fp64 for merges, masses and decisions",
+            "arithmetic": "statistics pass: fp32 exp2 and lane/wave sums, fp64 merges; decisions fp64; the draw "
+                          "fp64 throughout (exponentials, normalisers, masses)",
             "logical_bytes_per_step": logical,
             "positions_per_step": positions,
             "logits_GBps": round(logical / (ms_step / 1e3) / 1e9, 1),
@@ -872,6 +953,7 @@ def main():
             "parallelism": "single GPU",
         },
         "roofline": roofline,
+        "per_call": dist,
         "cpu_baseline": cpu,
         **({"two_batches_in_flight": two} if two else {}),
         **({"calibration": calib} if calib else {}),

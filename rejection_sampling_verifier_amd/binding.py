@@ -18,7 +18,7 @@ SV_F32, SV_BF16 = 0, 1
 PROBE_POS, PROBE_ROW = 8, 4
 STATUS = {0: "SV_OK", -1: "SV_EINVAL", -2: "SV_ESHAPE", -3: "SV_EDTYPE", -4: "SV_EHIP", -5: "SV_ENOMEM",
           -6: "SV_EALIGN", -7: "SV_ECAPTURE", -8: "SV_ETOOBIG"}
-KERNEL_KINDS = ("stats", "topp", "rows", "smc", "produce", "fused")
+KERNEL_KINDS = ("stats", "topp", "rows", "smc", "produce")
 
 EXPORTS = ("spec_verify", "spec_verify_noalloc", "spec_verify_probe", "spec_greedy_verify", "spec_hispec_verify", "spec_smc_step",
            "spec_draft_produce",

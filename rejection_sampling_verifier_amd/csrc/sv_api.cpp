@@ -2,6 +2,7 @@
 // kernel dispatch and optional per-kernel timing.  The operation itself is
 // described in include/specverify.h.
 
+#include <algorithm>
 #include <atomic>
 #include <cfloat>
 #include <cmath>

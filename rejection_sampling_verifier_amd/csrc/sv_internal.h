@@ -19,6 +19,7 @@ constexpr int kRunIds = kThreads * kRun;  // ids per run of an item (2048)
 constexpr int kRecWords = 4;         // 64-bit words per tagged statistics record
 constexpr int kQRecWords = 88;       // 64-bit words per row-pass item record
 constexpr int kQCnt = 21;            // word of item 0's record: the row's arrival count
+constexpr int kQMass = 22;           // word of an item's record: its exact mass in a second round
 constexpr int kMaxV = 1 << 21;       // largest vocabulary of the sampling entry points
 constexpr int kCand = 256;           // nucleus candidates a statistics chunk lists at most
 constexpr int kMaxTopK = 64;         // greedy verify: largest top-k

@@ -280,11 +280,11 @@ __device__ __forceinline__ void combine_partials(const Params& P, int b, int slo
 // records (the statistics kernel has finished).  The workgroup loads up to
 // kThreads records at once, stages them in LDS, and wave w merges logit rows
 // w, w+4, ... (chunk order within a lane, then a fixed wave tree, then pass
-// order).  Every thread must call it (it ends with a barrier).
+// order).  Every thread must call it (it ends with a barrier); `stage` is
+// kThreads entries of LDS.
 constexpr int kLaneMergeMax = 32;  // chunks per logit row merged by one lane
 static_assert(2 * kMaxK + 1 <= 64, "one lane per logit row");
-__device__ __forceinline__ void fill_row_from_partials(const Params& P, int b, int Le, RowShared& R) {
-    __shared__ Partial stage[kThreads];
+__device__ __forceinline__ void fill_row_from_partials(const Params& P, int b, int Le, RowShared& R, Partial* stage) {
     __shared__ int stage_bad;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int nrv = 2 * Le + 1, nch = P.nch;
@@ -1844,6 +1844,7 @@ struct DrawParam {
     float tvT, tvD;            // nucleus bounds (top-p)
     int32_t cutT, cutD;
     double dstar, delta;       // classification of residual ids (see above)
+    float dlo, dhi;            // the float32 band of d = lT - lD holding [d~* - Delta, d~* + Delta]
     double rho;                // exact ST/SD, known after the exchange
 };
 __device__ __forceinline__ double sgpr_f64(double v) {
@@ -1877,19 +1878,6 @@ __device__ __forceinline__ void id_exps(float lt, float ld, int id, const DrawPa
     if (RESID) {
         eD = exp2_f64(fma(static_cast<double>(ld), dp.c, -dp.oD), tab);
         if (TOPP && !kept_l(ld, dp.tvD, id, dp.cutD)) eD = 0.0;
-    }
-}
-
-template <int DT, int R>
-__device__ __forceinline__ void unpack_item_run(const Params& P, const ItemRaw<DT, R>& raw, int r, int k, bool interior,
-                                                bool resid, float* lt, float* ld) {
-    const int64_t id0 = item_run_id0<R>(r, k);
-    if (interior) {
-        unpack_run<DT>(raw.t[k], lt);
-        if (resid) unpack_run<DT>(raw.d[k], ld);
-    } else {
-        unpack_masked<DT>(raw.t[k], id0, P.V, lt);
-        if (resid) unpack_masked<DT>(raw.d[k], id0, P.V, ld);
     }
 }
 
@@ -1932,10 +1920,10 @@ __device__ __forceinline__ void for_item_runs(const Params& P, const uint8_t* ro
     }
 }
 
-// Per-thread sums of one item's first pass (rho~ classification); the
-// per-run sums A and B of the thread go to LDS (sA[k][tid], sB[k][tid]).
+// Per-thread sums of one item's first pass (rho~ classification); its sums
+// per (run, wave) go to LDS (kwA[k][w], kwB[k][w]).
 struct ItemSums {
-    double ST, SD;          // all ids
+    double ST, SD, A, B;    // all ids; the ids certainly in the residual
     double sT, sD, skey;    // one stashed group of ambiguous ids (equal d, run srun)
     int srun;
     bool shas, sover;
@@ -1944,13 +1932,15 @@ struct ItemSums {
 template <int DT, bool TOPP, bool RESID, int R>
 __device__ __forceinline__ void item_first_pass(const Params& P, const uint8_t* rowT, const uint8_t* rowD, bool aligned,
                                                 int r, bool interior, const DrawParam& dp, const double* tab,
-                                                double (*sA)[kThreads], double (*sB)[kThreads], ItemSums& s) {
+                                                double (*kwA)[kWaves], double (*kwB)[kWaves], ItemSums& s) {
     s.ST = 0.0;
     s.SD = 0.0;
+    s.A = 0.0;
+    s.B = 0.0;
     s.sT = s.sD = s.skey = 0.0;
     s.srun = -1;
     s.shas = s.sover = false;
-    const int tid = threadIdx.x;
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     for_item_runs<DT, R, RESID>(P, rowT, rowD, aligned, r, interior, [&](int k, float* lt, float* ld, int i0) {
         double a = 0.0, bsum = 0.0;
 #pragma unroll
@@ -1966,17 +1956,21 @@ __device__ __forceinline__ void item_first_pass(const Params& P, const uint8_t* 
                 s.ST += eT[h];
                 if (RESID) {
                     s.SD += eD[h];
-                    // w > 0 iff d > d*: certain beyond Delta of d~*; an id
-                    // outside the draft nucleus (eD = 0) keeps eT, one outside
-                    // the target's (eT = 0) has none
-                    const double key = static_cast<double>(lt[i + h]) - static_cast<double>(ld[i + h]);
-                    const double dd = key - dp.dstar;
+                    // w > 0 iff d = lT - lD > d*: certain outside the float32
+                    // band [dlo, dhi] around d~* (which holds Delta and the
+                    // rounding of lT - lD in float32); an id outside the draft
+                    // nucleus (eD = 0) keeps eT, one outside the target's
+                    // (eT = 0) has none
+                    const float d = lt[i + h] - ld[i + h];
                     const bool inT = eT[h] > 0.0;
-                    const bool in = inT && (eD[h] == 0.0 || dd > dp.delta);
+                    const bool in = inT && (eD[h] == 0.0 || d > dp.dhi);
                     const double m = in ? 1.0 : 0.0;
                     a = fma(m, eT[h], a);
                     bsum = fma(m, eD[h], bsum);
-                    if (inT && eD[h] > 0.0 && fabs(dd) <= dp.delta) {
+                    if (inT && eD[h] > 0.0 && d >= dp.dlo && d <= dp.dhi) {
+                        // within the band (rare): grouped by the exact d (one
+                        // group per thread, more flags an overflow)
+                        const double key = static_cast<double>(lt[i + h]) - static_cast<double>(ld[i + h]);
                         if (!s.shas) {
                             s.shas = true;
                             s.sT = eT[h];
@@ -1995,19 +1989,25 @@ __device__ __forceinline__ void item_first_pass(const Params& P, const uint8_t* 
                 }
             }
         }
-        sA[k][tid] = a;
-        sB[k][tid] = bsum;
+        s.A += a;
+        s.B += bsum;
+        const double wa = wave_sum_dpp(a);
+        const double wb = RESID ? wave_sum_dpp(bsum) : 0.0;
+        if (lane == 0) {
+            kwA[k][wv] = wa;
+            kwB[k][wv] = wb;
+        }
     });
 }
 
-// Per-run weight totals of a second, exact pass (rho known; `bonus`: w = eT,
-// the draw from p' when the residual vanished): sA[k][tid] = sum w over run
-// k, sB = 0.
+// Per-(run, wave) weight totals of a second, exact pass over item r (rho
+// known; `bonus`: w = eT, the draw from p' when the residual vanished):
+// kwA[k][w] = sum of w over run k's ids of wave w, kwB = 0.
 template <int DT, bool TOPP, bool RESID, int R>
 __device__ __forceinline__ void item_exact_pass(const Params& P, const uint8_t* rowT, const uint8_t* rowD, bool aligned,
                                                 int r, bool interior, const DrawParam& dp, const double* tab,
-                                                bool bonus, double (*sA)[kThreads], double (*sB)[kThreads]) {
-    const int tid = threadIdx.x;
+                                                bool bonus, double (*kwA)[kWaves], double (*kwB)[kWaves]) {
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
     auto body = [&](auto resid_c, int k, float* lt, float* ld, int i0) {
         constexpr bool RS = decltype(resid_c)::value;
         double a = 0.0;
@@ -2021,8 +2021,11 @@ __device__ __forceinline__ void item_exact_pass(const Params& P, const uint8_t* 
 #pragma unroll
             for (int h = 0; h < 2; ++h) a += RS ? fmax(fma(-dp.rho, eD[h], eT[h]), 0.0) : eT[h];
         }
-        sA[k][tid] = a;
-        sB[k][tid] = 0.0;
+        const double wa = wave_sum_dpp(a);
+        if (lane == 0) {
+            kwA[k][wv] = wa;
+            kwB[k][wv] = 0.0;
+        }
     };
     if (RESID && !bonus)
         for_item_runs<DT, R, true>(P, rowT, rowD, aligned, r, interior, [&](int k, float* lt, float* ld, int i0) {
@@ -2096,32 +2099,122 @@ __device__ __forceinline__ bool row_arrive(uint64_t* cnt, int nq) {
     return old + 1u == static_cast<uint64_t>(nq);
 }
 
-template <int R> struct DrawShared {
+// The draw's LDS (one instance per workgroup, shared by the residual and
+// bonus variants of the kernel).  kwall holds every item's published
+// per-(run, wave) sums when they fit (kKwPre doubles), the statistics
+// records staged by the decision before that.
+constexpr int kKwPre = 512;
+template <int DT, int R> struct DrawShared {
     double tab[kExpTab];
     double red[4][kWaves];
-    double wt[R][kWaves];
-    double A[R][kThreads], B[R][kThreads];  // per (run, thread) sums
+    double kwA[R][kWaves], kwB[R][kWaves];  // this item's sums per (run, wave)
+    double kw[2 * R * kWaves];              // the holding item's
+    union {
+        double kwall[kKwPre];
+        Partial stage[kThreads];
+    };
     int item, mode, ok, hk, hw, last, fin, whole;
     double pre, Z, t, rho, hoff, ST;
     // ambiguous groups of the item (key, GT, GD), their count and overflow
     double gkey[kAmbGroups], gT[kAmbGroups], gD[kAmbGroups];
     int gn, gover;
-    double kw[2 * R * kWaves];  // the holding item's per-(run, wave) sums
-    union {
-        double qm[kMaxItems];       // exact item masses (second round)
-        double kwall[kMaxItems];    // every item's per-(run, wave) sums, when they fit
-    };
 };
+static_assert(sizeof(Partial) * kThreads <= sizeof(double) * kKwPre, "stage fits the prefetch area");
+
+// The token of a run-wave: the kRun*64 ids of run k, wave w of item h, two
+// per thread, their exact weights, a block scan from `hoff` (the mass before
+// them), the first id whose running mass passes t (with `last`, or when
+// rounding leaves none, the last id with mass).  Every thread must call it;
+// returns the token (block-uniform) or -1 if no id has mass.
+template <int DT, bool TOPP, int R>
+__device__ __forceinline__ int pick_run_wave(const Params& P, const uint8_t* rowT, const uint8_t* rowD, int h, int k,
+                                             int w, double hoff, double t, bool last, bool resid,
+                                             const DrawParam& dp, const double* tab) {
+    __shared__ int s_y;
+    const int tid = threadIdx.x;
+    const int64_t id0 = static_cast<int64_t>(h) * (R * kRunIds) + static_cast<int64_t>(k) * kRunIds +
+                        static_cast<int64_t>(w) * (64 * kRun) + 2 * tid;
+    double wv2[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int64_t id = id0 + i;
+        float lt = -SV_INF, ld = -SV_INF;
+        if (id < P.V) {
+            lt = load_logit<DT>(rowT, id);
+            if (resid) ld = load_logit<DT>(rowD, id);
+        }
+        double eT, eD;
+        if (resid) {
+            id_exps<TOPP, true>(lt, ld, static_cast<int>(id), dp, tab, eT, eD);
+            wv2[i] = fmax(fma(-dp.rho, eD, eT), 0.0);
+        } else {
+            id_exps<TOPP, false>(lt, 0.f, static_cast<int>(id), dp, tab, eT, eD);
+            wv2[i] = eT;
+        }
+    }
+    const double mine = wv2[0] + wv2[1];
+    double incl, excl, total;
+    block_scan(mine, incl, excl, total);
+    const int cross = block_min_int((mine > 0.0 && !last && hoff + incl > t) ? tid : 0x7FFFFFFF);
+    int who = cross;
+    bool lastmode = last;
+    if (cross == 0x7FFFFFFF) {
+        who = block_max_int(mine > 0.0 ? tid : -1);
+        lastmode = true;
+    }
+    if (tid == 0) s_y = -1;
+    __syncthreads();
+    if (tid == who) {
+        int y;
+        if (lastmode) y = static_cast<int>(wv2[1] > 0.0 ? id0 + 1 : id0);
+        else y = static_cast<int>((wv2[0] > 0.0 && hoff + excl + wv2[0] > t) || !(wv2[1] > 0.0) ? id0 : id0 + 1);
+        s_y = y;
+    }
+    __syncthreads();
+    return s_y;
+}
+
+// The (run, wave) holding t among R*kWaves sums in id order (run-major,
+// then wave), from `base` (the mass before the item); past the item's total
+// (rounding, or `last`), the last one with mass.  One thread.
+template <int R>
+__device__ __forceinline__ void find_run_wave(const double* kA, const double* kB, double rho, bool resid, double base,
+                                              double t, int& last, int& hk, int& hw, double& hoff) {
+    hk = -1;
+    hw = -1;
+    int lk = -1, lw = -1;
+    double loff = 0.0;
+    hoff = 0.0;
+    for (int k = 0; k < R; ++k)
+        for (int w2 = 0; w2 < kWaves; ++w2) {
+            const double a = kA[k * kWaves + w2];
+            const double tot = resid ? fma(-rho, kB[k * kWaves + w2], a) : a;
+            if (tot > 0.0) {
+                if (hk < 0 && !last && base + tot > t) {
+                    hk = k;
+                    hw = w2;
+                    hoff = base;
+                }
+                lk = k;
+                lw = w2;
+                loff = base;
+            }
+            base += tot;
+        }
+    if (hk < 0) {
+        hk = lk;
+        hw = lw;
+        hoff = loff;
+        last = 1;
+    }
+}
 
 template <int DT, bool TOPP, bool RESID, int R>
 __device__ __forceinline__ void resample_body(const Params& P, int b, int r, const RowParam& rp, int rn,
-                                              DrawShared<R>* sh_) {
-    DrawShared<R>& sh = *sh_;
+                                              DrawShared<DT, R>* sh_) {
+    DrawShared<DT, R>& sh = *sh_;
     double* const s_tab = sh.tab;
     double (*const s_red)[kWaves] = sh.red;
-    double (*const s_wt)[kWaves] = sh.wt;
-    double (*const s_A)[kThreads] = sh.A;
-    double (*const s_B)[kThreads] = sh.B;
     int &s_item = sh.item, &s_mode = sh.mode, &s_ok = sh.ok, &s_hk = sh.hk, &s_hw = sh.hw, &s_last = sh.last;
     double &s_pre = sh.pre, &s_Z = sh.Z, &s_t = sh.t, &s_rho = sh.rho, &s_hoff = sh.hoff, &s_ST = sh.ST;
     double* const s_gkey = sh.gkey;
@@ -2132,9 +2225,10 @@ __device__ __forceinline__ void resample_body(const Params& P, int b, int r, con
     const uint8_t* rowT = row_ptr<DT>(P, true, b, rn);
     const uint8_t* rowD = RESID ? row_ptr<DT>(P, false, b, rn) : rowT;
     const bool aligned = ((reinterpret_cast<uintptr_t>(rowT) & 15) == 0) && ((reinterpret_cast<uintptr_t>(rowD) & 15) == 0);
-    const bool interior = static_cast<int64_t>(r + 1) * (R * kThreads * kRun) <= P.V;
+    const bool interior = static_cast<int64_t>(r + 1) * (R * kRunIds) <= P.V;
     const int nq = P.nq;
     uint64_t* qrec = P.qrec + static_cast<size_t>(b) * nq * kQRecWords;
+    constexpr int kKw = 2 * R * kWaves;
 
     DrawParam dp;
     dp.c = P.c64;
@@ -2147,6 +2241,8 @@ __device__ __forceinline__ void resample_body(const Params& P, int b, int r, con
     dp.rho = 0.0;
     dp.dstar = 0.0;
     dp.delta = 0.0;
+    dp.dlo = 0.f;
+    dp.dhi = 0.f;
     const double rtil = sgpr_f64(rp.keptT / rp.keptD);  // rho~
     if (RESID) {
         // d~* from rho~: eT > rho~ eD iff (lT - lD) c - oT + oD > log2 rho~;
@@ -2154,6 +2250,16 @@ __device__ __forceinline__ void resample_body(const Params& P, int b, int r, con
         // rounding of d and d~*
         dp.dstar = sgpr_f64((log2(rtil) + dp.oT - dp.oD) / dp.c);
         dp.delta = sgpr_f64(1.01 * P.amb_band / (dp.c * kLn2) + 1e-12 * (fabs(dp.dstar) + 1.0));
+        // d is taken in float32: lT - lD rounds once (relative error below
+        // 2^-24, below 2^-22 of |d~*| near the band), so the band widens by
+        // that much and rounds outward to float32
+        const double widen = dp.delta + fabs(dp.dstar) * 0x1p-22 + 1e-37;
+        const double lo = dp.dstar - widen, hi = dp.dstar + widen;
+        float flo = static_cast<float>(lo), fhi = static_cast<float>(hi);
+        if (static_cast<double>(flo) > lo) flo = nextafterf(flo, -SV_INF);
+        if (static_cast<double>(fhi) < hi) fhi = nextafterf(fhi, SV_INF);
+        dp.dlo = sgpr_f32(flo);
+        dp.dhi = sgpr_f32(fhi);
     }
     // (the exponential table was filled at the kernel's start)
     if (tid == 0) {
@@ -2162,30 +2268,13 @@ __device__ __forceinline__ void resample_body(const Params& P, int b, int r, con
     }
     __syncthreads();
 
-    // 1. the item's float64 sums (one pass over its ids)
+    // 1. the item's float64 sums (one pass over its ids); its sums per
+    // (run, wave) in LDS
     ItemSums s;
-    item_first_pass<DT, TOPP, RESID, R>(P, rowT, rowD, aligned, r, interior, dp, s_tab, s_A, s_B, s);
+    item_first_pass<DT, TOPP, RESID, R>(P, rowT, rowD, aligned, r, interior, dp, s_tab, sh.kwA, sh.kwB, s);
     {
-        // the item's totals, and its sums per (run, wave) straight to the
-        // record (lane 0 of each wave)
-        uint64_t* kw = qrec + static_cast<size_t>(r) * kQRecWords + kQKw;
-        double Aall = 0.0, Ball = 0.0;
-#pragma unroll
-        for (int k = 0; k < R; ++k) {
-            const double a = s_A[k][tid], bk = s_B[k][tid];
-            Aall += a;
-            Ball += bk;
-            const double wa = wave_sum_dpp(a);
-            const double wb = RESID ? wave_sum_dpp(bk) : 0.0;
-            if (lane < 4) {
-                // two tagged words per sum: A_kw, then B_kw
-                const double x = lane < 2 ? wa : wb;
-                const int slot = lane < 2 ? k * kWaves + wv : (R + k) * kWaves + wv;
-                st_agent(kw + 2 * slot + (lane & 1), tagged(P.tag, f64_word(x, lane & 1)));
-            }
-        }
         const double v0 = wave_sum_dpp(s.ST), v1 = wave_sum_dpp(s.SD);
-        const double v2 = wave_sum_dpp(Aall), v3 = wave_sum_dpp(Ball);
+        const double v2 = wave_sum_dpp(s.A), v3 = wave_sum_dpp(s.B);
         if (lane == 0) {
             s_red[0][wv] = v0;
             s_red[1][wv] = v1;
@@ -2238,7 +2327,8 @@ __device__ __forceinline__ void resample_body(const Params& P, int b, int r, con
         own.gD[g] = g < own.n ? s_gD[g] : 0.0;
     }
 
-    // 2. publish: the header, ST, SD, A, B, the groups
+    // 2. publish: the header, ST, SD, A, B, the groups, and the sums per
+    // (run, wave), all tagged (two words per float64)
     if (tid < kQHdr + 4 * own.n) {
         uint32_t v;
         if (tid == 0) {
@@ -2252,6 +2342,12 @@ __device__ __forceinline__ void resample_body(const Params& P, int b, int r, con
             v = f64_word(f == 0 ? s_gT[g] : s_gD[g], (tid - kQHdr) & 1);
         }
         st_agent(qrec + static_cast<size_t>(r) * kQRecWords + tid, tagged(P.tag, v));
+    }
+    if (tid >= 64 && tid < 64 + 2 * kKw) {
+        const int q = tid - 64, slot = q >> 1;
+        const double x = slot < R * kWaves ? sh.kwA[slot / kWaves][slot % kWaves]
+                                           : sh.kwB[(slot - R * kWaves) / kWaves][(slot - R * kWaves) % kWaves];
+        st_agent(qrec + static_cast<size_t>(r) * kQRecWords + kQKw + q, tagged(P.tag, f64_word(x, q & 1)));
     }
 
     // 3. arrival: the item that completes the row's count finishes the draw;
@@ -2268,22 +2364,20 @@ __device__ __forceinline__ void resample_body(const Params& P, int b, int r, con
 
     // 4. every item's record in id order (wave 0; lane l takes items
     // [l*g, (l+1)*g)): exact rho, the items' masses, Z, t = u*Z and the item
-    // holding t.
+    // holding t; the other waves meanwhile fetch every item's per-(run, wave)
+    // sums when they fit.
     const int gper = (nq + 63) / 64;
     const int e0 = min(lane * gper, nq), e1 = min(e0 + gper, nq);
-    // one item per lane (nq <= 64): its record is read once, and its masses
-    // kept once rho is known
-    double m1 = 0.0, mST = 0.0;
+    double m1 = 0.0, mST = 0.0;  // one item per lane: its masses once rho is known
     int ng1 = 0;
-    // the other waves meanwhile fetch every item's per-(run, wave) sums
-    constexpr int kKw = 2 * R * kWaves;
-    const bool kwpre = nq * kKw <= kMaxItems;
+    const bool kwpre = nq * kKw <= kKwPre;
     if (wv > 0 && kwpre) {
         bool okk = true;
         for (int i = tid - 64; i < nq * kKw; i += kThreads - 64) {
-            uint32_t w[2];
-            okk = poll_words<2>(qrec + static_cast<size_t>(i / kKw) * kQRecWords + kQKw + 2 * (i % kKw), P.tag, w) && okk;
-            sh.kwall[i] = f64_of(w[0], w[1]);
+            uint32_t w2[2];
+            okk = poll_words<2>(qrec + static_cast<size_t>(i / kKw) * kQRecWords + kQKw + 2 * (i % kKw), P.tag, w2) &&
+                  okk;
+            sh.kwall[i] = f64_of(w2[0], w2[1]);
         }
         if (!okk) s_ok = 0;
     }
@@ -2328,17 +2422,19 @@ __device__ __forceinline__ void resample_body(const Params& P, int b, int r, con
     const bool round2 = s_mode == 2;
     if (round2) {
         // some ids could not be classified against rho~ (rare): every item's
-        // exact mass, one item after another
+        // exact mass, one item after another, kept in its record's word
+        // kQMass (this workgroup writes and reads it)
         for (int e = 0; e < nq; ++e) {
             const bool in_e = static_cast<int64_t>(e + 1) * (R * kRunIds) <= P.V;
-            item_exact_pass<DT, TOPP, RESID, R>(P, rowT, rowD, aligned, e, in_e, dp, s_tab, false, s_A, s_B);
-            double w = 0.0;
-#pragma unroll
-            for (int k = 0; k < R; ++k) w += s_A[k][tid];
-            w = wave_sum_dpp(w);
-            if (lane == 0) s_red[0][wv] = w;
+            item_exact_pass<DT, TOPP, RESID, R>(P, rowT, rowD, aligned, e, in_e, dp, s_tab, false, sh.kwA, sh.kwB);
             __syncthreads();
-            if (tid == 0) sh.qm[e] = (s_red[0][0] + s_red[0][1]) + (s_red[0][2] + s_red[0][3]);
+            if (tid == 0) {
+                double w = 0.0;
+                for (int k = 0; k < R; ++k)
+                    for (int w2 = 0; w2 < kWaves; ++w2) w += sh.kwA[k][w2];
+                st_agent(qrec + static_cast<size_t>(e) * kQRecWords + kQMass,
+                         static_cast<uint64_t>(__double_as_longlong(w)));
+            }
             __syncthreads();
         }
     }
@@ -2348,7 +2444,9 @@ __device__ __forceinline__ void resample_body(const Params& P, int b, int r, con
         bool ok = true;
         auto mass_of = [&](int e, bool sel, int& ng) {
             ng = 0;
-            if (round2 && !sel) return sh.qm[e];
+            if (round2 && !sel)
+                return __longlong_as_double(
+                    static_cast<long long>(ld_agent(qrec + static_cast<size_t>(e) * kQRecWords + kQMass)));
             if (gper == 1) {
                 ng = ng1;
                 return (RESID && !sel) ? m1 : mST;
@@ -2432,210 +2530,58 @@ __device__ __forceinline__ void resample_body(const Params& P, int b, int r, con
     }
     const int h = s_item;
     const double t = s_t;
-    double* pr = P.probe_row ? P.probe_row + static_cast<size_t>(b) * 4 : nullptr;
-    // the verify step's token at position n, or an SMC particle's bonus
-    int32_t* outp = P.smc ? P.out_tokens + b : P.out_tokens + static_cast<size_t>(b) * (P.K + 1) + rn;
     const bool sel = s_mode == 1;
     const bool resid = RESID && !sel;
-    if (!sh.whole) {
-        // 5a. the (run, wave) of item h holding t, from its published sums in
-        // id order (run-major, then wave), then its kRun*64 ids, two per
-        // thread: their exact weights, a block scan, the token
-        if (tid < kKw) {
-            if (kwpre) {
-                sh.kw[tid] = sh.kwall[h * kKw + tid];
-            } else {
-                uint32_t w[2];
-                if (!poll_words<2>(qrec + static_cast<size_t>(h) * kQRecWords + kQKw + 2 * tid, P.tag, w)) s_ok = 0;
-                sh.kw[tid] = f64_of(w[0], w[1]);
-            }
-        }
-        __syncthreads();
-        if (!s_ok) {
-            row_failed(P, b);
-            return;
-        }
-        if (tid == 0) {
-            double base = s_pre;
-            int hk = -1, hw = -1, lk = -1, lw = -1;
-            double hoff = 0.0, loff = 0.0;
-            for (int k = 0; k < R; ++k)
-                for (int w2 = 0; w2 < kWaves; ++w2) {
-                    const double a = sh.kw[k * kWaves + w2];
-                    const double tot = resid ? fma(-dp.rho, sh.kw[(R + k) * kWaves + w2], a) : a;
-                    if (tot > 0.0) {
-                        if (hk < 0 && !s_last && base + tot > t) {
-                            hk = k;
-                            hw = w2;
-                            hoff = base;
-                        }
-                        lk = k;
-                        lw = w2;
-                        loff = base;
-                    }
-                    base += tot;
-                }
-            if (hk < 0) {
-                hk = lk;
-                hw = lw;
-                hoff = loff;
-                s_last = 1;
-            }
-            s_hk = hk;
-            s_hw = hw;
-            s_hoff = hoff;
-        }
-        __syncthreads();
-        const int hk = s_hk, hw = s_hw;
-        if (hk < 0) {
-            // no (run, wave) of the item has mass (cannot happen for the
-            // holding item): its first id
-            if (tid == 0) *outp = static_cast<int>(static_cast<int64_t>(h) * (R * kRunIds));
-            return;
-        }
-        const int64_t id0 = static_cast<int64_t>(h) * (R * kRunIds) + static_cast<int64_t>(hk) * kRunIds +
-                            static_cast<int64_t>(hw) * (64 * kRun) + 2 * tid;
-        double w2v[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int64_t id = id0 + i;
-            float lt = -SV_INF, ld = -SV_INF;
-            if (id < P.V) {
-                lt = load_logit<DT>(rowT, id);
-                if (resid) ld = load_logit<DT>(rowD, id);
-            }
-            double eT, eD;
-            if (resid) {
-                id_exps<TOPP, true>(lt, ld, static_cast<int>(id), dp, s_tab, eT, eD);
-                w2v[i] = fmax(fma(-dp.rho, eD, eT), 0.0);
-            } else {
-                id_exps<TOPP, false>(lt, 0.f, static_cast<int>(id), dp, s_tab, eT, eD);
-                w2v[i] = eT;
-            }
-        }
-        const double mine = w2v[0] + w2v[1];
-        double incl, excl, total;
-        block_scan(mine, incl, excl, total);
-        const bool last = s_last != 0;
-        const int cross = block_min_int((mine > 0.0 && !last && s_hoff + incl > t) ? tid : 0x7FFFFFFF);
-        int who = cross;
-        bool lastmode = last;
-        if (cross == 0x7FFFFFFF) {
-            // past the (run, wave)'s total (rounding, or t beyond every
-            // item): the last id with mass
-            who = block_max_int(mine > 0.0 ? tid : -1);
-            lastmode = true;
-        }
-        if (tid == who) {
-            int y;
-            if (lastmode) {
-                y = static_cast<int>(w2v[1] > 0.0 ? id0 + 1 : id0);
-            } else {
-                const double run0 = s_hoff + excl;
-                y = static_cast<int>((w2v[0] > 0.0 && run0 + w2v[0] > t) || !(w2v[1] > 0.0) ? id0 : id0 + 1);
-            }
-            *outp = y;
-            if (pr) {
-                // Z and t in units of p' (the target's kept mass ST)
-                pr[0] = s_Z / s_ST;
-                pr[1] = t / s_ST;
-            }
-        }
-        if (who < 0 && tid == 0) *outp = static_cast<int>(id0);
-        return;
-    }
 
-    // 5b. the holding item recomputed whole (a second round, the draw from
-    // p', or ambiguous ids in it): exact weights per (run, thread), then the
-    // (run, wave), the lane and its run's ids in order.
-    const bool interior_h = static_cast<int64_t>(h + 1) * (R * kRunIds) <= P.V;
-    item_exact_pass<DT, TOPP, RESID, R>(P, rowT, rowD, aligned, h, interior_h, dp, s_tab, sel, s_A, s_B);
-#pragma unroll
-    for (int k = 0; k < R; ++k) {
-        const double wik = wave_scan_dpp(s_A[k][tid]);
-        if (lane == 63) s_wt[k][wv] = wik;
+    // 5. the holding item's sums per (run, wave): published (fetched above,
+    // or now), or recomputed exactly (a second round, the draw from p', or
+    // ambiguous ids in it); then its (run, wave) holding t and its token
+    if (sh.whole) {
+        const bool interior_h = static_cast<int64_t>(h + 1) * (R * kRunIds) <= P.V;
+        item_exact_pass<DT, TOPP, RESID, R>(P, rowT, rowD, aligned, h, interior_h, dp, s_tab, sel, sh.kwA, sh.kwB);
+        __syncthreads();
+        if (tid < kKw) sh.kw[tid] = tid < R * kWaves ? sh.kwA[tid / kWaves][tid % kWaves] : 0.0;
+    } else if (tid < kKw) {
+        if (kwpre) {
+            sh.kw[tid] = sh.kwall[h * kKw + tid];
+        } else {
+            uint32_t w2[2];
+            if (!poll_words<2>(qrec + static_cast<size_t>(h) * kQRecWords + kQKw + 2 * tid, P.tag, w2)) s_ok = 0;
+            sh.kw[tid] = f64_of(w2[0], w2[1]);
+        }
     }
     __syncthreads();
+    if (!s_ok) {
+        row_failed(P, b);
+        return;
+    }
     if (tid == 0) {
-        double base = s_pre;
-        int hk = -1, hw = -1, lk = -1, lw = -1;
-        double hoff = 0.0, loff = 0.0;
-        for (int k = 0; k < R; ++k)
-            for (int w2 = 0; w2 < kWaves; ++w2) {
-                const double tot = s_wt[k][w2];
-                if (tot > 0.0) {
-                    if (hk < 0 && !s_last && base + tot > t) {
-                        hk = k;
-                        hw = w2;
-                        hoff = base;
-                    }
-                    lk = k;
-                    lw = w2;
-                    loff = base;
-                }
-                base += tot;
-            }
-        if (hk < 0) {
-            hk = lk;
-            hw = lw;
-            hoff = loff;
-            s_last = 1;
-        }
+        int last = s_last, hk, hw;
+        double hoff;
+        find_run_wave<R>(sh.kw, sh.kw + R * kWaves, dp.rho, resid && !sh.whole, s_pre, t, last, hk, hw, hoff);
         s_hk = hk;
         s_hw = hw;
         s_hoff = hoff;
+        s_last = last;
     }
     __syncthreads();
+    // the verify step's token at position n, or an SMC particle's bonus
+    int32_t* outp = P.smc ? P.out_tokens + b : P.out_tokens + static_cast<size_t>(b) * (P.K + 1) + rn;
     const int hk = s_hk, hw = s_hw;
     if (hk < 0) {
-        if (tid == 0) *outp = static_cast<int>(item_run_id0<R>(h, 0));
+        // no (run, wave) of the item has mass (cannot happen for the holding
+        // item): its first id
+        if (tid == 0) *outp = static_cast<int>(static_cast<int64_t>(h) * (R * kRunIds));
         return;
     }
-    if (wv != hw) return;
-    // wave hw: the first lane of run hk whose inclusive prefix passes t (or
-    // the last lane with mass)
-    const double myx = s_A[hk][tid];
-    const double incl = s_hoff + wave_scan_dpp(myx);
-    bool last = s_last != 0;
-    unsigned long long hm = __ballot(myx > 0.0 && (last || incl > t));
-    if (hm == 0ull) {
-        last = true;
-        hm = __ballot(myx > 0.0);
-    }
-    const int hl = last ? 63 - __clzll(static_cast<long long>(hm)) : __ffsll(static_cast<long long>(hm)) - 1;
-    if (lane == hl) {
-        // this thread's run hk: its ids' weights again, exactly as summed
-        const int64_t id0 = item_run_id0<R>(h, hk);
-        uint4 vt[ItemRaw<DT, 1>::NVR], vd[ItemRaw<DT, 1>::NVR];
-        issue_run<DT>(rowT, id0, P.V, aligned, vt);
-        if (resid) issue_run<DT>(rowD, id0, P.V, aligned, vd);
-        if (aligned && run_straddles<DT>(id0, P.V)) {
-            load_run_elems<DT>(rowT, id0, P.V, vt);
-            if (resid) load_run_elems<DT>(rowD, id0, P.V, vd);
-        }
-        float lt[kRun], ld[kRun];
-        unpack_masked<DT>(vt, id0, P.V, lt);
-        if (resid) unpack_masked<DT>(vd, id0, P.V, ld);
-        double run = incl - myx;  // exclusive prefix of this thread's run
-        int y = -1, lastw = -1;
-#pragma unroll
-        for (int i = 0; i < kRun; ++i) {
-            double eT, eD, wi;
-            if (resid) {
-                id_exps<TOPP, true>(lt[i], ld[i], static_cast<int>(id0) + i, dp, s_tab, eT, eD);
-                wi = fmax(fma(-dp.rho, eD, eT), 0.0);
-            } else {
-                id_exps<TOPP, false>(lt[i], 0.f, static_cast<int>(id0) + i, dp, s_tab, eT, eD);
-                wi = eT;
-            }
-            if (wi > 0.0) {
-                lastw = static_cast<int>(id0 + i);
-                if (y < 0 && !last && run + wi > t) y = lastw;
-            }
-            run += wi;
-        }
-        *outp = y >= 0 ? y : (lastw >= 0 ? lastw : static_cast<int>(id0));
+    const int y = pick_run_wave<DT, TOPP, R>(P, rowT, rowD, h, hk, hw, s_hoff, t, s_last != 0, resid, dp, s_tab);
+    if (tid == 0) {
+        const int64_t first = static_cast<int64_t>(h) * (R * kRunIds) + static_cast<int64_t>(hk) * kRunIds +
+                              static_cast<int64_t>(hw) * (64 * kRun);
+        *outp = y >= 0 ? y : static_cast<int>(first);
+        double* pr = P.probe_row ? P.probe_row + static_cast<size_t>(b) * 4 : nullptr;
         if (pr) {
+            // Z and t in units of p' (the target's kept mass ST)
             pr[0] = s_Z / s_ST;
             pr[1] = t / s_ST;
         }
@@ -2643,7 +2589,8 @@ __device__ __forceinline__ void resample_body(const Params& P, int b, int r, con
 }
 
 template <int DT, bool TOPP, int R>
-__device__ __forceinline__ void resample_item(const Params& P, int b, int r, const RowParam& rp, DrawShared<R>& sh) {
+__device__ __forceinline__ void resample_item(const Params& P, int b, int r, const RowParam& rp,
+                                              DrawShared<DT, R>& sh) {
     // the row's mode and n are the same for every lane: keep them scalar
     const int mode = __builtin_amdgcn_readfirstlane(rp.mode);
     const int rn = __builtin_amdgcn_readfirstlane(rp.n);
@@ -2667,7 +2614,7 @@ template <int DT, bool TOPP, int R>
 __global__ __launch_bounds__(kThreads) void k_rows(Params P) {
     __shared__ RowShared RS;
     __shared__ RowParam s_rp;
-    __shared__ DrawShared<R> DS;
+    __shared__ DrawShared<DT, R> DS;
     // the draw's exponential table, filled while the records load (the
     // barriers of the decision order it before any use)
     exp2_table_fill(DS.tab);
@@ -2682,7 +2629,7 @@ __global__ __launch_bounds__(kThreads) void k_rows(Params P) {
         if ((threadIdx.x >> 6) == 0) fill_row_from_rv(P, b, Le, RS);
         __syncthreads();
     } else {
-        fill_row_from_partials(P, b, Le, RS);
+        fill_row_from_partials(P, b, Le, RS, DS.stage);
     }
     if ((threadIdx.x >> 6) == 0) {
         RowParam rp;
@@ -2753,12 +2700,12 @@ template <int DT, int R>
 __global__ __launch_bounds__(kThreads) void k_smc_rows(Params P) {
     __shared__ RowShared RS;
     __shared__ RowParam s_rp;
-    __shared__ DrawShared<R> DS;
+    __shared__ DrawShared<DT, R> DS;
     exp2_table_fill(DS.tab);
     const int b = blockIdx.x / P.nq;
     const int r = blockIdx.x - b * P.nq;
     const int x = lane_token(P, b, P.K);
-    fill_row_from_partials(P, b, P.K, RS);
+    fill_row_from_partials(P, b, P.K, RS, DS.stage);
     if ((threadIdx.x >> 6) == 0) {
         RowParam rp;
         smc_particle(P, b, RS, r == 0, x, rp);

@@ -31,7 +31,7 @@ struct Scratch {
 static_assert(SPECVERIFY_MAX_V == sv::kMaxV, "vocabulary limit");
 
 struct Layout {
-    size_t prec, rv, qrec, chdr, cand, cum, total;
+    size_t prec, rv, qrec, chdr, cand, cum, etab, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
@@ -39,7 +39,7 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 // Tagged records (statistics per chunk, masses per resample item) carry the
 // call's tag; RvState is rewritten before it is read.  The top-p candidate headers and lists (present only
 // when `topp`) are rewritten by the statistics pass of every top-p call.
-Layout layout(int64_t B, int nslot, int nch, int nq, bool topp, bool smc) {
+Layout layout(int64_t B, int nslot, int nch, int nq, bool topp, bool smc, bool tab) {
     Layout L;
     size_t off = 0;
     L.prec = off;
@@ -55,6 +55,8 @@ Layout layout(int64_t B, int nslot, int nch, int nq, bool topp, bool smc) {
     off = align256(off + chunks * sv::kCand * sizeof(uint64_t));
     L.cum = off;
     off = align256(off + (smc ? static_cast<size_t>(B) * sizeof(double) : 0));
+    L.etab = off;
+    off = align256(off + (tab ? static_cast<size_t>(sv::kTabN) * sizeof(double) : 0));
     L.total = off;
     return L;
 }
@@ -226,6 +228,7 @@ struct Setup {
     bool topp = false;
     hipStream_t stream = nullptr;
     Layout lay;
+    bool tab = false;
 };
 
 enum Mode { MODE_VERIFY = 0, MODE_SMC = 1, MODE_GREEDY = 2 };
@@ -282,7 +285,10 @@ int plan(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_tokens, 
 
     // greedy verify takes its argmaxes and top-k from the candidate lists
     const bool topp = top_p < 1.f || greedy;
-    S.lay = layout(B, nslot, nch, nq, topp, smc);
+    // the top-p row pass's exponential table (bfloat16 rows; for larger c its
+    // entries 2^(u*c) would leave the float64 range)
+    S.tab = dtype == sv::DT_BF16 && !greedy && !smc && top_p < 1.f && c <= sv::kTabMaxC;
+    S.lay = layout(B, nslot, nch, nq, topp, smc, S.tab);
 
     Params& p = S.p;
     std::memset(&p, 0, sizeof(p));
@@ -340,6 +346,7 @@ void bind(Setup& S, uint8_t* base) {
     p.chdr = S.topp ? reinterpret_cast<uint64_t*>(base + lay.chdr) : nullptr;
     p.cand = S.topp ? reinterpret_cast<uint64_t*>(base + lay.cand) : nullptr;
     p.smc_cum = p.smc ? reinterpret_cast<double*>(base + lay.cum) : nullptr;
+    p.etab = S.tab ? reinterpret_cast<double*>(base + lay.etab) : nullptr;
 }
 
 // plan + scratch + bind for a single pass.

@@ -24,6 +24,13 @@ constexpr int kMaxV = 1 << 21;       // largest vocabulary of the sampling entry
 constexpr int kCand = 256;           // nucleus candidates a statistics chunk lists at most
 constexpr int kMaxTopK = 64;         // greedy verify: largest top-k
 constexpr uint32_t kNoCover = 0xFFFFFFFFu;  // candidate header: the chunk's list covers nothing
+// Exponential table of the top-p row pass for bfloat16 logits: 2^(u*c) in
+// float64 for every bfloat16 u with 2^-8 <= |u| < 2^6 (biased exponents
+// 119..132), entry ((bits(u) & 0x7FFF) - kTabMagLo) * 2 + sign(u).
+constexpr uint32_t kTabMagLo = 119u << 7;
+constexpr int kTabMags = 14 * 128;
+constexpr int kTabN = 2 * kTabMags;
+constexpr double kTabMaxC = 14.0;   // the table is used for c <= 14 (|u*c| < 896)
 
 enum DType : int { DT_F32 = 0, DT_BF16 = 1 };
 enum RowMode : int { MODE_SKIP = 0, MODE_RESID = 1, MODE_BONUS = 2 };
@@ -94,6 +101,8 @@ struct Params {
     uint64_t* prec;               // [B, nslot, nch] tagged statistics records
     RvState* rv;                  // [B, nslot]
     uint64_t* qrec;               // [B, nq, kQRecWords] tagged row-pass item records
+    double* etab;                 // [kTabN] exponential table (bfloat16 top-p calls with c <= kTabMaxC),
+                                  // written by the statistics kernel, read by the row pass; else null
     // SMC-SD step (smc = 1): B particles, every one with K drafted tokens
     int smc;
     double ess_frac;              // resample when ESS < ess_frac * B

@@ -834,6 +834,17 @@ __global__ __launch_bounds__(kThreads, 8) void k_stats(Params P) {
         const int64_t e = static_cast<int64_t>(item) * per + threadIdx.x;
         if (static_cast<int>(threadIdx.x) < per && e < words) P.qrec[e] = 0ull;
     }
+    if (DT == DT_BF16 && CAND && P.etab) {
+        // the top-p row pass's exponential table, 2^(u*c) for the bfloat16
+        // values u of its window (the kernels of one call run in order: the
+        // row pass reads it after this kernel has finished)
+        const int64_t grid = static_cast<int64_t>(P.B) * P.nslot * P.nch;
+        for (int64_t e = static_cast<int64_t>(item) * kThreads + threadIdx.x; e < kTabN; e += grid * kThreads) {
+            const uint32_t bits = ((static_cast<uint32_t>(e) & 1u) << 31) |
+                                  (((static_cast<uint32_t>(e) >> 1) + kTabMagLo) << 16);
+            P.etab[e] = exp2(static_cast<double>(__uint_as_float(bits)) * P.c64);
+        }
+    }
     const int rvi = item / P.nch;
     const int chunk = item - rvi * P.nch;
     const int b = rvi / P.nslot;
@@ -1735,6 +1746,24 @@ __device__ __forceinline__ double exp2_f64(double x, const double* tab) {
     return ldexp(fma(t, p, t), k >> kExpTabBits);
 }
 
+// The top-p row pass on bfloat16 logits (TB): 2^(l*c) itself from the
+// exponential table when l lies in its window (2^-8 <= |l| < 2^6; `tspan` is
+// kTabN when the row uses the table, else 0), which follows `tab` in LDS;
+// otherwise, and without TB, 2^(l*c - off) by exp2_f64.  A row takes all its
+// exponentials one way: with the table, off = 0.
+template <bool TB>
+__device__ __forceinline__ double exp_of(float l, double off, double c, uint32_t tspan, const double* tab) {
+    if (TB) {
+        const uint32_t f = __float_as_uint(l);
+        const uint32_t r = ((((f >> 16) & 0x7FFFu) - kTabMagLo) << 1) | (f >> 31);
+        const bool in = r < tspan;
+        double e = tab[kExpTab + (in ? r : 0u)];
+        if (!in) e = exp2_f64(fma(static_cast<double>(l), c, -off), tab);
+        return e;
+    }
+    return exp2_f64(fma(static_cast<double>(l), c, -off), tab);
+}
+
 // ---------------------------------------------------------------------------
 // Row pass, the draw (see the section header above k_rows).  Everything that
 // decides the drawn token is float64: per id eT = 2^(lT*c - oT) and eD =
@@ -1846,6 +1875,7 @@ struct DrawParam {
     double dstar, delta;       // classification of residual ids (see above)
     float dlo, dhi;            // the float32 band of d = lT - lD holding [d~* - Delta, d~* + Delta]
     double rho;                // exact ST/SD, known after the exchange
+    uint32_t tspan;            // kTabN: the row's exponentials come from the table (offsets 0); else 0
 };
 __device__ __forceinline__ double sgpr_f64(double v) {
     const long long b = __double_as_longlong(v);
@@ -1869,14 +1899,15 @@ __device__ __forceinline__ void pair_fence(double& a0, double& a1, double& b0, d
 }
 
 // eT (and eD) of one id: 0 outside the id's nucleus (top-p) and at -inf.
-template <bool TOPP, bool RESID>
+template <int DT, bool TOPP, bool RESID>
 __device__ __forceinline__ void id_exps(float lt, float ld, int id, const DrawParam& dp, const double* tab, double& eT,
                                         double& eD) {
-    eT = exp2_f64(fma(static_cast<double>(lt), dp.c, -dp.oT), tab);
+    constexpr bool TB = DT == DT_BF16 && TOPP;
+    eT = exp_of<TB>(lt, dp.oT, dp.c, dp.tspan, tab);
     if (TOPP && !kept_l(lt, dp.tvT, id, dp.cutT)) eT = 0.0;
     eD = 0.0;
     if (RESID) {
-        eD = exp2_f64(fma(static_cast<double>(ld), dp.c, -dp.oD), tab);
+        eD = exp_of<TB>(ld, dp.oD, dp.c, dp.tspan, tab);
         if (TOPP && !kept_l(ld, dp.tvD, id, dp.cutD)) eD = 0.0;
     }
 }
@@ -1948,7 +1979,7 @@ __device__ __forceinline__ void item_first_pass(const Params& P, const uint8_t* 
             double eT[2], eD[2];
 #pragma unroll
             for (int h = 0; h < 2; ++h)
-                id_exps<TOPP, RESID>(lt[i + h], RESID ? ld[i + h] : 0.f, i0 + i + h, dp, tab, eT[h], eD[h]);
+                id_exps<DT, TOPP, RESID>(lt[i + h], RESID ? ld[i + h] : 0.f, i0 + i + h, dp, tab, eT[h], eD[h]);
             if (i + 2 < kRun)
                 pair_fence<RESID>(eT[0], eT[1], eD[0], eD[1], lt[i + 2], lt[i + 3], ld[i + 2], ld[i + 3]);
 #pragma unroll
@@ -2016,7 +2047,7 @@ __device__ __forceinline__ void item_exact_pass(const Params& P, const uint8_t* 
             double eT[2], eD[2];
 #pragma unroll
             for (int h = 0; h < 2; ++h)
-                id_exps<TOPP, RS>(lt[i + h], RS ? ld[i + h] : 0.f, i0 + i + h, dp, tab, eT[h], eD[h]);
+                id_exps<DT, TOPP, RS>(lt[i + h], RS ? ld[i + h] : 0.f, i0 + i + h, dp, tab, eT[h], eD[h]);
             if (i + 2 < kRun) pair_fence<RS>(eT[0], eT[1], eD[0], eD[1], lt[i + 2], lt[i + 3], ld[i + 2], ld[i + 3]);
 #pragma unroll
             for (int h = 0; h < 2; ++h) a += RS ? fmax(fma(-dp.rho, eD[h], eT[h]), 0.0) : eT[h];
@@ -2104,8 +2135,9 @@ __device__ __forceinline__ bool row_arrive(uint64_t* cnt, int nq) {
 // per-(run, wave) sums when they fit (kKwPre doubles), the statistics
 // records staged by the decision before that.
 constexpr int kKwPre = 512;
-template <int DT, int R> struct DrawShared {
+template <int DT, int R, bool TB = false> struct alignas(16) DrawShared {
     double tab[kExpTab];
+    double etab[TB ? kTabN : 1];  // the top-p row pass on bfloat16 rows: the exponential table (read as tab + kExpTab)
     double red[4][kWaves];
     double kwA[R][kWaves], kwB[R][kWaves];  // this item's sums per (run, wave)
     double kw[2 * R * kWaves];              // the holding item's
@@ -2120,6 +2152,34 @@ template <int DT, int R> struct DrawShared {
     int gn, gover;
 };
 static_assert(sizeof(Partial) * kThreads <= sizeof(double) * kKwPre, "stage fits the prefetch area");
+template <int DT, bool TOPP, int R> using DrawSharedT = DrawShared<DT, R, DT == DT_BF16 && TOPP>;
+
+// The exponential table's copy into LDS, straight from global memory (each
+// lane's 16 bytes land at the wave's LDS base + 16 * lane; 1 KiB per wave per
+// load): issued at the kernel's start, waited for before the draw.
+constexpr int kTabChunks = kTabN * static_cast<int>(sizeof(double)) / 1024;
+static_assert(kTabChunks % kWaves == 0 && kTabChunks * 1024 == kTabN * static_cast<int>(sizeof(double)), "table copy");
+template <int DT, int R, bool TB>
+__device__ __forceinline__ void tab_issue(const Params& P, DrawShared<DT, R, TB>& sh) {
+    using DS = DrawShared<DT, R, TB>;
+    static_assert(offsetof(DS, etab) == offsetof(DS, tab) + sizeof(double) * kExpTab, "the table follows tab");
+    static_assert(offsetof(DS, etab) % 16 == 0, "16-byte aligned table");
+    if (TB && P.etab) {
+        typedef __attribute__((address_space(3))) void* lds_ptr;
+        const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+        const uint4* src = reinterpret_cast<const uint4*>(P.etab) + (threadIdx.x & 63);
+#pragma unroll
+        for (int q = 0; q < kTabChunks / kWaves; ++q) {
+            const int chunk = q * kWaves + wv;
+            __builtin_amdgcn_global_load_lds(src + chunk * 64, (lds_ptr)(reinterpret_cast<char*>(sh.etab) + chunk * 1024),
+                                             16, 0, 0);
+        }
+    }
+}
+template <bool TB>
+__device__ __forceinline__ void tab_wait(const Params& P) {
+    if (TB && P.etab) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
 
 // The token of a run-wave: the kRun*64 ids of run k, wave w of item h, two
 // per thread, their exact weights, a block scan from `hoff` (the mass before
@@ -2145,10 +2205,10 @@ __device__ __forceinline__ int pick_run_wave(const Params& P, const uint8_t* row
         }
         double eT, eD;
         if (resid) {
-            id_exps<TOPP, true>(lt, ld, static_cast<int>(id), dp, tab, eT, eD);
+            id_exps<DT, TOPP, true>(lt, ld, static_cast<int>(id), dp, tab, eT, eD);
             wv2[i] = fmax(fma(-dp.rho, eD, eT), 0.0);
         } else {
-            id_exps<TOPP, false>(lt, 0.f, static_cast<int>(id), dp, tab, eT, eD);
+            id_exps<DT, TOPP, false>(lt, 0.f, static_cast<int>(id), dp, tab, eT, eD);
             wv2[i] = eT;
         }
     }
@@ -2211,8 +2271,8 @@ __device__ __forceinline__ void find_run_wave(const double* kA, const double* kB
 
 template <int DT, bool TOPP, bool RESID, int R>
 __device__ __forceinline__ void resample_body(const Params& P, int b, int r, const RowParam& rp, int rn,
-                                              DrawShared<DT, R>* sh_) {
-    DrawShared<DT, R>& sh = *sh_;
+                                              DrawSharedT<DT, TOPP, R>* sh_) {
+    DrawSharedT<DT, TOPP, R>& sh = *sh_;
     double* const s_tab = sh.tab;
     double (*const s_red)[kWaves] = sh.red;
     int &s_item = sh.item, &s_mode = sh.mode, &s_ok = sh.ok, &s_hk = sh.hk, &s_hw = sh.hw, &s_last = sh.last;
@@ -2243,7 +2303,19 @@ __device__ __forceinline__ void resample_body(const Params& P, int b, int r, con
     dp.delta = 0.0;
     dp.dlo = 0.f;
     dp.dhi = 0.f;
-    const double rtil = sgpr_f64(rp.keptT / rp.keptD);  // rho~
+    double rtil = rp.keptT / rp.keptD;  // rho~
+    dp.tspan = 0u;
+    if (DT == DT_BF16 && TOPP && P.etab && fabsf(rp.oT) <= 256.f && (!RESID || fabsf(rp.oD) <= 256.f)) {
+        // exponentials from the table: 2^(l*c) with offsets 0 (the row's
+        // maxima keep them and their sums within float64); rho~ and rho are
+        // then ratios of offset-free sums
+        dp.tspan = kTabN;
+        if (RESID) rtil = ldexp(rtil, static_cast<int>(rp.oT - rp.oD));
+        dp.oT = 0.0;
+        dp.oD = 0.0;
+    }
+    rtil = sgpr_f64(rtil);
+    dp.tspan = __builtin_amdgcn_readfirstlane(dp.tspan);
     if (RESID) {
         // d~* from rho~: eT > rho~ eD iff (lT - lD) c - oT + oD > log2 rho~;
         // Delta covers the relative error P.amb_band of rho~ plus the float64
@@ -2590,7 +2662,7 @@ __device__ __forceinline__ void resample_body(const Params& P, int b, int r, con
 
 template <int DT, bool TOPP, int R>
 __device__ __forceinline__ void resample_item(const Params& P, int b, int r, const RowParam& rp,
-                                              DrawShared<DT, R>& sh) {
+                                              DrawSharedT<DT, TOPP, R>& sh) {
     // the row's mode and n are the same for every lane: keep them scalar
     const int mode = __builtin_amdgcn_readfirstlane(rp.mode);
     const int rn = __builtin_amdgcn_readfirstlane(rp.n);
@@ -2614,9 +2686,11 @@ template <int DT, bool TOPP, int R>
 __global__ __launch_bounds__(kThreads) void k_rows(Params P) {
     __shared__ RowShared RS;
     __shared__ RowParam s_rp;
-    __shared__ DrawShared<DT, R> DS;
-    // the draw's exponential table, filled while the records load (the
-    // barriers of the decision order it before any use)
+    __shared__ DrawSharedT<DT, TOPP, R> DS;
+    // the draw's exponential tables: the small one filled while the records
+    // load (the barriers of the decision order it before any use), the top-p
+    // bfloat16 one copied from the statistics kernel's
+    tab_issue(P, DS);
     exp2_table_fill(DS.tab);
     const int b = blockIdx.x / P.nq;
     const int r = blockIdx.x - b * P.nq;
@@ -2636,6 +2710,7 @@ __global__ __launch_bounds__(kThreads) void k_rows(Params P) {
         decide_row<TOPP>(P, b, Le, rowok, RS, r == 0, x, rp);
         if ((threadIdx.x & 63) == 0) s_rp = rp;
     }
+    tab_wait<DT == DT_BF16 && TOPP>(P);
     __syncthreads();
     const RowParam rp = s_rp;
     resample_item<DT, TOPP, R>(P, b, r, rp, DS);
@@ -2700,7 +2775,7 @@ template <int DT, int R>
 __global__ __launch_bounds__(kThreads) void k_smc_rows(Params P) {
     __shared__ RowShared RS;
     __shared__ RowParam s_rp;
-    __shared__ DrawShared<DT, R> DS;
+    __shared__ DrawSharedT<DT, false, R> DS;
     exp2_table_fill(DS.tab);
     const int b = blockIdx.x / P.nq;
     const int r = blockIdx.x - b * P.nq;

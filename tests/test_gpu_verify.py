@@ -145,6 +145,30 @@ def test_top_p_values(top_p, dtype):
     _parity(inp, label=f"top_p={top_p} {dtype}")
 
 
+@pytest.mark.parametrize("case", ["window", "wide", "large_offsets", "cold", "mixed_rows"])
+def test_top_p_bf16_exponential_table_paths(case):
+    # the top-p row pass on bfloat16 rows takes 2^(l*c) from its table for
+    # 2^-8 <= |l| < 2^6 and computes the rest; rows whose offsets exceed
+    # 256 compute every exponential (offsets kept), and for c > 14 the
+    # table is off for the call
+    T, scale = (0.09, 3.0) if case == "cold" else (0.7, {"wide": 25.0, "large_offsets": 100.0}.get(case, 3.0))
+    inp = W.synthetic(8, 3, 6007, dtype="bf16", temperature=T, top_p=0.9, scale=scale, sigma=1.0, seed=21,
+                      gen_seed={"window": 31, "wide": 32, "large_offsets": 33, "cold": 34, "mixed_rows": 35}[case])
+    if case == "mixed_rows":
+        t = W.bf16_bits_to_f32(inp.target)
+        d = W.bf16_bits_to_f32(inp.draft)
+        t[0] *= 40.0                       # offsets above 256: every exponential computed
+        d[0] *= 40.0
+        t[1, :, 5000:] = -np.inf           # masked tail
+        d[1, :, 5000:] = -np.inf
+        inp.draft_tokens[1] = [7, 70, 700]
+        t[2] *= 1e-3                       # logits below the window
+        d[2] *= 1e-3
+        inp.target[:] = W.f32_to_bf16_bits(t)
+        inp.draft[:] = W.f32_to_bf16_bits(d)
+    _parity(inp, label=f"bf16 top-p exponential table: {case}")
+
+
 def test_top_p_flat_rows_split_tie_groups():
     # all-equal logits: the whole row is one tie group; the cut keeps the
     # lowest ids; rows 2-3 draft ids outside the nucleus (r = 0/0 = 0, a

@@ -330,6 +330,7 @@ def smc_bench(args, binding, torch, dev, sets, dsets, logical, stream):
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline_smc(sets, args.cpu_rows, sets[0].workload.name)
+    dist = per_call_distribution(torch, stream, step, args.steps)
     line = {
         "metric": "SMC-SD step: scored particle positions/sec + logits HBM GB/s (% of peak) at N=64,K=5,V=128256",
         "value": round(positions / (ms_step / 1e3), 1),
@@ -438,6 +439,7 @@ def greedy_bench(args, binding, torch, dev, sets):
                "sample": f"{len(work)} rows of the batched workload, {passes} passes ({positions} draft positions), "
                          f"float64 NumPy oracle, one row per task over {cores} processes, {dt:.1f} s wall"}
     stats_s = us["stats"] * 1e-6
+    dist = per_call_distribution(torch, stream, step, args.steps)
     line = {
         "metric": "greedy verify + top-60: draft positions/sec + logits HBM GB/s (% of peak) at B=64,K=5,V=128256",
         "value": round(B * K / (ms_step / 1e3), 1),
@@ -615,7 +617,7 @@ def overlap_bench(args, binding, torch, dev, sets):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f32+f64",
         "data": "synthetic",
         "config": {"workload": "two batches of B=64 K=5 V=128256 bf16 T=0.7; verify on stream 0, the synthetic "
                                "draft producer on stream 1, roles swapped every step",
@@ -627,7 +629,7 @@ def overlap_bench(args, binding, torch, dev, sets):
         "kernels_us": kus,
         "graph_replay_matches_eager": replay_ok,
         "producer_GBps_alone": round(prod_bytes / (us["produce"] * 1e-6) / 1e9, 1),
-        "per_call": dist,
+        "per_call": None,  # graph replays of whole schedules: no per-call events
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
@@ -710,6 +712,7 @@ def hispec_bench(args, binding, torch, dev):
                "sample": f"{len(work)} rows of the three-layer workload, {passes} passes ({positions} draft "
                          f"positions), float64 NumPy oracle, one row per task over {cores} processes, "
                          f"{dt:.1f} s wall"}
+    dist = per_call_distribution(torch, stream, step, args.steps)
     line = {
         "metric": "two-stage verify: draft positions/sec + logits HBM GB/s (% of peak) at B=64,K=5,V=128256",
         "value": round(B * K / (ms_step / 1e3), 1),

@@ -151,3 +151,36 @@ def _produce(lib, B=3, P=4, K=2, V=64, tdata=0x1000, out=0x5000, osb=None, osp=N
 ])
 def test_produce_host_validation(lib, kw, code):
     assert _produce(lib, **kw) == code
+
+
+def _noalloc(lib, B=2, K=3, V=100):
+    t = binding.SvLogits(0x1000, 0, B, K + 1, V, (K + 1) * V, V)
+    d = binding.SvLogits(0x2000, 0, B, K, V, K * V, V)
+    v = ctypes.c_void_p
+    return lib.spec_verify_noalloc(ctypes.byref(t), ctypes.byref(d), v(0x3000), v(None), ctypes.c_float(1.0),
+                                   ctypes.c_float(1.0), ctypes.c_uint64(0), v(0x4000), v(0x5000), v(None))
+
+
+def test_forced_launch_failure_returns_ehip(lib, monkeypatch):
+    # SPECVERIFY_FAIL_LAUNCH makes every entry point fail as a failed kernel
+    # launch does, before it touches the device: SV_EHIP, with the message
+    monkeypatch.setenv("SPECVERIFY_FAIL_LAUNCH", "1")
+    assert _call(lib) == -4
+    assert b"SPECVERIFY_FAIL_LAUNCH" in lib.spec_verify_strerror(-4)
+    assert _call(lib, dtype=1, top_p=0.9) == -4
+    assert _smc(lib) == -4
+    assert _hispec(lib) == -4
+    assert _greedy(lib) == -4
+    assert _produce(lib) == -4
+    assert _noalloc(lib) == -4
+    # host-checked argument errors still come first
+    assert _call(lib, tdata=0) == -1
+    monkeypatch.delenv("SPECVERIFY_FAIL_LAUNCH")
+    assert _call(lib, tdata=0) == -1
+
+
+def test_release_without_scratch_is_harmless(lib):
+    # nothing allocated (no GPU call was made): releasing twice does nothing
+    lib.spec_verify_release()
+    lib.spec_verify_release()
+    assert lib.spec_verify_abi_version() == 1

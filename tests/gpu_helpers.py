@@ -115,6 +115,21 @@ def band_of(kind, res, b, inp):
     return BANDS[kind]
 
 
+def near_boundary(res, b, top_p):
+    """True when a decision of row b of the oracle result `res` lies within
+    the library's band for its kind (a row another finite-precision
+    implementation may legitimately decide differently)."""
+    if b not in res.margins:
+        return False
+    acc = BAND_ACCEPT_TOPP if float(top_p) < 1.0 else BAND_ACCEPT
+    for kind, _, mg in res.margins[b]:
+        band = {"accept": acc, "sample": sample_band(res, b)}.get(kind, BAND_NUCLEUS if kind.startswith("nucleus")
+                                                                  else math.inf)
+        if mg < band:
+            return True
+    return False
+
+
 @dataclass
 class ParityStats:
     rows: int = 0                 # rows compared

@@ -3,8 +3,10 @@ against the float64 oracle (oracle.hispec_verify) on the same seeded inputs,
 through the C ABI.
 
 Bar: identical stage-1 counts, final counts and emitted tokens on every row
-the oracle does not flag (a stage-1 or stage-2 decision within 1e-6 of its
-threshold); flagged rows a minority.
+with no decision inside the library's band for its kind (tests/gpu_helpers.py:
+acceptance tests 2.5e-6 on the u scale, 3.5e-6 with top-p; draws 1e-10 of
+the residual mass plus float64 rounding; nucleus cuts 3e-6), each stage
+judged by its own decisions; at most one such row per call.
 """
 
 import numpy as np
@@ -12,7 +14,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import dev_array, say
+from gpu_helpers import dev_array, near_boundary, say
 from rejection_sampling_verifier_amd import binding
 from rejection_sampling_verifier_amd import workloads as W
 
@@ -41,21 +43,21 @@ def _check(f, i, d, x, dl, T, top_p, seed, label):
     torch.cuda.synchronize()
     tok, n, n1 = tok.cpu().numpy(), n.cpu().numpy(), n1.cpu().numpy()
     r = oracle.hispec_verify(f, i, d, x, dl, T, top_p, seed)
-    checked = 0
+    checked = near = 0
     for b in range(B):
-        if r.stage1.flagged[b]:
+        if near_boundary(r.stage1, b, top_p):
+            near += 1
             continue
         assert n1[b] == r.n_stage1[b], (label, b, n1[b], r.n_stage1[b])
-        if r.stage2.flagged[b]:
+        if near_boundary(r.stage2, b, top_p):
+            near += 1
             continue
         checked += 1
         assert n[b] == r.n_accepted[b], (label, b, n[b], r.n_accepted[b])
         assert np.array_equal(tok[b], r.tokens[b]), (label, b, tok[b], r.tokens[b])
-    flagged = int(np.sum(r.flagged))
-    say(f"    rows checked={checked} flagged={flagged}; mean n1={np.mean(r.n_stage1):.2f} n={np.mean(r.n_accepted):.2f}")
-    # a sampled token's margin is below 1e-6 with probability about the mass
-    # of tokens lighter than 2e-6: a few percent at these vocabulary sizes
-    assert flagged <= max(2, B // 4)
+    say(f"    rows checked={checked} within a band={near} (oracle rows within 1e-6: {int(np.sum(r.flagged))}); "
+        f"mean n1={np.mean(r.n_stage1):.2f} n={np.mean(r.n_accepted):.2f}")
+    assert near <= 1, (label, near)
     return r
 
 

@@ -39,7 +39,7 @@ size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 // Tagged records (statistics per chunk, masses per resample item) carry the
 // call's tag; RvState is rewritten before it is read.  The top-p candidate headers and lists (present only
 // when `topp`) are rewritten by the statistics pass of every top-p call.
-Layout layout(int64_t B, int nslot, int nch, int nq, bool topp, bool smc, bool tab) {
+Layout layout(int64_t B, int nslot, int nch, int nq, int qwords, bool topp, bool smc, bool tab) {
     Layout L;
     size_t off = 0;
     L.prec = off;
@@ -47,7 +47,7 @@ Layout layout(int64_t B, int nslot, int nch, int nq, bool topp, bool smc, bool t
     L.rv = off;
     off = align256(off + static_cast<size_t>(B) * nslot * sizeof(sv::RvState));
     L.qrec = off;
-    off = align256(off + static_cast<size_t>(B) * nq * sv::kQRecWords * sizeof(uint64_t));
+    off = align256(off + static_cast<size_t>(B) * nq * qwords * sizeof(uint64_t));
     const size_t chunks = topp ? static_cast<size_t>(B) * nslot * nch : 0;
     L.chdr = off;
     off = align256(off + chunks * sv::kWaves * 4 * sizeof(uint64_t));  // four tagged words per wave
@@ -267,28 +267,33 @@ int plan(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_tokens, 
     const int cv = sv::kThreads * unroll;
     const int64_t nch64 = (nvec_max + cv - 1) / cv;
     const int nch = static_cast<int>(nch64);
-    // row pass: items of runs*kRunIds ids; one-run items when the batch would
-    // otherwise give fewer than two workgroups per CU
+    // row pass: items of runs*kRunIds ids.  Four-run items by default; one-run
+    // items when the batch would otherwise give fewer than two workgroups per
+    // CU; sixteen-run items when four-run items would not all be resident at
+    // once (four workgroups per CU), so that every row pays the pass's latency
+    // chain once instead of once per round of workgroups
     int runs = sv::kRunsMax;
     if (!greedy) {
         const int cus = device_cus();
-        const int64_t big = static_cast<int64_t>(B) * ((V + runs * sv::kRunIds - 1) / (runs * sv::kRunIds));
-        if (big < 2ll * cus) runs = 1;
+        auto items = [&](int ru) { return static_cast<int64_t>(B) * ((V + ru * sv::kRunIds - 1) / (ru * sv::kRunIds)); };
+        if (items(runs) < 2ll * cus) runs = 1;
+        else if (items(runs) > 4ll * cus && items(sv::kRunsBig) < items(runs)) runs = sv::kRunsBig;
         const int forced = env_int("SPECVERIFY_ROW_RUNS", 0);
-        if (forced == 1 || forced == 2 || forced == sv::kRunsMax) runs = forced;
+        if (forced == 1 || forced == 2 || forced == sv::kRunsMax || forced == sv::kRunsBig) runs = forced;
     }
     const int nq = greedy ? 0 : (V + runs * sv::kRunIds - 1) / (runs * sv::kRunIds);
+    const int qwords = sv::qrec_words(runs);
     const int64_t per_row = static_cast<int64_t>(nslot) * nch + nq;
     if (static_cast<int64_t>(B) * per_row >= (1ll << 31)) return SV_ESHAPE;
     // the statistics kernel clears the row pass's records, a few words each
-    if (static_cast<int64_t>(sv::kQRecWords) * nq > static_cast<int64_t>(sv::kThreads) * nslot * nch) return SV_ESHAPE;
+    if (static_cast<int64_t>(qwords) * nq > static_cast<int64_t>(sv::kThreads) * nslot * nch) return SV_ESHAPE;
 
     // greedy verify takes its argmaxes and top-k from the candidate lists
     const bool topp = top_p < 1.f || greedy;
     // the top-p row pass's exponential table (bfloat16 rows; for larger c its
     // entries 2^(u*c) would leave the float64 range)
     S.tab = dtype == sv::DT_BF16 && !greedy && !smc && top_p < 1.f && c <= sv::kTabMaxC;
-    S.lay = layout(B, nslot, nch, nq, topp, smc, S.tab);
+    S.lay = layout(B, nslot, nch, nq, qwords, topp, smc, S.tab);
 
     Params& p = S.p;
     std::memset(&p, 0, sizeof(p));
@@ -310,6 +315,7 @@ int plan(const sv_logits* tl, const sv_logits* dl, const int32_t* draft_tokens, 
     p.cv = cv;
     p.nq = nq;
     p.runs = runs;
+    p.qwords = qwords;
     p.tag = next_tag();
     // c = c_hi + c_lo with c_hi <= c rounded toward zero, so c_lo > 0.
     float c_hi = static_cast<float>(c);

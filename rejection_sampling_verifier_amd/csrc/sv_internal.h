@@ -15,9 +15,12 @@ constexpr int kStatsUnroll = 8;      // default 16-byte vectors in flight per la
 constexpr int kResTile = 8;          // consecutive ids per thread in the id-ordered scans
 constexpr int kRun = 8;              // ids per thread per run of a resample item
 constexpr int kRunsMax = 4;          // runs per thread per resample item, large batches
+constexpr int kRunsBig = 16;         // runs per item when four-run items would not all be resident at once
 constexpr int kRunIds = kThreads * kRun;  // ids per run of an item (2048)
 constexpr int kRecWords = 4;         // 64-bit words per tagged statistics record
-constexpr int kQRecWords = 88;       // 64-bit words per row-pass item record
+constexpr int kQKw = 24;             // word of an item's record where its per-(run, wave) sums start
+// 64-bit words per row-pass item record of items of `runs` runs
+constexpr int qrec_words(int runs) { return kQKw + 4 * runs * kWaves; }
 constexpr int kQCnt = 21;            // word of item 0's record: the row's arrival count
 constexpr int kQMass = 22;           // word of an item's record: its exact mass in a second round
 constexpr int kMaxV = 1 << 21;       // largest vocabulary of the sampling entry points
@@ -89,7 +92,8 @@ struct Params {
     int B, K, V, nslot;
     int nch, cv;                  // statistics pass: chunks per logit row, 16-byte vectors per chunk
     int nq;                       // resample items per batch row (runs*kRunIds ids each)
-    int runs;                     // runs per resample item: 1, 2 or kRunsMax
+    int runs;                     // runs per resample item: 1, 2, kRunsMax or kRunsBig
+    int qwords;                   // qrec_words(runs)
     uint32_t tag;                 // this call's record tag (never 0)
     float c_hi, c_lo;             // c = log2(e)/T = c_hi + c_lo, c_lo > 0 (float32 exponentials)
     double c64;                   // log2(e)/T in float64 (float64 exponentials and decisions)
@@ -100,7 +104,7 @@ struct Params {
     uint32_t stage;               // Philox counter word 2 of the decision (0; 1 for a second verification)
     uint64_t* prec;               // [B, nslot, nch] tagged statistics records
     RvState* rv;                  // [B, nslot]
-    uint64_t* qrec;               // [B, nq, kQRecWords] tagged row-pass item records
+    uint64_t* qrec;               // [B, nq, qwords] tagged row-pass item records
     double* etab;                 // [kTabN] exponential table (bfloat16 top-p calls with c <= kTabMaxC),
                                   // written by the statistics kernel, read by the row pass; else null
     // SMC-SD step (smc = 1): B particles, every one with K drafted tokens

@@ -828,7 +828,7 @@ __global__ __launch_bounds__(kThreads, 8) void k_stats(Params P) {
         // by an earlier call under the same tag (a replayed graph) would pass
         // for this call's (words [item*per, (item+1)*per), per <= kThreads by
         // the host)
-        const int64_t words = static_cast<int64_t>(P.B) * P.nq * kQRecWords;
+        const int64_t words = static_cast<int64_t>(P.B) * P.nq * P.qwords;
         const int64_t grid = static_cast<int64_t>(P.B) * P.nslot * P.nch;
         const int per = static_cast<int>((words + grid - 1) / grid);
         const int64_t e = static_cast<int64_t>(item) * per + threadIdx.x;
@@ -1794,8 +1794,7 @@ constexpr int kAmbGroups = 3;
 constexpr int kQHdr = 9;
 constexpr int kQRound1 = kQHdr + 4 * kAmbGroups;   // 21
 static_assert(kQCnt == kQRound1, "record layout");
-constexpr int kQKw = 24;
-static_assert(kQKw + 4 * kRunsMax * kWaves <= kQRecWords, "record layout");
+static_assert(kQKw >= kQMass + 1, "record layout");
 constexpr int kMaxItems = kMaxV / kRunIds;  // items of a row at most (one-run items)
 
 // Loads n record words until all carry `tag` (true), or kPollLimit polls.
@@ -2287,7 +2286,8 @@ __device__ __forceinline__ void resample_body(const Params& P, int b, int r, con
     const bool aligned = ((reinterpret_cast<uintptr_t>(rowT) & 15) == 0) && ((reinterpret_cast<uintptr_t>(rowD) & 15) == 0);
     const bool interior = static_cast<int64_t>(r + 1) * (R * kRunIds) <= P.V;
     const int nq = P.nq;
-    uint64_t* qrec = P.qrec + static_cast<size_t>(b) * nq * kQRecWords;
+    constexpr int QW = qrec_words(R);  // words per item record
+    uint64_t* qrec = P.qrec + static_cast<size_t>(b) * nq * QW;
     constexpr int kKw = 2 * R * kWaves;
 
     DrawParam dp;
@@ -2413,13 +2413,14 @@ __device__ __forceinline__ void resample_body(const Params& P, int b, int r, con
             const int g = (tid - kQHdr) >> 2, f = ((tid - kQHdr) >> 1) & 1;
             v = f64_word(f == 0 ? s_gT[g] : s_gD[g], (tid - kQHdr) & 1);
         }
-        st_agent(qrec + static_cast<size_t>(r) * kQRecWords + tid, tagged(P.tag, v));
+        st_agent(qrec + static_cast<size_t>(r) * QW + tid, tagged(P.tag, v));
     }
-    if (tid >= 64 && tid < 64 + 2 * kKw) {
-        const int q = tid - 64, slot = q >> 1;
+    // (2 * kKw words: more than the 192 threads past wave 0 for 16-run items)
+    for (int q = tid - 64; tid >= 64 && q < 2 * kKw; q += kThreads - 64) {
+        const int slot = q >> 1;
         const double x = slot < R * kWaves ? sh.kwA[slot / kWaves][slot % kWaves]
                                            : sh.kwB[(slot - R * kWaves) / kWaves][(slot - R * kWaves) % kWaves];
-        st_agent(qrec + static_cast<size_t>(r) * kQRecWords + kQKw + q, tagged(P.tag, f64_word(x, q & 1)));
+        st_agent(qrec + static_cast<size_t>(r) * QW + kQKw + q, tagged(P.tag, f64_word(x, q & 1)));
     }
 
     // 3. arrival: the item that completes the row's count finishes the draw;
@@ -2447,7 +2448,7 @@ __device__ __forceinline__ void resample_body(const Params& P, int b, int r, con
         bool okk = true;
         for (int i = tid - 64; i < nq * kKw; i += kThreads - 64) {
             uint32_t w2[2];
-            okk = poll_words<2>(qrec + static_cast<size_t>(i / kKw) * kQRecWords + kQKw + 2 * (i % kKw), P.tag, w2) &&
+            okk = poll_words<2>(qrec + static_cast<size_t>(i / kKw) * QW + kQKw + 2 * (i % kKw), P.tag, w2) &&
                   okk;
             sh.kwall[i] = f64_of(w2[0], w2[1]);
         }
@@ -2460,7 +2461,7 @@ __device__ __forceinline__ void resample_body(const Params& P, int b, int r, con
         ItemRec q1 = own;
         for (int e = e0; e < e1; ++e) {
             ItemRec q = own;
-            if (e != r) ok = read_item_record(qrec + static_cast<size_t>(e) * kQRecWords, P.tag, q) && ok;
+            if (e != r) ok = read_item_record(qrec + static_cast<size_t>(e) * QW, P.tag, q) && ok;
             sts += q.ST;
             sds += q.SD;
             over |= q.over;
@@ -2504,7 +2505,7 @@ __device__ __forceinline__ void resample_body(const Params& P, int b, int r, con
                 double w = 0.0;
                 for (int k = 0; k < R; ++k)
                     for (int w2 = 0; w2 < kWaves; ++w2) w += sh.kwA[k][w2];
-                st_agent(qrec + static_cast<size_t>(e) * kQRecWords + kQMass,
+                st_agent(qrec + static_cast<size_t>(e) * QW + kQMass,
                          static_cast<uint64_t>(__double_as_longlong(w)));
             }
             __syncthreads();
@@ -2518,13 +2519,13 @@ __device__ __forceinline__ void resample_body(const Params& P, int b, int r, con
             ng = 0;
             if (round2 && !sel)
                 return __longlong_as_double(
-                    static_cast<long long>(ld_agent(qrec + static_cast<size_t>(e) * kQRecWords + kQMass)));
+                    static_cast<long long>(ld_agent(qrec + static_cast<size_t>(e) * QW + kQMass)));
             if (gper == 1) {
                 ng = ng1;
                 return (RESID && !sel) ? m1 : mST;
             }
             ItemRec q = own;
-            if (e != r) ok = read_item_record(qrec + static_cast<size_t>(e) * kQRecWords, P.tag, q) && ok;
+            if (e != r) ok = read_item_record(qrec + static_cast<size_t>(e) * QW, P.tag, q) && ok;
             ng = q.n;
             return item_mass(q, dp.rho, RESID && !sel);
         };
@@ -2618,7 +2619,7 @@ __device__ __forceinline__ void resample_body(const Params& P, int b, int r, con
             sh.kw[tid] = sh.kwall[h * kKw + tid];
         } else {
             uint32_t w2[2];
-            if (!poll_words<2>(qrec + static_cast<size_t>(h) * kQRecWords + kQKw + 2 * tid, P.tag, w2)) s_ok = 0;
+            if (!poll_words<2>(qrec + static_cast<size_t>(h) * QW + kQKw + 2 * tid, P.tag, w2)) s_ok = 0;
             sh.kw[tid] = f64_of(w2[0], w2[1]);
         }
     }
@@ -3417,6 +3418,7 @@ static void launch_smc_rows_r(const Params& p, int dtype, hipStream_t s, const L
 hipError_t launch_smc_rows(const Params& p, int dtype, hipStream_t s, const LaunchEvents& ev) {
     if (p.runs == 1) launch_smc_rows_r<1>(p, dtype, s, ev);
     else if (p.runs == 2) launch_smc_rows_r<2>(p, dtype, s, ev);
+    else if (p.runs == kRunsBig) launch_smc_rows_r<kRunsBig>(p, dtype, s, ev);
     else launch_smc_rows_r<kRunsMax>(p, dtype, s, ev);
     return hipGetLastError();
 }
@@ -3436,6 +3438,7 @@ hipError_t launch_smc_resample(const Params& p, hipStream_t s, const LaunchEvent
 hipError_t launch_rows(const Params& p, int dtype, bool topp, hipStream_t s, const LaunchEvents& ev) {
     if (p.runs == 1) launch_rows_r<1>(p, dtype, topp, s, ev);
     else if (p.runs == 2) launch_rows_r<2>(p, dtype, topp, s, ev);
+    else if (p.runs == kRunsBig) launch_rows_r<kRunsBig>(p, dtype, topp, s, ev);
     else launch_rows_r<kRunsMax>(p, dtype, topp, s, ev);
     return hipGetLastError();
 }

@@ -365,18 +365,20 @@ def test_graph_capture_replays(top_p):
         np.testing.assert_array_equal(got_t, ref_t.cpu().numpy(), err_msg=f"replay {rep}")
 
 
-@pytest.mark.parametrize("runs", [1, 2, 4])
+@pytest.mark.parametrize("runs", [1, 2, 4, 16])
 @pytest.mark.parametrize("unroll", [4, 8])
 def test_kernel_variants(runs, unroll, monkeypatch):
     """Every compiled variant of the statistics kernel (4 or 8 vectors per
-    lane) and of the row pass (items of 1, 2 or 4 runs of 2048 ids) against
-    the oracle, with and without top-p; the library picks a variant per call
-    from the shapes, the environment forces one here."""
+    lane) and of the row pass (items of 1, 2, 4 or 16 runs of 2048 ids)
+    against the oracle, with and without top-p; the library picks a variant
+    per call from the shapes, the environment forces one here.  Sixteen-run
+    items also at a vocabulary of three items, the last one partial."""
     monkeypatch.setenv("SPECVERIFY_STATS_UNROLL", str(unroll))
     monkeypatch.setenv("SPECVERIFY_ROW_RUNS", str(runs))
-    for cfg, top_p in ((2, None), (4, 0.6)):
-        inp = W.make_inputs(cfg, 5, B=6, V=20011, top_p=top_p)
-        _parity(inp, label=f"variant unroll={unroll} runs={runs} cfg={cfg}")
+    for V in ((20011, 70001) if runs == 16 else (20011,)):
+        for cfg, top_p in ((2, None), (4, 0.6)):
+            inp = W.make_inputs(cfg, 5, B=6, V=V, top_p=top_p)
+            _parity(inp, label=f"variant unroll={unroll} runs={runs} cfg={cfg} V={V}")
 
 
 @pytest.mark.parametrize("top_p", [1.0, 0.9])

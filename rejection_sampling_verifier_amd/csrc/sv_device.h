@@ -177,6 +177,30 @@ __device__ __forceinline__ double dpp_f64(double v) {
     const int hi = __builtin_amdgcn_update_dpp(0, static_cast<int>(b >> 32), CTRL, ROWS, 0xF, false);
     return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned int>(lo));
 }
+// A lane move whose lanes outside the moved range read 0 and whose rows
+// outside ROWS are left undefined: for sums that only the group's last lane
+// keeps, where no `old` value needs setting first.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_mov_f64(double v) {
+    const long long b = __double_as_longlong(v);
+    const int lo = __builtin_amdgcn_mov_dpp(static_cast<int>(b), CTRL, ROWS, 0xF, true);
+    const int hi = __builtin_amdgcn_mov_dpp(static_cast<int>(b >> 32), CTRL, ROWS, 0xF, true);
+    return __longlong_as_double((static_cast<long long>(hi) << 32) | static_cast<unsigned int>(lo));
+}
+// Sum over each group of G consecutive lanes (G = 16, 32 or 64, groups
+// aligned to G), held by the group's last lane; other lanes hold partial or
+// undefined values.
+template <int G>
+__device__ __forceinline__ double group_sum_dpp(double v) {
+    static_assert(G == 16 || G == 32 || G == 64, "rows of 16 lanes");
+    v += dpp_mov_f64<kDppRowShr1, 0xF>(v);
+    v += dpp_mov_f64<kDppRowShr2, 0xF>(v);
+    v += dpp_mov_f64<kDppRowShr4, 0xF>(v);
+    v += dpp_mov_f64<kDppRowShr8, 0xF>(v);
+    if (G >= 32) v += dpp_mov_f64<kDppRowBcast15, 0xA>(v);
+    if (G >= 64) v += dpp_mov_f64<kDppRowBcast31, 0xC>(v);
+    return v;
+}
 // Inclusive prefix sum over the wave's lanes (fixed order of additions).
 __device__ __forceinline__ double wave_scan_dpp(double v) {
     v += dpp_f64<kDppRowShr1, 0xF>(v);

@@ -1795,7 +1795,6 @@ constexpr int kQHdr = 9;
 constexpr int kQRound1 = kQHdr + 4 * kAmbGroups;   // 21
 static_assert(kQCnt == kQRound1, "record layout");
 static_assert(kQKw >= kQMass + 1, "record layout");
-constexpr int kMaxItems = kMaxV / kRunIds;  // items of a row at most (one-run items)
 
 // Loads n record words until all carry `tag` (true), or kPollLimit polls.
 template <int N>
@@ -1950,8 +1949,7 @@ __device__ __forceinline__ void for_item_runs(const Params& P, const uint8_t* ro
     }
 }
 
-// Per-thread sums of one item's first pass (rho~ classification); its sums
-// per (run, wave) go to LDS (kwA[k][w], kwB[k][w]).
+// Per-thread sums of one item's first pass (rho~ classification).
 struct ItemSums {
     double ST, SD, A, B;    // all ids; the ids certainly in the residual
     double sT, sD, skey;    // one stashed group of ambiguous ids (equal d, run srun)
@@ -1959,10 +1957,86 @@ struct ItemSums {
     bool shas, sover;
 };
 
+// The first pass keeps each thread's (A, B) of a run in LDS, up to four runs
+// at a time, and sums them per (run, wave) once per group of runs.  Beside
+// the top-p exponential table (whose LDS leaves no room for more while four
+// workgroups fit a compute unit) each run is summed in its wave instead.
+template <int R, bool TB> constexpr int part_runs() { return TB ? 1 : (R < 4 ? R : 4); }
+
+// The ambiguous ids among this thread's ids i0 .. i0+kRun-1 of run k (rare;
+// see above), their logits loaded again: their exponentials, grouped by the
+// exact d (one group per thread; another flags an overflow).  The ids are
+// taken one at a time, so that this cold path holds few registers and the
+// pass around it need not keep its logits.
+template <int DT, bool TOPP>
+__device__ __forceinline__ void stash_ambiguous(const uint8_t* rowT, const uint8_t* rowD, int V, int i0, int k,
+                                                const DrawParam& dp, const double* tab, ItemSums& s) {
+#pragma unroll 1
+    for (int i = 0; i < kRun; ++i) {
+        const int id = i0 + i;
+        float lt = -SV_INF, ld = -SV_INF;
+        if (id < V) {
+            lt = load_logit<DT>(rowT, id);
+            ld = load_logit<DT>(rowD, id);
+        }
+        double eT, eD;
+        id_exps<DT, TOPP, true>(lt, ld, id, dp, tab, eT, eD);
+        const float d = lt - ld;
+        if (eT > 0.0 && eD > 0.0 && d >= dp.dlo && d <= dp.dhi) {
+            const double key = static_cast<double>(lt) - static_cast<double>(ld);
+            if (!s.shas) {
+                s.shas = true;
+                s.sT = eT;
+                s.sD = eD;
+                s.skey = key;
+                s.srun = k;
+            } else if (s.skey == key && s.srun == k) {
+                s.sT += eT;
+                s.sD += eD;
+            } else {
+                s.sover = true;
+            }
+        }
+    }
+}
+
+// Sums per (run, wave) of the runs k0 .. k0+G-1 from the threads' (A, B) in
+// `part`: 64/G threads per (run, wave), G lanes each, then a lane-group sum.
+// Every thread calls it between two barriers.
+template <int G>
+__device__ __forceinline__ void part_reduce(const double2 (*part)[kThreads], int k0, double (*kwA)[kWaves],
+                                            double (*kwB)[kWaves]) {
+    constexpr int TP = 64 / G;  // threads per (run, wave): 16, 32 or 64
+    const int tid = threadIdx.x;
+    const int pr = tid / TP, sub = tid - pr * TP;
+    const int j = pr / kWaves, w = pr - j * kWaves;
+    double a = 0.0, b = 0.0;
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+        const double2 v = part[j][w * 64 + sub * G + q];
+        a += v.x;
+        b += v.y;
+    }
+    a = group_sum_dpp<TP>(a);
+    b = group_sum_dpp<TP>(b);
+    if (sub == TP - 1) {
+        kwA[k0 + j][w] = a;
+        kwB[k0 + j][w] = b;
+    }
+}
+
+// One pass over item r's ids: per id eT, eD (two float64 exponentials) into
+// ST and SD, and into A and B when the id is certainly in the residual; the
+// ids of the band are found wave by wave and stashed apart.  Its sums per
+// (run, wave) go to LDS (kwA[k][w], kwB[k][w]).  Every thread calls it.
 template <int DT, bool TOPP, bool RESID, int R>
 __device__ __forceinline__ void item_first_pass(const Params& P, const uint8_t* rowT, const uint8_t* rowD, bool aligned,
                                                 int r, bool interior, const DrawParam& dp, const double* tab,
-                                                double (*kwA)[kWaves], double (*kwB)[kWaves], ItemSums& s) {
+                                                double2 (*part)[kThreads], double (*kwA)[kWaves],
+                                                double (*kwB)[kWaves], ItemSums& s) {
+    constexpr bool TB = DT == DT_BF16 && TOPP;
+    constexpr int G = part_runs<R, TB>();
+    static_assert(R % G == 0, "whole groups of runs");
     s.ST = 0.0;
     s.SD = 0.0;
     s.A = 0.0;
@@ -1970,9 +2044,10 @@ __device__ __forceinline__ void item_first_pass(const Params& P, const uint8_t* 
     s.sT = s.sD = s.skey = 0.0;
     s.srun = -1;
     s.shas = s.sover = false;
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int tid = threadIdx.x;
     for_item_runs<DT, R, RESID>(P, rowT, rowD, aligned, r, interior, [&](int k, float* lt, float* ld, int i0) {
-        double a = 0.0, bsum = 0.0;
+        double a = 0.0, bsum = 0.0, st = 0.0, sd = 0.0;
+        bool amb = false;
 #pragma unroll
         for (int i = 0; i < kRun; i += 2) {
             double eT[2], eD[2];
@@ -1983,49 +2058,57 @@ __device__ __forceinline__ void item_first_pass(const Params& P, const uint8_t* 
                 pair_fence<RESID>(eT[0], eT[1], eD[0], eD[1], lt[i + 2], lt[i + 3], ld[i + 2], ld[i + 3]);
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                s.ST += eT[h];
                 if (RESID) {
-                    s.SD += eD[h];
-                    // w > 0 iff d = lT - lD > d*: certain outside the float32
+                    st += eT[h];
+                    sd += eD[h];
+                    // w > 0 iff d = lT - lD > d*: certain above the float32
                     // band [dlo, dhi] around d~* (which holds Delta and the
-                    // rounding of lT - lD in float32); an id outside the draft
-                    // nucleus (eD = 0) keeps eT, one outside the target's
-                    // (eT = 0) has none
+                    // rounding of lT - lD in float32), ambiguous inside it.
+                    // With top-p an id outside the draft nucleus (eD = 0)
+                    // keeps eT and one outside the target's (eT = 0) has
+                    // none; without it eT or eD is 0 only at -inf logits or
+                    // below 2^-1074, where the test on d alone decides the
+                    // same up to that much mass.
                     const float d = lt[i + h] - ld[i + h];
-                    const bool inT = eT[h] > 0.0;
-                    const bool in = inT && (eD[h] == 0.0 || d > dp.dhi);
+                    const bool above = d > dp.dhi;
+                    bool in, inb;
+                    if (TOPP) {
+                        const bool inT = eT[h] > 0.0, dpos = eD[h] > 0.0;
+                        in = inT & (!dpos | above);
+                        inb = inT & dpos & !above & (d >= dp.dlo);
+                    } else {
+                        in = above;
+                        inb = !above & (d >= dp.dlo);
+                    }
                     const double m = in ? 1.0 : 0.0;
                     a = fma(m, eT[h], a);
                     bsum = fma(m, eD[h], bsum);
-                    if (inT && eD[h] > 0.0 && d >= dp.dlo && d <= dp.dhi) {
-                        // within the band (rare): grouped by the exact d (one
-                        // group per thread, more flags an overflow)
-                        const double key = static_cast<double>(lt[i + h]) - static_cast<double>(ld[i + h]);
-                        if (!s.shas) {
-                            s.shas = true;
-                            s.sT = eT[h];
-                            s.sD = eD[h];
-                            s.skey = key;
-                            s.srun = k;
-                        } else if (s.skey == key && s.srun == k) {
-                            s.sT += eT[h];
-                            s.sD += eD[h];
-                        } else {
-                            s.sover = true;
-                        }
-                    }
+                    amb = amb | inb;
                 } else {
                     a += eT[h];
                 }
             }
         }
+        s.ST += RESID ? st : a;
+        s.SD += sd;
         s.A += a;
         s.B += bsum;
-        const double wa = wave_sum_dpp(a);
-        const double wb = RESID ? wave_sum_dpp(bsum) : 0.0;
-        if (lane == 0) {
-            kwA[k][wv] = wa;
-            kwB[k][wv] = wb;
+        if (RESID && __builtin_expect(__ballot(amb) != 0ull, 0))
+            stash_ambiguous<DT, TOPP>(rowT, rowD, P.V, i0, k, dp, tab, s);
+        if (TB) {
+            const double wa = group_sum_dpp<64>(a);
+            const double wb = group_sum_dpp<64>(bsum);
+            if ((tid & 63) == 63) {
+                kwA[k][tid >> 6] = wa;
+                kwB[k][tid >> 6] = wb;
+            }
+            return;
+        }
+        part[k % G][tid] = make_double2(a, bsum);
+        if (k % G == G - 1) {
+            __syncthreads();
+            part_reduce<G>(part, k - (G - 1), kwA, kwB);
+            if (k + 1 < R) __syncthreads();
         }
     });
 }
@@ -2143,6 +2226,7 @@ template <int DT, int R, bool TB = false> struct alignas(16) DrawShared {
     union {
         double kwall[kKwPre];
         Partial stage[kThreads];
+        double2 part[part_runs<R, TB>()][kThreads];  // the first pass's per-thread (A, B) of a run
     };
     int item, mode, ok, hk, hw, last, fin, whole;
     double pre, Z, t, rho, hoff, ST;
@@ -2343,7 +2427,7 @@ __device__ __forceinline__ void resample_body(const Params& P, int b, int r, con
     // 1. the item's float64 sums (one pass over its ids); its sums per
     // (run, wave) in LDS
     ItemSums s;
-    item_first_pass<DT, TOPP, RESID, R>(P, rowT, rowD, aligned, r, interior, dp, s_tab, sh.kwA, sh.kwB, s);
+    item_first_pass<DT, TOPP, RESID, R>(P, rowT, rowD, aligned, r, interior, dp, s_tab, sh.part, sh.kwA, sh.kwB, s);
     {
         const double v0 = wave_sum_dpp(s.ST), v1 = wave_sum_dpp(s.SD);
         const double v2 = wave_sum_dpp(s.A), v3 = wave_sum_dpp(s.B);
@@ -2684,7 +2768,7 @@ __device__ __forceinline__ void resample_item(const Params& P, int b, int r, con
 // states (with top-p): the kernels before have finished, so nothing is
 // waited for; all items reach the same decision and item 0 writes it out.
 template <int DT, bool TOPP, int R>
-__global__ __launch_bounds__(kThreads) void k_rows(Params P) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DT == DT_BF16 ? 4 : 1))) void k_rows(Params P) {
     __shared__ RowShared RS;
     __shared__ RowParam s_rp;
     __shared__ DrawSharedT<DT, TOPP, R> DS;
@@ -2773,7 +2857,7 @@ __device__ __forceinline__ void smc_particle(const Params& P, int b, const RowSh
 // Particle pass: one workgroup per (particle, item), as the verify step's
 // row pass with every particle in bonus mode at position K.
 template <int DT, int R>
-__global__ __launch_bounds__(kThreads) void k_smc_rows(Params P) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(DT == DT_BF16 ? 4 : 1))) void k_smc_rows(Params P) {
     __shared__ RowShared RS;
     __shared__ RowParam s_rp;
     __shared__ DrawSharedT<DT, false, R> DS;

@@ -289,6 +289,16 @@ __device__ __forceinline__ void fill_row_from_partials(const Params& P, int b, i
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int nrv = 2 * Le + 1, nch = P.nch;
     const int nrec = nrv * nch;
+    // the first kThreads records are loaded before the first barrier, so that
+    // their round trip overlaps the other loads of the kernel's start
+    uint4 r0a = {0u, 0u, 0u, 0u}, r0c = {0u, 0u, 0u, 0u};
+    if (tid < nrec) {
+        const int rr = tid / nch, c = tid - rr * nch;
+        const uint4* rec = reinterpret_cast<const uint4*>(
+            P.prec + ((static_cast<size_t>(b) * P.nslot + rv_slot(rr, Le, P.K)) * nch + c) * kRecWords);
+        r0a = gload16(rec);
+        r0c = gload16(rec + 1);
+    }
     if (tid < nrv) {
         R.o[tid] = -SV_INF;
         R.m[tid] = -SV_INF;
@@ -303,8 +313,18 @@ __device__ __forceinline__ void fill_row_from_partials(const Params& P, int b, i
         if (e < nrec) {
             const int rr = e / nch, c = e - rr * nch;
             uint32_t pay[kRecWords];
-            const bool ok = read_record(
-                P.prec + ((static_cast<size_t>(b) * P.nslot + rv_slot(rr, Le, P.K)) * nch + c) * kRecWords, P.tag, pay);
+            bool ok;
+            if (base == 0) {
+                pay[0] = r0a.x;
+                pay[1] = r0a.z;
+                pay[2] = r0c.x;
+                pay[3] = r0c.z;
+                ok = r0a.y == P.tag && r0a.w == P.tag && r0c.y == P.tag && r0c.w == P.tag;
+            } else {
+                ok = read_record(
+                    P.prec + ((static_cast<size_t>(b) * P.nslot + rv_slot(rr, Le, P.K)) * nch + c) * kRecWords,
+                    P.tag, pay);
+            }
             stage[tid] = partial_from(pay);
             if (!ok) stage_bad = 1;
         }
@@ -1910,17 +1930,39 @@ __device__ __forceinline__ void id_exps(float lt, float ld, int id, const DrawPa
     }
 }
 
+// One run's raw 16-byte vectors for one thread (target, draft).
+template <int DT> struct RunRaw {
+    uint4 t[kRun / Fmt<DT>::VE], d[kRun / Fmt<DT>::VE];
+};
+// Issues the loads of item r's first run (ahead of the work that decides
+// nothing about them, so that their round trip overlaps it).
+template <int DT, int R, bool RD>
+__device__ __forceinline__ void issue_first_run(const uint8_t* rowT, const uint8_t* rowD, bool aligned, int r, int V,
+                                                RunRaw<DT>& c) {
+    issue_run<DT>(rowT, item_run_id0<R>(r, 0), V, aligned, c.t);
+    if (RD) issue_run<DT>(rowD, item_run_id0<R>(r, 0), V, aligned, c.d);
+}
+
 // Calls f(k, lt, ld, i0) for the runs k = 0..R-1 of item r (lt, ld: the
-// run's logits, i0 its first id), loading run k+1 while run k is processed.
-// The loop stays rolled: one copy of the float64 body keeps the registers of
-// one run live, whatever R.
+// run's logits, i0 its first id), loading run k+1 while run k is processed;
+// run 0 comes from `first` when given (issued by issue_first_run).  The loop
+// stays rolled: one copy of the float64 body keeps the registers of one run
+// live, whatever R.
 template <int DT, int R, bool RD, typename F>
 __device__ __forceinline__ void for_item_runs(const Params& P, const uint8_t* rowT, const uint8_t* rowD, bool aligned,
-                                              int r, bool interior, F&& f) {
+                                              int r, bool interior, F&& f, const RunRaw<DT>* first = nullptr) {
     constexpr int NVR = kRun / Fmt<DT>::VE;
     uint4 ct[NVR], cd[NVR], nt[NVR], nd[NVR];
-    issue_run<DT>(rowT, item_run_id0<R>(r, 0), P.V, aligned, ct);
-    if (RD) issue_run<DT>(rowD, item_run_id0<R>(r, 0), P.V, aligned, cd);
+    if (first) {
+#pragma unroll
+        for (int q = 0; q < NVR; ++q) {
+            ct[q] = first->t[q];
+            if (RD) cd[q] = first->d[q];
+        }
+    } else {
+        issue_run<DT>(rowT, item_run_id0<R>(r, 0), P.V, aligned, ct);
+        if (RD) issue_run<DT>(rowD, item_run_id0<R>(r, 0), P.V, aligned, cd);
+    }
 #pragma unroll 1
     for (int k = 0; k < R; ++k) {
         const int64_t id0 = item_run_id0<R>(r, k);
@@ -2033,7 +2075,7 @@ template <int DT, bool TOPP, bool RESID, int R>
 __device__ __forceinline__ void item_first_pass(const Params& P, const uint8_t* rowT, const uint8_t* rowD, bool aligned,
                                                 int r, bool interior, const DrawParam& dp, const double* tab,
                                                 double2 (*part)[kThreads], double (*kwA)[kWaves],
-                                                double (*kwB)[kWaves], ItemSums& s) {
+                                                double (*kwB)[kWaves], ItemSums& s, const RunRaw<DT>& first) {
     constexpr bool TB = DT == DT_BF16 && TOPP;
     constexpr int G = part_runs<R, TB>();
     static_assert(R % G == 0, "whole groups of runs");
@@ -2110,7 +2152,7 @@ __device__ __forceinline__ void item_first_pass(const Params& P, const uint8_t* 
             part_reduce<G>(part, k - (G - 1), kwA, kwB);
             if (k + 1 < R) __syncthreads();
         }
-    });
+    }, &first);
 }
 
 // Per-(run, wave) weight totals of a second, exact pass over item r (rho
@@ -2318,37 +2360,34 @@ __device__ __forceinline__ int pick_run_wave(const Params& P, const uint8_t* row
 }
 
 // The (run, wave) holding t among R*kWaves sums in id order (run-major,
-// then wave), from `base` (the mass before the item); past the item's total
-// (rounding, or `last`), the last one with mass.  One thread.
-template <int R>
+// then wave), from `base` (the mass before the item), by one wave (lane i
+// takes sum i, a wave scan gives the mass before it); past the item's total
+// (rounding, or `last`), the last one with mass.  Lane 0 stores the result.
+template <int R, typename SH>
 __device__ __forceinline__ void find_run_wave(const double* kA, const double* kB, double rho, bool resid, double base,
-                                              double t, int& last, int& hk, int& hw, double& hoff) {
-    hk = -1;
-    hw = -1;
-    int lk = -1, lw = -1;
-    double loff = 0.0;
-    hoff = 0.0;
-    for (int k = 0; k < R; ++k)
-        for (int w2 = 0; w2 < kWaves; ++w2) {
-            const double a = kA[k * kWaves + w2];
-            const double tot = resid ? fma(-rho, kB[k * kWaves + w2], a) : a;
-            if (tot > 0.0) {
-                if (hk < 0 && !last && base + tot > t) {
-                    hk = k;
-                    hw = w2;
-                    hoff = base;
-                }
-                lk = k;
-                lw = w2;
-                loff = base;
-            }
-            base += tot;
-        }
-    if (hk < 0) {
-        hk = lk;
-        hw = lw;
-        hoff = loff;
-        last = 1;
+                                              double t, SH& sh) {
+    static_assert(R * kWaves <= 64, "one lane per (run, wave)");
+    const int lane = threadIdx.x & 63;
+    const bool has = lane < R * kWaves;
+    double tot = 0.0;
+    if (has) tot = resid ? fma(-rho, kB[lane], kA[lane]) : kA[lane];
+    const double before = base + dpp_f64<kDppWaveShr1, 0xF>(wave_scan_dpp(tot));
+    const bool last = sh.last != 0;
+    const unsigned long long cm = __ballot(has && tot > 0.0 && !last && before + tot > t);
+    const unsigned long long pm = __ballot(has && tot > 0.0);
+    int i = -1, lastf = last ? 1 : 0;
+    if (cm) {
+        i = __ffsll(static_cast<long long>(cm)) - 1;
+    } else if (pm) {
+        i = 63 - __clzll(static_cast<long long>(pm));
+        lastf = 1;
+    }
+    const double hoff = i >= 0 ? readlane_f64(before, i) : 0.0;
+    if (lane == 0) {
+        sh.hk = i >= 0 ? i / kWaves : -1;
+        sh.hw = i >= 0 ? i % kWaves : -1;
+        sh.hoff = hoff;
+        sh.last = lastf;
     }
 }
 
@@ -2369,6 +2408,8 @@ __device__ __forceinline__ void resample_body(const Params& P, int b, int r, con
     const uint8_t* rowD = RESID ? row_ptr<DT>(P, false, b, rn) : rowT;
     const bool aligned = ((reinterpret_cast<uintptr_t>(rowT) & 15) == 0) && ((reinterpret_cast<uintptr_t>(rowD) & 15) == 0);
     const bool interior = static_cast<int64_t>(r + 1) * (R * kRunIds) <= P.V;
+    RunRaw<DT> first;
+    issue_first_run<DT, R, RESID>(rowT, rowD, aligned, r, P.V, first);
     const int nq = P.nq;
     constexpr int QW = qrec_words(R);  // words per item record
     uint64_t* qrec = P.qrec + static_cast<size_t>(b) * nq * QW;
@@ -2417,17 +2458,18 @@ __device__ __forceinline__ void resample_body(const Params& P, int b, int r, con
         dp.dlo = sgpr_f32(flo);
         dp.dhi = sgpr_f32(fhi);
     }
-    // (the exponential table was filled at the kernel's start)
+    // (the exponential table was filled at the kernel's start; the groups'
+    // count is read after the barriers that follow the first pass)
     if (tid == 0) {
         s_gn = 0;
         s_gover = 0;
     }
-    __syncthreads();
 
     // 1. the item's float64 sums (one pass over its ids); its sums per
     // (run, wave) in LDS
     ItemSums s;
-    item_first_pass<DT, TOPP, RESID, R>(P, rowT, rowD, aligned, r, interior, dp, s_tab, sh.part, sh.kwA, sh.kwB, s);
+    item_first_pass<DT, TOPP, RESID, R>(P, rowT, rowD, aligned, r, interior, dp, s_tab, sh.part, sh.kwA, sh.kwB, s,
+                                        first);
     {
         const double v0 = wave_sum_dpp(s.ST), v1 = wave_sum_dpp(s.SD);
         const double v2 = wave_sum_dpp(s.A), v3 = wave_sum_dpp(s.B);
@@ -2712,15 +2754,7 @@ __device__ __forceinline__ void resample_body(const Params& P, int b, int r, con
         row_failed(P, b);
         return;
     }
-    if (tid == 0) {
-        int last = s_last, hk, hw;
-        double hoff;
-        find_run_wave<R>(sh.kw, sh.kw + R * kWaves, dp.rho, resid && !sh.whole, s_pre, t, last, hk, hw, hoff);
-        s_hk = hk;
-        s_hw = hw;
-        s_hoff = hoff;
-        s_last = last;
-    }
+    if (wv == 0) find_run_wave<R>(sh.kw, sh.kw + R * kWaves, dp.rho, resid && !sh.whole, s_pre, t, sh);
     __syncthreads();
     // the verify step's token at position n, or an SMC particle's bonus
     int32_t* outp = P.smc ? P.out_tokens + b : P.out_tokens + static_cast<size_t>(b) * (P.K + 1) + rn;

@@ -2270,7 +2270,7 @@ template <int DT, int R, bool TB = false> struct alignas(16) DrawShared {
         Partial stage[kThreads];
         double2 part[part_runs<R, TB>()][kThreads];  // the first pass's per-thread (A, B) of a run
     };
-    int item, mode, ok, hk, hw, last, fin, whole;
+    int item, mode, ok, hk, hw, last, fin, whole, early;
     double pre, Z, t, rho, hoff, ST;
     // ambiguous groups of the item (key, GT, GD), their count and overflow
     double gkey[kAmbGroups], gT[kAmbGroups], gD[kAmbGroups];
@@ -2338,23 +2338,31 @@ __device__ __forceinline__ int pick_run_wave(const Params& P, const uint8_t* row
         }
     }
     const double mine = wv2[0] + wv2[1];
-    double incl, excl, total;
-    block_scan(mine, incl, excl, total);
-    const int cross = block_min_int((mine > 0.0 && !last && hoff + incl > t) ? tid : 0x7FFFFFFF);
-    int who = cross;
-    bool lastmode = last;
-    if (cross == 0x7FFFFFFF) {
-        who = block_max_int(mine > 0.0 ? tid : -1);
-        lastmode = true;
-    }
-    if (tid == 0) s_y = -1;
+    // the running mass: a wave scan in lane moves, the earlier waves' totals
+    // through LDS; in each wave the first thread whose running mass passes t
+    // offers its id, and the smallest offer is the token (ids grow with the
+    // thread)
+    __shared__ double s_wt[kWaves];
+    const int lane = tid & 63, wv = tid >> 6;
+    const double wincl = wave_scan_dpp(mine);
+    const double wexcl = dpp_f64<kDppWaveShr1, 0xF>(wincl);
+    if (lane == 63) s_wt[wv] = wincl;
+    if (tid == 0) s_y = 0x7FFFFFFF;
     __syncthreads();
-    if (tid == who) {
-        int y;
-        if (lastmode) y = static_cast<int>(wv2[1] > 0.0 ? id0 + 1 : id0);
-        else y = static_cast<int>((wv2[0] > 0.0 && hoff + excl + wv2[0] > t) || !(wv2[1] > 0.0) ? id0 : id0 + 1);
-        s_y = y;
+    double off = 0.0;
+    for (int k = 0; k < wv; ++k) off += s_wt[k];
+    const double incl = off + wincl, excl = off + wexcl;
+    const unsigned long long cm = __ballot(!last && mine > 0.0 && hoff + incl > t);
+    if (cm != 0ull && lane == __ffsll(static_cast<long long>(cm)) - 1) {
+        const int y = static_cast<int>((wv2[0] > 0.0 && hoff + excl + wv2[0] > t) || !(wv2[1] > 0.0) ? id0 : id0 + 1);
+        atomicMin(&s_y, y);
     }
+    __syncthreads();
+    if (s_y != 0x7FFFFFFF) return s_y;
+    // with `last`, or when rounding leaves no crossing: the last id with mass
+    const int who = block_max_int(mine > 0.0 ? tid : -1);
+    if (who < 0) return -1;
+    if (tid == who) s_y = static_cast<int>(wv2[1] > 0.0 ? id0 + 1 : id0);
     __syncthreads();
     return s_y;
 }
@@ -2365,14 +2373,13 @@ __device__ __forceinline__ int pick_run_wave(const Params& P, const uint8_t* row
 // (rounding, or `last`), the last one with mass.  Lane 0 stores the result.
 template <int R, typename SH>
 __device__ __forceinline__ void find_run_wave(const double* kA, const double* kB, double rho, bool resid, double base,
-                                              double t, SH& sh) {
+                                              double t, bool last, SH& sh) {
     static_assert(R * kWaves <= 64, "one lane per (run, wave)");
     const int lane = threadIdx.x & 63;
     const bool has = lane < R * kWaves;
     double tot = 0.0;
     if (has) tot = resid ? fma(-rho, kB[lane], kA[lane]) : kA[lane];
     const double before = base + dpp_f64<kDppWaveShr1, 0xF>(wave_scan_dpp(tot));
-    const bool last = sh.last != 0;
     const unsigned long long cm = __ballot(has && tot > 0.0 && !last && before + tot > t);
     const unsigned long long pm = __ballot(has && tot > 0.0);
     int i = -1, lastf = last ? 1 : 0;
@@ -2711,15 +2718,24 @@ __device__ __forceinline__ void resample_body(const Params& P, int b, int r, con
             last = 1;
         }
         const bool allok = __ballot(!ok) == 0ull;
+        const bool whole = round2 || sel || hng > 0;
+        // the common case: the holding item's published sums are in LDS
+        // already, so this wave finds its (run, wave) now (writing hk, hw,
+        // hoff and last)
+        const bool early = kwpre && !whole;
+        if (early)
+            find_run_wave<R>(sh.kwall + item * kKw, sh.kwall + item * kKw + R * kWaves, dp.rho, RESID && !sel, spre, t,
+                             last != 0, sh);
         if (lane == 0) {
             s_item = item;
             s_pre = spre;
             s_Z = Z;
             s_t = t;
-            s_last = last;
+            if (!early) s_last = last;
             s_ok = allok ? 1 : 0;
             if (sel) s_mode = 1;
-            sh.whole = (round2 || sel || hng > 0) ? 1 : 0;
+            sh.whole = whole ? 1 : 0;
+            sh.early = early ? 1 : 0;
         }
     }
     __syncthreads();
@@ -2735,27 +2751,30 @@ __device__ __forceinline__ void resample_body(const Params& P, int b, int r, con
     // 5. the holding item's sums per (run, wave): published (fetched above,
     // or now), or recomputed exactly (a second round, the draw from p', or
     // ambiguous ids in it); then its (run, wave) holding t and its token
-    if (sh.whole) {
-        const bool interior_h = static_cast<int64_t>(h + 1) * (R * kRunIds) <= P.V;
-        item_exact_pass<DT, TOPP, RESID, R>(P, rowT, rowD, aligned, h, interior_h, dp, s_tab, sel, sh.kwA, sh.kwB);
-        __syncthreads();
-        if (tid < kKw) sh.kw[tid] = tid < R * kWaves ? sh.kwA[tid / kWaves][tid % kWaves] : 0.0;
-    } else if (tid < kKw) {
-        if (kwpre) {
-            sh.kw[tid] = sh.kwall[h * kKw + tid];
-        } else {
-            uint32_t w2[2];
-            if (!poll_words<2>(qrec + static_cast<size_t>(h) * QW + kQKw + 2 * tid, P.tag, w2)) s_ok = 0;
-            sh.kw[tid] = f64_of(w2[0], w2[1]);
+    if (!sh.early) {
+        if (sh.whole) {
+            const bool interior_h = static_cast<int64_t>(h + 1) * (R * kRunIds) <= P.V;
+            item_exact_pass<DT, TOPP, RESID, R>(P, rowT, rowD, aligned, h, interior_h, dp, s_tab, sel, sh.kwA, sh.kwB);
+            __syncthreads();
+            if (tid < kKw) sh.kw[tid] = tid < R * kWaves ? sh.kwA[tid / kWaves][tid % kWaves] : 0.0;
+        } else if (tid < kKw) {
+            if (kwpre) {
+                sh.kw[tid] = sh.kwall[h * kKw + tid];
+            } else {
+                uint32_t w2[2];
+                if (!poll_words<2>(qrec + static_cast<size_t>(h) * QW + kQKw + 2 * tid, P.tag, w2)) s_ok = 0;
+                sh.kw[tid] = f64_of(w2[0], w2[1]);
+            }
         }
+        __syncthreads();
+        if (!s_ok) {
+            row_failed(P, b);
+            return;
+        }
+        if (wv == 0)
+            find_run_wave<R>(sh.kw, sh.kw + R * kWaves, dp.rho, resid && !sh.whole, s_pre, t, s_last != 0, sh);
+        __syncthreads();
     }
-    __syncthreads();
-    if (!s_ok) {
-        row_failed(P, b);
-        return;
-    }
-    if (wv == 0) find_run_wave<R>(sh.kw, sh.kw + R * kWaves, dp.rho, resid && !sh.whole, s_pre, t, sh);
-    __syncthreads();
     // the verify step's token at position n, or an SMC particle's bonus
     int32_t* outp = P.smc ? P.out_tokens + b : P.out_tokens + static_cast<size_t>(b) * (P.K + 1) + rn;
     const int hk = s_hk, hw = s_hw;

@@ -128,15 +128,42 @@ def _rng(cfg, step):
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence([0x5EED0000 + cfg, step])))
 
 
-def _gumbel_argmax(rng, logits, temperature, top=None):
-    """Exact sample of softmax(logits / T) by Gumbel-max (optionally over the
-    `top` largest logits only).  logits: [..., V] float32."""
+def _nucleus_gumbel(rng, logits, temperature, top_p, cand=4096):
+    """Sample of the top-p-filtered softmax(logits / T) per row: tokens sorted
+    by probability (descending, ties by the lower id), the shortest prefix
+    whose running mass reaches top_p kept, then Gumbel-max over the kept ids
+    (an exact sample of the renormalised prefix).  The prefix is looked for
+    among the `cand` largest logits first, the whole row when it lies deeper.
+    logits: [..., V] float32."""
     flat = logits.reshape(-1, logits.shape[-1])
     out = np.empty(flat.shape[0], np.int64)
     for i, row in enumerate(flat):
-        ids = np.arange(row.size) if top is None else np.argpartition(-row, top - 1)[:top]
-        g = -np.log(-np.log(rng.random(ids.size)))
-        out[i] = ids[int(np.argmax(row[ids].astype(np.float64) / temperature + g))]
+        z = row.astype(np.float64) / temperature
+        e = np.exp(z - np.max(z))
+        S = float(np.sum(e))
+        V = row.size
+        ids = np.arange(V) if V <= cand else np.sort(np.argpartition(-z, cand - 1)[:cand])
+        order = ids[np.argsort(-e[ids], kind="stable")]
+        run = np.cumsum(e[order]) / S
+        hit = np.nonzero(run >= top_p)[0]
+        if hit.size == 0 and ids.size < V:
+            order = np.argsort(-e, kind="stable")
+            run = np.cumsum(e[order]) / S
+            hit = np.nonzero(run >= top_p)[0]
+        kept = order[: int(hit[0]) + 1] if hit.size else order
+        g = -np.log(-np.log(rng.random(kept.size)))
+        out[i] = kept[int(np.argmax(z[kept] + g))]
+    return out.reshape(logits.shape[:-1])
+
+
+def _gumbel_argmax(rng, logits, temperature):
+    """Exact sample of softmax(logits / T) by Gumbel-max.  logits: [..., V]
+    float32."""
+    flat = logits.reshape(-1, logits.shape[-1])
+    out = np.empty(flat.shape[0], np.int64)
+    for i, row in enumerate(flat):
+        g = -np.log(-np.log(rng.random(row.size)))
+        out[i] = int(np.argmax(row.astype(np.float64) / temperature + g))
     return out.reshape(logits.shape[:-1])
 
 
@@ -169,8 +196,10 @@ def make_inputs(cfg, step=0, *, B=None, K=None, V=None, dtype=None, temperature=
     else:
         target_s, draft_s, draft_vals = target, draft.astype(np.float32), draft.astype(np.float32)
 
-    top = 64 if (tp < 1.0 and V > 64) else None
-    tokens = _gumbel_argmax(rng, draft_vals, float(T), top=top).astype(np.int32)
+    if tp < 1.0:
+        tokens = _nucleus_gumbel(rng, draft_vals, float(T), float(tp)).astype(np.int32)
+    else:
+        tokens = _gumbel_argmax(rng, draft_vals, float(T)).astype(np.int32)
 
     draft_len = None
     if w.ragged:

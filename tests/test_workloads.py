@@ -71,3 +71,28 @@ def test_full_batched_shape():
     x = W.make_inputs(2, 0)
     assert x.target.shape == (64, 6, 128256) and x.target.dtype == np.uint16
     assert x.logical_bytes() == 180584448 and x.positions() == 320
+
+
+def test_filtered_drafts_come_from_the_draft_nucleus():
+    # the filtered workload drafts from the top-p-filtered draft softmax:
+    # every drafted token lies in the oracle's nucleus of its draft row, and
+    # over many rows the tokens follow the filtered distribution
+    x = W.make_inputs(4, 0, B=6, V=5003)
+    for b in range(x.B):
+        for j in range(x.K):
+            p, _, _ = oracle.softmax(oracle.widen_bf16(x.draft[b, j]), float(x.temperature))
+            q, _, _ = oracle.nucleus(p, float(x.top_p))
+            assert q[x.draft_tokens[b, j]] > 0.0, (b, j)
+    rng = np.random.default_rng(5)
+    row = (rng.standard_normal(40) * 2.0).astype(np.float32)
+    p, _, _ = oracle.softmax(row.astype(np.float64), 0.7)
+    q, _, _ = oracle.nucleus(p, 0.9)
+    n = 20000
+    toks = W._nucleus_gumbel(np.random.default_rng(6), np.tile(row, (n, 1)), 0.7, 0.9, cand=8)
+    counts = np.bincount(toks, minlength=row.size)
+    assert np.all(counts[q == 0.0] == 0)
+    exp = q * n
+    m = exp > 0
+    chi2 = float(np.sum((counts[m] - exp[m]) ** 2 / exp[m]))
+    from scipy.stats import chi2 as C
+    assert C.sf(chi2, int(m.sum()) - 1) > 1e-4, chi2

@@ -599,11 +599,89 @@ template <int DT> __device__ __forceinline__ float elem_at(const uint4& v, int r
     return __uint_as_float((rx & 1) ? (w & 0xFFFF0000u) : (w << 16));
 }
 
+// The statistics of one lane's U vectors in one pass (top-p off): each
+// vector is unpacked once for its max and its terms 2^(l*c - o).  The offset
+// o is set kLaneHead above the first vector's max (scaled), so that later,
+// larger logits still give finite float32 terms; a vector whose max lies
+// more than kLaneSafe above o (rare: a logit far above the lane's first
+// vector's) moves o up first and rescales the partial sums by the exact
+// power of two (64 terms of at most 2^kLaneSafe cannot overflow; terms
+// flushed below 2^-126 lie at least 2^-62 below the lane's largest).
+constexpr float kLaneHead = 64.f;
+constexpr float kLaneSafe = 119.f;
+
+template <int DT, int U>
+__device__ __forceinline__ void reduce_lane_once(const RowGrid& g, uint4* raw, int64_t k0, int64_t k1, int V,
+                                                 bool edge, float c_hi, float c_lo, int64_t kx, int rx, float& lx,
+                                                 float& m, float& o, float& s) {
+    constexpr int VE = Fmt<DT>::VE;
+    static_assert((U & (U - 1)) == 0 && U <= 64, "U a power of two");
+    if (edge) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t k = k0 + u * kThreads + threadIdx.x;
+            if (k < k1 && (k == 0 || k == g.nvec - 1)) mask_edge_raw<DT>(raw[u], k, g.head, V);
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+        if (k0 + u * kThreads + threadIdx.x == kx) lx = elem_at<DT>(raw[u], rx);
+    // the vector sums combine pairwise as they come (a binary counter: at
+    // most log2(U) partial sums live)
+    float part[6] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float total = 0.f, mx = -SV_INF, oo = -SV_INF;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        // one vector at a time: its unpacked values die with it
+        __builtin_amdgcn_sched_barrier(0);
+        float e[VE];
+#pragma unroll
+        for (int i = 0; i < VE; ++i) e[i] = elem<DT>(raw[u], i);
+        float vm = e[0];
+#pragma unroll
+        for (int i = 1; i + 1 < VE; i += 2) vm = max3f(vm, e[i], e[i + 1]);
+        vm = fmaxf(vm, e[VE - 1]);
+        mx = fmaxf(mx, vm);
+        if (u == 0) {
+            oo = ceilf(vm * c_hi) + kLaneHead;  // -inf stays -inf
+        } else if (vm * c_hi > oo + kLaneSafe) {
+            const float no = ceilf(vm * c_hi) + kLaneHead;
+            const float sc = (oo == -SV_INF) ? 0.f : ldexpf(1.f, static_cast<int>(fmaxf(oo - no, -200.f)));
+#pragma unroll
+            for (int l = 0; l < 6; ++l) part[l] *= sc;
+            oo = no;
+        }
+        const float off = (oo == -SV_INF) ? 0.f : oo;
+#pragma unroll
+        for (int i = 0; i < VE; ++i) e[i] = tempexp(e[i], c_hi, c_lo, off);
+#pragma unroll
+        for (int w = VE / 2; w >= 1; w >>= 1)
+#pragma unroll
+            for (int i = 0; i < w; ++i) e[i] += e[i + w];
+        float v = e[0];
+#pragma unroll
+        for (int l = 0; l < 6; ++l) {
+            if ((1 << l) >= U) break;
+            if ((u >> l) & 1) {
+                v = part[l] + v;
+            } else {
+                part[l] = v;
+                break;
+            }
+        }
+        if (u == U - 1) total = v;
+    }
+    m = mx;
+    o = oo;
+    s = total;
+}
+
 // With top-p (CAND) the exponents are taken against the wave's offset
 // instead of the lane's, and every element with e = 2^(l*c - o) >= 2^-15
 // also counts into the wave's histogram `hist` by the top 9 bits of e
 // (exponent and two mantissa bits: quarter-octave bins of the mass, a
 // monotone function of l within the wave; the 64 bins cover [2^-15, 2)).
+
 template <int DT, int U, bool CAND>
 __device__ __forceinline__ void reduce_lane(const RowGrid& g, uint4* raw, int64_t k0, int64_t k1, int V, bool edge,
                                             float c_hi, float c_lo, int64_t kx, int rx, uint32_t* hist, float& lx,
@@ -791,8 +869,9 @@ __device__ __forceinline__ void stats_item(const Params& P, int b, int slot, int
         hist[lane] = 0u;  // each wave clears its own histogram (same-wave LDS order)
     }
     float lx = -SV_INF, m, o, sl;
-    reduce_lane<DT, U, CAND>(g, raw, k0, k1, P.V, k0 == 0 || k0 + STEP >= g.nvec - 1, P.c_hi, P.c_lo, kx, rx, hist,
-                             lx, m, o, sl);
+    const bool edge = k0 == 0 || k0 + STEP >= g.nvec - 1;
+    if (CAND) reduce_lane<DT, U, CAND>(g, raw, k0, k1, P.V, edge, P.c_hi, P.c_lo, kx, rx, hist, lx, m, o, sl);
+    else reduce_lane_once<DT, U>(g, raw, k0, k1, P.V, edge, P.c_hi, P.c_lo, kx, rx, lx, m, o, sl);
     if (CAND) {
         const size_t ci = (static_cast<size_t>(b) * P.nslot + slot) * P.nch + chunk;
         list_wave_candidates<DT, U>(P, g, raw, k0, o, hist, sh_stage[wv], ci * kCand + wv * kCandW,

@@ -2334,9 +2334,10 @@ __device__ __forceinline__ bool row_arrive(uint64_t* cnt, int nq) {
 }
 
 // The draw's LDS (one instance per workgroup, shared by the residual and
-// bonus variants of the kernel).  kwall holds every item's published
-// per-(run, wave) sums when they fit (kKwPre doubles), the statistics
-// records staged by the decision before that.
+// bonus variants of the kernel).  One LDS area serves three steps in turn:
+// the statistics records staged by the decision, the first pass's
+// per-thread run sums, and every item's published per-(run, wave) sums
+// fetched by the finisher when they fit (kKwPre doubles).
 constexpr int kKwPre = 512;
 template <int DT, int R, bool TB = false> struct alignas(16) DrawShared {
     double tab[kExpTab];

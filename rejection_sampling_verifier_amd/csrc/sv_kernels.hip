@@ -426,7 +426,7 @@ __device__ __forceinline__ void fill_row_from_rv(const Params& P, int b, int Le,
 // row's accepted tokens, -1 padding, n, and the probe records; the token at
 // position n is the resample's.
 // Lane j < Le's drafted id (loaded early by the callers, to overlap the load
-// with their waits).
+// with that of the statistics records).
 __device__ __forceinline__ int lane_token(const Params& P, int b, int Le) {
     const int lane = threadIdx.x & 63;
     return (lane < Le) ? P.tokens[static_cast<int64_t>(b) * P.K + lane] : -1;
@@ -1217,7 +1217,7 @@ constexpr float kGapPerBit = 64.f;
 constexpr int kRadixBins = 256;         // a radix pass splits a key interval by 8 bits
 constexpr int kCollect = 512;           // tokens a collect-and-sort step takes
 
-// Small enough that every logit row's workgroup is resident at once.
+// The nucleus pass's LDS (about 15 KB: several workgroups fit a CU).
 struct SelShared {
     double mass[kGapBins];              // gap histogram; radix masses in [0, kRadixBins)
     uint32_t cnt[kRadixBins];
@@ -1728,19 +1728,18 @@ __global__ __launch_bounds__(kThreads) void k_topp(Params P) {
 
 // ---------------------------------------------------------------------------
 // Row pass.  Workgroup (b, r) is resample item r of batch row b: ids
-// [r*I, (r+1)*I) of the row's position n, I = R*kThreads*kRun (R runs, 4 for
-// large batches, 1 when the batch has few items, which quadruples the
-// workgroups).  Run k is the kThreads*kRun ids from r*I + k*kThreads*kRun,
-// thread t taking
-// the kRun consecutive ids at t*kRun (16-byte loads, coalesced).  Without
-// top-p every item first makes the row's decision from the statistics
-// records (all items reach the same one; item 0 writes the outputs).  Each
-// item keeps its weights in LDS and publishes its residual (or bonus) mass W
-// and target mass as a tagged record; every item then reads all the row's
-// records, forms Z and t = u*Z, and the item holding t picks the token from
-// its weights.  The waits are on records of workgroups of the same row, which
-// are consecutive in the grid: when a row has an item still to start, all
-// earlier rows' items are running or done, so every wait ends.
+// [r*I, (r+1)*I) of the row's position n, I = R*kThreads*kRun (R runs: 4 by
+// default, 1 when the batch has few items, 16 when four-run items would not
+// all be resident at once).  Run k is the kThreads*kRun ids from r*I +
+// k*kThreads*kRun, thread t taking the kRun consecutive ids at t*kRun
+// (16-byte loads, coalesced).  Every item first makes the row's decision from
+// the statistics records or, with top-p, the nucleus row states (all items
+// reach the same one; item 0 writes the outputs).  It then takes one float64
+// pass over its ids, publishes its sums as a tagged record and adds 1 to the
+// row's arrival count; the item whose add completes the count finishes the
+// row from the others' records (exact rho, the masses, Z, t = u*Z, the item
+// and (run, wave) holding t, the token from that run-wave's recomputed
+// weights).  No workgroup waits for another to start or to reach any point.
 // ---------------------------------------------------------------------------
 
 // A readable 16-byte vector that stands in for loads past the end of a row.

@@ -243,6 +243,27 @@ def test_extreme_and_masked_logits():
     _parity(inp, label="extreme / masked")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_lane_offsets_moved_up(dtype):
+    """Rows whose statistics lanes see their larger logits only in later
+    vectors: the first vector of every lane of the chunk all -inf (then the
+    lane's offset starts at -inf), or a far larger logit in a later vector
+    (the offset moves up and the partial sums rescale)."""
+    V = 5000
+    first = 256 * (8 if dtype == "bf16" else 4)   # ids of the lanes' first vectors
+    inp = W.synthetic(4, 3, V, dtype="f32", temperature=0.7, seed=14, gen_seed=14)
+    inp.target[0, :, :first] = -np.inf
+    inp.draft[0, :, :first] = -np.inf
+    inp.draft_tokens[0] = [first + 17, first + 900, V - 3]
+    inp.target[1, :, first + 5::7] += 60.0    # far above each lane's first vector
+    inp.draft[1, :, first + 5::7] += 60.0
+    inp.target[2, :, :first] -= 40.0
+    if dtype == "bf16":
+        inp = W.Inputs(inp.workload, inp.step, W.f32_to_bf16_bits(inp.target), W.f32_to_bf16_bits(inp.draft),
+                       inp.draft_tokens, inp.draft_len, inp.temperature, inp.top_p, inp.seed)
+    _parity(inp, label=f"lane offsets moved up {dtype}")
+
+
 def test_identical_models_accept_all():
     inp = W.synthetic(10, 5, 4000, dtype="bf16", seed=12, gen_seed=12)
     inp.draft[:] = inp.target[:, :5]
